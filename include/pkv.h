@@ -1,0 +1,169 @@
+/*
+ * pkv.h -- paged grouped-query attention for MI355X (gfx950): C ABI.
+ *
+ * Pages cited below:
+ *   [P1] "Module 12: Final project - mini inference engine" (LLM Inference
+ *        Systems course), listings qwen_serve/paged.py and qwen_serve/model.py.
+ *   [P2] "Module 04: KV cache and memory arithmetic" (same course).
+ *   [P3] "Inference Optimization" (AI Engineering from Scratch), section
+ *        "Paged Attention".
+ *
+ * Data layout (all tensors contiguous, row-major, bf16 unless stated):
+ *   k_cache, v_cache   [num_blocks][block_size=16][Hkv][D]   one layer's page pool
+ *                      (the per-layer slice of [P1] paged.py's
+ *                      [n_layers, capacity, block_size, n_kv_heads, head_dim]:
+ *                      block b at dim 0, slot s at dim 1).
+ *   block_tables       int32 [B][max_blocks_per_seq]: logical page i of
+ *                      sequence b lives in physical page block_tables[b][i]
+ *                      ([P1] SequenceCache.blocks; [P3] page table).  Entries
+ *                      past a sequence's last page are never read.
+ *   context_lens       int32 [B]: tokens in each sequence's pages, counting
+ *                      the tokens appended in this step (append runs first).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller (except
+ * where "host" is stated).  The library allocates nothing, keeps no pointer
+ * after a call returns and enqueues all work on `stream` (a hipStream_t;
+ * NULL is the default stream): buffers must stay alive until the stream has
+ * passed the work.  Calls on one stream are ordered; calls on different
+ * streams that touch the same memory need the caller's synchronisation.
+ *
+ * Errors: every entry point returns PKV_OK (0) or a negative code and never
+ * throws.  Argument and shape errors are detected on the host before any
+ * launch (nothing is enqueued).  The contents of index arrays live on the
+ * device and are not inspected on the hot path: kernels stay inside their
+ * buffers whatever the indices hold (an out-of-range block id or length
+ * makes the affected outputs NaN; an out-of-range slot is skipped).  With
+ * the environment variable PKV_VALIDATE=1 each call first copies its index
+ * arrays to the host (synchronising `stream`) and rejects bad contents with
+ * PKV_EVALIDATE.  pkv_last_error() returns a thread-local message for the
+ * last non-OK return on the calling thread.
+ *
+ * Supported geometry: block_size 16 ([P1] default --block-size 16), D = 128
+ * (every model the pages name), Hq % Hkv == 0 with Hq/Hkv in {1,2,4,8};
+ * anything else returns PKV_EUNSUPPORTED.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* null pointer, negative size, inconsistent shapes */
+  PKV_EUNSUPPORTED = -2,  /* geometry outside the supported set */
+  PKV_EWORKSPACE = -3,    /* decode workspace smaller than required */
+  PKV_ELAUNCH = -4,       /* the HIP runtime reported an error */
+  PKV_EVALIDATE = -5      /* PKV_VALIDATE=1 found bad index contents */
+};
+
+#define PKV_BLOCK_SIZE 16
+#define PKV_HEAD_DIM 128
+
+/*
+ * Slot mapping ([P1] paged.py PagedKVCache.write: position s goes to
+ * (blocks[s // block_size], s % block_size); model.py forward: a step's
+ * tokens take positions start_pos .. start_pos+T-1, start_pos being the
+ * committed length).
+ *
+ * Sequence b appends n_b = cu_new_lens[b+1] - cu_new_lens[b] tokens which end
+ * its context, so token j (0 <= j < n_b) sits at p = context_lens[b] - n_b + j
+ * and gets the flat physical slot
+ *     slot_mapping[cu_new_lens[b] + j] = block_tables[b][p / 16] * 16 + p % 16.
+ * A position that would fall outside the table (p < 0 or p / 16 >=
+ * max_blocks_per_seq) yields -1 (skip).
+ *   slot_mapping  int32 [total_new] (output)
+ *   cu_new_lens   int32 [B+1], nondecreasing, cu_new_lens[0] = 0,
+ *                 cu_new_lens[B] = total_new
+ */
+int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* cu_new_lens, const int32_t* context_lens,
+                     int32_t B, int32_t max_blocks_per_seq, int32_t total_new,
+                     int32_t block_size, void* stream);
+
+/*
+ * KV append ([P1] paged.py PagedKVCache.write; model.py forward writes the
+ * step's K/V into the pages).  A bit-exact scatter of rows:
+ *     k_cache[slot / 16][slot % 16][:][:] = k_new[t][:][:]   (same for V)
+ * for every t with 0 <= slot = slot_mapping[t] < num_blocks*16; other slots
+ * (negative = padding) are skipped.  Slots must be distinct (duplicates race;
+ * PKV_VALIDATE=1 rejects them).
+ *   k_new, v_new  bf16 [T][Hkv][D]
+ */
+int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+               void* k_cache, void* v_cache, int32_t T, int32_t num_blocks,
+               int32_t Hkv, int32_t D, int32_t block_size, void* stream);
+
+/*
+ * Workspace for pkv_attn_decode: bytes of device memory the split-context
+ * path needs for the given shape (0 when the call runs in a single pass).
+ * Depends on the current device's compute-unit count.  Returns 0 for
+ * unsupported shapes as well; pkv_attn_decode reports those.
+ */
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t max_context_len);
+
+/* Number of context splits pkv_attn_decode uses for this shape (>= 1). */
+int32_t pkv_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t max_context_len);
+
+/*
+ * Decode attention ([P2] section 1: o_n = softmax(q_n K_{0:n}^T / sqrt(d_head))
+ * V_{0:n}; [P1] model.py forward with T = 1; GQA: query head h reads KV head
+ * h / (Hq/Hkv), [P1] q.view(T, n_kv, group, D)).
+ *     out[b][h][:] = sum_p w_p V_b[p][h/G][:],  w = softmax_p(scale * <q[b][h], K_b[p][h/G]>)
+ * over positions p < context_lens[b] read through block_tables[b].
+ * context_lens[b] == 0 gives zeros; a length above max_context_len (or past
+ * the table) gives NaN.  fp32 accumulation, bf16 output.
+ *   out, q        bf16 [B][Hq][D]; must not overlap
+ *   scale         normally 1/sqrt(D)
+ *   max_context_len  host-side upper bound of context_lens (plans the splits)
+ *   workspace     device buffer of at least pkv_decode_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); scratch only, its
+ *                 contents on entry do not matter.
+ */
+int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                    int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal chunked-prefill attention ([P1] model.py forward with T > 1: mask
+ * kpos <= qpos on absolute positions; [P1] "Why chunked prefill": prompt
+ * chunks of up to 512 tokens).  Sequence b owns query rows
+ * cu_q_lens[b] .. cu_q_lens[b+1]-1; they are the last T_b positions of its
+ * context, so row t sits at position context_lens[b] - T_b + t and attends to
+ * keys 0 .. that position, read through block_tables[b] (the chunk's own K/V
+ * must already be appended).  T_b > context_lens[b] makes that sequence's
+ * rows NaN; a sequence whose rows fall outside [0, total_q) or number more
+ * than max_q_len is skipped (its rows are left untouched).
+ *   out, q        bf16 [total_q][Hq][D]; must not overlap
+ *   cu_q_lens     int32 [B+1], nondecreasing, cu_q_lens[0] = 0,
+ *                 cu_q_lens[B] = total_q
+ *   max_q_len     host-side upper bound of T_b
+ */
+int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t total_q, int32_t max_q_len,
+                           int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, void* stream);
+
+/* Thread-local message describing the last non-OK return on this thread. */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,176 @@
+"""Thin Python binding of the C ABI in include/pkv.h (ctypes).
+
+Argument marshalling only: shapes are read off the tensors, pointers and the
+current HIP stream are passed through, the C status code is turned into an
+exception.  Every step of the computation runs in the library's kernels; if
+``libpkv.so`` is missing, loading fails loudly (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_ELAUNCH, PKV_EVALIDATE = 0, -1, -2, -3, -4, -5
+BLOCK_SIZE = 16
+
+_c_int, _c_size, _vp, _f = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+SIGNATURES = {
+    "pkv_slot_mapping": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "pkv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "pkv_decode_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pkv_decode_num_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pkv_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
+    "pkv_attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _f, _vp]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pkv error {code}: {msg}")
+        self.code = code
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpkv.so (built in-tree by ``python -m paged_kv_gqa_pkv_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m paged_kv_gqa_pkv_amd.build` "
+                           "(the library has no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != PKV_OK:
+        msg = load().pkv_last_error()
+        raise PkvError(rc, msg.decode() if msg else "")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: Optional[int] = None) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def pkv_slot_mapping(slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                     cu_new_lens: torch.Tensor, context_lens: torch.Tensor, stream=None) -> None:
+    """slot_mapping[int32 T] <- slots of the appended tokens (see include/pkv.h)."""
+    for t, n in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"),
+                 (cu_new_lens, "cu_new_lens"), (context_lens, "context_lens")):
+        _need(t, torch.int32, n)
+    B, mb = block_tables.shape
+    _check(load().pkv_slot_mapping(_p(slot_mapping), _p(block_tables), _p(cu_new_lens),
+                                   _p(context_lens), B, mb, slot_mapping.numel(), BLOCK_SIZE,
+                                   _stream(stream)))
+
+
+def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+               k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Scatter k_new/v_new [T, Hkv, D] into the pools [num_blocks, 16, Hkv, D]."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(slot_mapping, torch.int32, "slot_mapping", 1)
+    T, Hkv, D = k_new.shape
+    nb = k_cache.shape[0]
+    if v_new.shape != k_new.shape or v_cache.shape != k_cache.shape or \
+            tuple(k_cache.shape[2:]) != (Hkv, D) or slot_mapping.numel() != T:
+        raise ValueError("inconsistent shapes")
+    _check(load().pkv_append(_p(k_new), _p(v_new), _p(slot_mapping), _p(k_cache), _p(v_cache),
+                             T, nb, Hkv, D, k_cache.shape[1], _stream(stream)))
+
+
+def pkv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: int) -> int:
+    return int(load().pkv_decode_workspace_bytes(B, Hq, Hkv, D, max_context_len))
+
+
+def pkv_decode_num_splits(B: int, Hq: int, Hkv: int, D: int, max_context_len: int) -> int:
+    return int(load().pkv_decode_num_splits(B, Hq, Hkv, D, max_context_len))
+
+
+def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                    max_context_len: int, scale: float, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """out[B, Hq, D] <- decode attention of q[B, Hq, D] over the paged pools."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent shapes")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = _p(workspace), workspace.numel() * workspace.element_size()
+    _check(load().pkv_attn_decode(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                  _p(context_lens), B, Hq, Hkv, D, bs, nb, block_tables.shape[1],
+                                  int(max_context_len), float(scale), ws_ptr, ws_bytes,
+                                  _stream(stream)))
+
+
+def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                           k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_q_len: int, max_context_len: int, scale: float,
+                           stream=None) -> None:
+    """out[total_q, Hq, D] <- causal attention of the chunk rows q[total_q, Hq, D]."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    for t, n in ((cu_q_lens, "cu_q_lens"), (context_lens, "context_lens")):
+        _need(t, torch.int32, n, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    total_q, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_cache.shape
+    B = context_lens.numel()
+    if out.shape != q.shape or D2 != D or block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
+        raise ValueError("inconsistent shapes")
+    _check(load().pkv_attn_prefill_chunk(_p(out), _p(q), _p(cu_q_lens), _p(k_cache), _p(v_cache),
+                                         _p(block_tables), _p(context_lens), B, total_q,
+                                         int(max_q_len), Hq, Hkv, D, bs, nb,
+                                         block_tables.shape[1], int(max_context_len),
+                                         float(scale), _stream(stream)))

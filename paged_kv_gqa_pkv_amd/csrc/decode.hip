@@ -1,0 +1,437 @@
+// Decode attention over a paged KV cache, gfx950.
+//
+// What is computed (Module 04 page, section 1: o_n = softmax(q_n K^T /
+// sqrt(d_head)) V over the cached positions; Module 12 page, model.py
+// forward with T = 1, query heads grouped as q.view(T, n_kv, group, D)):
+// for every sequence b and query head h the softmax-weighted sum of the V
+// rows of KV head h / G over positions 0 .. context_lens[b]-1.
+//
+// Decomposition.  One workgroup owns one (sequence b, KV head g, context
+// split) and serves all G = Hq/Hkv query heads of the group from the same
+// loaded K/V rows, so every K/V byte is read from HBM once per step.  The
+// workgroup's 4 waves take disjoint page ranges of the split.  Inside a wave
+// a 16-token page of one head is 16 rows of 256 B: lane l holds rows
+// (l>>3) and (l>>3)+8 and the 16-byte chunks (l&7) and (l&7)+8 of each, so
+// every load instruction moves eight full 128-byte lines.  The K/V rows stay
+// in VGPRs (no LDS staging: the reuse across the G heads happens inside each
+// lane).  Scores use v_dot2_f32_bf16 on the packed bf16 data, an 8-lane DPP
+// butterfly finishes each dot product, and an fp32 online softmax runs per
+// lane group; the lane groups, then the waves (through LDS), are merged at
+// the end with the usual max/rescale rule.  Pages are software-pipelined:
+// the next group of pages is in flight while the current one is reduced.
+//
+// Long contexts with few (sequence, head) pairs are cut into splits of
+// pages_per_split pages (flash-decoding); each split writes its unnormalised
+// (m, l, acc) to the workspace and a second kernel merges the splits in fixed
+// order, so results are run-to-run bit-identical.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kWaves = 4;                    // waves per workgroup
+constexpr int kMaxPagesPerWave = 64;         // one VGPR of page ids per wave
+constexpr float kNegInf = -__builtin_inff();
+
+struct DecodeArgs {
+  uint16_t* out;                 // bf16 [B][Hq][D]
+  const u32x4* q;                // bf16 [B][Hq][D] as 16-byte chunks
+  const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D]
+  const u32x4* v_cache;
+  const int32_t* block_tables;   // [B][max_blocks]
+  const int32_t* ctx_lens;       // [B]
+  float2* ws_ml;                 // [B][Hq][S] (m, l), log2 domain
+  float* ws_acc;                 // [B][Hq][S][D]
+  int B, Hq, Hkv, num_blocks, max_blocks, splits, pages_per_split;
+  float scale_log2;              // scale * log2(e)
+};
+
+// K and V of one page for this lane: [row r0 / r0+8][chunk c / c+8].
+struct PageRegs {
+  u32x4 k[2][2];
+  u32x4 v[2][2];
+};
+
+__device__ __forceinline__ void load_page(PageRegs& r, const DecodeArgs& a, int64_t blk, int g,
+                                          int lane_off) {
+  const int64_t row_stride = (int64_t)a.Hkv * 16;             // chunks per token row
+  const int64_t base = (blk * kPage * a.Hkv + g) * 16;        // chunk 0 of row 0, head g
+  const u32x4* kp = a.k_cache + base;
+  const u32x4* vp = a.v_cache + base;
+  const int o8 = (int)(8 * row_stride);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    r.k[0][h] = __builtin_nontemporal_load(kp + lane_off + 8 * h);
+    r.k[1][h] = __builtin_nontemporal_load(kp + lane_off + o8 + 8 * h);
+    r.v[0][h] = __builtin_nontemporal_load(vp + lane_off + 8 * h);
+    r.v[1][h] = __builtin_nontemporal_load(vp + lane_off + o8 + 8 * h);
+  }
+}
+
+// Online-softmax update with U pages held in registers.  kMask: the single
+// page is the sequence's last, partially filled one; rows >= valid_rows are
+// excluded (score -inf, V forced to 0 so canary data cannot leak).
+template <int G, int U, bool kMask>
+__device__ __forceinline__ void process(const PageRegs (&buf)[U], const uint32_t (&qw)[G][8],
+                                        float (&m)[G], float (&l)[G], float (&acc)[G][16],
+                                        float scale_log2, int r0, int valid_rows) {
+  float s[U][2][G];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf[u].k[rr][h][i]),
+                                                as_bf16x2(qw[j][4 * h + i]), d, false);
+        d = sum8(d) * scale_log2;
+        if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
+        s[u][rr][j] = d;
+      }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float mc = s[0][0][j];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) mc = fmaxf(mc, s[u][rr][j]);
+    const float m_new = fmaxf(m[j], mc);
+    const float mu = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m[j] - mu);
+    m[j] = m_new;
+    l[j] *= alpha;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[j][d] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const float p = fast_exp2(s[u][rr][j] - mu);
+        s[u][rr][j] = p;
+        l[j] += p;
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      float v[16];
+      const bool keep = !kMask || (r0 + 8 * rr < valid_rows);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = keep ? buf[u].v[rr][h][i] : 0u;
+          v[8 * h + 2 * i] = bf16lo(w);
+          v[8 * h + 2 * i + 1] = bf16hi(w);
+        }
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int d = 0; d < 16; ++d) acc[j][d] = __builtin_fmaf(s[u][rr][j], v[d], acc[j][d]);
+    }
+}
+
+// Merge two online-softmax states (m in the log2 domain).
+__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float m2, float l2,
+                                            const float* acc2, int n) {
+  const float M = fmaxf(m, m2);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  const float a = fast_exp2(m - Mu), b = fast_exp2(m2 - Mu);
+  l = l * a + l2 * b;
+  for (int d = 0; d < n; ++d) acc[d] = acc[d] * a + acc2[d] * b;
+  m = M;
+}
+
+template <int G, int U>
+__global__ void __launch_bounds__(kWaves * kWave)
+decode_kernel(const DecodeArgs a) {
+  __shared__ float s_acc[kWaves][G][kD];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ int s_bad[kWaves];
+
+  const int bid = blockIdx.x;                 // ((b * S) + split) * Hkv + g
+  const int g = bid % a.Hkv;
+  const int rest = bid / a.Hkv;
+  const int split = rest % a.splits;
+  const int b = rest / a.splits;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int r0 = lane >> 3, c = lane & 7;
+  const int S = a.splits;
+
+  // A length outside [0, planned maximum] poisons the outputs of the sequence
+  // (the plan covers splits * pages_per_split pages; no read goes past it).
+  const int n = a.ctx_lens[b];
+  const bool bad_len = n < 0 || n > a.max_blocks * kPage ||
+                       (n + kPage - 1) / kPage > a.splits * a.pages_per_split;
+  const int n_pages = bad_len ? 0 : (n + kPage - 1) / kPage;
+  const int p0 = split * a.pages_per_split;
+  const int p1 = min(p0 + a.pages_per_split, n_pages);
+
+  if (p0 >= p1) {
+    // Nothing to read.  A single-pass call still owns the output: zeros for an
+    // empty context, NaN for an invalid length.  Split calls leave it to the
+    // merge kernel, which reads the length itself.
+    if (S == 1) {
+      for (int e = tid; e < G * kD; e += kWaves * kWave) {
+        const int j = e / kD, d = e % kD;
+        a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = bad_len ? 0x7fc0u : 0u;
+      }
+    }
+    return;
+  }
+
+  // This wave's pages: [w0, w1) of the split; full pages first, then the
+  // sequence's last page if it is partial and falls in range.
+  const int np = p1 - p0;
+  const int ppw = (np + kWaves - 1) / kWaves;
+  const int w0 = min(p0 + w * ppw, p1);
+  const int w1 = min(w0 + ppw, p1);
+  const int n_full = n / kPage;
+  const int full_end = min(w1, n_full);
+  const int nfull = max(0, full_end - w0);
+  const bool has_tail = (n % kPage) != 0 && n_full >= w0 && n_full < w1;
+  const int cnt = w1 - w0;                    // <= kMaxPagesPerWave by the plan
+
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  const int my_id = lane < cnt ? bt[w0 + lane] : 0;
+
+  // q for the G heads of this group: the lane's 16 dims as packed bf16 pairs.
+  uint32_t qw[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const u32x4* qp = a.q + ((int64_t)b * a.Hq + g * G + j) * 16;
+    const u32x4 lo = qp[c], hi = qp[c + 8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { qw[j][i] = lo[i]; qw[j][4 + i] = hi[i]; }
+  }
+
+  float m[G], l[G], acc[G][16];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = kNegInf; l[j] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[j][d] = 0.f;
+  }
+
+  const int lane_off = r0 * a.Hkv * 16 + c;
+  int bad = bad_len ? 1 : 0;
+  auto page_id = [&](int j) -> int64_t {
+    const int id = __builtin_amdgcn_readlane(my_id, j);
+    const bool ok = id >= 0 && id < a.num_blocks;
+    bad |= ok ? 0 : 1;
+    return ok ? id : 0;
+  };
+
+  // Full pages, U at a time, two groups in flight.
+  const int ngroups = nfull / U;
+  PageRegs bufA[U], bufB[U];
+  if (ngroups > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_page(bufA[u], a, page_id(u), g, lane_off);
+  }
+  for (int gi = 0; gi < ngroups; gi += 2) {
+    const bool more1 = gi + 1 < ngroups;
+    if (more1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_page(bufB[u], a, page_id((gi + 1) * U + u), g, lane_off);
+    }
+    process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
+    if (more1) {
+      if (gi + 2 < ngroups) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_page(bufA[u], a, page_id((gi + 2) * U + u), g, lane_off);
+      }
+      process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
+    }
+  }
+  // Leftover full pages (fewer than U), one at a time.
+  for (int j = ngroups * U; j < nfull; ++j) {
+    PageRegs one[1];
+    load_page(one[0], a, page_id(j), g, lane_off);
+    process<G, 1, false>(one, qw, m, l, acc, a.scale_log2, r0, kPage);
+  }
+  if (has_tail) {
+    PageRegs one[1];
+    load_page(one[0], a, page_id(n_full - w0), g, lane_off);
+    process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n % kPage);
+  }
+
+  // Merge the 8 lane groups (rows) of the wave: lanes xor 8, 16, 32.
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float t[16];
+    float mo = xor8(m[j]), lo = xor8(l[j]);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) t[d] = xor8(acc[j][d]);
+    merge_state(m[j], l[j], acc[j], mo, lo, t, 16);
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      mo = shfl_xor(m[j], sh); lo = shfl_xor(l[j], sh);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) t[d] = shfl_xor(acc[j][d], sh);
+      merge_state(m[j], l[j], acc[j], mo, lo, t, 16);
+    }
+  }
+
+  // Merge the waves through LDS.
+  if (lane < 8) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        s_acc[w][j][c * 8 + d] = acc[j][d];
+        s_acc[w][j][64 + c * 8 + d] = acc[j][8 + d];
+      }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) { s_m[w][j] = m[j]; s_l[w][j] = l[j]; }
+    s_bad[w] = bad;
+  }
+  __syncthreads();
+
+  int any_bad = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) any_bad |= s_bad[i];
+  for (int e = tid; e < G * kD; e += kWaves * kWave) {
+    const int j = e / kD, d = e % kD;
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][j]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const float f = fast_exp2(s_m[i][j] - Mu);
+      L = __builtin_fmaf(s_l[i][j], f, L);
+      A = __builtin_fmaf(s_acc[i][j][d], f, A);
+    }
+    const int h = g * G + j;
+    if (S == 1) {
+      const float o = any_bad ? __builtin_nanf("") : A / L;
+      a.out[((int64_t)b * a.Hq + h) * kD + d] = (uint16_t)f32_to_bf16_bits(o);
+    } else {
+      const int64_t r = ((int64_t)b * a.Hq + h) * S + split;
+      a.ws_acc[r * kD + d] = any_bad ? __builtin_nanf("") : A;
+      if (d == 0) a.ws_ml[r] = make_float2(M, any_bad ? __builtin_nanf("") : L);
+    }
+  }
+}
+
+// Merge the splits of one (sequence, query head) in fixed split order.
+// One wave; lane owns dims 2*lane and 2*lane+1.
+__global__ void __launch_bounds__(kWave)
+split_merge_kernel(const DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int lane = threadIdx.x;
+  const int n = a.ctx_lens[b];
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.out + (int64_t)bh * kD) + lane;
+  if (n < 0 || n > a.max_blocks * kPage ||
+      (n + kPage - 1) / kPage > a.splits * a.pages_per_split) {
+    *out = 0x7fc07fc0u;
+    return;
+  }
+  if (n == 0) { *out = 0u; return; }
+  const int n_pages = (n + kPage - 1) / kPage;
+  const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;   // <= splits
+  const float2* ml = a.ws_ml + (int64_t)bh * a.splits;
+  const float* acc = a.ws_acc + (int64_t)bh * a.splits * kD + 2 * lane;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, A0 = 0.f, A1 = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float2 e = ml[s];
+    const float f = fast_exp2(e.x - Mu);
+    L = __builtin_fmaf(e.y, f, L);
+    const float2 v = *reinterpret_cast<const float2*>(acc + (int64_t)s * kD);
+    A0 = __builtin_fmaf(v.x, f, A0);
+    A1 = __builtin_fmaf(v.y, f, A1);
+  }
+  *out = pack_bf16x2(A0 / L, A1 / L);
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)(a.B * a.Hkv * a.splits);
+  hipLaunchKernelGGL((decode_kernel<G, 2>), dim3(grid), dim3(kWaves * kWave), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// Split planner.  Work units are (sequence, KV head) pairs; a workgroup of 4
+// waves streams one split of a unit.  The planner aims for about 4 workgroups
+// per compute unit so that enough page loads are in flight to cover HBM
+// latency, keeps splits at least 8 pages long (2 per wave) so per-split
+// overhead stays small, and at most 256 pages (64 per wave: one VGPR of page
+// ids).  Only host-known sizes enter, so no device->host sync is needed.
+DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus) {
+  DecodePlan p{};
+  const int max_pages = max(1, (max_context_len + kPage - 1) / kPage);
+  const int units = max(1, B * Hkv);
+  const int target_wgs = 4 * max(1, num_cus);
+  int splits = (target_wgs + units - 1) / units;
+  const int min_pps = 2 * kWaves;
+  const int max_pps = kMaxPagesPerWave * kWaves;
+  int pps = (max_pages + splits - 1) / splits;
+  if (pps < min_pps) pps = min_pps;
+  if (pps > max_pps) pps = max_pps;
+  splits = (max_pages + pps - 1) / pps;
+  if (splits < 1) splits = 1;
+  p.splits = splits;
+  p.pages_per_split = pps;
+  if (splits > 1) {
+    p.ws_ml_bytes = align256((size_t)B * Hq * splits * sizeof(float2));
+    p.ws_acc_bytes = align256((size_t)B * Hq * splits * kD * sizeof(float));
+  }
+  p.ws_bytes = p.ws_ml_bytes + p.ws_acc_bytes;
+  return p;
+}
+
+hipError_t launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
+                         int Hkv, int num_blocks, int max_blocks, float scale,
+                         const DecodePlan& plan, void* workspace, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  DecodeArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const u32x4*>(q);
+  a.k_cache = static_cast<const u32x4*>(k_cache);
+  a.v_cache = static_cast<const u32x4*>(v_cache);
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.ws_ml = plan.splits > 1 ? static_cast<float2*>(workspace) : nullptr;
+  a.ws_acc = plan.splits > 1
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_bytes)
+                 : nullptr;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
+  a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  switch (Hq / Hkv) {
+    case 1: return launch_g<1>(a, stream);
+    case 2: return launch_g<2>(a, stream);
+    case 4: return launch_g<4>(a, stream);
+    case 8: return launch_g<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

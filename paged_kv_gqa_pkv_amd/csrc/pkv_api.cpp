@@ -1,0 +1,272 @@
+// C ABI of the paged GQA attention library: argument checks, split planning,
+// launches, thread-local error strings.  No allocation, no device->host sync
+// (except under PKV_VALIDATE=1, a debug mode that inspects index contents).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool validate_mode() {
+  static const bool on = [] {
+    const char* v = std::getenv("PKV_VALIDATE");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+// Compute units of the current device, cached per device id.
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+int check_geometry(int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size) {
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "head counts, head_dim and block_size must be positive");
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "block_size %d unsupported (pages hold 16 tokens)", block_size);
+  if (D != PKV_HEAD_DIM) return fail(PKV_EUNSUPPORTED, "head_dim %d unsupported (only 128)", D);
+  if (Hq % Hkv) return fail(PKV_EUNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_EUNSUPPORTED, "group size Hq/Hkv=%d unsupported (1, 2, 4 or 8)", G);
+  return PKV_OK;
+}
+
+template <typename T>
+bool to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipStreamSynchronize(stream) != hipSuccess) return false;
+  return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// PKV_VALIDATE: block tables and lengths of a decode/prefill call.
+int validate_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
+                    hipStream_t stream) {
+  std::vector<int32_t> ctx, bt;
+  if (!to_host(ctx, context_lens, (size_t)B, stream) ||
+      !to_host(bt, block_tables, (size_t)B * max_blocks, stream))
+    return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of index arrays failed");
+  for (int b = 0; b < B; ++b) {
+    const int n = ctx[b];
+    if (n < 0 || n > max_context_len)
+      return fail(PKV_EVALIDATE, "context_lens[%d]=%d outside [0, max_context_len=%d]", b, n,
+                  max_context_len);
+    if (n > max_blocks * PKV_BLOCK_SIZE)
+      return fail(PKV_EVALIDATE, "context_lens[%d]=%d exceeds the table (%d pages)", b, n,
+                  max_blocks);
+    for (int i = 0; i < (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE; ++i) {
+      const int blk = bt[(size_t)b * max_blocks + i];
+      if (blk < 0 || blk >= num_blocks)
+        return fail(PKV_EVALIDATE, "block_tables[%d][%d]=%d outside [0, %d)", b, i, blk,
+                    num_blocks);
+    }
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* cu_new_lens, const int32_t* context_lens, int32_t B,
+                     int32_t max_blocks_per_seq, int32_t total_new, int32_t block_size,
+                     void* stream) {
+  if (B < 0 || total_new < 0 || max_blocks_per_seq < 0)
+    return fail(PKV_EINVAL, "negative size");
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "block_size %d unsupported (pages hold 16 tokens)", block_size);
+  if (total_new == 0) return PKV_OK;
+  if (B == 0) return fail(PKV_EINVAL, "total_new=%d tokens but no sequences", total_new);
+  if (!slot_mapping || !block_tables || !cu_new_lens || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> cu, ctx;
+    if (!to_host(cu, cu_new_lens, (size_t)B + 1, s) || !to_host(ctx, context_lens, (size_t)B, s))
+      return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of index arrays failed");
+    if (cu[0] != 0 || cu[B] != total_new)
+      return fail(PKV_EVALIDATE, "cu_new_lens must start at 0 and end at total_new=%d", total_new);
+    for (int b = 0; b < B; ++b) {
+      if (cu[b + 1] < cu[b]) return fail(PKV_EVALIDATE, "cu_new_lens decreases at %d", b);
+      if (cu[b + 1] - cu[b] > ctx[b])
+        return fail(PKV_EVALIDATE, "sequence %d appends %d tokens but its context is %d", b,
+                    cu[b + 1] - cu[b], ctx[b]);
+      if (ctx[b] > max_blocks_per_seq * PKV_BLOCK_SIZE)
+        return fail(PKV_EVALIDATE, "context_lens[%d]=%d exceeds the table", b, ctx[b]);
+    }
+  }
+  return launch_status(pkv::launch_slot_mapping(slot_mapping, block_tables, cu_new_lens,
+                                                context_lens, B, max_blocks_per_seq, total_new,
+                                                s),
+                       "pkv_slot_mapping");
+}
+
+int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
+               void* v_cache, int32_t T, int32_t num_blocks, int32_t Hkv, int32_t D,
+               int32_t block_size, void* stream) {
+  if (T < 0 || num_blocks < 0) return fail(PKV_EINVAL, "negative size");
+  int rc = check_geometry(Hkv, Hkv, D, block_size);
+  if (rc) return rc;
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (k_cache == v_cache) return fail(PKV_EINVAL, "k_cache and v_cache must differ");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> slots;
+    if (!to_host(slots, slot_mapping, (size_t)T, s))
+      return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of slot_mapping failed");
+    std::unordered_set<int32_t> seen;
+    for (int t = 0; t < T; ++t) {
+      const int32_t v = slots[t];
+      if (v < 0) continue;
+      if ((int64_t)v >= (int64_t)num_blocks * PKV_BLOCK_SIZE)
+        return fail(PKV_EVALIDATE, "slot_mapping[%d]=%d outside a pool of %d pages", t, v,
+                    num_blocks);
+      if (!seen.insert(v).second)
+        return fail(PKV_EVALIDATE, "slot %d appears twice in slot_mapping", v);
+    }
+  }
+  return launch_status(
+      pkv::launch_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, num_blocks, Hkv, D, s),
+      "pkv_append");
+}
+
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t max_context_len) {
+  if (B <= 0 || max_context_len < 0 || check_geometry(Hq, Hkv, D, PKV_BLOCK_SIZE) != PKV_OK)
+    return 0;
+  return pkv::plan_decode(B, Hq, Hkv, max_context_len, device_cus()).ws_bytes;
+}
+
+int32_t pkv_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t max_context_len) {
+  if (B <= 0 || max_context_len < 0 || check_geometry(Hq, Hkv, D, PKV_BLOCK_SIZE) != PKV_OK)
+    return 1;
+  return pkv::plan_decode(B, Hq, Hkv, max_context_len, device_cus()).splits;
+}
+
+int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+    return fail(PKV_EINVAL, "negative size");
+  int rc = check_geometry(Hq, Hkv, D, block_size);
+  if (rc) return rc;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (out == q) return fail(PKV_EINVAL, "out and q must not overlap");
+  if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
+                max_context_len, max_blocks_per_seq);
+  if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
+  const pkv::DecodePlan plan = pkv::plan_decode(B, Hq, Hkv, max_context_len, device_cus());
+  if (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace))
+    return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.ws_bytes,
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
+                         max_context_len, s);
+    if (rc) return rc;
+  }
+  return launch_status(pkv::launch_decode(out, q, k_cache, v_cache, block_tables, context_lens, B,
+                                          Hq, Hkv, num_blocks, max_blocks_per_seq, scale, plan,
+                                          workspace, s),
+                       "pkv_attn_decode");
+}
+
+int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t total_q,
+                           int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, void* stream) {
+  if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
+      max_context_len < 0)
+    return fail(PKV_EINVAL, "negative size");
+  int rc = check_geometry(Hq, Hkv, D, block_size);
+  if (rc) return rc;
+  if (B == 0 || total_q == 0) return PKV_OK;
+  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (out == q) return fail(PKV_EINVAL, "out and q must not overlap");
+  if (max_q_len > total_q) return fail(PKV_EINVAL, "max_q_len=%d > total_q=%d", max_q_len, total_q);
+  if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
+                max_context_len, max_blocks_per_seq);
+  if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> cu, ctx;
+    if (!to_host(cu, cu_q_lens, (size_t)B + 1, s) || !to_host(ctx, context_lens, (size_t)B, s))
+      return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of index arrays failed");
+    if (cu[0] != 0 || cu[B] != total_q)
+      return fail(PKV_EVALIDATE, "cu_q_lens must start at 0 and end at total_q=%d", total_q);
+    for (int b = 0; b < B; ++b) {
+      const int T = cu[b + 1] - cu[b];
+      if (T < 0 || T > max_q_len)
+        return fail(PKV_EVALIDATE, "sequence %d has %d query rows (max_q_len=%d)", b, T,
+                    max_q_len);
+      if (T > ctx[b])
+        return fail(PKV_EVALIDATE, "sequence %d has %d query rows but context %d", b, T, ctx[b]);
+    }
+    rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
+                         max_context_len, s);
+    if (rc) return rc;
+  }
+  return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables,
+                                           context_lens, B, total_q, max_q_len, Hq, Hkv,
+                                           num_blocks, max_blocks_per_seq, scale, s),
+                       "pkv_attn_prefill_chunk");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels (wave64, CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kPage = 16;     // tokens per page
+constexpr int kD = 128;       // head dim
+constexpr int kWave = 64;     // CDNA wavefront
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 pair packed in a u32 -> two floats (a bf16 value is the high half of
+// the float with the same value, so these are exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// DPP lane moves inside a row of 16 lanes (bound_ctrl: all lanes valid).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               kCtrl, 0xf, 0xf, true));
+}
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]  (lane ^ 1)
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]  (lane ^ 2)
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i within 8
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8 (lane ^ 8 within a row of 16)
+
+// Sum over aligned groups of 8 lanes; every lane of the group gets the sum.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f<kDppQuadSwap1>(x);
+  x += dpp_f<kDppQuadSwap2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x;
+}
+
+// Cross-lane xor shuffles for the 8-, 16- and 32-lane distances.
+__device__ __forceinline__ float xor8(float x) { return dpp_f<kDppRowRor8>(x); }
+__device__ __forceinline__ float shfl_xor(float x, int m) {
+  int src = (int)(threadIdx.x & 63) ^ m;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pkv

@@ -1,0 +1,40 @@
+// Host-side launchers of the gfx950 kernels (internal; the C ABI sits above).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_slot_mapping(int32_t* slots, const int32_t* block_tables, const int32_t* cu_new,
+                               const int32_t* ctx_lens, int B, int max_blocks, int total_new,
+                               hipStream_t stream);
+
+hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* slots,
+                         void* k_cache, void* v_cache, int T, int num_blocks, int Hkv, int D,
+                         hipStream_t stream);
+
+// Split plan of a decode call: S splits of pages_per_split pages each.
+struct DecodePlan {
+  int splits;
+  int pages_per_split;
+  size_t ws_ml_bytes;    // float2 (m, l) [B][Hq][S]
+  size_t ws_acc_bytes;   // float [B][Hq][S][D]
+  size_t ws_bytes;       // total, 0 for a single pass
+};
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus);
+
+hipError_t launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
+                         int Hkv, int num_blocks, int max_blocks, float scale,
+                         const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_tables,
+                          const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
+                          int Hkv, int num_blocks, int max_blocks, float scale,
+                          hipStream_t stream);
+
+}  // namespace pkv

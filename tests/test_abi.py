@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/pkv.h declares, and rejects bad arguments on the host (these paths
+return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_gqa_pkv_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.fail("libpkv.so is not built (run python -m paged_kv_gqa_pkv_amd.build)")
+    return bd.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"pkv_append", "pkv_attn_decode", "pkv_attn_prefill_chunk", "pkv_slot_mapping",
+            "pkv_decode_workspace_bytes", "pkv_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in bd.SIGNATURES, f"binding lacks {n}"
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.pkv_version()
+
+
+NULL = None
+
+
+def test_append_rejects_bad_arguments(lib):
+    # block size other than 16
+    assert lib.pkv_append(1, 1, 1, 1, 2, 4, 8, 8, 128, 8, NULL) == bd.PKV_EUNSUPPORTED
+    # head_dim other than 128
+    assert lib.pkv_append(1, 1, 1, 1, 2, 4, 8, 8, 64, 16, NULL) == bd.PKV_EUNSUPPORTED
+    assert b"head_dim" in lib.pkv_last_error()
+    # null pointers with tokens to write
+    assert lib.pkv_append(NULL, 1, 1, 1, 2, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    # same pool for K and V
+    assert lib.pkv_append(1, 1, 1, 5, 5, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    # negative sizes
+    assert lib.pkv_append(1, 1, 1, 1, 2, -1, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    # nothing to do is fine and launches nothing
+    assert lib.pkv_append(NULL, NULL, NULL, NULL, NULL, 0, 8, 8, 128, 16, NULL) == bd.PKV_OK
+
+
+def test_slot_mapping_rejects_bad_arguments(lib):
+    assert lib.pkv_slot_mapping(1, 1, 1, 1, 2, 4, 3, 8, NULL) == bd.PKV_EUNSUPPORTED
+    assert lib.pkv_slot_mapping(NULL, 1, 1, 1, 2, 4, 3, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_slot_mapping(1, 1, 1, 1, 0, 4, 3, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_slot_mapping(1, 1, 1, 1, -2, 4, 3, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_slot_mapping(NULL, NULL, NULL, NULL, 2, 4, 0, 16, NULL) == bd.PKV_OK
+
+
+def _decode(lib, out=1, q=2, B=2, Hq=16, Hkv=8, D=128, bs=16, nb=32, mb=4, mcl=64, scale=0.088):
+    return lib.pkv_attn_decode(out, q, 3, 4, 5, 6, B, Hq, Hkv, D, bs, nb, mb, mcl, scale,
+                               NULL, 0, NULL)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, Hq=12, Hkv=8) == bd.PKV_EUNSUPPORTED       # Hq % Hkv
+    assert _decode(lib, Hq=48, Hkv=16) == bd.PKV_EUNSUPPORTED      # group 3
+    assert _decode(lib, Hq=32, Hkv=2) == bd.PKV_EUNSUPPORTED       # group 16
+    assert _decode(lib, D=64) == bd.PKV_EUNSUPPORTED
+    assert _decode(lib, bs=32) == bd.PKV_EUNSUPPORTED
+    assert _decode(lib, out=NULL) == bd.PKV_EINVAL
+    assert _decode(lib, out=7, q=7) == bd.PKV_EINVAL                # aliasing
+    assert _decode(lib, mcl=65, mb=4) == bd.PKV_EINVAL              # beyond the table
+    assert _decode(lib, B=-1) == bd.PKV_EINVAL
+    assert _decode(lib, Hkv=0) == bd.PKV_EINVAL
+    assert _decode(lib, scale=float("nan")) == bd.PKV_EINVAL
+    assert _decode(lib, B=0, out=NULL) == bd.PKV_OK
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    def call(out=1, q=2, B=1, total_q=8, mq=8, Hq=16, Hkv=8, D=128, bs=16, mb=4, mcl=64):
+        return lib.pkv_attn_prefill_chunk(out, q, 3, 4, 5, 6, 7, B, total_q, mq, Hq, Hkv, D, bs,
+                                          32, mb, mcl, 0.088, NULL)
+    assert call(D=256) == bd.PKV_EUNSUPPORTED
+    assert call(Hq=10, Hkv=4) == bd.PKV_EUNSUPPORTED
+    assert call(q=NULL) == bd.PKV_EINVAL
+    assert call(mq=9) == bd.PKV_EINVAL                               # max_q_len > total_q
+    assert call(mcl=100, mb=4) == bd.PKV_EINVAL
+    assert call(total_q=0, out=NULL) == bd.PKV_OK
+
+
+def test_header_documents_each_entry_point():
+    """Each declaration carries a comment citing the passage it implements (or
+    stating what it is for)."""
+    src = open(HEADER).read()
+    for name in declared_functions():
+        m = re.search(r"^(?:const\s+)?\w+\s*\*?\s*" + name + r"\s*\(", src, flags=re.M)
+        assert m, name
+        before = src[:m.start()].rstrip()
+        assert before.endswith("*/"), f"{name} has no comment right above its declaration"

@@ -1,0 +1,298 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Acceptance: slot mapping and append are bit-exact over the whole pool
+(shared prefix pages and canary pages included); attention outputs from
+bf16 inputs with fp32 accumulation are within max abs 2e-2 and mean abs
+2e-3 of the oracle run on the same bf16 inputs, and finite (the NaN
+canaries in unwritten slots and unused pages would poison any stray read).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_oracle as O
+from paged_kv_gqa_pkv_amd import binding as bd
+from paged_kv_gqa_pkv_amd import step as ST
+from paged_kv_gqa_pkv_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return O.bf16_to_f64(u16(t))
+
+
+def assert_close(got: torch.Tensor, want: np.ndarray, what: str):
+    g = as_f64(got)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
+    err = np.abs(g - want)
+    print(f"{what}: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (what, err.max(), err.mean())
+
+
+def oracle_step(w, t, d):
+    """Slot mapping, append, prefill and decode on the CPU for one layer."""
+    bt = t.block_tables.numpy().tolist()
+    ctx = t.context_lens.numpy().tolist()
+    slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
+    kc, vc = O.append_ref(u16(d.k_cache), u16(d.v_cache), u16(d.k_new), u16(d.v_new), slots)
+    scale = O.default_scale(w.D)
+    npre = len(w.prefill_seqs)
+    dec = pre = None
+    if w.decode_seqs:
+        dec = O.decode_ref(u16(d.q_decode), kc, vc, bt[npre:], ctx[npre:], scale)
+    if w.prefill_seqs:
+        pre = O.prefill_ref(u16(d.q_prefill), S.prefill_cu(w).numpy().tolist(), kc, vc,
+                            bt[:npre], ctx[:npre], scale)
+    return slots, kc, vc, dec, pre
+
+
+def gpu_step(w, t, d):
+    plan = ST.plan_step(w, t)
+    dev = {k: getattr(d, k).cuda() if getattr(d, k) is not None else None
+           for k in ("k_cache", "v_cache", "k_new", "v_new", "q_decode", "q_prefill")}
+    out_dec = torch.empty_like(dev["q_decode"]) if w.decode_seqs else None
+    out_pre = torch.empty_like(dev["q_prefill"]) if w.prefill_seqs else None
+    ST.slot_mapping(plan)
+    ST.layer(plan, dev["k_cache"], dev["v_cache"], dev["k_new"], dev["v_new"],
+             dev["q_decode"], out_dec, dev["q_prefill"], out_pre)
+    torch.cuda.synchronize()
+    return plan, dev, out_dec, out_pre
+
+
+def check_workload(w, layer=0):
+    print(f"[parity] {w.name} layer {layer}: {w.description}", flush=True)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, layer)
+    plan, dev, out_dec, out_pre = gpu_step(w, t, d)
+    slots, kc, vc, dec, pre = oracle_step(w, t, d)
+    assert plan.slot_mapping.cpu().numpy().tolist() == slots, "slot mapping differs"
+    assert np.array_equal(u16(dev["k_cache"]), kc), "K pool after append differs"
+    assert np.array_equal(u16(dev["v_cache"]), vc), "V pool after append differs"
+    if dec is not None:
+        assert_close(out_dec, dec, f"{w.name} decode")
+    if pre is not None:
+        assert_close(out_pre, pre, f"{w.name} prefill")
+    return plan, dev, out_dec, out_pre
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_decode_configs(name):
+    check_workload(S.workload(name))
+
+
+def test_c3_another_layer_and_shared_pages_untouched():
+    w = S.workload("c3")
+    plan, dev, _, _ = check_workload(w, layer=27)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 27)
+    shared = t.block_tables[0, :13].long()
+    assert torch.equal(dev["k_cache"].cpu()[shared].view(torch.int16),
+                       d.k_cache[shared].view(torch.int16))
+
+
+@pytest.mark.parametrize("chunk_step", range(6))
+def test_mixed_step_configs(chunk_step):
+    check_workload(S.workload("c5", chunk_step))
+
+
+def _seqs_decode(ctxs):
+    return [S.SeqSpec(c - 1, 1, False) for c in ctxs]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_group_sizes_and_ragged_lengths(G):
+    Hkv = 2
+    ctxs = [1, 15, 16, 17, 31, 33, 200, 515]
+    w = S.custom_workload(f"ragged_G{G}", _seqs_decode(ctxs), Hq=Hkv * G, Hkv=Hkv, D=128,
+                          num_blocks=96, base_seed=70 + G)
+    check_workload(w)
+
+
+def test_decode_long_context_many_splits():
+    w = S.custom_workload("long_small_batch", _seqs_decode([5000, 777, 3]), Hq=32, Hkv=8, D=128,
+                          num_blocks=400, base_seed=80)
+    assert bd.pkv_decode_num_splits(3, 32, 8, 128, 5000) > 1
+    check_workload(w)
+
+
+def test_decode_single_pass_large_batch():
+    ctxs = [int(x) for x in np.random.default_rng(81).integers(1, 90, size=160)]
+    w = S.custom_workload("wide_batch", _seqs_decode(ctxs), Hq=16, Hkv=8, D=128,
+                          num_blocks=1200, base_seed=81)
+    assert bd.pkv_decode_num_splits(160, 16, 8, 128, max(ctxs)) == 1
+    check_workload(w)
+
+
+def test_prefill_varlen_batch():
+    seqs = [S.SeqSpec(0, 37, True), S.SeqSpec(100, 1, True), S.SeqSpec(60, 200, True),
+            S.SeqSpec(16, 16, True), S.SeqSpec(3, 1, False), S.SeqSpec(90, 1, False)]
+    for G, Hkv in ((1, 4), (2, 4), (4, 2), (8, 1)):
+        w = S.custom_workload(f"varlen_G{G}", seqs, Hq=Hkv * G, Hkv=Hkv, D=128, num_blocks=64,
+                              base_seed=90 + G)
+        check_workload(w)
+
+
+def test_ctx1_is_exact_value_row():
+    w = S.custom_workload("ctx1", _seqs_decode([1, 1, 1]), Hq=16, Hkv=8, D=128, num_blocks=8,
+                          base_seed=95)
+    plan, dev, out_dec, _ = check_workload(w)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0)
+    want = d.v_new.repeat_interleave(2, dim=1)          # head h reads KV head h // 2
+    assert torch.equal(out_dec.cpu().view(torch.int16), want.view(torch.int16))
+
+
+def test_context_zero_gives_zeros():
+    B, Hq, Hkv, D = 3, 16, 8, 128
+    k = S.randn_bf16((8, 16, Hkv, D), 1).cuda()
+    v = S.randn_bf16((8, 16, Hkv, D), 2).cuda()
+    q = S.randn_bf16((B, Hq, D), 3).cuda()
+    bt = torch.tensor([[0, 1], [2, 3], [4, 5]], dtype=torch.int32, device="cuda")
+    ctx = torch.tensor([0, 5, 0], dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, 7.0)
+    bd.pkv_attn_decode(out, q, k, v, bt, ctx, 32, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    want = O.decode_ref(u16(q[1:2]), u16(k), u16(v), [[2, 3]], [5], 128 ** -0.5)
+    assert_close(out[1:2], want, "ctx0 neighbour")
+
+
+def test_bulk_append_bit_exact():
+    slots, k_new, v_new, pk, pv = S.bulk_append_inputs(65536, 4096, 8, 128, seed=123)
+    dk, dv = pk.cuda(), pv.cuda()
+    bd.pkv_append(k_new.cuda(), v_new.cuda(), slots.cuda(), dk, dv)
+    torch.cuda.synchronize()
+    kc, vc = O.append_ref(u16(pk), u16(pv), u16(k_new), u16(v_new), slots.numpy().tolist())
+    assert np.array_equal(u16(dk), kc) and np.array_equal(u16(dv), vc)
+
+
+def test_append_skips_negative_slots_and_keeps_bits():
+    Hkv, D = 8, 128
+    pk = S.randn_bf16((4, 16, Hkv, D), 5)
+    pv = S.randn_bf16((4, 16, Hkv, D), 6)
+    k_new = torch.full((3, Hkv, D), 0x7FC1, dtype=torch.int16).view(torch.bfloat16)  # NaN payload
+    k_new.view(torch.int16)[1] = -32768                                              # -0.0
+    v_new = S.randn_bf16((3, Hkv, D), 7)
+    slots = torch.tensor([5, -1, 63], dtype=torch.int32)
+    dk, dv = pk.cuda(), pv.cuda()
+    bd.pkv_append(k_new.cuda(), v_new.cuda(), slots.cuda(), dk, dv)
+    torch.cuda.synchronize()
+    kc, vc = O.append_ref(u16(pk), u16(pv), u16(k_new), u16(v_new), [5, -1, 63])
+    assert np.array_equal(u16(dk), kc) and np.array_equal(u16(dv), vc)
+
+
+def test_determinism_and_placement_invariance():
+    """Repeated runs are bit-identical, and relabelling the physical pages (the
+    tables mapped through the same permutation) gives bit-identical outputs:
+    the kernels walk logical positions in the same order whatever the
+    placement."""
+    w = S.workload("c2")
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0)
+    _, _, o1, _ = gpu_step(w, t, d)
+    _, _, o2, _ = gpu_step(w, t, d)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    perm = torch.randperm(w.num_blocks, generator=torch.Generator().manual_seed(9))
+    t2 = S.Tables(torch.where(t.block_tables >= 0, perm[t.block_tables.long().clamp(min=0)].int(),
+                              t.block_tables), t.context_lens, t.cu_new, t.pre_lens)
+    kc = torch.empty_like(d.k_cache); vc = torch.empty_like(d.v_cache)
+    kc[perm] = d.k_cache; vc[perm] = d.v_cache
+    d2 = S.LayerData(kc, vc, d.k_new, d.v_new, d.q_decode, d.q_prefill)
+    _, _, o3, _ = gpu_step(w, t2, d2)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_invalid_indices_poison_outputs_without_faulting():
+    """A context beyond the table or a block id outside the pool makes the
+    affected outputs NaN; the kernels clamp the address and never read
+    outside the pool.  Other sequences are unaffected."""
+    Hq, Hkv, D = 16, 8, 128
+    k = S.randn_bf16((8, 16, Hkv, D), 11).cuda()
+    v = S.randn_bf16((8, 16, Hkv, D), 12).cuda()
+    q = S.randn_bf16((3, Hq, D), 13).cuda()
+    bt = torch.tensor([[0, 1], [2, 999], [3, 4]], dtype=torch.int32, device="cuda")
+    ctx = torch.tensor([20, 20, 20], dtype=torch.int32, device="cuda")
+    out = torch.zeros_like(q)
+    bd.pkv_attn_decode(out, q, k, v, bt, ctx, 32, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all()
+    assert torch.isfinite(out[0].float()).all() and torch.isfinite(out[2].float()).all()
+    ctx_bad = torch.tensor([20, 40, 20], dtype=torch.int32, device="cuda")   # 40 > 2 pages
+    bt_ok = torch.tensor([[0, 1], [2, 5], [3, 4]], dtype=torch.int32, device="cuda")
+    bd.pkv_attn_decode(out, q, k, v, bt_ok, ctx_bad, 32, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1].float()).all() and torch.isfinite(out[0].float()).all()
+
+
+def test_workspace_too_small_is_rejected():
+    w = S.workload("c2")
+    need = bd.pkv_decode_workspace_bytes(8, 16, 8, 128, 1024)
+    assert need > 0
+    q = torch.zeros((8, 16, 128), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((w.num_blocks, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((8, 64), dtype=torch.int32, device="cuda")
+    ctx = torch.ones(8, dtype=torch.int32, device="cuda")
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bd.PkvError) as e:
+        bd.pkv_attn_decode(torch.empty_like(q), q, pool, pool.clone(), bt, ctx, 1024,
+                           0.088, workspace=ws)
+    assert e.value.code == bd.PKV_EWORKSPACE
+
+
+def _sampled_full_size(name, samples):
+    """Full-size configuration, one layer, generated on the device; the oracle
+    recomputes sampled (sequence, head) outputs one by one."""
+    w = S.workload(name)
+    print(f"[parity] {w.name} full size, sampled: {w.description}", flush=True)
+    t = S.make_tables(w)
+    fill = S.page_fill_counts(w, t)
+    d = S.make_layer(w, t, 0, device="cuda", fill=fill)
+    k_pre, v_pre = u16(d.k_cache), u16(d.v_cache)
+    plan = ST.plan_step(w, t)
+    out = torch.empty_like(d.q_decode)
+    ST.slot_mapping(plan)
+    ST.layer(plan, d.k_cache, d.v_cache, d.k_new, d.v_new, d.q_decode, out)
+    torch.cuda.synchronize()
+    bt = t.block_tables.numpy().tolist()
+    ctx = t.context_lens.numpy().tolist()
+    slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
+    assert plan.slot_mapping.cpu().numpy().tolist() == slots
+    kn, vn = u16(d.k_new), u16(d.v_new)
+    # the oracle's append, restricted to the pages the sampled sequences read
+    kc, vc = O.append_ref(k_pre, v_pre, kn, vn, slots)
+    got = as_f64(out)
+    qh = u16(d.q_decode)
+    errs = []
+    for b, h in samples:
+        g = O.kv_head_of(h, w.Hq, w.Hkv)
+        n = ctx[b]
+        K = O.bf16_to_f64(O.gather_ref(kc, bt[b], n))[:, g, :]
+        V = O.bf16_to_f64(O.gather_ref(vc, bt[b], n))[:, g, :]
+        want = O.attend_one(O.bf16_to_f64(qh[b, h]), K, V, O.default_scale(w.D))
+        errs.append(np.abs(got[b, h] - want))
+    err = np.concatenate(errs)
+    print(f"{name} sampled: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+    # appended rows landed bit-exactly
+    dk = u16(d.k_cache)
+    for tkn, s in enumerate(slots):
+        assert np.array_equal(dk[s // 16, s % 16], kn[tkn])
+
+
+def test_full_size_c4a_sampled():
+    _sampled_full_size("c4a", [(0, 0), (7, 31), (33, 12), (63, 5), (63, 30)])
+
+
+def test_full_size_c4b_sampled():
+    _sampled_full_size("c4b", [(0, 0), (5, 17), (12, 31)])
