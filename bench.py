@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic inputs:
+slot mapping of the step's new tokens, then per layer the KV append and the
+attention launches (prefill chunk and/or decode, with the split merge).
+Inputs are resident in HBM before timing starts.
+
+Default workload: single-layer decode, Qwen3-0.6B attention shapes, batch 8,
+contexts ~ U[1,1024] (post-append), 512-page pool.  Other configurations:
+--workload c1|c3|c4a|c4b|c5.  Working sets under 1 GiB are rotated over
+enough independent copies (>= 512 MiB in total) that the 256 MB Infinity
+Cache cannot serve them.
+
+Prints one JSON line (rank 0).  value = algorithmic HBM bytes of the step /
+step time (GB/s); the roofline object reports the dominant kernel (the decode
+attention call, measured with HIP events on the launch stream), the
+cpu_baseline object the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) + decode tokens/s/GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="c2",
+                   choices=["c1", "c2", "c3", "c4a", "c4b", "c5"])
+    p.add_argument("--rotate-mib", type=int, default=512,
+                   help="total bytes of rotated input copies for small working sets")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    p.add_argument("--no-events", action="store_true",
+                   help="time steps only (no per-launch events), e.g. under a profiler")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of a step (what the method must move / compute)
+# ---------------------------------------------------------------------------
+
+def decode_bytes(w, t, rows):
+    """K/V of every token read once (pages shared by several tables counted
+    once), q in and out, the table entries and lengths."""
+    Hkv, D, Hq = w.Hkv, w.D, w.Hq
+    seen = {}
+    table_bytes = 0
+    for i in rows:
+        n = int(t.context_lens[i])
+        npg = (n + 15) // 16
+        table_bytes += 4 * npg + 4
+        for j in range(npg):
+            page = int(t.block_tables[i, j])
+            seen[page] = max(seen.get(page, 0), min(16, n - 16 * j))
+    kv_tokens = sum(seen.values())
+    return kv_tokens * 2 * Hkv * D * 2 + len(rows) * 2 * Hq * D * 2 + table_bytes
+
+
+def append_bytes(w, t):
+    T = int(t.cu_new[-1])
+    return T * (2 * 2 * w.Hkv * w.D * 2 + 4)
+
+
+def slot_bytes(w, t):
+    T = int(t.cu_new[-1])
+    return T * 12 + 4 * (len(w.seqs) * 2 + 1)
+
+
+def prefill_work(w, t):
+    """(bytes, causal FLOPs) of the prefill chunks: K/V of keys 0..o+T-1 once,
+    q and out; FLOPs over visible (query, key) pairs only."""
+    by, fl = 0, 0
+    for i in w.prefill_seqs:
+        s = w.seqs[i]
+        o, T, n = s.pre_len, s.new_len, s.ctx
+        by += n * 2 * w.Hkv * w.D * 2 + 2 * T * w.Hq * w.D * 2 + 4 * ((n + 15) // 16)
+        fl += 4 * w.D * w.Hq * (T * o + T * (T + 1) // 2)
+    return by, fl
+
+
+# ---------------------------------------------------------------------------
+
+def build_inputs(name, rotate_mib, device):
+    import torch
+    from paged_kv_gqa_pkv_amd import step as ST
+    from paged_kv_gqa_pkv_amd import synth as S
+
+    subs = []
+    if name == "c5":
+        base_w = S.workload("c5", 5)
+        base_t = S.make_tables(base_w)
+        for s in range(6):
+            w = S.workload("c5", s)
+            p = w.seqs[0]
+            ctx = base_t.context_lens.clone(); ctx[0] = p.ctx
+            new = torch.tensor([0, p.new_len] + [1] * len(w.decode_seqs), dtype=torch.int64)
+            t = S.Tables(base_t.block_tables, ctx, torch.cumsum(new, 0).to(torch.int32),
+                         torch.tensor([q.pre_len for q in w.seqs], dtype=torch.int32))
+            subs.append((w, t))
+        w0, t0 = base_w, base_t
+    else:
+        w0 = S.workload(name)
+        t0 = S.make_tables(w0)
+        subs.append((w0, t0))
+    pool_bytes = 2 * w0.num_blocks * 16 * w0.Hkv * w0.D * 2
+    n_layers = w0.n_layers
+    copies = 1
+    if n_layers * pool_bytes < (1 << 30):
+        copies = max(1, -(-rotate_mib * (1 << 20) // (n_layers * pool_bytes)))
+    fill = S.page_fill_counts(w0, t0)
+    layers = []
+    for c in range(copies):
+        for l in range(n_layers):
+            d = S.make_layer(w0, t0, l + 1000 * c, device=device, fill=fill)
+            layers.append(d)
+    plans = [ST.plan_step(w, t, device=device) for (w, t) in subs]
+    # per-sub-step q/out buffers (chunk sizes differ between c5 sub-steps)
+    qbufs = []
+    for (w, t) in subs:
+        npre = sum(w.seqs[i].new_len for i in w.prefill_seqs)
+        qd = S.randn_bf16((len(w.decode_seqs), w.Hq, w.D), 77, device) if w.decode_seqs else None
+        qp = S.randn_bf16((npre, w.Hq, w.D), 78, device) if npre else None
+        kn = S.randn_bf16((int(t.cu_new[-1]), w.Hkv, w.D), 79, device)
+        vn = S.randn_bf16((int(t.cu_new[-1]), w.Hkv, w.D), 80, device)
+        qbufs.append(dict(qd=qd, qp=qp, kn=kn, vn=vn,
+                          od=torch.empty_like(qd) if qd is not None else None,
+                          op=torch.empty_like(qp) if qp is not None else None))
+    return subs, plans, layers, qbufs, copies
+
+
+def run(args):
+    import torch
+    from paged_kv_gqa_pkv_amd import binding as bd
+    from paged_kv_gqa_pkv_amd import step as ST
+
+    bd.load()
+    device = "cuda"
+    torch.cuda.set_device(0)
+    subs, plans, layers, qbufs, copies = build_inputs(args.workload, args.rotate_mib, device)
+    w0 = subs[0][0]
+    n_layers = w0.n_layers
+    stream = torch.cuda.current_stream()
+    use_events = not args.no_events
+
+    # per-step algorithmic work (average over sub-steps for c5)
+    step_bytes, dec_bytes_launch, pre_flops, pre_bytes = [], [], [], []
+    for (w, t) in subs:
+        nd = len(w.decode_seqs)
+        db = decode_bytes(w, t, w.decode_seqs) if nd else 0
+        pb, pf = prefill_work(w, t)
+        dec_bytes_launch.append(db)
+        pre_flops.append(pf)
+        pre_bytes.append(pb)
+        step_bytes.append(slot_bytes(w, t) + n_layers * (append_bytes(w, t) + db + pb))
+
+    dec_events, pre_events = [], []
+
+    def one_step(i, record):
+        k = i % len(subs)
+        plan, qb = plans[k], qbufs[k]
+        c = i % copies
+        ST.slot_mapping(plan, stream=stream)
+        for l in range(n_layers):
+            d = layers[c * n_layers + l]
+            bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
+                          stream=stream)
+            if plan.n_prefill:
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+                bd.pkv_attn_prefill_chunk(qb["op"], qb["qp"], plan.cu_q, d.k_cache, d.v_cache,
+                                          plan.bt_prefill, plan.ctx_prefill, plan.max_q_len,
+                                          plan.max_ctx_prefill, plan.scale, stream=stream)
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+                    pre_events.append((k, e0, e1))
+            if plan.n_decode:
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+                bd.pkv_attn_decode(qb["od"], qb["qd"], d.k_cache, d.v_cache, plan.bt_decode,
+                                   plan.ctx_decode, plan.max_ctx_decode, plan.scale,
+                                   workspace=plan.workspace, stream=stream)
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+                    dec_events.append((k, e0, e1))
+
+    for i in range(args.warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i, use_events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    total_bytes = sum(step_bytes[i % len(subs)] for i in range(args.steps))
+    gbs = total_bytes / elapsed / 1e9
+    n_dec = len(w0.decode_seqs)
+    tok_s = n_dec * args.steps / elapsed
+
+    roofline = None
+    extra = {}
+    if dec_events:
+        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in dec_events]
+        bytes_ = [dec_bytes_launch[k] for (k, _, _) in dec_events]
+        avg_s = sum(durs) / len(durs)
+        achieved = (sum(bytes_) / len(bytes_)) / avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "pkv_attn_decode (decode_kernel + split_merge_kernel)",
+                    "avg_launch_us": round(avg_s * 1e6, 2),
+                    "bytes_per_launch": int(sum(bytes_) / len(bytes_))}
+    if pre_events:
+        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in pre_events]
+        fl = [pre_flops[k] for (k, _, _) in pre_events]
+        tflops = sum(fl) / sum(durs) / 1e12
+        extra["prefill_mfma"] = {"bound": "mfma", "achieved": round(tflops, 2),
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                 "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
+                                 "kernel": "pkv_attn_prefill_chunk (prefill_kernel)"}
+    cfg = {"workload": f"{args.workload}: {w0.description}" if args.workload != "c5"
+           else "c5: mixed step, 512-query causal prefill chunk at offsets 0..2560 (cycled) of a "
+                "3000-token prompt + 7 decode seqs ctx U[256,2048], 28 layers, Qwen3-0.6B attention",
+           "layers": n_layers, "Hq": w0.Hq, "Hkv": w0.Hkv, "head_dim": w0.D, "page_tokens": 16,
+           "decode_batch": n_dec, "pool_pages": w0.num_blocks,
+           "context_lens": [int(x) for x in subs[0][1].context_lens.tolist()]
+           if len(w0.seqs) <= 16 else f"{len(w0.seqs)} seqs, max {w0.max_ctx}",
+           "rotated_copies": copies, "bytes_per_step": int(sum(step_bytes) / len(step_bytes)),
+           "decode_splits": bd.pkv_decode_num_splits(n_dec, w0.Hq, w0.Hkv, w0.D,
+                                                     plans[0].max_ctx_decode) if n_dec else 0}
+    out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16, random page placement)",
+           "config": cfg, "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "decode_tokens_per_s": round(tok_s, 1), "roofline": roofline}
+    out.update(extra)
+    return out, subs
+
+
+def cpu_baseline(args, subs):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    one layer of the step (slot mapping, append, attention) repeated until the
+    time budget is spent, scaled to the whole step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pkv_oracle as O
+    from paged_kv_gqa_pkv_amd import synth as S
+
+    w, t = subs[0]
+    d = S.make_layer(w, t, 0)
+
+    def u16(x):
+        return x.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    kc0, vc0, kn, vn = u16(d.k_cache), u16(d.v_cache), u16(d.k_new), u16(d.v_new)
+    qd = u16(d.q_decode) if d.q_decode is not None else None
+    qp = u16(d.q_prefill) if d.q_prefill is not None else None
+    bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
+    cu = t.cu_new.numpy().tolist()
+    npre = len(w.prefill_seqs)
+    scale = O.default_scale(w.D)
+    n_layers = w.n_layers
+    reps, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            slots = O.slot_ref(bt, cu, ctx)
+            kc, vc = O.append_ref(kc0, vc0, kn, vn, slots)
+            if npre:
+                O.prefill_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, vc, bt[:npre],
+                              ctx[:npre], scale)
+            if w.decode_seqs:
+                O.decode_ref(qd, kc, vc, bt[npre:], ctx[npre:], scale)
+            reps += 1
+            t_used = time.perf_counter() - t0
+            if t_used >= args.cpu_seconds:
+                break
+    per_layer = t_used / reps
+    per_step = per_layer * n_layers
+    step_b = (slot_bytes(w, t) + n_layers * (append_bytes(w, t) +
+              (decode_bytes(w, t, w.decode_seqs) if w.decode_seqs else 0) +
+              prefill_work(w, t)[0]))
+    return {"value": round(step_b / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} repetitions of one layer of the step (slot mapping, append, "
+                      f"attention; {w.name}) in {t_used:.1f} s on 1 host thread, "
+                      f"{per_step * 1e3:.1f} ms per {n_layers}-layer step"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    out, subs = run(args)
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(args, subs)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

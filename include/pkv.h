@@ -117,14 +117,18 @@ int32_t pkv_decode_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * h / (Hq/Hkv), [P1] q.view(T, n_kv, group, D)).
  *     out[b][h][:] = sum_p w_p V_b[p][h/G][:],  w = softmax_p(scale * <q[b][h], K_b[p][h/G]>)
  * over positions p < context_lens[b] read through block_tables[b].
- * context_lens[b] == 0 gives zeros; a length above max_context_len (or past
- * the table) gives NaN.  fp32 accumulation, bf16 output.
+ * context_lens[b] == 0 gives zeros; a length past the table or beyond what
+ * max_context_len planned for gives NaN.  fp32 accumulation, bf16 output.
+ * One kernel launch: long contexts are cut into splits whose partial
+ * softmax states are merged, in split order, by the last split to finish.
  *   out, q        bf16 [B][Hq][D]; must not overlap
  *   scale         normally 1/sqrt(D)
  *   max_context_len  host-side upper bound of context_lens (plans the splits)
  *   workspace     device buffer of at least pkv_decode_workspace_bytes(...)
- *                 bytes (may be NULL when that is 0); scratch only, its
- *                 contents on entry do not matter.
+ *                 bytes (may be NULL when that is 0).  It must be
+ *                 zero-filled before its first use; every call leaves it
+ *                 ready for the next (its arrival counters back at zero).
+ *                 Calls that may overlap in time need separate workspaces.
  */
 int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,

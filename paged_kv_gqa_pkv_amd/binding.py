@@ -129,7 +129,8 @@ def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                     v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                     max_context_len: int, scale: float, workspace: Optional[torch.Tensor] = None,
                     stream=None) -> None:
-    """out[B, Hq, D] <- decode attention of q[B, Hq, D] over the paged pools."""
+    """out[B, Hq, D] <- decode attention of q[B, Hq, D] over the paged pools.
+    ``workspace``: zero-filled before first use (the library keeps it so)."""
     _need(q, torch.bfloat16, "q", 3)
     _need(out, torch.bfloat16, "out", 3)
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):

@@ -37,9 +37,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def _compile(hipcc: str, src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(hipcc: str, src: str, verbose: bool, defines, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc, *COMMON, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in line)
@@ -50,18 +51,22 @@ def _compile(hipcc: str, src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = OUT) -> str:
+    """Compile every source and link ``out``.  ``defines`` (NAME=VALUE strings)
+    override the kernels' tuning constants."""
+    build_dir = BUILD_DIR if out == OUT else os.path.join(
+        BUILD_DIR, os.path.splitext(os.path.basename(out))[0])
+    os.makedirs(build_dir, exist_ok=True)
     hipcc = _hipcc()
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(hipcc, s, verbose, defines, build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

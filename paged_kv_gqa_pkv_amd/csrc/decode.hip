@@ -22,8 +22,9 @@
 //
 // Long contexts with few (sequence, head) pairs are cut into splits of
 // pages_per_split pages (flash-decoding); each split writes its unnormalised
-// (m, l, acc) to the workspace and a second kernel merges the splits in fixed
-// order, so results are run-to-run bit-identical.
+// (m, l, acc) to the workspace, and the last split of a (sequence, KV head)
+// to finish merges them all in split order, so results are run-to-run
+// bit-identical and the whole call is one kernel.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -31,9 +32,38 @@ namespace pkv {
 
 namespace {
 
+// Tuning constants (measured on MI355X; overridable at build time).
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1            // streaming (non-temporal) K/V loads
+#endif
+#ifndef PKV_DECODE_WG_PER_CU
+#define PKV_DECODE_WG_PER_CU 2     // split planner: workgroups per compute unit
+#endif
+#ifndef PKV_DECODE_MIN_PPW
+#define PKV_DECODE_MIN_PPW 2       // split planner: minimum pages per wave
+#endif
+
+
 constexpr int kWaves = 4;                    // waves per workgroup
 constexpr int kMaxPagesPerWave = 64;         // one VGPR of page ids per wave
+
+__device__ __forceinline__ u32x4 load_kv(const u32x4* p) {
+#if PKV_DECODE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 constexpr float kNegInf = -__builtin_inff();
+
+// Split partials are written and read with agent-coherent accesses (the
+// last split to finish, possibly on another XCD, merges them).
+__device__ __forceinline__ void ws_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ws_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct DecodeArgs {
   uint16_t* out;                 // bf16 [B][Hq][D]
@@ -42,8 +72,9 @@ struct DecodeArgs {
   const u32x4* v_cache;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
-  float2* ws_ml;                 // [B][Hq][S] (m, l), log2 domain
+  float* ws_ml;                  // [B][Hq][S][2] (m, l), log2 domain
   float* ws_acc;                 // [B][Hq][S][D]
+  int* counters;                 // [B][Hkv] arrivals per (sequence, KV head); zero between calls
   int B, Hq, Hkv, num_blocks, max_blocks, splits, pages_per_split;
   float scale_log2;              // scale * log2(e)
 };
@@ -63,10 +94,10 @@ __device__ __forceinline__ void load_page(PageRegs& r, const DecodeArgs& a, int6
   const int o8 = (int)(8 * row_stride);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    r.k[0][h] = __builtin_nontemporal_load(kp + lane_off + 8 * h);
-    r.k[1][h] = __builtin_nontemporal_load(kp + lane_off + o8 + 8 * h);
-    r.v[0][h] = __builtin_nontemporal_load(vp + lane_off + 8 * h);
-    r.v[1][h] = __builtin_nontemporal_load(vp + lane_off + o8 + 8 * h);
+    r.k[0][h] = load_kv(kp + lane_off + 8 * h);
+    r.k[1][h] = load_kv(kp + lane_off + o8 + 8 * h);
+    r.v[0][h] = load_kv(vp + lane_off + 8 * h);
+    r.v[1][h] = load_kv(vp + lane_off + o8 + 8 * h);
   }
 }
 
@@ -157,6 +188,7 @@ decode_kernel(const DecodeArgs a) {
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ int s_bad[kWaves];
+  __shared__ int s_last;
 
   const int bid = blockIdx.x;                 // ((b * S) + split) * Hkv + g
   const int g = bid % a.Hkv;
@@ -168,45 +200,16 @@ decode_kernel(const DecodeArgs a) {
   const int w = uniform(tid >> 6);
   const int r0 = lane >> 3, c = lane & 7;
   const int S = a.splits;
+  const int ppw = a.pages_per_split / kWaves;  // pages per wave (the plan keeps this exact)
 
-  // A length outside [0, planned maximum] poisons the outputs of the sequence
-  // (the plan covers splits * pages_per_split pages; no read goes past it).
-  const int n = a.ctx_lens[b];
-  const bool bad_len = n < 0 || n > a.max_blocks * kPage ||
-                       (n + kPage - 1) / kPage > a.splits * a.pages_per_split;
-  const int n_pages = bad_len ? 0 : (n + kPage - 1) / kPage;
+  // Everything up to the page loads is independent of the context length, so
+  // the length, the page ids and q are fetched in parallel.  The wave's page
+  // range is fixed by the plan; ids past the sequence's last page are fetched
+  // (they lie inside the table row) but never used.
   const int p0 = split * a.pages_per_split;
-  const int p1 = min(p0 + a.pages_per_split, n_pages);
-
-  if (p0 >= p1) {
-    // Nothing to read.  A single-pass call still owns the output: zeros for an
-    // empty context, NaN for an invalid length.  Split calls leave it to the
-    // merge kernel, which reads the length itself.
-    if (S == 1) {
-      for (int e = tid; e < G * kD; e += kWaves * kWave) {
-        const int j = e / kD, d = e % kD;
-        a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = bad_len ? 0x7fc0u : 0u;
-      }
-    }
-    return;
-  }
-
-  // This wave's pages: [w0, w1) of the split; full pages first, then the
-  // sequence's last page if it is partial and falls in range.
-  const int np = p1 - p0;
-  const int ppw = (np + kWaves - 1) / kWaves;
-  const int w0 = min(p0 + w * ppw, p1);
-  const int w1 = min(w0 + ppw, p1);
-  const int n_full = n / kPage;
-  const int full_end = min(w1, n_full);
-  const int nfull = max(0, full_end - w0);
-  const bool has_tail = (n % kPage) != 0 && n_full >= w0 && n_full < w1;
-  const int cnt = w1 - w0;                    // <= kMaxPagesPerWave by the plan
-
+  const int wp0 = p0 + w * ppw;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
-  const int my_id = lane < cnt ? bt[w0 + lane] : 0;
-
-  // q for the G heads of this group: the lane's 16 dims as packed bf16 pairs.
+  const int my_id = (lane < ppw && wp0 + lane < a.max_blocks) ? bt[wp0 + lane] : 0;
   uint32_t qw[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -215,6 +218,34 @@ decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { qw[j][i] = lo[i]; qw[j][4 + i] = hi[i]; }
   }
+
+  // A length outside [0, planned maximum] poisons the outputs of the sequence
+  // (the plan covers splits * pages_per_split pages; no read goes past it).
+  const int n = a.ctx_lens[b];
+  const bool bad_len = n < 0 || n > a.max_blocks * kPage ||
+                       (n + kPage - 1) / kPage > S * a.pages_per_split;
+  const int n_pages = bad_len ? 0 : (n + kPage - 1) / kPage;
+  const int p1 = min(p0 + a.pages_per_split, n_pages);
+
+  if (p0 >= p1) {
+    // Nothing to read.  The first split owns the output of an empty or
+    // invalid sequence: zeros for an empty context, NaN for a bad length.
+    if (split == 0) {
+      for (int e = tid; e < G * kD; e += kWaves * kWave) {
+        const int j = e / kD, d = e % kD;
+        a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = bad_len ? 0x7fc0u : 0u;
+      }
+    }
+    return;
+  }
+
+  // This wave's pages: [w0, w1); full pages first, then the sequence's last
+  // page if it is partial and falls in range.
+  const int w0 = min(wp0, p1);
+  const int w1 = min(wp0 + ppw, p1);
+  const int n_full = n / kPage;
+  const int nfull = max(0, min(w1, n_full) - w0);
+  const bool has_tail = (n % kPage) != 0 && n_full >= w0 && n_full < w1;
 
   float m[G], l[G], acc[G][16];
 #pragma unroll
@@ -225,9 +256,10 @@ decode_kernel(const DecodeArgs a) {
   }
 
   const int lane_off = r0 * a.Hkv * 16 + c;
+  const int id_base = w0 - wp0;               // lane of my_id holding page w0
   int bad = bad_len ? 1 : 0;
   auto page_id = [&](int j) -> int64_t {
-    const int id = __builtin_amdgcn_readlane(my_id, j);
+    const int id = __builtin_amdgcn_readlane(my_id, id_base + j);
     const bool ok = id >= 0 && id < a.num_blocks;
     bad |= ok ? 0 : 1;
     return ok ? id : 0;
@@ -304,6 +336,7 @@ decode_kernel(const DecodeArgs a) {
   int any_bad = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) any_bad |= s_bad[i];
+  const float nan = __builtin_nanf("");
   for (int e = tid; e < G * kD; e += kWaves * kWave) {
     const int j = e / kD, d = e % kD;
     float M = kNegInf;
@@ -319,57 +352,71 @@ decode_kernel(const DecodeArgs a) {
     }
     const int h = g * G + j;
     if (S == 1) {
-      const float o = any_bad ? __builtin_nanf("") : A / L;
+      const float o = any_bad ? nan : A / L;
       a.out[((int64_t)b * a.Hq + h) * kD + d] = (uint16_t)f32_to_bf16_bits(o);
     } else {
       const int64_t r = ((int64_t)b * a.Hq + h) * S + split;
-      a.ws_acc[r * kD + d] = any_bad ? __builtin_nanf("") : A;
-      if (d == 0) a.ws_ml[r] = make_float2(M, any_bad ? __builtin_nanf("") : L);
+      ws_store(a.ws_acc + r * kD + d, any_bad ? nan : A);
+      if (d == 0) {
+        ws_store(a.ws_ml + 2 * r, M);
+        ws_store(a.ws_ml + 2 * r + 1, any_bad ? nan : L);
+      }
     }
   }
+  if (S == 1) return;
+
+  // Split path: the last of the sequence's non-empty splits to finish merges
+  // all of them, in split order (identical whichever split finishes last).
+  // The partials above were written with agent-coherent stores; waiting for
+  // their completion before the arrival is counted, and reading them back
+  // with agent-coherent loads, orders them without an L2 writeback.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  int* counter = a.counters + (int64_t)b * a.Hkv + g;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             ns - 1;
+  __syncthreads();
+  if (!s_last) return;
+  for (int e = tid; e < G * kD; e += kWaves * kWave) {
+    const int j = e / kD, d = e % kD;
+    const int64_t rs = ((int64_t)b * a.Hq + g * G + j) * S;
+    float M = kNegInf;
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ws_load(a.ws_ml + 2 * (rs + s2)));
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, A = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const float f = fast_exp2(ws_load(a.ws_ml + 2 * (rs + s2)) - Mu);
+      L = __builtin_fmaf(ws_load(a.ws_ml + 2 * (rs + s2) + 1), f, L);
+      A = __builtin_fmaf(ws_load(a.ws_acc + (rs + s2) * kD + d), f, A);
+    }
+    a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = (uint16_t)f32_to_bf16_bits(A / L);
+  }
+  // Leave the counter at zero for the next call on this workspace.
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge the splits of one (sequence, query head) in fixed split order.
-// One wave; lane owns dims 2*lane and 2*lane+1.
-__global__ void __launch_bounds__(kWave)
-split_merge_kernel(const DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq;
-  const int lane = threadIdx.x;
-  const int n = a.ctx_lens[b];
-  uint32_t* out = reinterpret_cast<uint32_t*>(a.out + (int64_t)bh * kD) + lane;
-  if (n < 0 || n > a.max_blocks * kPage ||
-      (n + kPage - 1) / kPage > a.splits * a.pages_per_split) {
-    *out = 0x7fc07fc0u;
-    return;
-  }
-  if (n == 0) { *out = 0u; return; }
-  const int n_pages = (n + kPage - 1) / kPage;
-  const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;   // <= splits
-  const float2* ml = a.ws_ml + (int64_t)bh * a.splits;
-  const float* acc = a.ws_acc + (int64_t)bh * a.splits * kD + 2 * lane;
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, A0 = 0.f, A1 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float2 e = ml[s];
-    const float f = fast_exp2(e.x - Mu);
-    L = __builtin_fmaf(e.y, f, L);
-    const float2 v = *reinterpret_cast<const float2*>(acc + (int64_t)s * kD);
-    A0 = __builtin_fmaf(v.x, f, A0);
-    A1 = __builtin_fmaf(v.y, f, A1);
-  }
-  *out = pack_bf16x2(A0 / L, A1 / L);
-}
 
-template <int G>
+// Pages held per pipeline stage, by group size (register budget: two stages
+// of U pages, 32 VGPRs per page, next to 16*G accumulators).
+#ifndef PKV_DECODE_U_G1
+#define PKV_DECODE_U_G1 2
+#endif
+#ifndef PKV_DECODE_U_G2
+#define PKV_DECODE_U_G2 2
+#endif
+#ifndef PKV_DECODE_U_G4
+#define PKV_DECODE_U_G4 1
+#endif
+#ifndef PKV_DECODE_U_G8
+#define PKV_DECODE_U_G8 1
+#endif
+
+template <int G, int U>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.B * a.Hkv * a.splits);
-  hipLaunchKernelGGL((decode_kernel<G, 2>), dim3(grid), dim3(kWaves * kWave), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<G, U>), dim3(grid), dim3(kWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -378,20 +425,22 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 // Split planner.  Work units are (sequence, KV head) pairs; a workgroup of 4
-// waves streams one split of a unit.  The planner aims for about 4 workgroups
-// per compute unit so that enough page loads are in flight to cover HBM
-// latency, keeps splits at least 8 pages long (2 per wave) so per-split
-// overhead stays small, and at most 256 pages (64 per wave: one VGPR of page
-// ids).  Only host-known sizes enter, so no device->host sync is needed.
+// waves streams one split of a unit.  The planner aims for about
+// PKV_DECODE_WG_PER_CU workgroups per compute unit so that enough page loads
+// are in flight to cover HBM latency, keeps splits at least
+// 4 * PKV_DECODE_MIN_PPW pages long so per-split overhead stays small, and at most 256 pages (64 per wave: one VGPR of page
+// ids); split lengths are multiples of 4 pages (one share per wave).  Only
+// host-known sizes enter, so no device->host sync is needed.
 DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus) {
   DecodePlan p{};
   const int max_pages = max(1, (max_context_len + kPage - 1) / kPage);
   const int units = max(1, B * Hkv);
-  const int target_wgs = 4 * max(1, num_cus);
+  const int target_wgs = PKV_DECODE_WG_PER_CU * max(1, num_cus);
   int splits = (target_wgs + units - 1) / units;
-  const int min_pps = 2 * kWaves;
+  const int min_pps = PKV_DECODE_MIN_PPW * kWaves;
   const int max_pps = kMaxPagesPerWave * kWaves;
   int pps = (max_pages + splits - 1) / splits;
+  pps = (pps + kWaves - 1) / kWaves * kWaves;
   if (pps < min_pps) pps = min_pps;
   if (pps > max_pps) pps = max_pps;
   splits = (max_pages + pps - 1) / pps;
@@ -401,8 +450,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus)
   if (splits > 1) {
     p.ws_ml_bytes = align256((size_t)B * Hq * splits * sizeof(float2));
     p.ws_acc_bytes = align256((size_t)B * Hq * splits * kD * sizeof(float));
+    p.ws_counter_bytes = align256((size_t)B * Hkv * sizeof(int));
   }
-  p.ws_bytes = p.ws_ml_bytes + p.ws_acc_bytes;
+  p.ws_bytes = p.ws_ml_bytes + p.ws_acc_bytes + p.ws_counter_bytes;
   return p;
 }
 
@@ -418,18 +468,20 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
   a.v_cache = static_cast<const u32x4*>(v_cache);
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
-  a.ws_ml = plan.splits > 1 ? static_cast<float2*>(workspace) : nullptr;
-  a.ws_acc = plan.splits > 1
-                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_bytes)
-                 : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  const bool split = plan.splits > 1;
+  a.ws_ml = split ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_acc = split ? reinterpret_cast<float*>(ws + plan.ws_ml_bytes) : nullptr;
+  a.counters = split ? reinterpret_cast<int*>(ws + plan.ws_ml_bytes + plan.ws_acc_bytes)
+                     : nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
   a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
   a.scale_log2 = scale * 1.4426950408889634f;
   switch (Hq / Hkv) {
-    case 1: return launch_g<1>(a, stream);
-    case 2: return launch_g<2>(a, stream);
-    case 4: return launch_g<4>(a, stream);
-    case 8: return launch_g<8>(a, stream);
+    case 1: return launch_g<1, PKV_DECODE_U_G1>(a, stream);
+    case 2: return launch_g<2, PKV_DECODE_U_G2>(a, stream);
+    case 4: return launch_g<4, PKV_DECODE_U_G4>(a, stream);
+    case 8: return launch_g<8, PKV_DECODE_U_G8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,6 +21,7 @@ struct DecodePlan {
   int pages_per_split;
   size_t ws_ml_bytes;    // float2 (m, l) [B][Hq][S]
   size_t ws_acc_bytes;   // float [B][Hq][S][D]
+  size_t ws_counter_bytes;  // int [B][Hkv] split arrival counters
   size_t ws_bytes;       // total, 0 for a single pass
 };
 

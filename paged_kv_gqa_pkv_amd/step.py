@@ -79,7 +79,7 @@ def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = No
     if dec:
         nbytes = bd.pkv_decode_workspace_bytes(len(dec), w.Hq, w.Hkv, w.D, max_ctx_dec)
         if nbytes:
-            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return StepPlan(
         n_prefill=len(pre), n_decode=len(dec), Hq=w.Hq, Hkv=w.Hkv, D=w.D,
         block_tables=t.block_tables.to(device), context_lens=t.context_lens.to(device),
