@@ -6,9 +6,10 @@ slot mapping of the step's new tokens, then per layer the KV append and the
 attention launches (prefill chunk and/or decode, with the split merge).
 Inputs are resident in HBM before timing starts.
 
-Default workload: single-layer decode, Qwen3-0.6B attention shapes, batch 8,
-contexts ~ U[1,1024] (post-append), 512-page pool.  Other configurations:
---workload c1|c3|c4a|c4b|c5.  Working sets under 1 GiB are rotated over
+Default workload (c4): the Qwen3-8B-shaped decode step, 36 layers, batch 64
+at context 4096 plus batch 13 at context 32768 (each with its own pools);
+a step runs both batches.  Other configurations: --workload
+c1|c2|c3|c4a|c4b|c5 (c5 cycles its six prefill-chunk offsets over steps).  Working sets under 1 GiB are rotated over
 enough independent copies (>= 512 MiB in total) that the 256 MB Infinity
 Cache cannot serve them.
 
@@ -37,10 +38,10 @@ METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) + decode tokens/s/GPU"
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c2",
-                   choices=["c1", "c2", "c3", "c4a", "c4b", "c5"])
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c4",
+                   choices=["c1", "c2", "c3", "c4", "c4a", "c4b", "c5"])
     p.add_argument("--rotate-mib", type=int, default=512,
                    help="total bytes of rotated input copies for small working sets")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -95,15 +96,63 @@ def prefill_work(w, t):
 
 # ---------------------------------------------------------------------------
 
-def build_inputs(name, rotate_mib, device):
+class Part:
+    """One independent decode/mixed step shape with its own pools."""
+
+    def __init__(self, w, t, plan, layers, bufs, copies):
+        self.w, self.t, self.plan, self.layers, self.bufs, self.copies = w, t, plan, layers, bufs, copies
+        nd = len(w.decode_seqs)
+        self.dec_bytes = decode_bytes(w, t, w.decode_seqs) if nd else 0
+        self.pre_bytes, self.pre_flops = prefill_work(w, t)
+        self.step_bytes = slot_bytes(w, t) + w.n_layers * (append_bytes(w, t) + self.dec_bytes +
+                                                           self.pre_bytes)
+
+
+def _bufs(w, t, device):
+    import torch
+    from paged_kv_gqa_pkv_amd import synth as S
+    npre = sum(w.seqs[i].new_len for i in w.prefill_seqs)
+    qd = S.randn_bf16((len(w.decode_seqs), w.Hq, w.D), 77, device) if w.decode_seqs else None
+    qp = S.randn_bf16((npre, w.Hq, w.D), 78, device) if npre else None
+    T = int(t.cu_new[-1])
+    return dict(qd=qd, qp=qp, kn=S.randn_bf16((T, w.Hkv, w.D), 79, device),
+                vn=S.randn_bf16((T, w.Hkv, w.D), 80, device),
+                od=torch.empty_like(qd) if qd is not None else None,
+                op=torch.empty_like(qp) if qp is not None else None)
+
+
+def _layers(w, t, rotate_mib, device):
+    from paged_kv_gqa_pkv_amd import synth as S
+    pool_bytes = 2 * w.num_blocks * 16 * w.Hkv * w.D * 2
+    copies = 1
+    if w.n_layers * pool_bytes < (1 << 30):
+        copies = max(1, -(-rotate_mib * (1 << 20) // (w.n_layers * pool_bytes)))
+    fill = S.page_fill_counts(w, t)
+    layers = [S.make_layer(w, t, l + 1000 * c, device=device, fill=fill)
+              for c in range(copies) for l in range(w.n_layers)]
+    return layers, copies
+
+
+def build_parts(name, rotate_mib, device):
+    """Returns (parts, schedule): schedule(i) lists the parts step i runs."""
     import torch
     from paged_kv_gqa_pkv_amd import step as ST
     from paged_kv_gqa_pkv_amd import synth as S
 
-    subs = []
+    if name == "c4":
+        parts = []
+        for sub in ("c4a", "c4b"):
+            w = S.workload(sub)
+            t = S.make_tables(w)
+            layers, copies = _layers(w, t, rotate_mib, device)
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device), layers,
+                              _bufs(w, t, device), copies))
+        return parts, (lambda i: [0, 1])
     if name == "c5":
         base_w = S.workload("c5", 5)
         base_t = S.make_tables(base_w)
+        layers, copies = _layers(base_w, base_t, rotate_mib, device)
+        parts = []
         for s in range(6):
             w = S.workload("c5", s)
             p = w.seqs[0]
@@ -111,36 +160,23 @@ def build_inputs(name, rotate_mib, device):
             new = torch.tensor([0, p.new_len] + [1] * len(w.decode_seqs), dtype=torch.int64)
             t = S.Tables(base_t.block_tables, ctx, torch.cumsum(new, 0).to(torch.int32),
                          torch.tensor([q.pre_len for q in w.seqs], dtype=torch.int32))
-            subs.append((w, t))
-        w0, t0 = base_w, base_t
-    else:
-        w0 = S.workload(name)
-        t0 = S.make_tables(w0)
-        subs.append((w0, t0))
-    pool_bytes = 2 * w0.num_blocks * 16 * w0.Hkv * w0.D * 2
-    n_layers = w0.n_layers
-    copies = 1
-    if n_layers * pool_bytes < (1 << 30):
-        copies = max(1, -(-rotate_mib * (1 << 20) // (n_layers * pool_bytes)))
-    fill = S.page_fill_counts(w0, t0)
-    layers = []
-    for c in range(copies):
-        for l in range(n_layers):
-            d = S.make_layer(w0, t0, l + 1000 * c, device=device, fill=fill)
-            layers.append(d)
-    plans = [ST.plan_step(w, t, device=device) for (w, t) in subs]
-    # per-sub-step q/out buffers (chunk sizes differ between c5 sub-steps)
-    qbufs = []
-    for (w, t) in subs:
-        npre = sum(w.seqs[i].new_len for i in w.prefill_seqs)
-        qd = S.randn_bf16((len(w.decode_seqs), w.Hq, w.D), 77, device) if w.decode_seqs else None
-        qp = S.randn_bf16((npre, w.Hq, w.D), 78, device) if npre else None
-        kn = S.randn_bf16((int(t.cu_new[-1]), w.Hkv, w.D), 79, device)
-        vn = S.randn_bf16((int(t.cu_new[-1]), w.Hkv, w.D), 80, device)
-        qbufs.append(dict(qd=qd, qp=qp, kn=kn, vn=vn,
-                          od=torch.empty_like(qd) if qd is not None else None,
-                          op=torch.empty_like(qp) if qp is not None else None))
-    return subs, plans, layers, qbufs, copies
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device), layers,
+                              _bufs(w, t, device), copies))
+        return parts, (lambda i: [i % 6])
+    w = S.workload(name)
+    t = S.make_tables(w)
+    layers, copies = _layers(w, t, rotate_mib, device)
+    return [Part(w, t, ST.plan_step(w, t, device=device), layers, _bufs(w, t, device),
+                 copies)], (lambda i: [0])
+
+
+WORKLOAD_TEXT = {
+    "c4": "c4: Qwen3-8B-shaped decode step, 36 layers, Hq=32 Hkv=8 D=128, pages of 16: batch 64 "
+          "at context 4096 (pool 16416 pages/layer) plus batch 13 at context 32768 (pool 26656 "
+          "pages/layer, split-context path), one append per sequence per layer",
+    "c5": "c5: mixed step, 512-query causal prefill chunk at offsets 0..2560 (cycled) of a "
+          "3000-token prompt + 7 decode seqs ctx U[256,2048], 28 layers, Qwen3-0.6B attention",
+}
 
 
 def run(args):
@@ -151,32 +187,19 @@ def run(args):
     bd.load()
     device = "cuda"
     torch.cuda.set_device(0)
-    subs, plans, layers, qbufs, copies = build_inputs(args.workload, args.rotate_mib, device)
-    w0 = subs[0][0]
-    n_layers = w0.n_layers
+    parts, schedule = build_parts(args.workload, args.rotate_mib, device)
     stream = torch.cuda.current_stream()
     use_events = not args.no_events
-
-    # per-step algorithmic work (average over sub-steps for c5)
-    step_bytes, dec_bytes_launch, pre_flops, pre_bytes = [], [], [], []
-    for (w, t) in subs:
-        nd = len(w.decode_seqs)
-        db = decode_bytes(w, t, w.decode_seqs) if nd else 0
-        pb, pf = prefill_work(w, t)
-        dec_bytes_launch.append(db)
-        pre_flops.append(pf)
-        pre_bytes.append(pb)
-        step_bytes.append(slot_bytes(w, t) + n_layers * (append_bytes(w, t) + db + pb))
-
     dec_events, pre_events = [], []
 
-    def one_step(i, record):
-        k = i % len(subs)
-        plan, qb = plans[k], qbufs[k]
-        c = i % copies
+    def run_part(k, i, record):
+        pt = parts[k]
+        plan, qb = pt.plan, pt.bufs
+        c = i % pt.copies
+        n_layers = pt.w.n_layers
         ST.slot_mapping(plan, stream=stream)
         for l in range(n_layers):
-            d = layers[c * n_layers + l]
+            d = pt.layers[c * n_layers + l]
             bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
                           stream=stream)
             if plan.n_prefill:
@@ -198,6 +221,10 @@ def run(args):
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     dec_events.append((k, e0, e1))
 
+    def one_step(i, record):
+        for k in schedule(i):
+            run_part(k, i, record)
+
     for i in range(args.warmup):
         one_step(i, False)
     torch.cuda.synchronize()
@@ -207,57 +234,55 @@ def run(args):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    ms_per_step = 1e3 * elapsed / args.steps
-    total_bytes = sum(step_bytes[i % len(subs)] for i in range(args.steps))
+    total_bytes = sum(parts[k].step_bytes for i in range(args.steps) for k in schedule(i))
+    dec_tokens = sum(len(parts[k].w.decode_seqs) for i in range(args.steps) for k in schedule(i))
     gbs = total_bytes / elapsed / 1e9
-    n_dec = len(w0.decode_seqs)
-    tok_s = n_dec * args.steps / elapsed
-
-    roofline = None
-    extra = {}
+    roofline, extra = None, {}
     if dec_events:
         durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in dec_events]
-        bytes_ = [dec_bytes_launch[k] for (k, _, _) in dec_events]
-        avg_s = sum(durs) / len(durs)
-        achieved = (sum(bytes_) / len(bytes_)) / avg_s / 1e9
+        byts = [parts[k].dec_bytes for (k, _, _) in dec_events]
+        achieved = sum(byts) / sum(durs) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "pkv_attn_decode (decode_kernel + split_merge_kernel)",
-                    "avg_launch_us": round(avg_s * 1e6, 2),
-                    "bytes_per_launch": int(sum(bytes_) / len(bytes_))}
+                    "kernel": "decode_kernel (pkv_attn_decode)",
+                    "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
+                    "bytes_per_launch": int(sum(byts) / len(byts)),
+                    "launches": len(durs)}
     if pre_events:
         durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in pre_events]
-        fl = [pre_flops[k] for (k, _, _) in pre_events]
+        fl = [parts[k].pre_flops for (k, _, _) in pre_events]
         tflops = sum(fl) / sum(durs) / 1e12
         extra["prefill_mfma"] = {"bound": "mfma", "achieved": round(tflops, 2),
                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                                  "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
-                                 "kernel": "pkv_attn_prefill_chunk (prefill_kernel)"}
-    cfg = {"workload": f"{args.workload}: {w0.description}" if args.workload != "c5"
-           else "c5: mixed step, 512-query causal prefill chunk at offsets 0..2560 (cycled) of a "
-                "3000-token prompt + 7 decode seqs ctx U[256,2048], 28 layers, Qwen3-0.6B attention",
-           "layers": n_layers, "Hq": w0.Hq, "Hkv": w0.Hkv, "head_dim": w0.D, "page_tokens": 16,
-           "decode_batch": n_dec, "pool_pages": w0.num_blocks,
-           "context_lens": [int(x) for x in subs[0][1].context_lens.tolist()]
-           if len(w0.seqs) <= 16 else f"{len(w0.seqs)} seqs, max {w0.max_ctx}",
-           "rotated_copies": copies, "bytes_per_step": int(sum(step_bytes) / len(step_bytes)),
-           "decode_splits": bd.pkv_decode_num_splits(n_dec, w0.Hq, w0.Hkv, w0.D,
-                                                     plans[0].max_ctx_decode) if n_dec else 0}
+                                 "kernel": "prefill_kernel (pkv_attn_prefill_chunk)"}
+    w0 = parts[0].w
+    cfg = {"workload": WORKLOAD_TEXT.get(args.workload, f"{args.workload}: {w0.description}"),
+           "parts": [{"name": p.w.name, "layers": p.w.n_layers, "Hq": p.w.Hq, "Hkv": p.w.Hkv,
+                      "head_dim": p.w.D, "decode_batch": len(p.w.decode_seqs),
+                      "max_context": p.w.max_ctx, "pool_pages": p.w.num_blocks,
+                      "rotated_copies": p.copies, "bytes_per_part_step": p.step_bytes,
+                      "decode_splits": bd.pkv_decode_num_splits(
+                          len(p.w.decode_seqs), p.w.Hq, p.w.Hkv, p.w.D,
+                          p.plan.max_ctx_decode) if p.w.decode_seqs else 0}
+                     for p in parts[:2]],
+           "page_tokens": 16, "launch": "eager, one stream"}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(1e3 * elapsed / args.steps, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) bf16, random page placement)",
            "config": cfg, "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-           "decode_tokens_per_s": round(tok_s, 1), "roofline": roofline}
+           "decode_tokens_per_s": round(dec_tokens / elapsed, 1), "roofline": roofline}
     out.update(extra)
-    return out, subs
+    return out, parts
 
 
-def cpu_baseline(args, subs):
+def cpu_baseline(args, parts):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    one layer of the step (slot mapping, append, attention) repeated until the
-    time budget is spent, scaled to the whole step."""
+    one layer of each part of the step (slot mapping, append, attention),
+    repeated until the time budget is spent, scaled to the whole step."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -265,45 +290,43 @@ def cpu_baseline(args, subs):
     from oracle import pkv_oracle as O
     from paged_kv_gqa_pkv_amd import synth as S
 
-    w, t = subs[0]
-    d = S.make_layer(w, t, 0)
-
     def u16(x):
         return x.cpu().view(torch.int16).numpy().view(np.uint16)
 
-    kc0, vc0, kn, vn = u16(d.k_cache), u16(d.v_cache), u16(d.k_new), u16(d.v_new)
-    qd = u16(d.q_decode) if d.q_decode is not None else None
-    qp = u16(d.q_prefill) if d.q_prefill is not None else None
-    bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
-    cu = t.cu_new.numpy().tolist()
-    npre = len(w.prefill_seqs)
-    scale = O.default_scale(w.D)
-    n_layers = w.n_layers
-    reps, t_used = 0, 0.0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            slots = O.slot_ref(bt, cu, ctx)
-            kc, vc = O.append_ref(kc0, vc0, kn, vn, slots)
-            if npre:
-                O.prefill_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, vc, bt[:npre],
-                              ctx[:npre], scale)
-            if w.decode_seqs:
-                O.decode_ref(qd, kc, vc, bt[npre:], ctx[npre:], scale)
-            reps += 1
-            t_used = time.perf_counter() - t0
-            if t_used >= args.cpu_seconds:
-                break
-    per_layer = t_used / reps
-    per_step = per_layer * n_layers
-    step_b = (slot_bytes(w, t) + n_layers * (append_bytes(w, t) +
-              (decode_bytes(w, t, w.decode_seqs) if w.decode_seqs else 0) +
-              prefill_work(w, t)[0]))
+    per_step, step_b, desc = 0.0, 0, []
+    budget = args.cpu_seconds / len(parts[:2])
+    for pt in parts[:2]:
+        w, t = pt.w, pt.t
+        d = S.make_layer(w, t, 0)
+        kc0, vc0, kn, vn = u16(d.k_cache), u16(d.v_cache), u16(d.k_new), u16(d.v_new)
+        qd = u16(d.q_decode) if d.q_decode is not None else None
+        qp = u16(d.q_prefill) if d.q_prefill is not None else None
+        bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
+        cu = t.cu_new.numpy().tolist()
+        npre = len(w.prefill_seqs)
+        scale = O.default_scale(w.D)
+        reps = 0
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            while True:
+                slots = O.slot_ref(bt, cu, ctx)
+                kc, vc = O.append_ref(kc0, vc0, kn, vn, slots)
+                if npre:
+                    O.prefill_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, vc, bt[:npre],
+                                  ctx[:npre], scale)
+                if w.decode_seqs:
+                    O.decode_ref(qd, kc, vc, bt[npre:], ctx[npre:], scale)
+                reps += 1
+                used = time.perf_counter() - t0
+                if used >= budget:
+                    break
+        per_step += used / reps * w.n_layers
+        step_b += pt.step_bytes
+        desc.append(f"{w.name}: {reps} x 1 of {w.n_layers} layers in {used:.1f} s")
     return {"value": round(step_b / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{reps} repetitions of one layer of the step (slot mapping, append, "
-                      f"attention; {w.name}) in {t_used:.1f} s on 1 host thread, "
-                      f"{per_step * 1e3:.1f} ms per {n_layers}-layer step"}
+            "sample": "; ".join(desc) + f" on 1 host thread (fp64 numpy, BLAS limited to 1 "
+                      f"thread), scaled to {per_step:.1f} s per full step"}
 
 
 def main():
@@ -314,9 +337,9 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
-    out, subs = run(args)
+    out, parts = run(args)
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(args, subs)
+        out["cpu_baseline"] = cpu_baseline(args, parts)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -42,6 +42,9 @@ namespace {
 #ifndef PKV_DECODE_MIN_PPW
 #define PKV_DECODE_MIN_PPW 2       // split planner: minimum pages per wave
 #endif
+#ifndef PKV_DECODE_WG_COST_PAGES
+#define PKV_DECODE_WG_COST_PAGES 3 // split planner: fixed workgroup cost, in page-times
+#endif
 
 
 constexpr int kWaves = 4;                    // waves per workgroup
@@ -425,31 +428,42 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 // Split planner.  Work units are (sequence, KV head) pairs; a workgroup of 4
-// waves streams one split of a unit.  The planner aims for about
-// PKV_DECODE_WG_PER_CU workgroups per compute unit so that enough page loads
-// are in flight to cover HBM latency, keeps splits at least
-// 4 * PKV_DECODE_MIN_PPW pages long so per-split overhead stays small, and at most 256 pages (64 per wave: one VGPR of page
-// ids); split lengths are multiples of 4 pages (one share per wave).  Only
-// host-known sizes enter, so no device->host sync is needed.
+// waves streams one split of a unit, and PKV_DECODE_WG_PER_CU workgroups fit
+// on a compute unit at once (the kernels' register budget), so the grid runs
+// in "rounds" of num_cus * PKV_DECODE_WG_PER_CU workgroups.  For each split
+// count the planner estimates the time as rounds * (pages per wave + a fixed
+// per-workgroup cost) and keeps the cheapest (fewest splits on ties).
+// Splits are 4*PKV_DECODE_MIN_PPW .. 256 pages long (at most 64 pages per
+// wave: one VGPR of page ids), in multiples of 4 pages (one share per wave).
+// Only host-known sizes enter, so no device->host sync is needed.
 DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus) {
   DecodePlan p{};
   const int max_pages = max(1, (max_context_len + kPage - 1) / kPage);
   const int units = max(1, B * Hkv);
-  const int target_wgs = PKV_DECODE_WG_PER_CU * max(1, num_cus);
-  int splits = (target_wgs + units - 1) / units;
+  const int64_t slots = (int64_t)PKV_DECODE_WG_PER_CU * max(1, num_cus);
   const int min_pps = PKV_DECODE_MIN_PPW * kWaves;
   const int max_pps = kMaxPagesPerWave * kWaves;
-  int pps = (max_pages + splits - 1) / splits;
-  pps = (pps + kWaves - 1) / kWaves * kWaves;
-  if (pps < min_pps) pps = min_pps;
-  if (pps > max_pps) pps = max_pps;
-  splits = (max_pages + pps - 1) / pps;
-  if (splits < 1) splits = 1;
-  p.splits = splits;
-  p.pages_per_split = pps;
-  if (splits > 1) {
-    p.ws_ml_bytes = align256((size_t)B * Hq * splits * sizeof(float2));
-    p.ws_acc_bytes = align256((size_t)B * Hq * splits * kD * sizeof(float));
+  int best_s = 1, best_pps = 0;
+  int64_t best_cost = -1;
+  int last_pps = -1;
+  for (int s_try = 1; s_try <= max_pages; ++s_try) {
+    int pps = (max_pages + s_try - 1) / s_try;
+    pps = (pps + kWaves - 1) / kWaves * kWaves;
+    if (pps > max_pps) continue;
+    if (pps < min_pps) pps = min_pps;
+    if (pps == last_pps) continue;
+    last_pps = pps;
+    const int splits = (max_pages + pps - 1) / pps;
+    const int64_t rounds = ((int64_t)units * splits + slots - 1) / slots;
+    const int64_t cost = rounds * (pps / kWaves + PKV_DECODE_WG_COST_PAGES);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_s = splits; best_pps = pps; }
+    if (pps == min_pps) break;
+  }
+  p.splits = best_s;
+  p.pages_per_split = best_pps;
+  if (best_s > 1) {
+    p.ws_ml_bytes = align256((size_t)B * Hq * best_s * 2 * sizeof(float));
+    p.ws_acc_bytes = align256((size_t)B * Hq * best_s * kD * sizeof(float));
     p.ws_counter_bytes = align256((size_t)B * Hkv * sizeof(int));
   }
   p.ws_bytes = p.ws_ml_bytes + p.ws_acc_bytes + p.ws_counter_bytes;
