@@ -207,7 +207,8 @@ def run(args):
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
                 bd.pkv_attn_prefill_chunk(qb["op"], qb["qp"], plan.cu_q, d.k_cache, d.v_cache,
                                           plan.bt_prefill, plan.ctx_prefill, plan.max_q_len,
-                                          plan.max_ctx_prefill, plan.scale, stream=stream)
+                                          plan.max_ctx_prefill, plan.scale,
+                                          workspace=plan.prefill_workspace, stream=stream)
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     pre_events.append((k, e0, e1))

@@ -138,6 +138,14 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace for pkv_attn_prefill_chunk: bytes of device memory the call needs
+ * for this shape (0 when it runs without key splits).  Depends on the current
+ * device's compute-unit count.  0 for unsupported shapes as well.
+ */
+size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int32_t Hkv,
+                                   int32_t D, int32_t max_context_len);
+
+/*
  * Causal chunked-prefill attention ([P1] model.py forward with T > 1: mask
  * kpos <= qpos on absolute positions; [P1] "Why chunked prefill": prompt
  * chunks of up to 512 tokens).  Sequence b owns query rows
@@ -146,11 +154,18 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
  * keys 0 .. that position, read through block_tables[b] (the chunk's own K/V
  * must already be appended).  T_b > context_lens[b] makes that sequence's
  * rows NaN; a sequence whose rows fall outside [0, total_q) or number more
- * than max_q_len is skipped (its rows are left untouched).
+ * than max_q_len is skipped (its rows are left untouched).  bf16 MFMA with
+ * fp32 accumulation and fp32 softmax statistics, bf16 output.  Contexts up
+ * to 131072 tokens (longer: PKV_EUNSUPPORTED).
  *   out, q        bf16 [total_q][Hq][D]; must not overlap
  *   cu_q_lens     int32 [B+1], nondecreasing, cu_q_lens[0] = 0,
  *                 cu_q_lens[B] = total_q
  *   max_q_len     host-side upper bound of T_b
+ *   max_context_len  host-side upper bound of context_lens (plans key splits)
+ *   workspace     device buffer of at least pkv_prefill_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); zero-filled before its
+ *                 first use, left ready for the next call.  Calls that may
+ *                 overlap in time need separate workspaces.
  */
 int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            const void* k_cache, const void* v_cache,
@@ -158,7 +173,8 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            int32_t B, int32_t total_q, int32_t max_q_len,
                            int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
                            int32_t num_blocks, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, float scale, void* stream);
+                           int32_t max_context_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Thread-local message describing the last non-OK return on this thread. */
 const char* pkv_last_error(void);

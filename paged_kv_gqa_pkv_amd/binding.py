@@ -27,9 +27,10 @@ SIGNATURES = {
     "pkv_decode_num_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
+    "pkv_prefill_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                        _f, _vp]),
+                                        _f, _vp, _c_size, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -125,6 +126,19 @@ def pkv_decode_num_splits(B: int, Hq: int, Hkv: int, D: int, max_context_len: in
     return int(load().pkv_decode_num_splits(B, Hq, Hkv, D, max_context_len))
 
 
+def pkv_prefill_workspace_bytes(B: int, max_q_len: int, Hq: int, Hkv: int, D: int,
+                                max_context_len: int) -> int:
+    return int(load().pkv_prefill_workspace_bytes(B, max_q_len, Hq, Hkv, D, max_context_len))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return _p(workspace), workspace.numel() * workspace.element_size()
+
+
 def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                     v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                     max_context_len: int, scale: float, workspace: Optional[torch.Tensor] = None,
@@ -141,11 +155,7 @@ def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     nb, bs, Hkv, D2 = k_cache.shape
     if out.shape != q.shape or D2 != D or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent shapes")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous device tensor")
-        ws_ptr, ws_bytes = _p(workspace), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _ws(workspace)
     _check(load().pkv_attn_decode(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
                                   _p(context_lens), B, Hq, Hkv, D, bs, nb, block_tables.shape[1],
                                   int(max_context_len), float(scale), ws_ptr, ws_bytes,
@@ -156,8 +166,9 @@ def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.
                            k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor,
                            max_q_len: int, max_context_len: int, scale: float,
-                           stream=None) -> None:
-    """out[total_q, Hq, D] <- causal attention of the chunk rows q[total_q, Hq, D]."""
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out[total_q, Hq, D] <- causal attention of the chunk rows q[total_q, Hq, D].
+    ``workspace``: zero-filled before first use (the library keeps it so)."""
     _need(q, torch.bfloat16, "q", 3)
     _need(out, torch.bfloat16, "out", 3)
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -174,4 +185,4 @@ def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.
                                          _p(block_tables), _p(context_lens), B, total_q,
                                          int(max_q_len), Hq, Hkv, D, bs, nb,
                                          block_tables.shape[1], int(max_context_len),
-                                         float(scale), _stream(stream)))
+                                         float(scale), *_ws(workspace), _stream(stream)))

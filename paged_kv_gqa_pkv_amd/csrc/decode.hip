@@ -64,9 +64,7 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ void ws_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ws_load(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+
 
 struct DecodeArgs {
   uint16_t* out;                 // bf16 [B][Hq][D]
@@ -371,8 +369,9 @@ decode_kernel(const DecodeArgs a) {
   // Split path: the last of the sequence's non-empty splits to finish merges
   // all of them, in split order (identical whichever split finishes last).
   // The partials above were written with agent-coherent stores; waiting for
-  // their completion before the arrival is counted, and reading them back
-  // with agent-coherent loads, orders them without an L2 writeback.
+  // their completion before the arrival is counted, and an acquire fence
+  // (cache invalidate) before reading them back, orders them without an L2
+  // writeback.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
@@ -382,17 +381,19 @@ decode_kernel(const DecodeArgs a) {
              ns - 1;
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int e = tid; e < G * kD; e += kWaves * kWave) {
     const int j = e / kD, d = e % kD;
     const int64_t rs = ((int64_t)b * a.Hq + g * G + j) * S;
+    const float* ml = a.ws_ml + 2 * rs;
     float M = kNegInf;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ws_load(a.ws_ml + 2 * (rs + s2)));
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ml[2 * s2]);
     const float Mu = (M == kNegInf) ? 0.f : M;
     float L = 0.f, A = 0.f;
     for (int s2 = 0; s2 < ns; ++s2) {
-      const float f = fast_exp2(ws_load(a.ws_ml + 2 * (rs + s2)) - Mu);
-      L = __builtin_fmaf(ws_load(a.ws_ml + 2 * (rs + s2) + 1), f, L);
-      A = __builtin_fmaf(ws_load(a.ws_acc + (rs + s2) * kD + d), f, A);
+      const float f = fast_exp2(ml[2 * s2] - Mu);
+      L = __builtin_fmaf(ml[2 * s2 + 1], f, L);
+      A = __builtin_fmaf(a.ws_acc[(rs + s2) * kD + d], f, A);
     }
     a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = (uint16_t)f32_to_bf16_bits(A / L);
   }

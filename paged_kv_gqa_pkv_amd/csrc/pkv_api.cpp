@@ -224,12 +224,21 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                        "pkv_attn_decode");
 }
 
+size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int32_t Hkv,
+                                   int32_t D, int32_t max_context_len) {
+  if (B <= 0 || max_q_len <= 0 || max_context_len < 0 ||
+      check_geometry(Hq, Hkv, D, PKV_BLOCK_SIZE) != PKV_OK)
+    return 0;
+  return pkv::plan_prefill(B, max_q_len, Hq, Hkv, max_context_len, device_cus()).ws_bytes;
+}
+
 int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
                            const int32_t* context_lens, int32_t B, int32_t total_q,
                            int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, float scale, void* stream) {
+                           int32_t max_context_len, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
@@ -244,6 +253,15 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
     return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
                 max_context_len, max_blocks_per_seq);
   if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
+  if (max_q_len == 0) return PKV_OK;
+  const pkv::PrefillPlan plan =
+      pkv::plan_prefill(B, max_q_len, Hq, Hkv, max_context_len, device_cus());
+  if (!plan.ok)
+    return fail(PKV_EUNSUPPORTED, "max_context_len=%d exceeds the prefill kernel's 131072 keys",
+                max_context_len);
+  if (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace))
+    return fail(PKV_EWORKSPACE, "prefill needs %zu workspace bytes, got %zu", plan.ws_bytes,
+                workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validate_mode()) {
     std::vector<int32_t> cu, ctx;
@@ -265,7 +283,8 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
   }
   return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables,
                                            context_lens, B, total_q, max_q_len, Hq, Hkv,
-                                           num_blocks, max_blocks_per_seq, scale, s),
+                                           num_blocks, max_blocks_per_seq, scale, plan, workspace,
+                                           s),
                        "pkv_attn_prefill_chunk");
 }
 

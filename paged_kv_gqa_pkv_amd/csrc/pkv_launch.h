@@ -32,10 +32,25 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          int Hkv, int num_blocks, int max_blocks, float scale,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
 
+// Key-split plan of a prefill call: row tiles of 128 (token, head) rows,
+// key ranges of tiles_per_split 64-key tiles.
+struct PrefillPlan {
+  bool ok;                  // false: the context is longer than the kernel supports
+  int qtiles;
+  int splits;
+  int tiles_per_split;
+  size_t ws_acc_bytes;      // float [groups][S][D][128]
+  size_t ws_ml_bytes;       // float [groups][S][128][2]
+  size_t ws_counter_bytes;  // int [groups]
+  size_t ws_bytes;          // total, 0 without splits
+};
+
+PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_len, int num_cus);
+
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
                           const void* v_cache, const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale,
-                          hipStream_t stream);
+                          const PrefillPlan& plan, void* workspace, hipStream_t stream);
 
 }  // namespace pkv

@@ -10,10 +10,17 @@
 // Decomposition.  The G = Hq/Hkv query heads of one KV head are stacked as
 // extra rows (row R <-> token R / G, head R % G), so each K/V tile is used by
 // all of them.  A workgroup of 4 waves owns 128 such rows of one (sequence,
-// KV head); each wave owns 32 rows.  Keys are walked in tiles of 64 (four
-// pages, gathered through the block table) that all 4 waves share through
-// LDS, double-buffered so the next tile's global loads overlap the current
-// tile's MFMA work.
+// KV head) and one range of key tiles; each wave owns 32 rows.  Keys are
+// walked in tiles of 64 (four pages, gathered through the block table) that
+// the 4 waves share through LDS.  Tiles arrive by direct global->LDS loads
+// (global_load_lds_dwordx4, one page per wave) into a ring of LDS stages,
+// up to two tiles ahead of the MFMA work, so no registers hold data in
+// flight.  LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled
+// by row, which keeps the K reads (b128) and the V transpose reads free of
+// bank conflicts without padding.  When there are too few row
+// tiles to fill the chip, the key range is cut into splits; each split writes
+// its unnormalised (m, l, O) and the last split of a row tile to finish
+// merges them in split order (as the decode kernel does).
 //
 // Per tile and wave, on v_mfma_f32_32x32x16_bf16:
 //   S^T[keys x rows] = K[keys x D] . Q^T[D x rows]   (2 key blocks x 8 k-steps)
@@ -22,8 +29,15 @@
 // so the row max is a lane-local max plus one exchange with lane ^ 32, and
 // the S^T accumulator registers are already the B operand of the PV product
 // (the k index order inside an MFMA is free as long as both operands agree).
+// The V^T operand comes straight from the row-major V tile through the LDS
+// transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane i receives
+// element i%4 of the four 4-element rows addressed by lanes i/4 + 4k, so
+// pointing lane j+4k at V[key_k][d0+4j] hands lane i the column
+// V[key_0..3][d0+i].
 // Softmax statistics stay in fp32; P is rounded to bf16 only as an MFMA
-// operand, and the row sums use the same rounded values.
+// operand, and the row sums use the same rounded values.  The running max is
+// raised lazily (only when a row's max grows by more than 2^8), which keeps
+// every exponent <= 2^8 and skips most accumulator rescales.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -31,13 +45,39 @@ namespace pkv {
 
 namespace {
 
+#ifndef PKV_PREFILL_WG_PER_CU
+#define PKV_PREFILL_WG_PER_CU 1     // key-split planner: workgroups resident per CU
+#endif
+#ifndef PKV_PREFILL_MIN_TILES
+#define PKV_PREFILL_MIN_TILES 2     // key-split planner: minimum tiles per split
+#endif
+#ifndef PKV_PREFILL_WG_COST_TILES
+#define PKV_PREFILL_WG_COST_TILES 3   // planner: fixed workgroup cost, in tile-times
+#endif
+#ifndef PKV_PREFILL_MERGE_COST_TILES
+#define PKV_PREFILL_MERGE_COST_TILES 6  // planner: split-merge cost, in tile-times
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;   // 128
 constexpr int kTileKeys = 64;                       // 4 pages
-constexpr int kKStride = kD * 2 + 16;               // bytes per LDS key row (padded)
-constexpr int kTileBytes = kTileKeys * kKStride;    // one K or V tile in LDS
+constexpr int kRowBytes = kD * 2;                   // 256 B per key row in LDS
+constexpr int kTileBytes = kTileKeys * kRowBytes;   // 16 KB per K or V tile
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 3        // LDS ring depth (tiles in flight + 1)
+#endif
+#ifndef PKV_PREFILL_WAVES_PER_SIMD
+#define PKV_PREFILL_WAVES_PER_SIMD 1  // register budget target
+#endif
+constexpr int kStages = PKV_PREFILL_STAGES;
+constexpr int kMaxTilesPerSplit = 64;               // page ids of a split fit in LDS
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.f;               // log2 units
+constexpr int kMaxSplits = 32;                      // key splits per row tile (plan cap)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct PrefillArgs {
   uint16_t* out;                 // bf16 [total_q][Hq][D]
@@ -47,72 +87,79 @@ struct PrefillArgs {
   const u32x4* v_cache;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
-  int B, total_q, max_q_len, Hq, Hkv, G, num_blocks, max_blocks, qtiles;
+  float* ws_acc;                 // [groups][splits][D][128 rows]
+  float* ws_ml;                  // [groups][splits][128 rows][2]
+  int* counters;                 // [groups]; zero between calls
+  int B, total_q, max_q_len, Hq, Hkv, G, num_blocks, max_blocks, qtiles, splits,
+      tiles_per_split;
   float scale_log2;
 };
 
-// One thread's share of a tile: 4 chunks of K and 4 of V (16 B each).
-struct TileRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
+// Chunk swizzle of an LDS key row: logical 16-byte chunk c of row r sits at
+// position c ^ sw(r).  sw keeps chunk pairs (2m, 2m+1) together and gives
+// rows 0..15 sixteen distinct values.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// Thread t loads chunk (t & 15) of key rows (t >> 4) + 16*i, i = 0..3, so 16
-// consecutive threads read one 256-byte row.  Keys at or past `n` (the
-// context length) or past the table are zero-filled: they are always masked,
-// and zeros keep canary NaNs out of the products.
-__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillArgs& a, const int32_t* bt,
-                                          int key0, int n, int g, int tid, int& bad) {
-  const int chunk = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = key0 + (tid >> 4) + 16 * i;
-    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (key < n) {
-      int blk = bt[key >> 4];
-      if (blk < 0 || blk >= a.num_blocks) { bad = 1; blk = 0; }
-      const int64_t idx = (((int64_t)blk * kPage + (key & 15)) * a.Hkv + g) * 16 + chunk;
-      kv = __builtin_nontemporal_load(a.k_cache + idx);
-      vv = __builtin_nontemporal_load(a.v_cache + idx);
-    }
-    r.k[i] = kv;
-    r.v[i] = vv;
-  }
+// Direct global->LDS copy of 16 bytes per lane: lane i writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16).  Issued as inline asm so that the compiler
+// does not wait for it before unrelated LDS reads; completion is awaited
+// explicitly with s_waitcnt vmcnt before the tile is read.
+__device__ __forceinline__ void dma16(const u32x4* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory");
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& r, char* ks, char* vs, int tid) {
-  const int chunk = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = (tid >> 4) + 16 * i;
-    *reinterpret_cast<u32x4*>(ks + key * kKStride + chunk * 16) = r.k[i];
-    *reinterpret_cast<u32x4*>(vs + key * kKStride + chunk * 16) = r.v[i];
-  }
+// 32-bit LDS byte offset of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_offset(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-__global__ void __launch_bounds__(kWaves * kWave)
+// Wait until at most n vector-memory operations of this wave are in flight
+// (n in {0, 8, 16, 24}: the DMA loads of 0 .. 3 later tiles).
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 24)
+    __builtin_amdgcn_s_waitcnt((24 & 0xF) | ((24 >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  else if (n >= 16)
+    __builtin_amdgcn_s_waitcnt((16 & 0xF) | ((16 >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  else if (n >= 8)
+    __builtin_amdgcn_s_waitcnt(8 | (0x7 << 4) | (0xF << 8));
+  else
+    __builtin_amdgcn_s_waitcnt(0x7 << 4 | (0xF << 8));
+}
+
+__device__ __forceinline__ void ws_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void __launch_bounds__(kWaves * kWave, PKV_PREFILL_WAVES_PER_SIMD)
 prefill_kernel(const PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_k[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) char s_v[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char s_k[kStages][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char s_v[kStages][kTileBytes];
+  __shared__ int s_ids[kMaxTilesPerSplit * 4];
   __shared__ int s_bad;
+  __shared__ int s_last;
 
-  const int bid = blockIdx.x;                 // ((b * qtiles) + x) * Hkv + g
+  // ((b * qtiles + x) * splits + ks) * Hkv + g: the KV head varies fastest, so
+  // all workgroups of KV head g land on XCD g % 8 and share its L2.
+  const int bid = blockIdx.x;
   const int g = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
+  int rest = bid / a.Hkv;
+  const int ks = rest % a.splits;
+  rest /= a.splits;
   const int x = a.qtiles - 1 - (rest % a.qtiles);   // heaviest (latest) row tiles first
   const int b = rest / a.qtiles;
+  const int group = (b * a.qtiles + x) * a.Hkv + g;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int G = a.G;
 
-  const int q_lo_raw = a.cu_q[b];
-  const int T_raw = a.cu_q[b + 1] - q_lo_raw;
+  const int q_lo = a.cu_q[b];
+  const int T = a.cu_q[b + 1] - q_lo;
   const int n = a.ctx_lens[b];
   // Rows outside [0, total_q) or more than max_q_len of them: nothing is read
   // or written for this sequence (its rows, if any exist, are not ours).
-  if (q_lo_raw < 0 || T_raw < 0 || q_lo_raw + T_raw > a.total_q || T_raw > a.max_q_len) return;
-  const int q_lo = q_lo_raw, T = T_raw;
+  if (q_lo < 0 || T < 0 || q_lo + T > a.total_q || T > a.max_q_len) return;
   const int R0 = x * kRowsPerWG;
   if (R0 >= T * G) return;                    // uniform over the workgroup
   const bool bad_len = T > n || n > a.max_blocks * kPage;
@@ -124,25 +171,94 @@ prefill_kernel(const PrefillArgs a) {
   const int qpos = row_ok ? n - T + t_row : -1;
   const int half = lane >> 5;                 // which 8 of 16 k values the lane holds
 
-  // Q^T as the B operand: lane holds Q[row][16ks + 8*half .. +8], ks = 0..7.
+  // Keys this workgroup needs: 0 .. the last position of its rows; this
+  // split's share of the key tiles.
+  const int t_last = min(T - 1, (R0 + kRowsPerWG - 1) / G);
+  const int key_end = bad_len ? 0 : n - T + t_last + 1;
+  const int n_tiles = (key_end + kTileKeys - 1) / kTileKeys;
+  const int ns = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;   // non-empty splits
+  const int tile0 = ks * a.tiles_per_split;
+  const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
+  if (tile0 >= tile1) {
+    if (ks == 0 && row_ok) {                  // bad length: no keys at all -> NaN rows
+      uint32_t* orow = reinterpret_cast<uint32_t*>(
+          a.out + ((int64_t)(q_lo + t_row) * a.Hq + g * G + j_row) * kD);
+      for (int i = half; i < kD / 2; i += 2) orow[i] = 0x7fc07fc0u;
+    }
+    return;
+  }
+  const int nt = tile1 - tile0;               // <= kMaxTilesPerSplit by the plan
+  const int qpos_min = n - T + R0 / G;        // smallest position in the workgroup
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+
+  // Page ids of this split's tiles into LDS (0 for pages the workgroup does
+  // not need); invalid ids of needed pages poison the result.
+  int bad = 0;
+  for (int p = tid; p < nt * 4; p += kWaves * kWave) {
+    const int page = tile0 * 4 + p;
+    int id = 0;
+    if (page * kPage < key_end && page < a.max_blocks) {
+      id = bt[page];
+      if (id < 0 || id >= a.num_blocks) { bad = 1; id = 0; }
+    }
+    s_ids[p] = id;
+  }
+
+  // Q^T as the B operand: lane holds Q[row][16kk + 8*half .. +8], kk = 0..7.
   bf16x8 qb[8];
   {
     const u32x4* qp = a.q + ((int64_t)(q_lo + t_row) * a.Hq + g * G + j_row) * 16;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int kk = 0; kk < 8; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok && !bad_len) v = qp[2 * ks + half];
-      qb[ks] = __builtin_bit_cast(bf16x8, v);
+      if (row_ok && !bad_len) v = qp[2 * kk + half];
+      qb[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  __syncthreads();
 
-  // Keys this workgroup needs: 0 .. the last position of its rows.
-  const int t_last = min(T - 1, (R0 + kRowsPerWG - 1) / G);
-  const int key_end = bad_len ? 0 : n - T + t_last + 1;
-  const int n_tiles = (key_end + kTileKeys - 1) / kTileKeys;
-  const int t_first = R0 / G;
-  const int qpos_min = n - T + t_first;       // smallest position in the workgroup
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  // DMA of tile i (relative) into stage i % 3: wave w copies page w of the
+  // tile, 4 instructions of 4 rows for K and for V.  Lane l of instruction q
+  // fills row 16w + 4q + l/16 at chunk position l%16 with logical chunk
+  // (l%16) ^ sw(row).
+  const uint32_t k_lds = lds_offset(&s_k[0][0]);
+  const uint32_t v_lds = lds_offset(&s_v[0][0]);
+  const int dma_r16 = lane >> 4;              // + 4q: row within the page
+  auto issue = [&](int i) {
+    const int stage = i % kStages;
+    const int64_t blk = __builtin_amdgcn_readfirstlane(s_ids[4 * i + w]);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int r16 = 4 * qd + dma_r16;
+      const int c = (lane & 15) ^ swz(r16);
+      const int64_t idx = ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
+      const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
+      dma16(a.k_cache + idx, k_lds + off);
+      dma16(a.v_cache + idx, v_lds + off);
+    }
+  };
+
+  // Lane read offsets.  K (A operand of S^T): row lane%32 (+32 per key
+  // block), logical chunk 2kk + half.  V (transpose reads): row
+  // 8p + 4half + m/4 (+32kb + 16hh), dims 32db + 16*(lane/16 % 2) + 4*(m%4).
+  int kaddr[8];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kaddr[kk] = r * kRowBytes + (((2 * kk + half) ^ swz(r)) << 4);
+  }
+  int vaddr[2][4];
+  {
+    const int m = lane & 15, k4 = m >> 2, j = m & 3, dh = (lane >> 4) & 1;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int r = 8 * p + 4 * half + k4;
+        const int c = 4 * db + 2 * dh + (j >> 1);
+        vaddr[p][db] = r * kRowBytes + ((c ^ swz(r)) << 4) + (j & 1) * 8;
+      }
+  }
 
   f32x16 o[4];
 #pragma unroll
@@ -150,64 +266,76 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m = kNegInf, l = 0.f;
-  int bad = 0;
 
-  TileRegs tr;
-  if (n_tiles > 0) {
-    load_tile(tr, a, bt, 0, key_end, g, tid, bad);
-    store_tile(tr, s_k[0], s_v[0], tid);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nt) issue(i);
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int cur = it & 1;
-    const int key0 = it * kTileKeys;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(tr, a, bt, key0 + kTileKeys, key_end, g, tid, bad);
+  for (int i = 0; i < nt; ++i) {
+    const int stage = i % kStages;
+    const int key0 = (tile0 + i) * kTileKeys;
+    if (i + kStages - 1 < nt) issue(i + kStages - 1);
+    wait_vm(8 * min(kStages - 1, nt - 1 - i));
+    __syncthreads();                          // every wave's page of tile i has landed
 
-    const char* ks = s_k[cur];
-    const char* vs = s_v[cur];
+    const char* ksm = s_k[stage];
+    const char* vsm = s_v[stage];
+    if (key0 + kTileKeys > key_end) {
+      // Keys past key_end are always masked; zero their V rows so the canary
+      // NaNs of unwritten slots cannot reach the products (K is masked).
+      char* vz = s_v[stage];
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      for (int e = tid; e < kTileKeys * 16; e += kWaves * kWave) {
+        const int r = e >> 4;
+        if (key0 + r >= key_end) *reinterpret_cast<u32x4*>(vz + r * kRowBytes + (e & 15) * 16) = zero;
+      }
+      __syncthreads();
+    }
 
     // S^T = K . Q^T for the two 32-key blocks of the tile.
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const char* krow = ks + (kb * 32 + (lane & 31)) * kKStride + half * 16;
+      for (int ii = 0; ii < 16; ++ii) s[kb][ii] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + kk * 32);
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(ksm + kaddr[kk] + kb * 32 * kRowBytes);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], s[kb], 0, 0, 0);
       }
     }
 
-    // Scale, causal mask, running max.  Accumulator i of block kb holds key
-    // key0 + 32*kb + 8*(i/4) + 4*half + i%4.
+    // Scale, causal mask, running max.  Accumulator ii of block kb holds key
+    // key0 + 32*kb + 8*(ii/4) + 4*half + ii%4.
     const bool need_mask = key0 + kTileKeys - 1 > qpos_min;
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[kb][i] * a.scale_log2;
+      for (int ii = 0; ii < 16; ++ii) {
+        float v = s[kb][ii] * a.scale_log2;
         if (need_mask) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          const int key = key0 + 32 * kb + 8 * (ii >> 2) + 4 * half + (ii & 3);
           v = key <= qpos ? v : kNegInf;
         }
-        s[kb][i] = v;
+        s[kb][ii] = v;
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float mu = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - mu);
-    m = m_new;
-    l *= alpha;
+    // Raise the running max only when it grows by more than the slack (or on
+    // the first visible key); exponents stay <= 2^slack.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        for (int ii = 0; ii < 16; ++ii) o[db][ii] *= alpha;
+    }
+    const float mu = (m == kNegInf) ? 0.f : m;
 
     // P^T in bf16: B operand of the PV product, k-step (kb, hh) = registers
     // 8*hh .. 8*hh+7 of block kb.
@@ -215,35 +343,29 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const __bf16 p = (__bf16)fast_exp2(s[kb][i] - mu);
-        pb[kb][i >> 3][i & 7] = p;
+      for (int ii = 0; ii < 16; ++ii) {
+        const __bf16 p = (__bf16)fast_exp2(s[kb][ii] - mu);
+        pb[kb][ii >> 3][ii & 7] = p;
         l += (float)p;
       }
 
-    // O^T += V^T . P^T.  The A operand for dim block db, k-step (kb, hh):
-    // lane holds V[key][32*db + lane%32] for the 8 keys
-    // key0 + 32*kb + 16*hh + 8*(e/4) + 4*half + e%4, e = 0..7.
-    const uint16_t* vcol = reinterpret_cast<const uint16_t*>(vs) + (lane & 31);
+    // O^T += V^T . P^T.  A operand for dim block db, k-step (kb, hh): the lane
+    // needs V[key][32*db + lane%32] for the keys
+    // 32*kb + 16*hh + 8*(e/4) + 4*half + e%4, e = 0..7: two transpose reads.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int kbase = 32 * kb + 16 * hh + 4 * half;
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          bf16x8 va;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = kbase + 8 * (e >> 2) + (e & 3);
-            va[e] = __builtin_bit_cast(__bf16, vcol[key * (kKStride / 2) + 32 * db]);
-          }
+          const char* vb = vsm + (32 * kb + 16 * hh) * kRowBytes;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[0][db]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[1][db]));
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hh], o[db], 0, 0, 0);
         }
-      }
-
-    if (more) store_tile(tr, s_k[cur ^ 1], s_v[cur ^ 1], tid);
-    __syncthreads();
+    __syncthreads();                          // stage i may be refilled from here on
   }
 
   // Row sums: each half of the lanes summed its own keys.
@@ -252,33 +374,173 @@ prefill_kernel(const PrefillArgs a) {
   __syncthreads();
   if (bad) s_bad = 1;
   __syncthreads();
-  if (!row_ok) return;
   const bool poisoned = bad_len || s_bad;
-  const float inv = 1.f / l;
-  uint32_t* orow = reinterpret_cast<uint32_t*>(
-      a.out + ((int64_t)(q_lo + t_row) * a.Hq + g * G + j_row) * kD);
-  // O^T accumulator i of dim block db holds dim 32*db + 8*(i/4) + 4*half + i%4.
+  const float nan = __builtin_nanf("");
+
+  if (a.splits == 1) {
+    if (!row_ok) return;
+    const float inv = 1.f / l;
+    uint32_t* orow = reinterpret_cast<uint32_t*>(
+        a.out + ((int64_t)(q_lo + t_row) * a.Hq + g * G + j_row) * kD);
+    // O^T accumulator i of dim block db holds dim 32*db + 8*(i/4) + 4*half + i%4.
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = 32 * db + 8 * i4 + 4 * half;
+        uint32_t w0 = pack_bf16x2(o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv);
+        uint32_t w1 = pack_bf16x2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv);
+        if (poisoned) { w0 = 0x7fc07fc0u; w1 = 0x7fc07fc0u; }
+        orow[d0 / 2] = w0;
+        orow[d0 / 2 + 1] = w1;
+      }
+    return;
+  }
+
+  // Split path: write this split's unnormalised state for the workgroup's
+  // rows with agent-coherent stores (dim-major, so a store instruction covers
+  // 32 consecutive rows), count the arrival, and let the last split of the
+  // row tile merge all of them in split order.
+  const int lrow = w * kRowsPerWave + (lane & 31);          // row within the tile
+  const int64_t sbase = (int64_t)group * a.splits + ks;     // (group, split)
+  float* pacc = a.ws_acc + sbase * kD * kRowsPerWG + lrow;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = 32 * db + 8 * i4 + 4 * half;
-      float v0 = o[db][4 * i4 + 0] * inv, v1 = o[db][4 * i4 + 1] * inv;
-      float v2 = o[db][4 * i4 + 2] * inv, v3 = o[db][4 * i4 + 3] * inv;
-      uint32_t w0 = pack_bf16x2(v0, v1), w1 = pack_bf16x2(v2, v3);
-      if (poisoned) { w0 = 0x7fc07fc0u; w1 = 0x7fc07fc0u; }
-      orow[d0 / 2] = w0;
-      orow[d0 / 2 + 1] = w1;
+    for (int i = 0; i < 16; ++i) {
+      const int d = 32 * db + 8 * (i >> 2) + 4 * half + (i & 3);
+      ws_store(pacc + d * kRowsPerWG, poisoned ? nan : o[db][i]);
     }
+  if (half == 0) {
+    ws_store(a.ws_ml + 2 * (sbase * kRowsPerWG + lrow), m);
+    ws_store(a.ws_ml + 2 * (sbase * kRowsPerWG + lrow) + 1, poisoned ? nan : l);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int* counter = a.counters + group;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             ns - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // Merge.  The acquire fence drops stale cache lines, so plain (batched)
+  // loads see the other splits' agent-coherent stores.  (1) Per row, the
+  // split weights exp2(m_s - M) / L go to LDS.  (2) Thread (rows 4q..4q+3,
+  // dims dg + 8j) accumulates 16-byte loads over the splits in order.  (3)
+  // The bf16 tile is staged in LDS and written out in 16-byte row chunks.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int64_t g0 = (int64_t)group * a.splits;
+  float* fbuf = reinterpret_cast<float*>(&s_v[0][0]);       // [kMaxSplits][128], 16 KB
+  if (tid < kRowsPerWG) {
+    const float* ml = a.ws_ml + 2 * (g0 * kRowsPerWG + tid);
+    float M = kNegInf;
+    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ml[2 * s2 * kRowsPerWG]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float L = 0.f;
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const float f = fast_exp2(ml[2 * s2 * kRowsPerWG] - Mu);
+      fbuf[s2 * kRowsPerWG + tid] = f;
+      L = __builtin_fmaf(ml[2 * s2 * kRowsPerWG + 1], f, L);
+    }
+    const float inv = 1.f / L;
+    for (int s2 = 0; s2 < ns; ++s2) fbuf[s2 * kRowsPerWG + tid] *= inv;
+  }
+  __syncthreads();
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(&s_k[0][0]);  // [128][kD + 8], 34 KB
+  constexpr int kOStride = kD + 8;
+  {
+    const int rq = tid & 31, dg = tid >> 5;
+    const float* accb = a.ws_acc + g0 * kD * kRowsPerWG + 4 * rq;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      f32x4 acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < ns; ++s2) {
+        f32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int d = dg + 8 * (8 * pass + k);
+          v[k] = *reinterpret_cast<const f32x4*>(accb + ((int64_t)s2 * kD + d) * kRowsPerWG);
+        }
+        const f32x4 f = *reinterpret_cast<const f32x4*>(fbuf + s2 * kRowsPerWG + 4 * rq);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[k][e] = __builtin_fmaf(v[k][e], f[e], acc[k][e]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = dg + 8 * (8 * pass + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          obuf[(4 * rq + e) * kOStride + d] = (uint16_t)f32_to_bf16_bits(acc[k][e]);
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < kRowsPerWG * (kD / 8); c += kWaves * kWave) {
+    const int r = c / (kD / 8), ch = c % (kD / 8);
+    const int mrow = R0 + r, mt = mrow / G, mj = mrow % G;
+    if (mt < T) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + r * kOStride + ch * 8);
+      reinterpret_cast<u32x4*>(a.out + ((int64_t)(q_lo + mt) * a.Hq + g * G + mj) * kD)[ch] = v;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
+
+// Key-split planner.  Row tiles x KV heads x sequences give the "groups";
+// each group's key range is cut into splits of tiles_per_split 64-key tiles.
+// The grid runs in rounds of num_cus * PKV_PREFILL_WG_PER_CU workgroups; for
+// every split count the planner estimates rounds * (tiles per split + a fixed
+// workgroup cost) plus a merge cost when the key range is split, and keeps
+// the cheapest (fewest splits on ties).  Host-known bounds only.
+PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_len,
+                         int num_cus) {
+  PrefillPlan p{};
+  const int G = Hq / Hkv;
+  p.qtiles = max(1, (max_q_len * G + kRowsPerWG - 1) / kRowsPerWG);
+  const int64_t groups = (int64_t)B * p.qtiles * Hkv;
+  const int max_tiles = max(1, (max_context_len + kTileKeys - 1) / kTileKeys);
+  const int64_t slots = (int64_t)PKV_PREFILL_WG_PER_CU * max(1, num_cus);
+  int best_s = 0, best_tps = 0;
+  int64_t best_cost = -1;
+  int last_tps = -1;
+  for (int s_try = 1; s_try <= kMaxSplits; ++s_try) {
+    int tps = (max_tiles + s_try - 1) / s_try;
+    if (tps > kMaxTilesPerSplit) continue;
+    if (tps < PKV_PREFILL_MIN_TILES && s_try > 1) break;
+    if (tps == last_tps) continue;
+    last_tps = tps;
+    const int splits = (max_tiles + tps - 1) / tps;
+    const int64_t rounds = (groups * splits + slots - 1) / slots;
+    const int64_t cost = rounds * (tps + PKV_PREFILL_WG_COST_TILES) +
+                         (splits > 1 ? PKV_PREFILL_MERGE_COST_TILES : 0);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_s = splits; best_tps = tps; }
+  }
+  p.ok = best_s > 0;                       // contexts up to 32 * 64 * 64 = 131072 keys
+  p.splits = best_s > 0 ? best_s : 1;
+  p.tiles_per_split = best_s > 0 ? best_tps : max_tiles;
+  if (p.ok && p.splits > 1) {
+    p.ws_acc_bytes = align256((size_t)groups * p.splits * kRowsPerWG * kD * sizeof(float));
+    p.ws_ml_bytes = align256((size_t)groups * p.splits * kRowsPerWG * 2 * sizeof(float));
+    p.ws_counter_bytes = align256((size_t)groups * sizeof(int));
+  }
+  p.ws_bytes = p.ws_acc_bytes + p.ws_ml_bytes + p.ws_counter_bytes;
+  return p;
+}
 
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
                           const void* v_cache, const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale,
-                          hipStream_t stream) {
+                          const PrefillPlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0 || total_q == 0 || max_q_len == 0) return hipSuccess;
   PrefillArgs a;
   a.out = static_cast<uint16_t*>(out);
@@ -288,12 +550,20 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.v_cache = static_cast<const u32x4*>(v_cache);
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
+  char* ws = static_cast<char*>(workspace);
+  const bool split = plan.splits > 1;
+  a.ws_acc = split ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_ml = split ? reinterpret_cast<float*>(ws + plan.ws_acc_bytes) : nullptr;
+  a.counters = split ? reinterpret_cast<int*>(ws + plan.ws_acc_bytes + plan.ws_ml_bytes)
+                     : nullptr;
   a.B = B; a.total_q = total_q; a.max_q_len = max_q_len;
   a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.num_blocks = num_blocks; a.max_blocks = max_blocks;
-  a.qtiles = (max_q_len * a.G + kRowsPerWG - 1) / kRowsPerWG;
+  a.qtiles = plan.qtiles;
+  a.splits = plan.splits;
+  a.tiles_per_split = plan.tiles_per_split;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const unsigned grid = (unsigned)((int64_t)B * a.qtiles * Hkv);
+  const unsigned grid = (unsigned)((int64_t)B * a.qtiles * a.splits * Hkv);
   hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }

@@ -43,6 +43,7 @@ class StepPlan:
     max_ctx_prefill: int
     max_ctx_decode: int
     workspace: Optional[torch.Tensor]
+    prefill_workspace: Optional[torch.Tensor]
     scale: float
 
     @property
@@ -80,15 +81,21 @@ def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = No
         nbytes = bd.pkv_decode_workspace_bytes(len(dec), w.Hq, w.Hkv, w.D, max_ctx_dec)
         if nbytes:
             ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    pws = None
+    max_q = max((w.seqs[i].new_len for i in pre), default=0)
+    max_ctx_pre = max((w.seqs[i].ctx for i in pre), default=0)
+    if pre:
+        nbytes = bd.pkv_prefill_workspace_bytes(len(pre), max_q, w.Hq, w.Hkv, w.D, max_ctx_pre)
+        if nbytes:
+            pws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return StepPlan(
         n_prefill=len(pre), n_decode=len(dec), Hq=w.Hq, Hkv=w.Hkv, D=w.D,
         block_tables=t.block_tables.to(device), context_lens=t.context_lens.to(device),
         cu_new=t.cu_new.to(device),
         slot_mapping=torch.empty(total_new, dtype=torch.int32, device=device),
         cu_q=prefill_cu(w).to(device) if pre else None,
-        max_q_len=max((w.seqs[i].new_len for i in pre), default=0),
-        max_ctx_prefill=max((w.seqs[i].ctx for i in pre), default=0),
-        max_ctx_decode=max_ctx_dec, workspace=ws,
+        max_q_len=max_q, max_ctx_prefill=max_ctx_pre,
+        max_ctx_decode=max_ctx_dec, workspace=ws, prefill_workspace=pws,
         scale=scale if scale is not None else w.D ** -0.5)
 
 
@@ -105,7 +112,8 @@ def layer(plan: StepPlan, k_cache, v_cache, k_new, v_new, q_decode=None, out_dec
     if plan.n_prefill:
         bd.pkv_attn_prefill_chunk(out_prefill, q_prefill, plan.cu_q, k_cache, v_cache,
                                   plan.bt_prefill, plan.ctx_prefill, plan.max_q_len,
-                                  plan.max_ctx_prefill, plan.scale, stream=stream)
+                                  plan.max_ctx_prefill, plan.scale,
+                                  workspace=plan.prefill_workspace, stream=stream)
     if plan.n_decode:
         bd.pkv_attn_decode(out_decode, q_decode, k_cache, v_cache, plan.bt_decode,
                            plan.ctx_decode, plan.max_ctx_decode, plan.scale,

@@ -29,7 +29,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"pkv_append", "pkv_attn_decode", "pkv_attn_prefill_chunk", "pkv_slot_mapping",
-            "pkv_decode_workspace_bytes", "pkv_last_error"} <= set(names)
+            "pkv_decode_workspace_bytes", "pkv_prefill_workspace_bytes",
+            "pkv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
         assert n in bd.SIGNATURES, f"binding lacks {n}"
@@ -89,7 +90,7 @@ def test_decode_rejects_bad_arguments(lib):
 def test_prefill_rejects_bad_arguments(lib):
     def call(out=1, q=2, B=1, total_q=8, mq=8, Hq=16, Hkv=8, D=128, bs=16, mb=4, mcl=64):
         return lib.pkv_attn_prefill_chunk(out, q, 3, 4, 5, 6, 7, B, total_q, mq, Hq, Hkv, D, bs,
-                                          32, mb, mcl, 0.088, NULL)
+                                          32, mb, mcl, 0.088, NULL, 0, NULL)
     assert call(D=256) == bd.PKV_EUNSUPPORTED
     assert call(Hq=10, Hkv=4) == bd.PKV_EUNSUPPORTED
     assert call(q=NULL) == bd.PKV_EINVAL

@@ -142,6 +142,24 @@ def test_prefill_varlen_batch():
         check_workload(w)
 
 
+def test_prefill_short_contexts_single_split():
+    """Contexts of at most 4 key tiles run without key splits."""
+    seqs = [S.SeqSpec(0, 100, True), S.SeqSpec(150, 106, True), S.SeqSpec(7, 1, False)]
+    w = S.custom_workload("short_prefill", seqs, Hq=16, Hkv=8, D=128, num_blocks=48,
+                          base_seed=97)
+    assert bd.pkv_prefill_workspace_bytes(2, 106, 16, 8, 128, 256) == 0
+    check_workload(w)
+
+
+def test_prefill_many_key_splits():
+    """A long context with few row tiles is cut into many key splits."""
+    seqs = [S.SeqSpec(6000, 64, True)]
+    w = S.custom_workload("long_prefill", seqs, Hq=32, Hkv=8, D=128, num_blocks=400,
+                          base_seed=98)
+    assert bd.pkv_prefill_workspace_bytes(1, 64, 32, 8, 128, 6064) > 0
+    check_workload(w)
+
+
 def test_ctx1_is_exact_value_row():
     w = S.custom_workload("ctx1", _seqs_decode([1, 1, 1]), Hq=16, Hkv=8, D=128, num_blocks=8,
                           base_seed=95)
