@@ -48,7 +48,42 @@ def parse():
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--no-events", action="store_true",
                    help="time steps only (no per-launch events), e.g. under a profiler")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain 1 GiB device copies (counter calibration under rocprofv3)")
     return p.parse_args()
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_gqa_pkv_amd", "csrc", "decode.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE, scaled by the same counters on a plain copy), if the record
+    matches the current decode kernel source and this workload; else None."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("decode_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "copies": 3}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -244,7 +279,8 @@ def run(args):
         byts = [parts[k].dec_bytes for (k, _, _) in dec_events]
         achieved = sum(byts) / sum(durs) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(args.workload),
                     "kernel": "decode_kernel (pkv_attn_decode)",
                     "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / len(byts)),
@@ -338,6 +374,9 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     out, parts = run(args)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(args, parts)
