@@ -105,6 +105,17 @@ __device__ __forceinline__ void load_page(PageRegs& r, const DecodeArgs& a, int6
 // Online-softmax update with U pages held in registers.  kMask: the single
 // page is the sequence's last, partially filled one; rows >= valid_rows are
 // excluded (score -inf, V forced to 0 so canary data cannot leak).
+//
+// Each lane keeps its own state (m, l, acc) over the rows it holds.  m is a
+// reference point, not the exact running max: it moves only when a score
+// exceeds it by more than kRescaleSlack (log2 units), so exp2(s - m) stays
+// below 2^kRescaleSlack and the accumulator rescale is skipped (wave-uniformly)
+// on almost every page.  The probabilities are rounded to bf16 (as the
+// attention of the pages does before its PV product) and the PV product and
+// the row sum l run on v_dot2_f32_bf16, pairing the lane's rows r0 and r0+8.
+constexpr float kRescaleSlack = 8.f;
+constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // bf16 (1, 1)
+
 template <int G, int U, bool kMask>
 __device__ __forceinline__ void process(const PageRegs (&buf)[U], const uint32_t (&qw)[G][8],
                                         float (&m)[G], float (&l)[G], float (&acc)[G][16],
@@ -127,6 +138,7 @@ __device__ __forceinline__ void process(const PageRegs (&buf)[U], const uint32_t
         if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
         s[u][rr][j] = d;
       }
+  bf16x2 pp[U][G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     float mc = s[0][0][j];
@@ -134,41 +146,41 @@ __device__ __forceinline__ void process(const PageRegs (&buf)[U], const uint32_t
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) mc = fmaxf(mc, s[u][rr][j]);
-    const float m_new = fmaxf(m[j], mc);
-    const float mu = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m[j] - mu);
-    m[j] = m_new;
-    l[j] *= alpha;
+    const bool up = mc > m[j] + kRescaleSlack;   // false while all scores are -inf
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float alpha = up ? fast_exp2(m[j] - mc) : 1.f;   // m = -inf gives 0
+      m[j] = up ? mc : m[j];
+      l[j] *= alpha;
 #pragma unroll
-    for (int d = 0; d < 16; ++d) acc[j][d] *= alpha;
+      for (int d = 0; d < 16; ++d) acc[j][d] *= alpha;
+    }
+    const float mu = (m[j] == kNegInf) ? 0.f : m[j];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const float p = fast_exp2(s[u][rr][j] - mu);
-        s[u][rr][j] = p;
-        l[j] += p;
-      }
+    for (int u = 0; u < U; ++u) {
+      pp[u][j] = bf16x2{(__bf16)fast_exp2(s[u][0][j] - mu), (__bf16)fast_exp2(s[u][1][j] - mu)};
+      l[j] = __builtin_amdgcn_fdot2_f32_bf16(pp[u][j], as_bf16x2(kBf16PairOne), l[j], false);
+    }
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    const bool keep0 = !kMask || (r0 < valid_rows);
+    const bool keep1 = !kMask || (r0 + 8 < valid_rows);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      float v[16];
-      const bool keep = !kMask || (r0 + 8 * rr < valid_rows);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = keep0 ? buf[u].v[0][h][i] : 0u;   // row r0, dims 2i, 2i+1
+        const uint32_t w1 = keep1 ? buf[u].v[1][h][i] : 0u;   // row r0 + 8
+        const bf16x2 lo = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
+        const bf16x2 hi = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
+        const int d = 8 * h + 2 * i;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = keep ? buf[u].v[rr][h][i] : 0u;
-          v[8 * h + 2 * i] = bf16lo(w);
-          v[8 * h + 2 * i + 1] = bf16hi(w);
+        for (int j = 0; j < G; ++j) {
+          acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(lo, pp[u][j], acc[j][d], false);
+          acc[j][d + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, pp[u][j], acc[j][d + 1], false);
         }
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int d = 0; d < 16; ++d) acc[j][d] = __builtin_fmaf(s[u][rr][j], v[d], acc[j][d]);
-    }
+      }
+  }
 }
 
 // Merge two online-softmax states (m in the log2 domain).
