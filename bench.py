@@ -335,7 +335,9 @@ def cpu_baseline(args, parts):
     for pt in parts[:2]:
         w, t = pt.w, pt.t
         d = S.make_layer(w, t, 0)
-        kc0, vc0, kn, vn = u16(d.k_cache), u16(d.v_cache), u16(d.k_new), u16(d.v_new)
+        # the oracle reads pools in the pages' token-major order (an axis permutation)
+        kc0, vc0 = u16(d.k_cache.transpose(1, 2).contiguous()), u16(d.v_cache.transpose(1, 2).contiguous())
+        kn, vn = u16(d.k_new), u16(d.v_new)
         qd = u16(d.q_decode) if d.q_decode is not None else None
         qp = u16(d.q_prefill) if d.q_prefill is not None else None
         bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()

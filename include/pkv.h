@@ -9,10 +9,16 @@
  *        "Paged Attention".
  *
  * Data layout (all tensors contiguous, row-major, bf16 unless stated):
- *   k_cache, v_cache   [num_blocks][block_size=16][Hkv][D]   one layer's page pool
- *                      (the per-layer slice of [P1] paged.py's
- *                      [n_layers, capacity, block_size, n_kv_heads, head_dim]:
- *                      block b at dim 0, slot s at dim 1).
+ *   k_cache, v_cache   [num_blocks][Hkv][block_size=16][D]   one layer's page pool,
+ *                      head-major inside a page: the row of (page b, KV head
+ *                      g, slot s) starts at ((b*Hkv + g)*16 + s)*D elements.
+ *                      [P1] paged.py stores the same rows token-major
+ *                      ([n_layers, capacity, block_size, n_kv_heads,
+ *                      head_dim]); the pages' entries are the rows, and this
+ *                      library keeps each (page, KV head) as 16 contiguous
+ *                      rows (4 KiB at D = 128) so attention reads whole
+ *                      contiguous blocks.  Block b and slot s mean the same
+ *                      in both orders.
  *   block_tables       int32 [B][max_blocks_per_seq]: logical page i of
  *                      sequence b lives in physical page block_tables[b][i]
  *                      ([P1] SequenceCache.blocks; [P3] page table).  Entries
@@ -88,7 +94,7 @@ int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
 /*
  * KV append ([P1] paged.py PagedKVCache.write; model.py forward writes the
  * step's K/V into the pages).  A bit-exact scatter of rows:
- *     k_cache[slot / 16][slot % 16][:][:] = k_new[t][:][:]   (same for V)
+ *     k_cache[slot / 16][g][slot % 16][:] = k_new[t][g][:]   for every KV head g (same for V)
  * for every t with 0 <= slot = slot_mapping[t] < num_blocks*16; other slots
  * (negative = padding) are skipped.  Slots must be distinct (duplicates race;
  * PKV_VALIDATE=1 rejects them).

@@ -103,7 +103,7 @@ def pkv_slot_mapping(slot_mapping: torch.Tensor, block_tables: torch.Tensor,
 
 def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
                k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
-    """Scatter k_new/v_new [T, Hkv, D] into the pools [num_blocks, 16, Hkv, D]."""
+    """Scatter k_new/v_new [T, Hkv, D] into the head-major pools [num_blocks, Hkv, 16, D]."""
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t, torch.bfloat16, n, 3)
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -112,10 +112,10 @@ def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Ten
     T, Hkv, D = k_new.shape
     nb = k_cache.shape[0]
     if v_new.shape != k_new.shape or v_cache.shape != k_cache.shape or \
-            tuple(k_cache.shape[2:]) != (Hkv, D) or slot_mapping.numel() != T:
+            k_cache.shape[1] != Hkv or k_cache.shape[3] != D or slot_mapping.numel() != T:
         raise ValueError("inconsistent shapes")
     _check(load().pkv_append(_p(k_new), _p(v_new), _p(slot_mapping), _p(k_cache), _p(v_cache),
-                             T, nb, Hkv, D, k_cache.shape[1], _stream(stream)))
+                             T, nb, Hkv, D, k_cache.shape[2], _stream(stream)))
 
 
 def pkv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: int) -> int:
@@ -152,8 +152,9 @@ def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     B, Hq, D = q.shape
-    nb, bs, Hkv, D2 = k_cache.shape
-    if out.shape != q.shape or D2 != D or block_tables.shape[0] != B or context_lens.numel() != B:
+    nb, Hkv, bs, D2 = k_cache.shape            # head-major pages
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
+            block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent shapes")
     ws_ptr, ws_bytes = _ws(workspace)
     _check(load().pkv_attn_decode(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
@@ -177,9 +178,10 @@ def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.
         _need(t, torch.int32, n, 1)
     _need(block_tables, torch.int32, "block_tables", 2)
     total_q, Hq, D = q.shape
-    nb, bs, Hkv, D2 = k_cache.shape
+    nb, Hkv, bs, D2 = k_cache.shape            # head-major pages
     B = context_lens.numel()
-    if out.shape != q.shape or D2 != D or block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
+            block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
         raise ValueError("inconsistent shapes")
     _check(load().pkv_attn_prefill_chunk(_p(out), _p(q), _p(cu_q_lens), _p(k_cache), _p(v_cache),
                                          _p(block_tables), _p(context_lens), B, total_q,

@@ -9,16 +9,18 @@
 // Decomposition.  One workgroup owns one (sequence b, KV head g, context
 // split) and serves all G = Hq/Hkv query heads of the group from the same
 // loaded K/V rows, so every K/V byte is read from HBM once per step.  The
-// workgroup's 4 waves take disjoint page ranges of the split.  Inside a wave
-// a 16-token page of one head is 16 rows of 256 B: lane l holds rows
-// (l>>3) and (l>>3)+8 and the 16-byte chunks (l&7) and (l&7)+8 of each, so
-// every load instruction moves eight full 128-byte lines.  The K/V rows stay
-// in VGPRs (no LDS staging: the reuse across the G heads happens inside each
-// lane).  Scores use v_dot2_f32_bf16 on the packed bf16 data, an 8-lane DPP
-// butterfly finishes each dot product, and an fp32 online softmax runs per
-// lane group; the lane groups, then the waves (through LDS), are merged at
-// the end with the usual max/rescale rule.  Pages are software-pipelined:
-// the next group of pages is in flight while the current one is reduced.
+// workgroup's 4 waves take disjoint page ranges of the split.  Pages are
+// stored head-major, so a 16-token page of one head is 16 contiguous rows of
+// 256 B (4 KiB): lane l holds rows (l>>3) and (l>>3)+8 and the 16-byte chunks
+// (l&7) and (l&7)+8 of each, so every load instruction moves eight full
+// 128-byte lines.  The K/V rows stay in VGPRs (no LDS staging: the reuse
+// across the G heads happens inside each lane).  Scores use v_dot2_f32_bf16
+// on the packed bf16 data and an 8-lane DPP butterfly finishes each dot
+// product; each lane keeps an online-softmax state (fp32 m, l, acc) over its
+// rows, with bf16 probabilities in the PV product.  The lane states, then the
+// waves (through LDS), are merged at the end with the usual max/rescale rule.
+// Pages are software-pipelined: the next group of pages is in flight while
+// the current one is reduced.
 //
 // Long contexts with few (sequence, head) pairs are cut into splits of
 // pages_per_split pages (flash-decoding); each split writes its unnormalised
@@ -69,7 +71,7 @@ __device__ __forceinline__ void ws_store(float* p, float v) {
 struct DecodeArgs {
   uint16_t* out;                 // bf16 [B][Hq][D]
   const u32x4* q;                // bf16 [B][Hq][D] as 16-byte chunks
-  const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D]
+  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D]
   const u32x4* v_cache;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
@@ -88,8 +90,8 @@ struct PageRegs {
 
 __device__ __forceinline__ void load_page(PageRegs& r, const DecodeArgs& a, int64_t blk, int g,
                                           int lane_off) {
-  const int64_t row_stride = (int64_t)a.Hkv * 16;             // chunks per token row
-  const int64_t base = (blk * kPage * a.Hkv + g) * 16;        // chunk 0 of row 0, head g
+  const int64_t row_stride = 16;                              // chunks per row
+  const int64_t base = (blk * a.Hkv + g) * kPage * 16;        // chunk 0 of row 0, head g
   const u32x4* kp = a.k_cache + base;
   const u32x4* vp = a.v_cache + base;
   const int o8 = (int)(8 * row_stride);
@@ -268,7 +270,7 @@ decode_kernel(const DecodeArgs a) {
     for (int d = 0; d < 16; ++d) acc[j][d] = 0.f;
   }
 
-  const int lane_off = r0 * a.Hkv * 16 + c;
+  const int lane_off = r0 * 16 + c;
   const int id_base = w0 - wp0;               // lane of my_id holding page w0
   int bad = bad_len ? 1 : 0;
   auto page_id = [&](int j) -> int64_t {

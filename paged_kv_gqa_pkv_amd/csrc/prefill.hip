@@ -83,7 +83,7 @@ struct PrefillArgs {
   uint16_t* out;                 // bf16 [total_q][Hq][D]
   const u32x4* q;                // bf16 [total_q][Hq][D] as 16-byte chunks
   const int32_t* cu_q;           // [B+1]
-  const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D]
+  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D]
   const u32x4* v_cache;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
@@ -231,7 +231,7 @@ prefill_kernel(const PrefillArgs a) {
     for (int qd = 0; qd < 4; ++qd) {
       const int r16 = 4 * qd + dma_r16;
       const int c = (lane & 15) ^ swz(r16);
-      const int64_t idx = ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
+      const int64_t idx = ((blk * a.Hkv + g) * kPage + r16) * 16 + c;
       const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
       dma16(a.k_cache + idx, k_lds + off);
       dma16(a.v_cache + idx, v_lds + off);

@@ -21,7 +21,8 @@ Shapes and structure follow the workloads the pages describe:
 Values: fp32 N(0,1) samples rounded to bf16 by round-to-nearest-even (the
 torch ``.to(torch.bfloat16)`` cast).  Unused pages and the unwritten tail
 slots of each sequence's pages hold the bf16 quiet-NaN canary 0x7FC0, so any
-read of a slot the method must not read poisons the result.
+read of a slot the method must not read poisons the result.  Pools are
+generated in the library's head-major page order [num_blocks][Hkv][16][D].
 
 Seeds: stream ``k`` of layer ``l`` of a workload with base seed ``s`` uses
 ``s * 1_000_000 + l * 100 + k``.  Streams: 0 context lengths, 1 placement,
@@ -242,7 +243,7 @@ def page_fill_counts(w: Workload, t: Tables) -> torch.Tensor:
 @dataclasses.dataclass
 class LayerData:
     """One layer's tensors for a step (all on ``device``)."""
-    k_cache: torch.Tensor        # bf16 [num_blocks, 16, Hkv, D], pre-append contents
+    k_cache: torch.Tensor        # bf16 [num_blocks, Hkv, 16, D] (head-major pages), pre-append
     v_cache: torch.Tensor
     k_new: torch.Tensor          # bf16 [T_total, Hkv, D]
     v_new: torch.Tensor
@@ -251,12 +252,12 @@ class LayerData:
 
 
 def _pool(w: Workload, fill: torch.Tensor, seed: int, device) -> torch.Tensor:
-    shape = (w.num_blocks, PAGE, w.Hkv, w.D)
+    shape = (w.num_blocks, w.Hkv, PAGE, w.D)
     pool = randn_bf16(shape, seed, device)
     slot = torch.arange(PAGE, device=device).view(1, PAGE)
     dead = slot >= fill.to(device).view(-1, 1)            # [num_blocks, 16]
     bits = pool.view(torch.int16)
-    bits.masked_fill_(dead.view(w.num_blocks, PAGE, 1, 1), BF16_CANARY_BITS)
+    bits.masked_fill_(dead.view(w.num_blocks, 1, PAGE, 1), BF16_CANARY_BITS)
     return pool
 
 
@@ -294,6 +295,6 @@ def bulk_append_inputs(n_tokens: int, num_blocks: int, Hkv: int, D: int, seed: i
     slots = torch.randperm(num_blocks * PAGE, generator=g)[:n_tokens].to(torch.int32)
     k_new = randn_bf16((n_tokens, Hkv, D), seed + 1, device)
     v_new = randn_bf16((n_tokens, Hkv, D), seed + 2, device)
-    pool_k = randn_bf16((num_blocks, PAGE, Hkv, D), seed + 3, device)
-    pool_v = randn_bf16((num_blocks, PAGE, Hkv, D), seed + 4, device)
+    pool_k = randn_bf16((num_blocks, Hkv, PAGE, D), seed + 3, device)
+    pool_v = randn_bf16((num_blocks, Hkv, PAGE, D), seed + 4, device)
     return slots, k_new, v_new, pool_k, pool_v
