@@ -50,6 +50,11 @@ def parse():
                    help="time steps only (no per-launch events), e.g. under a profiler")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 1 GiB device copies (counter calibration under rocprofv3)")
+    p.add_argument("--write-traffic-record", nargs=4,
+                   metavar=("COPY_FETCH_CSV", "COPY_WRITE_CSV", "FETCH_CSV", "WRITE_CSV"),
+                   help="CPU only: build the decode traffic record from rocprofv3 --pmc "
+                        "counter_collection.csv files (FETCH_SIZE / WRITE_SIZE of the copy "
+                        "calibration and of this workload's run)")
     return p.parse_args()
 
 
@@ -72,6 +77,48 @@ def measured_traffic(workload):
     if rec.get("decode_source_sha256") != sha or rec.get("workload") != workload:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def write_traffic_record(args):
+    """HBM bytes per decode launch from rocprofv3 counters (KiB per dispatch):
+    each counter is scaled by true bytes / counted bytes of the plain 1 GiB
+    copy, then the decode dispatches' mean FETCH and WRITE are summed."""
+    import csv
+    import hashlib
+    import statistics
+
+    def values(path, key):
+        with open(path) as f:
+            return [(r["Grid_Size"], float(r["Counter_Value"]))
+                    for r in csv.DictReader(f) if key in r["Kernel_Name"]]
+
+    copy_f, copy_w, dec_f, dec_w = args.write_traffic_record
+    true_kib = (1 << 30) / 1024
+    cf = [v for _, v in values(copy_f, "copyBuffer")]
+    cw = [v for _, v in values(copy_w, "copyBuffer")]
+    fetch_scale, write_scale = true_kib / statistics.mean(cf), true_kib / statistics.mean(cw)
+    df, dw = values(dec_f, "decode_kernel"), values(dec_w, "decode_kernel")
+    per_grid = {}
+    for grid in sorted({g for g, _ in df}):
+        f = [v for g, v in df if g == grid]
+        w = [v for g, v in dw if g == grid]
+        per_grid[grid] = {"dispatches": len(f), "fetch_kib_mean": round(statistics.mean(f), 1),
+                          "write_kib_mean": round(statistics.mean(w), 1),
+                          "bytes": round(1024 * (statistics.mean(f) * fetch_scale +
+                                                 statistics.mean(w) * write_scale))}
+    traffic = round(1024 * (statistics.mean(v for _, v in df) * fetch_scale +
+                            statistics.mean(v for _, v in dw) * write_scale))
+    with open(DECODE_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = {"kernel": "decode_kernel (pkv_attn_decode)", "workload": args.workload,
+           "decode_source_sha256": sha, "traffic_bytes_per_launch": traffic,
+           "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
+           "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                                "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw},
+           "per_grid": per_grid}
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
 
 
 def calibrate_copy():
@@ -376,6 +423,9 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.write_traffic_record:
+        write_traffic_record(args)
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return
