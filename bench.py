@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -48,6 +49,9 @@ def parse():
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--no-events", action="store_true",
                    help="time steps only (no per-launch events), e.g. under a profiler")
+    p.add_argument("--graph", action="store_true",
+                   help="capture each distinct step in a HIP graph and time graph replays "
+                        "(per-launch events then come from a separate eager pass)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 1 GiB device copies (counter calibration under rocprofv3)")
     p.add_argument("--write-traffic-record", nargs=4,
@@ -311,11 +315,43 @@ def run(args):
     for i in range(args.warmup):
         one_step(i, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(i, use_events)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.graph:
+        # One graph per distinct step: the step pattern repeats with the
+        # schedule's period times every part's number of rotated copies.
+        period = 6 if args.workload == "c5" else 1
+        for pt in parts:
+            period = period * pt.copies // math.gcd(period, pt.copies)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        eager_stream = stream
+        stream = cap
+        with torch.cuda.stream(cap):
+            for i in range(period):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    one_step(i, False)
+                graphs.append(g)
+        stream = eager_stream
+        torch.cuda.synchronize()
+        for g in graphs:          # one untimed replay each
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % period].replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        if use_events:            # per-launch durations: a separate eager pass
+            for i in range(min(args.steps, 2 * period)):
+                one_step(i, True)
+            torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            one_step(i, use_events)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
 
     total_bytes = sum(parts[k].step_bytes for i in range(args.steps) for k in schedule(i))
     dec_tokens = sum(len(parts[k].w.decode_seqs) for i in range(args.steps) for k in schedule(i))
@@ -331,7 +367,10 @@ def run(args):
                     "kernel": "decode_kernel (pkv_attn_decode)",
                     "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / len(byts)),
-                    "launches": len(durs)}
+                    "launches": len(durs),
+                    "timing": ("HIP events around eager launches, a pass after the timed graph "
+                               "replays" if args.graph else
+                               "HIP events around each launch in the timed region")}
     if pre_events:
         durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in pre_events]
         fl = [parts[k].pre_flops for (k, _, _) in pre_events]
@@ -351,7 +390,8 @@ def run(args):
                           len(p.w.decode_seqs), p.w.Hq, p.w.Hkv, p.w.D,
                           p.plan.max_ctx_decode) if p.w.decode_seqs else 0}
                      for p in parts[:2]],
-           "page_tokens": 16, "launch": "eager, one stream"}
+           "page_tokens": 16,
+           "launch": "HIP graph per step, one stream" if args.graph else "eager, one stream"}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(1e3 * elapsed / args.steps, 5),

@@ -323,3 +323,47 @@ def test_full_size_c4a_sampled():
 
 def test_full_size_c4b_sampled():
     _sampled_full_size("c4b", [(0, 0), (5, 17), (12, 31)])
+
+
+def test_graph_replays_match_eager():
+    """A whole mixed step (slot mapping, append, prefill with key splits,
+    decode with splits) captured in one HIP graph: every replay, with eager
+    work and synchronisations between replays, is bit-identical to the eager
+    step (the kernels are deterministic and leave their workspaces ready)."""
+    seqs = [S.SeqSpec(2000, 300, True), S.SeqSpec(900, 1, False), S.SeqSpec(4000, 1, False)]
+    w = S.custom_workload("graph_step", seqs, Hq=16, Hkv=8, D=128, num_blocks=480, base_seed=99)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0, device="cuda")
+    plan = ST.plan_step(w, t)
+    assert plan.prefill_workspace is not None and plan.workspace is not None
+    k0, v0 = d.k_cache.clone(), d.v_cache.clone()
+    out_d, out_p = torch.empty_like(d.q_decode), torch.empty_like(d.q_prefill)
+
+    def step(stream=None):
+        ST.slot_mapping(plan, stream=stream)
+        ST.layer(plan, d.k_cache, d.v_cache, d.k_new, d.v_new, d.q_decode, out_d,
+                 d.q_prefill, out_p, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    want_d, want_p = out_d.clone(), out_p.clone()
+    want_k = d.k_cache.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step(stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out_d.fill_(0); out_p.fill_(0)
+        d.k_cache.copy_(k0); d.v_cache.copy_(v0)      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d.view(torch.int16), want_d.view(torch.int16)), rep
+        assert torch.equal(out_p.view(torch.int16), want_p.view(torch.int16)), rep
+        assert torch.equal(d.k_cache.view(torch.int16), want_k.view(torch.int16)), rep
+        step()                                         # an eager step in between
+        torch.cuda.synchronize()
+        assert torch.equal(out_d.view(torch.int16), want_d.view(torch.int16)), rep
