@@ -141,10 +141,12 @@ def calibrate_copy():
 # algorithmic work of a step (what the method must move / compute)
 # ---------------------------------------------------------------------------
 
-def decode_bytes(w, t, rows):
+def decode_bytes(w, t, rows, kv="bf16"):
     """K/V of every token read once (pages shared by several tables counted
-    once), q in and out, the table entries and lengths."""
+    once), q in and out, the table entries and lengths.  int8 pages: one byte
+    per element plus a float32 K and V scale per (token, KV head)."""
     Hkv, D, Hq = w.Hkv, w.D, w.Hq
+    per_token = 2 * Hkv * D * 2 if kv == "bf16" else 2 * Hkv * (D + 4)
     seen = {}
     table_bytes = 0
     for i in rows:
@@ -155,7 +157,7 @@ def decode_bytes(w, t, rows):
             page = int(t.block_tables[i, j])
             seen[page] = max(seen.get(page, 0), min(16, n - 16 * j))
     kv_tokens = sum(seen.values())
-    return kv_tokens * 2 * Hkv * D * 2 + len(rows) * 2 * Hq * D * 2 + table_bytes
+    return kv_tokens * per_token + len(rows) * 2 * Hq * D * 2 + table_bytes
 
 
 def append_bytes(w, t):

@@ -182,6 +182,51 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            int32_t max_context_len, float scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * int8 KV pages ([P2] kv_cache.py listing, section 5, class KV8Cache: one
+ * byte per element plus one float32 scale per (token, KV head); [P2] closing
+ * notes: 2112 B instead of 4096 B per token-layer at H_kv 8, d_head 128).
+ * Pool layout:
+ *   k_codes, v_codes  int8 [num_blocks][Hkv][16][D], the order of the bf16
+ *                     pools; a row of codes reads back as code * scale.
+ *   kv_scales         float32 [num_blocks][Hkv][8][2][2]: the K and V scales
+ *                     of slot s of (page b, KV head g) sit at
+ *                     [b][g][s % 8][s / 8][0] and [...][1].  (The 16 slots of
+ *                     a page are kept as 8 pairs (s, s+8) so that the decode
+ *                     kernel reads the four scales of a lane's two rows in one
+ *                     16-byte load.)
+ * Unwritten slots may hold anything; a NaN scale there is never read.
+ */
+
+/*
+ * int8 append ([P2] KV8Cache.write): every row x = k_new[t][g][:] (and the
+ * V row) is quantised in float32 exactly as the page does,
+ *     scale = max_d |x_d| / 127 + 1e-8,  code_d = clip(rint(x_d / scale), -127, 127)
+ * (IEEE division, round half to even), and codes and scale are written to the
+ * slot slot_mapping[t] of every KV head g; slots outside [0, num_blocks*16)
+ * are skipped.  Inputs must be finite.  Slots must be distinct (duplicates
+ * race; PKV_VALIDATE=1 rejects them).  D must be 128.
+ *   k_new, v_new  bf16 [T][Hkv][D]
+ */
+int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    void* k_codes, void* v_codes, float* kv_scales, int32_t T,
+                    int32_t num_blocks, int32_t Hkv, int32_t D, int32_t block_size, void* stream);
+
+/*
+ * Decode attention over int8 pages ([P2] KV8Cache.read: K and V read back as
+ * code * scale, then the attention of pkv_attn_decode).  Same arguments,
+ * outputs, error behaviour, split plan and workspace as pkv_attn_decode
+ * (pkv_decode_workspace_bytes / pkv_decode_num_splits apply unchanged).
+ * Scores use q . codes times the row's K scale; the row's V scale multiplies
+ * its probability, which is rounded to bf16 for the PV product.
+ */
+int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                         const float* kv_scales, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Thread-local message describing the last non-OK return on this thread. */
 const char* pkv_last_error(void);
 

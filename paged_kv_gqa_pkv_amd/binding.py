@@ -31,6 +31,11 @@ SIGNATURES = {
     "pkv_attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                         _f, _vp, _c_size, _vp]),
+    "pkv_append_int8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _vp]),
+    "pkv_attn_decode_int8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                      _c_int, _c_int, _c_int, _c_int, _c_int, _f, _vp, _c_size,
+                                      _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -188,3 +193,52 @@ def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.
                                          int(max_q_len), Hq, Hkv, D, bs, nb,
                                          block_tables.shape[1], int(max_context_len),
                                          float(scale), *_ws(workspace), _stream(stream)))
+
+
+def pkv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                    k_codes: torch.Tensor, v_codes: torch.Tensor, kv_scales: torch.Tensor,
+                    stream=None) -> None:
+    """Quantise k_new/v_new [T, Hkv, D] into int8 pools: codes [num_blocks, Hkv, 16, D],
+    scales [num_blocks, Hkv, 8, 2, 2] (slot s of a page at [s % 8][s // 8][K, V])."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need(t, torch.int8, n, 4)
+    _need(kv_scales, torch.float32, "kv_scales", 5)
+    _need(slot_mapping, torch.int32, "slot_mapping", 1)
+    T, Hkv, D = k_new.shape
+    nb = k_codes.shape[0]
+    if v_new.shape != k_new.shape or v_codes.shape != k_codes.shape or \
+            k_codes.shape[1] != Hkv or k_codes.shape[3] != D or slot_mapping.numel() != T or \
+            tuple(kv_scales.shape) != (nb, Hkv, 8, 2, 2):
+        raise ValueError("inconsistent shapes")
+    _check(load().pkv_append_int8(_p(k_new), _p(v_new), _p(slot_mapping), _p(k_codes),
+                                  _p(v_codes), _p(kv_scales), T, nb, Hkv, D, k_codes.shape[2],
+                                  _stream(stream)))
+
+
+def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tensor,
+                         v_codes: torch.Tensor, kv_scales: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         max_context_len: int, scale: float,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out[B, Hq, D] <- decode attention of q[B, Hq, D] over int8 pools (same
+    workspace as pkv_attn_decode)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need(t, torch.int8, n, 4)
+    _need(kv_scales, torch.float32, "kv_scales", 5)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_codes.shape
+    if out.shape != q.shape or D2 != D or v_codes.shape != k_codes.shape or \
+            tuple(kv_scales.shape) != (nb, Hkv, 8, 2, 2) or \
+            block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent shapes")
+    ws_ptr, ws_bytes = _ws(workspace)
+    _check(load().pkv_attn_decode_int8(_p(out), _p(q), _p(k_codes), _p(v_codes), _p(kv_scales),
+                                       _p(block_tables), _p(context_lens), B, Hq, Hkv, D, bs, nb,
+                                       block_tables.shape[1], int(max_context_len), float(scale),
+                                       ws_ptr, ws_bytes, _stream(stream)))

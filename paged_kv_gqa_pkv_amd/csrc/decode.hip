@@ -71,8 +71,10 @@ __device__ __forceinline__ void ws_store(float* p, float v) {
 struct DecodeArgs {
   uint16_t* out;                 // bf16 [B][Hq][D]
   const u32x4* q;                // bf16 [B][Hq][D] as 16-byte chunks
-  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D]
+  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D], or int8 codes (same order)
   const u32x4* v_cache;
+  const float* kv_scales;        // int8 pages: float32 [num_blocks][Hkv][8][2][2]: the (K, V)
+                                 // scales of slot s at [s % 8][s / 8]
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
   float* ws_ml;                  // [B][Hq][S][2] (m, l), log2 domain
@@ -82,108 +84,241 @@ struct DecodeArgs {
   float scale_log2;              // scale * log2(e)
 };
 
-// K and V of one page for this lane: [row r0 / r0+8][chunk c / c+8].
-struct PageRegs {
-  u32x4 k[2][2];
-  u32x4 v[2][2];
-};
-
-__device__ __forceinline__ void load_page(PageRegs& r, const DecodeArgs& a, int64_t blk, int g,
-                                          int lane_off) {
-  const int64_t row_stride = 16;                              // chunks per row
-  const int64_t base = (blk * a.Hkv + g) * kPage * 16;        // chunk 0 of row 0, head g
-  const u32x4* kp = a.k_cache + base;
-  const u32x4* vp = a.v_cache + base;
-  const int o8 = (int)(8 * row_stride);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    r.k[0][h] = load_kv(kp + lane_off + 8 * h);
-    r.k[1][h] = load_kv(kp + lane_off + o8 + 8 * h);
-    r.v[0][h] = load_kv(vp + lane_off + 8 * h);
-    r.v[1][h] = load_kv(vp + lane_off + o8 + 8 * h);
-  }
-}
-
-// Online-softmax update with U pages held in registers.  kMask: the single
-// page is the sequence's last, partially filled one; rows >= valid_rows are
-// excluded (score -inf, V forced to 0 so canary data cannot leak).
-//
-// Each lane keeps its own state (m, l, acc) over the rows it holds.  m is a
-// reference point, not the exact running max: it moves only when a score
-// exceeds it by more than kRescaleSlack (log2 units), so exp2(s - m) stays
-// below 2^kRescaleSlack and the accumulator rescale is skipped (wave-uniformly)
-// on almost every page.  The probabilities are rounded to bf16 (as the
-// attention of the pages does before its PV product) and the PV product and
-// the row sum l run on v_dot2_f32_bf16, pairing the lane's rows r0 and r0+8.
+// Online softmax per lane.  Each lane keeps its own state (m, l, acc) over
+// the rows it holds.  m is a reference point, not the exact running max: it
+// moves only when a score exceeds it by more than kRescaleSlack (log2 units),
+// so exp2(s - m) stays below 2^kRescaleSlack and the accumulator rescale is
+// skipped (wave-uniformly) on almost every page.  The probabilities are
+// rounded to bf16 (as the attention of the pages does before its PV product)
+// and the PV product runs on v_dot2_f32_bf16, pairing the lane's rows r0 and
+// r0+8.
 constexpr float kRescaleSlack = 8.f;
 constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // bf16 (1, 1)
 
-template <int G, int U, bool kMask>
-__device__ __forceinline__ void process(const PageRegs (&buf)[U], const uint32_t (&qw)[G][8],
-                                        float (&m)[G], float (&l)[G], float (&acc)[G][16],
-                                        float scale_log2, int r0, int valid_rows) {
-  float s[U][2][G];
+// Raises the lane's reference max for head j if this page's scores need it
+// (rescaling acc and l), then returns the reference to subtract.
+template <int U>
+__device__ __forceinline__ float softmax_ref(const float (&s)[U][2], float& m, float& l,
+                                             float (&acc)[16]) {
+  float mc = s[0][0];
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
+    for (int rr = 0; rr < 2; ++rr) mc = fmaxf(mc, s[u][rr]);
+  const bool up = mc > m + kRescaleSlack;   // false while all scores are -inf
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    const float alpha = up ? fast_exp2(m - mc) : 1.f;   // m = -inf gives 0
+    m = up ? mc : m;
+    l *= alpha;
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float d = 0.f;
+    for (int d = 0; d < 16; ++d) acc[d] *= alpha;
+  }
+  return (m == kNegInf) ? 0.f : m;
+}
+
+// bf16 pages.  A 16-token page of one head is 16 rows of 256 B: lane l holds
+// rows r0 = l>>3 and r0+8, and the 16-byte chunks c = l&7 and c+8 of each,
+// i.e. head dims 8c..8c+7 and 64+8c..64+8c+7 (accumulator d < 8 and d >= 8).
+struct Bf16Page {
+  struct Regs {
+    u32x4 k[2][2];   // [row r0 / r0+8][chunk c / c+8]
+    u32x4 v[2][2];
+  };
+  static __device__ __forceinline__ int dim(int c, int d) {
+    return d < 8 ? 8 * c + d : 64 + 8 * c + (d - 8);
+  }
+  static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
+    const u32x4 lo = qp[c], hi = qp[c + 8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < 4; ++i) { qw[i] = lo[i]; qw[4 + i] = hi[i]; }
+  }
+  static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
+                                              int r0, int c) {
+    const int64_t base = (blk * a.Hkv + g) * kPage * 16 + r0 * 16 + c;   // 16 chunks per row
+    const u32x4* kp = a.k_cache + base;
+    const u32x4* vp = a.v_cache + base;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf[u].k[rr][h][i]),
-                                                as_bf16x2(qw[j][4 * h + i]), d, false);
-        d = sum8(d) * scale_log2;
-        if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
-        s[u][rr][j] = d;
-      }
-  bf16x2 pp[U][G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float mc = s[0][0][j];
+    for (int h = 0; h < 2; ++h) {
+      r.k[0][h] = load_kv(kp + 8 * h);
+      r.k[1][h] = load_kv(kp + 128 + 8 * h);
+      r.v[0][h] = load_kv(vp + 8 * h);
+      r.v[1][h] = load_kv(vp + 128 + 8 * h);
+    }
+  }
+  // kMask: the page is the sequence's last, partially filled one; rows >=
+  // valid_rows are excluded (score -inf, V forced to 0 so canary data cannot
+  // leak).
+  template <int G, int U, bool kMask>
+  static __device__ __forceinline__ void process(const Regs (&buf)[U], const uint32_t (&qw)[G][8],
+                                                 float (&m)[G], float (&l)[G],
+                                                 float (&acc)[G][16], float scale_log2, int r0,
+                                                 int valid_rows) {
+    float s[G][U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) mc = fmaxf(mc, s[u][rr][j]);
-    const bool up = mc > m[j] + kRescaleSlack;   // false while all scores are -inf
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-      const float alpha = up ? fast_exp2(m[j] - mc) : 1.f;   // m = -inf gives 0
-      m[j] = up ? mc : m[j];
-      l[j] *= alpha;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) acc[j][d] *= alpha;
-    }
-    const float mu = (m[j] == kNegInf) ? 0.f : m[j];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      pp[u][j] = bf16x2{(__bf16)fast_exp2(s[u][0][j] - mu), (__bf16)fast_exp2(s[u][1][j] - mu)};
-      l[j] = __builtin_amdgcn_fdot2_f32_bf16(pp[u][j], as_bf16x2(kBf16PairOne), l[j], false);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool keep0 = !kMask || (r0 < valid_rows);
-    const bool keep1 = !kMask || (r0 + 8 < valid_rows);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = keep0 ? buf[u].v[0][h][i] : 0u;   // row r0, dims 2i, 2i+1
-        const uint32_t w1 = keep1 ? buf[u].v[1][h][i] : 0u;   // row r0 + 8
-        const bf16x2 lo = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
-        const bf16x2 hi = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
-        const int d = 8 * h + 2 * i;
+      for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(lo, pp[u][j], acc[j][d], false);
-          acc[j][d + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, pp[u][j], acc[j][d + 1], false);
+          float d = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf[u].k[rr][h][i]),
+                                                  as_bf16x2(qw[j][4 * h + i]), d, false);
+          d = sum8(d) * scale_log2;
+          if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
+          s[j][u][rr] = d;
+        }
+    bf16x2 pp[U][G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float mu = softmax_ref<U>(s[j], m[j], l[j], acc[j]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        pp[u][j] = bf16x2{(__bf16)fast_exp2(s[j][u][0] - mu), (__bf16)fast_exp2(s[j][u][1] - mu)};
+        l[j] = __builtin_amdgcn_fdot2_f32_bf16(pp[u][j], as_bf16x2(kBf16PairOne), l[j], false);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool keep0 = !kMask || (r0 < valid_rows);
+      const bool keep1 = !kMask || (r0 + 8 < valid_rows);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w0 = keep0 ? buf[u].v[0][h][i] : 0u;   // row r0, dims 2i, 2i+1
+          const uint32_t w1 = keep1 ? buf[u].v[1][h][i] : 0u;   // row r0 + 8
+          const bf16x2 lo = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
+          const bf16x2 hi = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
+          const int d = 8 * h + 2 * i;
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(lo, pp[u][j], acc[j][d], false);
+            acc[j][d + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, pp[u][j], acc[j][d + 1], false);
+          }
+        }
+    }
+  }
+};
+
+// int8 pages (codes with one float32 scale per (slot, head), read as
+// code * scale; Module 04 page, kv_cache.py listing, section 5).  A page of
+// one head is 16 rows of 128 codes (2 KiB) plus 16 (K, V) scale pairs, kept
+// as 8 row pairs (s, s+8): lane l holds rows r0 = l>>3 and r0+8, the 16-byte
+// chunk c = l&7 of each (head dims 16c..16c+15), and the four scales of its
+// two rows, which are one 16-byte load (a page is 5 loads per lane).  Codes are integers in
+// [-127, 127], exact in bf16, so q . codes runs on v_dot2_f32_bf16 and the
+// row's K scale multiplies the score; the row's V scale is folded into its
+// probability before the PV product.
+// Signed byte i of w as a float: one SDWA convert.  Written out because the
+// compiler otherwise splits it into a shift and a convert and hoists the
+// shifts of the next page's codes into the current iteration (a register
+// blow-up that also serialises the page pipeline).
+#define PKV_SBYTE(n)                                                               \
+  __device__ __forceinline__ float sbyte##n(uint32_t w) {                          \
+    float r;                                                                       \
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD "     \
+        "src0_sel:BYTE_" #n : "=v"(r) : "v"(w));                                   \
+    return r;                                                                      \
+  }
+PKV_SBYTE(0)
+PKV_SBYTE(1)
+PKV_SBYTE(2)
+PKV_SBYTE(3)
+#undef PKV_SBYTE
+__device__ __forceinline__ float sbyte(uint32_t w, int i) {
+  return i == 0 ? sbyte0(w) : i == 1 ? sbyte1(w) : i == 2 ? sbyte2(w) : sbyte3(w);
+}
+struct Int8Page {
+  struct Regs {
+    u32x4 k[2];      // [row r0 / r0+8], 16 codes each
+    u32x4 v[2];
+    f32x4 s;         // K scale r0, V scale r0, K scale r0+8, V scale r0+8
+  };
+  static __device__ __forceinline__ int dim(int c, int d) { return 16 * c + d; }
+  static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
+    const u32x4 lo = qp[2 * c], hi = qp[2 * c + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { qw[i] = lo[i]; qw[4 + i] = hi[i]; }
+  }
+  static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
+                                              int r0, int c) {
+    const int64_t row = (blk * a.Hkv + g) * kPage + r0;        // 8 chunks per row
+    r.k[0] = load_kv(a.k_cache + row * 8 + c);
+    r.k[1] = load_kv(a.k_cache + (row + 8) * 8 + c);
+    r.v[0] = load_kv(a.v_cache + row * 8 + c);
+    r.v[1] = load_kv(a.v_cache + (row + 8) * 8 + c);
+    r.s = reinterpret_cast<const f32x4*>(a.kv_scales)[(blk * a.Hkv + g) * 8 + r0];
+  }
+  // Codes of one 4-code word as two bf16 pairs (exact).
+  static __device__ __forceinline__ bf16x2 pair(uint32_t w, int lo) {
+    return bf16x2{(__bf16)sbyte(w, lo), (__bf16)sbyte(w, lo + 1)};
+  }
+  template <int G, int U, bool kMask>
+  static __device__ __forceinline__ void process(const Regs (&buf)[U], const uint32_t (&qw)[G][8],
+                                                 float (&m)[G], float (&l)[G],
+                                                 float (&acc)[G][16], float scale_log2, int r0,
+                                                 int valid_rows) {
+    float s[G][U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        bf16x2 kp[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kp[2 * i] = pair(buf[u].k[rr][i], 0);
+          kp[2 * i + 1] = pair(buf[u].k[rr][i], 2);
+        }
+        const float rs = buf[u].s[2 * rr] * scale_log2;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float d = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            d = __builtin_amdgcn_fdot2_f32_bf16(kp[i], as_bf16x2(qw[j][i]), d, false);
+          d = sum8(d) * rs;
+          if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
+          s[j][u][rr] = d;
         }
       }
+    bf16x2 pp[U][G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float mu = softmax_ref<U>(s[j], m[j], l[j], acc[j]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p0 = fast_exp2(s[j][u][0] - mu), p1 = fast_exp2(s[j][u][1] - mu);
+        l[j] += p0 + p1;
+        // masked rows: weight exactly 0 (their scale may be a NaN canary)
+        const float w0 = (!kMask || r0 < valid_rows) ? p0 * buf[u].s[1] : 0.f;
+        const float w1 = (!kMask || r0 + 8 < valid_rows) ? p1 * buf[u].s[3] : 0.f;
+        pp[u][j] = bf16x2{(__bf16)w0, (__bf16)w1};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool keep0 = !kMask || (r0 < valid_rows);
+      const bool keep1 = !kMask || (r0 + 8 < valid_rows);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = keep0 ? buf[u].v[0][i] : 0u;   // row r0, dims 4i .. 4i+3
+        const uint32_t w1 = keep1 ? buf[u].v[1][i] : 0u;   // row r0 + 8
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 vv = bf16x2{(__bf16)sbyte(w0, e), (__bf16)sbyte(w1, e)};
+          const int d = 4 * i + e;
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+            acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(vv, pp[u][j], acc[j][d], false);
+        }
+      }
+    }
   }
-}
+};
 
 // Merge two online-softmax states (m in the log2 domain).
 __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float m2, float l2,
@@ -196,7 +331,7 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = M;
 }
 
-template <int G, int U>
+template <class P, int G, int U>
 __global__ void __launch_bounds__(kWaves * kWave)
 decode_kernel(const DecodeArgs a) {
   __shared__ float s_acc[kWaves][G][kD];
@@ -227,12 +362,7 @@ decode_kernel(const DecodeArgs a) {
   const int my_id = (lane < ppw && wp0 + lane < a.max_blocks) ? bt[wp0 + lane] : 0;
   uint32_t qw[G][8];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const u32x4* qp = a.q + ((int64_t)b * a.Hq + g * G + j) * 16;
-    const u32x4 lo = qp[c], hi = qp[c + 8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { qw[j][i] = lo[i]; qw[j][4 + i] = hi[i]; }
-  }
+  for (int j = 0; j < G; ++j) P::load_q(qw[j], a.q + ((int64_t)b * a.Hq + g * G + j) * 16, c);
 
   // A length outside [0, planned maximum] poisons the outputs of the sequence
   // (the plan covers splits * pages_per_split pages; no read goes past it).
@@ -270,7 +400,6 @@ decode_kernel(const DecodeArgs a) {
     for (int d = 0; d < 16; ++d) acc[j][d] = 0.f;
   }
 
-  const int lane_off = r0 * 16 + c;
   const int id_base = w0 - wp0;               // lane of my_id holding page w0
   int bad = bad_len ? 1 : 0;
   auto page_id = [&](int j) -> int64_t {
@@ -280,38 +409,57 @@ decode_kernel(const DecodeArgs a) {
     return ok ? id : 0;
   };
 
-  // Full pages, U at a time, two groups in flight.
+  // Full pages, U at a time, two groups in flight.  The steady-state loop
+  // covers the pairs of groups whose successor exists, so all its loads are
+  // unconditional: the load counter sees one order on every path and the wait
+  // before reducing a group leaves the next group in flight.  The last one or
+  // two groups are reduced after the loop.
   const int ngroups = nfull / U;
-  PageRegs bufA[U], bufB[U];
+  typename P::Regs bufA[U], bufB[U];
+  // q, the length and the page ids have all arrived before the page loads
+  // start (the ids are needed for the first address anyway), which keeps
+  // them out of the loop's in-flight count.
+  __builtin_amdgcn_s_waitcnt(0);
   if (ngroups > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_page(bufA[u], a, page_id(u), g, lane_off);
-  }
-  for (int gi = 0; gi < ngroups; gi += 2) {
-    const bool more1 = gi + 1 < ngroups;
-    if (more1) {
+    for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id(u), g, r0, c);
+    const int steady = (ngroups - 1) / 2;
+    // The scheduling barriers keep each prefetch between the two reductions:
+    // issued before the group it overlaps is reduced, and after the group
+    // whose registers it reuses is done (else the two groups' registers
+    // overlap and the loop needs copies that wait for the prefetch).
+    for (int pi = 0; pi < steady; ++pi) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) load_page(bufB[u], a, page_id((gi + 1) * U + u), g, lane_off);
+      for (int u = 0; u < U; ++u) P::load(bufB[u], a, page_id((2 * pi + 1) * U + u), g, r0, c);
+      __builtin_amdgcn_sched_barrier(0);
+      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id((2 * pi + 2) * U + u), g, r0, c);
+      __builtin_amdgcn_sched_barrier(0);
+      P::template process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
     }
-    process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
-    if (more1) {
-      if (gi + 2 < ngroups) {
+    if (ngroups - 2 * steady == 2) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_page(bufA[u], a, page_id((gi + 2) * U + u), g, lane_off);
-      }
-      process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
+      for (int u = 0; u < U; ++u)
+        P::load(bufB[u], a, page_id((2 * steady + 1) * U + u), g, r0, c);
+      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
+      P::template process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
+    } else {
+      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
     }
   }
   // Leftover full pages (fewer than U), one at a time.
   for (int j = ngroups * U; j < nfull; ++j) {
-    PageRegs one[1];
-    load_page(one[0], a, page_id(j), g, lane_off);
-    process<G, 1, false>(one, qw, m, l, acc, a.scale_log2, r0, kPage);
+    typename P::Regs one[1];
+    P::load(one[0], a, page_id(j), g, r0, c);
+    P::template process<G, 1, false>(one, qw, m, l, acc, a.scale_log2, r0, kPage);
   }
   if (has_tail) {
-    PageRegs one[1];
-    load_page(one[0], a, page_id(n_full - w0), g, lane_off);
-    process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n % kPage);
+    typename P::Regs one[1];
+    P::load(one[0], a, page_id(n_full - w0), g, r0, c);
+    P::template process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n % kPage);
   }
 
   // Merge the 8 lane groups (rows) of the wave: lanes xor 8, 16, 32.
@@ -336,10 +484,7 @@ decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        s_acc[w][j][c * 8 + d] = acc[j][d];
-        s_acc[w][j][64 + c * 8 + d] = acc[j][8 + d];
-      }
+      for (int d = 0; d < 16; ++d) s_acc[w][j][P::dim(c, d)] = acc[j][d];
   }
   if (lane == 0) {
 #pragma unroll
@@ -430,12 +575,50 @@ decode_kernel(const DecodeArgs a) {
 #ifndef PKV_DECODE_U_G8
 #define PKV_DECODE_U_G8 1
 #endif
+// int8 pages hold 20 VGPRs per page (codes and scales), so twice the pages fit.
+#ifndef PKV_DECODE_I8_U_G1
+#define PKV_DECODE_I8_U_G1 2
+#endif
+#ifndef PKV_DECODE_I8_U_G2
+#define PKV_DECODE_I8_U_G2 2
+#endif
+#ifndef PKV_DECODE_I8_U_G4
+#define PKV_DECODE_I8_U_G4 1
+#endif
+#ifndef PKV_DECODE_I8_U_G8
+#define PKV_DECODE_I8_U_G8 1
+#endif
 
-template <int G, int U>
+template <class P, int G, int U>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(a.B * a.Hkv * a.splits);
-  hipLaunchKernelGGL((decode_kernel<G, U>), dim3(grid), dim3(kWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<P, G, U>), dim3(grid), dim3(kWaves * kWave), 0, stream, a);
   return hipGetLastError();
+}
+
+DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const float* kv_scales,
+                     const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
+                     int Hkv, int num_blocks, int max_blocks, float scale,
+                     const DecodePlan& plan, void* workspace) {
+  DecodeArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const u32x4*>(q);
+  a.k_cache = static_cast<const u32x4*>(k_cache);
+  a.v_cache = static_cast<const u32x4*>(v_cache);
+  a.kv_scales = kv_scales;
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  char* ws = static_cast<char*>(workspace);
+  const bool split = plan.splits > 1;
+  a.ws_ml = split ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_acc = split ? reinterpret_cast<float*>(ws + plan.ws_ml_bytes) : nullptr;
+  a.counters = split ? reinterpret_cast<int*>(ws + plan.ws_ml_bytes + plan.ws_acc_bytes)
+                     : nullptr;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
+  a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -490,27 +673,32 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          int Hkv, int num_blocks, int max_blocks, float scale,
                          const DecodePlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  DecodeArgs a;
-  a.out = static_cast<uint16_t*>(out);
-  a.q = static_cast<const u32x4*>(q);
-  a.k_cache = static_cast<const u32x4*>(k_cache);
-  a.v_cache = static_cast<const u32x4*>(v_cache);
-  a.block_tables = block_tables;
-  a.ctx_lens = ctx_lens;
-  char* ws = static_cast<char*>(workspace);
-  const bool split = plan.splits > 1;
-  a.ws_ml = split ? reinterpret_cast<float*>(ws) : nullptr;
-  a.ws_acc = split ? reinterpret_cast<float*>(ws + plan.ws_ml_bytes) : nullptr;
-  a.counters = split ? reinterpret_cast<int*>(ws + plan.ws_ml_bytes + plan.ws_acc_bytes)
-                     : nullptr;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
-  a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables,
+                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
+                                 workspace);
   switch (Hq / Hkv) {
-    case 1: return launch_g<1, PKV_DECODE_U_G1>(a, stream);
-    case 2: return launch_g<2, PKV_DECODE_U_G2>(a, stream);
-    case 4: return launch_g<4, PKV_DECODE_U_G4>(a, stream);
-    case 8: return launch_g<8, PKV_DECODE_U_G8>(a, stream);
+    case 1: return launch_g<Bf16Page, 1, PKV_DECODE_U_G1>(a, stream);
+    case 2: return launch_g<Bf16Page, 2, PKV_DECODE_U_G2>(a, stream);
+    case 4: return launch_g<Bf16Page, 4, PKV_DECODE_U_G4>(a, stream);
+    case 8: return launch_g<Bf16Page, 8, PKV_DECODE_U_G8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                              const float* kv_scales, const int32_t* block_tables,
+                              const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
+                              int max_blocks, float scale, const DecodePlan& plan,
+                              void* workspace, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const DecodeArgs a = make_args(out, q, k_codes, v_codes, kv_scales, block_tables,
+                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
+                                 workspace);
+  switch (Hq / Hkv) {
+    case 1: return launch_g<Int8Page, 1, PKV_DECODE_I8_U_G1>(a, stream);
+    case 2: return launch_g<Int8Page, 2, PKV_DECODE_I8_U_G2>(a, stream);
+    case 4: return launch_g<Int8Page, 4, PKV_DECODE_I8_U_G4>(a, stream);
+    case 8: return launch_g<Int8Page, 8, PKV_DECODE_I8_U_G8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

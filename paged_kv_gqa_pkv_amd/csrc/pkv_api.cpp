@@ -104,6 +104,57 @@ int validate_tables(const int32_t* block_tables, const int32_t* context_lens, in
   return PKV_OK;
 }
 
+// PKV_VALIDATE: every slot inside the pool and no slot twice.
+int validate_slots(const int32_t* slot_mapping, int32_t T, int32_t num_blocks, hipStream_t s) {
+  std::vector<int32_t> slots;
+  if (!to_host(slots, slot_mapping, (size_t)T, s))
+    return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of slot_mapping failed");
+  std::unordered_set<int32_t> seen;
+  for (int t = 0; t < T; ++t) {
+    const int32_t v = slots[t];
+    if (v < 0) continue;
+    if ((int64_t)v >= (int64_t)num_blocks * PKV_BLOCK_SIZE)
+      return fail(PKV_EVALIDATE, "slot_mapping[%d]=%d outside a pool of %d pages", t, v,
+                  num_blocks);
+    if (!seen.insert(v).second)
+      return fail(PKV_EVALIDATE, "slot %d appears twice in slot_mapping", v);
+  }
+  return PKV_OK;
+}
+
+// Host checks shared by the decode entry points; fills the split plan.
+// done = true: nothing to launch (B == 0).
+int check_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t Hq,
+                 int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                 int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                 void* workspace, size_t workspace_bytes, void* stream, pkv::DecodePlan& plan,
+                 bool& done) {
+  done = false;
+  if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+    return fail(PKV_EINVAL, "negative size");
+  int rc = check_geometry(Hq, Hkv, D, block_size);
+  if (rc) return rc;
+  if (B == 0) { done = true; return PKV_OK; }
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (out == q) return fail(PKV_EINVAL, "out and q must not overlap");
+  if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
+                max_context_len, max_blocks_per_seq);
+  if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
+  plan = pkv::plan_decode(B, Hq, Hkv, max_context_len, device_cus());
+  if (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace))
+    return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.ws_bytes,
+                workspace_bytes);
+  if (validate_mode()) {
+    rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
+                         max_context_len, static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+  }
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,23 +209,32 @@ int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping
   if (k_cache == v_cache) return fail(PKV_EINVAL, "k_cache and v_cache must differ");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validate_mode()) {
-    std::vector<int32_t> slots;
-    if (!to_host(slots, slot_mapping, (size_t)T, s))
-      return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of slot_mapping failed");
-    std::unordered_set<int32_t> seen;
-    for (int t = 0; t < T; ++t) {
-      const int32_t v = slots[t];
-      if (v < 0) continue;
-      if ((int64_t)v >= (int64_t)num_blocks * PKV_BLOCK_SIZE)
-        return fail(PKV_EVALIDATE, "slot_mapping[%d]=%d outside a pool of %d pages", t, v,
-                    num_blocks);
-      if (!seen.insert(v).second)
-        return fail(PKV_EVALIDATE, "slot %d appears twice in slot_mapping", v);
-    }
+    rc = validate_slots(slot_mapping, T, num_blocks, s);
+    if (rc) return rc;
   }
   return launch_status(
       pkv::launch_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, num_blocks, Hkv, D, s),
       "pkv_append");
+}
+
+int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    void* k_codes, void* v_codes, float* kv_scales, int32_t T,
+                    int32_t num_blocks, int32_t Hkv, int32_t D, int32_t block_size, void* stream) {
+  if (T < 0 || num_blocks < 0) return fail(PKV_EINVAL, "negative size");
+  int rc = check_geometry(Hkv, Hkv, D, block_size);
+  if (rc) return rc;
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_codes || !v_codes || !kv_scales)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (k_codes == v_codes) return fail(PKV_EINVAL, "k_codes and v_codes must differ");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    rc = validate_slots(slot_mapping, T, num_blocks, s);
+    if (rc) return rc;
+  }
+  return launch_status(pkv::launch_append_int8(k_new, v_new, slot_mapping, k_codes, v_codes,
+                                               kv_scales, T, num_blocks, Hkv, D, s),
+                       "pkv_append_int8");
 }
 
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -196,32 +256,36 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
-    return fail(PKV_EINVAL, "negative size");
-  int rc = check_geometry(Hq, Hkv, D, block_size);
-  if (rc) return rc;
-  if (B == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PKV_EINVAL, "null pointer argument");
-  if (out == q) return fail(PKV_EINVAL, "out and q must not overlap");
-  if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE)
-    return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
-                max_context_len, max_blocks_per_seq);
-  if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
-  const pkv::DecodePlan plan = pkv::plan_decode(B, Hq, Hkv, max_context_len, device_cus());
-  if (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace))
-    return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.ws_bytes,
-                workspace_bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (validate_mode()) {
-    rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
-                         max_context_len, s);
-    if (rc) return rc;
-  }
+  pkv::DecodePlan plan;
+  bool done = false;
+  int rc = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                        workspace, workspace_bytes, stream, plan, done);
+  if (rc || done) return rc;
   return launch_status(pkv::launch_decode(out, q, k_cache, v_cache, block_tables, context_lens, B,
                                           Hq, Hkv, num_blocks, max_blocks_per_seq, scale, plan,
-                                          workspace, s),
+                                          workspace, static_cast<hipStream_t>(stream)),
                        "pkv_attn_decode");
+}
+
+int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                         const float* kv_scales, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::DecodePlan plan;
+  bool done = false;
+  if (B > 0 && !kv_scales) return fail(PKV_EINVAL, "null pointer argument");
+  int rc = check_decode(out, q, k_codes, v_codes, block_tables, context_lens, B, Hq, Hkv, D,
+                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                        workspace, workspace_bytes, stream, plan, done);
+  if (rc || done) return rc;
+  return launch_status(pkv::launch_decode_int8(out, q, k_codes, v_codes, kv_scales, block_tables,
+                                               context_lens, B, Hq, Hkv, num_blocks,
+                                               max_blocks_per_seq, scale, plan, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                       "pkv_attn_decode_int8");
 }
 
 size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int32_t Hkv,

@@ -32,6 +32,19 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          int Hkv, int num_blocks, int max_blocks, float scale,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
 
+// Decode over int8 pages (codes in the bf16 page order; float32 scales
+// [num_blocks][Hkv][8][2][2], the (K, V) scales of slot s at [s % 8][s / 8]);
+// same plan and workspace as launch_decode.
+hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                              const float* kv_scales, const int32_t* block_tables,
+                              const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
+                              int max_blocks, float scale, const DecodePlan& plan,
+                              void* workspace, hipStream_t stream);
+
+hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_t* slots,
+                              void* k_codes, void* v_codes, float* kv_scales, int T,
+                              int num_blocks, int Hkv, int D, hipStream_t stream);
+
 // Key-split plan of a prefill call: row tiles of 128 (token, head) rows,
 // key ranges of tiles_per_split 64-key tiles.
 struct PrefillPlan {

@@ -39,6 +39,16 @@ PAGE = 16
 BF16_CANARY_BITS = 0x7FC0
 
 S_CTX, S_PLACE, S_QDEC, S_KPOOL, S_VPOOL, S_KNEW, S_VNEW, S_QPRE = range(8)
+S_KSCALE = 8                     # int8 pools: per-(slot, head) K and V scales
+
+# int8 pools: codes are rounded N(0, CODE_SD^2) clipped to +-127 (the spread of
+# quantised N(0,1) rows of 128 values, whose largest magnitude is ~3.3 sd), and
+# scales are U[SCALE_LO, SCALE_HI] (that largest magnitude over 127).  Slots a
+# sequence has not filled hold scale NaN (float32 0x7FC00000), so any read of
+# them poisons the result.
+CODE_SD = 38.5
+SCALE_LO, SCALE_HI = 0.018, 0.030
+F32_CANARY_BITS = 0x7FC00000
 
 
 def stream_seed(base: int, layer: int, stream: int) -> int:
@@ -272,6 +282,56 @@ def make_layer(w: Workload, t: Tables, layer: int, device="cpu",
     return LayerData(
         k_cache=_pool(w, fill, s(S_KPOOL), device),
         v_cache=_pool(w, fill, s(S_VPOOL), device),
+        k_new=randn_bf16((T, w.Hkv, w.D), s(S_KNEW), device),
+        v_new=randn_bf16((T, w.Hkv, w.D), s(S_VNEW), device),
+        q_decode=randn_bf16((n_dec, w.Hq, w.D), s(S_QDEC), device) if n_dec else None,
+        q_prefill=randn_bf16((n_pre_q, w.Hq, w.D), s(S_QPRE), device) if n_pre_q else None,
+    )
+
+
+@dataclasses.dataclass
+class LayerDataInt8:
+    """One layer's tensors for a step over int8 pages (all on ``device``)."""
+    k_codes: torch.Tensor        # int8 [num_blocks, Hkv, 16, D] (head-major pages), pre-append
+    v_codes: torch.Tensor
+    kv_scales: torch.Tensor      # float32 [num_blocks, Hkv, 8, 2, 2]: slot s at [s % 8][s // 8][K, V]
+    k_new: torch.Tensor          # bf16 [T_total, Hkv, D]
+    v_new: torch.Tensor
+    q_decode: Optional[torch.Tensor]
+    q_prefill: Optional[torch.Tensor]
+
+
+def _codes(shape, seed, device) -> torch.Tensor:
+    x = torch.randn(tuple(shape), generator=_gen(seed, device), device=device,
+                    dtype=torch.float32)
+    return torch.clamp(torch.round(x * CODE_SD), -127, 127).to(torch.int8)
+
+
+def _kv_scales(w: Workload, fill: torch.Tensor, seed: int, device) -> torch.Tensor:
+    g = _gen(seed, device)
+    sc = torch.empty((w.num_blocks, w.Hkv, 8, 2, 2), device=device, dtype=torch.float32)
+    sc.uniform_(SCALE_LO, SCALE_HI, generator=g)
+    slot = (torch.arange(8, device=device).view(8, 1) +
+            8 * torch.arange(2, device=device).view(1, 2))          # [8, 2]: slot i + 8 rr
+    dead = slot.view(1, 8, 2) >= fill.to(device).view(-1, 1, 1)       # [num_blocks, 8, 2]
+    sc.view(torch.int32).masked_fill_(dead.view(w.num_blocks, 1, 8, 2, 1), F32_CANARY_BITS)
+    return sc
+
+
+def make_layer_int8(w: Workload, t: Tables, layer: int, device="cpu",
+                    fill: Optional[torch.Tensor] = None) -> LayerDataInt8:
+    """The same step as make_layer (same new K/V and queries) over int8 pools."""
+    if fill is None:
+        fill = page_fill_counts(w, t)
+    s = lambda k: stream_seed(w.base_seed, layer, k)
+    T = int(t.cu_new[-1])
+    n_dec = len(w.decode_seqs)
+    n_pre_q = sum(w.seqs[i].new_len for i in w.prefill_seqs)
+    shape = (w.num_blocks, w.Hkv, PAGE, w.D)
+    return LayerDataInt8(
+        k_codes=_codes(shape, s(S_KPOOL), device),
+        v_codes=_codes(shape, s(S_VPOOL), device),
+        kv_scales=_kv_scales(w, fill, s(S_KSCALE), device),
         k_new=randn_bf16((T, w.Hkv, w.D), s(S_KNEW), device),
         v_new=randn_bf16((T, w.Hkv, w.D), s(S_VNEW), device),
         q_decode=randn_bf16((n_dec, w.Hq, w.D), s(S_QDEC), device) if n_dec else None,

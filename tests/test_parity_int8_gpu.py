@@ -1,0 +1,199 @@
+"""Parity of the int8-page path (append with quantisation, decode) with the
+CPU oracle, through the C ABI.
+
+The int8 append must match the oracle bit for bit (codes and float32 scale
+bits: both sides quantise in float32 as [P2]'s KV8Cache.write does).  Decode
+over int8 pages is held to the same tolerance as the bf16 path against the
+float64 oracle on the same codes and scales.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_int8_oracle as Q
+from oracle import pkv_oracle as O
+from paged_kv_gqa_pkv_amd import binding as bd
+from paged_kv_gqa_pkv_amd import step as ST
+from paged_kv_gqa_pkv_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def u16(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def codes_pages_order(codes):
+    """Device codes [nb][Hkv][16][D] -> the pages' order [nb][16][Hkv][D]."""
+    return codes.detach().transpose(1, 2).contiguous().cpu().numpy()
+
+
+def scales_pages_order(kv_scales):
+    """Device scales [nb][Hkv][8][2][2] (slot s at [s % 8][s // 8]) -> the
+    pages' two arrays ks, vs [nb][16][Hkv] (axis permutations only)."""
+    sc = kv_scales.detach().cpu()
+    nb, hkv = sc.shape[0], sc.shape[1]
+    per_slot = sc.permute(0, 3, 2, 1, 4).reshape(nb, 16, hkv, 2)   # [nb][rr][i] -> slot i + 8 rr
+    return per_slot[..., 0].contiguous().numpy(), per_slot[..., 1].contiguous().numpy()
+
+
+def check_close(got, want, what):
+    g = O.bf16_to_f64(u16(got))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
+    err = np.abs(g - want)
+    print(f"{what}: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (what, err.max(), err.mean())
+
+
+def run_int8_step(w, layer=0):
+    """Slot mapping, int8 append and int8 decode on the GPU; the oracle's
+    append and decode on the CPU.  Returns (device layer data, out)."""
+    print(f"[int8 parity] {w.name} layer {layer}: {w.description}", flush=True)
+    assert not w.prefill_seqs
+    t = S.make_tables(w)
+    d = S.make_layer_int8(w, t, layer, device="cuda")
+    kc0, vc0 = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
+    ks0, vs0 = scales_pages_order(d.kv_scales)
+    plan = ST.plan_step(w, t)
+    out = torch.empty_like(d.q_decode)
+    ST.slot_mapping(plan)
+    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.kv_scales)
+    bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.kv_scales, plan.bt_decode,
+                            plan.ctx_decode, plan.max_ctx_decode, plan.scale,
+                            workspace=plan.workspace)
+    torch.cuda.synchronize()
+    bt = t.block_tables.numpy().tolist()
+    ctx = t.context_lens.numpy().tolist()
+    slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
+    kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, u16(d.k_new), u16(d.v_new), slots)
+    gk, gv = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
+    gks, gvs = scales_pages_order(d.kv_scales)
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc), "codes after append differ"
+    assert np.array_equal(gks.view(np.uint32), ks.view(np.uint32)), "K scales differ"
+    assert np.array_equal(gvs.view(np.uint32), vs.view(np.uint32)), "V scales differ"
+    want = Q.decode_int8_ref(u16(d.q_decode), kc, ks, vc, vs, bt, ctx, O.default_scale(w.D))
+    check_close(out, want, f"{w.name} int8 decode")
+    return d, out
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_int8_decode_configs(name):
+    run_int8_step(S.workload(name))
+
+
+def _seqs_decode(ctxs):
+    return [S.SeqSpec(c - 1, 1, False) for c in ctxs]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_int8_decode_group_sizes_and_ragged_lengths(G):
+    Hkv = 2
+    ctxs = [1, 15, 16, 17, 31, 33, 200, 515]
+    w = S.custom_workload(f"int8_ragged_G{G}", _seqs_decode(ctxs), Hq=Hkv * G, Hkv=Hkv, D=128,
+                          num_blocks=96, base_seed=170 + G)
+    run_int8_step(w)
+
+
+def test_int8_decode_long_context_many_splits():
+    w = S.custom_workload("int8_long", _seqs_decode([5000, 777, 3]), Hq=32, Hkv=8, D=128,
+                          num_blocks=400, base_seed=180)
+    assert bd.pkv_decode_num_splits(3, 32, 8, 128, 5000) > 1
+    run_int8_step(w)
+
+
+def test_int8_append_bulk_bit_exact_with_edge_rows():
+    """65 536 tokens to random distinct slots; rows include all-zero rows,
+    rows with one large value and tiny rows (the 1e-8 term matters there)."""
+    n, nb, Hkv, D = 65536, 4096, 8, 128
+    slots, k_new, v_new, _, _ = S.bulk_append_inputs(n, nb, Hkv, D, seed=321)
+    k = k_new.float()
+    k[0] = 0.0
+    k[1, :, 5] = 300.0
+    k[2] *= 1e-6
+    k_new = k.to(torch.bfloat16)
+    kc = torch.zeros((nb, Hkv, 16, D), dtype=torch.int8, device="cuda")
+    vc = torch.zeros_like(kc)
+    sc = torch.ones((nb, Hkv, 8, 2, 2), dtype=torch.float32, device="cuda")
+    bd.pkv_append_int8(k_new.cuda(), v_new.cuda(), slots.cuda(), kc, vc, sc)
+    torch.cuda.synchronize()
+    ks0 = np.ones((nb, 16, Hkv), np.float32)
+    z = np.zeros((nb, 16, Hkv, D), np.int8)
+    okc, ovc, oks, ovs = Q.append_int8_ref(z, z, ks0, ks0, u16(k_new), u16(v_new),
+                                           slots.numpy().tolist())
+    gks, gvs = scales_pages_order(sc)
+    assert np.array_equal(codes_pages_order(kc), okc) and np.array_equal(codes_pages_order(vc), ovc)
+    assert np.array_equal(gks.view(np.uint32), oks.view(np.uint32))
+    assert np.array_equal(gvs.view(np.uint32), ovs.view(np.uint32))
+
+
+def test_int8_append_skips_negative_slots():
+    Hkv, D, nb = 8, 128, 4
+    k_new = S.randn_bf16((3, Hkv, D), 41).cuda()
+    v_new = S.randn_bf16((3, Hkv, D), 42).cuda()
+    kc = torch.full((nb, Hkv, 16, D), 7, dtype=torch.int8, device="cuda")
+    vc = kc.clone()
+    sc = torch.full((nb, Hkv, 8, 2, 2), 0.5, dtype=torch.float32, device="cuda")
+    slots = torch.tensor([5, -1, 63], dtype=torch.int32, device="cuda")
+    bd.pkv_append_int8(k_new, v_new, slots, kc, vc, sc)
+    torch.cuda.synchronize()
+    ks0 = np.full((nb, 16, Hkv), 0.5, np.float32)
+    c0 = np.full((nb, 16, Hkv, D), 7, np.int8)
+    okc, ovc, oks, ovs = Q.append_int8_ref(c0, c0, ks0, ks0, u16(k_new), u16(v_new), [5, -1, 63])
+    gks, gvs = scales_pages_order(sc)
+    assert np.array_equal(codes_pages_order(kc), okc) and np.array_equal(codes_pages_order(vc), ovc)
+    assert np.array_equal(gks, oks) and np.array_equal(gvs, ovs)
+
+
+def _sampled_full_size_int8(name, samples):
+    w = S.workload(name)
+    print(f"[int8 parity] {w.name} full size, sampled", flush=True)
+    t = S.make_tables(w)
+    fill = S.page_fill_counts(w, t)
+    d = S.make_layer_int8(w, t, 0, device="cuda", fill=fill)
+    kc0, vc0 = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
+    ks0, vs0 = scales_pages_order(d.kv_scales)
+    plan = ST.plan_step(w, t)
+    out = torch.empty_like(d.q_decode)
+    ST.slot_mapping(plan)
+    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.kv_scales)
+    bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.kv_scales, plan.bt_decode,
+                            plan.ctx_decode, plan.max_ctx_decode, plan.scale,
+                            workspace=plan.workspace)
+    torch.cuda.synchronize()
+    bt = t.block_tables.numpy().tolist()
+    ctx = t.context_lens.numpy().tolist()
+    slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
+    assert plan.slot_mapping.cpu().numpy().tolist() == slots
+    # the oracle's own append (from the pre-append pools) feeds the oracle's attention
+    kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, u16(d.k_new), u16(d.v_new), slots)
+    gk = codes_pages_order(d.k_codes)
+    gks, _ = scales_pages_order(d.kv_scales)
+    for s_ in slots:                  # appended rows landed bit-exactly
+        assert np.array_equal(gk[s_ // 16, s_ % 16], kc[s_ // 16, s_ % 16])
+        assert np.array_equal(gks[s_ // 16, s_ % 16].view(np.uint32),
+                              ks[s_ // 16, s_ % 16].view(np.uint32))
+    got = O.bf16_to_f64(u16(out))
+    qh = u16(d.q_decode)
+    errs = []
+    for b, h in samples:
+        g = O.kv_head_of(h, w.Hq, w.Hkv)
+        n = ctx[b]
+        K = Q.gather_int8_ref(kc, ks, bt[b], n).astype(np.float64)[:, g, :]
+        V = Q.gather_int8_ref(vc, vs, bt[b], n).astype(np.float64)[:, g, :]
+        want = O.attend_one(O.bf16_to_f64(qh[b, h]), K, V, O.default_scale(w.D))
+        errs.append(np.abs(got[b, h] - want))
+    err = np.concatenate(errs)
+    print(f"{name} int8 sampled: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+
+
+def test_int8_full_size_c4a_sampled():
+    _sampled_full_size_int8("c4a", [(0, 0), (7, 31), (33, 12), (63, 5)])
+
+
+def test_int8_full_size_c4b_sampled():
+    _sampled_full_size_int8("c4b", [(0, 0), (5, 17), (12, 31)])
