@@ -49,6 +49,8 @@ def parse():
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--no-events", action="store_true",
                    help="time steps only (no per-launch events), e.g. under a profiler")
+    p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
+                   help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--graph", action="store_true",
                    help="capture each distinct step in a HIP graph and time graph replays "
                         "(per-launch events then come from a separate eager pass)")
@@ -66,19 +68,24 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_gqa_pkv_amd", "csrc", "decode.hip")
 
 
-def measured_traffic(workload):
-    """HBM bytes per decode launch measured with rocprofv3 counters (FETCH_SIZE,
-    WRITE_SIZE, scaled by the same counters on a plain copy), if the record
-    matches the current decode kernel source and this workload; else None."""
+def _decode_source_sha():
     import hashlib
+    with open(DECODE_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per decode launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE, scaled by the same counters on a plain copy) for this workload
+    key ("c4", "c4-int8", ...), if the record was taken on the current decode
+    kernel source; else None."""
     try:
         with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
-        with open(DECODE_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
+            rec = json.load(f).get("records", {}).get(key)
+        sha = _decode_source_sha()
+    except (OSError, ValueError):
         return None
-    if rec.get("decode_source_sha256") != sha or rec.get("workload") != workload:
+    if not rec or rec.get("decode_source_sha256") != sha:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -101,7 +108,10 @@ def write_traffic_record(args):
     cf = [v for _, v in values(copy_f, "copyBuffer")]
     cw = [v for _, v in values(copy_w, "copyBuffer")]
     fetch_scale, write_scale = true_kib / statistics.mean(cf), true_kib / statistics.mean(cw)
-    df, dw = values(dec_f, "decode_kernel"), values(dec_w, "decode_kernel")
+    kname = "Int8Page" if args.kv == "int8" else "Bf16Page"
+    df, dw = values(dec_f, kname), values(dec_w, kname)
+    if not df or not dw:
+        raise SystemExit(f"no {kname} decode dispatches in the counter files")
     per_grid = {}
     for grid in sorted({g for g, _ in df}):
         f = [v for g, v in df if g == grid]
@@ -112,16 +122,21 @@ def write_traffic_record(args):
                                                  statistics.mean(w) * write_scale))}
     traffic = round(1024 * (statistics.mean(v for _, v in df) * fetch_scale +
                             statistics.mean(v for _, v in dw) * write_scale))
-    with open(DECODE_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    rec = {"kernel": "decode_kernel (pkv_attn_decode)", "workload": args.workload,
-           "decode_source_sha256": sha, "traffic_bytes_per_launch": traffic,
+    key = args.workload if args.kv == "bf16" else f"{args.workload}-int8"
+    rec = {"kernel": f"decode_kernel<{kname}>", "workload": key,
+           "decode_source_sha256": _decode_source_sha(), "traffic_bytes_per_launch": traffic,
            "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
            "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
                                 "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw},
            "per_grid": per_grid}
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec.setdefault("records", {})[key] = rec
     with open(TRAFFIC_RECORD, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(allrec, f, indent=1)
     print(json.dumps(rec), flush=True)
 
 
@@ -160,9 +175,12 @@ def decode_bytes(w, t, rows, kv="bf16"):
     return kv_tokens * per_token + len(rows) * 2 * Hq * D * 2 + table_bytes
 
 
-def append_bytes(w, t):
+def append_bytes(w, t, kv="bf16"):
+    """Read the new bf16 K/V rows and the slot, write them into the pages (int8:
+    the codes and a float32 scale per row)."""
     T = int(t.cu_new[-1])
-    return T * (2 * 2 * w.Hkv * w.D * 2 + 4)
+    write = 2 * w.Hkv * w.D * 2 if kv == "bf16" else 2 * w.Hkv * (w.D + 4)
+    return T * (2 * w.Hkv * w.D * 2 + write + 4)
 
 
 def slot_bytes(w, t):
@@ -187,13 +205,14 @@ def prefill_work(w, t):
 class Part:
     """One independent decode/mixed step shape with its own pools."""
 
-    def __init__(self, w, t, plan, layers, bufs, copies):
+    def __init__(self, w, t, plan, layers, bufs, copies, kv="bf16"):
         self.w, self.t, self.plan, self.layers, self.bufs, self.copies = w, t, plan, layers, bufs, copies
+        self.kv = kv
         nd = len(w.decode_seqs)
-        self.dec_bytes = decode_bytes(w, t, w.decode_seqs) if nd else 0
+        self.dec_bytes = decode_bytes(w, t, w.decode_seqs, kv) if nd else 0
         self.pre_bytes, self.pre_flops = prefill_work(w, t)
-        self.step_bytes = slot_bytes(w, t) + w.n_layers * (append_bytes(w, t) + self.dec_bytes +
-                                                           self.pre_bytes)
+        self.step_bytes = slot_bytes(w, t) + w.n_layers * (append_bytes(w, t, kv) +
+                                                           self.dec_bytes + self.pre_bytes)
 
 
 def _bufs(w, t, device):
@@ -209,19 +228,21 @@ def _bufs(w, t, device):
                 op=torch.empty_like(qp) if qp is not None else None)
 
 
-def _layers(w, t, rotate_mib, device):
+def _layers(w, t, rotate_mib, device, kv="bf16"):
     from paged_kv_gqa_pkv_amd import synth as S
-    pool_bytes = 2 * w.num_blocks * 16 * w.Hkv * w.D * 2
+    per_slot = 2 * w.Hkv * w.D * 2 if kv == "bf16" else 2 * w.Hkv * (w.D + 4)
+    pool_bytes = w.num_blocks * 16 * per_slot
     copies = 1
     if w.n_layers * pool_bytes < (1 << 30):
         copies = max(1, -(-rotate_mib * (1 << 20) // (w.n_layers * pool_bytes)))
     fill = S.page_fill_counts(w, t)
-    layers = [S.make_layer(w, t, l + 1000 * c, device=device, fill=fill)
+    make = S.make_layer if kv == "bf16" else S.make_layer_int8
+    layers = [make(w, t, l + 1000 * c, device=device, fill=fill)
               for c in range(copies) for l in range(w.n_layers)]
     return layers, copies
 
 
-def build_parts(name, rotate_mib, device):
+def build_parts(name, rotate_mib, device, kv="bf16"):
     """Returns (parts, schedule): schedule(i) lists the parts step i runs."""
     import torch
     from paged_kv_gqa_pkv_amd import step as ST
@@ -232,11 +253,13 @@ def build_parts(name, rotate_mib, device):
         for sub in ("c4a", "c4b"):
             w = S.workload(sub)
             t = S.make_tables(w)
-            layers, copies = _layers(w, t, rotate_mib, device)
+            layers, copies = _layers(w, t, rotate_mib, device, kv)
             parts.append(Part(w, t, ST.plan_step(w, t, device=device), layers,
-                              _bufs(w, t, device), copies))
+                              _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [0, 1])
     if name == "c5":
+        if kv != "bf16":
+            raise SystemExit("bench.py: the prefill chunk runs on bf16 pages only (--kv bf16)")
         base_w = S.workload("c5", 5)
         base_t = S.make_tables(base_w)
         layers, copies = _layers(base_w, base_t, rotate_mib, device)
@@ -253,9 +276,9 @@ def build_parts(name, rotate_mib, device):
         return parts, (lambda i: [i % 6])
     w = S.workload(name)
     t = S.make_tables(w)
-    layers, copies = _layers(w, t, rotate_mib, device)
+    layers, copies = _layers(w, t, rotate_mib, device, kv)
     return [Part(w, t, ST.plan_step(w, t, device=device), layers, _bufs(w, t, device),
-                 copies)], (lambda i: [0])
+                 copies, kv)], (lambda i: [0])
 
 
 WORKLOAD_TEXT = {
@@ -275,7 +298,7 @@ def run(args):
     bd.load()
     device = "cuda"
     torch.cuda.set_device(0)
-    parts, schedule = build_parts(args.workload, args.rotate_mib, device)
+    parts, schedule = build_parts(args.workload, args.rotate_mib, device, args.kv)
     stream = torch.cuda.current_stream()
     use_events = not args.no_events
     dec_events, pre_events = [], []
@@ -288,8 +311,12 @@ def run(args):
         ST.slot_mapping(plan, stream=stream)
         for l in range(n_layers):
             d = pt.layers[c * n_layers + l]
-            bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
-                          stream=stream)
+            if pt.kv == "int8":
+                bd.pkv_append_int8(qb["kn"], qb["vn"], plan.slot_mapping, d.k_codes, d.v_codes,
+                                   d.kv_scales, stream=stream)
+            else:
+                bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
+                              stream=stream)
             if plan.n_prefill:
                 if record:
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
@@ -303,9 +330,15 @@ def run(args):
             if plan.n_decode:
                 if record:
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
-                bd.pkv_attn_decode(qb["od"], qb["qd"], d.k_cache, d.v_cache, plan.bt_decode,
-                                   plan.ctx_decode, plan.max_ctx_decode, plan.scale,
-                                   workspace=plan.workspace, stream=stream)
+                if pt.kv == "int8":
+                    bd.pkv_attn_decode_int8(qb["od"], qb["qd"], d.k_codes, d.v_codes,
+                                            d.kv_scales, plan.bt_decode, plan.ctx_decode,
+                                            plan.max_ctx_decode, plan.scale,
+                                            workspace=plan.workspace, stream=stream)
+                else:
+                    bd.pkv_attn_decode(qb["od"], qb["qd"], d.k_cache, d.v_cache,
+                                       plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode,
+                                       plan.scale, workspace=plan.workspace, stream=stream)
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     dec_events.append((k, e0, e1))
@@ -365,8 +398,10 @@ def run(args):
         achieved = sum(byts) / sum(durs) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(args.workload),
-                    "kernel": "decode_kernel (pkv_attn_decode)",
+                    "traffic": measured_traffic(args.workload if args.kv == "bf16"
+                                                else f"{args.workload}-int8"),
+                    "kernel": ("decode_kernel (pkv_attn_decode)" if args.kv == "bf16"
+                               else "decode_kernel<Int8Page> (pkv_attn_decode_int8)"),
                     "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / len(byts)),
                     "launches": len(durs),
@@ -393,11 +428,14 @@ def run(args):
                           p.plan.max_ctx_decode) if p.w.decode_seqs else 0}
                      for p in parts[:2]],
            "page_tokens": 16,
+           "kv_pages": ("bf16" if args.kv == "bf16" else
+                        "int8 codes + float32 (K, V) scale per slot and KV head"),
            "launch": "HIP graph per step, one stream" if args.graph else "eager, one stream"}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(1e3 * elapsed / args.steps, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if args.kv == "bf16" else "int8 pages, bf16 q/out",
            "data": "synthetic (seeded N(0,1) bf16, random page placement)",
            "config": cfg, "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
            "decode_tokens_per_s": round(dec_tokens / elapsed, 1), "roofline": roofline}
@@ -413,6 +451,7 @@ def cpu_baseline(args, parts):
     import torch
     from threadpoolctl import threadpool_limits
 
+    from oracle import pkv_int8_oracle as Q
     from oracle import pkv_oracle as O
     from paged_kv_gqa_pkv_amd import synth as S
 
@@ -423,9 +462,17 @@ def cpu_baseline(args, parts):
     budget = args.cpu_seconds / len(parts[:2])
     for pt in parts[:2]:
         w, t = pt.w, pt.t
-        d = S.make_layer(w, t, 0)
-        # the oracle reads pools in the pages' token-major order (an axis permutation)
-        kc0, vc0 = u16(d.k_cache.transpose(1, 2).contiguous()), u16(d.v_cache.transpose(1, 2).contiguous())
+        # the oracle reads pools in the pages' token-major order (axis permutations)
+        if pt.kv == "int8":
+            d = S.make_layer_int8(w, t, 0)
+            kc0 = d.k_codes.transpose(1, 2).contiguous().numpy()
+            vc0 = d.v_codes.transpose(1, 2).contiguous().numpy()
+            per_slot = d.kv_scales.permute(0, 3, 2, 1, 4).reshape(w.num_blocks, 16, w.Hkv, 2)
+            ks0, vs0 = per_slot[..., 0].contiguous().numpy(), per_slot[..., 1].contiguous().numpy()
+        else:
+            d = S.make_layer(w, t, 0)
+            kc0 = u16(d.k_cache.transpose(1, 2).contiguous())
+            vc0 = u16(d.v_cache.transpose(1, 2).contiguous())
         kn, vn = u16(d.k_new), u16(d.v_new)
         qd = u16(d.q_decode) if d.q_decode is not None else None
         qp = u16(d.q_prefill) if d.q_prefill is not None else None
@@ -438,6 +485,14 @@ def cpu_baseline(args, parts):
             t0 = time.perf_counter()
             while True:
                 slots = O.slot_ref(bt, cu, ctx)
+                if pt.kv == "int8":
+                    kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, kn, vn, slots)
+                    Q.decode_int8_ref(qd, kc, ks, vc, vs, bt, ctx, scale)
+                    reps += 1
+                    used = time.perf_counter() - t0
+                    if used >= budget:
+                        break
+                    continue
                 kc, vc = O.append_ref(kc0, vc0, kn, vn, slots)
                 if npre:
                     O.prefill_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, vc, bt[:npre],
