@@ -100,6 +100,24 @@ def append_ref(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
     return kc, vc
 
 
+def copy_blocks_ref(pool: np.ndarray, src: Sequence[int], dst: Sequence[int]) -> np.ndarray:
+    """Copy-on-write / fork page copy ([P1] paged.py, SequenceCache._cow_copy
+    and fork_from: ``k[:, nb] = k[:, src]``, the same for v): for each pair,
+    in order, every layer's block dst becomes a bit copy of block src.
+
+    pool: [n_layers][num_blocks][...] of any dtype (bits are copied).
+    Returns an updated copy; raises IndexError for a block outside the pool.
+    """
+    out = np.array(pool, copy=True)
+    nb = out.shape[1]
+    for s, d in zip(src, dst):
+        s, d = int(s), int(d)
+        if not (0 <= s < nb and 0 <= d < nb):
+            raise IndexError(f"block pair ({s}, {d}) outside a pool of {nb} blocks")
+        out[:, d] = out[:, s]
+    return out
+
+
 def gather_ref(cache: np.ndarray, table_row: Sequence[int], n: int,
                block_size: int = BLOCK_SIZE) -> np.ndarray:
     """Logical positions 0..n-1 of one sequence -> contiguous [n][Hkv][D]

@@ -561,6 +561,54 @@ def test_pool_bytes_of_the_0p6b_engine():
     assert 512 * per_layer_page * 28 == 896 * (1 << 20)
 
 
+def check_copy_on_write_scenario():
+    """[P1] test_copy_on_write (block size 4, one layer, one KV head, D 8):
+    sequence a writes 4 zero rows into its block; b forks from a, whose last
+    block is copied to a fresh block (fork_from); b then writes 4 rows of
+    ones into its next block.  The fork's block holds a's rows, a's block is
+    unchanged, and the write went to a block a does not use."""
+    bs, nb = 4, 8
+    pool = np.full((1, nb, bs, 1, 8), 0x7FC0, dtype=np.uint16)    # [L][blocks][slot][Hkv][D]
+    zeros = np.zeros((4, 1, 8), dtype=np.uint16)                   # bf16 +0.0
+    ones = np.full((4, 1, 8), 0x3F80, dtype=np.uint16)             # bf16 1.0
+    a_blocks = [2]
+    slots = O.slot_ref([a_blocks], [0, 4], [4], block_size=bs)
+    pool[0], _ = O.append_ref(pool[0], pool[0], zeros, zeros, slots, block_size=bs)
+    b_blocks = [5]                                                 # fork: tail copied (COW)
+    pool = O.copy_blocks_ref(pool, [a_blocks[-1]], [b_blocks[-1]])
+    assert np.array_equal(pool[0, 5], pool[0, 2])
+    b_blocks.append(6)                                             # b.reserve(4)
+    slots = O.slot_ref([b_blocks], [0, 4], [8], block_size=bs)
+    pool[0], _ = O.append_ref(pool[0], pool[0], ones, ones, slots, block_size=bs)
+    assert b_blocks[-1] != a_blocks[-1]
+    assert np.all(pool[0, 2] == 0) and np.all(pool[0, 5] == 0) and np.all(pool[0, 6] == 0x3F80)
+    assert np.all(pool[0, [0, 1, 3, 4, 7]] == 0x7FC0)
+
+
+def check_copy_blocks_bits_all_layers():
+    """Every layer's destination block becomes the source's bits (NaN
+    payloads, -0.0); sources and other blocks are untouched; pairs run in
+    order (a chain 1->3, 3->4 leaves block 4 equal to block 1)."""
+    rng = np.random.default_rng(40)
+    pool = rng.integers(0, 1 << 16, size=(3, 6, BS, 2, 4), dtype=np.uint16)
+    pool[1, 1, 0, 0, 0] = 0x7FC1
+    pool[2, 1, 3, 1, 2] = 0x8000
+    out = O.copy_blocks_ref(pool, [1, 3, 0], [3, 4, 5])
+    assert np.array_equal(out[:, 3], pool[:, 1]) and np.array_equal(out[:, 4], pool[:, 1])
+    assert np.array_equal(out[:, 5], pool[:, 0])
+    assert np.array_equal(out[:, :3], pool[:, :3])
+    with pytest.raises(IndexError):
+        O.copy_blocks_ref(pool, [6], [0])
+
+
+def test_copy_on_write_scenario():
+    check_copy_on_write_scenario()
+
+
+def test_copy_blocks_bits_all_layers():
+    check_copy_blocks_bits_all_layers()
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each one must fail at least one pin above
 # ---------------------------------------------------------------------------
@@ -568,7 +616,8 @@ def test_pool_bytes_of_the_0p6b_engine():
 PINS = [check_decode_brute_force, check_hand_example, check_ctx1_returns_v0,
         check_zero_query_gives_mean, check_dominant_key, check_rows_sum_to_one,
         check_gqa_equals_repeated_mha, check_prefill_brute_force, check_causal_hand_example,
-        check_mask_equivalence, check_reserve20_example, check_decode_slots_follow_context]
+        check_mask_equivalence, check_reserve20_example, check_decode_slots_follow_context,
+        check_copy_on_write_scenario, check_copy_blocks_bits_all_layers]
 
 
 def _mutants():
@@ -604,7 +653,15 @@ def _mutants():
                     out[lo + t, h] = orig_attend(O.bf16_to_f64(q[lo + t, h]), K[:qp, g], V[:qp, g], scale)
         return out
 
+    orig_copy = O.copy_blocks_ref
+
+    def copy_first_layer_only(pool, src, dst):
+        out = np.array(pool, copy=True)
+        out[:1] = orig_copy(pool[:1], src, dst)
+        return out
+
     return {
+        "block copy of layer 0 only": ("copy_blocks_ref", copy_first_layer_only),
         "head map h % Hkv": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
         "scale dropped": ("attend_one", lambda q, K, V, s: orig_attend(q, K, V, 1.0)),
         "scale applied twice": ("attend_one", lambda q, K, V, s: orig_attend(q, K, V, s * s)),
