@@ -105,6 +105,29 @@ int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping
                int32_t Hkv, int32_t D, int32_t block_size, void* stream);
 
 /*
+ * Block copy for copy-on-write and fork ([P1] paged.py: SequenceCache._cow_copy
+ * and fork_from copy block src to a fresh block nb in every layer,
+ * k[:, nb] = k[:, src] and the same for v; [P3] "Paged Attention": a shared
+ * page is copied before it is written).  For every pair i, block
+ * dst_blocks[i] of every layer of k_pool (and of v_pool unless it is NULL)
+ * becomes a bit copy of block src_blocks[i].
+ *   k_pool, v_pool   device memory holding n_layers pools, layer l starting
+ *                    at pool + l * layer_stride_bytes, block b of a layer at
+ *                    b * block_bytes from its start (any page format: bf16
+ *                    pools have block_bytes = Hkv*16*D*2, int8 codes
+ *                    Hkv*16*D, int8 scale arrays Hkv*16*2*4 with v_pool NULL)
+ *   src_blocks, dst_blocks  int32 [n_pairs], device
+ * Pointers, block_bytes and layer_stride_bytes must be multiples of 16.
+ * Destinations must be distinct and no destination may be a source (the
+ * pairs run in parallel; PKV_VALIDATE=1 rejects such pairs and ids outside
+ * [0, num_blocks)); without it, pairs with an id outside the pool are skipped.
+ */
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                    const int32_t* dst_blocks, int32_t n_pairs, int32_t num_blocks,
+                    int64_t block_bytes, int32_t n_layers, int64_t layer_stride_bytes,
+                    void* stream);
+
+/*
  * Workspace for pkv_attn_decode: bytes of device memory the split-context
  * path needs for the given shape (0 when the call runs in a single pass).
  * Depends on the current device's compute-unit count.  Returns 0 for

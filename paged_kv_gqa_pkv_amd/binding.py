@@ -36,6 +36,8 @@ SIGNATURES = {
     "pkv_attn_decode_int8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _f, _vp, _c_size,
                                       _vp]),
+    "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _c_int,
+                                 ctypes.c_int64, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -242,3 +244,37 @@ def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tens
                                        _p(block_tables), _p(context_lens), B, Hq, Hkv, D, bs, nb,
                                        block_tables.shape[1], int(max_context_len), float(scale),
                                        ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pkv_copy_blocks(src_blocks: torch.Tensor, dst_blocks: torch.Tensor, k_pool: torch.Tensor,
+                    v_pool: Optional[torch.Tensor] = None, layered: bool = False,
+                    stream=None) -> None:
+    """Copy block src -> dst in every layer of the pools (copy-on-write / fork).
+    layered=False: a pool is one layer, [num_blocks, ...], contiguous.
+    layered=True: a pool is [n_layers, num_blocks, ...]; each layer contiguous,
+    layers any 16-byte multiple apart."""
+    _need(src_blocks, torch.int32, "src_blocks", 1)
+    _need(dst_blocks, torch.int32, "dst_blocks", 1)
+    if src_blocks.numel() != dst_blocks.numel():
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    pools = [k_pool] + ([v_pool] if v_pool is not None else [])
+    if len({tuple(p.shape) for p in pools}) != 1 or len({p.dtype for p in pools}) != 1 or \
+            len({p.stride() for p in pools}) != 1:
+        raise ValueError("k_pool and v_pool differ in shape, dtype or strides")
+    if not all(p.is_cuda for p in pools):
+        raise TypeError("pools must be device tensors")
+    if layered:
+        if k_pool.dim() < 3:
+            raise ValueError("a layered pool is [n_layers, num_blocks, ...]")
+        if not all(p[0].is_contiguous() for p in pools):
+            raise ValueError("each layer of a pool must be contiguous")
+        n_layers, num_blocks = k_pool.shape[0], k_pool.shape[1]
+        stride = k_pool.stride(0) * k_pool.element_size()
+    else:
+        if k_pool.dim() < 2 or not all(p.is_contiguous() for p in pools):
+            raise ValueError("a pool is a contiguous [num_blocks, ...] tensor")
+        n_layers, num_blocks, stride = 1, k_pool.shape[0], 0
+    block_bytes = (k_pool[0, 0] if layered else k_pool[0]).numel() * k_pool.element_size()
+    _check(load().pkv_copy_blocks(_p(k_pool), _p(v_pool), _p(src_blocks), _p(dst_blocks),
+                                  src_blocks.numel(), num_blocks, block_bytes, n_layers, stride,
+                                  _stream(stream)))

@@ -133,6 +133,49 @@ hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_
   return hipGetLastError();
 }
 
+// Copy-on-write / fork page copy (Module 12 page, paged.py:
+// SequenceCache._cow_copy and fork_from copy block src to a fresh block dst
+// in every layer, K and V).  One work item is one 16-byte chunk of one block
+// of one layer of one pool; consecutive threads take consecutive chunks, so
+// reads and writes are contiguous runs of the block.  Pairs whose ids fall
+// outside the pool are skipped.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                   int64_t n_items, int64_t chunks_per_block, int pools, int n_layers,
+                   int64_t layer_stride, int num_blocks) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t block_bytes = chunks_per_block * 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_items; i += stride) {
+    const int64_t c = i % chunks_per_block;
+    int64_t rest = i / chunks_per_block;
+    const int pool = (int)(rest % pools);
+    rest /= pools;
+    const int layer = (int)(rest % n_layers);
+    const int64_t pair = rest / n_layers;
+    const int s = src[pair], d = dst[pair];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) continue;
+    char* base = (pool ? v_pool : k_pool) + layer * layer_stride;
+    reinterpret_cast<u32x4*>(base + d * block_bytes)[c] =
+        reinterpret_cast<const u32x4*>(base + s * block_bytes)[c];
+  }
+}
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                              int n_pairs, int num_blocks, int64_t block_bytes, int n_layers,
+                              int64_t layer_stride, hipStream_t stream) {
+  if (n_pairs == 0 || n_layers == 0 || block_bytes == 0) return hipSuccess;
+  const int pools = v_pool ? 2 : 1;
+  const int64_t cpb = block_bytes / 16;
+  const int64_t n_items = (int64_t)n_pairs * n_layers * pools * cpb;
+  int64_t blocks = (n_items + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), src, dst, n_items,
+                     cpb, pools, n_layers, layer_stride, num_blocks);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* block_tables, const int32_t* cu_new,
                                const int32_t* ctx_lens, int B, int max_blocks, int total_new,
                                hipStream_t stream) {

@@ -237,6 +237,43 @@ int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_ma
                        "pkv_append_int8");
 }
 
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                    const int32_t* dst_blocks, int32_t n_pairs, int32_t num_blocks,
+                    int64_t block_bytes, int32_t n_layers, int64_t layer_stride_bytes,
+                    void* stream) {
+  if (n_pairs < 0 || num_blocks < 0 || block_bytes < 0 || n_layers < 0 || layer_stride_bytes < 0)
+    return fail(PKV_EINVAL, "negative size");
+  if (n_pairs == 0 || n_layers == 0 || block_bytes == 0) return PKV_OK;
+  if (!k_pool || !src_blocks || !dst_blocks) return fail(PKV_EINVAL, "null pointer argument");
+  if (k_pool == v_pool) return fail(PKV_EINVAL, "k_pool and v_pool must differ");
+  if (block_bytes % 16 || layer_stride_bytes % 16 || (uintptr_t)k_pool % 16 ||
+      (uintptr_t)v_pool % 16)
+    return fail(PKV_EINVAL, "pools, block_bytes and layer_stride_bytes must be 16-byte aligned");
+  if (n_layers > 1 && layer_stride_bytes < (int64_t)num_blocks * block_bytes)
+    return fail(PKV_EINVAL, "layer_stride_bytes=%lld is smaller than a layer's %d blocks",
+                (long long)layer_stride_bytes, num_blocks);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> src, dst;
+    if (!to_host(src, src_blocks, (size_t)n_pairs, s) || !to_host(dst, dst_blocks, (size_t)n_pairs, s))
+      return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of the block pairs failed");
+    std::unordered_set<int32_t> srcs(src.begin(), src.end()), dsts;
+    for (int i = 0; i < n_pairs; ++i) {
+      if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
+        return fail(PKV_EVALIDATE, "pair %d (%d -> %d) outside a pool of %d blocks", i, src[i],
+                    dst[i], num_blocks);
+      if (!dsts.insert(dst[i]).second)
+        return fail(PKV_EVALIDATE, "block %d is a destination twice", dst[i]);
+      if (srcs.count(dst[i]))
+        return fail(PKV_EVALIDATE, "block %d is both a source and a destination", dst[i]);
+    }
+  }
+  return launch_status(pkv::launch_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, n_pairs,
+                                               num_blocks, block_bytes, n_layers,
+                                               layer_stride_bytes, s),
+                       "pkv_copy_blocks");
+}
+
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                   int32_t max_context_len) {
   if (B <= 0 || max_context_len < 0 || check_geometry(Hq, Hkv, D, PKV_BLOCK_SIZE) != PKV_OK)

@@ -15,6 +15,13 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* sl
                          void* k_cache, void* v_cache, int T, int num_blocks, int Hkv, int D,
                          hipStream_t stream);
 
+// Block copy for copy-on-write and fork: for each pair, block dst of every
+// layer of k_pool (and v_pool if not null) becomes a copy of block src.
+// Pool l starts at pool + l * layer_stride; blocks are block_bytes apart.
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                              int n_pairs, int num_blocks, int64_t block_bytes, int n_layers,
+                              int64_t layer_stride, hipStream_t stream);
+
 // Split plan of a decode call: S splits of pages_per_split pages each.
 struct DecodePlan {
   int splits;

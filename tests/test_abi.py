@@ -108,3 +108,30 @@ def test_header_documents_each_entry_point():
         assert m, name
         before = src[:m.start()].rstrip()
         assert before.endswith("*/"), f"{name} has no comment right above its declaration"
+
+
+def test_int8_entry_points_reject_bad_arguments(lib):
+    # append: D other than 128, null pointers, same code pool for K and V, nothing to do
+    assert lib.pkv_append_int8(1, 1, 1, 16, 32, 48, 4, 8, 8, 64, 16, NULL) == bd.PKV_EUNSUPPORTED
+    assert lib.pkv_append_int8(1, 1, 1, 16, 32, NULL, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_append_int8(1, 1, 1, 16, 16, 48, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_append_int8(NULL, NULL, NULL, NULL, NULL, NULL, 0, 8, 8, 128, 16,
+                               NULL) == bd.PKV_OK
+    # decode: missing scales, group size 3
+    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, NULL, 5, 6, 2, 16, 8, 128, 16, 32, 4, 64, 0.088,
+                                    NULL, 0, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, 5, 5, 6, 2, 24, 8, 128, 16, 32, 4, 64, 0.088,
+                                    NULL, 0, NULL) == bd.PKV_EUNSUPPORTED
+
+
+def test_copy_blocks_rejects_bad_arguments(lib):
+    call = lambda **k: lib.pkv_copy_blocks(
+        k.get("kp", 16), k.get("vp", 32), 48, 64, k.get("n", 2), k.get("nb", 8),
+        k.get("bb", 1024), k.get("layers", 1), k.get("stride", 0), NULL)
+    assert call(n=-1) == bd.PKV_EINVAL
+    assert call(bb=1000) == bd.PKV_EINVAL                      # not a multiple of 16
+    assert call(kp=8) == bd.PKV_EINVAL                         # misaligned pool
+    assert call(kp=16, vp=16) == bd.PKV_EINVAL                 # same pool twice
+    assert call(layers=2, stride=4096) == bd.PKV_EINVAL         # layers overlap (8 x 1024 B)
+    assert b"layer_stride" in lib.pkv_last_error()
+    assert call(n=0) == bd.PKV_OK and call(layers=0) == bd.PKV_OK
