@@ -216,6 +216,103 @@ def prefill_ref(q: np.ndarray, cu_q: Sequence[int], k_cache: np.ndarray,
     return out
 
 
+# --------------------------------------------------------------------------
+# Ring (sliding-window) paging  ([P2] section 4, "Capacity-cache": past
+# capacity the cache becomes a ring, position p written at p % capacity,
+# the oldest token overwritten; reads return the last min(end, capacity)
+# positions with their absolute positions; the mask compares absolute
+# positions.  [P2] kv_cache.py listing, KVCache.write/read and ring_demo.)
+# A ring of W tokens is the first W/block_size pages of a sequence's table.
+# --------------------------------------------------------------------------
+
+def ring_slot_ref(block_tables: Sequence[Sequence[int]], cu_new: Sequence[int],
+                  context_lens: Sequence[int], window: int,
+                  block_size: int = BLOCK_SIZE) -> List[int]:
+    """Slots of the appended tokens when each sequence's pages form a ring of
+    ``window`` tokens: position p is written at ring index p % window."""
+    if window <= 0 or window % block_size:
+        raise ValueError("window must be a positive multiple of the block size")
+    out: List[int] = []
+    for b in range(len(context_lens)):
+        n_new = int(cu_new[b + 1]) - int(cu_new[b])
+        start = int(context_lens[b]) - n_new
+        if n_new < 0 or start < 0:
+            raise ValueError("inconsistent lengths")
+        for p in range(start, start + n_new):
+            page, offset = divmod(p % window, block_size)
+            out.append(int(block_tables[b][page]) * block_size + offset)
+    return out
+
+
+def ring_read_ref(cache: np.ndarray, table_row: Sequence[int], end: int, window: int,
+                  block_size: int = BLOCK_SIZE) -> Tuple[np.ndarray, np.ndarray]:
+    """The ring's contents after ``end`` tokens were written: the rows of the
+    last min(end, window) positions in increasing position order, and those
+    absolute positions."""
+    n = min(end, window)
+    pos = np.arange(end - n, end)
+    rows = []
+    for p in pos:
+        page, offset = divmod(int(p) % window, block_size)
+        rows.append(cache[int(table_row[page]), offset])
+    if not rows:
+        return np.zeros((0,) + tuple(cache.shape[2:]), dtype=cache.dtype), pos
+    return np.stack(rows), pos
+
+
+def ring_decode_ref(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                    block_tables: Sequence[Sequence[int]], context_lens: Sequence[int],
+                    window: int, scale: float, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Decode over rings: the query at position n-1 attends to the ring's
+    keys (positions n - min(n, window) .. n-1, all at or before it)."""
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(context_lens[b])
+        if n == 0:
+            continue
+        Kb, _ = ring_read_ref(k_cache, block_tables[b], n, window, block_size)
+        Vb, _ = ring_read_ref(v_cache, block_tables[b], n, window, block_size)
+        K, V = bf16_to_f64(Kb), bf16_to_f64(Vb)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            out[b, h] = attend_one(bf16_to_f64(q[b, h]), K[:, g, :], V[:, g, :], scale)
+    return out
+
+
+def ring_prefill_ref(q: np.ndarray, cu_q: Sequence[int], k_cache: np.ndarray,
+                     v_cache: np.ndarray, block_tables: Sequence[Sequence[int]],
+                     context_lens: Sequence[int], window: int, scale: float,
+                     block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """A chunk over rings, after the chunk was written: row t (absolute
+    position n - T + t) attends to the ring's keys whose absolute position is
+    at most its own ([P2]: mask k_pos <= q_pos on the positions read returns)."""
+    total_q, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    out = np.zeros((total_q, Hq, D), dtype=np.float64)
+    for b in range(len(context_lens)):
+        lo, hi = int(cu_q[b]), int(cu_q[b + 1])
+        T, n = hi - lo, int(context_lens[b])
+        if T == 0:
+            continue
+        if T > n:
+            raise ValueError("more query rows than context")
+        Kb, pos = ring_read_ref(k_cache, block_tables[b], n, window, block_size)
+        Vb, _ = ring_read_ref(v_cache, block_tables[b], n, window, block_size)
+        K, V = bf16_to_f64(Kb), bf16_to_f64(Vb)
+        for t in range(T):
+            qpos = n - T + t
+            vis = pos <= qpos
+            if not np.any(vis):
+                raise ValueError("a query row sees no key (chunk longer than the ring)")
+            for h in range(Hq):
+                g = kv_head_of(h, Hq, Hkv)
+                out[lo + t, h] = attend_one(bf16_to_f64(q[lo + t, h]), K[vis, g, :],
+                                            V[vis, g, :], scale)
+    return out
+
+
 def decode_weights_ref(q_row: np.ndarray, k_cache: np.ndarray, table_row: Sequence[int],
                        n: int, g: int, scale: float,
                        block_size: int = BLOCK_SIZE) -> np.ndarray:
