@@ -250,6 +250,54 @@ int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const vo
                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Ring (sliding-window) paging ([P2] section 4, "Capacity-cache": beyond the
+ * capacity the cache becomes a ring, position p is written at index
+ * p % capacity over the oldest token, a read returns the last
+ * min(end, capacity) positions with their absolute positions, and the causal
+ * mask compares absolute positions; [P2] kv_cache.py listing,
+ * KVCache.write/read).  A sequence's ring of `window` tokens (a positive
+ * multiple of 16, at most max_blocks_per_seq * 16) is the first window / 16
+ * pages of its table: position p lives at page (p % window) / 16, offset
+ * p % 16.  context_lens count every position written so far and may exceed
+ * the table.  Each call below behaves as its non-ring counterpart except:
+ *   pkv_slot_mapping_ring       slots of positions p at ring index p % window;
+ *   pkv_attn_decode_ring        the query attends to the ring's min(n, window)
+ *                               keys (a sliding window of `window` tokens);
+ *                               workspace: pkv_decode_workspace_bytes(B, Hq,
+ *                               Hkv, D, min(max_context_len, window));
+ *   pkv_attn_prefill_chunk_ring the chunk is in the ring already; row t at
+ *                               position n - T + t attends to the ring's keys
+ *                               at positions max(0, n - window) .. its own;
+ *                               max_q_len <= window; workspace:
+ *                               pkv_prefill_workspace_bytes(B, max_q_len, Hq,
+ *                               Hkv, D, min(max_context_len, window + 64)).
+ */
+int pkv_slot_mapping_ring(int32_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* cu_new_lens, const int32_t* context_lens, int32_t B,
+                          int32_t max_blocks_per_seq, int32_t total_new, int32_t block_size,
+                          int32_t window, void* stream);
+
+/* Decode over rings ([P2] section 4): the query at position n - 1 attends to
+ * the last min(n, window) positions, all held by the ring. */
+int pkv_attn_decode_ring(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t window, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Causal chunk over rings ([P2] section 4 and KVCache.read: the chunk is
+ * written first; its rows see the ring's keys at or before their position). */
+int pkv_attn_prefill_chunk_ring(void* out, const void* q, const int32_t* cu_q_lens,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t total_q, int32_t max_q_len, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len,
+                                int32_t window, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Thread-local message describing the last non-OK return on this thread. */
 const char* pkv_last_error(void);
 

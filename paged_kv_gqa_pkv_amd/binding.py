@@ -38,6 +38,14 @@ SIGNATURES = {
                                       _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _c_int,
                                  ctypes.c_int64, _vp]),
+    "pkv_slot_mapping_ring": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _vp]),
+    "pkv_attn_decode_ring": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _f, _vp,
+                                      _c_size, _vp]),
+    "pkv_attn_prefill_chunk_ring": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -278,3 +286,66 @@ def pkv_copy_blocks(src_blocks: torch.Tensor, dst_blocks: torch.Tensor, k_pool: 
     _check(load().pkv_copy_blocks(_p(k_pool), _p(v_pool), _p(src_blocks), _p(dst_blocks),
                                   src_blocks.numel(), num_blocks, block_bytes, n_layers, stride,
                                   _stream(stream)))
+
+
+def pkv_slot_mapping_ring(slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                          cu_new_lens: torch.Tensor, context_lens: torch.Tensor, window: int,
+                          stream=None) -> None:
+    """slot_mapping <- ring slots (position p at ring index p % window)."""
+    for t, n in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"),
+                 (cu_new_lens, "cu_new_lens"), (context_lens, "context_lens")):
+        _need(t, torch.int32, n)
+    B, mb = block_tables.shape
+    _check(load().pkv_slot_mapping_ring(_p(slot_mapping), _p(block_tables), _p(cu_new_lens),
+                                        _p(context_lens), B, mb, slot_mapping.numel(),
+                                        BLOCK_SIZE, int(window), _stream(stream)))
+
+
+def pkv_attn_decode_ring(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                         v_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, max_context_len: int, window: int,
+                         scale: float, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """Decode over rings of `window` tokens (a sliding window)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
+            block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent shapes")
+    ws_ptr, ws_bytes = _ws(workspace)
+    _check(load().pkv_attn_decode_ring(_p(out), _p(q), _p(k_cache), _p(v_cache),
+                                       _p(block_tables), _p(context_lens), B, Hq, Hkv, D, bs, nb,
+                                       block_tables.shape[1], int(max_context_len), int(window),
+                                       float(scale), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pkv_attn_prefill_chunk_ring(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                                k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                max_q_len: int, max_context_len: int, window: int, scale: float,
+                                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Causal chunk over rings of `window` tokens."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    for t, n in ((cu_q_lens, "cu_q_lens"), (context_lens, "context_lens")):
+        _need(t, torch.int32, n, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    total_q, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    B = context_lens.numel()
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
+            block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
+        raise ValueError("inconsistent shapes")
+    _check(load().pkv_attn_prefill_chunk_ring(
+        _p(out), _p(q), _p(cu_q_lens), _p(k_cache), _p(v_cache), _p(block_tables),
+        _p(context_lens), B, total_q, int(max_q_len), Hq, Hkv, D, bs, nb,
+        block_tables.shape[1], int(max_context_len), int(window), float(scale),
+        *_ws(workspace), _stream(stream)))

@@ -81,6 +81,7 @@ struct DecodeArgs {
   float* ws_acc;                 // [B][Hq][S][D]
   int* counters;                 // [B][Hkv] arrivals per (sequence, KV head); zero between calls
   int B, Hq, Hkv, num_blocks, max_blocks, splits, pages_per_split;
+  int window;                    // > 0: each sequence's pages form a ring of `window` tokens
   float scale_log2;              // scale * log2(e)
 };
 
@@ -366,7 +367,12 @@ decode_kernel(const DecodeArgs a) {
 
   // A length outside [0, planned maximum] poisons the outputs of the sequence
   // (the plan covers splits * pages_per_split pages; no read goes past it).
-  const int n = a.ctx_lens[b];
+  // Ring paging (Module 04 page, section 4): a ring of `window` tokens holds
+  // the last min(n, window) positions, all at or before the query, in ring
+  // slots 0 .. min(n, window) - 1; attention does not depend on their order,
+  // so the ring is read like a sequence of that many tokens.
+  const int n_ctx = a.ctx_lens[b];
+  const int n = (a.window > 0 && n_ctx > a.window) ? a.window : n_ctx;
   const bool bad_len = n < 0 || n > a.max_blocks * kPage ||
                        (n + kPage - 1) / kPage > S * a.pages_per_split;
   const int n_pages = bad_len ? 0 : (n + kPage - 1) / kPage;
@@ -600,7 +606,7 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
                      const float* kv_scales,
                      const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
                      int Hkv, int num_blocks, int max_blocks, float scale,
-                     const DecodePlan& plan, void* workspace) {
+                     const DecodePlan& plan, void* workspace, int window) {
   DecodeArgs a;
   a.out = static_cast<uint16_t*>(out);
   a.q = static_cast<const u32x4*>(q);
@@ -617,6 +623,7 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
                      : nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
   a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
+  a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;
 }
@@ -670,12 +677,12 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus)
 
 hipError_t launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
-                         int Hkv, int num_blocks, int max_blocks, float scale,
+                         int Hkv, int num_blocks, int max_blocks, float scale, int window,
                          const DecodePlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables,
                                  ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
-                                 workspace);
+                                 workspace, window);
   switch (Hq / Hkv) {
     case 1: return launch_g<Bf16Page, 1, PKV_DECODE_U_G1>(a, stream);
     case 2: return launch_g<Bf16Page, 2, PKV_DECODE_U_G2>(a, stream);
@@ -693,7 +700,7 @@ hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, con
   if (B == 0) return hipSuccess;
   const DecodeArgs a = make_args(out, q, k_codes, v_codes, kv_scales, block_tables,
                                  ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
-                                 workspace);
+                                 workspace, 0);
   switch (Hq / Hkv) {
     case 1: return launch_g<Int8Page, 1, PKV_DECODE_I8_U_G1>(a, stream);
     case 2: return launch_g<Int8Page, 2, PKV_DECODE_I8_U_G2>(a, stream);

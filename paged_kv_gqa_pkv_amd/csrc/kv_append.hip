@@ -17,7 +17,7 @@ namespace pkv {
 __global__ void __launch_bounds__(256)
 slot_mapping_kernel(int32_t* __restrict__ slots, const int32_t* __restrict__ block_tables,
                     const int32_t* __restrict__ cu_new, const int32_t* __restrict__ ctx_lens,
-                    int B, int max_blocks, int total_new) {
+                    int B, int max_blocks, int total_new, int window) {
   int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= total_new) return;
   int lo = 0, hi = B;               // find b with cu[b] <= t < cu[b+1]
@@ -28,6 +28,9 @@ slot_mapping_kernel(int32_t* __restrict__ slots, const int32_t* __restrict__ blo
   int b = lo;
   int n_new = cu_new[b + 1] - cu_new[b];
   int p = ctx_lens[b] - n_new + (t - cu_new[b]);
+  // A ring of `window` tokens (Module 04 page, section 4) writes position p at
+  // ring index p % window.
+  if (window > 0 && p >= 0) p %= window;
   int page = p >> 4;
   int slot = -1;
   if (p >= 0 && page < max_blocks) {
@@ -178,11 +181,11 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, co
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* block_tables, const int32_t* cu_new,
                                const int32_t* ctx_lens, int B, int max_blocks, int total_new,
-                               hipStream_t stream) {
+                               int window, hipStream_t stream) {
   if (total_new == 0) return hipSuccess;
   dim3 grid((total_new + 255) / 256);
   hipLaunchKernelGGL(slot_mapping_kernel, grid, dim3(256), 0, stream, slots, block_tables, cu_new,
-                     ctx_lens, B, max_blocks, total_new);
+                     ctx_lens, B, max_blocks, total_new, window);
   return hipGetLastError();
 }
 

@@ -81,7 +81,7 @@ bool to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
 // PKV_VALIDATE: block tables and lengths of a decode/prefill call.
 int validate_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
-                    hipStream_t stream) {
+                    hipStream_t stream, int32_t window = 0) {
   std::vector<int32_t> ctx, bt;
   if (!to_host(ctx, context_lens, (size_t)B, stream) ||
       !to_host(bt, block_tables, (size_t)B * max_blocks, stream))
@@ -91,10 +91,11 @@ int validate_tables(const int32_t* block_tables, const int32_t* context_lens, in
     if (n < 0 || n > max_context_len)
       return fail(PKV_EVALIDATE, "context_lens[%d]=%d outside [0, max_context_len=%d]", b, n,
                   max_context_len);
-    if (n > max_blocks * PKV_BLOCK_SIZE)
+    if (window == 0 && n > max_blocks * PKV_BLOCK_SIZE)
       return fail(PKV_EVALIDATE, "context_lens[%d]=%d exceeds the table (%d pages)", b, n,
                   max_blocks);
-    for (int i = 0; i < (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE; ++i) {
+    const int used = window > 0 && n > window ? window : n;   // a ring uses its first pages
+    for (int i = 0; i < (used + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE; ++i) {
       const int blk = bt[(size_t)b * max_blocks + i];
       if (blk < 0 || blk >= num_blocks)
         return fail(PKV_EVALIDATE, "block_tables[%d][%d]=%d outside [0, %d)", b, i, blk,
@@ -122,6 +123,16 @@ int validate_slots(const int32_t* slot_mapping, int32_t T, int32_t num_blocks, h
   return PKV_OK;
 }
 
+// A ring of `window` tokens: a positive multiple of the page size that fits the table.
+int check_window(int32_t window, int32_t max_blocks_per_seq) {
+  if (window <= 0 || window % PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "window=%d must be a positive multiple of %d", window, PKV_BLOCK_SIZE);
+  if (window > max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "window=%d exceeds the block table (%d pages)", window,
+                max_blocks_per_seq);
+  return PKV_OK;
+}
+
 // Host checks shared by the decode entry points; fills the split plan.
 // done = true: nothing to launch (B == 0).
 int check_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -129,7 +140,7 @@ int check_decode(void* out, const void* q, const void* k_cache, const void* v_ca
                  int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                  void* workspace, size_t workspace_bytes, void* stream, pkv::DecodePlan& plan,
-                 bool& done) {
+                 bool& done, int32_t window = 0) {
   done = false;
   if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
@@ -139,17 +150,22 @@ int check_decode(void* out, const void* q, const void* k_cache, const void* v_ca
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "null pointer argument");
   if (out == q) return fail(PKV_EINVAL, "out and q must not overlap");
-  if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE)
+  if (window > 0) {
+    rc = check_window(window, max_blocks_per_seq);
+    if (rc) return rc;
+  } else if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE) {
     return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
                 max_context_len, max_blocks_per_seq);
+  }
   if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
-  plan = pkv::plan_decode(B, Hq, Hkv, max_context_len, device_cus());
+  const int32_t plan_ctx = window > 0 && max_context_len > window ? window : max_context_len;
+  plan = pkv::plan_decode(B, Hq, Hkv, plan_ctx, device_cus());
   if (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace))
     return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.ws_bytes,
                 workspace_bytes);
   if (validate_mode()) {
     rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
-                         max_context_len, static_cast<hipStream_t>(stream));
+                         max_context_len, static_cast<hipStream_t>(stream), window);
     if (rc) return rc;
   }
   return PKV_OK;
@@ -163,16 +179,20 @@ const char* pkv_last_error(void) { return g_err; }
 
 const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
 
-int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
-                     const int32_t* cu_new_lens, const int32_t* context_lens, int32_t B,
-                     int32_t max_blocks_per_seq, int32_t total_new, int32_t block_size,
-                     void* stream) {
+static int slot_mapping_impl(int32_t* slot_mapping, const int32_t* block_tables,
+                             const int32_t* cu_new_lens, const int32_t* context_lens, int32_t B,
+                             int32_t max_blocks_per_seq, int32_t total_new, int32_t block_size,
+                             int32_t window, void* stream) {
   if (B < 0 || total_new < 0 || max_blocks_per_seq < 0)
     return fail(PKV_EINVAL, "negative size");
   if (block_size != PKV_BLOCK_SIZE)
     return fail(PKV_EUNSUPPORTED, "block_size %d unsupported (pages hold 16 tokens)", block_size);
   if (total_new == 0) return PKV_OK;
   if (B == 0) return fail(PKV_EINVAL, "total_new=%d tokens but no sequences", total_new);
+  if (window > 0) {
+    const int rc = check_window(window, max_blocks_per_seq);
+    if (rc) return rc;
+  }
   if (!slot_mapping || !block_tables || !cu_new_lens || !context_lens)
     return fail(PKV_EINVAL, "null pointer argument");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -187,15 +207,33 @@ int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
       if (cu[b + 1] - cu[b] > ctx[b])
         return fail(PKV_EVALIDATE, "sequence %d appends %d tokens but its context is %d", b,
                     cu[b + 1] - cu[b], ctx[b]);
-      if (ctx[b] > max_blocks_per_seq * PKV_BLOCK_SIZE)
+      if (window == 0 && ctx[b] > max_blocks_per_seq * PKV_BLOCK_SIZE)
         return fail(PKV_EVALIDATE, "context_lens[%d]=%d exceeds the table", b, ctx[b]);
     }
   }
   return launch_status(pkv::launch_slot_mapping(slot_mapping, block_tables, cu_new_lens,
                                                 context_lens, B, max_blocks_per_seq, total_new,
-                                                s),
+                                                window, s),
                        "pkv_slot_mapping");
 }
+
+int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* cu_new_lens, const int32_t* context_lens, int32_t B,
+                     int32_t max_blocks_per_seq, int32_t total_new, int32_t block_size,
+                     void* stream) {
+  return slot_mapping_impl(slot_mapping, block_tables, cu_new_lens, context_lens, B,
+                           max_blocks_per_seq, total_new, block_size, 0, stream);
+}
+
+int pkv_slot_mapping_ring(int32_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* cu_new_lens, const int32_t* context_lens, int32_t B,
+                          int32_t max_blocks_per_seq, int32_t total_new, int32_t block_size,
+                          int32_t window, void* stream) {
+  if (window <= 0) return fail(PKV_EINVAL, "window=%d must be positive", window);
+  return slot_mapping_impl(slot_mapping, block_tables, cu_new_lens, context_lens, B,
+                           max_blocks_per_seq, total_new, block_size, window, stream);
+}
+
 
 int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
                void* v_cache, int32_t T, int32_t num_blocks, int32_t Hkv, int32_t D,
@@ -300,9 +338,28 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                         workspace, workspace_bytes, stream, plan, done);
   if (rc || done) return rc;
   return launch_status(pkv::launch_decode(out, q, k_cache, v_cache, block_tables, context_lens, B,
-                                          Hq, Hkv, num_blocks, max_blocks_per_seq, scale, plan,
+                                          Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0, plan,
                                           workspace, static_cast<hipStream_t>(stream)),
                        "pkv_attn_decode");
+}
+
+int pkv_attn_decode_ring(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t window, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (window <= 0) return fail(PKV_EINVAL, "window=%d must be positive", window);
+  pkv::DecodePlan plan;
+  bool done = false;
+  int rc = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                        workspace, workspace_bytes, stream, plan, done, window);
+  if (rc || done) return rc;
+  return launch_status(pkv::launch_decode(out, q, k_cache, v_cache, block_tables, context_lens, B,
+                                          Hq, Hkv, num_blocks, max_blocks_per_seq, scale, window,
+                                          plan, workspace, static_cast<hipStream_t>(stream)),
+                       "pkv_attn_decode_ring");
 }
 
 int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
@@ -333,13 +390,13 @@ size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int
   return pkv::plan_prefill(B, max_q_len, Hq, Hkv, max_context_len, device_cus()).ws_bytes;
 }
 
-int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
-                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                           const int32_t* context_lens, int32_t B, int32_t total_q,
-                           int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
-                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, float scale, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
+                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t B, int32_t total_q,
+                        int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
+                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, int32_t window, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
@@ -350,13 +407,21 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
     return fail(PKV_EINVAL, "null pointer argument");
   if (out == q) return fail(PKV_EINVAL, "out and q must not overlap");
   if (max_q_len > total_q) return fail(PKV_EINVAL, "max_q_len=%d > total_q=%d", max_q_len, total_q);
-  if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE)
+  if (window > 0) {
+    rc = check_window(window, max_blocks_per_seq);
+    if (rc) return rc;
+    if (max_q_len > window)
+      return fail(PKV_EINVAL, "max_q_len=%d exceeds the ring of %d tokens", max_q_len, window);
+  } else if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE) {
     return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
                 max_context_len, max_blocks_per_seq);
+  }
   if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
   if (max_q_len == 0) return PKV_OK;
-  const pkv::PrefillPlan plan =
-      pkv::plan_prefill(B, max_q_len, Hq, Hkv, max_context_len, device_cus());
+  // A ring's keys span at most window positions, i.e. window / 64 + 1 key tiles.
+  const int32_t plan_ctx =
+      window > 0 && max_context_len > window + 64 ? window + 64 : max_context_len;
+  const pkv::PrefillPlan plan = pkv::plan_prefill(B, max_q_len, Hq, Hkv, plan_ctx, device_cus());
   if (!plan.ok)
     return fail(PKV_EUNSUPPORTED, "max_context_len=%d exceeds the prefill kernel's 131072 keys",
                 max_context_len);
@@ -379,14 +444,43 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
         return fail(PKV_EVALIDATE, "sequence %d has %d query rows but context %d", b, T, ctx[b]);
     }
     rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
-                         max_context_len, s);
+                         max_context_len, s, window);
     if (rc) return rc;
   }
   return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables,
                                            context_lens, B, total_q, max_q_len, Hq, Hkv,
-                                           num_blocks, max_blocks_per_seq, scale, plan, workspace,
-                                           s),
+                                           num_blocks, max_blocks_per_seq, scale, window, plan,
+                                           workspace, s),
                        "pkv_attn_prefill_chunk");
 }
+
+int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t total_q,
+                           int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, B,
+                      total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+                      max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
+                      stream);
+}
+
+int pkv_attn_prefill_chunk_ring(void* out, const void* q, const int32_t* cu_q_lens,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t total_q, int32_t max_q_len, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len,
+                                int32_t window, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (window <= 0) return fail(PKV_EINVAL, "window=%d must be positive", window);
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, B,
+                      total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+                      max_blocks_per_seq, max_context_len, window, scale, workspace,
+                      workspace_bytes, stream);
+}
+
 
 }  // extern "C"

@@ -7,9 +7,10 @@
 
 namespace pkv {
 
+// window > 0: each sequence's pages form a ring of `window` tokens.
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* block_tables, const int32_t* cu_new,
                                const int32_t* ctx_lens, int B, int max_blocks, int total_new,
-                               hipStream_t stream);
+                               int window, hipStream_t stream);
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* slots,
                          void* k_cache, void* v_cache, int T, int num_blocks, int Hkv, int D,
@@ -36,7 +37,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus)
 
 hipError_t launch_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
-                         int Hkv, int num_blocks, int max_blocks, float scale,
+                         int Hkv, int num_blocks, int max_blocks, float scale, int window,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
 
 // Decode over int8 pages (codes in the bf16 page order; float32 scales
@@ -70,7 +71,7 @@ PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
                           const void* v_cache, const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
-                          int Hkv, int num_blocks, int max_blocks, float scale,
+                          int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream);
 
 }  // namespace pkv

@@ -92,6 +92,7 @@ struct PrefillArgs {
   int* counters;                 // [groups]; zero between calls
   int B, total_q, max_q_len, Hq, Hkv, G, num_blocks, max_blocks, qtiles, splits,
       tiles_per_split;
+  int window;                    // > 0: the pages form a ring of `window` tokens
   float scale_log2;
 };
 
@@ -162,7 +163,12 @@ prefill_kernel(const PrefillArgs a) {
   if (q_lo < 0 || T < 0 || q_lo + T > a.total_q || T > a.max_q_len) return;
   const int R0 = x * kRowsPerWG;
   if (R0 >= T * G) return;                    // uniform over the workgroup
-  const bool bad_len = T > n || n > a.max_blocks * kPage;
+  // Ring paging (Module 04 page, section 4): position p sits at ring index
+  // p % window, i.e. in the table's page (p / 16) % (window / 16); the ring
+  // holds positions n - window .. n - 1, so keys below key_lo are gone.
+  const bool ring = a.window > 0;
+  const int ring_pages = ring ? a.window / kPage : 0;
+  const bool bad_len = T > n || (ring ? T > a.window : n > a.max_blocks * kPage);
 
   // This lane's query row (lane column of the MFMA tiles).
   const int row = R0 + w * kRowsPerWave + (lane & 31);
@@ -175,10 +181,13 @@ prefill_kernel(const PrefillArgs a) {
   // split's share of the key tiles.
   const int t_last = min(T - 1, (R0 + kRowsPerWG - 1) / G);
   const int key_end = bad_len ? 0 : n - T + t_last + 1;
-  const int n_tiles = (key_end + kTileKeys - 1) / kTileKeys;
+  const int key_lo = ring && !bad_len ? max(0, n - a.window) : 0;
+  const int tile_first = key_lo / kTileKeys;
+  const int tile_end = (key_end + kTileKeys - 1) / kTileKeys;
+  const int n_tiles = max(0, tile_end - tile_first);
   const int ns = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;   // non-empty splits
-  const int tile0 = ks * a.tiles_per_split;
-  const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
+  const int tile0 = tile_first + ks * a.tiles_per_split;
+  const int tile1 = min(tile0 + a.tiles_per_split, tile_end);
   if (tile0 >= tile1) {
     if (ks == 0 && row_ok) {                  // bad length: no keys at all -> NaN rows
       uint32_t* orow = reinterpret_cast<uint32_t*>(
@@ -195,10 +204,11 @@ prefill_kernel(const PrefillArgs a) {
   // not need); invalid ids of needed pages poison the result.
   int bad = 0;
   for (int p = tid; p < nt * 4; p += kWaves * kWave) {
-    const int page = tile0 * 4 + p;
+    const int page = tile0 * 4 + p;             // page of absolute positions
+    const int tpage = ring ? page % ring_pages : page;
     int id = 0;
-    if (page * kPage < key_end && page < a.max_blocks) {
-      id = bt[page];
+    if (page * kPage < key_end && page * kPage + kPage > key_lo && tpage < a.max_blocks) {
+      id = bt[tpage];
       if (id < 0 || id >= a.num_blocks) { bad = 1; id = 0; }
     }
     s_ids[p] = id;
@@ -280,14 +290,16 @@ prefill_kernel(const PrefillArgs a) {
 
     const char* ksm = s_k[stage];
     const char* vsm = s_v[stage];
-    if (key0 + kTileKeys > key_end) {
-      // Keys past key_end are always masked; zero their V rows so the canary
-      // NaNs of unwritten slots cannot reach the products (K is masked).
+    if (key0 + kTileKeys > key_end || key0 < key_lo) {
+      // Keys past key_end (and, in a ring, below key_lo) are always masked;
+      // zero their V rows so the canary NaNs of unwritten slots cannot reach
+      // the products (K is masked).
       char* vz = s_v[stage];
       const u32x4 zero = {0u, 0u, 0u, 0u};
       for (int e = tid; e < kTileKeys * 16; e += kWaves * kWave) {
         const int r = e >> 4;
-        if (key0 + r >= key_end) *reinterpret_cast<u32x4*>(vz + r * kRowBytes + (e & 15) * 16) = zero;
+        if (key0 + r >= key_end || key0 + r < key_lo)
+          *reinterpret_cast<u32x4*>(vz + r * kRowBytes + (e & 15) * 16) = zero;
       }
       __syncthreads();
     }
@@ -308,7 +320,7 @@ prefill_kernel(const PrefillArgs a) {
 
     // Scale, causal mask, running max.  Accumulator ii of block kb holds key
     // key0 + 32*kb + 8*(ii/4) + 4*half + ii%4.
-    const bool need_mask = key0 + kTileKeys - 1 > qpos_min;
+    const bool need_mask = key0 + kTileKeys - 1 > qpos_min || key0 < key_lo;
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -317,7 +329,7 @@ prefill_kernel(const PrefillArgs a) {
         float v = s[kb][ii] * a.scale_log2;
         if (need_mask) {
           const int key = key0 + 32 * kb + 8 * (ii >> 2) + 4 * half + (ii & 3);
-          v = key <= qpos ? v : kNegInf;
+          v = (key <= qpos && key >= key_lo) ? v : kNegInf;
         }
         s[kb][ii] = v;
         mx = fmaxf(mx, v);
@@ -539,7 +551,7 @@ PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
                           const void* v_cache, const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
-                          int Hkv, int num_blocks, int max_blocks, float scale,
+                          int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0 || total_q == 0 || max_q_len == 0) return hipSuccess;
   PrefillArgs a;
@@ -562,6 +574,7 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.qtiles = plan.qtiles;
   a.splits = plan.splits;
   a.tiles_per_split = plan.tiles_per_split;
+  a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   const unsigned grid = (unsigned)((int64_t)B * a.qtiles * a.splits * Hkv);
   hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kWaves * kWave), 0, stream, a);

@@ -1,0 +1,128 @@
+"""Ring (sliding-window) paging on the GPU through the C ABI, against the
+oracle's ring functions ([P2] section 4, "Capacity-cache"; KVCache
+write/read): ring slot mapping bit-exact, append, decode and chunked prefill
+over rings within the attention tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_oracle as O
+from paged_kv_gqa_pkv_amd import binding as bd
+from paged_kv_gqa_pkv_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+D = 128
+
+
+def u16(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def pages_order(pool):
+    return u16(pool.transpose(1, 2))
+
+
+def check(got, want, what):
+    g = O.bf16_to_f64(u16(got))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
+    err = np.abs(g - want)
+    print(f"{what}: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (what, err.max(), err.mean())
+
+
+def ring_setup(pre_lens, new_lens, W, Hkv, seed):
+    """Pools whose rings already hold each sequence's first pre_len positions
+    (random rows), with NaN in the ring slots no position has reached yet."""
+    B = len(pre_lens)
+    rp = W // 16
+    nb = B * rp + 5
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(seed))
+    tables = perm[:B * rp].view(B, rp).to(torch.int32)
+    k = S.randn_bf16((nb, Hkv, 16, D), seed + 1)
+    v = S.randn_bf16((nb, Hkv, 16, D), seed + 2)
+    for b in range(B):
+        reached = pre_lens[b] + new_lens[b]
+        for idx in range(min(reached, W), W):          # ring slots never written
+            page, off = divmod(idx, 16)
+            blk = int(tables[b, page])
+            k.view(torch.int16)[blk, :, off] = S.BF16_CANARY_BITS
+            v.view(torch.int16)[blk, :, off] = S.BF16_CANARY_BITS
+    ctx = torch.tensor([p + n for p, n in zip(pre_lens, new_lens)], dtype=torch.int32)
+    cu = torch.cumsum(torch.tensor([0] + list(new_lens)), 0).to(torch.int32)
+    T = int(cu[-1])
+    kn = S.randn_bf16((T, Hkv, D), seed + 3)
+    vn = S.randn_bf16((T, Hkv, D), seed + 4)
+    return tables, ctx, cu, k, v, kn, vn
+
+
+def run_ring(pre_lens, new_lens, W, Hq, Hkv, seed, prefill):
+    tables, ctx, cu, k, v, kn, vn = ring_setup(pre_lens, new_lens, W, Hkv, seed)
+    B = len(pre_lens)
+    kc0, vc0 = pages_order(k), pages_order(v)
+    dk, dv = k.cuda(), v.cuda()
+    T = int(cu[-1])
+    sm = torch.empty(T, dtype=torch.int32, device="cuda")
+    bd.pkv_slot_mapping_ring(sm, tables.cuda(), cu.cuda(), ctx.cuda(), W)
+    bd.pkv_append(kn.cuda(), vn.cuda(), sm, dk, dv)
+    scale = 128 ** -0.5
+    max_ctx = int(ctx.max())
+    if prefill:
+        q = S.randn_bf16((T, Hq, D), seed + 5).cuda()
+        out = torch.empty_like(q)
+        max_q = max(new_lens)
+        nbytes = bd.pkv_prefill_workspace_bytes(B, max_q, Hq, Hkv, D, min(max_ctx, W + 64))
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        bd.pkv_attn_prefill_chunk_ring(out, q, cu.cuda(), dk, dv, tables.cuda(), ctx.cuda(),
+                                       max_q, max_ctx, W, scale, workspace=ws)
+    else:
+        q = S.randn_bf16((B, Hq, D), seed + 5).cuda()
+        out = torch.empty_like(q)
+        nbytes = bd.pkv_decode_workspace_bytes(B, Hq, Hkv, D, min(max_ctx, W))
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        bd.pkv_attn_decode_ring(out, q, dk, dv, tables.cuda(), ctx.cuda(), max_ctx, W, scale,
+                                workspace=ws)
+    torch.cuda.synchronize()
+    bt = tables.tolist()
+    slots = O.ring_slot_ref(bt, cu.tolist(), ctx.tolist(), W)
+    assert sm.cpu().tolist() == slots, "ring slot mapping differs"
+    kc, vc = O.append_ref(kc0, vc0, u16(kn), u16(vn), slots)
+    assert np.array_equal(pages_order(dk), kc) and np.array_equal(pages_order(dv), vc)
+    if prefill:
+        want = O.ring_prefill_ref(u16(q), cu.tolist(), kc, vc, bt, ctx.tolist(), W, scale)
+    else:
+        want = O.ring_decode_ref(u16(q), kc, vc, bt, ctx.tolist(), W, scale)
+    return out, want
+
+
+def test_ring_decode_before_at_and_past_the_wrap():
+    pre = [99, 255, 699, 1499, 0]
+    out, want = run_ring(pre, [1] * 5, 256, Hq=16, Hkv=8, seed=700, prefill=False)
+    check(out, want, "ring decode W=256")
+
+
+def test_ring_decode_long_window_with_splits():
+    pre = [19999, 3000]
+    assert bd.pkv_decode_num_splits(2, 32, 8, 128, 8192) > 1
+    out, want = run_ring(pre, [1, 1], 8192, Hq=32, Hkv=8, seed=710, prefill=False)
+    check(out, want, "ring decode W=8192")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_ring_prefill_before_and_after_wrap(G):
+    Hkv = 8 // G if G < 8 else 1
+    pre = [80, 600, 1000, 0]
+    new = [100, 100, 37, 200]
+    out, want = run_ring(pre, new, 256, Hq=Hkv * G, Hkv=Hkv, seed=720 + G, prefill=True)
+    check(out, want, f"ring prefill W=256 G={G}")
+
+
+def test_ring_prefill_long_ring_many_key_splits():
+    out, want = run_ring([9936], [64], 4096, Hq=32, Hkv=8, seed=730, prefill=True)
+    check(out, want, "ring prefill W=4096")
+
+
+def test_ring_chunk_as_long_as_the_ring():
+    out, want = run_ring([300], [256], 256, Hq=16, Hkv=8, seed=740, prefill=True)
+    check(out, want, "ring prefill T=W")
