@@ -206,6 +206,40 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The step before attention, fused ([P1] model.py: rms_norm, _rope_tables,
+ * apply_rope and forward, which normalises q and k per head, rotates both at
+ * the token's absolute position and writes k and v into the cache; the
+ * pages name this fusion as the first one to write for the GPU).  For every
+ * new token t of sequence b (cu_new_lens / context_lens as in
+ * pkv_slot_mapping; position p = context_lens[b] - n_new_b + local index):
+ *     q_out[t][h] = rope(rms_norm(q_in[t][h], q_norm_w), p)   for each query head h
+ *     k_cache[slot][g] = rope(rms_norm(k_in[t][g], k_norm_w), p),  v_cache[slot][g] = v_in[t][g]
+ * with rms_norm(x, w) = bf16(bf16(x * rsqrt(mean(x^2) + eps)) * w) (mean and
+ * rsqrt in float32) and rope(x, p) = bf16(bf16(x * cos[p]) +
+ * bf16(rotate_half(x) * sin[p])), rotate_half(x) = (-x[D/2:], x[:D/2]): the
+ * listing's bf16 tensor arithmetic.  The slot is found from block_tables as
+ * pkv_slot_mapping finds it and written to slot_mapping[t] (if not NULL; -1
+ * when the table has no page there).  A token whose slot is -1 writes no
+ * K/V; a position outside [0, max_pos) gives NaN q rows and writes no K/V.
+ *   q_in, q_out     bf16 [T][Hq][D] (must not overlap)
+ *   k_in, v_in      bf16 [T][Hkv][D]
+ *   q_norm_w, k_norm_w  bf16 [D]
+ *   cos_table, sin_table  bf16 [max_pos][D], both halves of a row equal
+ *                   ([P1] _rope_tables: inv_freq = 1 / theta^(2i/D))
+ *   k_cache, v_cache  the bf16 page pools (head-major, as pkv_append)
+ * The only difference from the listing's arithmetic is the order of the
+ * 128-term float32 sum of squares.
+ */
+int pkv_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in, const void* v_in,
+                            const void* q_norm_w, const void* k_norm_w, const void* cos_table,
+                            const void* sin_table, int32_t max_pos, const int32_t* block_tables,
+                            const int32_t* cu_new_lens, const int32_t* context_lens,
+                            int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t B,
+                            int32_t max_blocks_per_seq, int32_t T, int32_t num_blocks,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, float eps,
+                            void* stream);
+
+/*
  * int8 KV pages ([P2] kv_cache.py listing, section 5, class KV8Cache: one
  * byte per element plus one float32 scale per (token, KV head); [P2] closing
  * notes: 2112 B instead of 4096 B per token-layer at H_kv 8, d_head 128).

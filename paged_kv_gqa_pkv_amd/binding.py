@@ -46,6 +46,8 @@ SIGNATURES = {
     "pkv_attn_prefill_chunk_ring": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
+    "pkv_qk_norm_rope_append": (_c_int, [_vp] * 8 + [_c_int] + [_vp] * 6 +
+                                [_c_int] * 8 + [_f, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -349,3 +351,41 @@ def pkv_attn_prefill_chunk_ring(out: torch.Tensor, q: torch.Tensor, cu_q_lens: t
         _p(context_lens), B, total_q, int(max_q_len), Hq, Hkv, D, bs, nb,
         block_tables.shape[1], int(max_context_len), int(window), float(scale),
         *_ws(workspace), _stream(stream)))
+
+
+def pkv_qk_norm_rope_append(q_out: torch.Tensor, q_in: torch.Tensor, k_in: torch.Tensor,
+                            v_in: torch.Tensor, q_norm_w: torch.Tensor, k_norm_w: torch.Tensor,
+                            cos_table: torch.Tensor, sin_table: torch.Tensor,
+                            block_tables: torch.Tensor, cu_new_lens: torch.Tensor,
+                            context_lens: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, eps: float,
+                            slot_mapping: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q/k RMSNorm + RoPE; rotated q to q_out, rotated k and v into their page slots."""
+    for t, n in ((q_out, "q_out"), (q_in, "q_in"), (k_in, "k_in"), (v_in, "v_in")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        _need(t, torch.bfloat16, n, 1)
+    for t, n in ((cos_table, "cos_table"), (sin_table, "sin_table")):
+        _need(t, torch.bfloat16, n, 2)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(cu_new_lens, torch.int32, "cu_new_lens", 1)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    T, Hq, D = q_in.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    B = context_lens.numel()
+    if q_out.shape != q_in.shape or k_in.shape != (T, Hkv, D) or v_in.shape != k_in.shape or \
+            D2 != D or v_cache.shape != k_cache.shape or q_norm_w.numel() != D or \
+            k_norm_w.numel() != D or cos_table.shape != sin_table.shape or \
+            cos_table.shape[1] != D or block_tables.shape[0] != B or cu_new_lens.numel() != B + 1:
+        raise ValueError("inconsistent shapes")
+    if slot_mapping is not None:
+        _need(slot_mapping, torch.int32, "slot_mapping", 1)
+        if slot_mapping.numel() != T:
+            raise ValueError("slot_mapping must hold T entries")
+    _check(load().pkv_qk_norm_rope_append(
+        _p(q_out), _p(q_in), _p(k_in), _p(v_in), _p(q_norm_w), _p(k_norm_w), _p(cos_table),
+        _p(sin_table), cos_table.shape[0], _p(block_tables), _p(cu_new_lens), _p(context_lens),
+        _p(slot_mapping), _p(k_cache), _p(v_cache), B, block_tables.shape[1], T, nb, Hq, Hkv, D,
+        bs, float(eps), _stream(stream)))

@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "pkv_api.cpp"]
+SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "qk_rope.hip", "pkv_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

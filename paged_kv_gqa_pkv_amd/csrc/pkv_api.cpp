@@ -312,6 +312,52 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
                        "pkv_copy_blocks");
 }
 
+int pkv_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in, const void* v_in,
+                            const void* q_norm_w, const void* k_norm_w, const void* cos_table,
+                            const void* sin_table, int32_t max_pos, const int32_t* block_tables,
+                            const int32_t* cu_new_lens, const int32_t* context_lens,
+                            int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t B,
+                            int32_t max_blocks_per_seq, int32_t T, int32_t num_blocks,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, float eps,
+                            void* stream) {
+  if (B < 0 || T < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_pos < 0)
+    return fail(PKV_EINVAL, "negative size");
+  int rc = check_geometry(Hq, Hkv, D, block_size);
+  if (rc) return rc;
+  if (T == 0) return PKV_OK;
+  if (B == 0) return fail(PKV_EINVAL, "T=%d tokens but no sequences", T);
+  if (!q_out || !q_in || !k_in || !v_in || !q_norm_w || !k_norm_w || !cos_table || !sin_table ||
+      !block_tables || !cu_new_lens || !context_lens || !k_cache || !v_cache)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if (q_out == q_in) return fail(PKV_EINVAL, "q_out and q_in must not overlap");
+  if (k_cache == v_cache) return fail(PKV_EINVAL, "k_cache and v_cache must differ");
+  if (!(eps >= 0.f)) return fail(PKV_EINVAL, "eps must be >= 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    std::vector<int32_t> cu, ctx;
+    if (!to_host(cu, cu_new_lens, (size_t)B + 1, s) || !to_host(ctx, context_lens, (size_t)B, s))
+      return fail(PKV_ELAUNCH, "PKV_VALIDATE: copy of index arrays failed");
+    if (cu[0] != 0 || cu[B] != T)
+      return fail(PKV_EVALIDATE, "cu_new_lens must start at 0 and end at T=%d", T);
+    for (int b = 0; b < B; ++b) {
+      if (cu[b + 1] < cu[b] || cu[b + 1] - cu[b] > ctx[b])
+        return fail(PKV_EVALIDATE, "sequence %d: inconsistent cu_new_lens / context_lens", b);
+      if (ctx[b] > max_pos)
+        return fail(PKV_EVALIDATE, "context_lens[%d]=%d beyond the RoPE tables (%d rows)", b,
+                    ctx[b], max_pos);
+    }
+    rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
+                         max_blocks_per_seq * PKV_BLOCK_SIZE, s);
+    if (rc) return rc;
+  }
+  return launch_status(pkv::launch_qk_norm_rope_append(
+                           q_out, q_in, k_in, v_in, q_norm_w, k_norm_w, cos_table, sin_table,
+                           max_pos, block_tables, cu_new_lens, context_lens, slot_mapping,
+                           k_cache, v_cache, B, max_blocks_per_seq, T, num_blocks, Hq, Hkv, eps,
+                           s),
+                       "pkv_qk_norm_rope_append");
+}
+
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                   int32_t max_context_len) {
   if (B <= 0 || max_context_len < 0 || check_geometry(Hq, Hkv, D, PKV_BLOCK_SIZE) != PKV_OK)

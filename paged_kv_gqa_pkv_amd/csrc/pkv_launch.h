@@ -23,6 +23,19 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, co
                               int n_pairs, int num_blocks, int64_t block_bytes, int n_layers,
                               int64_t layer_stride, hipStream_t stream);
 
+// q/k RMSNorm + RoPE + append of the rotated k and of v into their slots
+// (slots found from the tables, as launch_slot_mapping does; written to
+// `slots` when it is not null).
+hipError_t launch_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in,
+                                      const void* v_in, const void* q_norm_w,
+                                      const void* k_norm_w, const void* cos_table,
+                                      const void* sin_table, int max_pos,
+                                      const int32_t* block_tables, const int32_t* cu_new,
+                                      const int32_t* ctx_lens, int32_t* slots, void* k_cache,
+                                      void* v_cache, int B, int max_blocks, int T,
+                                      int num_blocks, int Hq, int Hkv, float eps,
+                                      hipStream_t stream);
+
 // Split plan of a decode call: S splits of pages_per_split pages each.
 struct DecodePlan {
   int splits;

@@ -135,3 +135,32 @@ def test_copy_blocks_rejects_bad_arguments(lib):
     assert call(layers=2, stride=4096) == bd.PKV_EINVAL         # layers overlap (8 x 1024 B)
     assert b"layer_stride" in lib.pkv_last_error()
     assert call(n=0) == bd.PKV_OK and call(layers=0) == bd.PKV_OK
+
+
+def test_fused_norm_rope_append_rejects_bad_arguments(lib):
+    p8 = [16, 32, 48, 64, 80, 96, 112, 128]
+    tail = [144, 160, 176, 192, 208, 224]
+    # block size 8, negative T, G = 3, null pool, NaN eps, nothing to do
+    assert lib.pkv_qk_norm_rope_append(*p8, 4096, *tail, 2, 4, 3, 32, 16, 8, 128, 8, 1e-6,
+                                       NULL) == bd.PKV_EUNSUPPORTED
+    assert lib.pkv_qk_norm_rope_append(*p8, 4096, *tail, 2, 4, -3, 32, 16, 8, 128, 16, 1e-6,
+                                       NULL) == bd.PKV_EINVAL
+    assert lib.pkv_qk_norm_rope_append(*p8, 4096, *tail, 2, 4, 3, 32, 24, 8, 128, 16, 1e-6,
+                                       NULL) == bd.PKV_EUNSUPPORTED
+    assert lib.pkv_qk_norm_rope_append(*p8, 4096, *tail[:5], NULL, 2, 4, 3, 32, 16, 8, 128, 16,
+                                       1e-6, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_qk_norm_rope_append(*p8, 4096, *tail, 2, 4, 3, 32, 16, 8, 128, 16,
+                                       float("nan"), NULL) == bd.PKV_EINVAL
+    assert lib.pkv_qk_norm_rope_append(*([NULL] * 8), 0, *([NULL] * 6), 0, 0, 0, 0, 16, 8, 128,
+                                       16, 1e-6, NULL) == bd.PKV_OK
+
+
+def test_ring_entry_points_reject_bad_windows(lib):
+    # window not a multiple of 16, window beyond the table, chunk longer than the ring
+    assert lib.pkv_slot_mapping_ring(1, 2, 3, 4, 2, 4, 3, 16, 40, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_slot_mapping_ring(1, 2, 3, 4, 2, 4, 3, 16, 128, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_attn_decode_ring(1, 2, 3, 4, 5, 6, 2, 16, 8, 128, 16, 32, 4, 500, 0, 0.088,
+                                    NULL, 0, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_attn_prefill_chunk_ring(1, 2, 3, 4, 5, 6, 7, 1, 100, 100, 16, 8, 128, 16, 64,
+                                           8, 1000, 64, 0.088, NULL, 0, NULL) == bd.PKV_EINVAL
+    assert b"ring" in lib.pkv_last_error()
