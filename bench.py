@@ -51,6 +51,9 @@ def parse():
                    help="time steps only (no per-launch events), e.g. under a profiler")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
+    p.add_argument("--kernels", action="store_true",
+                   help="time the page-write kernels (append, int8 append, block copy, fused "
+                        "norm+RoPE+append, slot mapping) by HIP-graph replay; one JSON line")
     p.add_argument("--graph", action="store_true",
                    help="capture each distinct step in a HIP graph and time graph replays "
                         "(per-launch events then come from a separate eager pass)")
@@ -512,6 +515,115 @@ def cpu_baseline(args, parts):
                       f"thread), scaled to {per_step:.1f} s per full step"}
 
 
+def _graph_time(fn, n_variants, reps=40):
+    """GPU time per call: capture calls fn(0..k-1) (k >= 8, cycling over the
+    rotated inputs) in one HIP graph, replay it, HIP events around the replays."""
+    import torch
+    k = max(8, n_variants)
+    for i in range(k):
+        fn(i)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(k):
+                fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    r = max(2, reps // k)
+    e0.record()
+    for _ in range(r):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (r * k)
+
+
+def kernel_bench():
+    """Per-kernel GPU time of the page-write kernels on synthetic inputs of the
+    pages' shapes (Qwen3-8B-shaped heads: Hq 32, Hkv 8, D 128), each call on a
+    different copy of its inputs so the 256 MB MALL cannot serve them.
+    Algorithmic bytes: what the method must read and write once."""
+    import torch
+    from paged_kv_gqa_pkv_amd import binding as bd
+    from paged_kv_gqa_pkv_amd import synth as S
+
+    bd.load()
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    Hq, Hkv, D = 32, 8, 128
+    out = {}
+
+    def line(name, sec, nbytes, note):
+        out[name] = {"us": round(sec * 1e6, 2), "bytes": int(nbytes),
+                     "GBs": round(nbytes / sec / 1e9, 1),
+                     "frac_of_8TBs": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "work": note}
+
+    # bf16 and int8 append: 65536 tokens into distinct slots of a 4096-page pool
+    n_tok, nb, copies = 65536, 4096, 4
+    sets = [S.bulk_append_inputs(n_tok, nb, Hkv, D, seed=300 + c, device=dev) for c in range(copies)]
+    sets = [(sl.to(dev), kn, vn, pk, pv) for sl, kn, vn, pk, pv in sets]
+    sec = _graph_time(lambda i: bd.pkv_append(sets[i % copies][1], sets[i % copies][2],
+                                               sets[i % copies][0], sets[i % copies][3],
+                                               sets[i % copies][4]), copies)
+    line("append_bf16", sec, n_tok * (2 * 2 * Hkv * D * 2 + 4),
+         f"{n_tok} tokens: read K/V rows and slot, write K/V rows")
+    i8 = [(torch.zeros((nb, Hkv, 16, D), dtype=torch.int8, device=dev),
+           torch.zeros((nb, Hkv, 16, D), dtype=torch.int8, device=dev),
+           torch.zeros((nb, Hkv, 8, 2, 2), dtype=torch.float32, device=dev)) for _ in range(copies)]
+    sec = _graph_time(lambda i: bd.pkv_append_int8(sets[i % copies][1], sets[i % copies][2],
+                                                    sets[i % copies][0], *i8[i % copies]), copies)
+    line("append_int8", sec, n_tok * (2 * Hkv * D * 2 + 2 * Hkv * (D + 4) + 4),
+         f"{n_tok} tokens: read bf16 K/V rows and slot, write codes and scales")
+    del sets, i8
+    # block copy: 1024 (src, dst) pairs in all 36 layers of a layered K and V pool
+    L, nbc, pairs = 36, 4096, 1024
+    kp = torch.empty((L, nbc, Hkv, 16, D), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    perm = torch.randperm(nbc, generator=torch.Generator().manual_seed(5))
+    srcs = [perm[:pairs].to(torch.int32).to(dev), perm[pairs:2 * pairs].to(torch.int32).to(dev)]
+    dsts = [perm[2 * pairs:3 * pairs].to(torch.int32).to(dev),
+            perm[3 * pairs:4 * pairs].to(torch.int32).to(dev)]
+    sec = _graph_time(lambda i: bd.pkv_copy_blocks(srcs[i % 2], dsts[i % 2], kp, vp,
+                                                   layered=True), 2)
+    line("copy_blocks", sec, pairs * L * 2 * Hkv * 16 * D * 2 * 2,
+         f"{pairs} block pairs x {L} layers, K and V: read and write each block")
+    del kp, vp
+    # fused q/k RMSNorm + RoPE + append: 8192 decode tokens (one per sequence)
+    B = 8192
+    cos = (torch.rand((32768, D), device=dev) * 2 - 1).to(torch.bfloat16)
+    sin = (torch.rand((32768, D), device=dev) * 2 - 1).to(torch.bfloat16)
+    nbf = B * 4 + 16
+    ctx = torch.randint(1, 4 * 16, (B,), generator=torch.Generator().manual_seed(6)).to(torch.int32)
+    bt = torch.randperm(nbf, generator=torch.Generator().manual_seed(7))[:B * 4].view(B, 4)
+    bt, ctx = bt.to(torch.int32).to(dev), ctx.to(dev)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    fz = []
+    for c in range(2):
+        fz.append(dict(q=S.randn_bf16((B, Hq, D), 400 + c, dev), k=S.randn_bf16((B, Hkv, D), 410 + c, dev),
+                       v=S.randn_bf16((B, Hkv, D), 420 + c, dev),
+                       qo=torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev),
+                       kc=torch.empty((nbf, Hkv, 16, D), dtype=torch.bfloat16, device=dev),
+                       vc=torch.empty((nbf, Hkv, 16, D), dtype=torch.bfloat16, device=dev)))
+    w = torch.ones(D, dtype=torch.bfloat16, device=dev)
+    sm = torch.empty(B, dtype=torch.int32, device=dev)
+    sec = _graph_time(lambda i: bd.pkv_qk_norm_rope_append(
+        fz[i % 2]["qo"], fz[i % 2]["q"], fz[i % 2]["k"], fz[i % 2]["v"], w, w, cos, sin, bt, cu, ctx,
+        fz[i % 2]["kc"], fz[i % 2]["vc"], 1e-6, slot_mapping=sm), 2)
+    per_tok = 2 * Hq * D * 2 + 2 * Hkv * D * 2 * 2 + 2 * D * 2 + 4 * 3
+    line("qk_norm_rope_append", sec, B * per_tok,
+         f"{B} tokens: read q, k, v rows and the cos/sin rows of their positions, "
+         "write rotated q and the K/V rows, slot and table entries")
+    sec = _graph_time(lambda i: bd.pkv_slot_mapping(sm, bt, cu, ctx), 1)
+    line("slot_mapping", sec, B * 12, f"{B} tokens: read table entry and lengths, write slot")
+    return {"kernels": out, "note": "GPU time per call from HIP-graph replay of >= 8 calls"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -525,6 +637,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.kernels:
+        print(json.dumps(kernel_bench()), flush=True)
         return
     out, parts = run(args)
     if args.cpu_seconds > 0:
