@@ -621,6 +621,13 @@ def kernel_bench():
          "write rotated q and the K/V rows, slot and table entries")
     sec = _graph_time(lambda i: bd.pkv_slot_mapping(sm, bt, cu, ctx), 1)
     line("slot_mapping", sec, B * 12, f"{B} tokens: read table entry and lengths, write slot")
+    del fz
+    # what a plain read+write stream reaches on this part: the ceiling for the
+    # append and copy kernels, which read and write every byte once
+    src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sec = _graph_time(lambda i: dst.copy_(src), 1)
+    line("device_copy", sec, 2 << 29, "torch copy of 512 MiB: read and write each byte once")
     return {"kernels": out, "note": "GPU time per call from HIP-graph replay of >= 8 calls"}
 
 

@@ -14,12 +14,14 @@
 // rounding), so the only difference from the listing's arithmetic is the
 // order of the 128-term sum of squares.
 //
-// Layout of the work: 16 lanes own one row (token, head) of 128 values, 8
-// per lane (one 16-byte load).  The sum of squares is a DPP reduction inside
-// the 16-lane row; the rotate-half partner of dims 8s..8s+7 (dims +-64) sits
-// in lane s ^ 8 of the same row, one DPP row rotation away.  A token's
-// position and slot are found as the slot-mapping kernel finds them (binary
-// search over cu_new_lens), so no separate slot-mapping launch is needed.
+// Layout of the work: one workgroup per token; 16 lanes own one row (head)
+// of 128 values, 8 per lane (one 16-byte load), and the 16 row slots of the
+// workgroup walk the token's Hq + 2 Hkv rows.  The sum of squares is a DPP
+// reduction inside the 16-lane row; the rotate-half partner of dims
+// 8s..8s+7 (dims +-64) sits in lane s ^ 8 of the same row, one DPP row
+// rotation away.  The token's position and slot are found once per
+// workgroup, as the slot-mapping kernel finds them (binary search over
+// cu_new_lens), so no separate slot-mapping launch is needed.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -53,7 +55,6 @@ struct QkRopeArgs {
   int32_t* slots;              // [T] out (may be null)
   u32x4* k_cache;              // bf16 [num_blocks][Hkv][16][D]
   u32x4* v_cache;
-  int64_t n_rows;              // T * (Hq + 2 * Hkv)
   int B, max_blocks, T, num_blocks, Hq, Hkv, max_pos;
   float eps;
 };
@@ -61,27 +62,24 @@ struct QkRopeArgs {
 __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeArgs a) {
   const int sub = threadIdx.x & 15;
   const int per_tok = a.Hq + 2 * a.Hkv;
-  const int64_t rows_per_step = (int64_t)gridDim.x * (blockDim.x / 16);
-  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4); r < a.n_rows;
-       r += rows_per_step) {
-    // All 16 lanes of a row share r, so the DPP below only reads lanes of the
-    // same active row.
-    const int t = (int)(r / per_tok);
-    const int j = (int)(r % per_tok);        // [0, Hq): q head; then k heads; then v heads
-    int lo = 0, hi = a.B;                    // sequence b with cu[b] <= t < cu[b+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_new[mid] <= t) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    const int p = a.ctx_lens[b] - (a.cu_new[b + 1] - a.cu_new[b]) + (t - a.cu_new[b]);
-    int64_t slot = -1;
-    if (p >= 0 && (p >> 4) < a.max_blocks) {
-      const int blk = a.block_tables[(int64_t)b * a.max_blocks + (p >> 4)];
-      if (blk >= 0 && blk < a.num_blocks) slot = (int64_t)blk * kPage + (p & (kPage - 1));
-    }
-    if (j == 0 && sub == 0 && a.slots) a.slots[t] = (int32_t)slot;
-
+  const int t = blockIdx.x;                  // one token per workgroup
+  int lo = 0, hi = a.B;                      // sequence b with cu[b] <= t < cu[b+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_new[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int p = a.ctx_lens[b] - (a.cu_new[b + 1] - a.cu_new[b]) + (t - a.cu_new[b]);
+  int64_t slot = -1;
+  if (p >= 0 && (p >> 4) < a.max_blocks) {
+    const int blk = a.block_tables[(int64_t)b * a.max_blocks + (p >> 4)];
+    if (blk >= 0 && blk < a.num_blocks) slot = (int64_t)blk * kPage + (p & (kPage - 1));
+  }
+  if (threadIdx.x == 0 && a.slots) a.slots[t] = (int32_t)slot;
+  // All 16 lanes of a row share j, so the DPP below only reads lanes of the
+  // same active row.
+  for (int j = threadIdx.x >> 4; j < per_tok; j += blockDim.x / 16) {
+    // j in [0, Hq): q head; then the k heads; then the v heads
     if (j >= a.Hq + a.Hkv) {                 // v: a bit copy into the page slot
       const int h = j - a.Hq - a.Hkv;
       if (slot >= 0) {
@@ -168,12 +166,9 @@ hipError_t launch_qk_norm_rope_append(void* q_out, const void* q_in, const void*
   a.slots = slots;
   a.k_cache = static_cast<u32x4*>(k_cache);
   a.v_cache = static_cast<u32x4*>(v_cache);
-  a.n_rows = (int64_t)T * (Hq + 2 * Hkv);
   a.B = B; a.max_blocks = max_blocks; a.T = T; a.num_blocks = num_blocks;
   a.Hq = Hq; a.Hkv = Hkv; a.max_pos = max_pos; a.eps = eps;
-  int64_t blocks = (a.n_rows + 15) / 16;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(qk_norm_rope_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(qk_norm_rope_append_kernel, dim3((unsigned)T), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
