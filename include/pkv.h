@@ -285,6 +285,23 @@ int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const vo
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Causal chunked prefill over int8 pages ([P2] KV8Cache.read: K and V read
+ * back as code * scale; then the attention of pkv_attn_prefill_chunk).  Same
+ * arguments, outputs, error behaviour, split plan and workspace as
+ * pkv_attn_prefill_chunk (pkv_prefill_workspace_bytes applies unchanged),
+ * with the pools replaced by k_codes, v_codes and kv_scales in the layout
+ * above.  Each tile of 64 keys is dequantised once per workgroup, code *
+ * scale rounded to bf16, and the bf16 MFMA path runs on the result.
+ */
+int pkv_attn_prefill_chunk_int8(void* out, const void* q, const int32_t* cu_q_lens,
+                                const void* k_codes, const void* v_codes, const float* kv_scales,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t total_q, int32_t max_q_len, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Ring (sliding-window) paging ([P2] section 4, "Capacity-cache": beyond the
  * capacity the cache becomes a ring, position p is written at index
  * p % capacity over the oldest token, a read returns the last

@@ -46,6 +46,7 @@ SIGNATURES = {
     "pkv_attn_prefill_chunk_ring": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
+    "pkv_attn_prefill_chunk_int8": (_c_int, [_vp] * 8 + [_c_int] * 10 + [_f, _vp, _c_size, _vp]),
     "pkv_qk_norm_rope_append": (_c_int, [_vp] * 8 + [_c_int] + [_vp] * 6 +
                                 [_c_int] * 8 + [_f, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -254,6 +255,35 @@ def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tens
                                        _p(block_tables), _p(context_lens), B, Hq, Hkv, D, bs, nb,
                                        block_tables.shape[1], int(max_context_len), float(scale),
                                        ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pkv_attn_prefill_chunk_int8(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                                k_codes: torch.Tensor, v_codes: torch.Tensor,
+                                kv_scales: torch.Tensor, block_tables: torch.Tensor,
+                                context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
+                                scale: float, workspace: Optional[torch.Tensor] = None,
+                                stream=None) -> None:
+    """out[total_q, Hq, D] <- causal attention of the chunk rows over int8 pools
+    (same workspace as pkv_attn_prefill_chunk)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need(t, torch.int8, n, 4)
+    _need(kv_scales, torch.float32, "kv_scales", 5)
+    for t, n in ((cu_q_lens, "cu_q_lens"), (context_lens, "context_lens")):
+        _need(t, torch.int32, n, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    total_q, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_codes.shape
+    B = context_lens.numel()
+    if out.shape != q.shape or D2 != D or v_codes.shape != k_codes.shape or \
+            tuple(kv_scales.shape) != (nb, Hkv, 8, 2, 2) or \
+            block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
+        raise ValueError("inconsistent shapes")
+    _check(load().pkv_attn_prefill_chunk_int8(
+        _p(out), _p(q), _p(cu_q_lens), _p(k_codes), _p(v_codes), _p(kv_scales), _p(block_tables),
+        _p(context_lens), B, total_q, int(max_q_len), Hq, Hkv, D, bs, nb, block_tables.shape[1],
+        int(max_context_len), float(scale), *_ws(workspace), _stream(stream)))
 
 
 def pkv_copy_blocks(src_blocks: torch.Tensor, dst_blocks: torch.Tensor, k_pool: torch.Tensor,

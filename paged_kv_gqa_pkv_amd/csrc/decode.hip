@@ -214,25 +214,6 @@ struct Bf16Page {
 // [-127, 127], exact in bf16, so q . codes runs on v_dot2_f32_bf16 and the
 // row's K scale multiplies the score; the row's V scale is folded into its
 // probability before the PV product.
-// Signed byte i of w as a float: one SDWA convert.  Written out because the
-// compiler otherwise splits it into a shift and a convert and hoists the
-// shifts of the next page's codes into the current iteration (a register
-// blow-up that also serialises the page pipeline).
-#define PKV_SBYTE(n)                                                               \
-  __device__ __forceinline__ float sbyte##n(uint32_t w) {                          \
-    float r;                                                                       \
-    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD "     \
-        "src0_sel:BYTE_" #n : "=v"(r) : "v"(w));                                   \
-    return r;                                                                      \
-  }
-PKV_SBYTE(0)
-PKV_SBYTE(1)
-PKV_SBYTE(2)
-PKV_SBYTE(3)
-#undef PKV_SBYTE
-__device__ __forceinline__ float sbyte(uint32_t w, int i) {
-  return i == 0 ? sbyte0(w) : i == 1 ? sbyte1(w) : i == 2 ? sbyte2(w) : sbyte3(w);
-}
 struct Int8Page {
   struct Regs {
     u32x4 k[2];      // [row r0 / r0+8], 16 codes each

@@ -437,7 +437,8 @@ size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int
 }
 
 static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
-                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const void* k_cache, const void* v_cache, const float* kv_scales,
+                        const int32_t* block_tables,
                         const int32_t* context_lens, int32_t B, int32_t total_q,
                         int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -493,11 +494,11 @@ static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
                          max_context_len, s, window);
     if (rc) return rc;
   }
-  return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables,
-                                           context_lens, B, total_q, max_q_len, Hq, Hkv,
-                                           num_blocks, max_blocks_per_seq, scale, window, plan,
-                                           workspace, s),
-                       "pkv_attn_prefill_chunk");
+  return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, kv_scales,
+                                           block_tables, context_lens, B, total_q, max_q_len, Hq,
+                                           Hkv, num_blocks, max_blocks_per_seq, scale, window,
+                                           plan, workspace, s),
+                       kv_scales ? "pkv_attn_prefill_chunk_int8" : "pkv_attn_prefill_chunk");
 }
 
 int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
@@ -507,8 +508,8 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_context_len, float scale, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, B,
-                      total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, nullptr, block_tables, context_lens,
+                      B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
                       stream);
 }
@@ -522,11 +523,24 @@ int pkv_attn_prefill_chunk_ring(void* out, const void* q, const int32_t* cu_q_le
                                 int32_t window, float scale, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (window <= 0) return fail(PKV_EINVAL, "window=%d must be positive", window);
-  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, B,
-                      total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, nullptr, block_tables, context_lens,
+                      B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, window, scale, workspace,
                       workspace_bytes, stream);
 }
 
+int pkv_attn_prefill_chunk_int8(void* out, const void* q, const int32_t* cu_q_lens,
+                                const void* k_codes, const void* v_codes, const float* kv_scales,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t total_q, int32_t max_q_len, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && total_q > 0 && !kv_scales) return fail(PKV_EINVAL, "null pointer argument");
+  return prefill_impl(out, q, cu_q_lens, k_codes, v_codes, kv_scales, block_tables, context_lens,
+                      B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+                      max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
+                      stream);
+}
 
 }  // extern "C"

@@ -81,8 +81,9 @@ struct PrefillPlan {
 
 PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_len, int num_cus);
 
+// kv_scales null: bf16 pages; else int8 codes in k_cache / v_cache.
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
-                          const void* v_cache, const int32_t* block_tables,
+                          const void* v_cache, const float* kv_scales, const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream);

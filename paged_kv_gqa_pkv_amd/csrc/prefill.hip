@@ -38,6 +38,13 @@
 // operand, and the row sums use the same rounded values.  The running max is
 // raised lazily (only when a row's max grows by more than 2^8), which keeps
 // every exponent <= 2^8 and skips most accumulator rescales.
+//
+// int8 pages (Module 04 page, section 5, KV8Cache: a row is read back as
+// its codes times its float32 scale).  The DMA ring then carries codes (half the bytes
+// of a bf16 tile) and the pages' scale blocks; once a tile has landed, the
+// workgroup dequantises it once into a bf16 tile (code * scale, rounded to
+// bf16), double-buffered in LDS, and the MFMA work above runs unchanged on
+// it.  Each element is converted once per workgroup, not once per wave.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -79,12 +86,31 @@ constexpr int kMaxSplits = 32;                      // key splits per row tile (
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// LDS layout.  bf16 pages: kStages K tiles, then kStages V tiles (the DMA
+// ring).  int8 pages: two dequantised bf16 K tiles and two V tiles (double
+// buffer), then kStages code stages of {K codes, V codes, one 1 KB scale DMA
+// slot per page}.  After the key loop, the split merge reuses the space:
+// the bf16 output tile (34 KB) at offset 0 and the split weights (16 KB) at
+// kFbufOff.
+constexpr int kCodeTileBytes = kTileKeys * kD;                 // 8 KB of codes
+constexpr int kScaleSlotBytes = kWave * 16;                    // one 64-lane DMA
+constexpr int kCodeStageBytes = 2 * kCodeTileBytes + 4 * kScaleSlotBytes;
+template <bool kI8>
+struct PrefillLds {
+  static constexpr int kVOff = kI8 ? 2 * kTileBytes : kStages * kTileBytes;
+  static constexpr int kCodeOff = 4 * kTileBytes;
+  static constexpr int kBytes = kI8 ? kCodeOff + kStages * kCodeStageBytes : 2 * kStages * kTileBytes;
+  static constexpr int kFbufOff = kI8 ? kCodeOff : kVOff;
+  static constexpr int kVmPerTile = kI8 ? 5 : 8;   // DMA instructions per wave and tile
+};
+
 struct PrefillArgs {
   uint16_t* out;                 // bf16 [total_q][Hq][D]
   const u32x4* q;                // bf16 [total_q][Hq][D] as 16-byte chunks
   const int32_t* cu_q;           // [B+1]
-  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D]
+  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D], or int8 codes
   const u32x4* v_cache;
+  const u32x4* kv_scales;        // int8 pages: float [num_blocks][Hkv][8][2][2]
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
   float* ws_acc;                 // [groups][splits][D][128 rows]
@@ -115,27 +141,32 @@ __device__ __forceinline__ uint32_t lds_offset(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Wait until at most n vector-memory operations of this wave are in flight
-// (n in {0, 8, 16, 24}: the DMA loads of 0 .. 3 later tiles).
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 24)
-    __builtin_amdgcn_s_waitcnt((24 & 0xF) | ((24 >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  else if (n >= 16)
-    __builtin_amdgcn_s_waitcnt((16 & 0xF) | ((16 >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  else if (n >= 8)
-    __builtin_amdgcn_s_waitcnt(8 | (0x7 << 4) | (0xF << 8));
+// s_waitcnt immediate: vector-memory count n, export and LDS counts left open.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Wait until the DMA loads of at most `ahead` later tiles (0 .. 3) of this
+// wave are still in flight, P loads per tile.
+template <int P>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if (ahead >= 3)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * P));
+  else if (ahead == 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * P));
+  else if (ahead == 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(P));
   else
-    __builtin_amdgcn_s_waitcnt(0x7 << 4 | (0xF << 8));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 __device__ __forceinline__ void ws_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <bool kI8>
 __global__ void __launch_bounds__(kWaves * kWave, PKV_PREFILL_WAVES_PER_SIMD)
 prefill_kernel(const PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char s_k[kStages][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char s_v[kStages][kTileBytes];
+  using Lds = PrefillLds<kI8>;
+  __shared__ __attribute__((aligned(1024))) char smem[Lds::kBytes];
   __shared__ int s_ids[kMaxTilesPerSplit * 4];
   __shared__ int s_bad;
   __shared__ int s_last;
@@ -200,6 +231,18 @@ prefill_kernel(const PrefillArgs a) {
   const int qpos_min = n - T + R0 / G;        // smallest position in the workgroup
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
 
+  // Q^T as the B operand: lane holds Q[row][16kk + 8*half .. +8], kk = 0..7.
+  bf16x8 qb[8];
+  {
+    const u32x4* qp = a.q + ((int64_t)(q_lo + t_row) * a.Hq + g * G + j_row) * 16;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok && !bad_len) v = qp[2 * kk + half];
+      qb[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
   // Page ids of this split's tiles into LDS (0 for pages the workgroup does
   // not need); invalid ids of needed pages poison the result.
   int bad = 0;
@@ -214,37 +257,80 @@ prefill_kernel(const PrefillArgs a) {
     s_ids[p] = id;
   }
 
-  // Q^T as the B operand: lane holds Q[row][16kk + 8*half .. +8], kk = 0..7.
-  bf16x8 qb[8];
-  {
-    const u32x4* qp = a.q + ((int64_t)(q_lo + t_row) * a.Hq + g * G + j_row) * 16;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok && !bad_len) v = qp[2 * kk + half];
-      qb[kk] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  // The ring's DMA loads are invisible to the compiler's wait counting, so
+  // if a plain load (Q, the table) could still be in flight when the loop
+  // starts, it would wait for vmcnt(0), i.e. for every tile in flight,
+  // before each tile's first MFMA.  One explicit full wait here (Q has been
+  // loading during the table reads) keeps those waits out of the loop.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // DMA of tile i (relative) into stage i % 3: wave w copies page w of the
-  // tile, 4 instructions of 4 rows for K and for V.  Lane l of instruction q
-  // fills row 16w + 4q + l/16 at chunk position l%16 with logical chunk
-  // (l%16) ^ sw(row).
-  const uint32_t k_lds = lds_offset(&s_k[0][0]);
-  const uint32_t v_lds = lds_offset(&s_v[0][0]);
+  // DMA of tile i (relative) into stage i % kStages: wave w copies page w of
+  // the tile.  bf16: 4 instructions of 4 rows for K and for V; lane l of
+  // instruction q fills row 16w + 4q + l/16 at chunk position l%16 with
+  // logical chunk (l%16) ^ sw(row).  int8: the page's 2 KB of K codes and of
+  // V codes (2 instructions each, rows in order, 128 B apart) and its 128 B
+  // scale block, which lanes l and l+8k all load (lanes 0..7 give it in
+  // order; the rest of the 1 KB slot is never read).
+  const uint32_t k_lds = lds_offset(smem);
+  const uint32_t v_lds = k_lds + Lds::kVOff;
   const int dma_r16 = lane >> 4;              // + 4q: row within the page
   auto issue = [&](int i) {
     const int stage = i % kStages;
     const int64_t blk = __builtin_amdgcn_readfirstlane(s_ids[4 * i + w]);
+    if constexpr (kI8) {
+      const uint32_t cs = k_lds + Lds::kCodeOff + stage * kCodeStageBytes;
+      const int64_t pg = blk * a.Hkv + g;     // (page, KV head): 128 chunks of codes
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int r16 = 4 * qd + dma_r16;
-      const int c = (lane & 15) ^ swz(r16);
-      const int64_t idx = ((blk * a.Hkv + g) * kPage + r16) * 16 + c;
-      const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
-      dma16(a.k_cache + idx, k_lds + off);
-      dma16(a.v_cache + idx, v_lds + off);
+      for (int qd = 0; qd < 2; ++qd) {
+        const uint32_t off = (uint32_t)(w * kPage * kD + qd * 1024);
+        dma16(a.k_cache + pg * 128 + qd * 64 + lane, cs + off);
+        dma16(a.v_cache + pg * 128 + qd * 64 + lane, cs + kCodeTileBytes + off);
+      }
+      dma16(a.kv_scales + pg * 8 + (lane & 7), cs + 2 * kCodeTileBytes + w * kScaleSlotBytes);
+    } else {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int r16 = 4 * qd + dma_r16;
+        const int c = (lane & 15) ^ swz(r16);
+        const int64_t idx = ((blk * a.Hkv + g) * kPage + r16) * 16 + c;
+        const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
+        dma16(a.k_cache + idx, k_lds + off);
+        dma16(a.v_cache + idx, v_lds + off);
+      }
+    }
+  };
+
+  // int8: dequantise code stage `stage` into bf16 buffer `buf` (swizzled
+  // rows, as the bf16 DMA writes them).  Thread: rows tid/8 and tid/8 + 32,
+  // 16 codes (dims 16c .. 16c+15, c = tid % 8), K then V.  V rows outside
+  // [key_lo, key_end) get scale 0: they are never visible, and zeros keep
+  // whatever their slots hold out of the PV product.
+  auto dequant = [&](int stage, int buf, int key0, int key_end, int key_lo) {
+    const char* cs = smem + Lds::kCodeOff + stage * kCodeStageBytes;
+    const int c = tid & 7;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int which = k >> 1;                  // 0: K, 1: V
+      const int r = (tid >> 3) + 32 * (k & 1);   // key row of the tile
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(cs + which * kCodeTileBytes + r * kD + c * 16);
+      const int slot = r & 15;                   // scales of a page: [slot % 8][slot / 8][K, V]
+      float sc = *reinterpret_cast<const float*>(
+          cs + 2 * kCodeTileBytes + (r >> 4) * kScaleSlotBytes +
+          ((slot & 7) * 4 + (slot >> 3) * 2 + which) * 4);
+      if (which && (key0 + r >= key_end || key0 + r < key_lo)) sc = 0.f;
+      uint32_t o8[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o8[2 * j] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(sbyte0(cw[j]) * sc),
+                                                        (__bf16)(sbyte1(cw[j]) * sc)});
+        o8[2 * j + 1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(sbyte2(cw[j]) * sc),
+                                                            (__bf16)(sbyte3(cw[j]) * sc)});
+      }
+      char* dst = smem + which * Lds::kVOff + buf * kTileBytes + r * kRowBytes;
+      *reinterpret_cast<u32x4*>(dst + (((2 * c) ^ swz(r)) << 4)) = u32x4{o8[0], o8[1], o8[2], o8[3]};
+      *reinterpret_cast<u32x4*>(dst + (((2 * c + 1) ^ swz(r)) << 4)) =
+          u32x4{o8[4], o8[5], o8[6], o8[7]};
     }
   };
 
@@ -285,16 +371,27 @@ prefill_kernel(const PrefillArgs a) {
     const int stage = i % kStages;
     const int key0 = (tile0 + i) * kTileKeys;
     if (i + kStages - 1 < nt) issue(i + kStages - 1);
-    wait_vm(8 * min(kStages - 1, nt - 1 - i));
+    wait_tiles<Lds::kVmPerTile>(min(kStages - 1, nt - 1 - i));
     __syncthreads();                          // every wave's page of tile i has landed
 
-    const char* ksm = s_k[stage];
-    const char* vsm = s_v[stage];
-    if (key0 + kTileKeys > key_end || key0 < key_lo) {
+    const char* ksm;
+    const char* vsm;
+    if constexpr (kI8) {
+      // The code stage of tile i is refilled only after the next barrier;
+      // bf16 buffer i % 2 was last read two tiles ago, before this barrier.
+      dequant(stage, i & 1, key0, key_end, key_lo);
+      __syncthreads();
+      ksm = smem + (i & 1) * kTileBytes;
+      vsm = smem + Lds::kVOff + (i & 1) * kTileBytes;
+    } else {
+      ksm = smem + stage * kTileBytes;
+      vsm = smem + Lds::kVOff + stage * kTileBytes;
+    }
+    if (!kI8 && (key0 + kTileKeys > key_end || key0 < key_lo)) {
       // Keys past key_end (and, in a ring, below key_lo) are always masked;
       // zero their V rows so the canary NaNs of unwritten slots cannot reach
       // the products (K is masked).
-      char* vz = s_v[stage];
+      char* vz = smem + Lds::kVOff + stage * kTileBytes;
       const u32x4 zero = {0u, 0u, 0u, 0u};
       for (int e = tid; e < kTileKeys * 16; e += kWaves * kWave) {
         const int r = e >> 4;
@@ -377,7 +474,7 @@ prefill_kernel(const PrefillArgs a) {
               bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hh], o[db], 0, 0, 0);
         }
-    __syncthreads();                          // stage i may be refilled from here on
+    if constexpr (!kI8) __syncthreads();      // stage i may be refilled from here on
   }
 
   // Row sums: each half of the lanes summed its own keys.
@@ -443,7 +540,7 @@ prefill_kernel(const PrefillArgs a) {
   // The bf16 tile is staged in LDS and written out in 16-byte row chunks.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int64_t g0 = (int64_t)group * a.splits;
-  float* fbuf = reinterpret_cast<float*>(&s_v[0][0]);       // [kMaxSplits][128], 16 KB
+  float* fbuf = reinterpret_cast<float*>(smem + Lds::kFbufOff);   // [kMaxSplits][128], 16 KB
   if (tid < kRowsPerWG) {
     const float* ml = a.ws_ml + 2 * (g0 * kRowsPerWG + tid);
     float M = kNegInf;
@@ -459,7 +556,7 @@ prefill_kernel(const PrefillArgs a) {
     for (int s2 = 0; s2 < ns; ++s2) fbuf[s2 * kRowsPerWG + tid] *= inv;
   }
   __syncthreads();
-  uint16_t* obuf = reinterpret_cast<uint16_t*>(&s_k[0][0]);  // [128][kD + 8], 34 KB
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(smem);        // [128][kD + 8], 34 KB
   constexpr int kOStride = kD + 8;
   {
     const int rq = tid & 31, dg = tid >> 5;
@@ -549,7 +646,7 @@ PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_
 }
 
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
-                          const void* v_cache, const int32_t* block_tables,
+                          const void* v_cache, const float* kv_scales, const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream) {
@@ -560,6 +657,7 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.cu_q = cu_q;
   a.k_cache = static_cast<const u32x4*>(k_cache);
   a.v_cache = static_cast<const u32x4*>(v_cache);
+  a.kv_scales = reinterpret_cast<const u32x4*>(kv_scales);
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
   char* ws = static_cast<char*>(workspace);
@@ -577,7 +675,10 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   const unsigned grid = (unsigned)((int64_t)B * a.qtiles * a.splits * Hkv);
-  hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
+  if (kv_scales)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 

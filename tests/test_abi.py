@@ -122,6 +122,14 @@ def test_int8_entry_points_reject_bad_arguments(lib):
                                     NULL, 0, NULL) == bd.PKV_EINVAL
     assert lib.pkv_attn_decode_int8(1, 2, 3, 4, 5, 5, 6, 2, 24, 8, 128, 16, 32, 4, 64, 0.088,
                                     NULL, 0, NULL) == bd.PKV_EUNSUPPORTED
+    # prefill: missing scales, D other than 128, context past the table, nothing to do
+    def pre(scales=5, D=128, mcl=64, total_q=8, out=1):
+        return lib.pkv_attn_prefill_chunk_int8(out, 2, 3, 4, 6, scales, 7, 8, 1, total_q, 8, 16,
+                                               8, D, 16, 32, 4, mcl, 0.088, NULL, 0, NULL)
+    assert pre(scales=NULL) == bd.PKV_EINVAL
+    assert pre(D=64) == bd.PKV_EUNSUPPORTED
+    assert pre(mcl=100) == bd.PKV_EINVAL
+    assert pre(total_q=0, out=NULL, scales=NULL) == bd.PKV_OK
 
 
 def test_copy_blocks_rejects_bad_arguments(lib):

@@ -1,10 +1,10 @@
-"""Parity of the int8-page path (append with quantisation, decode) with the
-CPU oracle, through the C ABI.
+"""Parity of the int8-page path (append with quantisation, decode, chunked
+prefill) with the CPU oracle, through the C ABI.
 
 The int8 append must match the oracle bit for bit (codes and float32 scale
 bits: both sides quantise in float32 as [P2]'s KV8Cache.write does).  Decode
 over int8 pages is held to the same tolerance as the bf16 path against the
-float64 oracle on the same codes and scales.
+float64 oracle on the same codes and scales, and so is chunked prefill.
 """
 import numpy as np
 import pytest
@@ -49,21 +49,29 @@ def check_close(got, want, what):
 
 
 def run_int8_step(w, layer=0):
-    """Slot mapping, int8 append and int8 decode on the GPU; the oracle's
-    append and decode on the CPU.  Returns (device layer data, out)."""
+    """Slot mapping, int8 append, then int8 prefill (chunk sequences) and
+    int8 decode on the GPU; the oracle's append, prefill and decode on the
+    CPU.  Returns (device layer data, decode out, prefill out)."""
     print(f"[int8 parity] {w.name} layer {layer}: {w.description}", flush=True)
-    assert not w.prefill_seqs
     t = S.make_tables(w)
     d = S.make_layer_int8(w, t, layer, device="cuda")
     kc0, vc0 = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
     ks0, vs0 = scales_pages_order(d.kv_scales)
     plan = ST.plan_step(w, t)
-    out = torch.empty_like(d.q_decode)
     ST.slot_mapping(plan)
     bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.kv_scales)
-    bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.kv_scales, plan.bt_decode,
-                            plan.ctx_decode, plan.max_ctx_decode, plan.scale,
-                            workspace=plan.workspace)
+    out = out_pre = None
+    if w.decode_seqs:
+        out = torch.empty_like(d.q_decode)
+        bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.kv_scales,
+                                plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode, plan.scale,
+                                workspace=plan.workspace)
+    if w.prefill_seqs:
+        out_pre = torch.empty_like(d.q_prefill)
+        bd.pkv_attn_prefill_chunk_int8(out_pre, d.q_prefill, plan.cu_q, d.k_codes, d.v_codes,
+                                       d.kv_scales, plan.bt_prefill, plan.ctx_prefill,
+                                       plan.max_q_len, plan.max_ctx_prefill, plan.scale,
+                                       workspace=plan.prefill_workspace)
     torch.cuda.synchronize()
     bt = t.block_tables.numpy().tolist()
     ctx = t.context_lens.numpy().tolist()
@@ -74,9 +82,16 @@ def run_int8_step(w, layer=0):
     assert np.array_equal(gk, kc) and np.array_equal(gv, vc), "codes after append differ"
     assert np.array_equal(gks.view(np.uint32), ks.view(np.uint32)), "K scales differ"
     assert np.array_equal(gvs.view(np.uint32), vs.view(np.uint32)), "V scales differ"
-    want = Q.decode_int8_ref(u16(d.q_decode), kc, ks, vc, vs, bt, ctx, O.default_scale(w.D))
-    check_close(out, want, f"{w.name} int8 decode")
-    return d, out
+    npre = len(w.prefill_seqs)
+    scale = O.default_scale(w.D)
+    if w.decode_seqs:
+        want = Q.decode_int8_ref(u16(d.q_decode), kc, ks, vc, vs, bt[npre:], ctx[npre:], scale)
+        check_close(out, want, f"{w.name} int8 decode")
+    if w.prefill_seqs:
+        want = Q.prefill_int8_ref(u16(d.q_prefill), S.prefill_cu(w).numpy().tolist(), kc, ks,
+                                  vc, vs, bt[:npre], ctx[:npre], scale)
+        check_close(out_pre, want, f"{w.name} int8 prefill")
+    return d, out, out_pre
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
@@ -101,6 +116,30 @@ def test_int8_decode_long_context_many_splits():
     w = S.custom_workload("int8_long", _seqs_decode([5000, 777, 3]), Hq=32, Hkv=8, D=128,
                           num_blocks=400, base_seed=180)
     assert bd.pkv_decode_num_splits(3, 32, 8, 128, 5000) > 1
+    run_int8_step(w)
+
+
+@pytest.mark.parametrize("chunk_step", [0, 2, 5])
+def test_int8_mixed_step_chunked_prefill(chunk_step):
+    """The mixed step (a 3000-token prompt in 512-token chunks plus 7 decode
+    sequences) over int8 pages: chunk at offset 0, a middle one, the last."""
+    run_int8_step(S.workload("c5", chunk_step))
+
+
+def test_int8_prefill_varlen_batch_group_sizes():
+    seqs = [S.SeqSpec(0, 37, True), S.SeqSpec(100, 1, True), S.SeqSpec(60, 200, True),
+            S.SeqSpec(16, 16, True), S.SeqSpec(3, 1, False), S.SeqSpec(90, 1, False)]
+    for G, Hkv in ((1, 4), (2, 4), (4, 2), (8, 1)):
+        w = S.custom_workload(f"int8_varlen_G{G}", seqs, Hq=Hkv * G, Hkv=Hkv, D=128,
+                              num_blocks=64, base_seed=190 + G)
+        run_int8_step(w)
+
+
+def test_int8_prefill_many_key_splits():
+    """A long context with few row tiles: many key splits and the merge."""
+    w = S.custom_workload("int8_long_prefill", [S.SeqSpec(6000, 64, True)], Hq=32, Hkv=8,
+                          D=128, num_blocks=400, base_seed=198)
+    assert bd.pkv_prefill_workspace_bytes(1, 64, 32, 8, 128, 6064) > 0
     run_int8_step(w)
 
 
