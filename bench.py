@@ -261,11 +261,9 @@ def build_parts(name, rotate_mib, device, kv="bf16"):
                               _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [0, 1])
     if name == "c5":
-        if kv != "bf16":
-            raise SystemExit("bench.py: the prefill chunk runs on bf16 pages only (--kv bf16)")
         base_w = S.workload("c5", 5)
         base_t = S.make_tables(base_w)
-        layers, copies = _layers(base_w, base_t, rotate_mib, device)
+        layers, copies = _layers(base_w, base_t, rotate_mib, device, kv)
         parts = []
         for s in range(6):
             w = S.workload("c5", s)
@@ -275,7 +273,7 @@ def build_parts(name, rotate_mib, device, kv="bf16"):
             t = S.Tables(base_t.block_tables, ctx, torch.cumsum(new, 0).to(torch.int32),
                          torch.tensor([q.pre_len for q in w.seqs], dtype=torch.int32))
             parts.append(Part(w, t, ST.plan_step(w, t, device=device), layers,
-                              _bufs(w, t, device), copies))
+                              _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [i % 6])
     w = S.workload(name)
     t = S.make_tables(w)
@@ -306,31 +304,40 @@ def run(args):
     use_events = not args.no_events
     dec_events, pre_events = [], []
 
-    def run_part(k, i, record):
+    def run_part(k, i, record, only=None):
         pt = parts[k]
         plan, qb = pt.plan, pt.bufs
         c = i % pt.copies
         n_layers = pt.w.n_layers
-        ST.slot_mapping(plan, stream=stream)
+        if only is None:
+            ST.slot_mapping(plan, stream=stream)
         for l in range(n_layers):
             d = pt.layers[c * n_layers + l]
-            if pt.kv == "int8":
+            if only is None and pt.kv == "int8":
                 bd.pkv_append_int8(qb["kn"], qb["vn"], plan.slot_mapping, d.k_codes, d.v_codes,
                                    d.kv_scales, stream=stream)
-            else:
+            elif only is None:
                 bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
                               stream=stream)
-            if plan.n_prefill:
+            if plan.n_prefill and only in (None, "prefill"):
                 if record:
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
-                bd.pkv_attn_prefill_chunk(qb["op"], qb["qp"], plan.cu_q, d.k_cache, d.v_cache,
-                                          plan.bt_prefill, plan.ctx_prefill, plan.max_q_len,
-                                          plan.max_ctx_prefill, plan.scale,
-                                          workspace=plan.prefill_workspace, stream=stream)
+                if pt.kv == "int8":
+                    bd.pkv_attn_prefill_chunk_int8(qb["op"], qb["qp"], plan.cu_q, d.k_codes,
+                                                   d.v_codes, d.kv_scales, plan.bt_prefill,
+                                                   plan.ctx_prefill, plan.max_q_len,
+                                                   plan.max_ctx_prefill, plan.scale,
+                                                   workspace=plan.prefill_workspace,
+                                                   stream=stream)
+                else:
+                    bd.pkv_attn_prefill_chunk(qb["op"], qb["qp"], plan.cu_q, d.k_cache,
+                                              d.v_cache, plan.bt_prefill, plan.ctx_prefill,
+                                              plan.max_q_len, plan.max_ctx_prefill, plan.scale,
+                                              workspace=plan.prefill_workspace, stream=stream)
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
-                    pre_events.append((k, e0, e1))
-            if plan.n_decode:
+                    pre_events.append((k, e0, e1, 1))
+            if plan.n_decode and only in (None, "decode"):
                 if record:
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
                 if pt.kv == "int8":
@@ -344,11 +351,11 @@ def run(args):
                                        plan.scale, workspace=plan.workspace, stream=stream)
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
-                    dec_events.append((k, e0, e1))
+                    dec_events.append((k, e0, e1, 1))
 
-    def one_step(i, record):
+    def one_step(i, record, only=None):
         for k in schedule(i):
-            run_part(k, i, record)
+            run_part(k, i, record, only)
 
     for i in range(args.warmup):
         one_step(i, False)
@@ -380,10 +387,33 @@ def run(args):
             graphs[i % period].replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        if use_events:            # per-launch durations: a separate eager pass
-            for i in range(min(args.steps, 2 * period)):
-                one_step(i, True)
-            torch.cuda.synchronize()
+        if use_events:
+            # Per-launch durations: for each distinct step, a graph of one
+            # kernel's launches alone (all layers, back to back), replayed
+            # with HIP events around the replays on the replay stream.
+            for only, events in (("prefill", pre_events), ("decode", dec_events)):
+                for i in range(period):
+                    for k in schedule(i):
+                        pt = parts[k]
+                        if not (pt.plan.n_prefill if only == "prefill" else pt.plan.n_decode):
+                            continue
+                        g = torch.cuda.CUDAGraph()
+                        stream = cap
+                        with torch.cuda.stream(cap):
+                            with torch.cuda.graph(g, stream=cap):
+                                run_part(k, i, False, only)
+                        stream = eager_stream
+                        torch.cuda.synchronize()
+                        g.replay()
+                        reps = 5
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        for _ in range(reps):
+                            g.replay()
+                        e1.record()
+                        torch.cuda.synchronize()
+                        events.append((k, e0, e1, reps * pt.w.n_layers))
     else:
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -396,8 +426,9 @@ def run(args):
     gbs = total_bytes / elapsed / 1e9
     roofline, extra = None, {}
     if dec_events:
-        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in dec_events]
-        byts = [parts[k].dec_bytes for (k, _, _) in dec_events]
+        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b, _) in dec_events]
+        byts = [parts[k].dec_bytes * n for (k, _, _, n) in dec_events]
+        n_launch = sum(n for (_, _, _, n) in dec_events)
         achieved = sum(byts) / sum(durs) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -405,21 +436,25 @@ def run(args):
                                                 else f"{args.workload}-int8"),
                     "kernel": ("decode_kernel (pkv_attn_decode)" if args.kv == "bf16"
                                else "decode_kernel<Int8Page> (pkv_attn_decode_int8)"),
-                    "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
-                    "bytes_per_launch": int(sum(byts) / len(byts)),
-                    "launches": len(durs),
-                    "timing": ("HIP events around eager launches, a pass after the timed graph "
-                               "replays" if args.graph else
+                    "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
+                    "bytes_per_launch": int(sum(byts) / n_launch),
+                    "launches": n_launch,
+                    "timing": ("HIP events around replays of graphs of this kernel's launches "
+                               "alone, after the timed step replays" if args.graph else
                                "HIP events around each launch in the timed region")}
     if pre_events:
-        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b) in pre_events]
-        fl = [parts[k].pre_flops for (k, _, _) in pre_events]
+        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b, _) in pre_events]
+        fl = [parts[k].pre_flops * n for (k, _, _, n) in pre_events]
+        n_launch = sum(n for (_, _, _, n) in pre_events)
         tflops = sum(fl) / sum(durs) / 1e12
         extra["prefill_mfma"] = {"bound": "mfma", "achieved": round(tflops, 2),
                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                                 "avg_launch_us": round(sum(durs) / len(durs) * 1e6, 2),
-                                 "kernel": "prefill_kernel (pkv_attn_prefill_chunk)"}
+                                 "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
+                                 "launches": n_launch,
+                                 "kernel": ("prefill_kernel (pkv_attn_prefill_chunk)"
+                                            if args.kv == "bf16" else
+                                            "prefill_kernel<int8> (pkv_attn_prefill_chunk_int8)")}
     w0 = parts[0].w
     cfg = {"workload": WORKLOAD_TEXT.get(args.workload, f"{args.workload}: {w0.description}"),
            "parts": [{"name": p.w.name, "layers": p.w.n_layers, "Hq": p.w.Hq, "Hkv": p.w.Hkv,
@@ -490,18 +525,18 @@ def cpu_baseline(args, parts):
                 slots = O.slot_ref(bt, cu, ctx)
                 if pt.kv == "int8":
                     kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, kn, vn, slots)
-                    Q.decode_int8_ref(qd, kc, ks, vc, vs, bt, ctx, scale)
-                    reps += 1
-                    used = time.perf_counter() - t0
-                    if used >= budget:
-                        break
-                    continue
-                kc, vc = O.append_ref(kc0, vc0, kn, vn, slots)
-                if npre:
-                    O.prefill_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, vc, bt[:npre],
-                                  ctx[:npre], scale)
-                if w.decode_seqs:
-                    O.decode_ref(qd, kc, vc, bt[npre:], ctx[npre:], scale)
+                    if npre:
+                        Q.prefill_int8_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, ks, vc, vs,
+                                           bt[:npre], ctx[:npre], scale)
+                    if w.decode_seqs:
+                        Q.decode_int8_ref(qd, kc, ks, vc, vs, bt[npre:], ctx[npre:], scale)
+                else:
+                    kc, vc = O.append_ref(kc0, vc0, kn, vn, slots)
+                    if npre:
+                        O.prefill_ref(qp, S.prefill_cu(w).numpy().tolist(), kc, vc, bt[:npre],
+                                      ctx[:npre], scale)
+                    if w.decode_seqs:
+                        O.decode_ref(qd, kc, vc, bt[npre:], ctx[npre:], scale)
                 reps += 1
                 used = time.perf_counter() - t0
                 if used >= budget:

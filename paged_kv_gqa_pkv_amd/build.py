@@ -30,6 +30,14 @@ COMMON = [
 ]
 
 
+# Per-source extra flags.  prefill.hip: keep the MFMA accumulators in VGPRs
+# (otherwise, with more than 256 registers, they land in AGPRs and every
+# tile copies them back and forth for the softmax rescale).
+EXTRA = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -39,7 +47,7 @@ def _hipcc() -> str:
 
 def _compile(hipcc: str, src: str, verbose: bool, defines, build_dir: str) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *COMMON, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+    cmd = [hipcc, *COMMON, *EXTRA.get(src, []), *[f"-D{d}" for d in defines], "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()

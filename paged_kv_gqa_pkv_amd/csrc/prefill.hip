@@ -13,9 +13,9 @@
 // KV head) and one range of key tiles; each wave owns 32 rows.  Keys are
 // walked in tiles of 64 (four pages, gathered through the block table) that
 // the 4 waves share through LDS.  Tiles arrive by direct global->LDS loads
-// (global_load_lds_dwordx4, one page per wave) into a ring of LDS stages,
-// up to two tiles ahead of the MFMA work, so no registers hold data in
-// flight.  LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled
+// (global_load_lds_dwordx4, one page per wave) into a ring of LDS stages
+// (two: the next tile loads while this one is used; deeper rings measured
+// no faster), so no registers hold data in flight.  LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled
 // by row, which keeps the K reads (b128) and the V transpose reads free of
 // bank conflicts without padding.  When there are too few row
 // tiles to fill the chip, the key range is cut into splits; each split writes
@@ -72,7 +72,7 @@ constexpr int kTileKeys = 64;                       // 4 pages
 constexpr int kRowBytes = kD * 2;                   // 256 B per key row in LDS
 constexpr int kTileBytes = kTileKeys * kRowBytes;   // 16 KB per K or V tile
 #ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 3        // LDS ring depth (tiles in flight + 1)
+#define PKV_PREFILL_STAGES 2        // LDS ring depth (tiles in flight + 1)
 #endif
 #ifndef PKV_PREFILL_WAVES_PER_SIMD
 #define PKV_PREFILL_WAVES_PER_SIMD 1  // register budget target
@@ -90,8 +90,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // ring).  int8 pages: two dequantised bf16 K tiles and two V tiles (double
 // buffer), then kStages code stages of {K codes, V codes, one 1 KB scale DMA
 // slot per page}.  After the key loop, the split merge reuses the space:
-// the bf16 output tile (34 KB) at offset 0 and the split weights (16 KB) at
-// kFbufOff.
+// the bf16 output tile (128 rows of kD + 8 values, 34 KB) at offset 0 and
+// the split weights (kMaxSplits x 128 floats, 16 KB) right after it.
 constexpr int kCodeTileBytes = kTileKeys * kD;                 // 8 KB of codes
 constexpr int kScaleSlotBytes = kWave * 16;                    // one 64-lane DMA
 constexpr int kCodeStageBytes = 2 * kCodeTileBytes + 4 * kScaleSlotBytes;
@@ -100,7 +100,9 @@ struct PrefillLds {
   static constexpr int kVOff = kI8 ? 2 * kTileBytes : kStages * kTileBytes;
   static constexpr int kCodeOff = 4 * kTileBytes;
   static constexpr int kBytes = kI8 ? kCodeOff + kStages * kCodeStageBytes : 2 * kStages * kTileBytes;
-  static constexpr int kFbufOff = kI8 ? kCodeOff : kVOff;
+  static constexpr int kObufBytes = kRowsPerWG * (kD + 8) * 2;
+  static constexpr int kFbufOff = (kObufBytes + 1023) / 1024 * 1024;
+  static_assert(kFbufOff + kMaxSplits * kRowsPerWG * 4 <= kBytes, "merge buffers exceed LDS");
   static constexpr int kVmPerTile = kI8 ? 5 : 8;   // DMA instructions per wave and tile
 };
 
@@ -119,7 +121,8 @@ struct PrefillArgs {
   int B, total_q, max_q_len, Hq, Hkv, G, num_blocks, max_blocks, qtiles, splits,
       tiles_per_split;
   int window;                    // > 0: the pages form a ring of `window` tokens
-  float scale_log2;
+  int neg_q;                     // scale < 0: q enters with its sign flipped
+  float scale_log2;              // |scale| * log2(e), > 0
 };
 
 // Chunk swizzle of an LDS key row: logical 16-byte chunk c of row r sits at
@@ -156,6 +159,15 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(P));
   else
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+// max of three floats in one instruction.  Written out because fmaxf on
+// MFMA results costs an extra NaN-quieting max per operand (the compiler
+// cannot tell they are canonical).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ void ws_store(float* p, float v) {
@@ -239,6 +251,7 @@ prefill_kernel(const PrefillArgs a) {
     for (int kk = 0; kk < 8; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row_ok && !bad_len) v = qp[2 * kk + half];
+      if (a.neg_q) v ^= 0x80008000u;          // (-q) . k * |scale| = q . k * scale, exactly
       qb[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -415,23 +428,26 @@ prefill_kernel(const PrefillArgs a) {
       }
     }
 
-    // Scale, causal mask, running max.  Accumulator ii of block kb holds key
-    // key0 + 32*kb + 8*(ii/4) + 4*half + ii%4.
-    const bool need_mask = key0 + kTileKeys - 1 > qpos_min || key0 < key_lo;
+    // Causal mask (in place, only on tiles that need it), running max and
+    // probabilities.  Accumulator ii of block kb holds key key0 + 32*kb +
+    // 8*(ii/4) + 4*half + ii%4.  The scale (> 0) is folded into the
+    // exponent, exp2(s * scale_log2 - m), one fma per score; m is in the
+    // scaled domain.
+    if (key0 + kTileKeys - 1 > qpos_min || key0 < key_lo) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int key = key0 + 32 * kb + 8 * (ii >> 2) + 4 * half + (ii & 3);
+          s[kb][ii] = (key <= qpos && key >= key_lo) ? s[kb][ii] : kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        float v = s[kb][ii] * a.scale_log2;
-        if (need_mask) {
-          const int key = key0 + 32 * kb + 8 * (ii >> 2) + 4 * half + (ii & 3);
-          v = (key <= qpos && key >= key_lo) ? v : kNegInf;
-        }
-        s[kb][ii] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+      for (int ii = 0; ii < 16; ii += 2) mx = max3(mx, s[kb][ii], s[kb][ii + 1]);
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
     // Raise the running max only when it grows by more than the slack (or on
     // the first visible key); exponents stay <= 2^slack.
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
@@ -444,19 +460,30 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) o[db][ii] *= alpha;
     }
-    const float mu = (m == kNegInf) ? 0.f : m;
+    const float nmu = (m == kNegInf) ? 0.f : -m;
 
-    // P^T in bf16: B operand of the PV product, k-step (kb, hh) = registers
-    // 8*hh .. 8*hh+7 of block kb.
+    // P^T in bf16, two values per convert: B operand of the PV product,
+    // k-step (kb, hh) = registers 8*hh .. 8*hh+7 of block kb.  The row sum
+    // adds the same rounded values, a pair per v_dot2 with (1, 1).
     bf16x8 pb[2][2];
+    float lp[2] = {0.f, 0.f};
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        const __bf16 p = (__bf16)fast_exp2(s[kb][ii] - mu);
-        pb[kb][ii >> 3][ii & 7] = p;
-        l += (float)p;
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = 8 * hh + 2 * e;
+          const bf16x2 pp = {(__bf16)fast_exp2(__builtin_fmaf(s[kb][ii], a.scale_log2, nmu)),
+                             (__bf16)fast_exp2(__builtin_fmaf(s[kb][ii + 1], a.scale_log2, nmu))};
+          lp[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lp[e & 1], false);
+          w4[e] = __builtin_bit_cast(uint32_t, pp);
+        }
+        pb[kb][hh] = __builtin_bit_cast(bf16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
       }
+    l += lp[0] + lp[1];
 
     // O^T += V^T . P^T.  A operand for dim block db, k-step (kb, hh): the lane
     // needs V[key][32*db + lane%32] for the keys
@@ -558,6 +585,7 @@ prefill_kernel(const PrefillArgs a) {
   __syncthreads();
   uint16_t* obuf = reinterpret_cast<uint16_t*>(smem);        // [128][kD + 8], 34 KB
   constexpr int kOStride = kD + 8;
+  static_assert(kRowsPerWG * kOStride * 2 <= Lds::kFbufOff, "output tile overlaps the weights");
   {
     const int rq = tid & 31, dg = tid >> 5;
     const float* accb = a.ws_acc + g0 * kD * kRowsPerWG + 4 * rq;
@@ -673,7 +701,13 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.splits = plan.splits;
   a.tiles_per_split = plan.tiles_per_split;
   a.window = window;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // The kernel needs a positive scale (it scales the row max, and masked
+  // scores are -inf): a negative one flips q's sign instead, and 0 becomes
+  // the least normal float, for which every product s * scale rounds to 0
+  // or a subnormal as it does for 0, so every weight is exp2(0) = 1 alike.
+  a.neg_q = scale < 0.f;
+  a.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+  if (!(a.scale_log2 > 0.f)) a.scale_log2 = 1.17549435e-38f;
   const unsigned grid = (unsigned)((int64_t)B * a.qtiles * a.splits * Hkv);
   if (kv_scales)
     hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
