@@ -54,9 +54,10 @@ def parse():
     p.add_argument("--kernels", action="store_true",
                    help="time the page-write kernels (append, int8 append, block copy, fused "
                         "norm+RoPE+append, slot mapping) by HIP-graph replay; one JSON line")
-    p.add_argument("--graph", action="store_true",
-                   help="capture each distinct step in a HIP graph and time graph replays "
-                        "(per-launch events then come from a separate eager pass)")
+    p.add_argument("--eager", dest="graph", action="store_false",
+                   help="launch every kernel from Python in the timed steps (default: capture "
+                        "each distinct step in a HIP graph and time graph replays; per-kernel "
+                        "times then come from graphs of one kernel's launches alone)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 1 GiB device copies (counter calibration under rocprofv3)")
     p.add_argument("--write-traffic-record", nargs=4,

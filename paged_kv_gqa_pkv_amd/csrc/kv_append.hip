@@ -70,12 +70,19 @@ append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
 // int8 append: quantise each new (token, KV head) row as the Module 04 page
 // does (kv_cache.py listing, section 5, KV8Cache.write), in float32:
 //   scale = max_d |x_d| / 127 + 1e-8,   code_d = clip(rint(x_d / scale), -127, 127)
-// with IEEE division (the default, correctly rounded) and round half to even,
-// so the codes and scale match the page's numpy float32 arithmetic bit for
-// bit.  16 lanes own one row of 128 values (8 per lane): the row max is a DPP
-// reduction inside the 16-lane row, each lane writes its 8 codes (8 bytes),
-// and the first lane writes the scale into the row-pair order of the scale
-// array ([page][head][s % 8][s / 8][K, V]).
+// with round half to even, so the codes and scale match the page's numpy
+// float32 arithmetic bit for bit.  16 lanes own one row of 128 values (8 per
+// lane): the row max is a DPP reduction inside the 16-lane row, each lane
+// writes its 8 codes (8 bytes), and the first lane writes the scale into the
+// row-pair order of the scale array ([page][head][s % 8][s / 8][K, V]).
+//
+// The quotients x_d / scale are the correctly rounded ones without a full
+// division each: with y = 1 / scale correctly rounded (one IEEE division per
+// row) and q = x * y, the residual e = x - q * scale is exact in an fma and
+// q + e * y rounds to the correctly rounded quotient (Markstein's theorem for
+// round-to-nearest division; it needs no underflow in the residual, which
+// holds for every |x| >= scale / 2, the only quotients that can round to a
+// nonzero code; smaller ones give code 0 either way).
 __device__ __forceinline__ float max16(float x) {
   x = fmaxf(x, dpp_f<kDppQuadSwap1>(x));
   x = fmaxf(x, dpp_f<kDppQuadSwap2>(x));
@@ -89,37 +96,39 @@ append_int8_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_
                    uint2* __restrict__ v_codes, float* __restrict__ kv_scales, int64_t n_rows,
                    int Hkv, int64_t num_slots) {
   const int sub = threadIdx.x & 15;                    // lane within the row group
-  const int64_t rows_per_step = (int64_t)gridDim.x * (blockDim.x / 16);
-  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4); r < n_rows;
-       r += rows_per_step) {
-    // r = (t * 2 + which) * Hkv + h: all 16 lanes of a row group share r, so
-    // the DPP reduction below only reads lanes of the same, active row.
-    const int h = (int)(r % Hkv);
-    const int which = (int)((r / Hkv) & 1);
-    const int64_t t = r / (2 * (int64_t)Hkv);
-    const u32x4 w = (which ? v_new : k_new)[(t * Hkv + h) * 16 + sub];
-    float x[8];
+  // r = (t * 2 + which) * Hkv + h, one row per 16-lane group: all 16 lanes
+  // share r, so the DPP reduction below only reads lanes of the same row.
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);
+  if (r >= n_rows) return;
+  const int h = (int)(r % Hkv);
+  const int which = (int)((r / Hkv) & 1);
+  const int64_t t = r / (2 * (int64_t)Hkv);
+  const int64_t slot = slots[t];
+  const u32x4 w = (which ? v_new : k_new)[(t * Hkv + h) * 16 + sub];
+  float x[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo(w[i]); x[2 * i + 1] = bf16hi(w[i]); }
-    float mx = 0.f;
+  for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo(w[i]); x[2 * i + 1] = bf16hi(w[i]); }
+  float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(x[i]));
-    mx = max16(mx);
-    const float scale = mx / 127.0f + 1e-8f;
-    uint32_t pk[2] = {0u, 0u};
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(x[i]));
+  mx = max16(mx);
+  const float scale = mx / 127.0f + 1e-8f;
+  const float y = 1.0f / scale;
+  uint32_t pk[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q = fminf(fmaxf(__builtin_rintf(x[i] / scale), -127.f), 127.f);
-      pk[i >> 2] |= ((uint32_t)(int32_t)q & 0xffu) << (8 * (i & 3));
-    }
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / kPage, off = slot % kPage;
-    const int64_t row = (blk * Hkv + h) * kPage + off;            // codes row (128 B)
-    (which ? v_codes : k_codes)[row * 16 + sub] = make_uint2(pk[0], pk[1]);
-    if (sub == 0)
-      kv_scales[((blk * Hkv + h) * 8 + (off & 7)) * 4 + (off >> 3) * 2 + which] = scale;
+  for (int i = 0; i < 8; ++i) {
+    const float q0 = x[i] * y;
+    const float e = __builtin_fmaf(-q0, scale, x[i]);
+    const float q = __builtin_fmaf(e, y, q0);
+    const float c = fminf(fmaxf(__builtin_rintf(q), -127.f), 127.f);
+    pk[i >> 2] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (i & 3));
   }
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / kPage, off = slot % kPage;
+  const int64_t row = (blk * Hkv + h) * kPage + off;              // codes row (128 B)
+  (which ? v_codes : k_codes)[row * 16 + sub] = make_uint2(pk[0], pk[1]);
+  if (sub == 0)
+    kv_scales[((blk * Hkv + h) * 8 + (off & 7)) * 4 + (off >> 3) * 2 + which] = scale;
 }
 
 hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_t* slots,
@@ -128,8 +137,8 @@ hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_
   if (T == 0) return hipSuccess;
   if (D != 128) return hipErrorInvalidValue;       // 16 lanes x 8 values per row
   const int64_t n_rows = (int64_t)T * 2 * Hkv;
-  int64_t blocks = (n_rows + 15) / 16;
-  if (blocks > 8192) blocks = 8192;
+  const int64_t blocks = (n_rows + 15) / 16;          // one row per 16 lanes
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(append_int8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const u32x4*)k_new, (const u32x4*)v_new, slots, (uint2*)k_codes,
                      (uint2*)v_codes, kv_scales, n_rows, Hkv, (int64_t)num_blocks * kPage);

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeAr
     // j in [0, Hq): q head; then the k heads; then the v heads
     if (j >= a.Hq + a.Hkv) {                 // v: a bit copy into the page slot
       const int h = j - a.Hq - a.Hkv;
-      if (slot >= 0) {
+      if (slot >= 0 && p >= 0 && p < a.max_pos) {
         const int64_t row = ((slot / kPage) * a.Hkv + h) * kPage + (slot % kPage);
         a.v_cache[row * 16 + sub] = a.v_in[((int64_t)t * a.Hkv + h) * 16 + sub];
       }
@@ -112,8 +112,8 @@ __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeAr
     // upper half's values when they move to the lower half.
     const bool low = sub < 8;
     const bool pos_ok = p >= 0 && p < a.max_pos;
-    const int64_t pe = pos_ok ? p : 0;
-    const u32x4 cw = a.cos_t[pe * 16 + sub], sw = a.sin_t[pe * 16 + sub];
+    u32x4 cw = {0u, 0u, 0u, 0u}, sw = {0u, 0u, 0u, 0u};
+    if (pos_ok) { cw = a.cos_t[(int64_t)p * 16 + sub]; sw = a.sin_t[(int64_t)p * 16 + sub]; }
     uint32_t out[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

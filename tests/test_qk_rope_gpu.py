@@ -144,3 +144,44 @@ def test_fused_decode_batch_and_missing_page():
     assert torch.isfinite(q_out.float()).all()
     changed = np.any(u16(dk) != before, axis=(1, 3))      # [block, slot] rows that changed
     assert changed.sum() == T - 1
+
+
+def test_fused_positions_beyond_the_tables():
+    """Tables of 64 positions; tokens at positions 63 and 64, 99: the first is
+    rotated as usual, the others give NaN q rows and write neither K nor V."""
+    ctxs = [10, 64, 65, 100]
+    seqs = [S.SeqSpec(c - 1, 1, False) for c in ctxs]
+    w = S.custom_workload("fused_beyond", seqs, Hq=16, Hkv=8, D=128, num_blocks=40,
+                          base_seed=920)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0)
+    T = len(ctxs)
+    cos_full, sin_full = tables()
+    cos_t, sin_t = cos_full[:64].contiguous(), sin_full[:64].contiguous()
+    q_in = S.randn_bf16((T, 16, 128), 921)
+    q_out = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
+    dk, dv = d.k_cache.cuda(), d.v_cache.cuda()
+    k0, v0 = u16(dk), u16(dv)
+    sm = torch.empty(T, dtype=torch.int32, device="cuda")
+    ones = torch.ones(128, dtype=torch.bfloat16)
+    bd.pkv_qk_norm_rope_append(q_out, q_in.cuda(), d.k_new.cuda(), d.v_new.cuda(), ones.cuda(),
+                               ones.cuda(), cos_t.cuda(), sin_t.cuda(), t.block_tables.cuda(),
+                               t.cu_new.cuda(), t.context_lens.cuda(), dk, dv, EPS,
+                               slot_mapping=sm)
+    torch.cuda.synchronize()
+    slots = O.slot_ref(t.block_tables.tolist(), t.cu_new.tolist(), t.context_lens.tolist())
+    assert sm.cpu().tolist() == slots
+    q = q_out.float().cpu()
+    assert torch.isfinite(q[:2]).all() and torch.isnan(q[2:]).all()
+    pos = R.positions_ref(t.cu_new.tolist(), t.context_lens.tolist())
+    f32 = lambda x: R.bits_to_f32(u16(x))
+    q_ref, _ = R.qk_norm_rope_ref(f32(q_in[:2]), f32(d.k_new[:2]), f32(ones), f32(ones),
+                                  R.bits_to_f32(u16(cos_t)), R.bits_to_f32(u16(sin_t)), pos[:2],
+                                  EPS, bf16=True)
+    assert ulps(u16(q_out[:2]), q_ref).max() <= 2
+    gk, gv = u16(dk), u16(dv)
+    for i, s_ in enumerate(slots):                     # [block][head][slot] rows
+        blk, off = divmod(s_, 16)
+        changed_k = not np.array_equal(gk[blk, :, off], k0[blk, :, off])
+        changed_v = not np.array_equal(gv[blk, :, off], v0[blk, :, off])
+        assert changed_k == (i < 2) and changed_v == (i < 2), (i, changed_k, changed_v)
