@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+GATE_CYCLES = 500_000          # GPU sleep queued before a timed launch (about 200 us)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) + decode tokens/s/GPU"
 
@@ -49,6 +50,9 @@ def parse():
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--no-events", action="store_true",
                    help="time steps only (no per-launch events), e.g. under a profiler")
+    p.add_argument("--gate-cycles", type=int, default=GATE_CYCLES,
+                   help="GPU sleep (cycles) queued before each launch timed by events in "
+                        "graph mode")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--kernels", action="store_true",
@@ -322,6 +326,8 @@ def run(args):
                               stream=stream)
             if plan.n_prefill and only in (None, "prefill"):
                 if record:
+                    if record == "gated":
+                        torch.cuda._sleep(args.gate_cycles)
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
                 if pt.kv == "int8":
                     bd.pkv_attn_prefill_chunk_int8(qb["op"], qb["qp"], plan.cu_q, d.k_codes,
@@ -340,6 +346,8 @@ def run(args):
                     pre_events.append((k, e0, e1, 1))
             if plan.n_decode and only in (None, "decode"):
                 if record:
+                    if record == "gated":
+                        torch.cuda._sleep(args.gate_cycles)
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
                 if pt.kv == "int8":
                     bd.pkv_attn_decode_int8(qb["od"], qb["qd"], d.k_codes, d.v_codes,
@@ -389,32 +397,13 @@ def run(args):
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         if use_events:
-            # Per-launch durations: for each distinct step, a graph of one
-            # kernel's launches alone (all layers, back to back), replayed
-            # with HIP events around the replays on the replay stream.
-            for only, events in (("prefill", pre_events), ("decode", dec_events)):
-                for i in range(period):
-                    for k in schedule(i):
-                        pt = parts[k]
-                        if not (pt.plan.n_prefill if only == "prefill" else pt.plan.n_decode):
-                            continue
-                        g = torch.cuda.CUDAGraph()
-                        stream = cap
-                        with torch.cuda.stream(cap):
-                            with torch.cuda.graph(g, stream=cap):
-                                run_part(k, i, False, only)
-                        stream = eager_stream
-                        torch.cuda.synchronize()
-                        g.replay()
-                        reps = 5
-                        e0 = torch.cuda.Event(enable_timing=True)
-                        e1 = torch.cuda.Event(enable_timing=True)
-                        e0.record()
-                        for _ in range(reps):
-                            g.replay()
-                        e1.record()
-                        torch.cuda.synchronize()
-                        events.append((k, e0, e1, reps * pt.w.n_layers))
+            # Per-launch durations: an eager pass after the timed replays, HIP
+            # events around each launch on its stream, each (event, launch,
+            # event) queued behind a GPU sleep so that the GPU never waits
+            # for Python between them and the events bracket the kernel alone.
+            for i in range(2 * period):
+                one_step(i, "gated")
+            torch.cuda.synchronize()
     else:
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -440,8 +429,9 @@ def run(args):
                     "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / n_launch),
                     "launches": n_launch,
-                    "timing": ("HIP events around replays of graphs of this kernel's launches "
-                               "alone, after the timed step replays" if args.graph else
+                    "timing": ("HIP events around each launch of an eager pass after the timed "
+                               "graph replays, each launch queued behind a GPU sleep"
+                               if args.graph else
                                "HIP events around each launch in the timed region")}
     if pre_events:
         durs = [a.elapsed_time(b) * 1e-3 for (_, a, b, _) in pre_events]
