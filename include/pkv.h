@@ -192,9 +192,11 @@ size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int
  *   max_q_len     host-side upper bound of T_b
  *   max_context_len  host-side upper bound of context_lens (plans key splits)
  *   workspace     device buffer of at least pkv_prefill_workspace_bytes(...)
- *                 bytes (may be NULL when that is 0); zero-filled before its
- *                 first use, left ready for the next call.  Calls that may
- *                 overlap in time need separate workspaces.
+ *                 bytes (may be NULL when that is 0); it holds the key
+ *                 splits' partial results between the attention launch and
+ *                 the merge launch that follows it on the stream, so it
+ *                 needs no initialisation.  Calls that may overlap in time
+ *                 need separate workspaces.
  */
 int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            const void* k_cache, const void* v_cache,

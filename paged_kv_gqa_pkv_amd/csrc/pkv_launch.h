@@ -75,7 +75,6 @@ struct PrefillPlan {
   int tiles_per_split;
   size_t ws_acc_bytes;      // float [groups][S][D][128]
   size_t ws_ml_bytes;       // float [groups][S][128][2]
-  size_t ws_counter_bytes;  // int [groups]
   size_t ws_bytes;          // total, 0 without splits
 };
 

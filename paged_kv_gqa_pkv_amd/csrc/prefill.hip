@@ -117,7 +117,6 @@ struct PrefillArgs {
   const int32_t* ctx_lens;       // [B]
   float* ws_acc;                 // [groups][splits][D][128 rows]
   float* ws_ml;                  // [groups][splits][128 rows][2]
-  int* counters;                 // [groups]; zero between calls
   int B, total_q, max_q_len, Hq, Hkv, G, num_blocks, max_blocks, qtiles, splits,
       tiles_per_split;
   int window;                    // > 0: the pages form a ring of `window` tokens
@@ -170,8 +169,37 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
-__device__ __forceinline__ void ws_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The rows of sequence b and the keys that row tile x of them needs; the
+// attention kernel and the merge kernel both derive their work from it.
+struct TileKeys {
+  int q_lo, T, n;
+  bool skip;          // rows outside [0, total_q), more than max_q_len, or none in this tile
+  bool bad_len;       // more rows than context (or than the ring): NaN rows
+  int key_lo, key_end, tile_first, n_tiles, ns;   // ns: non-empty key splits
+};
+
+__device__ __forceinline__ TileKeys tile_keys(const PrefillArgs& a, int b, int x) {
+  TileKeys k;
+  k.q_lo = a.cu_q[b];
+  k.T = a.cu_q[b + 1] - k.q_lo;
+  k.n = a.ctx_lens[b];
+  const int R0 = x * kRowsPerWG;
+  k.skip = k.q_lo < 0 || k.T < 0 || k.q_lo + k.T > a.total_q || k.T > a.max_q_len ||
+           R0 >= k.T * a.G;
+  // Ring paging (Module 04 page, section 4): position p sits at ring index
+  // p % window, i.e. in the table's page (p / 16) % (window / 16); the ring
+  // holds positions n - window .. n - 1, so keys below key_lo are gone.
+  const bool ring = a.window > 0;
+  k.bad_len = k.T > k.n || (ring ? k.T > a.window : k.n > a.max_blocks * kPage);
+  // Keys: 0 .. the last position of the tile's rows (from key_lo in a ring).
+  const int t_last = min(k.T - 1, (R0 + kRowsPerWG - 1) / a.G);
+  k.key_end = k.bad_len ? 0 : k.n - k.T + t_last + 1;
+  k.key_lo = ring && !k.bad_len ? max(0, k.n - a.window) : 0;
+  k.tile_first = k.key_lo / kTileKeys;
+  const int tile_end = (k.key_end + kTileKeys - 1) / kTileKeys;
+  k.n_tiles = max(0, tile_end - k.tile_first);
+  k.ns = (k.n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  return k;
 }
 
 template <bool kI8>
@@ -181,7 +209,6 @@ prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[Lds::kBytes];
   __shared__ int s_ids[kMaxTilesPerSplit * 4];
   __shared__ int s_bad;
-  __shared__ int s_last;
 
   // ((b * qtiles + x) * splits + ks) * Hkv + g: the KV head varies fastest, so
   // all workgroups of KV head g land on XCD g % 8 and share its L2.
@@ -198,20 +225,15 @@ prefill_kernel(const PrefillArgs a) {
   const int w = uniform(tid >> 6);
   const int G = a.G;
 
-  const int q_lo = a.cu_q[b];
-  const int T = a.cu_q[b + 1] - q_lo;
-  const int n = a.ctx_lens[b];
   // Rows outside [0, total_q) or more than max_q_len of them: nothing is read
   // or written for this sequence (its rows, if any exist, are not ours).
-  if (q_lo < 0 || T < 0 || q_lo + T > a.total_q || T > a.max_q_len) return;
+  const TileKeys tk = tile_keys(a, b, x);
+  if (tk.skip) return;                        // uniform over the workgroup
+  const int q_lo = tk.q_lo, T = tk.T, n = tk.n;
   const int R0 = x * kRowsPerWG;
-  if (R0 >= T * G) return;                    // uniform over the workgroup
-  // Ring paging (Module 04 page, section 4): position p sits at ring index
-  // p % window, i.e. in the table's page (p / 16) % (window / 16); the ring
-  // holds positions n - window .. n - 1, so keys below key_lo are gone.
   const bool ring = a.window > 0;
   const int ring_pages = ring ? a.window / kPage : 0;
-  const bool bad_len = T > n || (ring ? T > a.window : n > a.max_blocks * kPage);
+  const bool bad_len = tk.bad_len;
 
   // This lane's query row (lane column of the MFMA tiles).
   const int row = R0 + w * kRowsPerWave + (lane & 31);
@@ -220,16 +242,10 @@ prefill_kernel(const PrefillArgs a) {
   const int qpos = row_ok ? n - T + t_row : -1;
   const int half = lane >> 5;                 // which 8 of 16 k values the lane holds
 
-  // Keys this workgroup needs: 0 .. the last position of its rows; this
-  // split's share of the key tiles.
-  const int t_last = min(T - 1, (R0 + kRowsPerWG - 1) / G);
-  const int key_end = bad_len ? 0 : n - T + t_last + 1;
-  const int key_lo = ring && !bad_len ? max(0, n - a.window) : 0;
-  const int tile_first = key_lo / kTileKeys;
-  const int tile_end = (key_end + kTileKeys - 1) / kTileKeys;
-  const int n_tiles = max(0, tile_end - tile_first);
-  const int ns = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;   // non-empty splits
-  const int tile0 = tile_first + ks * a.tiles_per_split;
+  // This split's share of the key tiles.
+  const int key_end = tk.key_end, key_lo = tk.key_lo;
+  const int tile_end = tk.tile_first + tk.n_tiles;
+  const int tile0 = tk.tile_first + ks * a.tiles_per_split;
   const int tile1 = min(tile0 + a.tiles_per_split, tile_end);
   if (tile0 >= tile1) {
     if (ks == 0 && row_ok) {                  // bad length: no keys at all -> NaN rows
@@ -534,9 +550,8 @@ prefill_kernel(const PrefillArgs a) {
   }
 
   // Split path: write this split's unnormalised state for the workgroup's
-  // rows with agent-coherent stores (dim-major, so a store instruction covers
-  // 32 consecutive rows), count the arrival, and let the last split of the
-  // row tile merge all of them in split order.
+  // rows (dim-major, so a store instruction covers 32 consecutive rows) and
+  // end; the merge kernel that follows on the stream combines the splits.
   const int lrow = w * kRowsPerWave + (lane & 31);          // row within the tile
   const int64_t sbase = (int64_t)group * a.splits + ks;     // (group, split)
   float* pacc = a.ws_acc + sbase * kD * kRowsPerWG + lrow;
@@ -545,87 +560,102 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int d = 32 * db + 8 * (i >> 2) + 4 * half + (i & 3);
-      ws_store(pacc + d * kRowsPerWG, poisoned ? nan : o[db][i]);
+      pacc[d * kRowsPerWG] = poisoned ? nan : o[db][i];
     }
   if (half == 0) {
-    ws_store(a.ws_ml + 2 * (sbase * kRowsPerWG + lrow), m);
-    ws_store(a.ws_ml + 2 * (sbase * kRowsPerWG + lrow) + 1, poisoned ? nan : l);
+    a.ws_ml[2 * (sbase * kRowsPerWG + lrow)] = m;
+    a.ws_ml[2 * (sbase * kRowsPerWG + lrow) + 1] = poisoned ? nan : l;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int* counter = a.counters + group;
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             ns - 1;
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // Merge.  The acquire fence drops stale cache lines, so plain (batched)
-  // loads see the other splits' agent-coherent stores.  (1) Per row, the
-  // split weights exp2(m_s - M) / L go to LDS.  (2) Thread (rows 4q..4q+3,
-  // dims dg + 8j) accumulates 16-byte loads over the splits in order.  (3)
-  // The bf16 tile is staged in LDS and written out in 16-byte row chunks.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+// Split merge: one workgroup per (group, 32-row slice).  (1) Per row, the
+// split weights exp2(m_s - M) / L go to LDS, all splits' (m, l) loaded at
+// once.  (2) Thread (dim d = tid / 2, rows 16 (tid % 2) .. +15 of the slice)
+// accumulates the splits in split order, 8 splits' loads in flight at a
+// time.  (3) The bf16 slice is staged in LDS and written in 16-byte row
+// chunks.  Groups whose key range fits one split still wrote partials when
+// the launch has splits; empty splits wrote nothing and are not read.
+constexpr int kMergeRows = 32;
+__global__ void __launch_bounds__(256) prefill_merge_kernel(const PrefillArgs a) {
+  __shared__ float s_w[kMaxSplits][kMergeRows];
+  __shared__ __attribute__((aligned(16))) uint16_t s_o[kMergeRows][kD + 8];
+  constexpr int kSlices = kRowsPerWG / kMergeRows;
+  const int slice = blockIdx.x % kSlices;
+  const int group = blockIdx.x / kSlices;
+  const int g = group % a.Hkv;
+  const int rest = group / a.Hkv;
+  const int x = rest % a.qtiles;
+  const int b = rest / a.qtiles;
+  const TileKeys tk = tile_keys(a, b, x);
+  const int G = a.G;
+  const int rs0 = x * kRowsPerWG + slice * kMergeRows;      // first row of the slice
+  if (tk.skip || tk.ns == 0 || rs0 >= tk.T * G) return;     // ns 0: NaN rows written already
+  // A context longer than the plan's bound has more non-empty splits than
+  // were launched; only the launched ones hold partials.
+  const int ns = min(tk.ns, a.splits);
+  const int tid = threadIdx.x;
   const int64_t g0 = (int64_t)group * a.splits;
-  float* fbuf = reinterpret_cast<float*>(smem + Lds::kFbufOff);   // [kMaxSplits][128], 16 KB
-  if (tid < kRowsPerWG) {
-    const float* ml = a.ws_ml + 2 * (g0 * kRowsPerWG + tid);
+  const int lrow0 = slice * kMergeRows;                     // slice's first row in the tile
+  if (tid < kMergeRows) {
+    const float* ml = a.ws_ml + 2 * (g0 * kRowsPerWG + lrow0 + tid);
+    f32x2 mlv[kMaxSplits];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2)
+      mlv[s2] = s2 < ns ? *reinterpret_cast<const f32x2*>(ml + 2 * s2 * kRowsPerWG)
+                        : f32x2{kNegInf, 0.f};
     float M = kNegInf;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ml[2 * s2 * kRowsPerWG]);
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) M = fmaxf(M, mlv[s2][0]);
     const float Mu = (M == kNegInf) ? 0.f : M;
+    float f[kMaxSplits];
     float L = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) {
-      const float f = fast_exp2(ml[2 * s2 * kRowsPerWG] - Mu);
-      fbuf[s2 * kRowsPerWG + tid] = f;
-      L = __builtin_fmaf(ml[2 * s2 * kRowsPerWG + 1], f, L);
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+      f[s2] = s2 < ns ? fast_exp2(mlv[s2][0] - Mu) : 0.f;
+      L = __builtin_fmaf(mlv[s2][1], f[s2], L);
     }
     const float inv = 1.f / L;
-    for (int s2 = 0; s2 < ns; ++s2) fbuf[s2 * kRowsPerWG + tid] *= inv;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2)
+      if (s2 < ns) s_w[s2][tid] = f[s2] * inv;
   }
   __syncthreads();
-  uint16_t* obuf = reinterpret_cast<uint16_t*>(smem);        // [128][kD + 8], 34 KB
-  constexpr int kOStride = kD + 8;
-  static_assert(kRowsPerWG * kOStride * 2 <= Lds::kFbufOff, "output tile overlaps the weights");
-  {
-    const int rq = tid & 31, dg = tid >> 5;
-    const float* accb = a.ws_acc + g0 * kD * kRowsPerWG + 4 * rq;
+  const int d = tid >> 1, r0 = 16 * (tid & 1);
+  const float* accb = a.ws_acc + (g0 * kD + d) * kRowsPerWG + lrow0 + r0;
+  f32x4 acc[4] = {};
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    f32x4 v[8][4];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      f32x4 acc[8];
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < ns; ++s2) {
-        f32x4 v[8];
+      for (int q = 0; q < 4; ++q)
+        v[j][q] = s0 + j < ns ? *reinterpret_cast<const f32x4*>(
+                                    accb + (int64_t)(s0 + j) * kD * kRowsPerWG + 4 * q)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int d = dg + 8 * (8 * pass + k);
-          v[k] = *reinterpret_cast<const f32x4*>(accb + ((int64_t)s2 * kD + d) * kRowsPerWG);
-        }
-        const f32x4 f = *reinterpret_cast<const f32x4*>(fbuf + s2 * kRowsPerWG + 4 * rq);
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j >= ns) break;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[k][e] = __builtin_fmaf(v[k][e], f[e], acc[k][e]);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int d = dg + 8 * (8 * pass + k);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          obuf[(4 * rq + e) * kOStride + d] = (uint16_t)f32_to_bf16_bits(acc[k][e]);
-      }
+          acc[q][e] = __builtin_fmaf(v[j][q][e], s_w[s0 + j][r0 + 4 * q + e], acc[q][e]);
     }
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      s_o[r0 + 4 * q + e][d] = (uint16_t)f32_to_bf16_bits(acc[q][e]);
   __syncthreads();
-  for (int c = tid; c < kRowsPerWG * (kD / 8); c += kWaves * kWave) {
+  for (int c = tid; c < kMergeRows * (kD / 8); c += 256) {
     const int r = c / (kD / 8), ch = c % (kD / 8);
-    const int mrow = R0 + r, mt = mrow / G, mj = mrow % G;
-    if (mt < T) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + r * kOStride + ch * 8);
-      reinterpret_cast<u32x4*>(a.out + ((int64_t)(q_lo + mt) * a.Hq + g * G + mj) * kD)[ch] = v;
+    const int mrow = rs0 + r, mt = mrow / G, mj = mrow % G;
+    if (mt < tk.T) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&s_o[r][ch * 8]);
+      reinterpret_cast<u32x4*>(a.out + ((int64_t)(tk.q_lo + mt) * a.Hq + g * G + mj) * kD)[ch] = v;
     }
   }
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -667,9 +697,8 @@ PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_
   if (p.ok && p.splits > 1) {
     p.ws_acc_bytes = align256((size_t)groups * p.splits * kRowsPerWG * kD * sizeof(float));
     p.ws_ml_bytes = align256((size_t)groups * p.splits * kRowsPerWG * 2 * sizeof(float));
-    p.ws_counter_bytes = align256((size_t)groups * sizeof(int));
   }
-  p.ws_bytes = p.ws_acc_bytes + p.ws_ml_bytes + p.ws_counter_bytes;
+  p.ws_bytes = p.ws_acc_bytes + p.ws_ml_bytes;
   return p;
 }
 
@@ -692,8 +721,6 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   const bool split = plan.splits > 1;
   a.ws_acc = split ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_ml = split ? reinterpret_cast<float*>(ws + plan.ws_acc_bytes) : nullptr;
-  a.counters = split ? reinterpret_cast<int*>(ws + plan.ws_acc_bytes + plan.ws_ml_bytes)
-                     : nullptr;
   a.B = B; a.total_q = total_q; a.max_q_len = max_q_len;
   a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.num_blocks = num_blocks; a.max_blocks = max_blocks;
@@ -713,6 +740,10 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
     hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
   else
     hipLaunchKernelGGL(prefill_kernel<false>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
+  if (split) {
+    const unsigned mgrid = (unsigned)((int64_t)B * a.qtiles * Hkv * (kRowsPerWG / kMergeRows));
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3(mgrid), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
