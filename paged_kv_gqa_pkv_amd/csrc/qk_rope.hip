@@ -36,9 +36,9 @@ __device__ __forceinline__ float sum16(float x) {
   return x + dpp_f<kDppRowRor8>(x);
 }
 
-__device__ __forceinline__ float round_bf16(float x) {
-  return __uint_as_float(f32_to_bf16_bits(x) << 16);
-}
+// float -> nearest bf16 (ties to even) -> float: the hardware convert
+// (v_cvt_pk_bf16_f32) and a shift back.
+__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
 
 struct QkRopeArgs {
   uint16_t* q_out;             // bf16 [T][Hq][D]
@@ -127,7 +127,8 @@ __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeAr
         const float s = e ? bf16hi(sw[i]) : bf16lo(sw[i]);
         o2[e] = round_bf16(round_bf16(yi * c) + round_bf16(rot * s));
       }
-      out[i] = pos_ok ? (f32_to_bf16_bits(o2[0]) | (f32_to_bf16_bits(o2[1]) << 16)) : 0x7fc07fc0u;
+      out[i] = pos_ok ? __builtin_bit_cast(uint32_t, bf16x2{(__bf16)o2[0], (__bf16)o2[1]})
+                    : 0x7fc07fc0u;
     }
     const u32x4 ov = {out[0], out[1], out[2], out[3]};
     if (is_q) {
