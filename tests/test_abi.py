@@ -96,6 +96,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(q=NULL) == bd.PKV_EINVAL
     assert call(mq=9) == bd.PKV_EINVAL                               # max_q_len > total_q
     assert call(mcl=100, mb=4) == bd.PKV_EINVAL
+    assert call(mcl=131073, mb=8193) == bd.PKV_EUNSUPPORTED           # past 32 x 64 x 64 keys
     assert call(total_q=0, out=NULL) == bd.PKV_OK
 
 
