@@ -586,6 +586,34 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(const PrefillArgs a)
   const int rest = group / a.Hkv;
   const int x = rest % a.qtiles;
   const int b = rest / a.qtiles;
+  // Every load of the first 8 launched splits' partials and of all (m, l)
+  // goes out before the split count is known (the workspace holds every
+  // launched split, so these stay in bounds); the counts only decide what
+  // is used, so one memory latency covers the whole merge.
+  const int tid = threadIdx.x;
+  const int64_t g0 = (int64_t)group * a.splits;
+  const int lrow0 = slice * kMergeRows;                     // slice's first row in the tile
+  const int d = tid >> 1, r0 = 16 * (tid & 1);
+  const float* accb = a.ws_acc + (g0 * kD + d) * kRowsPerWG + lrow0 + r0;
+  auto load8 = [&](f32x4 (&v)[8][4], int s0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[j][q] = s0 + j < a.splits ? *reinterpret_cast<const f32x4*>(
+                                          accb + (int64_t)(s0 + j) * kD * kRowsPerWG + 4 * q)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  f32x4 v[8][4];
+  load8(v, 0);
+  f32x2 mlv[kMaxSplits];
+  if (tid < kMergeRows) {
+    const float* ml = a.ws_ml + 2 * (g0 * kRowsPerWG + lrow0 + tid);
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2)
+      mlv[s2] = s2 < a.splits ? *reinterpret_cast<const f32x2*>(ml + 2 * s2 * kRowsPerWG)
+                              : f32x2{kNegInf, 0.f};
+  }
   const TileKeys tk = tile_keys(a, b, x);
   const int G = a.G;
   const int rs0 = x * kRowsPerWG + slice * kMergeRows;      // first row of the slice
@@ -593,26 +621,18 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(const PrefillArgs a)
   // A context longer than the plan's bound has more non-empty splits than
   // were launched; only the launched ones hold partials.
   const int ns = min(tk.ns, a.splits);
-  const int tid = threadIdx.x;
-  const int64_t g0 = (int64_t)group * a.splits;
-  const int lrow0 = slice * kMergeRows;                     // slice's first row in the tile
   if (tid < kMergeRows) {
-    const float* ml = a.ws_ml + 2 * (g0 * kRowsPerWG + lrow0 + tid);
-    f32x2 mlv[kMaxSplits];
-#pragma unroll
-    for (int s2 = 0; s2 < kMaxSplits; ++s2)
-      mlv[s2] = s2 < ns ? *reinterpret_cast<const f32x2*>(ml + 2 * s2 * kRowsPerWG)
-                        : f32x2{kNegInf, 0.f};
     float M = kNegInf;
 #pragma unroll
-    for (int s2 = 0; s2 < kMaxSplits; ++s2) M = fmaxf(M, mlv[s2][0]);
+    for (int s2 = 0; s2 < kMaxSplits; ++s2)
+      if (s2 < ns) M = fmaxf(M, mlv[s2][0]);
     const float Mu = (M == kNegInf) ? 0.f : M;
     float f[kMaxSplits];
     float L = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < kMaxSplits; ++s2) {
       f[s2] = s2 < ns ? fast_exp2(mlv[s2][0] - Mu) : 0.f;
-      L = __builtin_fmaf(mlv[s2][1], f[s2], L);
+      L = s2 < ns ? __builtin_fmaf(mlv[s2][1], f[s2], L) : L;
     }
     const float inv = 1.f / L;
 #pragma unroll
@@ -620,18 +640,9 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(const PrefillArgs a)
       if (s2 < ns) s_w[s2][tid] = f[s2] * inv;
   }
   __syncthreads();
-  const int d = tid >> 1, r0 = 16 * (tid & 1);
-  const float* accb = a.ws_acc + (g0 * kD + d) * kRowsPerWG + lrow0 + r0;
   f32x4 acc[4] = {};
   for (int s0 = 0; s0 < ns; s0 += 8) {
-    f32x4 v[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[j][q] = s0 + j < ns ? *reinterpret_cast<const f32x4*>(
-                                    accb + (int64_t)(s0 + j) * kD * kRowsPerWG + 4 * q)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s0 > 0) load8(v, s0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (s0 + j >= ns) break;
