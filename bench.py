@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--gate-cycles", type=int, default=GATE_CYCLES,
                    help="GPU sleep (cycles) queued before each launch timed by events in "
                         "graph mode")
+    p.add_argument("--one-stream", action="store_true",
+                   help="run a mixed step's decode after its chunk on one stream (default: "
+                        "on a second stream, concurrent with the chunk)")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--kernels", action="store_true",
@@ -306,6 +309,9 @@ def run(args):
     torch.cuda.set_device(0)
     parts, schedule = build_parts(args.workload, args.rotate_mib, device, args.kv)
     stream = torch.cuda.current_stream()
+    # A mixed step's decode runs on a second stream, concurrent with the
+    # chunk (both only read the pools after the append); default priority.
+    dstream = torch.cuda.Stream()
     use_events = not args.no_events
     dec_events, pre_events = [], []
 
@@ -344,23 +350,31 @@ def run(args):
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     pre_events.append((k, e0, e1, 1))
+            # the gated timing pass keeps one stream so that each kernel runs alone
+            overlap = (bool(plan.n_prefill) and not args.one_stream and record != "gated"
+                       and only is None)
+            ds = dstream if overlap else stream
+            if overlap:
+                ev = torch.cuda.Event(); ev.record(stream); ds.wait_event(ev)
             if plan.n_decode and only in (None, "decode"):
                 if record:
                     if record == "gated":
                         torch.cuda._sleep(args.gate_cycles)
-                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record(ds)
                 if pt.kv == "int8":
                     bd.pkv_attn_decode_int8(qb["od"], qb["qd"], d.k_codes, d.v_codes,
                                             d.kv_scales, plan.bt_decode, plan.ctx_decode,
                                             plan.max_ctx_decode, plan.scale,
-                                            workspace=plan.workspace, stream=stream)
+                                            workspace=plan.workspace, stream=ds)
                 else:
                     bd.pkv_attn_decode(qb["od"], qb["qd"], d.k_cache, d.v_cache,
                                        plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode,
-                                       plan.scale, workspace=plan.workspace, stream=stream)
+                                       plan.scale, workspace=plan.workspace, stream=ds)
                 if record:
-                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record(ds)
                     dec_events.append((k, e0, e1, 1))
+            if overlap:
+                ev = torch.cuda.Event(); ev.record(ds); stream.wait_event(ev)
 
     def one_step(i, record, only=None):
         for k in schedule(i):
@@ -459,7 +473,10 @@ def run(args):
            "page_tokens": 16,
            "kv_pages": ("bf16" if args.kv == "bf16" else
                         "int8 codes + float32 (K, V) scale per slot and KV head"),
-           "launch": "HIP graph per step, one stream" if args.graph else "eager, one stream"}
+           "launch": (("HIP graph per step" if args.graph else "eager") + (
+               ", one stream" if args.one_stream or not any(p.plan.n_prefill and p.plan.n_decode
+                                                             for p in parts)
+               else ", decode on a second stream concurrent with the chunk"))}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(1e3 * elapsed / args.steps, 5),

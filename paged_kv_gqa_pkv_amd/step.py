@@ -106,15 +106,31 @@ def slot_mapping(plan: StepPlan, stream=None) -> None:
 
 
 def layer(plan: StepPlan, k_cache, v_cache, k_new, v_new, q_decode=None, out_decode=None,
-          q_prefill=None, out_prefill=None, stream=None) -> None:
-    """Append the layer's new K/V, then run the chunk and decode attention."""
-    bd.pkv_append(k_new, v_new, plan.slot_mapping, k_cache, v_cache, stream=stream)
+          q_prefill=None, out_prefill=None, stream=None, decode_stream=None) -> None:
+    """Append the layer's new K/V, then run the chunk and decode attention.
+
+    With ``decode_stream`` (a stream of default priority), a step that has
+    both runs its decode launch there, concurrently with the chunk: both only
+    read the pools once the append is done, so the decode stream waits for
+    the append and ``stream`` waits for the decode before anything after.
+    """
+    s = stream if stream is not None else torch.cuda.current_stream()
+    bd.pkv_append(k_new, v_new, plan.slot_mapping, k_cache, v_cache, stream=s)
+    both = bool(plan.n_prefill and plan.n_decode and decode_stream is not None)
+    if both:
+        appended = torch.cuda.Event()
+        appended.record(s)
+        decode_stream.wait_event(appended)
     if plan.n_prefill:
         bd.pkv_attn_prefill_chunk(out_prefill, q_prefill, plan.cu_q, k_cache, v_cache,
                                   plan.bt_prefill, plan.ctx_prefill, plan.max_q_len,
                                   plan.max_ctx_prefill, plan.scale,
-                                  workspace=plan.prefill_workspace, stream=stream)
+                                  workspace=plan.prefill_workspace, stream=s)
     if plan.n_decode:
         bd.pkv_attn_decode(out_decode, q_decode, k_cache, v_cache, plan.bt_decode,
                            plan.ctx_decode, plan.max_ctx_decode, plan.scale,
-                           workspace=plan.workspace, stream=stream)
+                           workspace=plan.workspace, stream=decode_stream if both else s)
+    if both:
+        decoded = torch.cuda.Event()
+        decoded.record(decode_stream)
+        s.wait_event(decoded)

@@ -367,3 +367,55 @@ def test_graph_replays_match_eager():
         step()                                         # an eager step in between
         torch.cuda.synchronize()
         assert torch.equal(out_d.view(torch.int16), want_d.view(torch.int16)), rep
+
+
+def test_concurrent_decode_stream_matches_and_replays():
+    """The decode launch on a second stream, concurrent with the chunk (the
+    two only read the pools after the append): outputs and pools bit-identical
+    to the one-stream step, eagerly and in every replay of a graph captured
+    with both streams."""
+    seqs = [S.SeqSpec(2000, 300, True), S.SeqSpec(900, 1, False), S.SeqSpec(4000, 1, False)]
+    w = S.custom_workload("two_streams", seqs, Hq=16, Hkv=8, D=128, num_blocks=480,
+                          base_seed=98)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0, device="cuda")
+    plan = ST.plan_step(w, t)
+    k0, v0 = d.k_cache.clone(), d.v_cache.clone()
+    out_d, out_p = torch.empty_like(d.q_decode), torch.empty_like(d.q_prefill)
+
+    def step(stream=None, decode_stream=None):
+        ST.slot_mapping(plan, stream=stream)
+        ST.layer(plan, d.k_cache, d.v_cache, d.k_new, d.v_new, d.q_decode, out_d,
+                 d.q_prefill, out_p, stream=stream, decode_stream=decode_stream)
+
+    def reset():
+        out_d.fill_(0); out_p.fill_(0)
+        d.k_cache.copy_(k0); d.v_cache.copy_(v0)
+        torch.cuda.synchronize()
+
+    step()
+    torch.cuda.synchronize()
+    want_d, want_p, want_k = out_d.clone(), out_p.clone(), d.k_cache.clone()
+
+    def same(tag):
+        assert torch.equal(out_d.view(torch.int16), want_d.view(torch.int16)), tag
+        assert torch.equal(out_p.view(torch.int16), want_p.view(torch.int16)), tag
+        assert torch.equal(d.k_cache.view(torch.int16), want_k.view(torch.int16)), tag
+
+    side = torch.cuda.Stream()
+    reset()
+    step(decode_stream=side)
+    torch.cuda.synchronize()
+    same("eager, two streams")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step(stream=cap, decode_stream=side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        g.replay()
+        torch.cuda.synchronize()
+        same(f"replay {rep}")
