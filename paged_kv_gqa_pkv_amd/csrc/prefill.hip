@@ -13,14 +13,22 @@
 // KV head) and one range of key tiles; each wave owns 32 rows.  Keys are
 // walked in tiles of 64 (four pages, gathered through the block table) that
 // the 4 waves share through LDS.  Tiles arrive by direct global->LDS loads
-// (global_load_lds_dwordx4, one page per wave) into a ring of LDS stages
-// (two: the next tile loads while this one is used; deeper rings measured
-// no faster), so no registers hold data in flight.  LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled
-// by row, which keeps the K reads (b128) and the V transpose reads free of
-// bank conflicts without padding.  When there are too few row
-// tiles to fill the chip, the key range is cut into splits; each split writes
-// its unnormalised (m, l, O) and the last split of a row tile to finish
-// merges them in split order (as the decode kernel does).
+// (global_load_lds_dwordx4, one page per wave), so no registers hold data in
+// flight: bf16 pages through separate K and V rings of two stages (64 KB,
+// two workgroups per CU), int8 pages through a deeper ring of code stages.
+// LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled by row,
+// which keeps the K reads (b128) and the V transpose reads free of bank
+// conflicts without padding.  When there are too few row tiles to fill the
+// chip, the key range is cut into splits; each split writes its
+// unnormalised (m, l, O) and a small merge kernel that follows combines them
+// in split order.
+//
+// The key loop is software-pipelined: the score products of tile i+1 run on
+// the matrix cores while the VALU turns the scores of tile i into
+// probabilities, and the PV products of tile i while tile i+1 is masked and
+// its row max taken.  Exponentials and matrix products of one wave overlap;
+// those of different waves on one SIMD mostly do not, so the overlap has to
+// come from within the wave.
 //
 // Per tile and wave, on v_mfma_f32_32x32x16_bf16:
 //   S^T[keys x rows] = K[keys x D] . Q^T[D x rows]   (2 key blocks x 8 k-steps)
@@ -72,12 +80,10 @@ constexpr int kTileKeys = 64;                       // 4 pages
 constexpr int kRowBytes = kD * 2;                   // 256 B per key row in LDS
 constexpr int kTileBytes = kTileKeys * kRowBytes;   // 16 KB per K or V tile
 #ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 2        // LDS ring depth (tiles in flight + 1)
-#endif
-#ifndef PKV_PREFILL_WAVES_PER_SIMD
-#define PKV_PREFILL_WAVES_PER_SIMD 1  // register budget target
+#define PKV_PREFILL_STAGES 4        // int8 code ring depth (tiles in use: 2; loading: the rest)
 #endif
 constexpr int kStages = PKV_PREFILL_STAGES;
+static_assert(kStages >= 3 && kStages <= 6, "two tiles in use plus at least one loading");
 constexpr int kMaxTilesPerSplit = 64;               // page ids of a split fit in LDS
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;               // log2 units
@@ -97,13 +103,13 @@ constexpr int kScaleSlotBytes = kWave * 16;                    // one 64-lane DM
 constexpr int kCodeStageBytes = 2 * kCodeTileBytes + 4 * kScaleSlotBytes;
 template <bool kI8>
 struct PrefillLds {
-  static constexpr int kVOff = kI8 ? 2 * kTileBytes : kStages * kTileBytes;
+  static constexpr int kVOff = 2 * kTileBytes;
   static constexpr int kCodeOff = 4 * kTileBytes;
-  static constexpr int kBytes = kI8 ? kCodeOff + kStages * kCodeStageBytes : 2 * kStages * kTileBytes;
+  static constexpr int kBytes = kI8 ? kCodeOff + kStages * kCodeStageBytes : 4 * kTileBytes;
   static constexpr int kObufBytes = kRowsPerWG * (kD + 8) * 2;
   static constexpr int kFbufOff = (kObufBytes + 1023) / 1024 * 1024;
   static_assert(kFbufOff + kMaxSplits * kRowsPerWG * 4 <= kBytes, "merge buffers exceed LDS");
-  static constexpr int kVmPerTile = kI8 ? 5 : 8;   // DMA instructions per wave and tile
+  static constexpr int kVmPerTile = kI8 ? 5 : 4;   // DMA instructions per wave and tile (bf16: K or V)
 };
 
 struct PrefillArgs {
@@ -163,6 +169,11 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 // max of three floats in one instruction.  Written out because fmaxf on
 // MFMA results costs an extra NaN-quieting max per operand (the compiler
 // cannot tell they are canonical).
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 __device__ __forceinline__ float max3(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -202,8 +213,11 @@ __device__ __forceinline__ TileKeys tile_keys(const PrefillArgs& a, int b, int x
   return k;
 }
 
+// Register budget: bf16 pages run two workgroups per CU (two waves per SIMD,
+// so at most 256 registers each); int8 pages one (their code ring fills the
+// LDS).
 template <bool kI8>
-__global__ void __launch_bounds__(kWaves * kWave, PKV_PREFILL_WAVES_PER_SIMD)
+__global__ void __launch_bounds__(kWaves * kWave, kI8 ? 1 : 2)
 prefill_kernel(const PrefillArgs a) {
   using Lds = PrefillLds<kI8>;
   __shared__ __attribute__((aligned(1024))) char smem[Lds::kBytes];
@@ -294,20 +308,21 @@ prefill_kernel(const PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // DMA of tile i (relative) into stage i % kStages: wave w copies page w of
-  // the tile.  bf16: 4 instructions of 4 rows for K and for V; lane l of
-  // instruction q fills row 16w + 4q + l/16 at chunk position l%16 with
-  // logical chunk (l%16) ^ sw(row).  int8: the page's 2 KB of K codes and of
+  // DMA of tile i (relative): wave w copies page w of the tile.  bf16: the K
+  // or the V pages into stage i % 2 of their ring, 4 instructions of 4 rows;
+  // lane l of instruction q fills row 16w + 4q + l/16 at chunk position l%16
+  // with logical chunk (l%16) ^ sw(row).  int8: the page's 2 KB of K codes and of
   // V codes (2 instructions each, rows in order, 128 B apart) and its 128 B
   // scale block, which lanes l and l+8k all load (lanes 0..7 give it in
   // order; the rest of the 1 KB slot is never read).
   const uint32_t k_lds = lds_offset(smem);
   const uint32_t v_lds = k_lds + Lds::kVOff;
   const int dma_r16 = lane >> 4;              // + 4q: row within the page
-  auto issue = [&](int i) {
-    const int stage = i % kStages;
+  auto issue = [&](int i, bool is_v = false) {
+    const int stage = kI8 ? i % kStages : (i & 1);
     const int64_t blk = __builtin_amdgcn_readfirstlane(s_ids[4 * i + w]);
     if constexpr (kI8) {
+      (void)is_v;
       const uint32_t cs = k_lds + Lds::kCodeOff + stage * kCodeStageBytes;
       const int64_t pg = blk * a.Hkv + g;     // (page, KV head): 128 chunks of codes
 #pragma unroll
@@ -324,8 +339,10 @@ prefill_kernel(const PrefillArgs a) {
         const int c = (lane & 15) ^ swz(r16);
         const int64_t idx = ((blk * a.Hkv + g) * kPage + r16) * 16 + c;
         const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
-        dma16(a.k_cache + idx, k_lds + off);
-        dma16(a.v_cache + idx, v_lds + off);
+        if (is_v)
+          dma16(a.v_cache + idx, v_lds + off);
+        else
+          dma16(a.k_cache + idx, k_lds + off);
       }
     }
   };
@@ -363,26 +380,24 @@ prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // Lane read offsets.  K (A operand of S^T): row lane%32 (+32 per key
-  // block), logical chunk 2kk + half.  V (transpose reads): row
-  // 8p + 4half + m/4 (+32kb + 16hh), dims 32db + 16*(lane/16 % 2) + 4*(m%4).
-  int kaddr[8];
-  {
-    const int r = lane & 31;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kaddr[kk] = r * kRowBytes + (((2 * kk + half) ^ swz(r)) << 4);
-  }
-  int vaddr[2][4];
+  // Lane read offsets.  K (A operand of S^T): row r = lane%32 (+32 per key
+  // block), logical chunk 2kk + half, i.e. byte r*256 + ((2kk + half) ^
+  // sw(r))*16 = kbase ^ 32kk.  V (transpose reads): row r = 8p + 4half + m/4
+  // (+32kb + 16hh), dims 32db + 16*(lane/16 % 2) + 4*(m%4), i.e. logical
+  // chunk c = 4db + 2*(lane/16 % 2) + (m%4)/2 at byte r*256 + (c ^ sw(r))*16
+  // + 8*(m%2) = vbase[p] ^ 64db.  (The XOR terms sit in bits 4-7, clear of
+  // the row and stage bits, so a stage offset can be added first.)  One
+  // register per base instead of one per offset keeps the kernel within the
+  // two-waves-per-SIMD register budget.
+  const int kbase = (lane & 31) * kRowBytes + ((half ^ swz(lane & 31)) << 4);
+  int vbase[2];
   {
     const int m = lane & 15, k4 = m >> 2, j = m & 3, dh = (lane >> 4) & 1;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int r = 8 * p + 4 * half + k4;
-        const int c = 4 * db + 2 * dh + (j >> 1);
-        vaddr[p][db] = r * kRowBytes + ((c ^ swz(r)) << 4) + (j & 1) * 8;
-      }
+    for (int p = 0; p < 2; ++p) {
+      const int r = 8 * p + 4 * half + k4;
+      vbase[p] = r * kRowBytes + (((2 * dh + (j >> 1)) ^ swz(r)) << 4) + (j & 1) * 8;
+    }
   }
 
   f32x16 o[4];
@@ -392,46 +407,91 @@ prefill_kernel(const PrefillArgs a) {
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m = kNegInf, l = 0.f;
 
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < nt) issue(i);
+  // Software pipeline over the key tiles.  Step i, one wave's view:
+  //   phase A: S(i+1) = K(i+1) Q^T on the matrix cores while the VALU turns
+  //            S(i) into probabilities P(i);
+  //   phase B: O += V(i)^T P(i) on the matrix cores while S(i+1) is masked
+  //            (tiles on the diagonal or the ring's lower bound) and its row
+  //            max taken; the max is raised (O and l rescaled) after the PV
+  //            products.
+  // Every tile still goes mask -> max -> raise -> probabilities -> products,
+  // and O sees the products and rescales in tile order, so the result is
+  // the one of processing the tiles one at a time.  The score products of
+  // the next tile and the probabilities of this one are independent, which
+  // keeps the matrix cores fed from one wave.
+  //
+  // Loads.  bf16 pages: separate K and V rings of two stages (64 KB, two
+  // workgroups per CU); step i reads K(i+1) and V(i) while K(i+2) and
+  // V(i+1) load.  int8 pages: one ring of kStages code stages, each tile
+  // dequantised (K and V) into one of two bf16 buffers one step ahead.
+  auto key0_of = [&](int i) { return (tile0 + i) * kTileKeys; };
+  auto needs_mask = [&](int i) {
+    const int key0 = key0_of(i);
+    return key0 + kTileKeys - 1 > qpos_min || key0 < key_lo;
+  };
+  // Tiles with keys outside [key_lo, key_end): their V rows are zeroed.
+  auto has_invisible = [&](int i) {
+    const int key0 = key0_of(i);
+    return key0 + kTileKeys > key_end || key0 < key_lo;
+  };
+  // LDS byte offsets of the K and V tiles of tile i, passed through an
+  // empty asm so that the read addresses are formed inside each step (the
+  // loop is unrolled by two, which would otherwise make all 16 of them
+  // loop-invariant and keep them in registers).
+  auto k_tile = [&](int i) {
+    int off = (i & 1) * kTileBytes + kbase;
+    asm volatile("" : "+v"(off));
+    return off;
+  };
+  auto v_tile = [&](int i) {
+    int off = Lds::kVOff + (i & 1) * kTileBytes;
+    asm volatile("" : "+s"(off));
+    return off;
+  };
 
-  for (int i = 0; i < nt; ++i) {
-    const int stage = i % kStages;
-    const int key0 = (tile0 + i) * kTileKeys;
-    if (i + kStages - 1 < nt) issue(i + kStages - 1);
-    wait_tiles<Lds::kVmPerTile>(min(kStages - 1, nt - 1 - i));
-    __syncthreads();                          // every wave's page of tile i has landed
-
-    const char* ksm;
-    const char* vsm;
+  // int8: make tile j usable (before step j - 1, or before the loop for
+  // j = 0).  Tiles j - 1 and j are in use during step j - 1 and tiles j + 1
+  // .. j + kStages - 2 are loading, so the code stage refilled here is the
+  // one of tile j - 2, which every wave finished with before the barrier;
+  // bf16 buffer j % 2 last held tile j - 2 (read in steps j - 3, j - 2).
+  auto arrive8 = [&](int j) {
+    wait_tiles<Lds::kVmPerTile>(min(kStages - 3, nt - 1 - j));
+    __syncthreads();                            // every wave's page of tile j has landed
+    if (j + kStages - 2 < nt) issue(j + kStages - 2);
+    dequant(j % kStages, j & 1, key0_of(j), key_end, key_lo);
+    __syncthreads();
+  };
+  // Before step i: K(i+1) (if any) and V(i) become readable everywhere.
+  auto top = [&](int i) {
     if constexpr (kI8) {
-      // The code stage of tile i is refilled only after the next barrier;
-      // bf16 buffer i % 2 was last read two tiles ago, before this barrier.
-      dequant(stage, i & 1, key0, key_end, key_lo);
-      __syncthreads();
-      ksm = smem + (i & 1) * kTileBytes;
-      vsm = smem + Lds::kVOff + (i & 1) * kTileBytes;
+      if (i + 1 < nt) arrive8(i + 1);
     } else {
-      ksm = smem + stage * kTileBytes;
-      vsm = smem + Lds::kVOff + stage * kTileBytes;
-    }
-    if (!kI8 && (key0 + kTileKeys > key_end || key0 < key_lo)) {
-      // Keys past key_end (and, in a ring, below key_lo) are always masked;
-      // zero their V rows so the canary NaNs of unwritten slots cannot reach
-      // the products (K is masked).
-      char* vz = smem + Lds::kVOff + stage * kTileBytes;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      for (int e = tid; e < kTileKeys * 16; e += kWaves * kWave) {
-        const int r = e >> 4;
-        if (key0 + r >= key_end || key0 + r < key_lo)
-          *reinterpret_cast<u32x4*>(vz + r * kRowBytes + (e & 15) * 16) = zero;
-      }
+      // K(i+1) and V(i), issued before step i - 1, are the only loads in
+      // flight; after the barrier every wave is done with step i - 1, so
+      // K(i)'s and V(i-1)'s stages take K(i+2) and V(i+1).
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
+      if (i + 2 < nt) issue(i + 2, false);
+      if (i + 1 < nt) issue(i + 1, true);
+      if (has_invisible(i)) {
+        // Keys past key_end (and, in a ring, below key_lo) are always
+        // masked; zero their V rows so the canary NaNs of unwritten slots
+        // cannot reach the products (K is masked).
+        char* vz = smem + Lds::kVOff + (i & 1) * kTileBytes;
+        const int key0 = key0_of(i);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int e = tid; e < kTileKeys * 16; e += kWaves * kWave) {
+          const int r = e >> 4;
+          if (key0 + r >= key_end || key0 + r < key_lo)
+            *reinterpret_cast<u32x4*>(vz + r * kRowBytes + (e & 15) * 16) = zero;
+        }
+        __syncthreads();
+      }
     }
+  };
 
-    // S^T = K . Q^T for the two 32-key blocks of the tile.
-    f32x16 s[2];
+  // S^T = K . Q^T for the two 32-key blocks of a tile.
+  auto scores = [&](f32x16 (&s)[2], int kof) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -439,51 +499,54 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(ksm + kaddr[kk] + kb * 32 * kRowBytes);
+            *reinterpret_cast<const bf16x8*>(smem + ((kof ^ (kk << 5)) + kb * 32 * kRowBytes));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], s[kb], 0, 0, 0);
       }
     }
-
-    // Causal mask (in place, only on tiles that need it), running max and
-    // probabilities.  Accumulator ii of block kb holds key key0 + 32*kb +
-    // 8*(ii/4) + 4*half + ii%4.  The scale (> 0) is folded into the
-    // exponent, exp2(s * scale_log2 - m), one fma per score; m is in the
-    // scaled domain.
-    if (key0 + kTileKeys - 1 > qpos_min || key0 < key_lo) {
+  };
+  // Causal mask (and the ring's lower bound) in place; accumulator ii of
+  // block kb holds key key0 + 32*kb + 8*(ii/4) + 4*half + ii%4.
+  auto mask = [&](f32x16 (&s)[2], int key0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-          const int key = key0 + 32 * kb + 8 * (ii >> 2) + 4 * half + (ii & 3);
-          s[kb][ii] = (key <= qpos && key >= key_lo) ? s[kb][ii] : kNegInf;
-        }
-    }
+      for (int ii = 0; ii < 16; ++ii) {
+        const int key = key0 + 32 * kb + 8 * (ii >> 2) + 4 * half + (ii & 3);
+        s[kb][ii] = (key <= qpos && key >= key_lo) ? s[kb][ii] : kNegInf;
+      }
+  };
+  // Row max of a tile, scaled.
+  auto tile_max = [&](const f32x16 (&s)[2]) {
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ii = 0; ii < 16; ii += 2) mx = max3(mx, s[kb][ii], s[kb][ii + 1]);
-    mx = fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
-    // Raise the running max only when it grows by more than the slack (or on
-    // the first visible key); exponents stay <= 2^slack.
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
-      m = m_new;
-      l *= alpha;
+    return fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
+  };
+  // Raise the running max only when it grows by more than the slack (or on
+  // the first visible key); exponents stay <= 2^slack.
+  auto raise_max = [&](float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) == 0) return;
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
+    m = m_new;
+    l *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) o[db][ii] *= alpha;
-    }
+      for (int ii = 0; ii < 16; ++ii) o[db][ii] *= alpha;
+  };
+  // P^T of a tile in bf16, two values per convert, exp2(s * scale_log2 - m)
+  // with one fma per score (scale > 0; m in the scaled domain): the B
+  // operand of the PV product, k-step (kb, hh) = registers 8*hh .. 8*hh+7 of
+  // block kb.  The row sum adds the same rounded values, a pair per v_dot2
+  // with (1, 1), and is added to l.
+  bf16x8 pb[2][2];
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  auto probs = [&](const f32x16 (&s)[2]) {
     const float nmu = (m == kNegInf) ? 0.f : -m;
-
-    // P^T in bf16, two values per convert: B operand of the PV product,
-    // k-step (kb, hh) = registers 8*hh .. 8*hh+7 of block kb.  The row sum
-    // adds the same rounded values, a pair per v_dot2 with (1, 1).
-    bf16x8 pb[2][2];
     float lp[2] = {0.f, 0.f};
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -500,24 +563,76 @@ prefill_kernel(const PrefillArgs a) {
         pb[kb][hh] = __builtin_bit_cast(bf16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
       }
     l += lp[0] + lp[1];
-
-    // O^T += V^T . P^T.  A operand for dim block db, k-step (kb, hh): the lane
-    // needs V[key][32*db + lane%32] for the keys
-    // 32*kb + 16*hh + 8*(e/4) + 4*half + e%4, e = 0..7: two transpose reads.
+  };
+  // O^T += V^T . P^T.  A operand for dim block db, k-step (kb, hh): the lane
+  // needs V[key][32*db + lane%32] for the keys
+  // 32*kb + 16*hh + 8*(e/4) + 4*half + e%4, e = 0..7: two transpose reads.
+  auto pv = [&](int vof) {
+    const int vb0 = vof + vbase[0], vb1 = vof + vbase[1];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const char* vb = vsm + (32 * kb + 16 * hh) * kRowBytes;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[0][db]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[1][db]));
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const char* vb = smem + (32 * kb + 16 * hh) * kRowBytes;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (vb0 ^ (db << 6))));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + (vb1 ^ (db << 6))));
+          const bf16x8 va =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hh], o[db], 0, 0, 0);
         }
-    if constexpr (!kI8) __syncthreads();      // stage i may be refilled from here on
+  };
+  // Step i with a next tile: S(i) in sc, S(i+1) into sn.
+  auto step = [&](int i, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    top(i);
+    scores(sn, k_tile(i + 1));
+    probs(sc);
+    // keep the probabilities ahead of the branch below, beside the score
+    // products (the compiler would otherwise sink them into phase B)
+    asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l));
+    if (needs_mask(i + 1)) mask(sn, key0_of(i + 1));
+    pv(v_tile(i));
+    raise_max(tile_max(sn));
+  };
+  // The last step: no next tile.
+  auto last = [&](int i, f32x16 (&sc)[2]) {
+    top(i);
+    probs(sc);
+    pv(v_tile(i));
+  };
+
+  // K(0) first (bf16: with K(1) and V(0) behind it; int8: tiles 0 ..
+  // kStages - 3), then S(0).
+  if constexpr (kI8) {
+#pragma unroll
+    for (int i = 0; i < kStages - 2; ++i)
+      if (i < nt) issue(i);
+    arrive8(0);
+  } else {
+    issue(0, false);
+    if (nt > 1) issue(1, false);
+    issue(0, true);
+    if (nt > 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Lds::kVmPerTile));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(Lds::kVmPerTile));
+    __syncthreads();                            // every wave's page of K(0) has landed
+  }
+  f32x16 sa[2], sb[2];
+  scores(sa, k_tile(0));
+  if (needs_mask(0)) mask(sa, key0_of(0));
+  raise_max(tile_max(sa));
+  int it = 0;
+  for (; it + 2 < nt; it += 2) {              // two steps, the score registers swap roles
+    step(it, sa, sb);
+    step(it + 1, sb, sa);
+  }
+  if (it + 1 < nt) {
+    step(it, sa, sb);
+    last(it + 1, sb);
+  } else {
+    last(it, sa);
   }
 
   // Row sums: each half of the lanes summed its own keys.
