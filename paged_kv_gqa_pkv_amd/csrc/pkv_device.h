@@ -61,6 +61,21 @@ __device__ __forceinline__ float shfl_xor(float x, int m) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
+// The values of lanes i % 32 and i % 32 + 32, in every lane i, from one
+// v_permlane32_swap (a VALU op, no LDS round trip): swapping two copies of
+// x exchanges the upper half of one with the lower half of the other.
+// Written as asm: the compiler's builtin returns the first result for both.
+// The s_nop gives the two wait states the swap needs after a VALU write of
+// its operands.
+struct Halves {
+  float lo, hi;
+};
+__device__ __forceinline__ Halves halves32(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return {lo, hi};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Signed byte i of w as a float: one SDWA convert.  Written out because the

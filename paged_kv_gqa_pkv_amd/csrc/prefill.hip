@@ -522,7 +522,8 @@ prefill_kernel(const PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ii = 0; ii < 16; ii += 2) mx = max3(mx, s[kb][ii], s[kb][ii + 1]);
-    return fmaxf(mx, shfl_xor(mx, 32)) * a.scale_log2;
+    const Halves h = halves32(mx);
+    return max3(h.lo, h.hi, h.hi) * a.scale_log2;
   };
   // Raise the running max only when it grows by more than the slack (or on
   // the first visible key); exponents stay <= 2^slack.
@@ -636,7 +637,10 @@ prefill_kernel(const PrefillArgs a) {
   }
 
   // Row sums: each half of the lanes summed its own keys.
-  l += shfl_xor(l, 32);
+  {
+    const Halves h = halves32(l);
+    l = h.lo + h.hi;
+  }
   if (tid == 0) s_bad = 0;
   __syncthreads();
   if (bad) s_bad = 1;
