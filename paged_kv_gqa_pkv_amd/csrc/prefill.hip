@@ -70,7 +70,7 @@ namespace {
 #define PKV_PREFILL_WG_COST_TILES 3   // planner: fixed workgroup cost, in tile-times
 #endif
 #ifndef PKV_PREFILL_MERGE_COST_TILES
-#define PKV_PREFILL_MERGE_COST_TILES 6  // planner: split-merge cost, in tile-times
+#define PKV_PREFILL_MERGE_COST_TILES 3  // planner: split-merge cost, in tile-times
 #endif
 
 constexpr int kWaves = 4;
@@ -699,10 +699,12 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(const PrefillArgs a)
   __shared__ float s_w[kMaxSplits][kMergeRows];
   __shared__ __attribute__((aligned(16))) uint16_t s_o[kMergeRows][kD + 8];
   constexpr int kSlices = kRowsPerWG / kMergeRows;
-  const int slice = blockIdx.x % kSlices;
-  const int group = blockIdx.x / kSlices;
-  const int g = group % a.Hkv;
-  const int rest = group / a.Hkv;
+  // (rest, slice, g) with the KV head fastest, as in the attention grid: the
+  // workgroups of KV head g run on the XCD whose L2 took its partials.
+  const int g = blockIdx.x % a.Hkv;
+  const int slice = (blockIdx.x / a.Hkv) % kSlices;
+  const int rest = blockIdx.x / a.Hkv / kSlices;
+  const int group = rest * a.Hkv + g;
   const int x = rest % a.qtiles;
   const int b = rest / a.qtiles;
   // Every load of the first 8 launched splits' partials and of all (m, l)
