@@ -92,12 +92,10 @@ constexpr int kMaxSplits = 32;                      // key splits per row tile (
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// LDS layout.  bf16 pages: kStages K tiles, then kStages V tiles (the DMA
-// ring).  int8 pages: two dequantised bf16 K tiles and two V tiles (double
-// buffer), then kStages code stages of {K codes, V codes, one 1 KB scale DMA
-// slot per page}.  After the key loop, the split merge reuses the space:
-// the bf16 output tile (128 rows of kD + 8 values, 34 KB) at offset 0 and
-// the split weights (kMaxSplits x 128 floats, 16 KB) right after it.
+// LDS layout.  Two bf16 K tiles, then two bf16 V tiles (bf16 pages: the
+// two-stage K and V rings the DMA fills; int8 pages: the double-buffered
+// dequantised tiles), then for int8 pages kStages code stages of {K codes,
+// V codes, one 1 KB scale DMA slot per page}.
 constexpr int kCodeTileBytes = kTileKeys * kD;                 // 8 KB of codes
 constexpr int kScaleSlotBytes = kWave * 16;                    // one 64-lane DMA
 constexpr int kCodeStageBytes = 2 * kCodeTileBytes + 4 * kScaleSlotBytes;
@@ -106,9 +104,6 @@ struct PrefillLds {
   static constexpr int kVOff = 2 * kTileBytes;
   static constexpr int kCodeOff = 4 * kTileBytes;
   static constexpr int kBytes = kI8 ? kCodeOff + kStages * kCodeStageBytes : 4 * kTileBytes;
-  static constexpr int kObufBytes = kRowsPerWG * (kD + 8) * 2;
-  static constexpr int kFbufOff = (kObufBytes + 1023) / 1024 * 1024;
-  static_assert(kFbufOff + kMaxSplits * kRowsPerWG * 4 <= kBytes, "merge buffers exceed LDS");
   static constexpr int kVmPerTile = kI8 ? 5 : 4;   // DMA instructions per wave and tile (bf16: K or V)
 };
 
@@ -796,7 +791,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Key-split planner.  Row tiles x KV heads x sequences give the "groups";
 // each group's key range is cut into splits of tiles_per_split 64-key tiles.
-// The grid runs in rounds of num_cus * PKV_PREFILL_WG_PER_CU workgroups; for
+// The grid runs in rounds of num_cus * PKV_PREFILL_WG_PER_CU workgroups (1:
+// counting the two bf16 workgroups a CU holds measured slower); for
 // every split count the planner estimates rounds * (tiles per split + a fixed
 // workgroup cost) plus a merge cost when the key range is split, and keeps
 // the cheapest (fewest splits on ties).  Host-known bounds only.
