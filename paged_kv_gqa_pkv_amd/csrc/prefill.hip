@@ -342,18 +342,18 @@ prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // int8: dequantise code stage `stage` into bf16 buffer `buf` (swizzled
-  // rows, as the bf16 DMA writes them).  Thread: rows tid/8 and tid/8 + 32,
-  // 16 codes (dims 16c .. 16c+15, c = tid % 8), K then V.  V rows outside
-  // [key_lo, key_end) get scale 0: they are never visible, and zeros keep
-  // whatever their slots hold out of the PV product.
-  auto dequant = [&](int stage, int buf, int key0, int key_end, int key_lo) {
+  // int8: dequantise the K (which = 0) or V (which = 1) codes of code stage
+  // `stage` into bf16 buffer `buf` of that kind (swizzled rows, as the bf16
+  // DMA writes them).  Thread: rows tid/8 and tid/8 + 32, 16 codes (dims
+  // 16c .. 16c+15, c = tid % 8).  V rows outside [key_lo, key_end) get
+  // scale 0: they are never visible, and zeros keep whatever their slots
+  // hold out of the PV product.
+  auto dequant = [&](int stage, int buf, int which, int key0) {
     const char* cs = smem + Lds::kCodeOff + stage * kCodeStageBytes;
     const int c = tid & 7;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int which = k >> 1;                  // 0: K, 1: V
-      const int r = (tid >> 3) + 32 * (k & 1);   // key row of the tile
+    for (int k = 0; k < 2; ++k) {
+      const int r = (tid >> 3) + 32 * k;         // key row of the tile
       const u32x4 cw = *reinterpret_cast<const u32x4*>(cs + which * kCodeTileBytes + r * kD + c * 16);
       const int slot = r & 15;                   // scales of a page: [slot % 8][slot / 8][K, V]
       float sc = *reinterpret_cast<const float*>(
@@ -444,22 +444,28 @@ prefill_kernel(const PrefillArgs a) {
     return off;
   };
 
-  // int8: make tile j usable (before step j - 1, or before the loop for
-  // j = 0).  Tiles j - 1 and j are in use during step j - 1 and tiles j + 1
-  // .. j + kStages - 2 are loading, so the code stage refilled here is the
-  // one of tile j - 2, which every wave finished with before the barrier;
-  // bf16 buffer j % 2 last held tile j - 2 (read in steps j - 3, j - 2).
-  auto arrive8 = [&](int j) {
-    wait_tiles<Lds::kVmPerTile>(min(kStages - 3, nt - 1 - j));
-    __syncthreads();                            // every wave's page of tile j has landed
-    if (j + kStages - 2 < nt) issue(j + kStages - 2);
-    dequant(j % kStages, j & 1, key0_of(j), key_end, key_lo);
-    __syncthreads();
+  // int8 pages: step i reads the bf16 K(i+1) and V(i) and, between its two
+  // phases, dequantises K(i+2) and V(i+1) into the buffers of K(i) and
+  // V(i-1), which every wave finished with before the step's barrier; the
+  // barrier at the top of step i+1 publishes them.  So the codes of tile j
+  // are read in steps j - 2 (K) and j - 1 (V), and the code ring holds tiles
+  // i+1 .. i + kStages during step i: tile i + kStages is issued at the top
+  // of step i into the stage of tile i.  Called only in steps with a next
+  // tile; in the one before the last, K(i+2) does not exist and the call
+  // turns stale codes into a buffer that is never read again (no branch, so
+  // that the dequantisation stays in one scheduling region with the PV
+  // products).
+  auto dequant_ahead = [&](int i) {
+    dequant((i + 2) % kStages, i & 1, 0, key0_of(i + 2));
+    dequant((i + 1) % kStages, (i + 1) & 1, 1, key0_of(i + 1));
   };
   // Before step i: K(i+1) (if any) and V(i) become readable everywhere.
   auto top = [&](int i) {
     if constexpr (kI8) {
-      if (i + 1 < nt) arrive8(i + 1);
+      // the codes of tile i+2, issued before step i - 1 or in the prologue
+      if (i + 2 < nt) wait_tiles<Lds::kVmPerTile>(min(kStages - 3, nt - 3 - i));
+      __syncthreads();
+      if (i + kStages < nt) issue(i + kStages);
     } else {
       // K(i+1) and V(i), issued before step i - 1, are the only loads in
       // flight; after the barrier every wave is done with step i - 1, so
@@ -589,6 +595,7 @@ prefill_kernel(const PrefillArgs a) {
     asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l));
     if (needs_mask(i + 1)) mask(sn, key0_of(i + 1));
     pv(v_tile(i));
+    if constexpr (kI8) dequant_ahead(i);
     raise_max(tile_max(sn));
   };
   // The last step: no next tile.
@@ -598,13 +605,19 @@ prefill_kernel(const PrefillArgs a) {
     pv(v_tile(i));
   };
 
-  // K(0) first (bf16: with K(1) and V(0) behind it; int8: tiles 0 ..
-  // kStages - 3), then S(0).
+  // K(0) first (bf16: with K(1) and V(0) behind it; int8: the codes of
+  // tiles 0 .. kStages - 1, of which 0 and 1 are dequantised here: K(0),
+  // V(0), K(1)), then S(0).
   if constexpr (kI8) {
 #pragma unroll
-    for (int i = 0; i < kStages - 2; ++i)
+    for (int i = 0; i < kStages; ++i)
       if (i < nt) issue(i);
-    arrive8(0);
+    wait_tiles<Lds::kVmPerTile>(max(0, min(kStages, nt) - 2));
+    __syncthreads();                            // every wave's codes of tiles 0, 1 have landed
+    dequant(0, 0, 0, key0_of(0));
+    dequant(0, 0, 1, key0_of(0));
+    if (nt > 1) dequant(1 % kStages, 1, 0, key0_of(1));
+    __syncthreads();
   } else {
     issue(0, false);
     if (nt > 1) issue(1, false);
