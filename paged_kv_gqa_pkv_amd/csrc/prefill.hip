@@ -133,7 +133,10 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 // Direct global->LDS copy of 16 bytes per lane: lane i writes LDS bytes
 // [lds + 16 i, lds + 16 i + 16).  Issued as inline asm so that the compiler
 // does not wait for it before unrelated LDS reads; completion is awaited
-// explicitly with s_waitcnt vmcnt before the tile is read.
+// explicitly with s_waitcnt vmcnt before the tile is read.  The asm sets m0
+// (the LDS base of the copy) without declaring it: the compiler reserves m0
+// (it refuses it as a clobber) and nothing else in these kernels reads it
+// (LDS instructions on gfx9 and later do not use it).
 __device__ __forceinline__ void dma16(const u32x4* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(lds) : "memory");
