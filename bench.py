@@ -54,8 +54,10 @@ def parse():
                    help="GPU sleep (cycles) queued before each launch timed by events in "
                         "graph mode")
     p.add_argument("--one-stream", action="store_true",
-                   help="run a mixed step's decode after its chunk on one stream (default: "
-                        "on a second stream, concurrent with the chunk)")
+                   help="run everything on one stream: a step's parts one after the other, a "
+                        "mixed step's decode after its chunk (default: each part of a step "
+                        "on its own stream, and a mixed step's decode on a second stream, "
+                        "concurrent with the chunk)")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--kernels", action="store_true",
@@ -312,10 +314,15 @@ def run(args):
     # A mixed step's decode runs on a second stream, concurrent with the
     # chunk (both only read the pools after the append); default priority.
     dstream = torch.cuda.Stream()
+    # The parts of a step (c4: the batch at context 4096 and the batch at
+    # 32768, separate pools) are independent, so each runs on its own stream
+    # (default priority); their workgroups then share the compute units
+    # instead of each launch's last round running part-empty.
+    pstreams = [torch.cuda.Stream() for _ in parts]
     use_events = not args.no_events
     dec_events, pre_events = [], []
 
-    def run_part(k, i, record, only=None):
+    def run_part(k, i, record, only=None, stream=None):
         pt = parts[k]
         plan, qb = pt.plan, pt.bufs
         c = i % pt.copies
@@ -377,8 +384,22 @@ def run(args):
                 ev = torch.cuda.Event(); ev.record(ds); stream.wait_event(ev)
 
     def one_step(i, record, only=None):
-        for k in schedule(i):
-            run_part(k, i, record, only)
+        ks = list(schedule(i))
+        if len(ks) == 1 or args.one_stream or record == "gated" or only is not None:
+            for k in ks:
+                run_part(k, i, record, only, stream)
+            return
+        fork = torch.cuda.Event()
+        fork.record(stream)
+        for j, k in enumerate(ks):
+            ps = stream if j == 0 else pstreams[j]
+            if j:
+                ps.wait_event(fork)
+            run_part(k, i, record, only, ps)
+        for j in range(1, len(ks)):
+            join = torch.cuda.Event()
+            join.record(pstreams[j])
+            stream.wait_event(join)
 
     for i in range(args.warmup):
         one_step(i, False)
@@ -474,8 +495,9 @@ def run(args):
            "kv_pages": ("bf16" if args.kv == "bf16" else
                         "int8 codes + float32 (K, V) scale per slot and KV head"),
            "launch": (("HIP graph per step" if args.graph else "eager") + (
-               ", one stream" if args.one_stream or not any(p.plan.n_prefill and p.plan.n_decode
-                                                             for p in parts)
+               ", one stream" if args.one_stream or (len(parts) == 1 and not any(
+                   p.plan.n_prefill and p.plan.n_decode for p in parts))
+               else ", each part on its own stream" if len(parts) > 1
                else ", decode on a second stream concurrent with the chunk"))}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
