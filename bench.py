@@ -727,6 +727,46 @@ def kernel_bench():
                                      "TFLOPs": round(flops / sec / 1e12, 1),
                                      "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
                                      "work": "the same chunk over int8 pages"}
+    del kc8, vc8, sc8, kp, vp
+    # sliding-window ring paging, a window of 4096 tokens (Module 04 page,
+    # section 4): the batch-64 decode of Qwen3-8B heads at position 32768,
+    # each sequence reading its last 4096 tokens through a 256-page ring
+    # (two pool copies, alternated), and one 512-query chunk at positions
+    # 32768..33279 through the first sequence's ring
+    W, n_r, Br = 4096, 32768, 64
+    rpages = W // 16
+    npool = Br * rpages + 16
+    pools = [(S.randn_bf16((npool, Hkv, 16, D), 440 + c, dev),
+              S.randn_bf16((npool, Hkv, 16, D), 450 + c, dev)) for c in range(2)]
+    btr = (torch.randperm(npool, generator=torch.Generator().manual_seed(9))[:Br * rpages]
+           .view(Br, rpages).to(torch.int32).to(dev))
+    ctxr = torch.full((Br,), n_r, dtype=torch.int32, device=dev)
+    qd = S.randn_bf16((Br, Hq, D), 460, dev)
+    od = torch.empty_like(qd)
+    nwd = bd.pkv_decode_workspace_bytes(Br, Hq, Hkv, D, min(n_r, W))
+    wsd = torch.zeros(max(nwd, 1), dtype=torch.uint8, device=dev) if nwd else None
+    sec = _graph_time(lambda i: bd.pkv_attn_decode_ring(od, qd, pools[i % 2][0], pools[i % 2][1],
+                                                        btr, ctxr, n_r, W, D ** -0.5,
+                                                        workspace=wsd), 2)
+    line("decode_ring_w4096", sec, Br * (W * 2 * Hkv * D * 2 + 2 * Hq * D * 2 + 4 * rpages + 4),
+         f"{Br} sequences at position {n_r}, window {W}: read the window's K/V once, q, "
+         "the ring table and length, write out")
+    T, n_p = 512, n_r + 512
+    qr = S.randn_bf16((T, Hq, D), 470, dev)
+    orr = torch.empty_like(qr)
+    cur = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    ctxp1 = torch.tensor([n_p], dtype=torch.int32, device=dev)
+    nwp = bd.pkv_prefill_workspace_bytes(1, T, Hq, Hkv, D, min(n_p, W + 64))
+    wsp = torch.zeros(max(nwp, 1), dtype=torch.uint8, device=dev) if nwp else None
+    flops = 4 * D * Hq * (T * (W - T) + T * (T + 1) // 2)
+    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk_ring(
+        orr, qr, cur, pools[i % 2][0], pools[i % 2][1], btr[:1], ctxp1, T, n_p, W, D ** -0.5,
+        workspace=wsp), 2)
+    out["prefill_ring_w4096"] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 1),
+                                 "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                 "work": f"one {T}-query chunk at positions {n_r}..{n_p - 1} over a "
+                                         f"ring of {W} tokens, Hq {Hq} Hkv {Hkv}, "
+                                         f"{flops / 1e9:.1f} GFLOP"}
     return {"kernels": out, "note": "GPU time per call from HIP-graph replay of >= 8 calls"}
 
 
