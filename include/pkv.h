@@ -81,7 +81,8 @@ enum {
  * and gets the flat physical slot
  *     slot_mapping[cu_new_lens[b] + j] = block_tables[b][p / 16] * 16 + p % 16.
  * A position that would fall outside the table (p < 0 or p / 16 >=
- * max_blocks_per_seq) yields -1 (skip).
+ * max_blocks_per_seq), or whose table entry is negative or at least 2^27
+ * (its slot would not fit in int32), yields -1 (skip).
  *   slot_mapping  int32 [total_new] (output)
  *   cu_new_lens   int32 [B+1], nondecreasing, cu_new_lens[0] = 0,
  *                 cu_new_lens[B] = total_new
@@ -221,7 +222,8 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
  * bf16(rotate_half(x) * sin[p])), rotate_half(x) = (-x[D/2:], x[:D/2]): the
  * listing's bf16 tensor arithmetic.  The slot is found from block_tables as
  * pkv_slot_mapping finds it and written to slot_mapping[t] (if not NULL; -1
- * when the table has no page there).  A token whose slot is -1 writes no
+ * when the table has no page there, or an entry outside [0, num_blocks) or
+ * at least 2^27).  A token whose slot is -1 writes no
  * K/V; a position outside [0, max_pos) gives NaN q rows and writes no K/V.
  *   q_in, q_out     bf16 [T][Hq][D] (must not overlap)
  *   k_in, v_in      bf16 [T][Hkv][D]

@@ -35,7 +35,9 @@ slot_mapping_kernel(int32_t* __restrict__ slots, const int32_t* __restrict__ blo
   int slot = -1;
   if (p >= 0 && page < max_blocks) {
     int blk = block_tables[(int64_t)b * max_blocks + page];
-    if (blk >= 0) slot = blk * kPage + (p & (kPage - 1));
+    // Slots are int32: an id at or above kMaxSlotBlocks has no slot and is
+    // treated like a missing page.
+    if (blk >= 0 && blk < kMaxSlotBlocks) slot = blk * kPage + (p & (kPage - 1));
   }
   slots[t] = slot;
 }

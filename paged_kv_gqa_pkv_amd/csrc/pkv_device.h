@@ -7,6 +7,9 @@
 namespace pkv {
 
 constexpr int kPage = 16;     // tokens per page
+// Slots are int32 (block id * 16 + offset), so only block ids below 2^27
+// have one.
+constexpr int kMaxSlotBlocks = 1 << 27;
 constexpr int kD = 128;       // head dim
 constexpr int kWave = 64;     // CDNA wavefront
 

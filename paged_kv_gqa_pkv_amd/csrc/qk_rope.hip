@@ -73,7 +73,8 @@ __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeAr
   int64_t slot = -1;
   if (p >= 0 && (p >> 4) < a.max_blocks) {
     const int blk = a.block_tables[(int64_t)b * a.max_blocks + (p >> 4)];
-    if (blk >= 0 && blk < a.num_blocks) slot = (int64_t)blk * kPage + (p & (kPage - 1));
+    if (blk >= 0 && blk < a.num_blocks && blk < kMaxSlotBlocks)
+      slot = (int64_t)blk * kPage + (p & (kPage - 1));
   }
   if (threadIdx.x == 0 && a.slots) a.slots[t] = (int32_t)slot;
   // All 16 lanes of a row share j, so the DPP below only reads lanes of the

@@ -203,6 +203,20 @@ def test_bulk_append_bit_exact():
     assert np.array_equal(pages_order(dk), kc) and np.array_equal(pages_order(dv), vc)
 
 
+def test_slot_mapping_entries_without_a_slot():
+    """Slots are int32: the largest block id with a slot (2^27 - 1) maps to
+    2^31 - 16 + offset; a negative entry, an id of 2^27 or more, or a page
+    past the table gives -1."""
+    big = (1 << 27) - 1
+    bt = torch.tensor([[big, 0], [0, 1 << 27], [0, -1], [0, 0], [0, 0]], dtype=torch.int32)
+    ctx = torch.tensor([1, 17, 18, 5, 40], dtype=torch.int32)
+    cu = torch.arange(6, dtype=torch.int32)
+    sm = torch.full((5,), 7, dtype=torch.int32, device="cuda")
+    bd.pkv_slot_mapping(sm, bt.cuda(), cu.cuda(), ctx.cuda())
+    torch.cuda.synchronize()
+    assert sm.cpu().tolist() == [(1 << 31) - 16, -1, -1, 4, -1]
+
+
 def test_append_skips_negative_slots_and_keeps_bits():
     Hkv, D = 8, 128
     pk = S.randn_bf16((4, Hkv, 16, D), 5)
