@@ -22,7 +22,9 @@
  *   block_tables       int32 [B][max_blocks_per_seq]: logical page i of
  *                      sequence b lives in physical page block_tables[b][i]
  *                      ([P1] SequenceCache.blocks; [P3] page table).  Entries
- *                      past a sequence's last page are never read.
+ *                      past a sequence's last page are never read.  Positions
+ *                      are int32, so max_blocks_per_seq < 2^27 (else
+ *                      PKV_EINVAL).
  *   context_lens       int32 [B]: tokens in each sequence's pages, counting
  *                      the tokens appended in this step (append runs first).
  *

@@ -91,7 +91,7 @@ int validate_tables(const int32_t* block_tables, const int32_t* context_lens, in
     if (n < 0 || n > max_context_len)
       return fail(PKV_EVALIDATE, "context_lens[%d]=%d outside [0, max_context_len=%d]", b, n,
                   max_context_len);
-    if (window == 0 && n > max_blocks * PKV_BLOCK_SIZE)
+    if (window == 0 && (int64_t)n > (int64_t)max_blocks * PKV_BLOCK_SIZE)
       return fail(PKV_EVALIDATE, "context_lens[%d]=%d exceeds the table (%d pages)", b, n,
                   max_blocks);
     const int used = window > 0 && n > window ? window : n;   // a ring uses its first pages
@@ -124,10 +124,19 @@ int validate_slots(const int32_t* slot_mapping, int32_t T, int32_t num_blocks, h
 }
 
 // A ring of `window` tokens: a positive multiple of the page size that fits the table.
+// Positions and slots are int32, so a block table row is at most 2^27 - 1
+// pages wide (its token count, width * 16, then fits in int32).
+int check_table_width(int32_t max_blocks_per_seq) {
+  if (max_blocks_per_seq >= (1 << 27))
+    return fail(PKV_EINVAL, "max_blocks_per_seq=%d: a table row holds at most 2^27 - 1 pages",
+                max_blocks_per_seq);
+  return PKV_OK;
+}
+
 int check_window(int32_t window, int32_t max_blocks_per_seq) {
   if (window <= 0 || window % PKV_BLOCK_SIZE)
     return fail(PKV_EINVAL, "window=%d must be a positive multiple of %d", window, PKV_BLOCK_SIZE);
-  if (window > max_blocks_per_seq * PKV_BLOCK_SIZE)
+  if ((int64_t)window > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
     return fail(PKV_EINVAL, "window=%d exceeds the block table (%d pages)", window,
                 max_blocks_per_seq);
   return PKV_OK;
@@ -144,6 +153,7 @@ int check_decode(void* out, const void* q, const void* k_cache, const void* v_ca
   done = false;
   if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
+  if (check_table_width(max_blocks_per_seq)) return PKV_EINVAL;
   int rc = check_geometry(Hq, Hkv, D, block_size);
   if (rc) return rc;
   if (B == 0) { done = true; return PKV_OK; }
@@ -153,7 +163,7 @@ int check_decode(void* out, const void* q, const void* k_cache, const void* v_ca
   if (window > 0) {
     rc = check_window(window, max_blocks_per_seq);
     if (rc) return rc;
-  } else if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE) {
+  } else if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE) {
     return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
                 max_context_len, max_blocks_per_seq);
   }
@@ -185,6 +195,7 @@ static int slot_mapping_impl(int32_t* slot_mapping, const int32_t* block_tables,
                              int32_t window, void* stream) {
   if (B < 0 || total_new < 0 || max_blocks_per_seq < 0)
     return fail(PKV_EINVAL, "negative size");
+  if (check_table_width(max_blocks_per_seq)) return PKV_EINVAL;
   if (block_size != PKV_BLOCK_SIZE)
     return fail(PKV_EUNSUPPORTED, "block_size %d unsupported (pages hold 16 tokens)", block_size);
   if (total_new == 0) return PKV_OK;
@@ -207,7 +218,7 @@ static int slot_mapping_impl(int32_t* slot_mapping, const int32_t* block_tables,
       if (cu[b + 1] - cu[b] > ctx[b])
         return fail(PKV_EVALIDATE, "sequence %d appends %d tokens but its context is %d", b,
                     cu[b + 1] - cu[b], ctx[b]);
-      if (window == 0 && ctx[b] > max_blocks_per_seq * PKV_BLOCK_SIZE)
+      if (window == 0 && (int64_t)ctx[b] > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
         return fail(PKV_EVALIDATE, "context_lens[%d]=%d exceeds the table", b, ctx[b]);
     }
   }
@@ -322,6 +333,7 @@ int pkv_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in, con
                             void* stream) {
   if (B < 0 || T < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_pos < 0)
     return fail(PKV_EINVAL, "negative size");
+  if (check_table_width(max_blocks_per_seq)) return PKV_EINVAL;
   int rc = check_geometry(Hq, Hkv, D, block_size);
   if (rc) return rc;
   if (T == 0) return PKV_OK;
@@ -447,6 +459,7 @@ static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
   if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
+  if (check_table_width(max_blocks_per_seq)) return PKV_EINVAL;
   int rc = check_geometry(Hq, Hkv, D, block_size);
   if (rc) return rc;
   if (B == 0 || total_q == 0) return PKV_OK;
@@ -459,7 +472,7 @@ static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
     if (rc) return rc;
     if (max_q_len > window)
       return fail(PKV_EINVAL, "max_q_len=%d exceeds the ring of %d tokens", max_q_len, window);
-  } else if (max_context_len > max_blocks_per_seq * PKV_BLOCK_SIZE) {
+  } else if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE) {
     return fail(PKV_EINVAL, "max_context_len=%d exceeds the block table (%d pages)",
                 max_context_len, max_blocks_per_seq);
   }

@@ -64,6 +64,7 @@ def test_slot_mapping_rejects_bad_arguments(lib):
     assert lib.pkv_slot_mapping(NULL, 1, 1, 1, 2, 4, 3, 16, NULL) == bd.PKV_EINVAL
     assert lib.pkv_slot_mapping(1, 1, 1, 1, 0, 4, 3, 16, NULL) == bd.PKV_EINVAL
     assert lib.pkv_slot_mapping(1, 1, 1, 1, -2, 4, 3, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_slot_mapping(1, 1, 1, 1, 2, 1 << 27, 3, 16, NULL) == bd.PKV_EINVAL  # int32 positions
     assert lib.pkv_slot_mapping(NULL, NULL, NULL, NULL, 2, 4, 0, 16, NULL) == bd.PKV_OK
 
 
@@ -81,6 +82,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, out=NULL) == bd.PKV_EINVAL
     assert _decode(lib, out=7, q=7) == bd.PKV_EINVAL                # aliasing
     assert _decode(lib, mcl=65, mb=4) == bd.PKV_EINVAL              # beyond the table
+    assert _decode(lib, mb=1 << 27) == bd.PKV_EINVAL                # wider than int32 positions
     assert _decode(lib, B=-1) == bd.PKV_EINVAL
     assert _decode(lib, Hkv=0) == bd.PKV_EINVAL
     assert _decode(lib, scale=float("nan")) == bd.PKV_EINVAL
@@ -96,6 +98,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(q=NULL) == bd.PKV_EINVAL
     assert call(mq=9) == bd.PKV_EINVAL                               # max_q_len > total_q
     assert call(mcl=100, mb=4) == bd.PKV_EINVAL
+    assert call(mb=1 << 27) == bd.PKV_EINVAL
     assert call(mcl=131073, mb=8193) == bd.PKV_EUNSUPPORTED           # past 32 x 64 x 64 keys
     assert call(total_q=0, out=NULL) == bd.PKV_OK
 
