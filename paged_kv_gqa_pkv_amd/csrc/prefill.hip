@@ -16,9 +16,9 @@
 // (global_load_lds_dwordx4, one page per wave), so no registers hold data in
 // flight: bf16 pages through separate K and V rings of two stages (64 KB,
 // two workgroups per CU), int8 pages through a deeper ring of code stages.
-// LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled by row,
-// which keeps the K reads (b128) and the V transpose reads free of bank
-// conflicts without padding.  When there are too few row tiles to fill the
+// LDS rows are 256 B with their sixteen 16-byte chunks XOR-swizzled by row
+// (one swizzle for K tiles, another for V tiles), which keeps the K reads
+// (b128) and the V transpose reads free of bank conflicts without padding.  When there are too few row tiles to fill the
 // chip, the key range is cut into splits; each split writes its
 // unnormalised (m, l, O) and a small merge kernel that follows combines them
 // in split order.
@@ -125,10 +125,19 @@ struct PrefillArgs {
   float scale_log2;              // |scale| * log2(e), > 0
 };
 
-// Chunk swizzle of an LDS key row: logical 16-byte chunk c of row r sits at
-// position c ^ sw(r).  sw keeps chunk pairs (2m, 2m+1) together and gives
-// rows 0..15 sixteen distinct values.
+// Chunk swizzles of the LDS key rows: logical 16-byte chunk c of row r sits at
+// position c ^ sw(r).  Both keep chunk pairs (2m, 2m+1) together and give
+// rows 0..15 sixteen distinct values, so a 16-lane group of b128 reads (one
+// row each) or of DMA writes (one row) covers all banks.
+//  - K tiles, swz: the b128 K reads take rows 0..15 in one 16-lane group.
+//  - V tiles, swzv: a b64 transpose read serves lanes 0..31 in one cycle and
+//    32..63 in the next, and each half reads 4 rows (r & 3 = 0..3) in one
+//    4-chunk group of dims.  swzv puts r & 3 in chunk bits 2-3, so the 4 rows
+//    land in 4 different groups and each half covers all 256 bytes of banks.
+//    (With swz the halves reached only chunks 0..7 or 8..15: two cycles more
+//    per read, as the LDS bank-conflict counter showed.)
 __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swzv(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Direct global->LDS copy of 16 bytes per lane: lane i writes LDS bytes
 // [lds + 16 i, lds + 16 i + 16).  Issued as inline asm so that the compiler
@@ -334,7 +343,7 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const int r16 = 4 * qd + dma_r16;
-        const int c = (lane & 15) ^ swz(r16);
+        const int c = (lane & 15) ^ (is_v ? swzv(r16) : swz(r16));
         const int64_t idx = ((blk * a.Hkv + g) * kPage + r16) * 16 + c;
         const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
         if (is_v)
@@ -372,17 +381,18 @@ prefill_kernel(const PrefillArgs a) {
                                                             (__bf16)(sbyte3(cw[j]) * sc)});
       }
       char* dst = smem + which * Lds::kVOff + buf * kTileBytes + r * kRowBytes;
-      *reinterpret_cast<u32x4*>(dst + (((2 * c) ^ swz(r)) << 4)) = u32x4{o8[0], o8[1], o8[2], o8[3]};
-      *reinterpret_cast<u32x4*>(dst + (((2 * c + 1) ^ swz(r)) << 4)) =
+      const int sw = which ? swzv(r) : swz(r);
+      *reinterpret_cast<u32x4*>(dst + (((2 * c) ^ sw) << 4)) = u32x4{o8[0], o8[1], o8[2], o8[3]};
+      *reinterpret_cast<u32x4*>(dst + (((2 * c + 1) ^ sw) << 4)) =
           u32x4{o8[4], o8[5], o8[6], o8[7]};
     }
   };
 
   // Lane read offsets.  K (A operand of S^T): row r = lane%32 (+32 per key
   // block), logical chunk 2kk + half, i.e. byte r*256 + ((2kk + half) ^
-  // sw(r))*16 = kbase ^ 32kk.  V (transpose reads): row r = 8p + 4half + m/4
+  // swz(r))*16 = kbase ^ 32kk.  V (transpose reads): row r = 8p + 4half + m/4
   // (+32kb + 16hh), dims 32db + 16*(lane/16 % 2) + 4*(m%4), i.e. logical
-  // chunk c = 4db + 2*(lane/16 % 2) + (m%4)/2 at byte r*256 + (c ^ sw(r))*16
+  // chunk c = 4db + 2*(lane/16 % 2) + (m%4)/2 at byte r*256 + (c ^ swzv(r))*16
   // + 8*(m%2) = vbase[p] ^ 64db.  (The XOR terms sit in bits 4-7, clear of
   // the row and stage bits, so a stage offset can be added first.)  One
   // register per base instead of one per offset keeps the kernel within the
@@ -394,7 +404,7 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int r = 8 * p + 4 * half + k4;
-      vbase[p] = r * kRowBytes + (((2 * dh + (j >> 1)) ^ swz(r)) << 4) + (j & 1) * 8;
+      vbase[p] = r * kRowBytes + (((2 * dh + (j >> 1)) ^ swzv(r)) << 4) + (j & 1) * 8;
     }
   }
 
