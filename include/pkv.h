@@ -169,6 +169,33 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_context_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the per-GPU array of pkv_attn_decode_noalloc and of its counter
+ * region (16 MiB, 64 KiB). */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define PKV_NOALLOC_COUNTER_BYTES (64u << 10)
+
+/*
+ * Decode attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and error behaviour as
+ * pkv_attn_decode minus the workspace: the split path keeps its partials
+ * and arrival counters in one array the library holds on each GPU (its
+ * first call on a device resolves that array and clears its counters with a
+ * small kernel on `stream`; the array lives until the process ends).  The
+ * call allocates nothing.  Shapes whose split plan needs more than
+ * PKV_NOALLOC_SCRATCH_BYTES - PKV_NOALLOC_COUNTER_BYTES bytes of partials,
+ * or more than PKV_NOALLOC_COUNTER_BYTES / 4 (sequence, KV head) pairs,
+ * return PKV_EWORKSPACE before anything is enqueued (pkv_attn_decode with a
+ * workspace covers them).  All calls on one GPU share the array: calls that
+ * may overlap in time on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.
+ */
+int pkv_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, float scale, void* stream);
+
 /*
  * Workspace for pkv_attn_prefill_chunk: bytes of device memory the call needs
  * for this shape (0 when it runs without key splits).  Depends on the current

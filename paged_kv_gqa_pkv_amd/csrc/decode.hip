@@ -27,8 +27,13 @@
 // (m, l, acc) to the workspace, and the last split of a (sequence, KV head)
 // to finish merges them all in split order, so results are run-to-run
 // bit-identical and the whole call is one kernel.
+#include "pkv.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
+
+#include <mutex>
+#include <type_traits>
+#include <vector>
 
 namespace pkv {
 
@@ -583,11 +588,26 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Where the split path keeps its partials and arrival counters.
+struct SplitBuffers {
+  float* ml;
+  float* acc;
+  int* counters;
+};
+
+// A caller workspace of plan.ws_bytes: (m, l), then acc, then the counters.
+SplitBuffers workspace_buffers(const DecodePlan& plan, void* workspace) {
+  char* ws = static_cast<char*>(workspace);
+  if (plan.splits <= 1 || !ws) return {nullptr, nullptr, nullptr};
+  return {reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + plan.ws_ml_bytes),
+          reinterpret_cast<int*>(ws + plan.ws_ml_bytes + plan.ws_acc_bytes)};
+}
+
 DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const float* kv_scales,
                      const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
                      int Hkv, int num_blocks, int max_blocks, float scale,
-                     const DecodePlan& plan, void* workspace, int window) {
+                     const DecodePlan& plan, const SplitBuffers& wsb, int window) {
   DecodeArgs a;
   a.out = static_cast<uint16_t*>(out);
   a.q = static_cast<const u32x4*>(q);
@@ -596,17 +616,75 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
   a.kv_scales = kv_scales;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
-  char* ws = static_cast<char*>(workspace);
   const bool split = plan.splits > 1;
-  a.ws_ml = split ? reinterpret_cast<float*>(ws) : nullptr;
-  a.ws_acc = split ? reinterpret_cast<float*>(ws + plan.ws_ml_bytes) : nullptr;
-  a.counters = split ? reinterpret_cast<int*>(ws + plan.ws_ml_bytes + plan.ws_acc_bytes)
-                     : nullptr;
+  a.ws_ml = split ? wsb.ml : nullptr;
+  a.ws_acc = split ? wsb.acc : nullptr;
+  a.counters = split ? wsb.counters : nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
   a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
   a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;
+}
+
+// Instantiations by group size G = Hq / Hkv (pages per pipeline stage U by
+// the register budget of each).
+template <class P>
+hipError_t launch_by_group(const DecodeArgs& a, int G, hipStream_t stream) {
+  constexpr bool kI8 = std::is_same<P, Int8Page>::value;
+  switch (G) {
+    case 1: return launch_g<P, 1, kI8 ? PKV_DECODE_I8_U_G1 : PKV_DECODE_U_G1>(a, stream);
+    case 2: return launch_g<P, 2, kI8 ? PKV_DECODE_I8_U_G2 : PKV_DECODE_U_G2>(a, stream);
+    case 4: return launch_g<P, 4, kI8 ? PKV_DECODE_I8_U_G4 : PKV_DECODE_U_G4>(a, stream);
+    case 8: return launch_g<P, 8, kI8 ? PKV_DECODE_I8_U_G8 : PKV_DECODE_U_G8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Library-owned split buffers for callers that cannot allocate
+// (launch_decode_noalloc).  One array per device, held until the process
+// ends: the arrival counters first (a fixed region, so that every call finds
+// them at the same place and at zero: each call leaves the counters it used
+// at zero, and the region is cleared once per device before the first use),
+// then the (m, l) and acc partials of the call in flight, which need no
+// initialisation.  Host code never passes `scratch` itself to a kernel (its
+// name is a host-side stand-in there): it uses the device address obtained
+// from hipGetSymbolAddress, kept per device.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+constexpr size_t kScratchCounterBytes = PKV_NOALLOC_COUNTER_BYTES;
+static_assert(kScratchCounterBytes % 256 == 0 && kScratchCounterBytes < PKV_NOALLOC_SCRATCH_BYTES,
+              "counter region inside the scratch array");
+
+__global__ void __launch_bounds__(256) zero_words_kernel(int* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Device address of `scratch` on the current device; on the first call for a
+// device the symbol is resolved (with that device current) and its counter
+// region cleared by a fill kernel on `stream` (a kernel, not a memset, so
+// that the clear is also valid inside a captured graph).
+hipError_t scratch_address(char** out, hipStream_t stream) {
+  static std::mutex mu;
+  static std::vector<char*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    const int words = (int)(kScratchCounterBytes / sizeof(int));
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<int*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<char*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -661,16 +739,34 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          int Hkv, int num_blocks, int max_blocks, float scale, int window,
                          const DecodePlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables,
-                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
-                                 workspace, window);
-  switch (Hq / Hkv) {
-    case 1: return launch_g<Bf16Page, 1, PKV_DECODE_U_G1>(a, stream);
-    case 2: return launch_g<Bf16Page, 2, PKV_DECODE_U_G2>(a, stream);
-    case 4: return launch_g<Bf16Page, 4, PKV_DECODE_U_G4>(a, stream);
-    case 8: return launch_g<Bf16Page, 8, PKV_DECODE_U_G8>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables, ctx_lens, B,
+                                 Hq, Hkv, num_blocks, max_blocks, scale, plan,
+                                 workspace_buffers(plan, workspace), window);
+  return launch_by_group<Bf16Page>(a, Hq / Hkv, stream);
+}
+
+bool noalloc_fits(const DecodePlan& plan, int B, int Hkv) {
+  if (plan.splits <= 1) return true;
+  return (size_t)B * Hkv * sizeof(int) <= kScratchCounterBytes &&
+         plan.ws_ml_bytes + plan.ws_acc_bytes <= PKV_NOALLOC_SCRATCH_BYTES - kScratchCounterBytes;
+}
+
+hipError_t launch_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
+                                 int max_blocks, float scale, const DecodePlan& plan,
+                                 hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  if (!noalloc_fits(plan, B, Hkv)) return hipErrorInvalidValue;
+  char* base = nullptr;
+  const hipError_t e = scratch_address(&base, stream);
+  if (e != hipSuccess) return e;
+  const SplitBuffers wsb{reinterpret_cast<float*>(base + kScratchCounterBytes),
+                         reinterpret_cast<float*>(base + kScratchCounterBytes + plan.ws_ml_bytes),
+                         reinterpret_cast<int*>(base)};
+  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables, ctx_lens, B,
+                                 Hq, Hkv, num_blocks, max_blocks, scale, plan, wsb, 0);
+  return launch_by_group<Bf16Page>(a, Hq / Hkv, stream);
 }
 
 hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
@@ -679,16 +775,10 @@ hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, con
                               int max_blocks, float scale, const DecodePlan& plan,
                               void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  const DecodeArgs a = make_args(out, q, k_codes, v_codes, kv_scales, block_tables,
-                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
-                                 workspace, 0);
-  switch (Hq / Hkv) {
-    case 1: return launch_g<Int8Page, 1, PKV_DECODE_I8_U_G1>(a, stream);
-    case 2: return launch_g<Int8Page, 2, PKV_DECODE_I8_U_G2>(a, stream);
-    case 4: return launch_g<Int8Page, 4, PKV_DECODE_I8_U_G4>(a, stream);
-    case 8: return launch_g<Int8Page, 8, PKV_DECODE_I8_U_G8>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  const DecodeArgs a = make_args(out, q, k_codes, v_codes, kv_scales, block_tables, ctx_lens, B,
+                                 Hq, Hkv, num_blocks, max_blocks, scale, plan,
+                                 workspace_buffers(plan, workspace), 0);
+  return launch_by_group<Int8Page>(a, Hq / Hkv, stream);
 }
 
 }  // namespace pkv

@@ -143,13 +143,14 @@ int check_window(int32_t window, int32_t max_blocks_per_seq) {
 }
 
 // Host checks shared by the decode entry points; fills the split plan.
-// done = true: nothing to launch (B == 0).
+// done = true: nothing to launch (B == 0).  own_buffers: the split buffers
+// are the library's array (checked by the caller), not `workspace`.
 int check_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t Hq,
                  int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                  void* workspace, size_t workspace_bytes, void* stream, pkv::DecodePlan& plan,
-                 bool& done, int32_t window = 0) {
+                 bool& done, int32_t window = 0, bool own_buffers = false) {
   done = false;
   if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
@@ -170,9 +171,16 @@ int check_decode(void* out, const void* q, const void* k_cache, const void* v_ca
   if (!(scale == scale)) return fail(PKV_EINVAL, "scale is NaN");
   const int32_t plan_ctx = window > 0 && max_context_len > window ? window : max_context_len;
   plan = pkv::plan_decode(B, Hq, Hkv, plan_ctx, device_cus());
-  if (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace))
+  if (!own_buffers && (plan.ws_bytes > workspace_bytes || (plan.ws_bytes && !workspace)))
     return fail(PKV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.ws_bytes,
                 workspace_bytes);
+  if (own_buffers && !pkv::noalloc_fits(plan, B, Hkv))
+    return fail(PKV_EWORKSPACE,
+                "decode of this shape needs %zu bytes of split buffers (%d counters); the "
+                "library's array holds %d bytes (%d counters): use pkv_attn_decode with a "
+                "workspace",
+                plan.ws_bytes, B * Hkv, (int)PKV_NOALLOC_SCRATCH_BYTES,
+                (int)(PKV_NOALLOC_COUNTER_BYTES / sizeof(int)));
   if (validate_mode()) {
     rc = validate_tables(block_tables, context_lens, B, max_blocks_per_seq, num_blocks,
                          max_context_len, static_cast<hipStream_t>(stream), window);
@@ -399,6 +407,24 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                                           Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0, plan,
                                           workspace, static_cast<hipStream_t>(stream)),
                        "pkv_attn_decode");
+}
+
+int pkv_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, float scale, void* stream) {
+  pkv::DecodePlan plan;
+  bool done = false;
+  const int rc = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv,
+                              D, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                              scale, nullptr, 0, stream, plan, done, 0, true);
+  if (rc || done) return rc;
+  return launch_status(pkv::launch_decode_noalloc(out, q, k_cache, v_cache, block_tables,
+                                                  context_lens, B, Hq, Hkv, num_blocks,
+                                                  max_blocks_per_seq, scale, plan,
+                                                  static_cast<hipStream_t>(stream)),
+                       "pkv_attn_decode_noalloc");
 }
 
 int pkv_attn_decode_ring(void* out, const void* q, const void* k_cache, const void* v_cache,

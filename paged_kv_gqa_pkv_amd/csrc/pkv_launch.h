@@ -53,6 +53,15 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          int Hkv, int num_blocks, int max_blocks, float scale, int window,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
 
+// Decode with the split buffers in the library's own per-device array
+// (no caller workspace).  noalloc_fits tells whether a plan fits that array.
+bool noalloc_fits(const DecodePlan& plan, int B, int Hkv);
+hipError_t launch_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
+                                 int max_blocks, float scale, const DecodePlan& plan,
+                                 hipStream_t stream);
+
 // Decode over int8 pages (codes in the bf16 page order; float32 scales
 // [num_blocks][Hkv][8][2][2], the (K, V) scales of slot s at [s % 8][s / 8]);
 // same plan and workspace as launch_decode.

@@ -176,3 +176,20 @@ def test_ring_entry_points_reject_bad_windows(lib):
     assert lib.pkv_attn_prefill_chunk_ring(1, 2, 3, 4, 5, 6, 7, 1, 100, 100, 16, 8, 128, 16, 64,
                                            8, 1000, 64, 0.088, NULL, 0, NULL) == bd.PKV_EINVAL
     assert b"ring" in lib.pkv_last_error()
+
+
+def test_noalloc_decode_rejects_shapes_beyond_its_array(lib):
+    """pkv_attn_decode_noalloc refuses, on the host, a split plan whose
+    partials do not fit the library's array (here 64 sequences x 64 heads at
+    131072 tokens: about 65 MiB of partials), and checks arguments like
+    pkv_attn_decode."""
+    def call(B=64, Hq=64, Hkv=8, mb=8192, mcl=131072, out=1, q=2):
+        return lib.pkv_attn_decode_noalloc(out, q, 3, 4, 5, 6, B, Hq, Hkv, 128, 16, 1 << 20, mb,
+                                           mcl, 0.088, NULL)
+    assert bd.pkv_decode_workspace_bytes(64, 64, 8, 128, 131072) > 16 << 20
+    assert call() == bd.PKV_EWORKSPACE
+    assert b"pkv_attn_decode with a workspace" in lib.pkv_last_error()
+    assert call(Hq=24) == bd.PKV_EUNSUPPORTED
+    assert call(out=7, q=7) == bd.PKV_EINVAL
+    assert call(mcl=131073) == bd.PKV_EINVAL                        # beyond the table
+    assert call(B=0, out=NULL) == bd.PKV_OK

@@ -1,0 +1,101 @@
+"""pkv_attn_decode_noalloc, the decode entry point that allocates nothing (its
+split buffers live in the library's own per-GPU array), against
+pkv_attn_decode with a caller workspace: bit-identical outputs on calls in a
+row of different sizes (the second smaller than the first), and both within
+the tolerance of the fp64 oracle.  Called through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_oracle as O
+from paged_kv_gqa_pkv_amd import binding as bd
+from paged_kv_gqa_pkv_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def pages_order(pool: torch.Tensor) -> np.ndarray:
+    """Head-major device pool -> the bits of the pages' token-major order."""
+    return u16(pool.transpose(1, 2))
+
+
+def from_pages_order(bits: np.ndarray) -> torch.Tensor:
+    """The oracle's token-major pool bits -> a head-major device pool."""
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    return t.transpose(1, 2).contiguous().cuda()
+
+
+def _case(name, ctxs, Hq, Hkv, num_blocks, seed):
+    """Pools after the step's append (done by the oracle), q, tables."""
+    w = S.custom_workload(name, [S.SeqSpec(c - 1, 1, False) for c in ctxs], Hq=Hq, Hkv=Hkv,
+                          D=128, num_blocks=num_blocks, base_seed=seed)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0)
+    bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
+    slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
+    kc, vc = O.append_ref(pages_order(d.k_cache), pages_order(d.v_cache), u16(d.k_new),
+                          u16(d.v_new), slots)
+    want = O.decode_ref(u16(d.q_decode), kc, vc, bt, ctx, O.default_scale(128))
+    return dict(q=d.q_decode.cuda(), k=from_pages_order(kc), v=from_pages_order(vc),
+                bt=t.block_tables.cuda(), ctx=t.context_lens.cuda(), max_ctx=max(ctxs),
+                want=want, B=len(ctxs), Hq=Hq, Hkv=Hkv)
+
+
+def _run_both(c):
+    scale = 128 ** -0.5
+    nbytes = bd.pkv_decode_workspace_bytes(c["B"], c["Hq"], c["Hkv"], 128, c["max_ctx"])
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    ref = torch.empty_like(c["q"])
+    bd.pkv_attn_decode(ref, c["q"], c["k"], c["v"], c["bt"], c["ctx"], c["max_ctx"], scale,
+                       workspace=ws)
+    got = torch.full_like(c["q"], float("nan"))
+    bd.pkv_attn_decode_noalloc(got, c["q"], c["k"], c["v"], c["bt"], c["ctx"], c["max_ctx"],
+                               scale)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def _check(c, ref, got, what):
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), \
+        f"{what}: no-alloc output differs from the workspace call"
+    g = O.bf16_to_f64(u16(got))
+    assert np.all(np.isfinite(g)), what
+    err = np.abs(g - c["want"])
+    print(f"{what}: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, what
+
+
+def test_noalloc_decode_matches_workspace_decode_on_consecutive_calls():
+    big = _case("noalloc_big", [5000, 4100, 777, 3000, 1, 4500], Hq=32, Hkv=8,
+                num_blocks=1400, seed=91)
+    small = _case("noalloc_small", [2500, 40, 1800], Hq=16, Hkv=8, num_blocks=320, seed=92)
+    assert bd.pkv_decode_num_splits(6, 32, 8, 128, 5000) > 1
+    assert bd.pkv_decode_num_splits(3, 16, 8, 128, 2500) > 1
+    print("[noalloc] call 1: 6 sequences, Hq 32, up to 5000 tokens", flush=True)
+    ref1, got1 = _run_both(big)
+    _check(big, ref1, got1, "noalloc call 1")
+    print("[noalloc] call 2: 3 sequences, Hq 16, up to 2500 tokens", flush=True)
+    ref2, got2 = _run_both(small)
+    _check(small, ref2, got2, "noalloc call 2 (smaller)")
+    # the counters the first call used are back at zero: the same call again
+    # is bit-identical
+    print("[noalloc] call 3: call 1 again", flush=True)
+    _, got3 = _run_both(big)
+    assert torch.equal(got3.view(torch.int16), got1.view(torch.int16))
+
+
+def test_noalloc_decode_single_pass_shape():
+    c = _case("noalloc_single", [64, 200, 17, 300] * 40, Hq=16, Hkv=8, num_blocks=2000,
+              seed=93)
+    assert bd.pkv_decode_num_splits(160, 16, 8, 128, 300) == 1
+    print("[noalloc] single pass: 160 sequences", flush=True)
+    ref, got = _run_both(c)
+    _check(c, ref, got, "noalloc single pass")
