@@ -208,11 +208,18 @@ __device__ __forceinline__ TileKeys tile_keys(const PrefillArgs& a, int b, int x
   // p % window, i.e. in the table's page (p / 16) % (window / 16); the ring
   // holds positions n - window .. n - 1, so keys below key_lo are gone.
   const bool ring = a.window > 0;
-  k.bad_len = k.T > k.n || (ring ? k.T > a.window : k.n > a.max_blocks * kPage);
+  bool bad = k.T > k.n || (ring ? k.T > a.window : k.n > a.max_blocks * kPage);
+  // A context with more key tiles than the launch covers (a length past the
+  // host's max_context_len) poisons the sequence's rows, as in decode, rather
+  // than dropping the keys no split reaches.
+  const int seq_key_lo = ring ? max(0, k.n - a.window) : 0;
+  const int seq_tiles = (k.n + kTileKeys - 1) / kTileKeys - seq_key_lo / kTileKeys;
+  bad = bad || seq_tiles > a.splits * a.tiles_per_split;
+  k.bad_len = bad;
   // Keys: 0 .. the last position of the tile's rows (from key_lo in a ring).
   const int t_last = min(k.T - 1, (R0 + kRowsPerWG - 1) / a.G);
-  k.key_end = k.bad_len ? 0 : k.n - k.T + t_last + 1;
-  k.key_lo = ring && !k.bad_len ? max(0, k.n - a.window) : 0;
+  k.key_end = bad ? 0 : k.n - k.T + t_last + 1;
+  k.key_lo = bad ? 0 : seq_key_lo;
   k.tile_first = k.key_lo / kTileKeys;
   const int tile_end = (k.key_end + kTileKeys - 1) / kTileKeys;
   k.n_tiles = max(0, tile_end - k.tile_first);
@@ -760,9 +767,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(const PrefillArgs a)
   const int G = a.G;
   const int rs0 = x * kRowsPerWG + slice * kMergeRows;      // first row of the slice
   if (tk.skip || tk.ns == 0 || rs0 >= tk.T * G) return;     // ns 0: NaN rows written already
-  // A context longer than the plan's bound has more non-empty splits than
-  // were launched; only the launched ones hold partials.
-  const int ns = min(tk.ns, a.splits);
+  const int ns = tk.ns;                                      // <= a.splits (longer: bad_len)
   if (tid < kMergeRows) {
     float M = kNegInf;
 #pragma unroll

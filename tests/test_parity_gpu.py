@@ -275,6 +275,36 @@ def test_invalid_indices_poison_outputs_without_faulting():
     assert torch.isnan(out[1].float()).all() and torch.isfinite(out[0].float()).all()
 
 
+def test_prefill_context_past_the_plan_poisons_that_sequence():
+    """A sequence whose context holds more key tiles than the launch was
+    planned for (max_context_len below its real length) gets NaN rows, as
+    decode does, instead of silently dropping the keys no split reaches; the
+    other sequence of the call is unaffected."""
+    seqs = [S.SeqSpec(136, 64, True), S.SeqSpec(2936, 64, True)]
+    w = S.custom_workload("past_plan", seqs, Hq=16, Hkv=8, D=128, num_blocks=210, base_seed=83)
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0)
+    bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
+    slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
+    kc, vc = O.append_ref(pages_order(d.k_cache), pages_order(d.v_cache), u16(d.k_new),
+                          u16(d.v_new), slots)
+    want0 = O.prefill_ref(u16(d.q_prefill[:64]), [0, 64], kc, vc, bt[:1], ctx[:1],
+                          O.default_scale(128))
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16).copy()).view(
+        torch.bfloat16).transpose(1, 2).contiguous().cuda()
+    q = d.q_prefill.cuda()
+    out = torch.zeros_like(q)
+    cu = torch.tensor([0, 64, 128], dtype=torch.int32, device="cuda")
+    nbytes = bd.pkv_prefill_workspace_bytes(2, 64, 16, 8, 128, 200)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda") if nbytes else None
+    bd.pkv_attn_prefill_chunk(out, q, cu, to_dev(kc), to_dev(vc), t.block_tables.cuda(),
+                              t.context_lens.cuda(), 64, 200, O.default_scale(128),
+                              workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[64:].float()).all(), "rows past the plan must be NaN"
+    assert_close(out[:64], want0, "prefill sequence inside the plan")
+
+
 def test_workspace_too_small_is_rejected():
     w = S.workload("c2")
     need = bd.pkv_decode_workspace_bytes(8, 16, 8, 128, 1024)
