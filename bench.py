@@ -333,7 +333,7 @@ def run(args):
             d = pt.layers[c * n_layers + l]
             if only is None and pt.kv == "int8":
                 bd.pkv_append_int8(qb["kn"], qb["vn"], plan.slot_mapping, d.k_codes, d.v_codes,
-                                   d.kv_scales, stream=stream)
+                                   d.k_scales, d.v_scales, stream=stream)
             elif only is None:
                 bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
                               stream=stream)
@@ -344,7 +344,8 @@ def run(args):
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
                 if pt.kv == "int8":
                     bd.pkv_attn_prefill_chunk_int8(qb["op"], qb["qp"], plan.cu_q, d.k_codes,
-                                                   d.v_codes, d.kv_scales, plan.bt_prefill,
+                                                   d.v_codes, d.k_scales, d.v_scales,
+                                                   plan.bt_prefill,
                                                    plan.ctx_prefill, plan.max_q_len,
                                                    plan.max_ctx_prefill, plan.scale,
                                                    workspace=plan.prefill_workspace,
@@ -370,7 +371,8 @@ def run(args):
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(ds)
                 if pt.kv == "int8":
                     bd.pkv_attn_decode_int8(qb["od"], qb["qd"], d.k_codes, d.v_codes,
-                                            d.kv_scales, plan.bt_decode, plan.ctx_decode,
+                                            d.k_scales, d.v_scales, plan.bt_decode,
+                                            plan.ctx_decode,
                                             plan.max_ctx_decode, plan.scale,
                                             workspace=plan.workspace, stream=ds)
                 else:
@@ -530,17 +532,13 @@ def cpu_baseline(args, parts):
     budget = args.cpu_seconds / len(parts[:2])
     for pt in parts[:2]:
         w, t = pt.w, pt.t
-        # the oracle reads pools in the pages' token-major order (axis permutations)
         if pt.kv == "int8":
             d = S.make_layer_int8(w, t, 0)
-            kc0 = d.k_codes.transpose(1, 2).contiguous().numpy()
-            vc0 = d.v_codes.transpose(1, 2).contiguous().numpy()
-            per_slot = d.kv_scales.permute(0, 3, 2, 1, 4).reshape(w.num_blocks, 16, w.Hkv, 2)
-            ks0, vs0 = per_slot[..., 0].contiguous().numpy(), per_slot[..., 1].contiguous().numpy()
+            kc0, vc0 = d.k_codes.numpy(), d.v_codes.numpy()
+            ks0, vs0 = d.k_scales.numpy(), d.v_scales.numpy()
         else:
             d = S.make_layer(w, t, 0)
-            kc0 = u16(d.k_cache.transpose(1, 2).contiguous())
-            vc0 = u16(d.v_cache.transpose(1, 2).contiguous())
+            kc0, vc0 = u16(d.k_cache), u16(d.v_cache)
         kn, vn = u16(d.k_new), u16(d.v_new)
         qd = u16(d.q_decode) if d.q_decode is not None else None
         qp = u16(d.q_prefill) if d.q_prefill is not None else None
@@ -638,9 +636,10 @@ def kernel_bench():
                                                sets[i % copies][4]), copies)
     line("append_bf16", sec, n_tok * (2 * 2 * Hkv * D * 2 + 4),
          f"{n_tok} tokens: read K/V rows and slot, write K/V rows")
-    i8 = [(torch.zeros((nb, Hkv, 16, D), dtype=torch.int8, device=dev),
-           torch.zeros((nb, Hkv, 16, D), dtype=torch.int8, device=dev),
-           torch.zeros((nb, Hkv, 8, 2, 2), dtype=torch.float32, device=dev)) for _ in range(copies)]
+    i8 = [(torch.zeros((nb, 16, Hkv, D), dtype=torch.int8, device=dev),
+           torch.zeros((nb, 16, Hkv, D), dtype=torch.int8, device=dev),
+           torch.zeros((nb, 16, Hkv), dtype=torch.float32, device=dev),
+           torch.zeros((nb, 16, Hkv), dtype=torch.float32, device=dev)) for _ in range(copies)]
     sec = _graph_time(lambda i: bd.pkv_append_int8(sets[i % copies][1], sets[i % copies][2],
                                                     sets[i % copies][0], *i8[i % copies]), copies)
     line("append_int8", sec, n_tok * (2 * Hkv * D * 2 + 2 * Hkv * (D + 4) + 4),
@@ -648,7 +647,7 @@ def kernel_bench():
     del sets, i8
     # block copy: 1024 (src, dst) pairs in all 36 layers of a layered K and V pool
     L, nbc, pairs = 36, 4096, 1024
-    kp = torch.empty((L, nbc, Hkv, 16, D), dtype=torch.bfloat16, device=dev)
+    kp = torch.empty((L, nbc, 16, Hkv, D), dtype=torch.bfloat16, device=dev)
     vp = torch.empty_like(kp)
     perm = torch.randperm(nbc, generator=torch.Generator().manual_seed(5))
     srcs = [perm[:pairs].to(torch.int32).to(dev), perm[pairs:2 * pairs].to(torch.int32).to(dev)]
@@ -673,8 +672,8 @@ def kernel_bench():
         fz.append(dict(q=S.randn_bf16((B, Hq, D), 400 + c, dev), k=S.randn_bf16((B, Hkv, D), 410 + c, dev),
                        v=S.randn_bf16((B, Hkv, D), 420 + c, dev),
                        qo=torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev),
-                       kc=torch.empty((nbf, Hkv, 16, D), dtype=torch.bfloat16, device=dev),
-                       vc=torch.empty((nbf, Hkv, 16, D), dtype=torch.bfloat16, device=dev)))
+                       kc=torch.empty((nbf, 16, Hkv, D), dtype=torch.bfloat16, device=dev),
+                       vc=torch.empty((nbf, 16, Hkv, D), dtype=torch.bfloat16, device=dev)))
     w = torch.ones(D, dtype=torch.bfloat16, device=dev)
     sm = torch.empty(B, dtype=torch.int32, device=dev)
     sec = _graph_time(lambda i: bd.pkv_qk_norm_rope_append(
@@ -706,8 +705,8 @@ def kernel_bench():
     cuq = torch.tensor([0, T], dtype=torch.int32, device=dev)
     qp = S.randn_bf16((T, Hq, D), 430, dev)
     op = torch.empty_like(qp)
-    kp = S.randn_bf16((nbp, Hkv, 16, D), 431, dev)
-    vp = S.randn_bf16((nbp, Hkv, 16, D), 432, dev)
+    kp = S.randn_bf16((nbp, 16, Hkv, D), 431, dev)
+    vp = S.randn_bf16((nbp, 16, Hkv, D), 432, dev)
     nws = bd.pkv_prefill_workspace_bytes(1, T, Hq, Hkv, D, n)
     ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
     flops = 4 * D * Hq * (T * o + T * (T + 1) // 2)
@@ -717,17 +716,18 @@ def kernel_bench():
                                 "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
                                 "work": f"one {T}-query causal chunk at positions {o}..{n - 1}, "
                                         f"Hq {Hq} Hkv {Hkv}, {flops / 1e9:.1f} GFLOP"}
-    kc8 = torch.randint(-127, 128, (nbp, Hkv, 16, D), dtype=torch.int8, device=dev)
-    vc8 = torch.randint(-127, 128, (nbp, Hkv, 16, D), dtype=torch.int8, device=dev)
-    sc8 = torch.full((nbp, Hkv, 8, 2, 2), 0.024, dtype=torch.float32, device=dev)
-    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk_int8(op, qp, cuq, kc8, vc8, sc8, btp,
-                                                               ctxp, T, n, D ** -0.5,
+    kc8 = torch.randint(-127, 128, (nbp, 16, Hkv, D), dtype=torch.int8, device=dev)
+    vc8 = torch.randint(-127, 128, (nbp, 16, Hkv, D), dtype=torch.int8, device=dev)
+    ks8 = torch.full((nbp, 16, Hkv), 0.024, dtype=torch.float32, device=dev)
+    vs8 = ks8.clone()
+    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk_int8(op, qp, cuq, kc8, vc8, ks8, vs8,
+                                                               btp, ctxp, T, n, D ** -0.5,
                                                                workspace=ws), 1)
     out["prefill_int8_2048x8192"] = {"us": round(sec * 1e6, 2),
                                      "TFLOPs": round(flops / sec / 1e12, 1),
                                      "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
                                      "work": "the same chunk over int8 pages"}
-    del kc8, vc8, sc8, kp, vp
+    del kc8, vc8, ks8, vs8, kp, vp
     # sliding-window ring paging, a window of 4096 tokens (Module 04 page,
     # section 4): the batch-64 decode of Qwen3-8B heads at position 32768,
     # each sequence reading its last 4096 tokens through a 256-page ring
@@ -736,8 +736,8 @@ def kernel_bench():
     W, n_r, Br = 4096, 32768, 64
     rpages = W // 16
     npool = Br * rpages + 16
-    pools = [(S.randn_bf16((npool, Hkv, 16, D), 440 + c, dev),
-              S.randn_bf16((npool, Hkv, 16, D), 450 + c, dev)) for c in range(2)]
+    pools = [(S.randn_bf16((npool, 16, Hkv, D), 440 + c, dev),
+              S.randn_bf16((npool, 16, Hkv, D), 450 + c, dev)) for c in range(2)]
     btr = (torch.randperm(npool, generator=torch.Generator().manual_seed(9))[:Br * rpages]
            .view(Br, rpages).to(torch.int32).to(dev))
     ctxr = torch.full((Br,), n_r, dtype=torch.int32, device=dev)

@@ -9,16 +9,14 @@
  *        "Paged Attention".
  *
  * Data layout (all tensors contiguous, row-major, bf16 unless stated):
- *   k_cache, v_cache   [num_blocks][Hkv][block_size=16][D]   one layer's page pool,
- *                      head-major inside a page: the row of (page b, KV head
- *                      g, slot s) starts at ((b*Hkv + g)*16 + s)*D elements.
- *                      [P1] paged.py stores the same rows token-major
- *                      ([n_layers, capacity, block_size, n_kv_heads,
- *                      head_dim]); the pages' entries are the rows, and this
- *                      library keeps each (page, KV head) as 16 contiguous
- *                      rows (4 KiB at D = 128) so attention reads whole
- *                      contiguous blocks.  Block b and slot s mean the same
- *                      in both orders.
+ *   k_cache, v_cache   [num_blocks][block_size=16][Hkv][D]   one layer's page
+ *                      pool, the per-layer slice of [P1] paged.py's
+ *                      [n_layers, capacity, block_size, n_kv_heads,
+ *                      head_dim]: the row of (page b, slot s, KV head g)
+ *                      starts at ((b*16 + s)*Hkv + g)*D elements, so one
+ *                      token's K (or V) for all KV heads is Hkv*D contiguous
+ *                      values and flat slot b*16 + s is row block
+ *                      b*16 + s of [num_blocks*16][Hkv][D].
  *   block_tables       int32 [B][max_blocks_per_seq]: logical page i of
  *                      sequence b lives in physical page block_tables[b][i]
  *                      ([P1] SequenceCache.blocks; [P3] page table).  Entries
@@ -97,7 +95,7 @@ int pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
 /*
  * KV append ([P1] paged.py PagedKVCache.write; model.py forward writes the
  * step's K/V into the pages).  A bit-exact scatter of rows:
- *     k_cache[slot / 16][g][slot % 16][:] = k_new[t][g][:]   for every KV head g (same for V)
+ *     k_cache[slot / 16][slot % 16][:][:] = k_new[t][:][:]   (all KV heads; same for V)
  * for every t with 0 <= slot = slot_mapping[t] < num_blocks*16; other slots
  * (negative = padding) are skipped.  Slots must be distinct (duplicates race;
  * PKV_VALIDATE=1 rejects them).
@@ -117,8 +115,8 @@ int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping
  *   k_pool, v_pool   device memory holding n_layers pools, layer l starting
  *                    at pool + l * layer_stride_bytes, block b of a layer at
  *                    b * block_bytes from its start (any page format: bf16
- *                    pools have block_bytes = Hkv*16*D*2, int8 codes
- *                    Hkv*16*D, int8 scale arrays Hkv*16*2*4 with v_pool NULL)
+ *                    pools have block_bytes = 16*Hkv*D*2, int8 codes
+ *                    16*Hkv*D, int8 scale arrays 16*Hkv*4)
  *   src_blocks, dst_blocks  int32 [n_pairs], device
  * Pointers, block_bytes and layer_stride_bytes must be multiples of 16.
  * Destinations must be distinct and no destination may be a source (the
@@ -259,7 +257,7 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
  *   q_norm_w, k_norm_w  bf16 [D]
  *   cos_table, sin_table  bf16 [max_pos][D], both halves of a row equal
  *                   ([P1] _rope_tables: inv_freq = 1 / theta^(2i/D))
- *   k_cache, v_cache  the bf16 page pools (head-major, as pkv_append)
+ *   k_cache, v_cache  the bf16 page pools ([num_blocks][16][Hkv][D], as pkv_append)
  * The only difference from the listing's arithmetic is the order of the
  * 128-term float32 sum of squares.
  */
@@ -276,15 +274,12 @@ int pkv_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in, con
  * int8 KV pages ([P2] kv_cache.py listing, section 5, class KV8Cache: one
  * byte per element plus one float32 scale per (token, KV head); [P2] closing
  * notes: 2112 B instead of 4096 B per token-layer at H_kv 8, d_head 128).
- * Pool layout:
- *   k_codes, v_codes  int8 [num_blocks][Hkv][16][D], the order of the bf16
- *                     pools; a row of codes reads back as code * scale.
- *   kv_scales         float32 [num_blocks][Hkv][8][2][2]: the K and V scales
- *                     of slot s of (page b, KV head g) sit at
- *                     [b][g][s % 8][s / 8][0] and [...][1].  (The 16 slots of
- *                     a page are kept as 8 pairs (s, s+8) so that the decode
- *                     kernel reads the four scales of a lane's two rows in one
- *                     16-byte load.)
+ * Pool layout, the per-layer slice of KV8Cache's k, v [L, cap, H_kv, D] and
+ * ks, vs [L, cap, H_kv] with cap cut into pages of 16 slots:
+ *   k_codes, v_codes    int8 [num_blocks][16][Hkv][D], the order of the bf16
+ *                       pools; a row of codes reads back as code * scale.
+ *   k_scales, v_scales  float32 [num_blocks][16][Hkv]: the scale of the row
+ *                       of (page b, slot s, KV head g) at [b][s][g].
  * Unwritten slots may hold anything; a NaN scale there is never read.
  */
 
@@ -299,7 +294,7 @@ int pkv_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in, con
  *   k_new, v_new  bf16 [T][Hkv][D]
  */
 int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
-                    void* k_codes, void* v_codes, float* kv_scales, int32_t T,
+                    void* k_codes, void* v_codes, float* k_scales, float* v_scales, int32_t T,
                     int32_t num_blocks, int32_t Hkv, int32_t D, int32_t block_size, void* stream);
 
 /*
@@ -311,7 +306,8 @@ int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_ma
  * its probability, which is rounded to bf16 for the PV product.
  */
 int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
-                         const float* kv_scales, const int32_t* block_tables,
+                         const float* k_scales, const float* v_scales,
+                         const int32_t* block_tables,
                          const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
                          int32_t D, int32_t block_size, int32_t num_blocks,
                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
@@ -322,12 +318,13 @@ int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const vo
  * back as code * scale; then the attention of pkv_attn_prefill_chunk).  Same
  * arguments, outputs, error behaviour, split plan and workspace as
  * pkv_attn_prefill_chunk (pkv_prefill_workspace_bytes applies unchanged),
- * with the pools replaced by k_codes, v_codes and kv_scales in the layout
- * above.  Each tile of 64 keys is dequantised once per workgroup, code *
+ * with the pools replaced by k_codes, v_codes, k_scales and v_scales in the
+ * layout above.  Each tile of 64 keys is dequantised once per workgroup, code *
  * scale rounded to bf16, and the bf16 MFMA path runs on the result.
  */
 int pkv_attn_prefill_chunk_int8(void* out, const void* q, const int32_t* cu_q_lens,
-                                const void* k_codes, const void* v_codes, const float* kv_scales,
+                                const void* k_codes, const void* v_codes, const float* k_scales,
+                                const float* v_scales,
                                 const int32_t* block_tables, const int32_t* context_lens,
                                 int32_t B, int32_t total_q, int32_t max_q_len, int32_t Hq,
                                 int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,

@@ -33,11 +33,8 @@ SIGNATURES = {
     "pkv_attn_prefill_chunk": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                         _f, _vp, _c_size, _vp]),
-    "pkv_append_int8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
-                                 _c_int, _vp]),
-    "pkv_attn_decode_int8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
-                                      _c_int, _c_int, _c_int, _c_int, _c_int, _f, _vp, _c_size,
-                                      _vp]),
+    "pkv_append_int8": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_vp]),
+    "pkv_attn_decode_int8": (_c_int, [_vp] * 8 + [_c_int] * 8 + [_f, _vp, _c_size, _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _c_int,
                                  ctypes.c_int64, _vp]),
     "pkv_slot_mapping_ring": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
@@ -48,7 +45,7 @@ SIGNATURES = {
     "pkv_attn_prefill_chunk_ring": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
-    "pkv_attn_prefill_chunk_int8": (_c_int, [_vp] * 8 + [_c_int] * 10 + [_f, _vp, _c_size, _vp]),
+    "pkv_attn_prefill_chunk_int8": (_c_int, [_vp] * 9 + [_c_int] * 10 + [_f, _vp, _c_size, _vp]),
     "pkv_qk_norm_rope_append": (_c_int, [_vp] * 8 + [_c_int] + [_vp] * 6 +
                                 [_c_int] * 8 + [_f, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -123,7 +120,7 @@ def pkv_slot_mapping(slot_mapping: torch.Tensor, block_tables: torch.Tensor,
 
 def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
                k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
-    """Scatter k_new/v_new [T, Hkv, D] into the head-major pools [num_blocks, Hkv, 16, D]."""
+    """Scatter k_new/v_new [T, Hkv, D] into the pools [num_blocks, 16, Hkv, D]."""
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t, torch.bfloat16, n, 3)
     for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -132,10 +129,10 @@ def pkv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Ten
     T, Hkv, D = k_new.shape
     nb = k_cache.shape[0]
     if v_new.shape != k_new.shape or v_cache.shape != k_cache.shape or \
-            k_cache.shape[1] != Hkv or k_cache.shape[3] != D or slot_mapping.numel() != T:
+            k_cache.shape[2] != Hkv or k_cache.shape[3] != D or slot_mapping.numel() != T:
         raise ValueError("inconsistent shapes")
     _check(load().pkv_append(_p(k_new), _p(v_new), _p(slot_mapping), _p(k_cache), _p(v_cache),
-                             T, nb, Hkv, D, k_cache.shape[2], _stream(stream)))
+                             T, nb, Hkv, D, k_cache.shape[1], _stream(stream)))
 
 
 def pkv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_context_len: int) -> int:
@@ -172,7 +169,7 @@ def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     B, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape            # head-major pages
+    nb, bs, Hkv, D2 = k_cache.shape            # [num_blocks, 16, Hkv, D] pages
     if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
             block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent shapes")
@@ -196,7 +193,7 @@ def pkv_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     B, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape            # head-major pages
+    nb, bs, Hkv, D2 = k_cache.shape            # [num_blocks, 16, Hkv, D] pages
     if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
             block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent shapes")
@@ -221,7 +218,7 @@ def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.
         _need(t, torch.int32, n, 1)
     _need(block_tables, torch.int32, "block_tables", 2)
     total_q, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape            # head-major pages
+    nb, bs, Hkv, D2 = k_cache.shape            # [num_blocks, 16, Hkv, D] pages
     B = context_lens.numel()
     if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
             block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
@@ -233,30 +230,36 @@ def pkv_attn_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.
                                          float(scale), *_ws(workspace), _stream(stream)))
 
 
+def _need_scales(k_scales: torch.Tensor, v_scales: torch.Tensor, codes: torch.Tensor) -> None:
+    for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        _need(t, torch.float32, n, 3)
+    if k_scales.shape != codes.shape[:3] or v_scales.shape != codes.shape[:3]:
+        raise ValueError("scales must be [num_blocks, 16, Hkv] like the codes' first dims")
+
+
 def pkv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
-                    k_codes: torch.Tensor, v_codes: torch.Tensor, kv_scales: torch.Tensor,
-                    stream=None) -> None:
-    """Quantise k_new/v_new [T, Hkv, D] into int8 pools: codes [num_blocks, Hkv, 16, D],
-    scales [num_blocks, Hkv, 8, 2, 2] (slot s of a page at [s % 8][s // 8][K, V])."""
+                    k_codes: torch.Tensor, v_codes: torch.Tensor, k_scales: torch.Tensor,
+                    v_scales: torch.Tensor, stream=None) -> None:
+    """Quantise k_new/v_new [T, Hkv, D] into int8 pools: codes [num_blocks, 16, Hkv, D],
+    scales [num_blocks, 16, Hkv] for K and for V."""
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t, torch.bfloat16, n, 3)
     for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
         _need(t, torch.int8, n, 4)
-    _need(kv_scales, torch.float32, "kv_scales", 5)
+    _need_scales(k_scales, v_scales, k_codes)
     _need(slot_mapping, torch.int32, "slot_mapping", 1)
     T, Hkv, D = k_new.shape
     nb = k_codes.shape[0]
     if v_new.shape != k_new.shape or v_codes.shape != k_codes.shape or \
-            k_codes.shape[1] != Hkv or k_codes.shape[3] != D or slot_mapping.numel() != T or \
-            tuple(kv_scales.shape) != (nb, Hkv, 8, 2, 2):
+            k_codes.shape[2] != Hkv or k_codes.shape[3] != D or slot_mapping.numel() != T:
         raise ValueError("inconsistent shapes")
     _check(load().pkv_append_int8(_p(k_new), _p(v_new), _p(slot_mapping), _p(k_codes),
-                                  _p(v_codes), _p(kv_scales), T, nb, Hkv, D, k_codes.shape[2],
-                                  _stream(stream)))
+                                  _p(v_codes), _p(k_scales), _p(v_scales), T, nb, Hkv, D,
+                                  k_codes.shape[1], _stream(stream)))
 
 
 def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tensor,
-                         v_codes: torch.Tensor, kv_scales: torch.Tensor,
+                         v_codes: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
                          block_tables: torch.Tensor, context_lens: torch.Tensor,
                          max_context_len: int, scale: float,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -266,49 +269,49 @@ def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tens
     _need(out, torch.bfloat16, "out", 3)
     for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
         _need(t, torch.int8, n, 4)
-    _need(kv_scales, torch.float32, "kv_scales", 5)
+    _need_scales(k_scales, v_scales, k_codes)
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     B, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_codes.shape
+    nb, bs, Hkv, D2 = k_codes.shape
     if out.shape != q.shape or D2 != D or v_codes.shape != k_codes.shape or \
-            tuple(kv_scales.shape) != (nb, Hkv, 8, 2, 2) or \
             block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent shapes")
     ws_ptr, ws_bytes = _ws(workspace)
-    _check(load().pkv_attn_decode_int8(_p(out), _p(q), _p(k_codes), _p(v_codes), _p(kv_scales),
-                                       _p(block_tables), _p(context_lens), B, Hq, Hkv, D, bs, nb,
-                                       block_tables.shape[1], int(max_context_len), float(scale),
-                                       ws_ptr, ws_bytes, _stream(stream)))
+    _check(load().pkv_attn_decode_int8(_p(out), _p(q), _p(k_codes), _p(v_codes), _p(k_scales),
+                                       _p(v_scales), _p(block_tables), _p(context_lens), B, Hq,
+                                       Hkv, D, bs, nb, block_tables.shape[1],
+                                       int(max_context_len), float(scale), ws_ptr, ws_bytes,
+                                       _stream(stream)))
 
 
 def pkv_attn_prefill_chunk_int8(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,
                                 k_codes: torch.Tensor, v_codes: torch.Tensor,
-                                kv_scales: torch.Tensor, block_tables: torch.Tensor,
-                                context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
-                                scale: float, workspace: Optional[torch.Tensor] = None,
-                                stream=None) -> None:
+                                k_scales: torch.Tensor, v_scales: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                max_q_len: int, max_context_len: int, scale: float,
+                                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """out[total_q, Hq, D] <- causal attention of the chunk rows over int8 pools
     (same workspace as pkv_attn_prefill_chunk)."""
     _need(q, torch.bfloat16, "q", 3)
     _need(out, torch.bfloat16, "out", 3)
     for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
         _need(t, torch.int8, n, 4)
-    _need(kv_scales, torch.float32, "kv_scales", 5)
+    _need_scales(k_scales, v_scales, k_codes)
     for t, n in ((cu_q_lens, "cu_q_lens"), (context_lens, "context_lens")):
         _need(t, torch.int32, n, 1)
     _need(block_tables, torch.int32, "block_tables", 2)
     total_q, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_codes.shape
+    nb, bs, Hkv, D2 = k_codes.shape
     B = context_lens.numel()
     if out.shape != q.shape or D2 != D or v_codes.shape != k_codes.shape or \
-            tuple(kv_scales.shape) != (nb, Hkv, 8, 2, 2) or \
             block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
         raise ValueError("inconsistent shapes")
     _check(load().pkv_attn_prefill_chunk_int8(
-        _p(out), _p(q), _p(cu_q_lens), _p(k_codes), _p(v_codes), _p(kv_scales), _p(block_tables),
-        _p(context_lens), B, total_q, int(max_q_len), Hq, Hkv, D, bs, nb, block_tables.shape[1],
-        int(max_context_len), float(scale), *_ws(workspace), _stream(stream)))
+        _p(out), _p(q), _p(cu_q_lens), _p(k_codes), _p(v_codes), _p(k_scales), _p(v_scales),
+        _p(block_tables), _p(context_lens), B, total_q, int(max_q_len), Hq, Hkv, D, bs, nb,
+        block_tables.shape[1], int(max_context_len), float(scale), *_ws(workspace),
+        _stream(stream)))
 
 
 def pkv_copy_blocks(src_blocks: torch.Tensor, dst_blocks: torch.Tensor, k_pool: torch.Tensor,
@@ -371,7 +374,7 @@ def pkv_attn_decode_ring(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
     _need(block_tables, torch.int32, "block_tables", 2)
     _need(context_lens, torch.int32, "context_lens", 1)
     B, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape
+    nb, bs, Hkv, D2 = k_cache.shape
     if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
             block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent shapes")
@@ -396,7 +399,7 @@ def pkv_attn_prefill_chunk_ring(out: torch.Tensor, q: torch.Tensor, cu_q_lens: t
         _need(t, torch.int32, n, 1)
     _need(block_tables, torch.int32, "block_tables", 2)
     total_q, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape
+    nb, bs, Hkv, D2 = k_cache.shape
     B = context_lens.numel()
     if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
             block_tables.shape[0] != B or cu_q_lens.numel() != B + 1:
@@ -428,7 +431,7 @@ def pkv_qk_norm_rope_append(q_out: torch.Tensor, q_in: torch.Tensor, k_in: torch
     _need(cu_new_lens, torch.int32, "cu_new_lens", 1)
     _need(context_lens, torch.int32, "context_lens", 1)
     T, Hq, D = q_in.shape
-    nb, Hkv, bs, D2 = k_cache.shape
+    nb, bs, Hkv, D2 = k_cache.shape
     B = context_lens.numel()
     if q_out.shape != q_in.shape or k_in.shape != (T, Hkv, D) or v_in.shape != k_in.shape or \
             D2 != D or v_cache.shape != k_cache.shape or q_norm_w.numel() != D or \

@@ -10,10 +10,11 @@
 // split) and serves all G = Hq/Hkv query heads of the group from the same
 // loaded K/V rows, so every K/V byte is read from HBM once per step.  The
 // workgroup's 4 waves take disjoint page ranges of the split.  Pages are
-// stored head-major, so a 16-token page of one head is 16 contiguous rows of
-// 256 B (4 KiB): lane l holds rows (l>>3) and (l>>3)+8 and the 16-byte chunks
-// (l&7) and (l&7)+8 of each, so every load instruction moves eight full
-// 128-byte lines.  The K/V rows stay in VGPRs (no LDS staging: the reuse
+// stored token-major as in the Module 12 page's paged.py ([page][16 slots][KV
+// head][D]), so a 16-token page of one head is 16 rows of 256 B, Hkv*256 B
+// apart: lane l holds rows (l>>3) and (l>>3)+8 and the 16-byte chunks (l&7)
+// and (l&7)+8 of each, so every load instruction moves eight full 128-byte
+// lines.  The K/V rows stay in VGPRs (no LDS staging: the reuse
 // across the G heads happens inside each lane).  Scores use v_dot2_f32_bf16
 // on the packed bf16 data and an 8-lane DPP butterfly finishes each dot
 // product; each lane keeps an online-softmax state (fp32 m, l, acc) over its
@@ -76,10 +77,10 @@ __device__ __forceinline__ void ws_store(float* p, float v) {
 struct DecodeArgs {
   uint16_t* out;                 // bf16 [B][Hq][D]
   const u32x4* q;                // bf16 [B][Hq][D] as 16-byte chunks
-  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D], or int8 codes (same order)
+  const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D], or int8 codes (same order)
   const u32x4* v_cache;
-  const float* kv_scales;        // int8 pages: float32 [num_blocks][Hkv][8][2][2]: the (K, V)
-                                 // scales of slot s at [s % 8][s / 8]
+  const float* k_scales;         // int8 pages: float32 [num_blocks][16][Hkv]
+  const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
   float* ws_ml;                  // [B][Hq][S][2] (m, l), log2 domain
@@ -122,9 +123,10 @@ __device__ __forceinline__ float softmax_ref(const float (&s)[U][2], float& m, f
   return (m == kNegInf) ? 0.f : m;
 }
 
-// bf16 pages.  A 16-token page of one head is 16 rows of 256 B: lane l holds
-// rows r0 = l>>3 and r0+8, and the 16-byte chunks c = l&7 and c+8 of each,
-// i.e. head dims 8c..8c+7 and 64+8c..64+8c+7 (accumulator d < 8 and d >= 8).
+// bf16 pages.  A 16-token page of one head is 16 rows of 256 B, one per slot
+// (Hkv rows apart): lane l holds rows r0 = l>>3 and r0+8, and the 16-byte
+// chunks c = l&7 and c+8 of each, i.e. head dims 8c..8c+7 and 64+8c..64+8c+7
+// (accumulator d < 8 and d >= 8).
 struct Bf16Page {
   struct Regs {
     u32x4 k[2][2];   // [row r0 / r0+8][chunk c / c+8]
@@ -140,15 +142,16 @@ struct Bf16Page {
   }
   static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
                                               int r0, int c) {
-    const int64_t base = (blk * a.Hkv + g) * kPage * 16 + r0 * 16 + c;   // 16 chunks per row
+    const int64_t base = ((blk * kPage + r0) * a.Hkv + g) * 16 + c;   // 16 chunks per row
+    const int64_t r8 = (int64_t)8 * a.Hkv * 16;                       // row r0 + 8
     const u32x4* kp = a.k_cache + base;
     const u32x4* vp = a.v_cache + base;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       r.k[0][h] = load_kv(kp + 8 * h);
-      r.k[1][h] = load_kv(kp + 128 + 8 * h);
+      r.k[1][h] = load_kv(kp + r8 + 8 * h);
       r.v[0][h] = load_kv(vp + 8 * h);
-      r.v[1][h] = load_kv(vp + 128 + 8 * h);
+      r.v[1][h] = load_kv(vp + r8 + 8 * h);
     }
   }
   // kMask: the page is the sequence's last, partially filled one; rows >=
@@ -212,18 +215,21 @@ struct Bf16Page {
 
 // int8 pages (codes with one float32 scale per (slot, head), read as
 // code * scale; Module 04 page, kv_cache.py listing, section 5).  A page of
-// one head is 16 rows of 128 codes (2 KiB) plus 16 (K, V) scale pairs, kept
-// as 8 row pairs (s, s+8): lane l holds rows r0 = l>>3 and r0+8, the 16-byte
-// chunk c = l&7 of each (head dims 16c..16c+15), and the four scales of its
-// two rows, which are one 16-byte load (a page is 5 loads per lane).  Codes are integers in
-// [-127, 127], exact in bf16, so q . codes runs on v_dot2_f32_bf16 and the
-// row's K scale multiplies the score; the row's V scale is folded into its
-// probability before the PV product.
+// one head is 16 rows of 128 codes (Hkv*128 B apart) plus 16 K and 16 V
+// scales: lane l holds rows r0 = l>>3 and r0+8 and the 16-byte chunk c = l&7
+// of each (head dims 16c..16c+15).  The four scales of those two rows are
+// loaded once per 4-lane quad, lane c & 3 of it taking K(r0), K(r0+8), V(r0)
+// or V(r0+8), and handed to the whole quad by DPP broadcasts (a page is 5
+// loads per lane).  Codes are integers in [-127, 127], exact in bf16, so
+// q . codes runs on v_dot2_f32_bf16 and the row's K scale multiplies the
+// score; the row's V scale is folded into its probability before the PV
+// product.
+constexpr int kQuadBcast0 = 0x00, kQuadBcast1 = 0x55, kQuadBcast2 = 0xAA, kQuadBcast3 = 0xFF;
 struct Int8Page {
   struct Regs {
     u32x4 k[2];      // [row r0 / r0+8], 16 codes each
     u32x4 v[2];
-    f32x4 s;         // K scale r0, V scale r0, K scale r0+8, V scale r0+8
+    float s;         // lane c & 3 of the quad: K(r0), K(r0+8), V(r0), V(r0+8)
   };
   static __device__ __forceinline__ int dim(int c, int d) { return 16 * c + d; }
   static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
@@ -233,12 +239,13 @@ struct Int8Page {
   }
   static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
                                               int r0, int c) {
-    const int64_t row = (blk * a.Hkv + g) * kPage + r0;        // 8 chunks per row
+    const int64_t row = (blk * kPage + r0) * a.Hkv + g;        // 8 chunks per row
+    const int64_t r8 = (int64_t)8 * a.Hkv;                      // row r0 + 8
     r.k[0] = load_kv(a.k_cache + row * 8 + c);
-    r.k[1] = load_kv(a.k_cache + (row + 8) * 8 + c);
+    r.k[1] = load_kv(a.k_cache + (row + r8) * 8 + c);
     r.v[0] = load_kv(a.v_cache + row * 8 + c);
-    r.v[1] = load_kv(a.v_cache + (row + 8) * 8 + c);
-    r.s = reinterpret_cast<const f32x4*>(a.kv_scales)[(blk * a.Hkv + g) * 8 + r0];
+    r.v[1] = load_kv(a.v_cache + (row + r8) * 8 + c);
+    r.s = ((c & 2) ? a.v_scales : a.k_scales)[row + ((c & 1) ? r8 : 0)];
   }
   // Codes of one 4-code word as two bf16 pairs (exact).
   static __device__ __forceinline__ bf16x2 pair(uint32_t w, int lo) {
@@ -249,6 +256,15 @@ struct Int8Page {
                                                  float (&m)[G], float (&l)[G],
                                                  float (&acc)[G][16], float scale_log2, int r0,
                                                  int valid_rows) {
+    // the quad's four scales in every lane: K(r0), K(r0+8), V(r0), V(r0+8)
+    float ks[U][2], vs[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ks[u][0] = dpp_f<kQuadBcast0>(buf[u].s);
+      ks[u][1] = dpp_f<kQuadBcast1>(buf[u].s);
+      vs[u][0] = dpp_f<kQuadBcast2>(buf[u].s);
+      vs[u][1] = dpp_f<kQuadBcast3>(buf[u].s);
+    }
     float s[G][U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -260,7 +276,7 @@ struct Int8Page {
           kp[2 * i] = pair(buf[u].k[rr][i], 0);
           kp[2 * i + 1] = pair(buf[u].k[rr][i], 2);
         }
-        const float rs = buf[u].s[2 * rr] * scale_log2;
+        const float rs = ks[u][rr] * scale_log2;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           float d = 0.f;
@@ -281,8 +297,8 @@ struct Int8Page {
         const float p0 = fast_exp2(s[j][u][0] - mu), p1 = fast_exp2(s[j][u][1] - mu);
         l[j] += p0 + p1;
         // masked rows: weight exactly 0 (their scale may be a NaN canary)
-        const float w0 = (!kMask || r0 < valid_rows) ? p0 * buf[u].s[1] : 0.f;
-        const float w1 = (!kMask || r0 + 8 < valid_rows) ? p1 * buf[u].s[3] : 0.f;
+        const float w0 = (!kMask || r0 < valid_rows) ? p0 * vs[u][0] : 0.f;
+        const float w1 = (!kMask || r0 + 8 < valid_rows) ? p1 * vs[u][1] : 0.f;
         pp[u][j] = bf16x2{(__bf16)w0, (__bf16)w1};
       }
     }
@@ -604,7 +620,7 @@ SplitBuffers workspace_buffers(const DecodePlan& plan, void* workspace) {
 }
 
 DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* v_cache,
-                     const float* kv_scales,
+                     const float* k_scales, const float* v_scales,
                      const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
                      int Hkv, int num_blocks, int max_blocks, float scale,
                      const DecodePlan& plan, const SplitBuffers& wsb, int window) {
@@ -613,7 +629,8 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
   a.q = static_cast<const u32x4*>(q);
   a.k_cache = static_cast<const u32x4*>(k_cache);
   a.v_cache = static_cast<const u32x4*>(v_cache);
-  a.kv_scales = kv_scales;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
   const bool split = plan.splits > 1;
@@ -739,8 +756,8 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          int Hkv, int num_blocks, int max_blocks, float scale, int window,
                          const DecodePlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables, ctx_lens, B,
-                                 Hq, Hkv, num_blocks, max_blocks, scale, plan,
+  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
                                  workspace_buffers(plan, workspace), window);
   return launch_by_group<Bf16Page>(a, Hq / Hkv, stream);
 }
@@ -764,19 +781,20 @@ hipError_t launch_decode_noalloc(void* out, const void* q, const void* k_cache,
   const SplitBuffers wsb{reinterpret_cast<float*>(base + kScratchCounterBytes),
                          reinterpret_cast<float*>(base + kScratchCounterBytes + plan.ws_ml_bytes),
                          reinterpret_cast<int*>(base)};
-  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, block_tables, ctx_lens, B,
-                                 Hq, Hkv, num_blocks, max_blocks, scale, plan, wsb, 0);
+  const DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan, wsb,
+                                 0);
   return launch_by_group<Bf16Page>(a, Hq / Hkv, stream);
 }
 
 hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
-                              const float* kv_scales, const int32_t* block_tables,
-                              const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
-                              int max_blocks, float scale, const DecodePlan& plan,
-                              void* workspace, hipStream_t stream) {
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
+                              int Hkv, int num_blocks, int max_blocks, float scale,
+                              const DecodePlan& plan, void* workspace, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  const DecodeArgs a = make_args(out, q, k_codes, v_codes, kv_scales, block_tables, ctx_lens, B,
-                                 Hq, Hkv, num_blocks, max_blocks, scale, plan,
+  const DecodeArgs a = make_args(out, q, k_codes, v_codes, k_scales, v_scales, block_tables,
+                                 ctx_lens, B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
                                  workspace_buffers(plan, workspace), 0);
   return launch_by_group<Int8Page>(a, Hq / Hkv, stream);
 }

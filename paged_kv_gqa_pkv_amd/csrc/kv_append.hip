@@ -4,9 +4,9 @@
 // PagedKVCache.write: position s lands in page blocks[s // 16] at offset
 // s % 16; model.py forward: the step's tokens take positions start_pos ..
 // start_pos+T-1).  Append is the same write as a row copy: pages are stored
-// head-major ([page][KV head][16 slots][D]), so one token's K (or V) for all
-// KV heads is Hkv rows of D*2 contiguous bytes, one per head, each copied
-// with 16-byte moves.
+// token-major as in paged.py ([page][16 slots][KV head][D]), so one token's K
+// (or V) for all KV heads is one contiguous run of Hkv*D*2 bytes in its page,
+// copied with 16-byte moves.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -42,15 +42,15 @@ slot_mapping_kernel(int32_t* __restrict__ slots, const int32_t* __restrict__ blo
   slots[t] = slot;
 }
 
-// Work item = one 16-byte chunk of one token's K or V row of one KV head.
-// Consecutive threads take consecutive chunks of a token's [Hkv][D] row in
-// k_new, so the read is fully coalesced and each head's 256-byte row lands
-// as a contiguous run in its page.
+// Work item = one 16-byte chunk of one token's K or V row ([Hkv][D]).
+// Consecutive threads take consecutive chunks of that row, so both the read
+// from k_new and the write into the token's slot are contiguous runs.
 __global__ void __launch_bounds__(256)
 append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
               const int32_t* __restrict__ slots, u32x4* __restrict__ k_cache,
               u32x4* __restrict__ v_cache, int64_t n_items, int Hkv, int chunks_per_head,
               int64_t num_slots) {
+  // slot s of the pool starts at chunk s * chunks_per_row (pages of 16 slots)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int chunks_per_row = Hkv * chunks_per_head;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_items; i += stride) {
@@ -58,14 +58,11 @@ append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
     const int row_item = (int)(i % (2 * chunks_per_row));
     const int which = row_item / chunks_per_row;
     const int r = row_item % chunks_per_row;     // chunk within the token's [Hkv][D] row
-    const int h = r / chunks_per_head;
-    const int c = r % chunks_per_head;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / kPage, off = slot % kPage;
     const u32x4* src = which ? v_new : k_new;
     u32x4* dst = which ? v_cache : k_cache;
-    dst[((blk * Hkv + h) * kPage + off) * chunks_per_head + c] = src[t * chunks_per_row + r];
+    dst[slot * chunks_per_row + r] = src[t * chunks_per_row + r];
   }
 }
 
@@ -75,8 +72,10 @@ append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
 // with round half to even, so the codes and scale match the page's numpy
 // float32 arithmetic bit for bit.  16 lanes own one row of 128 values (8 per
 // lane): the row max is a DPP reduction inside the 16-lane row, each lane
-// writes its 8 codes (8 bytes), and the first lane writes the scale into the
-// row-pair order of the scale array ([page][head][s % 8][s / 8][K, V]).
+// writes its 8 codes (8 bytes), and the first lane writes the scale.  Codes
+// are token-major like the bf16 pools ([page][16 slots][KV head][D]) and the
+// scales sit at [page][slot][KV head] of k_scales or v_scales (the listing's
+// ks and vs [L, cap, H_kv], one layer, cap cut into pages).
 //
 // The quotients x_d / scale are the correctly rounded ones without a full
 // division each: with y = 1 / scale correctly rounded (one IEEE division per
@@ -95,8 +94,8 @@ __device__ __forceinline__ float max16(float x) {
 __global__ void __launch_bounds__(256)
 append_int8_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
                    const int32_t* __restrict__ slots, uint2* __restrict__ k_codes,
-                   uint2* __restrict__ v_codes, float* __restrict__ kv_scales, int64_t n_rows,
-                   int Hkv, int64_t num_slots) {
+                   uint2* __restrict__ v_codes, float* __restrict__ k_scales,
+                   float* __restrict__ v_scales, int64_t n_rows, int Hkv, int64_t num_slots) {
   const int sub = threadIdx.x & 15;                    // lane within the row group
   // r = (t * 2 + which) * Hkv + h, one row per 16-lane group: all 16 lanes
   // share r, so the DPP reduction below only reads lanes of the same row.
@@ -126,16 +125,14 @@ append_int8_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_
     pk[i >> 2] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (i & 3));
   }
   if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / kPage, off = slot % kPage;
-  const int64_t row = (blk * Hkv + h) * kPage + off;              // codes row (128 B)
+  const int64_t row = slot * Hkv + h;                             // codes row (128 B)
   (which ? v_codes : k_codes)[row * 16 + sub] = make_uint2(pk[0], pk[1]);
-  if (sub == 0)
-    kv_scales[((blk * Hkv + h) * 8 + (off & 7)) * 4 + (off >> 3) * 2 + which] = scale;
+  if (sub == 0) (which ? v_scales : k_scales)[row] = scale;
 }
 
 hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_t* slots,
-                              void* k_codes, void* v_codes, float* kv_scales, int T,
-                              int num_blocks, int Hkv, int D, hipStream_t stream) {
+                              void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                              int T, int num_blocks, int Hkv, int D, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (D != 128) return hipErrorInvalidValue;       // 16 lanes x 8 values per row
   const int64_t n_rows = (int64_t)T * 2 * Hkv;
@@ -143,7 +140,8 @@ hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(append_int8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const u32x4*)k_new, (const u32x4*)v_new, slots, (uint2*)k_codes,
-                     (uint2*)v_codes, kv_scales, n_rows, Hkv, (int64_t)num_blocks * kPage);
+                     (uint2*)v_codes, k_scales, v_scales, n_rows, Hkv,
+                     (int64_t)num_blocks * kPage);
   return hipGetLastError();
 }
 

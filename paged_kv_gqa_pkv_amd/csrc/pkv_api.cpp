@@ -275,22 +275,23 @@ int pkv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping
 }
 
 int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
-                    void* k_codes, void* v_codes, float* kv_scales, int32_t T,
+                    void* k_codes, void* v_codes, float* k_scales, float* v_scales, int32_t T,
                     int32_t num_blocks, int32_t Hkv, int32_t D, int32_t block_size, void* stream) {
   if (T < 0 || num_blocks < 0) return fail(PKV_EINVAL, "negative size");
   int rc = check_geometry(Hkv, Hkv, D, block_size);
   if (rc) return rc;
   if (T == 0) return PKV_OK;
-  if (!k_new || !v_new || !slot_mapping || !k_codes || !v_codes || !kv_scales)
+  if (!k_new || !v_new || !slot_mapping || !k_codes || !v_codes || !k_scales || !v_scales)
     return fail(PKV_EINVAL, "null pointer argument");
   if (k_codes == v_codes) return fail(PKV_EINVAL, "k_codes and v_codes must differ");
+  if (k_scales == v_scales) return fail(PKV_EINVAL, "k_scales and v_scales must differ");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validate_mode()) {
     rc = validate_slots(slot_mapping, T, num_blocks, s);
     if (rc) return rc;
   }
   return launch_status(pkv::launch_append_int8(k_new, v_new, slot_mapping, k_codes, v_codes,
-                                               kv_scales, T, num_blocks, Hkv, D, s),
+                                               k_scales, v_scales, T, num_blocks, Hkv, D, s),
                        "pkv_append_int8");
 }
 
@@ -447,19 +448,21 @@ int pkv_attn_decode_ring(void* out, const void* q, const void* k_cache, const vo
 }
 
 int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
-                         const float* kv_scales, const int32_t* block_tables,
+                         const float* k_scales, const float* v_scales,
+                         const int32_t* block_tables,
                          const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
                          int32_t D, int32_t block_size, int32_t num_blocks,
                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                          void* workspace, size_t workspace_bytes, void* stream) {
   pkv::DecodePlan plan;
   bool done = false;
-  if (B > 0 && !kv_scales) return fail(PKV_EINVAL, "null pointer argument");
+  if (B > 0 && (!k_scales || !v_scales)) return fail(PKV_EINVAL, "null pointer argument");
   int rc = check_decode(out, q, k_codes, v_codes, block_tables, context_lens, B, Hq, Hkv, D,
                         block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
                         workspace, workspace_bytes, stream, plan, done);
   if (rc || done) return rc;
-  return launch_status(pkv::launch_decode_int8(out, q, k_codes, v_codes, kv_scales, block_tables,
+  return launch_status(pkv::launch_decode_int8(out, q, k_codes, v_codes, k_scales, v_scales,
+                                               block_tables,
                                                context_lens, B, Hq, Hkv, num_blocks,
                                                max_blocks_per_seq, scale, plan, workspace,
                                                static_cast<hipStream_t>(stream)),
@@ -475,7 +478,8 @@ size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int
 }
 
 static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
-                        const void* k_cache, const void* v_cache, const float* kv_scales,
+                        const void* k_cache, const void* v_cache, const float* k_scales,
+                        const float* v_scales,
                         const int32_t* block_tables,
                         const int32_t* context_lens, int32_t B, int32_t total_q,
                         int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
@@ -533,11 +537,11 @@ static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
                          max_context_len, s, window);
     if (rc) return rc;
   }
-  return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, kv_scales,
+  return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, k_scales, v_scales,
                                            block_tables, context_lens, B, total_q, max_q_len, Hq,
                                            Hkv, num_blocks, max_blocks_per_seq, scale, window,
                                            plan, workspace, s),
-                       kv_scales ? "pkv_attn_prefill_chunk_int8" : "pkv_attn_prefill_chunk");
+                       k_scales ? "pkv_attn_prefill_chunk_int8" : "pkv_attn_prefill_chunk");
 }
 
 int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
@@ -547,8 +551,8 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_context_len, float scale, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, nullptr, block_tables, context_lens,
-                      B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, nullptr, nullptr, block_tables,
+                      context_lens, B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
                       stream);
 }
@@ -562,22 +566,24 @@ int pkv_attn_prefill_chunk_ring(void* out, const void* q, const int32_t* cu_q_le
                                 int32_t window, float scale, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (window <= 0) return fail(PKV_EINVAL, "window=%d must be positive", window);
-  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, nullptr, block_tables, context_lens,
-                      B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, nullptr, nullptr, block_tables,
+                      context_lens, B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, window, scale, workspace,
                       workspace_bytes, stream);
 }
 
 int pkv_attn_prefill_chunk_int8(void* out, const void* q, const int32_t* cu_q_lens,
-                                const void* k_codes, const void* v_codes, const float* kv_scales,
+                                const void* k_codes, const void* v_codes, const float* k_scales,
+                                const float* v_scales,
                                 const int32_t* block_tables, const int32_t* context_lens,
                                 int32_t B, int32_t total_q, int32_t max_q_len, int32_t Hq,
                                 int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
                                 int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  if (B > 0 && total_q > 0 && !kv_scales) return fail(PKV_EINVAL, "null pointer argument");
-  return prefill_impl(out, q, cu_q_lens, k_codes, v_codes, kv_scales, block_tables, context_lens,
-                      B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+  if (B > 0 && total_q > 0 && (!k_scales || !v_scales))
+    return fail(PKV_EINVAL, "null pointer argument");
+  return prefill_impl(out, q, cu_q_lens, k_codes, v_codes, k_scales, v_scales, block_tables,
+                      context_lens, B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
                       stream);
 }

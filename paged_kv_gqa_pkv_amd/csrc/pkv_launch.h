@@ -63,17 +63,18 @@ hipError_t launch_decode_noalloc(void* out, const void* q, const void* k_cache,
                                  hipStream_t stream);
 
 // Decode over int8 pages (codes in the bf16 page order; float32 scales
-// [num_blocks][Hkv][8][2][2], the (K, V) scales of slot s at [s % 8][s / 8]);
-// same plan and workspace as launch_decode.
+// [num_blocks][16][Hkv] for K and for V); same plan and workspace as
+// launch_decode.
 hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
-                              const float* kv_scales, const int32_t* block_tables,
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables,
                               const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
                               int max_blocks, float scale, const DecodePlan& plan,
                               void* workspace, hipStream_t stream);
 
 hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_t* slots,
-                              void* k_codes, void* v_codes, float* kv_scales, int T,
-                              int num_blocks, int Hkv, int D, hipStream_t stream);
+                              void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                              int T, int num_blocks, int Hkv, int D, hipStream_t stream);
 
 // Key-split plan of a prefill call: row tiles of 128 (token, head) rows,
 // key ranges of tiles_per_split 64-key tiles.
@@ -89,9 +90,11 @@ struct PrefillPlan {
 
 PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_len, int num_cus);
 
-// kv_scales null: bf16 pages; else int8 codes in k_cache / v_cache.
+// k_scales null: bf16 pages; else int8 codes in k_cache / v_cache with
+// their scales in k_scales / v_scales.
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
-                          const void* v_cache, const float* kv_scales, const int32_t* block_tables,
+                          const void* v_cache, const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream);

@@ -95,9 +95,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // LDS layout.  Two bf16 K tiles, then two bf16 V tiles (bf16 pages: the
 // two-stage K and V rings the DMA fills; int8 pages: the double-buffered
 // dequantised tiles), then for int8 pages kStages code stages of {K codes,
-// V codes, one 1 KB scale DMA slot per page}.
+// V codes, one 256 B scale DMA slot per page: the page's 16 K scales, then
+// its 16 V scales, then a copy of both that is never read}.
 constexpr int kCodeTileBytes = kTileKeys * kD;                 // 8 KB of codes
-constexpr int kScaleSlotBytes = kWave * 16;                    // one 64-lane DMA
+constexpr int kScaleSlotBytes = kWave * 4;                     // one 64-lane dword DMA
 constexpr int kCodeStageBytes = 2 * kCodeTileBytes + 4 * kScaleSlotBytes;
 template <bool kI8>
 struct PrefillLds {
@@ -111,9 +112,10 @@ struct PrefillArgs {
   uint16_t* out;                 // bf16 [total_q][Hq][D]
   const u32x4* q;                // bf16 [total_q][Hq][D] as 16-byte chunks
   const int32_t* cu_q;           // [B+1]
-  const u32x4* k_cache;          // bf16 [num_blocks][Hkv][16][D], or int8 codes
+  const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D], or int8 codes
   const u32x4* v_cache;
-  const u32x4* kv_scales;        // int8 pages: float [num_blocks][Hkv][8][2][2]
+  const float* k_scales;         // int8 pages: float [num_blocks][16][Hkv]
+  const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
   float* ws_acc;                 // [groups][splits][D][128 rows]
@@ -148,6 +150,11 @@ __device__ __forceinline__ int swzv(int r) { return ((r & 3) << 2) | ((r >> 2) &
 // (LDS instructions on gfx9 and later do not use it).
 __device__ __forceinline__ void dma16(const u32x4* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory");
+}
+// The same with 4 bytes per lane: lane i writes LDS bytes [lds + 4 i, lds + 4 i + 4).
+__device__ __forceinline__ void dma4(const float* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :: "v"(g), "s"(lds) : "memory");
 }
 
@@ -322,13 +329,15 @@ prefill_kernel(const PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // DMA of tile i (relative): wave w copies page w of the tile.  bf16: the K
-  // or the V pages into stage i % 2 of their ring, 4 instructions of 4 rows;
-  // lane l of instruction q fills row 16w + 4q + l/16 at chunk position l%16
-  // with logical chunk (l%16) ^ sw(row).  int8: the page's 2 KB of K codes and of
-  // V codes (2 instructions each, rows in order, 128 B apart) and its 128 B
-  // scale block, which lanes l and l+8k all load (lanes 0..7 give it in
-  // order; the rest of the 1 KB slot is never read).
+  // DMA of tile i (relative): wave w copies page w of the tile, the 16 rows
+  // of KV head g (token-major pages: Hkv rows apart).  bf16: the K or the V
+  // rows into stage i % 2 of their ring, 4 instructions of 4 rows; lane l of
+  // instruction q fills row 16w + 4q + l/16 at chunk position l%16 with
+  // logical chunk (l%16) ^ sw(row).  int8: the page's 16 rows of 128 K codes
+  // and of V codes (2 instructions each, 8 rows per instruction, written in
+  // row order 128 B apart) and its scales (one dword instruction: lanes 0..15
+  // the K scales of slots 0..15, lanes 16..31 the V scales, lanes 32..63 the
+  // same again into bytes that are never read).
   const uint32_t k_lds = lds_offset(smem);
   const uint32_t v_lds = k_lds + Lds::kVOff;
   const int dma_r16 = lane >> 4;              // + 4q: row within the page
@@ -338,20 +347,22 @@ prefill_kernel(const PrefillArgs a) {
     if constexpr (kI8) {
       (void)is_v;
       const uint32_t cs = k_lds + Lds::kCodeOff + stage * kCodeStageBytes;
-      const int64_t pg = blk * a.Hkv + g;     // (page, KV head): 128 chunks of codes
 #pragma unroll
       for (int qd = 0; qd < 2; ++qd) {
         const uint32_t off = (uint32_t)(w * kPage * kD + qd * 1024);
-        dma16(a.k_cache + pg * 128 + qd * 64 + lane, cs + off);
-        dma16(a.v_cache + pg * 128 + qd * 64 + lane, cs + kCodeTileBytes + off);
+        const int64_t row = (blk * kPage + 8 * qd + (lane >> 3)) * a.Hkv + g;   // 8 chunks per row
+        dma16(a.k_cache + row * 8 + (lane & 7), cs + off);
+        dma16(a.v_cache + row * 8 + (lane & 7), cs + kCodeTileBytes + off);
       }
-      dma16(a.kv_scales + pg * 8 + (lane & 7), cs + 2 * kCodeTileBytes + w * kScaleSlotBytes);
+      const int si = lane & 31;
+      dma4(((si & 16) ? a.v_scales : a.k_scales) + (blk * kPage + (si & 15)) * a.Hkv + g,
+           cs + 2 * kCodeTileBytes + w * kScaleSlotBytes);
     } else {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const int r16 = 4 * qd + dma_r16;
         const int c = (lane & 15) ^ (is_v ? swzv(r16) : swz(r16));
-        const int64_t idx = ((blk * a.Hkv + g) * kPage + r16) * 16 + c;
+        const int64_t idx = ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
         const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
         if (is_v)
           dma16(a.v_cache + idx, v_lds + off);
@@ -374,10 +385,9 @@ prefill_kernel(const PrefillArgs a) {
     for (int k = 0; k < 2; ++k) {
       const int r = (tid >> 3) + 32 * k;         // key row of the tile
       const u32x4 cw = *reinterpret_cast<const u32x4*>(cs + which * kCodeTileBytes + r * kD + c * 16);
-      const int slot = r & 15;                   // scales of a page: [slot % 8][slot / 8][K, V]
+      const int slot = r & 15;                   // scales of a page: 16 K, then 16 V
       float sc = *reinterpret_cast<const float*>(
-          cs + 2 * kCodeTileBytes + (r >> 4) * kScaleSlotBytes +
-          ((slot & 7) * 4 + (slot >> 3) * 2 + which) * 4);
+          cs + 2 * kCodeTileBytes + (r >> 4) * kScaleSlotBytes + (which * 16 + slot) * 4);
       if (which && (key0 + r >= key_end || key0 + r < key_lo)) sc = 0.f;
       uint32_t o8[8];
 #pragma unroll
@@ -862,7 +872,8 @@ PrefillPlan plan_prefill(int B, int max_q_len, int Hq, int Hkv, int max_context_
 }
 
 hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const void* k_cache,
-                          const void* v_cache, const float* kv_scales, const int32_t* block_tables,
+                          const void* v_cache, const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables,
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream) {
@@ -873,7 +884,8 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.cu_q = cu_q;
   a.k_cache = static_cast<const u32x4*>(k_cache);
   a.v_cache = static_cast<const u32x4*>(v_cache);
-  a.kv_scales = reinterpret_cast<const u32x4*>(kv_scales);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
   char* ws = static_cast<char*>(workspace);
@@ -895,7 +907,7 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
   a.scale_log2 = fabsf(scale) * 1.4426950408889634f;
   if (!(a.scale_log2 > 0.f)) a.scale_log2 = 1.17549435e-38f;
   const unsigned grid = (unsigned)((int64_t)B * a.qtiles * a.splits * Hkv);
-  if (kv_scales)
+  if (k_scales)
     hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);
   else
     hipLaunchKernelGGL(prefill_kernel<false>, dim3(grid), dim3(kWaves * kWave), 0, stream, a);

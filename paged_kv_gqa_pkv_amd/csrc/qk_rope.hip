@@ -53,7 +53,7 @@ struct QkRopeArgs {
   const int32_t* cu_new;       // [B+1]
   const int32_t* ctx_lens;     // [B]
   int32_t* slots;              // [T] out (may be null)
-  u32x4* k_cache;              // bf16 [num_blocks][Hkv][16][D]
+  u32x4* k_cache;              // bf16 [num_blocks][16][Hkv][D]
   u32x4* v_cache;
   int B, max_blocks, T, num_blocks, Hq, Hkv, max_pos;
   float eps;
@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeAr
     if (j >= a.Hq + a.Hkv) {                 // v: a bit copy into the page slot
       const int h = j - a.Hq - a.Hkv;
       if (slot >= 0 && p >= 0 && p < a.max_pos) {
-        const int64_t row = ((slot / kPage) * a.Hkv + h) * kPage + (slot % kPage);
+        const int64_t row = slot * a.Hkv + h;   // (page, slot) then KV head
         a.v_cache[row * 16 + sub] = a.v_in[((int64_t)t * a.Hkv + h) * 16 + sub];
       }
       continue;
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_append_kernel(const QkRopeAr
     if (is_q) {
       reinterpret_cast<u32x4*>(a.q_out)[((int64_t)t * a.Hq + h) * 16 + sub] = ov;
     } else if (slot >= 0 && pos_ok) {
-      const int64_t row = ((slot / kPage) * a.Hkv + h) * kPage + (slot % kPage);
+      const int64_t row = slot * a.Hkv + h;
       a.k_cache[row * 16 + sub] = ov;
     }
   }

@@ -22,7 +22,9 @@ Values: fp32 N(0,1) samples rounded to bf16 by round-to-nearest-even (the
 torch ``.to(torch.bfloat16)`` cast).  Unused pages and the unwritten tail
 slots of each sequence's pages hold the bf16 quiet-NaN canary 0x7FC0, so any
 read of a slot the method must not read poisons the result.  Pools are
-generated in the library's head-major page order [num_blocks][Hkv][16][D].
+generated in the pages' token-major order [num_blocks][16][Hkv][D] (the
+per-layer slice of the Module 12 listing's [n_layers, capacity, 16,
+n_kv_heads, head_dim]).
 
 Seeds: stream ``k`` of layer ``l`` of a workload with base seed ``s`` uses
 ``s * 1_000_000 + l * 100 + k``.  Streams: 0 context lengths, 1 placement,
@@ -253,7 +255,7 @@ def page_fill_counts(w: Workload, t: Tables) -> torch.Tensor:
 @dataclasses.dataclass
 class LayerData:
     """One layer's tensors for a step (all on ``device``)."""
-    k_cache: torch.Tensor        # bf16 [num_blocks, Hkv, 16, D] (head-major pages), pre-append
+    k_cache: torch.Tensor        # bf16 [num_blocks, 16, Hkv, D], pre-append
     v_cache: torch.Tensor
     k_new: torch.Tensor          # bf16 [T_total, Hkv, D]
     v_new: torch.Tensor
@@ -262,13 +264,18 @@ class LayerData:
 
 
 def _pool(w: Workload, fill: torch.Tensor, seed: int, device) -> torch.Tensor:
-    shape = (w.num_blocks, w.Hkv, PAGE, w.D)
+    shape = (w.num_blocks, PAGE, w.Hkv, w.D)
     pool = randn_bf16(shape, seed, device)
-    slot = torch.arange(PAGE, device=device).view(1, PAGE)
-    dead = slot >= fill.to(device).view(-1, 1)            # [num_blocks, 16]
     bits = pool.view(torch.int16)
-    bits.masked_fill_(dead.view(w.num_blocks, 1, PAGE, 1), BF16_CANARY_BITS)
+    bits.masked_fill_(_dead_slots(w, fill, device).view(w.num_blocks, PAGE, 1, 1),
+                      BF16_CANARY_BITS)
     return pool
+
+
+def _dead_slots(w: Workload, fill: torch.Tensor, device) -> torch.Tensor:
+    """bool [num_blocks, 16]: slots no sequence has filled before the step."""
+    slot = torch.arange(PAGE, device=device).view(1, PAGE)
+    return slot >= fill.to(device).view(-1, 1)
 
 
 def make_layer(w: Workload, t: Tables, layer: int, device="cpu",
@@ -292,9 +299,10 @@ def make_layer(w: Workload, t: Tables, layer: int, device="cpu",
 @dataclasses.dataclass
 class LayerDataInt8:
     """One layer's tensors for a step over int8 pages (all on ``device``)."""
-    k_codes: torch.Tensor        # int8 [num_blocks, Hkv, 16, D] (head-major pages), pre-append
+    k_codes: torch.Tensor        # int8 [num_blocks, 16, Hkv, D], pre-append
     v_codes: torch.Tensor
-    kv_scales: torch.Tensor      # float32 [num_blocks, Hkv, 8, 2, 2]: slot s at [s % 8][s // 8][K, V]
+    k_scales: torch.Tensor       # float32 [num_blocks, 16, Hkv]
+    v_scales: torch.Tensor
     k_new: torch.Tensor          # bf16 [T_total, Hkv, D]
     v_new: torch.Tensor
     q_decode: Optional[torch.Tensor]
@@ -307,15 +315,15 @@ def _codes(shape, seed, device) -> torch.Tensor:
     return torch.clamp(torch.round(x * CODE_SD), -127, 127).to(torch.int8)
 
 
-def _kv_scales(w: Workload, fill: torch.Tensor, seed: int, device) -> torch.Tensor:
+def _kv_scales(w: Workload, fill: torch.Tensor, seed: int, device):
+    """(k_scales, v_scales), float32 [num_blocks, 16, Hkv] each, drawn as one
+    [2, num_blocks, 16, Hkv] array."""
     g = _gen(seed, device)
-    sc = torch.empty((w.num_blocks, w.Hkv, 8, 2, 2), device=device, dtype=torch.float32)
+    sc = torch.empty((2, w.num_blocks, PAGE, w.Hkv), device=device, dtype=torch.float32)
     sc.uniform_(SCALE_LO, SCALE_HI, generator=g)
-    slot = (torch.arange(8, device=device).view(8, 1) +
-            8 * torch.arange(2, device=device).view(1, 2))          # [8, 2]: slot i + 8 rr
-    dead = slot.view(1, 8, 2) >= fill.to(device).view(-1, 1, 1)       # [num_blocks, 8, 2]
-    sc.view(torch.int32).masked_fill_(dead.view(w.num_blocks, 1, 8, 2, 1), F32_CANARY_BITS)
-    return sc
+    dead = _dead_slots(w, fill, device).view(1, w.num_blocks, PAGE, 1)
+    sc.view(torch.int32).masked_fill_(dead, F32_CANARY_BITS)
+    return sc[0].contiguous(), sc[1].contiguous()
 
 
 def make_layer_int8(w: Workload, t: Tables, layer: int, device="cpu",
@@ -327,11 +335,12 @@ def make_layer_int8(w: Workload, t: Tables, layer: int, device="cpu",
     T = int(t.cu_new[-1])
     n_dec = len(w.decode_seqs)
     n_pre_q = sum(w.seqs[i].new_len for i in w.prefill_seqs)
-    shape = (w.num_blocks, w.Hkv, PAGE, w.D)
+    shape = (w.num_blocks, PAGE, w.Hkv, w.D)
+    k_scales, v_scales = _kv_scales(w, fill, s(S_KSCALE), device)
     return LayerDataInt8(
         k_codes=_codes(shape, s(S_KPOOL), device),
         v_codes=_codes(shape, s(S_VPOOL), device),
-        kv_scales=_kv_scales(w, fill, s(S_KSCALE), device),
+        k_scales=k_scales, v_scales=v_scales,
         k_new=randn_bf16((T, w.Hkv, w.D), s(S_KNEW), device),
         v_new=randn_bf16((T, w.Hkv, w.D), s(S_VNEW), device),
         q_decode=randn_bf16((n_dec, w.Hq, w.D), s(S_QDEC), device) if n_dec else None,
@@ -355,6 +364,6 @@ def bulk_append_inputs(n_tokens: int, num_blocks: int, Hkv: int, D: int, seed: i
     slots = torch.randperm(num_blocks * PAGE, generator=g)[:n_tokens].to(torch.int32)
     k_new = randn_bf16((n_tokens, Hkv, D), seed + 1, device)
     v_new = randn_bf16((n_tokens, Hkv, D), seed + 2, device)
-    pool_k = randn_bf16((num_blocks, Hkv, PAGE, D), seed + 3, device)
-    pool_v = randn_bf16((num_blocks, Hkv, PAGE, D), seed + 4, device)
+    pool_k = randn_bf16((num_blocks, PAGE, Hkv, D), seed + 3, device)
+    pool_v = randn_bf16((num_blocks, PAGE, Hkv, D), seed + 4, device)
     return slots, k_new, v_new, pool_k, pool_v

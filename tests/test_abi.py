@@ -115,25 +115,32 @@ def test_header_documents_each_entry_point():
 
 
 def test_int8_entry_points_reject_bad_arguments(lib):
-    # append: D other than 128, null pointers, same code pool for K and V, nothing to do
-    assert lib.pkv_append_int8(1, 1, 1, 16, 32, 48, 4, 8, 8, 64, 16, NULL) == bd.PKV_EUNSUPPORTED
-    assert lib.pkv_append_int8(1, 1, 1, 16, 32, NULL, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
-    assert lib.pkv_append_int8(1, 1, 1, 16, 16, 48, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
-    assert lib.pkv_append_int8(NULL, NULL, NULL, NULL, NULL, NULL, 0, 8, 8, 128, 16,
+    # append: D other than 128, null scales, same code pool for K and V, same
+    # scale array for K and V, nothing to do
+    assert lib.pkv_append_int8(1, 1, 1, 16, 32, 48, 64, 4, 8, 8, 64, 16,
+                               NULL) == bd.PKV_EUNSUPPORTED
+    assert lib.pkv_append_int8(1, 1, 1, 16, 32, NULL, 64, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_append_int8(1, 1, 1, 16, 32, 48, NULL, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_append_int8(1, 1, 1, 16, 16, 48, 64, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_append_int8(1, 1, 1, 16, 32, 48, 48, 4, 8, 8, 128, 16, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_append_int8(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, 8, 8, 128, 16,
                                NULL) == bd.PKV_OK
     # decode: missing scales, group size 3
-    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, NULL, 5, 6, 2, 16, 8, 128, 16, 32, 4, 64, 0.088,
-                                    NULL, 0, NULL) == bd.PKV_EINVAL
-    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, 5, 5, 6, 2, 24, 8, 128, 16, 32, 4, 64, 0.088,
+    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, NULL, 9, 5, 6, 2, 16, 8, 128, 16, 32, 4, 64,
+                                    0.088, NULL, 0, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, 8, NULL, 5, 6, 2, 16, 8, 128, 16, 32, 4, 64,
+                                    0.088, NULL, 0, NULL) == bd.PKV_EINVAL
+    assert lib.pkv_attn_decode_int8(1, 2, 3, 4, 8, 9, 5, 6, 2, 24, 8, 128, 16, 32, 4, 64, 0.088,
                                     NULL, 0, NULL) == bd.PKV_EUNSUPPORTED
     # prefill: missing scales, D other than 128, context past the table, nothing to do
-    def pre(scales=5, D=128, mcl=64, total_q=8, out=1):
-        return lib.pkv_attn_prefill_chunk_int8(out, 2, 3, 4, 6, scales, 7, 8, 1, total_q, 8, 16,
+    def pre(ks=5, vs=9, D=128, mcl=64, total_q=8, out=1):
+        return lib.pkv_attn_prefill_chunk_int8(out, 2, 3, 4, 6, ks, vs, 7, 8, 1, total_q, 8, 16,
                                                8, D, 16, 32, 4, mcl, 0.088, NULL, 0, NULL)
-    assert pre(scales=NULL) == bd.PKV_EINVAL
+    assert pre(ks=NULL) == bd.PKV_EINVAL
+    assert pre(vs=NULL) == bd.PKV_EINVAL
     assert pre(D=64) == bd.PKV_EUNSUPPORTED
     assert pre(mcl=100) == bd.PKV_EINVAL
-    assert pre(total_q=0, out=NULL, scales=NULL) == bd.PKV_OK
+    assert pre(total_q=0, out=NULL, ks=NULL, vs=NULL) == bd.PKV_OK
 
 
 def test_copy_blocks_rejects_bad_arguments(lib):

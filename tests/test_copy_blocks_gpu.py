@@ -27,10 +27,10 @@ def ids(xs):
 
 def test_copy_layered_bf16_pools():
     L, nb, Hkv, D = 3, 24, 8, 128
-    k = S.randn_bf16((L, nb, Hkv, 16, D), 501).cuda()
-    v = S.randn_bf16((L, nb, Hkv, 16, D), 502).cuda()
+    k = S.randn_bf16((L, nb, 16, Hkv, D), 501).cuda()
+    v = S.randn_bf16((L, nb, 16, Hkv, D), 502).cuda()
     k.view(torch.int16)[1, 7, 0, 0, 0] = 0x7FC1                 # NaN payload
-    k.view(torch.int16)[2, 2, 3, 5, 9] = -32768                  # -0.0
+    k.view(torch.int16)[2, 2, 5, 3, 9] = -32768                  # -0.0
     src, dst = [2, 7, 11], [20, 3, 15]
     want_k = O.copy_blocks_ref(bits(k), src, dst)
     want_v = O.copy_blocks_ref(bits(v), src, dst)
@@ -44,7 +44,7 @@ def test_copy_strided_layers_leave_padding_untouched():
     allocation): only the viewed blocks move; the padding between layers keeps
     its bits."""
     L, nb, Hkv, D = 2, 10, 2, 128
-    full = S.randn_bf16((L, nb + 3, Hkv, 16, D), 503).cuda()
+    full = S.randn_bf16((L, nb + 3, 16, Hkv, D), 503).cuda()
     before = bits(full)
     view = full[:, :nb]
     bd.pkv_copy_blocks(ids([1, 4]), ids([9, 0]), view, layered=True)
@@ -62,17 +62,18 @@ def test_copy_int8_codes_and_scales():
     src, dst = [5, 17, 300], [511, 0, 64]
     want_kc = O.copy_blocks_ref(bits(d.k_codes)[None], src, dst)[0]
     want_vc = O.copy_blocks_ref(bits(d.v_codes)[None], src, dst)[0]
-    want_sc = O.copy_blocks_ref(bits(d.kv_scales)[None], src, dst)[0]
+    want_ks = O.copy_blocks_ref(bits(d.k_scales)[None], src, dst)[0]
+    want_vs = O.copy_blocks_ref(bits(d.v_scales)[None], src, dst)[0]
     bd.pkv_copy_blocks(ids(src), ids(dst), d.k_codes, d.v_codes)
-    bd.pkv_copy_blocks(ids(src), ids(dst), d.kv_scales)
+    bd.pkv_copy_blocks(ids(src), ids(dst), d.k_scales, d.v_scales)
     torch.cuda.synchronize()
     assert np.array_equal(bits(d.k_codes), want_kc) and np.array_equal(bits(d.v_codes), want_vc)
-    assert np.array_equal(bits(d.kv_scales), want_sc)
+    assert np.array_equal(bits(d.k_scales), want_ks) and np.array_equal(bits(d.v_scales), want_vs)
 
 
 def test_copy_skips_pairs_outside_the_pool():
     nb = 6
-    k = S.randn_bf16((nb, 2, 16, 128), 504).cuda()
+    k = S.randn_bf16((nb, 16, 2, 128), 504).cuda()
     before = bits(k)
     bd.pkv_copy_blocks(ids([1, 99, -1, 2]), ids([3, 4, 5, 200]), k)
     torch.cuda.synchronize()
@@ -86,8 +87,8 @@ def test_copy_on_write_fork_then_append_and_decode():
     and decode.  a's pages keep their bits except the slot a wrote; each
     output matches the oracle on its own table."""
     Hq, Hkv, D, nb = 16, 8, 128, 12
-    k = S.randn_bf16((nb, Hkv, 16, D), 505).cuda()
-    v = S.randn_bf16((nb, Hkv, 16, D), 506).cuda()
+    k = S.randn_bf16((nb, 16, Hkv, D), 505).cuda()
+    v = S.randn_bf16((nb, 16, Hkv, D), 506).cuda()
     ta, tb = [4, 9, 2], [4, 9, 7]                     # page 7 <- copy of a's tail page 2
     bd.pkv_copy_blocks(ids([2]), ids([7]), k, v)
     torch.cuda.synchronize()
@@ -99,8 +100,8 @@ def test_copy_on_write_fork_then_append_and_decode():
     assert slots == [2 * 16 + 8, 7 * 16 + 8]
     kn = S.randn_bf16((2, Hkv, D), 507).cuda()
     vn = S.randn_bf16((2, Hkv, D), 508).cuda()
-    pages_k = lambda: bits(k.transpose(1, 2)).view(np.uint16)       # the pages' token-major order
-    pages_v = lambda: bits(v.transpose(1, 2)).view(np.uint16)
+    pages_k = lambda: bits(k).view(np.uint16)
+    pages_v = lambda: bits(v).view(np.uint16)
     kc0, vc0 = pages_k(), pages_v()
     sm = torch.empty(2, dtype=torch.int32, device="cuda")
     bd.pkv_slot_mapping(sm, tables.cuda(), cu.cuda(), ctx.cuda())
@@ -121,5 +122,5 @@ def test_copy_on_write_fork_then_append_and_decode():
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
     # the fork's copy differs from a's page only in the slot each one wrote
     ka, kb = kc[2], kc[7]
-    diff = np.any(ka != kb, axis=(1, 2))
+    diff = np.any(ka != kb, axis=(1, 2))             # per slot
     assert diff.tolist() == [i == 8 for i in range(16)]

@@ -23,10 +23,6 @@ def u16(t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def pages_order(pool):
-    return u16(pool.transpose(1, 2))
-
-
 def workload(kind):
     if kind == "prefill":
         seqs = [S.SeqSpec(MAX_CTX - 64, 64, True)]
@@ -47,7 +43,7 @@ def test_prefill_at_the_longest_context_bf16():
     w = workload("prefill")
     t = S.make_tables(w)
     d = S.make_layer(w, t, 0, device="cuda")
-    k0, v0 = pages_order(d.k_cache), pages_order(d.v_cache)
+    k0, v0 = u16(d.k_cache), u16(d.v_cache)
     plan = ST.plan_step(w, t)
     assert bd.pkv_prefill_workspace_bytes(1, 64, 32, 8, 128, MAX_CTX) > 0
     out = torch.empty_like(d.q_prefill)
@@ -75,22 +71,22 @@ def test_prefill_at_the_longest_context_int8():
     w = workload("prefill")
     t = S.make_tables(w)
     d = S.make_layer_int8(w, t, 0, device="cuda")
+    # the oracle starts from the pre-append pools and appends on its own
+    kc0, vc0 = d.k_codes.cpu().numpy(), d.v_codes.cpu().numpy()
+    ks0, vs0 = d.k_scales.cpu().numpy(), d.v_scales.cpu().numpy()
     plan = ST.plan_step(w, t)
     ST.slot_mapping(plan)
-    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.kv_scales)
+    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.k_scales,
+                       d.v_scales)
     out = torch.empty_like(d.q_prefill)
     bd.pkv_attn_prefill_chunk_int8(out, d.q_prefill, plan.cu_q, d.k_codes, d.v_codes,
-                                   d.kv_scales, plan.bt_prefill, plan.ctx_prefill,
+                                   d.k_scales, d.v_scales, plan.bt_prefill, plan.ctx_prefill,
                                    plan.max_q_len, plan.max_ctx_prefill, plan.scale,
                                    workspace=plan.prefill_workspace)
     torch.cuda.synchronize()
-    # the oracle reads the pools after the GPU's append (its bit-exactness is
-    # checked elsewhere); the pages' order: codes [nb][16][Hkv][D], scales [nb][16][Hkv]
-    kc = d.k_codes.transpose(1, 2).contiguous().cpu().numpy()
-    vc = d.v_codes.transpose(1, 2).contiguous().cpu().numpy()
-    per_slot = d.kv_scales.cpu().permute(0, 3, 2, 1, 4).reshape(w.num_blocks, 16, 8, 2)
-    ks, vs = per_slot[..., 0].contiguous().numpy(), per_slot[..., 1].contiguous().numpy()
     bt = t.block_tables.tolist()
+    slots = O.slot_ref(bt, t.cu_new.tolist(), t.context_lens.tolist())
+    kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, u16(d.k_new), u16(d.v_new), slots)
     K = Q.gather_int8_ref(kc, ks, bt[0], MAX_CTX).astype(np.float64)
     V = Q.gather_int8_ref(vc, vs, bt[0], MAX_CTX).astype(np.float64)
     q, got = u16(d.q_prefill), O.bf16_to_f64(u16(out))
@@ -108,7 +104,7 @@ def test_decode_at_the_longest_context():
     w = workload("decode")
     t = S.make_tables(w)
     d = S.make_layer(w, t, 0, device="cuda")
-    k0, v0 = pages_order(d.k_cache), pages_order(d.v_cache)
+    k0, v0 = u16(d.k_cache), u16(d.v_cache)
     plan = ST.plan_step(w, t)
     assert bd.pkv_decode_num_splits(2, 32, 8, 128, MAX_CTX) > 1
     out = torch.empty_like(d.q_decode)

@@ -27,13 +27,6 @@ def u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def pages_order(pool: torch.Tensor) -> np.ndarray:
-    """A pool in the library's head-major order [num_blocks][Hkv][16][D] as the
-    bits of the pages' token-major order [num_blocks][16][Hkv][D], which the
-    oracle reads (an axis permutation: the same rows, no arithmetic)."""
-    return u16(pool.transpose(1, 2))
-
-
 def as_f64(t: torch.Tensor) -> np.ndarray:
     return O.bf16_to_f64(u16(t))
 
@@ -51,7 +44,7 @@ def oracle_step(w, t, d):
     bt = t.block_tables.numpy().tolist()
     ctx = t.context_lens.numpy().tolist()
     slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
-    kc, vc = O.append_ref(pages_order(d.k_cache), pages_order(d.v_cache), u16(d.k_new),
+    kc, vc = O.append_ref(u16(d.k_cache), u16(d.v_cache), u16(d.k_new),
                           u16(d.v_new), slots)
     scale = O.default_scale(w.D)
     npre = len(w.prefill_seqs)
@@ -84,8 +77,8 @@ def check_workload(w, layer=0):
     plan, dev, out_dec, out_pre = gpu_step(w, t, d)
     slots, kc, vc, dec, pre = oracle_step(w, t, d)
     assert plan.slot_mapping.cpu().numpy().tolist() == slots, "slot mapping differs"
-    assert np.array_equal(pages_order(dev["k_cache"]), kc), "K pool after append differs"
-    assert np.array_equal(pages_order(dev["v_cache"]), vc), "V pool after append differs"
+    assert np.array_equal(u16(dev["k_cache"]), kc), "K pool after append differs"
+    assert np.array_equal(u16(dev["v_cache"]), vc), "V pool after append differs"
     if dec is not None:
         assert_close(out_dec, dec, f"{w.name} decode")
     if pre is not None:
@@ -180,8 +173,8 @@ def test_ctx1_is_exact_value_row():
 
 def test_context_zero_gives_zeros():
     B, Hq, Hkv, D = 3, 16, 8, 128
-    k = S.randn_bf16((8, Hkv, 16, D), 1).cuda()
-    v = S.randn_bf16((8, Hkv, 16, D), 2).cuda()
+    k = S.randn_bf16((8, 16, Hkv, D), 1).cuda()
+    v = S.randn_bf16((8, 16, Hkv, D), 2).cuda()
     q = S.randn_bf16((B, Hq, D), 3).cuda()
     bt = torch.tensor([[0, 1], [2, 3], [4, 5]], dtype=torch.int32, device="cuda")
     ctx = torch.tensor([0, 5, 0], dtype=torch.int32, device="cuda")
@@ -189,7 +182,7 @@ def test_context_zero_gives_zeros():
     bd.pkv_attn_decode(out, q, k, v, bt, ctx, 32, 128 ** -0.5)
     torch.cuda.synchronize()
     assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
-    want = O.decode_ref(u16(q[1:2]), pages_order(k), pages_order(v), [[2, 3]], [5], 128 ** -0.5)
+    want = O.decode_ref(u16(q[1:2]), u16(k), u16(v), [[2, 3]], [5], 128 ** -0.5)
     assert_close(out[1:2], want, "ctx0 neighbour")
 
 
@@ -198,9 +191,9 @@ def test_bulk_append_bit_exact():
     dk, dv = pk.cuda(), pv.cuda()
     bd.pkv_append(k_new.cuda(), v_new.cuda(), slots.cuda(), dk, dv)
     torch.cuda.synchronize()
-    kc, vc = O.append_ref(pages_order(pk), pages_order(pv), u16(k_new), u16(v_new),
+    kc, vc = O.append_ref(u16(pk), u16(pv), u16(k_new), u16(v_new),
                           slots.numpy().tolist())
-    assert np.array_equal(pages_order(dk), kc) and np.array_equal(pages_order(dv), vc)
+    assert np.array_equal(u16(dk), kc) and np.array_equal(u16(dv), vc)
 
 
 def test_slot_mapping_entries_without_a_slot():
@@ -219,8 +212,8 @@ def test_slot_mapping_entries_without_a_slot():
 
 def test_append_skips_negative_slots_and_keeps_bits():
     Hkv, D = 8, 128
-    pk = S.randn_bf16((4, Hkv, 16, D), 5)
-    pv = S.randn_bf16((4, Hkv, 16, D), 6)
+    pk = S.randn_bf16((4, 16, Hkv, D), 5)
+    pv = S.randn_bf16((4, 16, Hkv, D), 6)
     k_new = torch.full((3, Hkv, D), 0x7FC1, dtype=torch.int16).view(torch.bfloat16)  # NaN payload
     k_new.view(torch.int16)[1] = -32768                                              # -0.0
     v_new = S.randn_bf16((3, Hkv, D), 7)
@@ -228,8 +221,8 @@ def test_append_skips_negative_slots_and_keeps_bits():
     dk, dv = pk.cuda(), pv.cuda()
     bd.pkv_append(k_new.cuda(), v_new.cuda(), slots.cuda(), dk, dv)
     torch.cuda.synchronize()
-    kc, vc = O.append_ref(pages_order(pk), pages_order(pv), u16(k_new), u16(v_new), [5, -1, 63])
-    assert np.array_equal(pages_order(dk), kc) and np.array_equal(pages_order(dv), vc)
+    kc, vc = O.append_ref(u16(pk), u16(pv), u16(k_new), u16(v_new), [5, -1, 63])
+    assert np.array_equal(u16(dk), kc) and np.array_equal(u16(dv), vc)
 
 
 def test_determinism_and_placement_invariance():
@@ -258,8 +251,8 @@ def test_invalid_indices_poison_outputs_without_faulting():
     affected outputs NaN; the kernels clamp the address and never read
     outside the pool.  Other sequences are unaffected."""
     Hq, Hkv, D = 16, 8, 128
-    k = S.randn_bf16((8, Hkv, 16, D), 11).cuda()
-    v = S.randn_bf16((8, Hkv, 16, D), 12).cuda()
+    k = S.randn_bf16((8, 16, Hkv, D), 11).cuda()
+    v = S.randn_bf16((8, 16, Hkv, D), 12).cuda()
     q = S.randn_bf16((3, Hq, D), 13).cuda()
     bt = torch.tensor([[0, 1], [2, 999], [3, 4]], dtype=torch.int32, device="cuda")
     ctx = torch.tensor([20, 20, 20], dtype=torch.int32, device="cuda")
@@ -286,12 +279,12 @@ def test_prefill_context_past_the_plan_poisons_that_sequence():
     d = S.make_layer(w, t, 0)
     bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
     slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
-    kc, vc = O.append_ref(pages_order(d.k_cache), pages_order(d.v_cache), u16(d.k_new),
+    kc, vc = O.append_ref(u16(d.k_cache), u16(d.v_cache), u16(d.k_new),
                           u16(d.v_new), slots)
     want0 = O.prefill_ref(u16(d.q_prefill[:64]), [0, 64], kc, vc, bt[:1], ctx[:1],
                           O.default_scale(128))
     to_dev = lambda bits: torch.from_numpy(bits.view(np.int16).copy()).view(
-        torch.bfloat16).transpose(1, 2).contiguous().cuda()
+        torch.bfloat16).cuda()
     q = d.q_prefill.cuda()
     out = torch.zeros_like(q)
     cu = torch.tensor([0, 64, 128], dtype=torch.int32, device="cuda")
@@ -310,7 +303,7 @@ def test_workspace_too_small_is_rejected():
     need = bd.pkv_decode_workspace_bytes(8, 16, 8, 128, 1024)
     assert need > 0
     q = torch.zeros((8, 16, 128), dtype=torch.bfloat16, device="cuda")
-    pool = torch.zeros((w.num_blocks, 8, 16, 128), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((w.num_blocks, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
     bt = torch.zeros((8, 64), dtype=torch.int32, device="cuda")
     ctx = torch.ones(8, dtype=torch.int32, device="cuda")
     ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
@@ -328,7 +321,7 @@ def _sampled_full_size(name, samples):
     t = S.make_tables(w)
     fill = S.page_fill_counts(w, t)
     d = S.make_layer(w, t, 0, device="cuda", fill=fill)
-    k_pre, v_pre = pages_order(d.k_cache), pages_order(d.v_cache)
+    k_pre, v_pre = u16(d.k_cache), u16(d.v_cache)
     plan = ST.plan_step(w, t)
     out = torch.empty_like(d.q_decode)
     ST.slot_mapping(plan)
@@ -356,7 +349,7 @@ def _sampled_full_size(name, samples):
     assert np.all(np.isfinite(got))
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
     # appended rows landed bit-exactly
-    dk = pages_order(d.k_cache)
+    dk = u16(d.k_cache)
     for tkn, s in enumerate(slots):
         assert np.array_equal(dk[s // 16, s % 16], kn[tkn])
 

@@ -26,18 +26,9 @@ def u16(t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def codes_pages_order(codes):
-    """Device codes [nb][Hkv][16][D] -> the pages' order [nb][16][Hkv][D]."""
-    return codes.detach().transpose(1, 2).contiguous().cpu().numpy()
-
-
-def scales_pages_order(kv_scales):
-    """Device scales [nb][Hkv][8][2][2] (slot s at [s % 8][s // 8]) -> the
-    pages' two arrays ks, vs [nb][16][Hkv] (axis permutations only)."""
-    sc = kv_scales.detach().cpu()
-    nb, hkv = sc.shape[0], sc.shape[1]
-    per_slot = sc.permute(0, 3, 2, 1, 4).reshape(nb, 16, hkv, 2)   # [nb][rr][i] -> slot i + 8 rr
-    return per_slot[..., 0].contiguous().numpy(), per_slot[..., 1].contiguous().numpy()
+def host(t):
+    """A device pool (codes or scales) as a numpy array, same order."""
+    return t.detach().contiguous().cpu().numpy()
 
 
 def check_close(got, want, what):
@@ -55,21 +46,21 @@ def run_int8_step(w, layer=0):
     print(f"[int8 parity] {w.name} layer {layer}: {w.description}", flush=True)
     t = S.make_tables(w)
     d = S.make_layer_int8(w, t, layer, device="cuda")
-    kc0, vc0 = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
-    ks0, vs0 = scales_pages_order(d.kv_scales)
+    kc0, vc0 = host(d.k_codes), host(d.v_codes)
+    ks0, vs0 = host(d.k_scales), host(d.v_scales)
     plan = ST.plan_step(w, t)
     ST.slot_mapping(plan)
-    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.kv_scales)
+    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.k_scales, d.v_scales)
     out = out_pre = None
     if w.decode_seqs:
         out = torch.empty_like(d.q_decode)
-        bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.kv_scales,
+        bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.k_scales, d.v_scales,
                                 plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode, plan.scale,
                                 workspace=plan.workspace)
     if w.prefill_seqs:
         out_pre = torch.empty_like(d.q_prefill)
         bd.pkv_attn_prefill_chunk_int8(out_pre, d.q_prefill, plan.cu_q, d.k_codes, d.v_codes,
-                                       d.kv_scales, plan.bt_prefill, plan.ctx_prefill,
+                                       d.k_scales, d.v_scales, plan.bt_prefill, plan.ctx_prefill,
                                        plan.max_q_len, plan.max_ctx_prefill, plan.scale,
                                        workspace=plan.prefill_workspace)
     torch.cuda.synchronize()
@@ -77,8 +68,8 @@ def run_int8_step(w, layer=0):
     ctx = t.context_lens.numpy().tolist()
     slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
     kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, u16(d.k_new), u16(d.v_new), slots)
-    gk, gv = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
-    gks, gvs = scales_pages_order(d.kv_scales)
+    gk, gv = host(d.k_codes), host(d.v_codes)
+    gks, gvs = host(d.k_scales), host(d.v_scales)
     assert np.array_equal(gk, kc) and np.array_equal(gv, vc), "codes after append differ"
     assert np.array_equal(gks.view(np.uint32), ks.view(np.uint32)), "K scales differ"
     assert np.array_equal(gvs.view(np.uint32), vs.view(np.uint32)), "V scales differ"
@@ -153,17 +144,18 @@ def test_int8_append_bulk_bit_exact_with_edge_rows():
     k[1, :, 5] = 300.0
     k[2] *= 1e-6
     k_new = k.to(torch.bfloat16)
-    kc = torch.zeros((nb, Hkv, 16, D), dtype=torch.int8, device="cuda")
+    kc = torch.zeros((nb, 16, Hkv, D), dtype=torch.int8, device="cuda")
     vc = torch.zeros_like(kc)
-    sc = torch.ones((nb, Hkv, 8, 2, 2), dtype=torch.float32, device="cuda")
-    bd.pkv_append_int8(k_new.cuda(), v_new.cuda(), slots.cuda(), kc, vc, sc)
+    ks = torch.ones((nb, 16, Hkv), dtype=torch.float32, device="cuda")
+    vs = torch.ones_like(ks)
+    bd.pkv_append_int8(k_new.cuda(), v_new.cuda(), slots.cuda(), kc, vc, ks, vs)
     torch.cuda.synchronize()
     ks0 = np.ones((nb, 16, Hkv), np.float32)
     z = np.zeros((nb, 16, Hkv, D), np.int8)
     okc, ovc, oks, ovs = Q.append_int8_ref(z, z, ks0, ks0, u16(k_new), u16(v_new),
                                            slots.numpy().tolist())
-    gks, gvs = scales_pages_order(sc)
-    assert np.array_equal(codes_pages_order(kc), okc) and np.array_equal(codes_pages_order(vc), ovc)
+    gks, gvs = host(ks), host(vs)
+    assert np.array_equal(host(kc), okc) and np.array_equal(host(vc), ovc)
     assert np.array_equal(gks.view(np.uint32), oks.view(np.uint32))
     assert np.array_equal(gvs.view(np.uint32), ovs.view(np.uint32))
 
@@ -172,17 +164,18 @@ def test_int8_append_skips_negative_slots():
     Hkv, D, nb = 8, 128, 4
     k_new = S.randn_bf16((3, Hkv, D), 41).cuda()
     v_new = S.randn_bf16((3, Hkv, D), 42).cuda()
-    kc = torch.full((nb, Hkv, 16, D), 7, dtype=torch.int8, device="cuda")
+    kc = torch.full((nb, 16, Hkv, D), 7, dtype=torch.int8, device="cuda")
     vc = kc.clone()
-    sc = torch.full((nb, Hkv, 8, 2, 2), 0.5, dtype=torch.float32, device="cuda")
+    ks = torch.full((nb, 16, Hkv), 0.5, dtype=torch.float32, device="cuda")
+    vs = ks.clone()
     slots = torch.tensor([5, -1, 63], dtype=torch.int32, device="cuda")
-    bd.pkv_append_int8(k_new, v_new, slots, kc, vc, sc)
+    bd.pkv_append_int8(k_new, v_new, slots, kc, vc, ks, vs)
     torch.cuda.synchronize()
     ks0 = np.full((nb, 16, Hkv), 0.5, np.float32)
     c0 = np.full((nb, 16, Hkv, D), 7, np.int8)
     okc, ovc, oks, ovs = Q.append_int8_ref(c0, c0, ks0, ks0, u16(k_new), u16(v_new), [5, -1, 63])
-    gks, gvs = scales_pages_order(sc)
-    assert np.array_equal(codes_pages_order(kc), okc) and np.array_equal(codes_pages_order(vc), ovc)
+    gks, gvs = host(ks), host(vs)
+    assert np.array_equal(host(kc), okc) and np.array_equal(host(vc), ovc)
     assert np.array_equal(gks, oks) and np.array_equal(gvs, ovs)
 
 
@@ -192,13 +185,13 @@ def _sampled_full_size_int8(name, samples):
     t = S.make_tables(w)
     fill = S.page_fill_counts(w, t)
     d = S.make_layer_int8(w, t, 0, device="cuda", fill=fill)
-    kc0, vc0 = codes_pages_order(d.k_codes), codes_pages_order(d.v_codes)
-    ks0, vs0 = scales_pages_order(d.kv_scales)
+    kc0, vc0 = host(d.k_codes), host(d.v_codes)
+    ks0, vs0 = host(d.k_scales), host(d.v_scales)
     plan = ST.plan_step(w, t)
     out = torch.empty_like(d.q_decode)
     ST.slot_mapping(plan)
-    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.kv_scales)
-    bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.kv_scales, plan.bt_decode,
+    bd.pkv_append_int8(d.k_new, d.v_new, plan.slot_mapping, d.k_codes, d.v_codes, d.k_scales, d.v_scales)
+    bd.pkv_attn_decode_int8(out, d.q_decode, d.k_codes, d.v_codes, d.k_scales, d.v_scales, plan.bt_decode,
                             plan.ctx_decode, plan.max_ctx_decode, plan.scale,
                             workspace=plan.workspace)
     torch.cuda.synchronize()
@@ -208,8 +201,8 @@ def _sampled_full_size_int8(name, samples):
     assert plan.slot_mapping.cpu().numpy().tolist() == slots
     # the oracle's own append (from the pre-append pools) feeds the oracle's attention
     kc, vc, ks, vs = Q.append_int8_ref(kc0, vc0, ks0, vs0, u16(d.k_new), u16(d.v_new), slots)
-    gk = codes_pages_order(d.k_codes)
-    gks, _ = scales_pages_order(d.kv_scales)
+    gk = host(d.k_codes)
+    gks, _ = host(d.k_scales), host(d.v_scales)
     for s_ in slots:                  # appended rows landed bit-exactly
         assert np.array_equal(gk[s_ // 16, s_ % 16], kc[s_ // 16, s_ % 16])
         assert np.array_equal(gks[s_ // 16, s_ % 16].view(np.uint32),

@@ -4,7 +4,7 @@ the register and will not take it as a clobber).  That is sound only while
 nothing else in those kernels uses m0.  This CPU test compiles prefill.hip to
 gfx950 assembly with the library's flags and checks that every mention of m0
 is one of those `s_mov_b32 m0, sN` immediately followed by its
-global_load_lds_dwordx4, and that no instruction which reads m0 implicitly
+global_load_lds_dword(x4), and that no instruction which reads m0 implicitly
 (movrel, sendmsg, GWS, ordered count, append/consume, addtid, interpolation,
 buffer->LDS loads) appears."""
 import os
@@ -49,8 +49,8 @@ def test_m0_only_feeds_the_lds_copies(tmp_path):
         assert not IMPLICIT_M0.match(code), f"implicit m0 user in prefill: {code}"
         if re.search(r"\bm0\b", code):
             assert re.fullmatch(r"s_mov_b32 m0, s\d+", code), f"other use of m0: {code}"
-            assert ins[i + 1].startswith("global_load_lds_dwordx4"), \
+            assert ins[i + 1].startswith("global_load_lds_dword"), \
                 f"m0 set but not used by the next instruction: {code} / {ins[i + 1]}"
             copies += 1
-    n_dma = sum(c.startswith("global_load_lds_dwordx4") for c in ins)
+    n_dma = sum(c.startswith("global_load_lds_dword") for c in ins)
     assert copies > 0 and copies == n_dma, (copies, n_dma)

@@ -57,8 +57,8 @@ def run_case(w, seed):
     qw = (1 + 0.2 * torch.randn(w.D, generator=gen)).to(torch.bfloat16)
     kw = (1 + 0.2 * torch.randn(w.D, generator=gen)).to(torch.bfloat16)
     cos_t, sin_t = tables()
-    kc0 = u16(d.k_cache.transpose(1, 2))
-    vc0 = u16(d.v_cache.transpose(1, 2))
+    kc0 = u16(d.k_cache)
+    vc0 = u16(d.v_cache)
     dk, dv = d.k_cache.cuda(), d.v_cache.cuda()
     q_out = torch.empty((T, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
     sm = torch.full((T,), -7, dtype=torch.int32, device="cuda")
@@ -76,8 +76,8 @@ def run_case(w, seed):
                                       pos, EPS, bf16=True)
     uq = ulps(u16(q_out), q_ref)
     kc_ref, vc_ref = O.append_ref(kc0, vc0, R.bf16_bits(k_ref), u16(v_in), slots)
-    got_k = u16(dk.transpose(1, 2))
-    assert np.array_equal(u16(dv.transpose(1, 2)), vc_ref), "V rows differ"
+    got_k = u16(dk)
+    assert np.array_equal(u16(dv), vc_ref), "V rows differ"
     sl = np.array(slots)
     uk = ulps(got_k[sl // 16, sl % 16], R.bits_to_f32(kc_ref[sl // 16, sl % 16]))
     untouched = np.ones(got_k.shape[:2], bool)
@@ -142,7 +142,7 @@ def test_fused_decode_batch_and_missing_page():
     torch.cuda.synchronize()
     assert sm.cpu().tolist()[2] == -1
     assert torch.isfinite(q_out.float()).all()
-    changed = np.any(u16(dk) != before, axis=(1, 3))      # [block, slot] rows that changed
+    changed = np.any(u16(dk) != before, axis=(2, 3))      # [block, slot] rows that changed
     assert changed.sum() == T - 1
 
 
@@ -180,8 +180,8 @@ def test_fused_positions_beyond_the_tables():
                                   EPS, bf16=True)
     assert ulps(u16(q_out[:2]), q_ref).max() <= 2
     gk, gv = u16(dk), u16(dv)
-    for i, s_ in enumerate(slots):                     # [block][head][slot] rows
+    for i, s_ in enumerate(slots):                     # [block][slot] rows of all heads
         blk, off = divmod(s_, 16)
-        changed_k = not np.array_equal(gk[blk, :, off], k0[blk, :, off])
-        changed_v = not np.array_equal(gv[blk, :, off], v0[blk, :, off])
+        changed_k = not np.array_equal(gk[blk, off], k0[blk, off])
+        changed_v = not np.array_equal(gv[blk, off], v0[blk, off])
         assert changed_k == (i < 2) and changed_v == (i < 2), (i, changed_k, changed_v)

@@ -20,10 +20,6 @@ def u16(t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def pages_order(pool):
-    return u16(pool.transpose(1, 2))
-
-
 def check(got, want, what):
     g = O.bf16_to_f64(u16(got))
     assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
@@ -40,15 +36,15 @@ def ring_setup(pre_lens, new_lens, W, Hkv, seed):
     nb = B * rp + 5
     perm = torch.randperm(nb, generator=torch.Generator().manual_seed(seed))
     tables = perm[:B * rp].view(B, rp).to(torch.int32)
-    k = S.randn_bf16((nb, Hkv, 16, D), seed + 1)
-    v = S.randn_bf16((nb, Hkv, 16, D), seed + 2)
+    k = S.randn_bf16((nb, 16, Hkv, D), seed + 1)
+    v = S.randn_bf16((nb, 16, Hkv, D), seed + 2)
     for b in range(B):
         reached = pre_lens[b] + new_lens[b]
         for idx in range(min(reached, W), W):          # ring slots never written
             page, off = divmod(idx, 16)
             blk = int(tables[b, page])
-            k.view(torch.int16)[blk, :, off] = S.BF16_CANARY_BITS
-            v.view(torch.int16)[blk, :, off] = S.BF16_CANARY_BITS
+            k.view(torch.int16)[blk, off] = S.BF16_CANARY_BITS
+            v.view(torch.int16)[blk, off] = S.BF16_CANARY_BITS
     ctx = torch.tensor([p + n for p, n in zip(pre_lens, new_lens)], dtype=torch.int32)
     cu = torch.cumsum(torch.tensor([0] + list(new_lens)), 0).to(torch.int32)
     T = int(cu[-1])
@@ -60,7 +56,7 @@ def ring_setup(pre_lens, new_lens, W, Hkv, seed):
 def run_ring(pre_lens, new_lens, W, Hq, Hkv, seed, prefill):
     tables, ctx, cu, k, v, kn, vn = ring_setup(pre_lens, new_lens, W, Hkv, seed)
     B = len(pre_lens)
-    kc0, vc0 = pages_order(k), pages_order(v)
+    kc0, vc0 = u16(k), u16(v)
     dk, dv = k.cuda(), v.cuda()
     T = int(cu[-1])
     sm = torch.empty(T, dtype=torch.int32, device="cuda")
@@ -88,7 +84,7 @@ def run_ring(pre_lens, new_lens, W, Hq, Hkv, seed, prefill):
     slots = O.ring_slot_ref(bt, cu.tolist(), ctx.tolist(), W)
     assert sm.cpu().tolist() == slots, "ring slot mapping differs"
     kc, vc = O.append_ref(kc0, vc0, u16(kn), u16(vn), slots)
-    assert np.array_equal(pages_order(dk), kc) and np.array_equal(pages_order(dv), vc)
+    assert np.array_equal(u16(dk), kc) and np.array_equal(u16(dv), vc)
     if prefill:
         want = O.ring_prefill_ref(u16(q), cu.tolist(), kc, vc, bt, ctx.tolist(), W, scale)
     else:

@@ -52,9 +52,9 @@ def test_canaries_mark_unwritten_slots_and_data_is_seeded():
         if page not in used:
             assert fill[page] == 0 and np.all(kb[page] == S.BF16_CANARY_BITS)
         else:
-            assert np.all(kb[page, :, fill[page]:] == S.BF16_CANARY_BITS)
-            assert not np.any(kb[page, :, :fill[page]] == S.BF16_CANARY_BITS)
-    assert kb.shape == (w.num_blocks, w.Hkv, S.PAGE, w.D)   # head-major pages
+            assert np.all(kb[page, fill[page]:] == S.BF16_CANARY_BITS)
+            assert not np.any(kb[page, :fill[page]] == S.BF16_CANARY_BITS)
+    assert kb.shape == (w.num_blocks, S.PAGE, w.Hkv, w.D)   # token-major pages
     assert d1.q_decode.shape == (8, 16, 128) and d1.k_new.shape == (8, 8, 128)
     d3 = S.make_layer(w, t, 1)
     assert not torch.equal(d1.q_decode, d3.q_decode)

@@ -22,15 +22,9 @@ def u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def pages_order(pool: torch.Tensor) -> np.ndarray:
-    """Head-major device pool -> the bits of the pages' token-major order."""
-    return u16(pool.transpose(1, 2))
-
-
-def from_pages_order(bits: np.ndarray) -> torch.Tensor:
-    """The oracle's token-major pool bits -> a head-major device pool."""
-    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
-    return t.transpose(1, 2).contiguous().cuda()
+def to_device(bits: np.ndarray) -> torch.Tensor:
+    """The oracle's pool bits -> a device pool (the same token-major order)."""
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
 
 
 def _case(name, ctxs, Hq, Hkv, num_blocks, seed):
@@ -41,10 +35,10 @@ def _case(name, ctxs, Hq, Hkv, num_blocks, seed):
     d = S.make_layer(w, t, 0)
     bt, ctx = t.block_tables.numpy().tolist(), t.context_lens.numpy().tolist()
     slots = O.slot_ref(bt, t.cu_new.numpy().tolist(), ctx)
-    kc, vc = O.append_ref(pages_order(d.k_cache), pages_order(d.v_cache), u16(d.k_new),
+    kc, vc = O.append_ref(u16(d.k_cache), u16(d.v_cache), u16(d.k_new),
                           u16(d.v_new), slots)
     want = O.decode_ref(u16(d.q_decode), kc, vc, bt, ctx, O.default_scale(128))
-    return dict(q=d.q_decode.cuda(), k=from_pages_order(kc), v=from_pages_order(vc),
+    return dict(q=d.q_decode.cuda(), k=to_device(kc), v=to_device(vc),
                 bt=t.block_tables.cuda(), ctx=t.context_lens.cuda(), max_ctx=max(ctxs),
                 want=want, B=len(ctxs), Hq=Hq, Hkv=Hkv)
 
