@@ -58,6 +58,9 @@ def parse():
                         "mixed step's decode after its chunk (default: each part of a step "
                         "on its own stream, and a mixed step's decode on a second stream, "
                         "concurrent with the chunk)")
+    p.add_argument("--no-fuse", dest="fuse", action="store_false",
+                   help="run a decode-only step's layers as pkv_append + pkv_attn_decode "
+                        "(default: one pkv_attn_decode_append call per layer, bf16 pages)")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--kernels", action="store_true",
@@ -223,6 +226,9 @@ class Part:
         self.kv = kv
         nd = len(w.decode_seqs)
         self.dec_bytes = decode_bytes(w, t, w.decode_seqs, kv) if nd else 0
+        # the timed decode launch: a fused call also writes the step's K/V rows
+        # (read from the new rows in place of the pool: the same bytes)
+        self.launch_bytes = self.dec_bytes + (nd * 2 * w.Hkv * w.D * 2 if plan.fused else 0)
         self.pre_bytes, self.pre_flops = prefill_work(w, t)
         self.step_bytes = slot_bytes(w, t) + w.n_layers * (append_bytes(w, t, kv) +
                                                            self.dec_bytes + self.pre_bytes)
@@ -255,7 +261,7 @@ def _layers(w, t, rotate_mib, device, kv="bf16"):
     return layers, copies
 
 
-def build_parts(name, rotate_mib, device, kv="bf16"):
+def build_parts(name, rotate_mib, device, kv="bf16", fuse=True):
     """Returns (parts, schedule): schedule(i) lists the parts step i runs."""
     import torch
     from paged_kv_gqa_pkv_amd import step as ST
@@ -267,8 +273,8 @@ def build_parts(name, rotate_mib, device, kv="bf16"):
             w = S.workload(sub)
             t = S.make_tables(w)
             layers, copies = _layers(w, t, rotate_mib, device, kv)
-            parts.append(Part(w, t, ST.plan_step(w, t, device=device), layers,
-                              _bufs(w, t, device), copies, kv))
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device, fused=fuse and kv == "bf16"),
+                              layers, _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [0, 1])
     if name == "c5":
         base_w = S.workload("c5", 5)
@@ -288,8 +294,8 @@ def build_parts(name, rotate_mib, device, kv="bf16"):
     w = S.workload(name)
     t = S.make_tables(w)
     layers, copies = _layers(w, t, rotate_mib, device, kv)
-    return [Part(w, t, ST.plan_step(w, t, device=device), layers, _bufs(w, t, device),
-                 copies, kv)], (lambda i: [0])
+    return [Part(w, t, ST.plan_step(w, t, device=device, fused=fuse and kv == "bf16"), layers,
+                 _bufs(w, t, device), copies, kv)], (lambda i: [0])
 
 
 WORKLOAD_TEXT = {
@@ -309,7 +315,7 @@ def run(args):
     bd.load()
     device = "cuda"
     torch.cuda.set_device(0)
-    parts, schedule = build_parts(args.workload, args.rotate_mib, device, args.kv)
+    parts, schedule = build_parts(args.workload, args.rotate_mib, device, args.kv, args.fuse)
     stream = torch.cuda.current_stream()
     # A mixed step's decode runs on a second stream, concurrent with the
     # chunk (both only read the pools after the append); default priority.
@@ -327,10 +333,24 @@ def run(args):
         plan, qb = pt.plan, pt.bufs
         c = i % pt.copies
         n_layers = pt.w.n_layers
-        if only is None:
+        if only is None and not plan.fused:
             ST.slot_mapping(plan, stream=stream)
         for l in range(n_layers):
             d = pt.layers[c * n_layers + l]
+            if plan.fused:
+                # decode-only step: the layer's append and decode in one call
+                if record:
+                    if record == "gated":
+                        torch.cuda._sleep(args.gate_cycles)
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+                bd.pkv_attn_decode_append(qb["od"], qb["qd"], qb["kn"], qb["vn"], d.k_cache,
+                                          d.v_cache, plan.bt_decode, plan.ctx_decode,
+                                          plan.max_ctx_decode, plan.scale,
+                                          workspace=plan.workspace, stream=stream)
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+                    dec_events.append((k, e0, e1, 1))
+                continue
             if only is None and pt.kv == "int8":
                 bd.pkv_append_int8(qb["kn"], qb["vn"], plan.slot_mapping, d.k_codes, d.v_codes,
                                    d.k_scales, d.v_scales, stream=stream)
@@ -454,15 +474,16 @@ def run(args):
     roofline, extra = None, {}
     if dec_events:
         durs = [a.elapsed_time(b) * 1e-3 for (_, a, b, _) in dec_events]
-        byts = [parts[k].dec_bytes * n for (k, _, _, n) in dec_events]
+        byts = [parts[k].launch_bytes * n for (k, _, _, n) in dec_events]
         n_launch = sum(n for (_, _, _, n) in dec_events)
         achieved = sum(byts) / sum(durs) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(args.workload if args.kv == "bf16"
                                                 else f"{args.workload}-int8"),
-                    "kernel": ("decode_kernel (pkv_attn_decode)" if args.kv == "bf16"
-                               else "decode_kernel<Int8Page> (pkv_attn_decode_int8)"),
+                    "kernel": ("decode_kernel<Int8Page> (pkv_attn_decode_int8)" if args.kv == "int8"
+                               else "decode_kernel<Bf16Page, append> (pkv_attn_decode_append)"
+                               if parts[0].plan.fused else "decode_kernel (pkv_attn_decode)"),
                     "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / n_launch),
                     "launches": n_launch,
@@ -500,7 +521,9 @@ def run(args):
                ", one stream" if args.one_stream or (len(parts) == 1 and not any(
                    p.plan.n_prefill and p.plan.n_decode for p in parts))
                else ", each part on its own stream" if len(parts) > 1
-               else ", decode on a second stream concurrent with the chunk"))}
+               else ", decode on a second stream concurrent with the chunk") + (
+               "; decode-only layers: one fused append + decode call"
+               if any(p.plan.fused for p in parts) else ""))}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(1e3 * elapsed / args.steps, 5),

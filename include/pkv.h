@@ -167,6 +167,28 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_context_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode with the step's append fused in ([P1] model.py forward: each layer
+ * reads the cached prefix, concatenates the step's own k/v to it, attends,
+ * and writes the step's k/v into the cache).  Every sequence b appends one
+ * token, at position p = context_lens[b] - 1 (context_lens count it, as for
+ * pkv_attn_decode): the call is pkv_append of k_new[b] / v_new[b] into the
+ * slot of p, found from block_tables as pkv_slot_mapping finds it (no row is
+ * written where that gives -1), followed by pkv_attn_decode, with the same
+ * outputs, except that position p's K/V rows are taken from k_new / v_new
+ * instead of being read back from the pool (the same bits).  One launch; no
+ * slot mapping needed.  Same errors, split plan and workspace as
+ * pkv_attn_decode (pkv_decode_workspace_bytes applies unchanged).
+ *   k_new, v_new     bf16 [B][Hkv][D], the step's rows
+ *   k_cache, v_cache the pools, read and written ([num_blocks][16][Hkv][D])
+ */
+int pkv_attn_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Size of the per-GPU array of pkv_attn_decode_noalloc and of its counter
  * region (16 MiB, 64 KiB). */
 #define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)

@@ -27,6 +27,7 @@ SIGNATURES = {
     "pkv_decode_num_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _f, _vp, _c_size, _vp]),
+    "pkv_attn_decode_append": (_c_int, [_vp] * 8 + [_c_int] * 8 + [_f, _vp, _c_size, _vp]),
     "pkv_attn_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                          _c_int, _c_int, _c_int, _c_int, _c_int, _f, _vp]),
     "pkv_prefill_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -178,6 +179,35 @@ def pkv_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                                   _p(context_lens), B, Hq, Hkv, D, bs, nb, block_tables.shape[1],
                                   int(max_context_len), float(scale), ws_ptr, ws_bytes,
                                   _stream(stream)))
+
+
+def pkv_attn_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                           v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: float,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append k_new/v_new [B, Hkv, D] (one token per sequence, at position
+    context_lens[b] - 1) and run decode attention, in one launch."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or \
+            k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape or \
+            block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent shapes")
+    ws_ptr, ws_bytes = _ws(workspace)
+    _check(load().pkv_attn_decode_append(_p(out), _p(q), _p(k_new), _p(v_new), _p(k_cache),
+                                         _p(v_cache), _p(block_tables), _p(context_lens), B, Hq,
+                                         Hkv, D, bs, nb, block_tables.shape[1],
+                                         int(max_context_len), float(scale), ws_ptr, ws_bytes,
+                                         _stream(stream)))
 
 
 def pkv_attn_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,

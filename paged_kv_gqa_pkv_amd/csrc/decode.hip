@@ -45,7 +45,7 @@ namespace {
 #define PKV_DECODE_NT 1            // streaming (non-temporal) K/V loads
 #endif
 #ifndef PKV_DECODE_WG_PER_CU
-#define PKV_DECODE_WG_PER_CU 2     // split planner: workgroups per compute unit
+#define PKV_DECODE_WG_PER_CU 2     // split planner: waves per SIMD the register budget allows
 #endif
 #ifndef PKV_DECODE_MIN_PPW
 #define PKV_DECODE_MIN_PPW 2       // split planner: minimum pages per wave
@@ -53,9 +53,25 @@ namespace {
 #ifndef PKV_DECODE_WG_COST_PAGES
 #define PKV_DECODE_WG_COST_PAGES 3 // split planner: fixed workgroup cost, in page-times
 #endif
+#ifndef PKV_DECODE_MERGE_COST_PAGES
+#define PKV_DECODE_MERGE_COST_PAGES 2  // split planner: fixed cost of the split merge, page-times
+#endif
+#ifndef PKV_DECODE_SPLIT_COST_EIGHTHS
+#define PKV_DECODE_SPLIT_COST_EIGHTHS 8  // split planner: cost per split (its arrival), 1/8 page-time
+#endif
+#ifndef PKV_DECODE_MAX_HG
+#define PKV_DECODE_MAX_HG 1        // most KV heads per workgroup
+#endif
+#ifndef PKV_DECODE_PARTS
+#define PKV_DECODE_PARTS 4         // waves per KV head, splitting its pages
+#endif
+#ifndef PKV_DECODE_WIDE_PPW
+#define PKV_DECODE_WIDE_PPW 16     // pages per wave from which workgroups take two KV heads (0: never)
+#endif
+#ifndef PKV_DECODE_FORCE_PPW
+#define PKV_DECODE_FORCE_PPW 0     // > 0: every plan uses this many pages per wave (tuning)
+#endif
 
-
-constexpr int kWaves = 4;                    // waves per workgroup
 constexpr int kMaxPagesPerWave = 64;         // one VGPR of page ids per wave
 
 __device__ __forceinline__ u32x4 load_kv(const u32x4* p) {
@@ -69,8 +85,10 @@ constexpr float kNegInf = -__builtin_inff();
 
 // Split partials are written and read with agent-coherent accesses (the
 // last split to finish, possibly on another XCD, merges them).
-__device__ __forceinline__ void ws_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void ws_store2(float* p, float lo, float hi) {
+  const uint64_t bits = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 
@@ -83,10 +101,20 @@ struct DecodeArgs {
   const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
+  // Fused append (bf16 pages, no ring): each sequence's newest position,
+  // context_lens[b] - 1, takes its K/V rows from k_new/v_new [B][Hkv][D]
+  // instead of the pool, and the call writes those rows into that position's
+  // slot (k_pool/v_pool are the same pools as k_cache/v_cache).
+  const u32x4* k_new;
+  const u32x4* v_new;
+  u32x4* k_pool;
+  u32x4* v_pool;
   float* ws_ml;                  // [B][Hq][S][2] (m, l), log2 domain
   float* ws_acc;                 // [B][Hq][S][D]
-  int* counters;                 // [B][Hkv] arrivals per (sequence, KV head); zero between calls
+  int* counters;                 // [B][Hkv / heads_per_wg] arrivals per (sequence, head group)
   int B, Hq, Hkv, num_blocks, max_blocks, splits, pages_per_split;
+  int heads_per_wg;              // KV heads per workgroup
+  int parts;                     // waves per KV head, each over 1/parts of the split's pages
   int window;                    // > 0: each sequence's pages form a ring of `window` tokens
   float scale_log2;              // scale * log2(e)
 };
@@ -323,44 +351,77 @@ struct Int8Page {
   }
 };
 
-// Merge two online-softmax states (m in the log2 domain).
-__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float m2, float l2,
-                                            const float* acc2, int n) {
-  const float M = fmaxf(m, m2);
+// One reduce-scatter step of the lane states: exchange with lane ^ (8 << K)
+// (row bit K of the lane), keep the upper half of `in` if that bit is set,
+// else the lower half, merged with the partner's copy of the same half.
+template <int K>
+__device__ __forceinline__ float xchg(float x) {
+  if constexpr (K == 0)
+    return xor8(x);
+  else
+    return shfl_xor(x, 8 << K);
+}
+template <int K, int N>
+__device__ __forceinline__ void rs_step(float& m, float& l, const float (&in)[N],
+                                        float (&out)[N / 2], int r0) {
+  const bool hi = (r0 >> K) & 1;
+  float send[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    send[i] = hi ? in[i] : in[N / 2 + i];
+    out[i] = hi ? in[N / 2 + i] : in[i];
+  }
+  const float mo = xchg<K>(m), lo = xchg<K>(l);
+  const float M = fmaxf(m, mo);
   const float Mu = (M == kNegInf) ? 0.f : M;
-  const float a = fast_exp2(m - Mu), b = fast_exp2(m2 - Mu);
-  l = l * a + l2 * b;
-  for (int d = 0; d < n; ++d) acc[d] = acc[d] * a + acc2[d] * b;
+  const float wa = fast_exp2(m - Mu), wb = fast_exp2(mo - Mu);
+  l = l * wa + lo * wb;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) out[i] = out[i] * wa + xchg<K>(send[i]) * wb;
   m = M;
 }
 
-template <class P, int G, int U>
-__global__ void __launch_bounds__(kWaves * kWave)
+// Workgroup = one (sequence b, context split, group of heads_per_wg KV
+// heads); its heads_per_wg * parts waves are (head hw, page part pw), wave
+// w = pw * heads_per_wg + hw.  Wave (hw, pw) serves KV head g = group *
+// heads_per_wg + hw and its G query heads over part pw of the split's pages
+// (pages_per_split / parts consecutive pages).  The lane states of a wave
+// are merged by a reduce-scatter (each lane ends with two head dims), the
+// parts of a head through LDS.  With splits, the part-0 wave of each head
+// writes its unnormalised (m, l, acc) and the last workgroup of (b, head
+// group) to finish merges the splits; the number of splits is kept small,
+// since arrivals on one counter are serialised by the memory system.
+template <class P, int G, int U, int kMaxWaves, bool kAppend>
+__global__ void __launch_bounds__(kMaxWaves * kWave)
 decode_kernel(const DecodeArgs a) {
-  __shared__ float s_acc[kWaves][G][kD];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ int s_bad[kWaves];
   __shared__ int s_last;
+  __shared__ float s_part[kMaxWaves][G][kWave][2];   // parts > 0: two dims per lane and head
+  __shared__ float s_ml[kMaxWaves][G][2];
+  __shared__ int s_bad[kMaxWaves];
 
-  const int bid = blockIdx.x;                 // ((b * S) + split) * Hkv + g
-  const int g = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
+  const int HG = a.heads_per_wg;
+  const int PW = a.parts;
+  const int n_groups = a.Hkv / HG;
+  const int bid = blockIdx.x;                 // ((b * S) + split) * n_groups + group
+  const int grp = bid % n_groups;
+  const int rest = bid / n_groups;
   const int split = rest % a.splits;
   const int b = rest / a.splits;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = uniform(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int hw = w % HG, pw = w / HG;
+  const int g = grp * HG + hw;
   const int r0 = lane >> 3, c = lane & 7;
   const int S = a.splits;
-  const int ppw = a.pages_per_split / kWaves;  // pages per wave (the plan keeps this exact)
+  const int pps = a.pages_per_split;
+  const int ppw = pps / PW;                   // pages per wave (the plan keeps this exact)
 
   // Everything up to the page loads is independent of the context length, so
   // the length, the page ids and q are fetched in parallel.  The wave's page
-  // range is fixed by the plan; ids past the sequence's last page are fetched
-  // (they lie inside the table row) but never used.
-  const int p0 = split * a.pages_per_split;
-  const int wp0 = p0 + w * ppw;
+  // range is fixed by the plan; ids past the sequence's last page are
+  // fetched (they lie inside the table row) but never used.
+  const int p0 = split * pps;
+  const int wp0 = p0 + pw * ppw;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
   const int my_id = (lane < ppw && wp0 + lane < a.max_blocks) ? bt[wp0 + lane] : 0;
   uint32_t qw[G][8];
@@ -376,18 +437,55 @@ decode_kernel(const DecodeArgs a) {
   const int n_ctx = a.ctx_lens[b];
   const int n = (a.window > 0 && n_ctx > a.window) ? a.window : n_ctx;
   const bool bad_len = n < 0 || n > a.max_blocks * kPage ||
-                       (n + kPage - 1) / kPage > S * a.pages_per_split;
-  const int n_pages = bad_len ? 0 : (n + kPage - 1) / kPage;
-  const int p1 = min(p0 + a.pages_per_split, n_pages);
+                       (n + kPage - 1) / kPage > S * pps;
 
-  if (p0 >= p1) {
+  // Fused append: position n - 1 comes from k_new / v_new (its slot is not
+  // read), and the workgroup whose split holds that position's page (the
+  // last split if the length is past the plan) writes the rows into the slot
+  // and its part-0 waves add the position's key to their state.  The
+  // position's table entry is checked as decode checks every page it reads:
+  // an invalid one poisons the output (and, as in slot mapping, no row is
+  // written).
+  typename P::Regs nrow[1] = {};
+  const int n_cache = (kAppend && n >= 1) ? n - 1 : n;
+  const int n_pages = bad_len ? 0 : (n_cache + kPage - 1) / kPage;
+  const int ns = (n_pages + pps - 1) / pps;     // splits holding cached pages
+  // the split owning the new position (-1: none); it is >= ns - 1, since the
+  // new position's page is at or after the last cached page
+  const int app_split =
+      (kAppend && n_ctx >= 1) ? min(((n_ctx - 1) / kPage) / pps, S - 1) : -1;
+  const bool owns_new = kAppend && !bad_len && split == app_split;   // uniform
+  // splits that contribute: 0 .. nsplit - 1
+  const int nsplit = (kAppend && !bad_len && app_split >= 0) ? max(ns, app_split + 1) : ns;
+  const bool has_new = owns_new && pw == 0;
+  bool new_bad = false;
+  if constexpr (kAppend) {
+    if (split == app_split && pw == 0) {
+      const u32x4* kn = a.k_new + ((int64_t)b * a.Hkv + g) * 16;
+      const u32x4* vn = a.v_new + ((int64_t)b * a.Hkv + g) * 16;
+      nrow[0].k[0][0] = kn[c]; nrow[0].k[0][1] = kn[c + 8];
+      nrow[0].v[0][0] = vn[c]; nrow[0].v[0][1] = vn[c + 8];
+      const int tp = (n_ctx - 1) / kPage;
+      const int id = tp < a.max_blocks ? bt[tp] : -1;
+      new_bad = !(id >= 0 && id < a.num_blocks);
+      // lanes 0..7 (r0 = 0) hold chunks c and c + 8 of the new rows
+      if (!new_bad && id < kMaxSlotBlocks && r0 == 0) {
+        const int64_t slot = (int64_t)id * kPage + (n_ctx - 1) % kPage;
+        u32x4* kd = a.k_pool + (slot * a.Hkv + g) * 16;
+        u32x4* vd = a.v_pool + (slot * a.Hkv + g) * 16;
+        kd[c] = nrow[0].k[0][0]; kd[c + 8] = nrow[0].k[0][1];
+        vd[c] = nrow[0].v[0][0]; vd[c + 8] = nrow[0].v[0][1];
+      }
+    }
+  }
+  const int p1 = min(p0 + pps, n_pages);
+
+  const int64_t orow = ((int64_t)b * a.Hq + g * G) * kD;   // this head's first output row
+  if (p0 >= p1 && !owns_new) {
     // Nothing to read.  The first split owns the output of an empty or
     // invalid sequence: zeros for an empty context, NaN for a bad length.
-    if (split == 0) {
-      for (int e = tid; e < G * kD; e += kWaves * kWave) {
-        const int j = e / kD, d = e % kD;
-        a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = bad_len ? 0x7fc0u : 0u;
-      }
+    if (split == 0 && pw == 0) {
+      for (int e = lane; e < G * kD; e += kWave) a.out[orow + e] = bad_len ? 0x7fc0u : 0u;
     }
     return;
   }
@@ -396,9 +494,9 @@ decode_kernel(const DecodeArgs a) {
   // page if it is partial and falls in range.
   const int w0 = min(wp0, p1);
   const int w1 = min(wp0 + ppw, p1);
-  const int n_full = n / kPage;
+  const int n_full = n_cache / kPage;
   const int nfull = max(0, min(w1, n_full) - w0);
-  const bool has_tail = (n % kPage) != 0 && n_full >= w0 && n_full < w1;
+  const bool has_tail = (n_cache % kPage) != 0 && n_full >= w0 && n_full < w1;
 
   float m[G], l[G], acc[G][16];
 #pragma unroll
@@ -409,7 +507,7 @@ decode_kernel(const DecodeArgs a) {
   }
 
   const int id_base = w0 - wp0;               // lane of my_id holding page w0
-  int bad = bad_len ? 1 : 0;
+  int bad = (bad_len || (has_new && new_bad)) ? 1 : 0;
   auto page_id = [&](int j) -> int64_t {
     const int id = __builtin_amdgcn_readlane(my_id, id_base + j);
     const bool ok = id >= 0 && id < a.num_blocks;
@@ -467,107 +565,151 @@ decode_kernel(const DecodeArgs a) {
   if (has_tail) {
     typename P::Regs one[1];
     P::load(one[0], a, page_id(n_full - w0), g, r0, c);
-    P::template process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n % kPage);
+    P::template process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n_cache % kPage);
+  }
+  if constexpr (kAppend) {
+    // the new position as a page whose only valid row is row 0 (lanes 0..7)
+    if (has_new) P::template process<G, 1, true>(nrow, qw, m, l, acc, a.scale_log2, r0, 1);
   }
 
-  // Merge the 8 lane groups (rows) of the wave: lanes xor 8, 16, 32.
+  // Reduce-scatter over the wave's 8 row groups (lane bits r0 = 0..2): at
+  // step k each lane merges half of its accumulators with those of lane
+  // ^ (8 << k) and keeps that half, so after three steps lane (r0, c) holds
+  // the wave's merged state for two head dims, d0 and d0 + 1 of its 16
+  // (P::dim(c, .)), with d0 = 8 (r0 & 1) + 4 ((r0 >> 1) & 1) + 2 (r0 >> 2).
+  float v2[G][2];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    float t[16];
-    float mo = xor8(m[j]), lo = xor8(l[j]);
-#pragma unroll
-    for (int d = 0; d < 16; ++d) t[d] = xor8(acc[j][d]);
-    merge_state(m[j], l[j], acc[j], mo, lo, t, 16);
-#pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
-      mo = shfl_xor(m[j], sh); lo = shfl_xor(l[j], sh);
-#pragma unroll
-      for (int d = 0; d < 16; ++d) t[d] = shfl_xor(acc[j][d], sh);
-      merge_state(m[j], l[j], acc[j], mo, lo, t, 16);
-    }
+    float v8[8], v4[4];
+    rs_step<0, 16>(m[j], l[j], acc[j], v8, r0);
+    rs_step<1, 8>(m[j], l[j], v8, v4, r0);
+    rs_step<2, 4>(m[j], l[j], v4, v2[j], r0);
   }
+  const int d0 = 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2);
+  const int dd = P::dim(c, d0);               // head dims dd, dd + 1
 
-  // Merge the waves through LDS.
-  if (lane < 8) {
+  // Merge the page parts of each head through LDS into its part-0 wave.
+  if (PW > 1) {
+    if (pw > 0) {
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int d = 0; d < 16; ++d) s_acc[w][j][P::dim(c, d)] = acc[j][d];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) { s_m[w][j] = m[j]; s_l[w][j] = l[j]; }
-    s_bad[w] = bad;
-  }
-  __syncthreads();
-
-  int any_bad = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) any_bad |= s_bad[i];
-  const float nan = __builtin_nanf("");
-  for (int e = tid; e < G * kD; e += kWaves * kWave) {
-    const int j = e / kD, d = e % kD;
-    float M = kNegInf;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][j]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      const float f = fast_exp2(s_m[i][j] - Mu);
-      L = __builtin_fmaf(s_l[i][j], f, L);
-      A = __builtin_fmaf(s_acc[i][j][d], f, A);
+      for (int j = 0; j < G; ++j) {
+        s_part[w][j][lane][0] = v2[j][0];
+        s_part[w][j][lane][1] = v2[j][1];
+        if (lane == 0) { s_ml[w][j][0] = m[j]; s_ml[w][j][1] = l[j]; }
+      }
     }
-    const int h = g * G + j;
-    if (S == 1) {
-      const float o = any_bad ? nan : A / L;
-      a.out[((int64_t)b * a.Hq + h) * kD + d] = (uint16_t)f32_to_bf16_bits(o);
+    if (lane == 0) s_bad[w] = bad;
+    __syncthreads();
+    if (pw > 0) {
+      // other waves only take part in the workgroup's barriers from here
+      if (S == 1 || nsplit <= 1) return;
     } else {
-      const int64_t r = ((int64_t)b * a.Hq + h) * S + split;
-      ws_store(a.ws_acc + r * kD + d, any_bad ? nan : A);
-      if (d == 0) {
-        ws_store(a.ws_ml + 2 * r, M);
-        ws_store(a.ws_ml + 2 * r + 1, any_bad ? nan : L);
+      for (int q = 1; q < PW; ++q) {
+        const int wq = q * HG + hw;
+        bad |= s_bad[wq];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float mo = s_ml[wq][j][0], lo = s_ml[wq][j][1];
+          const float M = fmaxf(m[j], mo);
+          const float Mu = (M == kNegInf) ? 0.f : M;
+          const float wa = fast_exp2(m[j] - Mu), wb = fast_exp2(mo - Mu);
+          l[j] = l[j] * wa + lo * wb;
+          v2[j][0] = v2[j][0] * wa + s_part[wq][j][lane][0] * wb;
+          v2[j][1] = v2[j][1] * wa + s_part[wq][j][lane][1] * wb;
+          m[j] = M;
+        }
       }
     }
   }
-  if (S == 1) return;
 
-  // Split path: the last of the sequence's non-empty splits to finish merges
-  // all of them, in split order (identical whichever split finishes last).
-  // The partials above were written with agent-coherent stores; waiting for
+  const float nan = __builtin_nanf("");
+  if (S == 1 || nsplit <= 1) {
+    // a single contributing split (split 0): normalise and write the output
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float inv = 1.f / l[j];
+      *reinterpret_cast<uint32_t*>(a.out + orow + j * kD + dd) =
+          bad ? 0x7fc07fc0u : pack_bf16x2(v2[j][0] * inv, v2[j][1] * inv);
+    }
+    return;
+  }
+  if (pw == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t r = ((int64_t)b * a.Hq + g * G + j) * S + split;
+      ws_store2(a.ws_acc + r * kD + dd, bad ? nan : v2[j][0], bad ? nan : v2[j][1]);
+      if (lane == 0) ws_store2(a.ws_ml + 2 * r, m[j], bad ? nan : l[j]);
+    }
+  }
+
+  // Split path: the last of the sequence's contributing splits to finish
+  // merges all of them (identical whichever split finishes last).  The
+  // partials above were written with agent-coherent stores; waiting for
   // their completion before the arrival is counted, and an acquire fence
   // (cache invalidate) before reading them back, orders them without an L2
   // writeback.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
-  int* counter = a.counters + (int64_t)b * a.Hkv + g;
-  if (tid == 0)
+  int* counter = a.counters + (int64_t)b * n_groups + grp;
+  if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             ns - 1;
+             nsplit - 1;
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last || pw > 0) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int e = tid; e < G * kD; e += kWaves * kWave) {
-    const int j = e / kD, d = e % kD;
-    const int64_t rs = ((int64_t)b * a.Hq + g * G + j) * S;
-    const float* ml = a.ws_ml + 2 * rs;
-    float M = kNegInf;
-    for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, ml[2 * s2]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, A = 0.f;
-    for (int s2 = 0; s2 < ns; ++s2) {
-      const float f = fast_exp2(ml[2 * s2] - Mu);
-      L = __builtin_fmaf(ml[2 * s2 + 1], f, L);
-      A = __builtin_fmaf(a.ws_acc[(rs + s2) * kD + d], f, A);
+  // Each part-0 wave merges its own head's G query heads, online over
+  // batches of kBatch splits.  A batch's loads all go out together: its
+  // (m, l) pairs (lane u holds split s0 + u) and every lane's two dims of the
+  // partial outputs; then the batch's reference max, the rescale of what the
+  // earlier batches summed, and the weighted sum in split order.  Addresses
+  // past the last split are clamped and weighted 0, so the loads are
+  // unconditional.
+  constexpr int kBatch = 64 / G;              // 2 * kBatch * G = 128 VGPRs of partials
+  float Mr[G], Lr[G], A[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j) { Mr[j] = kNegInf; Lr[j] = 0.f; A[j][0] = A[j][1] = 0.f; }
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    const int cnt = min(kBatch, nsplit - s0);
+    f32x2 mlv[G];
+    f32x2 v[G][kBatch];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t rs = ((int64_t)b * a.Hq + g * G + j) * S + s0;   // first split of the batch
+      mlv[j] = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * (rs + min(lane, cnt - 1)));
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        v[j][u] = *reinterpret_cast<const f32x2*>(a.ws_acc + (rs + min(u, cnt - 1)) * kD + dd);
     }
-    a.out[((int64_t)b * a.Hq + g * G + j) * kD + d] = (uint16_t)f32_to_bf16_bits(A / L);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float ms = lane < cnt ? mlv[j][0] : kNegInf;
+      const float Mn = fmaxf(Mr[j], wave_max(ms));
+      const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+      const float resc = fast_exp2(Mr[j] - Mu);
+      const float wl = lane < cnt ? fast_exp2(ms - Mu) : 0.f;   // weight of split s0 + lane
+      Lr[j] = Lr[j] * resc + wave_sum(lane < cnt ? mlv[j][1] * wl : 0.f);
+      A[j][0] *= resc;
+      A[j][1] *= resc;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float wgt =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+        A[j][0] = __builtin_fmaf(v[j][u][0], wgt, A[j][0]);
+        A[j][1] = __builtin_fmaf(v[j][u][1], wgt, A[j][1]);
+      }
+      Mr[j] = Mn;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float inv = 1.f / Lr[j];
+    *reinterpret_cast<uint32_t*>(a.out + orow + j * kD + dd) =
+        pack_bf16x2(A[j][0] * inv, A[j][1] * inv);
   }
   // Leave the counter at zero for the next call on this workspace.
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (hw == 0 && lane == 0)
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
 
 // Pages held per pipeline stage, by group size (register budget: two stages
 // of U pages, 32 VGPRs per page, next to 16*G accumulators).
@@ -597,10 +739,21 @@ decode_kernel(const DecodeArgs a) {
 #define PKV_DECODE_I8_U_G8 1
 #endif
 
-template <class P, int G, int U>
+// Waves a workgroup may hold: two waves per SIMD (eight per CU) fit the
+// register budget of the G <= 4 kernels (at most 256 VGPRs), one per SIMD the
+// G = 8 kernels.
+constexpr int max_waves_for(int G) { return G >= 8 ? 4 : 8; }
+
+template <class P, int G, int U, bool kAppend = false>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)(a.B * a.Hkv * a.splits);
-  hipLaunchKernelGGL((decode_kernel<P, G, U>), dim3(grid), dim3(kWaves * kWave), 0, stream, a);
+  constexpr int kMaxWaves = max_waves_for(G);
+  const int waves = a.heads_per_wg * a.parts;
+  if (a.heads_per_wg < 1 || a.parts < 1 || waves > kMaxWaves || a.Hkv % a.heads_per_wg ||
+      a.pages_per_split % a.parts || a.pages_per_split / a.parts > kMaxPagesPerWave)
+    return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((int64_t)a.B * a.splits * (a.Hkv / a.heads_per_wg));
+  hipLaunchKernelGGL((decode_kernel<P, G, U, kMaxWaves, kAppend>), dim3(grid),
+                     dim3(waves * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -633,12 +786,16 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
   a.v_scales = v_scales;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
+  a.k_new = a.v_new = nullptr;
+  a.k_pool = a.v_pool = nullptr;
   const bool split = plan.splits > 1;
   a.ws_ml = split ? wsb.ml : nullptr;
   a.ws_acc = split ? wsb.acc : nullptr;
   a.counters = split ? wsb.counters : nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
   a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
+  a.heads_per_wg = plan.heads_per_wg;
+  a.parts = plan.parts;
   a.window = window;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;
@@ -646,14 +803,14 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
 
 // Instantiations by group size G = Hq / Hkv (pages per pipeline stage U by
 // the register budget of each).
-template <class P>
+template <class P, bool kAppend = false>
 hipError_t launch_by_group(const DecodeArgs& a, int G, hipStream_t stream) {
   constexpr bool kI8 = std::is_same<P, Int8Page>::value;
   switch (G) {
-    case 1: return launch_g<P, 1, kI8 ? PKV_DECODE_I8_U_G1 : PKV_DECODE_U_G1>(a, stream);
-    case 2: return launch_g<P, 2, kI8 ? PKV_DECODE_I8_U_G2 : PKV_DECODE_U_G2>(a, stream);
-    case 4: return launch_g<P, 4, kI8 ? PKV_DECODE_I8_U_G4 : PKV_DECODE_U_G4>(a, stream);
-    case 8: return launch_g<P, 8, kI8 ? PKV_DECODE_I8_U_G8 : PKV_DECODE_U_G8>(a, stream);
+    case 1: return launch_g<P, 1, kI8 ? PKV_DECODE_I8_U_G1 : PKV_DECODE_U_G1, kAppend>(a, stream);
+    case 2: return launch_g<P, 2, kI8 ? PKV_DECODE_I8_U_G2 : PKV_DECODE_U_G2, kAppend>(a, stream);
+    case 4: return launch_g<P, 4, kI8 ? PKV_DECODE_I8_U_G4 : PKV_DECODE_U_G4, kAppend>(a, stream);
+    case 8: return launch_g<P, 8, kI8 ? PKV_DECODE_I8_U_G8 : PKV_DECODE_U_G8, kAppend>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -708,44 +865,74 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Split planner.  Work units are (sequence, KV head) pairs; a workgroup of 4
-// waves streams one split of a unit, and PKV_DECODE_WG_PER_CU workgroups fit
-// on a compute unit at once (the kernels' register budget), so the grid runs
-// in "rounds" of num_cus * PKV_DECODE_WG_PER_CU workgroups.  For each split
-// count the planner estimates the time as rounds * (pages per wave + a fixed
-// per-workgroup cost) and keeps the cheapest (fewest splits on ties).
-// Splits are 4*PKV_DECODE_MIN_PPW .. 256 pages long (at most 64 pages per
-// wave: one VGPR of page ids), in multiples of 4 pages (one share per wave).
-// Only host-known sizes enter, so no device->host sync is needed.
+// Split planner.  A workgroup streams one split of one (sequence, head
+// group): heads_per_wg KV heads times `parts` waves per head, each wave over
+// pages_per_split / parts pages.  A compute unit holds max_waves_for(G)
+// waves (times PKV_DECODE_WG_PER_CU / 2, the register budget's two waves per
+// SIMD being the default), so the grid runs in "rounds" of num_cus times
+// the workgroups that fit.  For each split length the planner estimates the
+// time as rounds * (pages per wave + a fixed per-workgroup cost) plus, when
+// the context is split, a merge cost that grows with the number of splits
+// (their arrivals on one counter are serialised), and keeps the cheapest
+// (fewest splits on ties).  Pages per wave are PKV_DECODE_MIN_PPW .. 64 (one
+// VGPR of page ids).  Only host-known sizes enter, so no device->host sync is
+// needed.
 DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus) {
   DecodePlan p{};
+  const int G = max(1, Hq / max(1, Hkv));
+  const int max_waves = max_waves_for(G);
+  int hg = 1;                                 // largest divisor of Hkv within the caps
+  for (int d = 1; d <= min(max_waves, PKV_DECODE_MAX_HG); ++d)
+    if (Hkv % d == 0) hg = d;
+  const int pw = max(1, min(PKV_DECODE_PARTS, max_waves / hg));
+  p.heads_per_wg = hg;
+  p.parts = pw;
   const int max_pages = max(1, (max_context_len + kPage - 1) / kPage);
-  const int units = max(1, B * Hkv);
-  const int64_t slots = (int64_t)PKV_DECODE_WG_PER_CU * max(1, num_cus);
-  const int min_pps = PKV_DECODE_MIN_PPW * kWaves;
-  const int max_pps = kMaxPagesPerWave * kWaves;
-  int best_s = 1, best_pps = 0;
+  const int64_t units = max(1, B * (Hkv / hg));
+  const int wg_per_cu = max(1, max_waves * PKV_DECODE_WG_PER_CU / 2 / (hg * pw));
+  const int64_t slots = (int64_t)wg_per_cu * max(1, num_cus);
+  int best_s = 1, best_ppw = 0;
   int64_t best_cost = -1;
-  int last_pps = -1;
+  int last_ppw = -1;
+  // the G <= 2 kernels reduce pages in pairs: an odd count leaves one alone
+  const int ustep = G <= 2 ? 2 : 1;
   for (int s_try = 1; s_try <= max_pages; ++s_try) {
-    int pps = (max_pages + s_try - 1) / s_try;
-    pps = (pps + kWaves - 1) / kWaves * kWaves;
-    if (pps > max_pps) continue;
-    if (pps < min_pps) pps = min_pps;
-    if (pps == last_pps) continue;
-    last_pps = pps;
-    const int splits = (max_pages + pps - 1) / pps;
-    const int64_t rounds = ((int64_t)units * splits + slots - 1) / slots;
-    const int64_t cost = rounds * (pps / kWaves + PKV_DECODE_WG_COST_PAGES);
-    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_s = splits; best_pps = pps; }
-    if (pps == min_pps) break;
+    int ppw = (max_pages + s_try * pw - 1) / (s_try * pw);
+    ppw = (ppw + ustep - 1) / ustep * ustep;
+    if (ppw > kMaxPagesPerWave) continue;
+    if (ppw < PKV_DECODE_MIN_PPW) ppw = PKV_DECODE_MIN_PPW;
+    if (ppw == last_ppw) continue;
+    last_ppw = ppw;
+    const int splits = (max_pages + ppw * pw - 1) / (ppw * pw);
+    const int64_t rounds = (units * splits + slots - 1) / slots;
+    // in eighths of a page-time
+    const int64_t cost = rounds * (ppw + PKV_DECODE_WG_COST_PAGES) * 8 +
+                         (splits > 1 ? PKV_DECODE_MERGE_COST_PAGES * 8 +
+                                           (int64_t)splits * PKV_DECODE_SPLIT_COST_EIGHTHS
+                                     : 0);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_s = splits; best_ppw = ppw; }
+    if (ppw == PKV_DECODE_MIN_PPW) break;
+  }
+#if PKV_DECODE_FORCE_PPW > 0
+  // tuning builds only: a fixed number of pages per wave
+  best_ppw = min(PKV_DECODE_FORCE_PPW, kMaxPagesPerWave);
+  best_s = (max_pages + best_ppw * pw - 1) / (best_ppw * pw);
+#endif
+  // Long page loops (bandwidth-bound) run faster with two KV heads per
+  // workgroup, whose waves then read two heads' rows of the same pages
+  // together; short ones (latency-bound) spread better over the compute
+  // units with one.  The split length stays as planned.
+  if (PKV_DECODE_WIDE_PPW > 0 && best_ppw >= PKV_DECODE_WIDE_PPW && hg == 1 && Hkv % 2 == 0 &&
+      2 * pw <= max_waves) {
+    hg = 2;
+    p.heads_per_wg = hg;
   }
   p.splits = best_s;
-  p.pages_per_split = best_pps;
+  p.pages_per_split = best_ppw * pw;
   if (best_s > 1) {
     p.ws_ml_bytes = align256((size_t)B * Hq * best_s * 2 * sizeof(float));
     p.ws_acc_bytes = align256((size_t)B * Hq * best_s * kD * sizeof(float));
-    p.ws_counter_bytes = align256((size_t)B * Hkv * sizeof(int));
+    p.ws_counter_bytes = align256((size_t)B * (Hkv / hg) * sizeof(int));
   }
   p.ws_bytes = p.ws_ml_bytes + p.ws_acc_bytes + p.ws_counter_bytes;
   return p;
@@ -762,9 +949,25 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
   return launch_by_group<Bf16Page>(a, Hq / Hkv, stream);
 }
 
+hipError_t launch_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* block_tables,
+                                const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
+                                int max_blocks, float scale, const DecodePlan& plan,
+                                void* workspace, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  DecodeArgs a = make_args(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, ctx_lens, B,
+                           Hq, Hkv, num_blocks, max_blocks, scale, plan,
+                           workspace_buffers(plan, workspace), 0);
+  a.k_new = static_cast<const u32x4*>(k_new);
+  a.v_new = static_cast<const u32x4*>(v_new);
+  a.k_pool = static_cast<u32x4*>(k_cache);
+  a.v_pool = static_cast<u32x4*>(v_cache);
+  return launch_by_group<Bf16Page, true>(a, Hq / Hkv, stream);
+}
+
 bool noalloc_fits(const DecodePlan& plan, int B, int Hkv) {
   if (plan.splits <= 1) return true;
-  return (size_t)B * Hkv * sizeof(int) <= kScratchCounterBytes &&
+  return plan.ws_counter_bytes <= kScratchCounterBytes &&
          plan.ws_ml_bytes + plan.ws_acc_bytes <= PKV_NOALLOC_SCRATCH_BYTES - kScratchCounterBytes;
 }
 

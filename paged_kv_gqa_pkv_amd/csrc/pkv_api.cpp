@@ -410,6 +410,27 @@ int pkv_attn_decode(void* out, const void* q, const void* k_cache, const void* v
                        "pkv_attn_decode");
 }
 
+int pkv_attn_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::DecodePlan plan;
+  bool done = false;
+  int rc = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D,
+                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                        workspace, workspace_bytes, stream, plan, done);
+  if (rc || done) return rc;
+  if (!k_new || !v_new) return fail(PKV_EINVAL, "null pointer argument");
+  if (k_cache == v_cache) return fail(PKV_EINVAL, "k_cache and v_cache must differ");
+  return launch_status(pkv::launch_decode_append(out, q, k_new, v_new, k_cache, v_cache,
+                                                 block_tables, context_lens, B, Hq, Hkv,
+                                                 num_blocks, max_blocks_per_seq, scale, plan,
+                                                 workspace, static_cast<hipStream_t>(stream)),
+                       "pkv_attn_decode_append");
+}
+
 int pkv_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,

@@ -81,6 +81,22 @@ __device__ __forceinline__ Halves halves32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum and max over the 64 lanes of a wave; every lane gets the result.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum8(x);
+  x += xor8(x);
+  x += shfl_xor(x, 16);
+  return x + shfl_xor(x, 32);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  x = fmaxf(x, xor8(x));
+  x = fmaxf(x, shfl_xor(x, 16));
+  return fmaxf(x, shfl_xor(x, 32));
+}
+
 // Signed byte i of w as a float: one SDWA convert.  Written out because the
 // compiler otherwise splits it into a shift and a convert and hoists the
 // shifts of the next page's codes into the current iteration (a register

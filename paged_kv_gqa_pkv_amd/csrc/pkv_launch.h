@@ -36,13 +36,17 @@ hipError_t launch_qk_norm_rope_append(void* q_out, const void* q_in, const void*
                                       int num_blocks, int Hq, int Hkv, float eps,
                                       hipStream_t stream);
 
-// Split plan of a decode call: S splits of pages_per_split pages each.
+// Split plan of a decode call: S splits of pages_per_split pages each, one
+// workgroup per (sequence, split, group of heads_per_wg KV heads) with
+// `parts` waves per head, each over pages_per_split / parts pages.
 struct DecodePlan {
   int splits;
   int pages_per_split;
+  int heads_per_wg;
+  int parts;
   size_t ws_ml_bytes;    // float2 (m, l) [B][Hq][S]
   size_t ws_acc_bytes;   // float [B][Hq][S][D]
-  size_t ws_counter_bytes;  // int [B][Hkv] split arrival counters
+  size_t ws_counter_bytes;  // int [B][Hkv / heads_per_wg] split arrival counters
   size_t ws_bytes;       // total, 0 for a single pass
 };
 
@@ -52,6 +56,16 @@ hipError_t launch_decode(void* out, const void* q, const void* k_cache, const vo
                          const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
                          int Hkv, int num_blocks, int max_blocks, float scale, int window,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+// Decode with the step's append fused in: position context_lens[b] - 1 of
+// each sequence takes its K/V rows from k_new / v_new [B][Hkv][D] (not from
+// the pool), and the call writes them into that position's slot.  Same plan
+// and workspace as launch_decode.
+hipError_t launch_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* block_tables,
+                                const int32_t* ctx_lens, int B, int Hq, int Hkv, int num_blocks,
+                                int max_blocks, float scale, const DecodePlan& plan,
+                                void* workspace, hipStream_t stream);
 
 // Decode with the split buffers in the library's own per-device array
 // (no caller workspace).  noalloc_fits tells whether a plan fits that array.

@@ -8,7 +8,10 @@ layer the step's K/V are written into the pages of every sequence and
 attention reads each sequence's context through its block table (model.py
 forward).  Here the append runs first and attention reads the post-append
 context, which gives the same numbers as the page's read-then-write order
-since the append is a bit copy.
+since the append is a bit copy.  A step with no prefill chunk (every
+sequence appends its one decode token) runs each layer as one fused call,
+pkv_attn_decode_append, which takes the step's own K/V from the new rows and
+writes them into their slots, as the page's forward does.
 
 Host code only marshals arguments: every operation is a library kernel.
 """
@@ -45,6 +48,7 @@ class StepPlan:
     workspace: Optional[torch.Tensor]
     prefill_workspace: Optional[torch.Tensor]
     scale: float
+    fused: bool = False            # decode-only step: one fused append + decode call per layer
 
     @property
     def bt_prefill(self):
@@ -63,7 +67,11 @@ class StepPlan:
         return self.context_lens[self.n_prefill:]
 
 
-def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = None) -> StepPlan:
+def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = None,
+              fused: bool = True) -> StepPlan:
+    """Index data and workspaces of a step.  fused: run a decode-only step as
+    one pkv_attn_decode_append call per layer (else pkv_append, then
+    pkv_attn_decode)."""
     pre, dec = w.prefill_seqs, w.decode_seqs
     if pre != list(range(len(pre))):
         raise ValueError("prefill sequences must come first")
@@ -96,11 +104,14 @@ def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = No
         cu_q=prefill_cu(w).to(device) if pre else None,
         max_q_len=max_q, max_ctx_prefill=max_ctx_pre,
         max_ctx_decode=max_ctx_dec, workspace=ws, prefill_workspace=pws,
-        scale=scale if scale is not None else w.D ** -0.5)
+        scale=scale if scale is not None else w.D ** -0.5,
+        fused=bool(fused and dec and not pre))
 
 
 def slot_mapping(plan: StepPlan, stream=None) -> None:
-    """Slots of the step's new tokens; shared by every layer's append."""
+    """Slots of the step's new tokens; shared by every layer's append (a
+    fused decode-only step finds them inside its decode calls and needs
+    none)."""
     bd.pkv_slot_mapping(plan.slot_mapping, plan.block_tables, plan.cu_new, plan.context_lens,
                         stream=stream)
 
@@ -115,6 +126,11 @@ def layer(plan: StepPlan, k_cache, v_cache, k_new, v_new, q_decode=None, out_dec
     the append and ``stream`` waits for the decode before anything after.
     """
     s = stream if stream is not None else torch.cuda.current_stream()
+    if plan.fused:
+        bd.pkv_attn_decode_append(out_decode, q_decode, k_new, v_new, k_cache, v_cache,
+                                  plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode,
+                                  plan.scale, workspace=plan.workspace, stream=s)
+        return
     bd.pkv_append(k_new, v_new, plan.slot_mapping, k_cache, v_cache, stream=s)
     both = bool(plan.n_prefill and plan.n_decode and decode_stream is not None)
     if both:

@@ -200,3 +200,19 @@ def test_noalloc_decode_rejects_shapes_beyond_its_array(lib):
     assert call(out=7, q=7) == bd.PKV_EINVAL
     assert call(mcl=131073) == bd.PKV_EINVAL                        # beyond the table
     assert call(B=0, out=NULL) == bd.PKV_OK
+
+
+def test_fused_decode_append_rejects_bad_arguments(lib):
+    """pkv_attn_decode_append checks what pkv_attn_decode checks, plus its new
+    rows and two distinct pools."""
+    def call(out=1, q=2, kn=3, vn=4, kc=5, vc=6, B=2, Hq=16, Hkv=8, D=128, bs=16, mb=4, mcl=64):
+        return lib.pkv_attn_decode_append(out, q, kn, vn, kc, vc, 7, 8, B, Hq, Hkv, D, bs, 32,
+                                          mb, mcl, 0.088, NULL, 0, NULL)
+    assert call(kn=NULL) == bd.PKV_EINVAL
+    assert call(vn=NULL) == bd.PKV_EINVAL
+    assert call(kc=9, vc=9) == bd.PKV_EINVAL                       # one pool for K and V
+    assert call(Hq=24) == bd.PKV_EUNSUPPORTED
+    assert call(D=64) == bd.PKV_EUNSUPPORTED
+    assert call(mcl=65) == bd.PKV_EINVAL                            # beyond the table
+    assert call(out=7, q=7) == bd.PKV_EINVAL
+    assert call(B=0, out=NULL, kn=NULL) == bd.PKV_OK

@@ -57,8 +57,8 @@ def oracle_step(w, t, d):
     return slots, kc, vc, dec, pre
 
 
-def gpu_step(w, t, d):
-    plan = ST.plan_step(w, t)
+def gpu_step(w, t, d, fused=True):
+    plan = ST.plan_step(w, t, fused=fused)
     dev = {k: getattr(d, k).cuda() if getattr(d, k) is not None else None
            for k in ("k_cache", "v_cache", "k_new", "v_new", "q_decode", "q_prefill")}
     out_dec = torch.empty_like(dev["q_decode"]) if w.decode_seqs else None
@@ -70,11 +70,13 @@ def gpu_step(w, t, d):
     return plan, dev, out_dec, out_pre
 
 
-def check_workload(w, layer=0):
-    print(f"[parity] {w.name} layer {layer}: {w.description}", flush=True)
+def check_workload(w, layer=0, fused=True):
+    """A decode-only step runs fused (pkv_attn_decode_append) unless fused is
+    False (pkv_append, then pkv_attn_decode)."""
+    print(f"[parity] {w.name} layer {layer} fused={fused}: {w.description}", flush=True)
     t = S.make_tables(w)
     d = S.make_layer(w, t, layer)
-    plan, dev, out_dec, out_pre = gpu_step(w, t, d)
+    plan, dev, out_dec, out_pre = gpu_step(w, t, d, fused)
     slots, kc, vc, dec, pre = oracle_step(w, t, d)
     assert plan.slot_mapping.cpu().numpy().tolist() == slots, "slot mapping differs"
     assert np.array_equal(u16(dev["k_cache"]), kc), "K pool after append differs"
@@ -86,9 +88,10 @@ def check_workload(w, layer=0):
     return plan, dev, out_dec, out_pre
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
-def test_decode_configs(name):
-    check_workload(S.workload(name))
+def test_decode_configs(name, fused):
+    check_workload(S.workload(name), fused=fused)
 
 
 def test_c3_another_layer_and_shared_pages_untouched():
@@ -116,7 +119,7 @@ def test_decode_group_sizes_and_ragged_lengths(G):
     ctxs = [1, 15, 16, 17, 31, 33, 200, 515]
     w = S.custom_workload(f"ragged_G{G}", _seqs_decode(ctxs), Hq=Hkv * G, Hkv=Hkv, D=128,
                           num_blocks=96, base_seed=70 + G)
-    check_workload(w)
+    check_workload(w, fused=False)
 
 
 def test_decode_long_context_many_splits():

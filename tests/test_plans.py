@@ -26,8 +26,9 @@ def test_decode_workspace_covers_the_partials(lib):
         if S == 1:
             assert ws == 0, (B, Hq, Hkv, ctx)
         else:
-            # (m, l) and acc per (sequence, query head, split), one counter per (sequence, KV head)
-            assert ws >= B * Hq * S * (D + 2) * 4 + B * Hkv * 4, (B, Hq, Hkv, ctx, S, ws)
+            # (m, l) and acc per (sequence, query head, split), and at least
+            # one arrival counter per sequence (one per (sequence, head group))
+            assert ws >= B * Hq * S * (D + 2) * 4 + B * 4, (B, Hq, Hkv, ctx, S, ws)
             pages = -(-ctx // 16)
             assert S <= pages, (B, ctx, S)
 
@@ -35,6 +36,10 @@ def test_decode_workspace_covers_the_partials(lib):
 def test_decode_plans_quoted_in_the_measurements(lib):
     assert bd.pkv_decode_num_splits(64, 32, 8, D, 4096) == 1      # c4a: one pass
     assert bd.pkv_decode_num_splits(13, 32, 8, D, 32768) == 9     # c4b: 9 x 228 pages
+    assert bd.pkv_decode_num_splits(8, 16, 8, D, 1024) == 4       # c3: 4 x 16 pages
+    assert bd.pkv_decode_num_splits(8, 16, 8, D, 959) == 4        # c2
+    assert bd.pkv_decode_num_splits(7, 16, 8, D, 1977) == 4       # c5's decode batch
+    assert bd.pkv_decode_num_splits(1, 16, 8, D, 64) == 1         # c1: one pass
 
 
 def test_prefill_workspace_covers_the_partials(lib):

@@ -46,10 +46,14 @@ def test_c5_steps_plan_the_chunk_and_the_decode_batch(lib):
 def test_decode_only_steps(lib):
     p = ST.plan_step(S.workload("c4a"), S.make_tables(S.workload("c4a")), device="cpu")
     assert (p.n_prefill, p.n_decode, p.cu_q, p.prefill_workspace) == (0, 64, None, None)
-    assert p.workspace is None                  # one pass: 64 x 8 workgroups fill the chip
+    assert p.fused                              # one append + decode call per layer
+    assert p.workspace is None                  # one pass: 64 x 8 (sequence, KV head) units
     p = ST.plan_step(S.workload("c4b"), S.make_tables(S.workload("c4b")), device="cpu")
     assert p.workspace is not None              # split context
     assert p.workspace.numel() == bd.pkv_decode_workspace_bytes(13, 32, 8, 128, 32768)
+    p = ST.plan_step(S.workload("c3"), S.make_tables(S.workload("c3")), device="cpu",
+                     fused=False)
+    assert not p.fused
 
 
 def test_step_at_the_budget_is_accepted(lib):
