@@ -72,6 +72,10 @@ def parse():
                         "times then come from graphs of one kernel's launches alone)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 1 GiB device copies (counter calibration under rocprofv3)")
+    p.add_argument("--write-trace-record", nargs=2, metavar=("KERNEL_TRACE_CSV", "LAUNCHES"),
+                   help="CPU only: record the mean duration of the last LAUNCHES decode "
+                        "dispatches (the launches the bench times one by one) from a "
+                        "rocprofv3 --kernel-trace csv of this workload's bench command")
     p.add_argument("--write-traffic-record", nargs=4,
                    metavar=("COPY_FETCH_CSV", "COPY_WRITE_CSV", "FETCH_CSV", "WRITE_CSV"),
                    help="CPU only: build the decode traffic record from rocprofv3 --pmc "
@@ -81,6 +85,7 @@ def parse():
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+TRACE_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_trace.json")
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_gqa_pkv_amd", "csrc", "decode.hip")
 
 
@@ -104,6 +109,63 @@ def measured_traffic(key):
     if not rec or rec.get("decode_source_sha256") != sha:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def _record_key(args):
+    return args.workload + ("" if args.kv == "bf16" else "-int8") + ("" if args.fuse else "-nofuse")
+
+
+def measured_trace(args, bytes_per_launch):
+    """The decode launches' mean duration in the committed rocprofv3 kernel
+    trace of this workload's bench command (profiles/decode_kernel_trace.json),
+    if it was taken on the current decode kernel source; else None."""
+    try:
+        with open(TRACE_RECORD) as f:
+            rec = json.load(f).get("records", {}).get(_record_key(args))
+        sha = _decode_source_sha()
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("decode_source_sha256") != sha:
+        return None
+    us = rec["avg_launch_us"]
+    achieved = bytes_per_launch / (us * 1e-6) / 1e9
+    return {"avg_launch_us": us, "achieved": round(achieved, 1),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "launches": rec["launches"],
+            "source": "rocprofv3 --kernel-trace, " + os.path.relpath(TRACE_RECORD, ROOT)}
+
+
+def write_trace_record(args):
+    """Mean duration of the last LAUNCHES decode dispatches of a rocprofv3
+    kernel trace (csv) of the bench command: the gated eager pass that the
+    bench's HIP events time launch by launch runs last."""
+    import csv
+    import statistics
+    path, n = args.write_trace_record[0], int(args.write_trace_record[1])
+    with open(path) as f:
+        rows = [r for r in csv.DictReader(f) if "decode_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = rows[-n:]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
+    per_grid = {}
+    for r, d in zip(last, durs):
+        per_grid.setdefault(r.get("Grid_Size", r.get("Grid_Size_X", "?")), []).append(d)
+    rec = {"workload": _record_key(args), "decode_source_sha256": _decode_source_sha(),
+           "launches": len(durs), "avg_launch_us": round(statistics.mean(durs), 2),
+           "per_grid": {g: {"dispatches": len(v), "mean_us": round(statistics.mean(v), 2),
+                            "median_us": round(statistics.median(v), 2)}
+                        for g, v in sorted(per_grid.items())},
+           "all_decode_dispatches": len(rows),
+           "command": "rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py "
+                      f"--workload {args.workload} --kv {args.kv}" + ("" if args.fuse else " --no-fuse")}
+    try:
+        with open(TRACE_RECORD) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec.setdefault("records", {})[rec["workload"]] = rec
+    with open(TRACE_RECORD, "w") as f:
+        json.dump(allrec, f, indent=1)
+    print(json.dumps(rec), flush=True)
 
 
 def write_traffic_record(args):
@@ -487,6 +549,7 @@ def run(args):
                     "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / n_launch),
                     "launches": n_launch,
+                    "trace": measured_trace(args, sum(byts) / n_launch),
                     "timing": ("HIP events around each launch of an eager pass after the timed "
                                "graph replays, each launch queued behind a GPU sleep"
                                if args.graph else
@@ -536,10 +599,34 @@ def run(args):
     return out, parts
 
 
-def cpu_baseline(args, parts):
-    """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    one layer of each part of the step (slot mapping, append, attention),
-    repeated until the time budget is spent, scaled to the whole step."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _host_threads():
+    """The host cores this process may use: its affinity set, capped by the
+    thread count the environment grants (OMP_NUM_THREADS, when set)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
+
+
+def _oracle_sample(parts, budget, threads):
+    """Seconds per full step of the oracle (as it stands) with BLAS limited to
+    `threads`: one layer of each part of the step (slot mapping, append,
+    attention), repeated until the part's share of the budget is spent, scaled
+    to all layers.  Returns (seconds per step, description)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -551,8 +638,8 @@ def cpu_baseline(args, parts):
     def u16(x):
         return x.cpu().view(torch.int16).numpy().view(np.uint16)
 
-    per_step, step_b, desc = 0.0, 0, []
-    budget = args.cpu_seconds / len(parts[:2])
+    per_step, desc = 0.0, []
+    share = budget / len(parts[:2])
     for pt in parts[:2]:
         w, t = pt.w, pt.t
         if pt.kv == "int8":
@@ -570,7 +657,7 @@ def cpu_baseline(args, parts):
         npre = len(w.prefill_seqs)
         scale = O.default_scale(w.D)
         reps = 0
-        with threadpool_limits(limits=1):
+        with threadpool_limits(limits=threads):
             t0 = time.perf_counter()
             while True:
                 slots = O.slot_ref(bt, cu, ctx)
@@ -590,15 +677,27 @@ def cpu_baseline(args, parts):
                         O.decode_ref(qd, kc, vc, bt[npre:], ctx[npre:], scale)
                 reps += 1
                 used = time.perf_counter() - t0
-                if used >= budget:
+                if used >= share:
                     break
         per_step += used / reps * w.n_layers
-        step_b += pt.step_bytes
         desc.append(f"{w.name}: {reps} x 1 of {w.n_layers} layers in {used:.1f} s")
-    return {"value": round(step_b / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "; ".join(desc) + f" on 1 host thread (fp64 numpy, BLAS limited to 1 "
-                      f"thread), scaled to {per_step:.1f} s per full step"}
+    return per_step, "; ".join(desc)
+
+
+def cpu_baseline(args, parts):
+    """The CPU oracle (fp64 numpy, as it stands) on a bounded sample of the
+    same workload, scaled to the whole step: on the host cores this process
+    may use (BLAS threads = that count), and on one thread for reference."""
+    step_b = sum(pt.step_bytes for pt in parts[:2])
+    threads = _host_threads()
+    per_step, desc = _oracle_sample(parts, args.cpu_seconds, threads)
+    per_step1, desc1 = _oracle_sample(parts, args.cpu_seconds / 2, 1)
+    return {"value": round(step_b / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "cpu": _cpu_model(),
+            "sample": f"{desc} on {threads} host threads (fp64 numpy, BLAS threads {threads}), "
+                      f"scaled to {per_step:.1f} s per full step",
+            "value_1_thread": round(step_b / per_step1 / 1e9, 4),
+            "sample_1_thread": f"{desc1} on 1 thread, scaled to {per_step1:.1f} s per full step"}
 
 
 def _graph_time(fn, n_variants, reps=40):
@@ -803,6 +902,9 @@ def main():
         sys.exit(2)
     if args.write_traffic_record:
         write_traffic_record(args)
+        return
+    if args.write_trace_record:
+        write_trace_record(args)
         return
     if args.calibrate_copy:
         calibrate_copy()
