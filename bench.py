@@ -815,41 +815,32 @@ def kernel_bench():
     sec = _graph_time(lambda i: dst.copy_(src), 1)
     line("device_copy", sec, 2 << 29, "torch copy of 512 MiB: read and write each byte once")
     del src, dst
-    # chunked prefill on a shape with enough work to fill the chip without key
-    # splits: one 2048-query chunk at positions 6144..8191 (Qwen3-8B heads),
-    # bf16 and int8 pages; reported against the bf16 MFMA peak
-    T, o = 2048, 6144
-    n = o + T
-    nbp = n // 16 + 8
-    perm = torch.randperm(nbp, generator=torch.Generator().manual_seed(8))[:n // 16]
-    btp = perm.view(1, -1).to(torch.int32).to(dev)
-    ctxp = torch.tensor([n], dtype=torch.int32, device=dev)
-    cuq = torch.tensor([0, T], dtype=torch.int32, device=dev)
-    qp = S.randn_bf16((T, Hq, D), 430, dev)
+    # chunked prefill on a large chunk: 2048 queries at positions 6144..8191
+    # (Qwen3-8B heads: 64 row tiles of 128 rows per KV head, 512 in all, which
+    # the planner cuts into 2 key splits), bf16 and int8 pages; reported
+    # against the bf16 MFMA peak
+    c = S.large_chunk_inputs(dev)
+    T, o, n = c["T"], c["offset"], c["n"]
+    btp, ctxp, cuq, qp = c["block_tables"], c["context_lens"], c["cu_q"], c["q"]
     op = torch.empty_like(qp)
-    kp = S.randn_bf16((nbp, 16, Hkv, D), 431, dev)
-    vp = S.randn_bf16((nbp, 16, Hkv, D), 432, dev)
     nws = bd.pkv_prefill_workspace_bytes(1, T, Hq, Hkv, D, n)
     ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev)
     flops = 4 * D * Hq * (T * o + T * (T + 1) // 2)
-    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk(op, qp, cuq, kp, vp, btp, ctxp, T, n,
-                                                          D ** -0.5, workspace=ws), 1)
+    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk(op, qp, cuq, c["k_cache"], c["v_cache"],
+                                                          btp, ctxp, T, n, D ** -0.5,
+                                                          workspace=ws), 1)
     out["prefill_2048x8192"] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 1),
                                 "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
                                 "work": f"one {T}-query causal chunk at positions {o}..{n - 1}, "
                                         f"Hq {Hq} Hkv {Hkv}, {flops / 1e9:.1f} GFLOP"}
-    kc8 = torch.randint(-127, 128, (nbp, 16, Hkv, D), dtype=torch.int8, device=dev)
-    vc8 = torch.randint(-127, 128, (nbp, 16, Hkv, D), dtype=torch.int8, device=dev)
-    ks8 = torch.full((nbp, 16, Hkv), 0.024, dtype=torch.float32, device=dev)
-    vs8 = ks8.clone()
-    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk_int8(op, qp, cuq, kc8, vc8, ks8, vs8,
-                                                               btp, ctxp, T, n, D ** -0.5,
-                                                               workspace=ws), 1)
+    sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk_int8(
+        op, qp, cuq, c["k_codes"], c["v_codes"], c["k_scales"], c["v_scales"], btp, ctxp, T, n,
+        D ** -0.5, workspace=ws), 1)
     out["prefill_int8_2048x8192"] = {"us": round(sec * 1e6, 2),
                                      "TFLOPs": round(flops / sec / 1e12, 1),
                                      "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
                                      "work": "the same chunk over int8 pages"}
-    del kc8, vc8, ks8, vs8, kp, vp
+    del c
     # sliding-window ring paging, a window of 4096 tokens (Module 04 page,
     # section 4): the batch-64 decode of Qwen3-8B heads at position 32768,
     # each sequence reading its last 4096 tokens through a 256-page ring

@@ -367,3 +367,32 @@ def bulk_append_inputs(n_tokens: int, num_blocks: int, Hkv: int, D: int, seed: i
     pool_k = randn_bf16((num_blocks, PAGE, Hkv, D), seed + 3, device)
     pool_v = randn_bf16((num_blocks, PAGE, Hkv, D), seed + 4, device)
     return slots, k_new, v_new, pool_k, pool_v
+
+
+def large_chunk_inputs(device="cpu", T: int = 2048, offset: int = 6144, Hq: int = 32,
+                       Hkv: int = 8, D: int = 128, seed: int = 430) -> dict:
+    """One causal chunk of T queries at positions offset..offset+T-1 of a
+    single sequence (Qwen3-8B-shaped heads by default), its pages scattered
+    over a pool 8 pages larger than the sequence needs: bf16 q and pools, and
+    int8 code pools (N(0, CODE_SD) rounded, clamped to +-127) with float32
+    scales uniform in [SCALE_LO, SCALE_HI], all seeded."""
+    n = offset + T
+    if n % PAGE:
+        raise ValueError("the chunk must end on a page boundary")
+    nbp = n // PAGE + 8
+    perm = torch.randperm(nbp, generator=_gen(seed - 422, "cpu"))[:n // PAGE]
+    scales = torch.empty((2, nbp, PAGE, Hkv), dtype=torch.float32)
+    scales.uniform_(SCALE_LO, SCALE_HI, generator=_gen(seed + 5, "cpu"))
+    return {
+        "T": T, "offset": offset, "n": n, "Hq": Hq, "Hkv": Hkv, "D": D, "num_blocks": nbp,
+        "block_tables": perm.view(1, -1).to(torch.int32).to(device),
+        "context_lens": torch.tensor([n], dtype=torch.int32, device=device),
+        "cu_q": torch.tensor([0, T], dtype=torch.int32, device=device),
+        "q": randn_bf16((T, Hq, D), seed, device),
+        "k_cache": randn_bf16((nbp, PAGE, Hkv, D), seed + 1, device),
+        "v_cache": randn_bf16((nbp, PAGE, Hkv, D), seed + 2, device),
+        "k_codes": _codes((nbp, PAGE, Hkv, D), seed + 3, "cpu").to(device),
+        "v_codes": _codes((nbp, PAGE, Hkv, D), seed + 4, "cpu").to(device),
+        "k_scales": scales[0].contiguous().to(device),
+        "v_scales": scales[1].contiguous().to(device),
+    }

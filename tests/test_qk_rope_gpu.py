@@ -6,8 +6,8 @@ Slots and V rows must be bit-exact.  q and the appended k rows may differ
 from the oracle only through the order of the float32 sum of squares, so
 they are compared in bf16 ulps at the larger of the oracle's value and 0.5
 (the scale of normalised values): at most 2 ulp, and differing in at most
-1 % of the values.  Attention over the resulting pools
-is then checked against the oracle's attention over its own pools.
+1 % of the values.  Attention over the resulting q and pools is then
+checked against the oracle's attention over its own q and pools.
 """
 import numpy as np
 import pytest
@@ -87,14 +87,15 @@ def run_case(w, seed):
         print(f"{w.name} {name}: max {u.max():.2f} ulp, {100 * np.mean(u > 0):.3f} % differ",
               flush=True)
         assert u.max() <= 2 and np.mean(u > 0) <= 0.01, (name, u.max(), np.mean(u > 0))
-    return w, t, q_out, dk, dv, kc_ref, vc_ref
+    return w, t, q_out, dk, dv, R.bf16_bits(q_ref), kc_ref, vc_ref
 
 
 @pytest.mark.parametrize("chunk_step", [0, 5])
 def test_fused_norm_rope_append_mixed_step(chunk_step):
-    w, t, q_out, dk, dv, kc_ref, vc_ref = run_case(S.workload("c5", chunk_step), 900 + chunk_step)
-    # attention over the fused path's pools and q, against the oracle on the
-    # oracle's pools and the GPU's q (q itself was checked above)
+    w, t, q_out, dk, dv, q_ref, kc_ref, vc_ref = run_case(S.workload("c5", chunk_step),
+                                                          900 + chunk_step)
+    # attention over the fused path's q and pools, against the oracle's
+    # attention over the oracle's own rotated q and appended pools
     plan = ST.plan_step(w, t)
     npre = len(w.prefill_seqs)
     Tp = sum(w.seqs[i].new_len for i in w.prefill_seqs)
@@ -107,9 +108,9 @@ def test_fused_norm_rope_append_mixed_step(chunk_step):
                        plan.scale, workspace=plan.workspace)
     torch.cuda.synchronize()
     bt, ctx = t.block_tables.tolist(), t.context_lens.tolist()
-    want_p = O.prefill_ref(u16(qp), S.prefill_cu(w).tolist(), kc_ref, vc_ref, bt[:npre],
+    want_p = O.prefill_ref(q_ref[:Tp], S.prefill_cu(w).tolist(), kc_ref, vc_ref, bt[:npre],
                            ctx[:npre], plan.scale)
-    want_d = O.decode_ref(u16(qd), kc_ref, vc_ref, bt[npre:], ctx[npre:], plan.scale)
+    want_d = O.decode_ref(q_ref[Tp:], kc_ref, vc_ref, bt[npre:], ctx[npre:], plan.scale)
     for got, want, what in ((op, want_p, "prefill"), (od, want_d, "decode")):
         err = np.abs(O.bf16_to_f64(u16(got)) - want)
         print(f"fused step {what}: max abs {err.max():.3e} mean abs {err.mean():.3e}", flush=True)
