@@ -61,6 +61,10 @@ def parse():
     p.add_argument("--no-fuse", dest="fuse", action="store_false",
                    help="run a decode-only step's layers as pkv_append + pkv_attn_decode "
                         "(default: one pkv_attn_decode_append call per layer, bf16 pages)")
+    p.add_argument("--no-mixed", dest="mixed", action="store_false",
+                   help="run a mixed step's attention as pkv_attn_prefill_chunk + "
+                        "pkv_attn_decode (default: one pkv_attn_prefill_decode call per "
+                        "layer, bf16 pages)")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--kernels", action="store_true",
@@ -86,13 +90,19 @@ def parse():
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
 TRACE_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_trace.json")
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_gqa_pkv_amd", "csrc", "decode.hip")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_gqa_pkv_amd", "csrc", f)
+                  for f in ("decode_kernel.h", "decode.hip")]
 
 
 def _decode_source_sha():
+    """SHA-256 over the decode kernel's sources (its device code, then the
+    launchers and planner)."""
     import hashlib
-    with open(DECODE_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(key):
@@ -323,7 +333,7 @@ def _layers(w, t, rotate_mib, device, kv="bf16"):
     return layers, copies
 
 
-def build_parts(name, rotate_mib, device, kv="bf16", fuse=True):
+def build_parts(name, rotate_mib, device, kv="bf16", fuse=True, mixed=True):
     """Returns (parts, schedule): schedule(i) lists the parts step i runs."""
     import torch
     from paged_kv_gqa_pkv_amd import step as ST
@@ -350,7 +360,8 @@ def build_parts(name, rotate_mib, device, kv="bf16", fuse=True):
             new = torch.tensor([0, p.new_len] + [1] * len(w.decode_seqs), dtype=torch.int64)
             t = S.Tables(base_t.block_tables, ctx, torch.cumsum(new, 0).to(torch.int32),
                          torch.tensor([q.pre_len for q in w.seqs], dtype=torch.int32))
-            parts.append(Part(w, t, ST.plan_step(w, t, device=device), layers,
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device,
+                                                 mixed=mixed and kv == "bf16"), layers,
                               _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [i % 6])
     w = S.workload(name)
@@ -377,7 +388,8 @@ def run(args):
     bd.load()
     device = "cuda"
     torch.cuda.set_device(0)
-    parts, schedule = build_parts(args.workload, args.rotate_mib, device, args.kv, args.fuse)
+    parts, schedule = build_parts(args.workload, args.rotate_mib, device, args.kv, args.fuse,
+                                  args.mixed)
     stream = torch.cuda.current_stream()
     # A mixed step's decode runs on a second stream, concurrent with the
     # chunk (both only read the pools after the append); default priority.
@@ -388,7 +400,7 @@ def run(args):
     # instead of each launch's last round running part-empty.
     pstreams = [torch.cuda.Stream() for _ in parts]
     use_events = not args.no_events
-    dec_events, pre_events = [], []
+    dec_events, pre_events, mix_events = [], [], []
 
     def run_part(k, i, record, only=None, stream=None):
         pt = parts[k]
@@ -419,6 +431,22 @@ def run(args):
             elif only is None:
                 bd.pkv_append(qb["kn"], qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache,
                               stream=stream)
+            if plan.mixed and only is None:
+                # the chunk's and the decode's workgroups in one launch
+                if record:
+                    if record == "gated":
+                        torch.cuda._sleep(args.gate_cycles)
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+                bd.pkv_attn_prefill_decode(qb["op"], qb["qp"], plan.cu_q, plan.bt_prefill,
+                                           plan.ctx_prefill, plan.max_q_len, plan.max_ctx_prefill,
+                                           qb["od"], qb["qd"], plan.bt_decode, plan.ctx_decode,
+                                           plan.max_ctx_decode, d.k_cache, d.v_cache, plan.scale,
+                                           prefill_workspace=plan.prefill_workspace,
+                                           decode_workspace=plan.workspace, stream=stream)
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+                    mix_events.append((k, e0, e1, 1))
+                continue
             if plan.n_prefill and only in (None, "prefill"):
                 if record:
                     if record == "gated":
@@ -567,6 +595,32 @@ def run(args):
                                  "kernel": ("prefill_kernel (pkv_attn_prefill_chunk)"
                                             if args.kv == "bf16" else
                                             "prefill_kernel<int8> (pkv_attn_prefill_chunk_int8)")}
+    if mix_events:
+        durs = [a.elapsed_time(b) * 1e-3 for (_, a, b, _) in mix_events]
+        n_launch = sum(n for (_, _, _, n) in mix_events)
+        byts = sum((parts[k].dec_bytes + parts[k].pre_bytes) * n for (k, _, _, n) in mix_events)
+        fl = sum(parts[k].pre_flops * n for (k, _, _, n) in mix_events)
+        achieved = byts / sum(durs) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "mixed_kernel (pkv_attn_prefill_decode)",
+                    "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
+                    "bytes_per_launch": int(byts / n_launch), "launches": n_launch,
+                    "work": "the decode half's K/V, q/out and tables plus the chunk's keys "
+                            "0..o+T-1, q and out, once each",
+                    "trace": None,
+                    "timing": ("HIP events around each launch of an eager pass after the timed "
+                               "graph replays, each launch queued behind a GPU sleep"
+                               if args.graph else
+                               "HIP events around each launch in the timed region")}
+        tflops = fl / sum(durs) / 1e12
+        extra["prefill_mfma"] = {"bound": "mfma", "achieved": round(tflops, 2),
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                 "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
+                                 "launches": n_launch,
+                                 "kernel": "mixed_kernel (pkv_attn_prefill_decode): the chunk's "
+                                           "causal FLOPs over the whole launch, decode included"}
     w0 = parts[0].w
     cfg = {"workload": WORKLOAD_TEXT.get(args.workload, f"{args.workload}: {w0.description}"),
            "parts": [{"name": p.w.name, "layers": p.w.n_layers, "Hq": p.w.Hq, "Hkv": p.w.Hkv,
@@ -581,12 +635,16 @@ def run(args):
            "kv_pages": ("bf16" if args.kv == "bf16" else
                         "int8 codes + float32 (K, V) scale per slot and KV head"),
            "launch": (("HIP graph per step" if args.graph else "eager") + (
-               ", one stream" if args.one_stream or (len(parts) == 1 and not any(
-                   p.plan.n_prefill and p.plan.n_decode for p in parts))
-               else ", each part on its own stream" if len(parts) > 1
-               else ", decode on a second stream concurrent with the chunk") + (
+               ", each part on its own stream"
+               if len(schedule(0)) > 1 and not args.one_stream
+               else ", decode on a second stream concurrent with the chunk"
+               if not args.one_stream and any(p.plan.n_prefill and p.plan.n_decode and
+                                              not p.plan.mixed for p in parts)
+               else ", one stream") + (
                "; decode-only layers: one fused append + decode call"
-               if any(p.plan.fused for p in parts) else ""))}
+               if any(p.plan.fused for p in parts) else "") + (
+               "; mixed layers: append, then one launch for the chunk and the decode"
+               if any(p.plan.mixed for p in parts) else ""))}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(1e3 * elapsed / args.steps, 5),

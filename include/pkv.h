@@ -242,11 +242,13 @@ size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int
  *   max_q_len     host-side upper bound of T_b
  *   max_context_len  host-side upper bound of context_lens (plans key splits)
  *   workspace     device buffer of at least pkv_prefill_workspace_bytes(...)
- *                 bytes (may be NULL when that is 0); it holds the key
- *                 splits' partial results between the attention launch and
- *                 the merge launch that follows it on the stream, so it
- *                 needs no initialisation.  Calls that may overlap in time
- *                 need separate workspaces.
+ *                 bytes (may be NULL when that is 0): the key splits'
+ *                 partial results and one arrival counter per (row tile,
+ *                 KV head).  One launch: the last split of a row tile to
+ *                 finish merges the partials in split order.  The buffer
+ *                 must be zero-filled before its first use; every call
+ *                 leaves its counters back at zero for the next.  Calls
+ *                 that may overlap in time need separate workspaces.
  */
 int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            const void* k_cache, const void* v_cache,
@@ -256,6 +258,50 @@ int pkv_attn_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                            int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_context_len, float scale,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The attention of a mixed step ([P1] "Why chunked prefill": one scheduler
+ * step carries a decode token for each decoding sequence beside prompt
+ * chunks; [P1] model.py forward runs attention for all of them over the
+ * pages) in one call: pkv_attn_prefill_chunk over the prefill sequences and
+ * pkv_attn_decode over the decode sequences, on the same pools, with the
+ * same outputs bit for bit.  Group sizes Hq/Hkv of 1, 2 and 4 run as one
+ * launch whose grid holds both kinds of workgroup (the two halves overlap on
+ * the chip instead of running one after the other); group size 8, or a call
+ * with one half empty, runs the two launches in order.
+ *   out_prefill, q_prefill, cu_q_lens, block_tables_prefill,
+ *   context_lens_prefill, B_prefill, total_q, max_q_len,
+ *   max_context_len_prefill     as out, q, cu_q_lens, block_tables,
+ *                               context_lens, B, total_q, max_q_len and
+ *                               max_context_len of pkv_attn_prefill_chunk
+ *   out_decode, q_decode, block_tables_decode, context_lens_decode,
+ *   B_decode, max_context_len_decode   as those of pkv_attn_decode
+ *   k_cache, v_cache, Hq, Hkv, D, block_size, num_blocks, scale
+ *                               shared by both halves
+ *   max_blocks_per_seq          row width of both block tables
+ *   prefill_workspace           pkv_prefill_workspace_bytes(B_prefill,
+ *                               max_q_len, ...) bytes, as for the chunk call
+ *   decode_workspace            pkv_decode_workspace_bytes(B_decode, ...)
+ *                               bytes, as for the decode call; both
+ *                               zero-filled before their first use and left
+ *                               so, and distinct
+ * Errors: those of either call (checked before anything is enqueued), and
+ * PKV_EINVAL if the two outputs or the two (non-empty) workspaces coincide.
+ * The step's K/V rows must be appended before the call.
+ */
+int pkv_attn_prefill_decode(void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
+                            const int32_t* block_tables_prefill,
+                            const int32_t* context_lens_prefill, int32_t B_prefill,
+                            int32_t total_q, int32_t max_q_len, int32_t max_context_len_prefill,
+                            void* out_decode, const void* q_decode,
+                            const int32_t* block_tables_decode,
+                            const int32_t* context_lens_decode, int32_t B_decode,
+                            int32_t max_context_len_decode, const void* k_cache,
+                            const void* v_cache, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            float scale, void* prefill_workspace, size_t prefill_workspace_bytes,
+                            void* decode_workspace, size_t decode_workspace_bytes,
+                            void* stream);
 
 /*
  * The step before attention, fused ([P1] model.py: rms_norm, _rope_tables,

@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "qk_rope.hip", "pkv_api.cpp"]
+SOURCES = ["kv_append.hip", "decode.hip", "prefill.hip", "mixed.hip", "qk_rope.hip", "pkv_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -30,11 +30,13 @@ COMMON = [
 ]
 
 
-# Per-source extra flags.  prefill.hip: keep the MFMA accumulators in VGPRs
+# Per-source extra flags.  prefill.hip, mixed.hip (which holds the prefill
+# kernel's body too): keep the MFMA accumulators in VGPRs
 # (otherwise, with more than 256 registers, they land in AGPRs and every
 # tile copies them back and forth for the softmax rescale).
 EXTRA = {
     "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "mixed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

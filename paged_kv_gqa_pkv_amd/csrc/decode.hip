@@ -1,748 +1,15 @@
-// Decode attention over a paged KV cache, gfx950.
-//
-// What is computed (Module 04 page, section 1: o_n = softmax(q_n K^T /
-// sqrt(d_head)) V over the cached positions; Module 12 page, model.py
-// forward with T = 1, query heads grouped as q.view(T, n_kv, group, D)):
-// for every sequence b and query head h the softmax-weighted sum of the V
-// rows of KV head h / G over positions 0 .. context_lens[b]-1.
-//
-// Decomposition.  One workgroup owns one (sequence b, KV head g, context
-// split) and serves all G = Hq/Hkv query heads of the group from the same
-// loaded K/V rows, so every K/V byte is read from HBM once per step.  The
-// workgroup's 4 waves take disjoint page ranges of the split.  Pages are
-// stored token-major as in the Module 12 page's paged.py ([page][16 slots][KV
-// head][D]), so a 16-token page of one head is 16 rows of 256 B, Hkv*256 B
-// apart: lane l holds rows (l>>3) and (l>>3)+8 and the 16-byte chunks (l&7)
-// and (l&7)+8 of each, so every load instruction moves eight full 128-byte
-// lines.  The K/V rows stay in VGPRs (no LDS staging: the reuse
-// across the G heads happens inside each lane).  Scores use v_dot2_f32_bf16
-// on the packed bf16 data and an 8-lane DPP butterfly finishes each dot
-// product; each lane keeps an online-softmax state (fp32 m, l, acc) over its
-// rows, with bf16 probabilities in the PV product.  The lane states, then the
-// waves (through LDS), are merged at the end with the usual max/rescale rule.
-// Pages are software-pipelined: the next group of pages is in flight while
-// the current one is reduced.
-//
-// Long contexts with few (sequence, head) pairs are cut into splits of
-// pages_per_split pages (flash-decoding); each split writes its unnormalised
-// (m, l, acc) to the workspace, and the last split of a (sequence, KV head)
-// to finish merges them all in split order, so results are run-to-run
-// bit-identical and the whole call is one kernel.
-#include "pkv.h"
-#include "pkv_device.h"
-#include "pkv_launch.h"
+// Decode launchers, split planner and the per-GPU scratch array of the
+// decode call that allocates nothing; the kernel is in decode_kernel.h.
+#include "decode_kernel.h"
 
 #include <mutex>
-#include <type_traits>
 #include <vector>
 
 namespace pkv {
 
+using namespace dec;
+
 namespace {
-
-// Tuning constants (measured on MI355X; overridable at build time).
-#ifndef PKV_DECODE_NT
-#define PKV_DECODE_NT 1            // streaming (non-temporal) K/V loads
-#endif
-#ifndef PKV_DECODE_WG_PER_CU
-#define PKV_DECODE_WG_PER_CU 2     // split planner: waves per SIMD the register budget allows
-#endif
-#ifndef PKV_DECODE_MIN_PPW
-#define PKV_DECODE_MIN_PPW 2       // split planner: minimum pages per wave
-#endif
-#ifndef PKV_DECODE_WG_COST_PAGES
-#define PKV_DECODE_WG_COST_PAGES 3 // split planner: fixed workgroup cost, in page-times
-#endif
-#ifndef PKV_DECODE_MERGE_COST_PAGES
-#define PKV_DECODE_MERGE_COST_PAGES 2  // split planner: fixed cost of the split merge, page-times
-#endif
-#ifndef PKV_DECODE_SPLIT_COST_EIGHTHS
-#define PKV_DECODE_SPLIT_COST_EIGHTHS 8  // split planner: cost per split (its arrival), 1/8 page-time
-#endif
-#ifndef PKV_DECODE_MAX_HG
-#define PKV_DECODE_MAX_HG 1        // most KV heads per workgroup
-#endif
-#ifndef PKV_DECODE_PARTS
-#define PKV_DECODE_PARTS 4         // waves per KV head, splitting its pages
-#endif
-#ifndef PKV_DECODE_WIDE_PPW
-#define PKV_DECODE_WIDE_PPW 16     // pages per wave from which workgroups take two KV heads (0: never)
-#endif
-#ifndef PKV_DECODE_FORCE_PPW
-#define PKV_DECODE_FORCE_PPW 0     // > 0: every plan uses this many pages per wave (tuning)
-#endif
-
-constexpr int kMaxPagesPerWave = 64;         // one VGPR of page ids per wave
-
-__device__ __forceinline__ u32x4 load_kv(const u32x4* p) {
-#if PKV_DECODE_NT
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-constexpr float kNegInf = -__builtin_inff();
-
-// Split partials are written and read with agent-coherent accesses (the
-// last split to finish, possibly on another XCD, merges them).
-__device__ __forceinline__ void ws_store2(float* p, float lo, float hi) {
-  const uint64_t bits = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
-
-struct DecodeArgs {
-  uint16_t* out;                 // bf16 [B][Hq][D]
-  const u32x4* q;                // bf16 [B][Hq][D] as 16-byte chunks
-  const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D], or int8 codes (same order)
-  const u32x4* v_cache;
-  const float* k_scales;         // int8 pages: float32 [num_blocks][16][Hkv]
-  const float* v_scales;
-  const int32_t* block_tables;   // [B][max_blocks]
-  const int32_t* ctx_lens;       // [B]
-  // Fused append (bf16 pages, no ring): each sequence's newest position,
-  // context_lens[b] - 1, takes its K/V rows from k_new/v_new [B][Hkv][D]
-  // instead of the pool, and the call writes those rows into that position's
-  // slot (k_pool/v_pool are the same pools as k_cache/v_cache).
-  const u32x4* k_new;
-  const u32x4* v_new;
-  u32x4* k_pool;
-  u32x4* v_pool;
-  float* ws_ml;                  // [B][Hq][S][2] (m, l), log2 domain
-  float* ws_acc;                 // [B][Hq][S][D]
-  int* counters;                 // [B][Hkv / heads_per_wg] arrivals per (sequence, head group)
-  int B, Hq, Hkv, num_blocks, max_blocks, splits, pages_per_split;
-  int heads_per_wg;              // KV heads per workgroup
-  int parts;                     // waves per KV head, each over 1/parts of the split's pages
-  int window;                    // > 0: each sequence's pages form a ring of `window` tokens
-  float scale_log2;              // scale * log2(e)
-};
-
-// Online softmax per lane.  Each lane keeps its own state (m, l, acc) over
-// the rows it holds.  m is a reference point, not the exact running max: it
-// moves only when a score exceeds it by more than kRescaleSlack (log2 units),
-// so exp2(s - m) stays below 2^kRescaleSlack and the accumulator rescale is
-// skipped (wave-uniformly) on almost every page.  The probabilities are
-// rounded to bf16 (as the attention of the pages does before its PV product)
-// and the PV product runs on v_dot2_f32_bf16, pairing the lane's rows r0 and
-// r0+8.
-constexpr float kRescaleSlack = 8.f;
-constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // bf16 (1, 1)
-
-// Raises the lane's reference max for head j if this page's scores need it
-// (rescaling acc and l), then returns the reference to subtract.
-template <int U>
-__device__ __forceinline__ float softmax_ref(const float (&s)[U][2], float& m, float& l,
-                                             float (&acc)[16]) {
-  float mc = s[0][0];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) mc = fmaxf(mc, s[u][rr]);
-  const bool up = mc > m + kRescaleSlack;   // false while all scores are -inf
-  if (__builtin_amdgcn_ballot_w64(up) != 0) {
-    const float alpha = up ? fast_exp2(m - mc) : 1.f;   // m = -inf gives 0
-    m = up ? mc : m;
-    l *= alpha;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) acc[d] *= alpha;
-  }
-  return (m == kNegInf) ? 0.f : m;
-}
-
-// bf16 pages.  A 16-token page of one head is 16 rows of 256 B, one per slot
-// (Hkv rows apart): lane l holds rows r0 = l>>3 and r0+8, and the 16-byte
-// chunks c = l&7 and c+8 of each, i.e. head dims 8c..8c+7 and 64+8c..64+8c+7
-// (accumulator d < 8 and d >= 8).
-struct Bf16Page {
-  struct Regs {
-    u32x4 k[2][2];   // [row r0 / r0+8][chunk c / c+8]
-    u32x4 v[2][2];
-  };
-  static __device__ __forceinline__ int dim(int c, int d) {
-    return d < 8 ? 8 * c + d : 64 + 8 * c + (d - 8);
-  }
-  static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
-    const u32x4 lo = qp[c], hi = qp[c + 8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { qw[i] = lo[i]; qw[4 + i] = hi[i]; }
-  }
-  static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
-                                              int r0, int c) {
-    const int64_t base = ((blk * kPage + r0) * a.Hkv + g) * 16 + c;   // 16 chunks per row
-    const int64_t r8 = (int64_t)8 * a.Hkv * 16;                       // row r0 + 8
-    const u32x4* kp = a.k_cache + base;
-    const u32x4* vp = a.v_cache + base;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      r.k[0][h] = load_kv(kp + 8 * h);
-      r.k[1][h] = load_kv(kp + r8 + 8 * h);
-      r.v[0][h] = load_kv(vp + 8 * h);
-      r.v[1][h] = load_kv(vp + r8 + 8 * h);
-    }
-  }
-  // kMask: the page is the sequence's last, partially filled one; rows >=
-  // valid_rows are excluded (score -inf, V forced to 0 so canary data cannot
-  // leak).
-  template <int G, int U, bool kMask>
-  static __device__ __forceinline__ void process(const Regs (&buf)[U], const uint32_t (&qw)[G][8],
-                                                 float (&m)[G], float (&l)[G],
-                                                 float (&acc)[G][16], float scale_log2, int r0,
-                                                 int valid_rows) {
-    float s[G][U][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          float d = 0.f;
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf[u].k[rr][h][i]),
-                                                  as_bf16x2(qw[j][4 * h + i]), d, false);
-          d = sum8(d) * scale_log2;
-          if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
-          s[j][u][rr] = d;
-        }
-    bf16x2 pp[U][G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mu = softmax_ref<U>(s[j], m[j], l[j], acc[j]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        pp[u][j] = bf16x2{(__bf16)fast_exp2(s[j][u][0] - mu), (__bf16)fast_exp2(s[j][u][1] - mu)};
-        l[j] = __builtin_amdgcn_fdot2_f32_bf16(pp[u][j], as_bf16x2(kBf16PairOne), l[j], false);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool keep0 = !kMask || (r0 < valid_rows);
-      const bool keep1 = !kMask || (r0 + 8 < valid_rows);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w0 = keep0 ? buf[u].v[0][h][i] : 0u;   // row r0, dims 2i, 2i+1
-          const uint32_t w1 = keep1 ? buf[u].v[1][h][i] : 0u;   // row r0 + 8
-          const bf16x2 lo = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
-          const bf16x2 hi = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
-          const int d = 8 * h + 2 * i;
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(lo, pp[u][j], acc[j][d], false);
-            acc[j][d + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, pp[u][j], acc[j][d + 1], false);
-          }
-        }
-    }
-  }
-};
-
-// int8 pages (codes with one float32 scale per (slot, head), read as
-// code * scale; Module 04 page, kv_cache.py listing, section 5).  A page of
-// one head is 16 rows of 128 codes (Hkv*128 B apart) plus 16 K and 16 V
-// scales: lane l holds rows r0 = l>>3 and r0+8 and the 16-byte chunk c = l&7
-// of each (head dims 16c..16c+15).  The four scales of those two rows are
-// loaded once per 4-lane quad, lane c & 3 of it taking K(r0), K(r0+8), V(r0)
-// or V(r0+8), and handed to the whole quad by DPP broadcasts (a page is 5
-// loads per lane).  Codes are integers in [-127, 127], exact in bf16, so
-// q . codes runs on v_dot2_f32_bf16 and the row's K scale multiplies the
-// score; the row's V scale is folded into its probability before the PV
-// product.
-constexpr int kQuadBcast0 = 0x00, kQuadBcast1 = 0x55, kQuadBcast2 = 0xAA, kQuadBcast3 = 0xFF;
-struct Int8Page {
-  struct Regs {
-    u32x4 k[2];      // [row r0 / r0+8], 16 codes each
-    u32x4 v[2];
-    float s;         // lane c & 3 of the quad: K(r0), K(r0+8), V(r0), V(r0+8)
-  };
-  static __device__ __forceinline__ int dim(int c, int d) { return 16 * c + d; }
-  static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
-    const u32x4 lo = qp[2 * c], hi = qp[2 * c + 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { qw[i] = lo[i]; qw[4 + i] = hi[i]; }
-  }
-  static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
-                                              int r0, int c) {
-    const int64_t row = (blk * kPage + r0) * a.Hkv + g;        // 8 chunks per row
-    const int64_t r8 = (int64_t)8 * a.Hkv;                      // row r0 + 8
-    r.k[0] = load_kv(a.k_cache + row * 8 + c);
-    r.k[1] = load_kv(a.k_cache + (row + r8) * 8 + c);
-    r.v[0] = load_kv(a.v_cache + row * 8 + c);
-    r.v[1] = load_kv(a.v_cache + (row + r8) * 8 + c);
-    r.s = ((c & 2) ? a.v_scales : a.k_scales)[row + ((c & 1) ? r8 : 0)];
-  }
-  // Codes of one 4-code word as two bf16 pairs (exact).
-  static __device__ __forceinline__ bf16x2 pair(uint32_t w, int lo) {
-    return bf16x2{(__bf16)sbyte(w, lo), (__bf16)sbyte(w, lo + 1)};
-  }
-  template <int G, int U, bool kMask>
-  static __device__ __forceinline__ void process(const Regs (&buf)[U], const uint32_t (&qw)[G][8],
-                                                 float (&m)[G], float (&l)[G],
-                                                 float (&acc)[G][16], float scale_log2, int r0,
-                                                 int valid_rows) {
-    // the quad's four scales in every lane: K(r0), K(r0+8), V(r0), V(r0+8)
-    float ks[U][2], vs[U][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ks[u][0] = dpp_f<kQuadBcast0>(buf[u].s);
-      ks[u][1] = dpp_f<kQuadBcast1>(buf[u].s);
-      vs[u][0] = dpp_f<kQuadBcast2>(buf[u].s);
-      vs[u][1] = dpp_f<kQuadBcast3>(buf[u].s);
-    }
-    float s[G][U][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        bf16x2 kp[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kp[2 * i] = pair(buf[u].k[rr][i], 0);
-          kp[2 * i + 1] = pair(buf[u].k[rr][i], 2);
-        }
-        const float rs = ks[u][rr] * scale_log2;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          float d = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            d = __builtin_amdgcn_fdot2_f32_bf16(kp[i], as_bf16x2(qw[j][i]), d, false);
-          d = sum8(d) * rs;
-          if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
-          s[j][u][rr] = d;
-        }
-      }
-    bf16x2 pp[U][G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mu = softmax_ref<U>(s[j], m[j], l[j], acc[j]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p0 = fast_exp2(s[j][u][0] - mu), p1 = fast_exp2(s[j][u][1] - mu);
-        l[j] += p0 + p1;
-        // masked rows: weight exactly 0 (their scale may be a NaN canary)
-        const float w0 = (!kMask || r0 < valid_rows) ? p0 * vs[u][0] : 0.f;
-        const float w1 = (!kMask || r0 + 8 < valid_rows) ? p1 * vs[u][1] : 0.f;
-        pp[u][j] = bf16x2{(__bf16)w0, (__bf16)w1};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool keep0 = !kMask || (r0 < valid_rows);
-      const bool keep1 = !kMask || (r0 + 8 < valid_rows);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = keep0 ? buf[u].v[0][i] : 0u;   // row r0, dims 4i .. 4i+3
-        const uint32_t w1 = keep1 ? buf[u].v[1][i] : 0u;   // row r0 + 8
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 vv = bf16x2{(__bf16)sbyte(w0, e), (__bf16)sbyte(w1, e)};
-          const int d = 4 * i + e;
-#pragma unroll
-          for (int j = 0; j < G; ++j)
-            acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(vv, pp[u][j], acc[j][d], false);
-        }
-      }
-    }
-  }
-};
-
-// One reduce-scatter step of the lane states: exchange with lane ^ (8 << K)
-// (row bit K of the lane), keep the upper half of `in` if that bit is set,
-// else the lower half, merged with the partner's copy of the same half.
-template <int K>
-__device__ __forceinline__ float xchg(float x) {
-  if constexpr (K == 0)
-    return xor8(x);
-  else
-    return shfl_xor(x, 8 << K);
-}
-template <int K, int N>
-__device__ __forceinline__ void rs_step(float& m, float& l, const float (&in)[N],
-                                        float (&out)[N / 2], int r0) {
-  const bool hi = (r0 >> K) & 1;
-  float send[N / 2];
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    send[i] = hi ? in[i] : in[N / 2 + i];
-    out[i] = hi ? in[N / 2 + i] : in[i];
-  }
-  const float mo = xchg<K>(m), lo = xchg<K>(l);
-  const float M = fmaxf(m, mo);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  const float wa = fast_exp2(m - Mu), wb = fast_exp2(mo - Mu);
-  l = l * wa + lo * wb;
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) out[i] = out[i] * wa + xchg<K>(send[i]) * wb;
-  m = M;
-}
-
-// Workgroup = one (sequence b, context split, group of heads_per_wg KV
-// heads); its heads_per_wg * parts waves are (head hw, page part pw), wave
-// w = pw * heads_per_wg + hw.  Wave (hw, pw) serves KV head g = group *
-// heads_per_wg + hw and its G query heads over part pw of the split's pages
-// (pages_per_split / parts consecutive pages).  The lane states of a wave
-// are merged by a reduce-scatter (each lane ends with two head dims), the
-// parts of a head through LDS.  With splits, the part-0 wave of each head
-// writes its unnormalised (m, l, acc) and the last workgroup of (b, head
-// group) to finish merges the splits; the number of splits is kept small,
-// since arrivals on one counter are serialised by the memory system.
-template <class P, int G, int U, int kMaxWaves, bool kAppend>
-__global__ void __launch_bounds__(kMaxWaves * kWave)
-decode_kernel(const DecodeArgs a) {
-  __shared__ int s_last;
-  __shared__ float s_part[kMaxWaves][G][kWave][2];   // parts > 0: two dims per lane and head
-  __shared__ float s_ml[kMaxWaves][G][2];
-  __shared__ int s_bad[kMaxWaves];
-
-  const int HG = a.heads_per_wg;
-  const int PW = a.parts;
-  const int n_groups = a.Hkv / HG;
-  const int bid = blockIdx.x;                 // ((b * S) + split) * n_groups + group
-  const int grp = bid % n_groups;
-  const int rest = bid / n_groups;
-  const int split = rest % a.splits;
-  const int b = rest / a.splits;
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const int hw = w % HG, pw = w / HG;
-  const int g = grp * HG + hw;
-  const int r0 = lane >> 3, c = lane & 7;
-  const int S = a.splits;
-  const int pps = a.pages_per_split;
-  const int ppw = pps / PW;                   // pages per wave (the plan keeps this exact)
-
-  // Everything up to the page loads is independent of the context length, so
-  // the length, the page ids and q are fetched in parallel.  The wave's page
-  // range is fixed by the plan; ids past the sequence's last page are
-  // fetched (they lie inside the table row) but never used.
-  const int p0 = split * pps;
-  const int wp0 = p0 + pw * ppw;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
-  const int my_id = (lane < ppw && wp0 + lane < a.max_blocks) ? bt[wp0 + lane] : 0;
-  uint32_t qw[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j) P::load_q(qw[j], a.q + ((int64_t)b * a.Hq + g * G + j) * 16, c);
-
-  // A length outside [0, planned maximum] poisons the outputs of the sequence
-  // (the plan covers splits * pages_per_split pages; no read goes past it).
-  // Ring paging (Module 04 page, section 4): a ring of `window` tokens holds
-  // the last min(n, window) positions, all at or before the query, in ring
-  // slots 0 .. min(n, window) - 1; attention does not depend on their order,
-  // so the ring is read like a sequence of that many tokens.
-  const int n_ctx = a.ctx_lens[b];
-  const int n = (a.window > 0 && n_ctx > a.window) ? a.window : n_ctx;
-  const bool bad_len = n < 0 || n > a.max_blocks * kPage ||
-                       (n + kPage - 1) / kPage > S * pps;
-
-  // Fused append: position n - 1 comes from k_new / v_new (its slot is not
-  // read), and the workgroup whose split holds that position's page (the
-  // last split if the length is past the plan) writes the rows into the slot
-  // and its part-0 waves add the position's key to their state.  The
-  // position's table entry is checked as decode checks every page it reads:
-  // an invalid one poisons the output (and, as in slot mapping, no row is
-  // written).
-  typename P::Regs nrow[1] = {};
-  const int n_cache = (kAppend && n >= 1) ? n - 1 : n;
-  const int n_pages = bad_len ? 0 : (n_cache + kPage - 1) / kPage;
-  const int ns = (n_pages + pps - 1) / pps;     // splits holding cached pages
-  // the split owning the new position (-1: none); it is >= ns - 1, since the
-  // new position's page is at or after the last cached page
-  const int app_split =
-      (kAppend && n_ctx >= 1) ? min(((n_ctx - 1) / kPage) / pps, S - 1) : -1;
-  const bool owns_new = kAppend && !bad_len && split == app_split;   // uniform
-  // splits that contribute: 0 .. nsplit - 1
-  const int nsplit = (kAppend && !bad_len && app_split >= 0) ? max(ns, app_split + 1) : ns;
-  const bool has_new = owns_new && pw == 0;
-  bool new_bad = false;
-  if constexpr (kAppend) {
-    if (split == app_split && pw == 0) {
-      const u32x4* kn = a.k_new + ((int64_t)b * a.Hkv + g) * 16;
-      const u32x4* vn = a.v_new + ((int64_t)b * a.Hkv + g) * 16;
-      nrow[0].k[0][0] = kn[c]; nrow[0].k[0][1] = kn[c + 8];
-      nrow[0].v[0][0] = vn[c]; nrow[0].v[0][1] = vn[c + 8];
-      const int tp = (n_ctx - 1) / kPage;
-      const int id = tp < a.max_blocks ? bt[tp] : -1;
-      new_bad = !(id >= 0 && id < a.num_blocks);
-      // lanes 0..7 (r0 = 0) hold chunks c and c + 8 of the new rows
-      if (!new_bad && id < kMaxSlotBlocks && r0 == 0) {
-        const int64_t slot = (int64_t)id * kPage + (n_ctx - 1) % kPage;
-        u32x4* kd = a.k_pool + (slot * a.Hkv + g) * 16;
-        u32x4* vd = a.v_pool + (slot * a.Hkv + g) * 16;
-        kd[c] = nrow[0].k[0][0]; kd[c + 8] = nrow[0].k[0][1];
-        vd[c] = nrow[0].v[0][0]; vd[c + 8] = nrow[0].v[0][1];
-      }
-    }
-  }
-  const int p1 = min(p0 + pps, n_pages);
-
-  const int64_t orow = ((int64_t)b * a.Hq + g * G) * kD;   // this head's first output row
-  if (p0 >= p1 && !owns_new) {
-    // Nothing to read.  The first split owns the output of an empty or
-    // invalid sequence: zeros for an empty context, NaN for a bad length.
-    if (split == 0 && pw == 0) {
-      for (int e = lane; e < G * kD; e += kWave) a.out[orow + e] = bad_len ? 0x7fc0u : 0u;
-    }
-    return;
-  }
-
-  // This wave's pages: [w0, w1); full pages first, then the sequence's last
-  // page if it is partial and falls in range.
-  const int w0 = min(wp0, p1);
-  const int w1 = min(wp0 + ppw, p1);
-  const int n_full = n_cache / kPage;
-  const int nfull = max(0, min(w1, n_full) - w0);
-  const bool has_tail = (n_cache % kPage) != 0 && n_full >= w0 && n_full < w1;
-
-  float m[G], l[G], acc[G][16];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = kNegInf; l[j] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) acc[j][d] = 0.f;
-  }
-
-  const int id_base = w0 - wp0;               // lane of my_id holding page w0
-  int bad = (bad_len || (has_new && new_bad)) ? 1 : 0;
-  auto page_id = [&](int j) -> int64_t {
-    const int id = __builtin_amdgcn_readlane(my_id, id_base + j);
-    const bool ok = id >= 0 && id < a.num_blocks;
-    bad |= ok ? 0 : 1;
-    return ok ? id : 0;
-  };
-
-  // Full pages, U at a time, two groups in flight.  The steady-state loop
-  // covers the pairs of groups whose successor exists, so all its loads are
-  // unconditional: the load counter sees one order on every path and the wait
-  // before reducing a group leaves the next group in flight.  The last one or
-  // two groups are reduced after the loop.
-  const int ngroups = nfull / U;
-  typename P::Regs bufA[U], bufB[U];
-  // q, the length and the page ids have all arrived before the page loads
-  // start (the ids are needed for the first address anyway), which keeps
-  // them out of the loop's in-flight count.
-  __builtin_amdgcn_s_waitcnt(0);
-  if (ngroups > 0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id(u), g, r0, c);
-    const int steady = (ngroups - 1) / 2;
-    // The scheduling barriers keep each prefetch between the two reductions:
-    // issued before the group it overlaps is reduced, and after the group
-    // whose registers it reuses is done (else the two groups' registers
-    // overlap and the loop needs copies that wait for the prefetch).
-    for (int pi = 0; pi < steady; ++pi) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) P::load(bufB[u], a, page_id((2 * pi + 1) * U + u), g, r0, c);
-      __builtin_amdgcn_sched_barrier(0);
-      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id((2 * pi + 2) * U + u), g, r0, c);
-      __builtin_amdgcn_sched_barrier(0);
-      P::template process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
-    }
-    if (ngroups - 2 * steady == 2) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        P::load(bufB[u], a, page_id((2 * steady + 1) * U + u), g, r0, c);
-      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
-      P::template process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
-    } else {
-      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
-    }
-  }
-  // Leftover full pages (fewer than U), one at a time.
-  for (int j = ngroups * U; j < nfull; ++j) {
-    typename P::Regs one[1];
-    P::load(one[0], a, page_id(j), g, r0, c);
-    P::template process<G, 1, false>(one, qw, m, l, acc, a.scale_log2, r0, kPage);
-  }
-  if (has_tail) {
-    typename P::Regs one[1];
-    P::load(one[0], a, page_id(n_full - w0), g, r0, c);
-    P::template process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n_cache % kPage);
-  }
-  if constexpr (kAppend) {
-    // the new position as a page whose only valid row is row 0 (lanes 0..7)
-    if (has_new) P::template process<G, 1, true>(nrow, qw, m, l, acc, a.scale_log2, r0, 1);
-  }
-
-  // Reduce-scatter over the wave's 8 row groups (lane bits r0 = 0..2): at
-  // step k each lane merges half of its accumulators with those of lane
-  // ^ (8 << k) and keeps that half, so after three steps lane (r0, c) holds
-  // the wave's merged state for two head dims, d0 and d0 + 1 of its 16
-  // (P::dim(c, .)), with d0 = 8 (r0 & 1) + 4 ((r0 >> 1) & 1) + 2 (r0 >> 2).
-  float v2[G][2];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float v8[8], v4[4];
-    rs_step<0, 16>(m[j], l[j], acc[j], v8, r0);
-    rs_step<1, 8>(m[j], l[j], v8, v4, r0);
-    rs_step<2, 4>(m[j], l[j], v4, v2[j], r0);
-  }
-  const int d0 = 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2);
-  const int dd = P::dim(c, d0);               // head dims dd, dd + 1
-
-  // Merge the page parts of each head through LDS into its part-0 wave.
-  if (PW > 1) {
-    if (pw > 0) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        s_part[w][j][lane][0] = v2[j][0];
-        s_part[w][j][lane][1] = v2[j][1];
-        if (lane == 0) { s_ml[w][j][0] = m[j]; s_ml[w][j][1] = l[j]; }
-      }
-    }
-    if (lane == 0) s_bad[w] = bad;
-    __syncthreads();
-    if (pw > 0) {
-      // other waves only take part in the workgroup's barriers from here
-      if (S == 1 || nsplit <= 1) return;
-    } else {
-      for (int q = 1; q < PW; ++q) {
-        const int wq = q * HG + hw;
-        bad |= s_bad[wq];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float mo = s_ml[wq][j][0], lo = s_ml[wq][j][1];
-          const float M = fmaxf(m[j], mo);
-          const float Mu = (M == kNegInf) ? 0.f : M;
-          const float wa = fast_exp2(m[j] - Mu), wb = fast_exp2(mo - Mu);
-          l[j] = l[j] * wa + lo * wb;
-          v2[j][0] = v2[j][0] * wa + s_part[wq][j][lane][0] * wb;
-          v2[j][1] = v2[j][1] * wa + s_part[wq][j][lane][1] * wb;
-          m[j] = M;
-        }
-      }
-    }
-  }
-
-  const float nan = __builtin_nanf("");
-  if (S == 1 || nsplit <= 1) {
-    // a single contributing split (split 0): normalise and write the output
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float inv = 1.f / l[j];
-      *reinterpret_cast<uint32_t*>(a.out + orow + j * kD + dd) =
-          bad ? 0x7fc07fc0u : pack_bf16x2(v2[j][0] * inv, v2[j][1] * inv);
-    }
-    return;
-  }
-  if (pw == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int64_t r = ((int64_t)b * a.Hq + g * G + j) * S + split;
-      ws_store2(a.ws_acc + r * kD + dd, bad ? nan : v2[j][0], bad ? nan : v2[j][1]);
-      if (lane == 0) ws_store2(a.ws_ml + 2 * r, m[j], bad ? nan : l[j]);
-    }
-  }
-
-  // Split path: the last of the sequence's contributing splits to finish
-  // merges all of them (identical whichever split finishes last).  The
-  // partials above were written with agent-coherent stores; waiting for
-  // their completion before the arrival is counted, and an acquire fence
-  // (cache invalidate) before reading them back, orders them without an L2
-  // writeback.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int* counter = a.counters + (int64_t)b * n_groups + grp;
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             nsplit - 1;
-  __syncthreads();
-  if (!s_last || pw > 0) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // Each part-0 wave merges its own head's G query heads, online over
-  // batches of kBatch splits.  A batch's loads all go out together: its
-  // (m, l) pairs (lane u holds split s0 + u) and every lane's two dims of the
-  // partial outputs; then the batch's reference max, the rescale of what the
-  // earlier batches summed, and the weighted sum in split order.  Addresses
-  // past the last split are clamped and weighted 0, so the loads are
-  // unconditional.
-  constexpr int kBatch = 64 / G;              // 2 * kBatch * G = 128 VGPRs of partials
-  float Mr[G], Lr[G], A[G][2];
-#pragma unroll
-  for (int j = 0; j < G; ++j) { Mr[j] = kNegInf; Lr[j] = 0.f; A[j][0] = A[j][1] = 0.f; }
-  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-    const int cnt = min(kBatch, nsplit - s0);
-    f32x2 mlv[G];
-    f32x2 v[G][kBatch];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int64_t rs = ((int64_t)b * a.Hq + g * G + j) * S + s0;   // first split of the batch
-      mlv[j] = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * (rs + min(lane, cnt - 1)));
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        v[j][u] = *reinterpret_cast<const f32x2*>(a.ws_acc + (rs + min(u, cnt - 1)) * kD + dd);
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float ms = lane < cnt ? mlv[j][0] : kNegInf;
-      const float Mn = fmaxf(Mr[j], wave_max(ms));
-      const float Mu = (Mn == kNegInf) ? 0.f : Mn;
-      const float resc = fast_exp2(Mr[j] - Mu);
-      const float wl = lane < cnt ? fast_exp2(ms - Mu) : 0.f;   // weight of split s0 + lane
-      Lr[j] = Lr[j] * resc + wave_sum(lane < cnt ? mlv[j][1] * wl : 0.f);
-      A[j][0] *= resc;
-      A[j][1] *= resc;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float wgt =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
-        A[j][0] = __builtin_fmaf(v[j][u][0], wgt, A[j][0]);
-        A[j][1] = __builtin_fmaf(v[j][u][1], wgt, A[j][1]);
-      }
-      Mr[j] = Mn;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float inv = 1.f / Lr[j];
-    *reinterpret_cast<uint32_t*>(a.out + orow + j * kD + dd) =
-        pack_bf16x2(A[j][0] * inv, A[j][1] * inv);
-  }
-  // Leave the counter at zero for the next call on this workspace.
-  if (hw == 0 && lane == 0)
-    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Pages held per pipeline stage, by group size (register budget: two stages
-// of U pages, 32 VGPRs per page, next to 16*G accumulators).
-#ifndef PKV_DECODE_U_G1
-#define PKV_DECODE_U_G1 2
-#endif
-#ifndef PKV_DECODE_U_G2
-#define PKV_DECODE_U_G2 2
-#endif
-#ifndef PKV_DECODE_U_G4
-#define PKV_DECODE_U_G4 1
-#endif
-#ifndef PKV_DECODE_U_G8
-#define PKV_DECODE_U_G8 1
-#endif
-// int8 pages hold 20 VGPRs per page (codes and scales), so twice the pages fit.
-#ifndef PKV_DECODE_I8_U_G1
-#define PKV_DECODE_I8_U_G1 2
-#endif
-#ifndef PKV_DECODE_I8_U_G2
-#define PKV_DECODE_I8_U_G2 2
-#endif
-#ifndef PKV_DECODE_I8_U_G4
-#define PKV_DECODE_I8_U_G4 1
-#endif
-#ifndef PKV_DECODE_I8_U_G8
-#define PKV_DECODE_I8_U_G8 1
-#endif
-
-// Waves a workgroup may hold: two waves per SIMD (eight per CU) fit the
-// register budget of the G <= 4 kernels (at most 256 VGPRs), one per SIMD the
-// G = 8 kernels.
-constexpr int max_waves_for(int G) { return G >= 8 ? 4 : 8; }
 
 template <class P, int G, int U, bool kAppend = false>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
@@ -757,49 +24,6 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Where the split path keeps its partials and arrival counters.
-struct SplitBuffers {
-  float* ml;
-  float* acc;
-  int* counters;
-};
-
-// A caller workspace of plan.ws_bytes: (m, l), then acc, then the counters.
-SplitBuffers workspace_buffers(const DecodePlan& plan, void* workspace) {
-  char* ws = static_cast<char*>(workspace);
-  if (plan.splits <= 1 || !ws) return {nullptr, nullptr, nullptr};
-  return {reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + plan.ws_ml_bytes),
-          reinterpret_cast<int*>(ws + plan.ws_ml_bytes + plan.ws_acc_bytes)};
-}
-
-DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* v_cache,
-                     const float* k_scales, const float* v_scales,
-                     const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,
-                     int Hkv, int num_blocks, int max_blocks, float scale,
-                     const DecodePlan& plan, const SplitBuffers& wsb, int window) {
-  DecodeArgs a;
-  a.out = static_cast<uint16_t*>(out);
-  a.q = static_cast<const u32x4*>(q);
-  a.k_cache = static_cast<const u32x4*>(k_cache);
-  a.v_cache = static_cast<const u32x4*>(v_cache);
-  a.k_scales = k_scales;
-  a.v_scales = v_scales;
-  a.block_tables = block_tables;
-  a.ctx_lens = ctx_lens;
-  a.k_new = a.v_new = nullptr;
-  a.k_pool = a.v_pool = nullptr;
-  const bool split = plan.splits > 1;
-  a.ws_ml = split ? wsb.ml : nullptr;
-  a.ws_acc = split ? wsb.acc : nullptr;
-  a.counters = split ? wsb.counters : nullptr;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.num_blocks = num_blocks; a.max_blocks = max_blocks;
-  a.splits = plan.splits; a.pages_per_split = plan.pages_per_split;
-  a.heads_per_wg = plan.heads_per_wg;
-  a.parts = plan.parts;
-  a.window = window;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return a;
-}
 
 // Instantiations by group size G = Hq / Hkv (pages per pipeline stage U by
 // the register budget of each).
@@ -932,7 +156,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_cus)
   if (best_s > 1) {
     p.ws_ml_bytes = align256((size_t)B * Hq * best_s * 2 * sizeof(float));
     p.ws_acc_bytes = align256((size_t)B * Hq * best_s * kD * sizeof(float));
-    p.ws_counter_bytes = align256((size_t)B * (Hkv / hg) * sizeof(int));
+    // one counter per (sequence, KV head) whatever the heads per workgroup,
+    // so that a launch with one head per workgroup fits the same workspace
+    p.ws_counter_bytes = align256((size_t)B * Hkv * sizeof(int));
   }
   p.ws_bytes = p.ws_ml_bytes + p.ws_acc_bytes + p.ws_counter_bytes;
   return p;

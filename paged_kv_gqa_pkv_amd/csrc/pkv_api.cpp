@@ -498,15 +498,18 @@ size_t pkv_prefill_workspace_bytes(int32_t B, int32_t max_q_len, int32_t Hq, int
   return pkv::plan_prefill(B, max_q_len, Hq, Hkv, max_context_len, device_cus()).ws_bytes;
 }
 
-static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
-                        const void* k_cache, const void* v_cache, const float* k_scales,
-                        const float* v_scales,
-                        const int32_t* block_tables,
-                        const int32_t* context_lens, int32_t B, int32_t total_q,
-                        int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
-                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                        int32_t max_context_len, int32_t window, float scale, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+// Host checks shared by the chunked-prefill entry points; fills the
+// key-split plan.  done = true: nothing to launch.
+static int check_prefill(void* out, const void* q, const int32_t* cu_q_lens,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t B, int32_t total_q,
+                         int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int32_t window, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream, pkv::PrefillPlan& plan,
+                         bool& done) {
+  done = true;
   if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0)
     return fail(PKV_EINVAL, "negative size");
@@ -532,7 +535,7 @@ static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
   // A ring's keys span at most window positions, i.e. window / 64 + 1 key tiles.
   const int32_t plan_ctx =
       window > 0 && max_context_len > window + 64 ? window + 64 : max_context_len;
-  const pkv::PrefillPlan plan = pkv::plan_prefill(B, max_q_len, Hq, Hkv, plan_ctx, device_cus());
+  plan = pkv::plan_prefill(B, max_q_len, Hq, Hkv, plan_ctx, device_cus());
   if (!plan.ok)
     return fail(PKV_EUNSUPPORTED, "max_context_len=%d exceeds the prefill kernel's 131072 keys",
                 max_context_len);
@@ -558,10 +561,30 @@ static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
                          max_context_len, s, window);
     if (rc) return rc;
   }
+  done = false;
+  return PKV_OK;
+}
+
+static int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens,
+                        const void* k_cache, const void* v_cache, const float* k_scales,
+                        const float* v_scales,
+                        const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t B, int32_t total_q,
+                        int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t D,
+                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, int32_t window, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  pkv::PrefillPlan plan;
+  bool done = true;
+  const int rc = check_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens,
+                               B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
+                               max_blocks_per_seq, max_context_len, window, scale, workspace,
+                               workspace_bytes, stream, plan, done);
+  if (rc || done) return rc;
   return launch_status(pkv::launch_prefill(out, q, cu_q_lens, k_cache, v_cache, k_scales, v_scales,
                                            block_tables, context_lens, B, total_q, max_q_len, Hq,
                                            Hkv, num_blocks, max_blocks_per_seq, scale, window,
-                                           plan, workspace, s),
+                                           plan, workspace, static_cast<hipStream_t>(stream)),
                        k_scales ? "pkv_attn_prefill_chunk_int8" : "pkv_attn_prefill_chunk");
 }
 
@@ -607,6 +630,69 @@ int pkv_attn_prefill_chunk_int8(void* out, const void* q, const int32_t* cu_q_le
                       context_lens, B, total_q, max_q_len, Hq, Hkv, D, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, 0, scale, workspace, workspace_bytes,
                       stream);
+}
+
+int pkv_attn_prefill_decode(void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
+                            const int32_t* block_tables_prefill,
+                            const int32_t* context_lens_prefill, int32_t B_prefill,
+                            int32_t total_q, int32_t max_q_len, int32_t max_context_len_prefill,
+                            void* out_decode, const void* q_decode,
+                            const int32_t* block_tables_decode,
+                            const int32_t* context_lens_decode, int32_t B_decode,
+                            int32_t max_context_len_decode, const void* k_cache,
+                            const void* v_cache, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            float scale, void* prefill_workspace, size_t prefill_workspace_bytes,
+                            void* decode_workspace, size_t decode_workspace_bytes,
+                            void* stream) {
+  pkv::PrefillPlan pplan;
+  bool pdone = true;
+  int rc = check_prefill(out_prefill, q_prefill, cu_q_lens, k_cache, v_cache,
+                         block_tables_prefill, context_lens_prefill, B_prefill, total_q,
+                         max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                         max_context_len_prefill, 0, scale, prefill_workspace,
+                         prefill_workspace_bytes, stream, pplan, pdone);
+  if (rc) return rc;
+  pkv::DecodePlan dplan;
+  bool ddone = false;
+  rc = check_decode(out_decode, q_decode, k_cache, v_cache, block_tables_decode,
+                    context_lens_decode, B_decode, Hq, Hkv, D, block_size, num_blocks,
+                    max_blocks_per_seq, max_context_len_decode, scale, decode_workspace,
+                    decode_workspace_bytes, stream, dplan, ddone);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!pdone && !ddone) {
+    if (out_prefill == out_decode) return fail(PKV_EINVAL, "the two outputs must differ");
+    if (pplan.ws_bytes && dplan.ws_bytes && prefill_workspace == decode_workspace)
+      return fail(PKV_EINVAL, "the two workspaces must differ");
+    if (pkv::mixed_plan_fits(dplan, Hq / Hkv))
+      return launch_status(
+          pkv::launch_prefill_decode(out_prefill, q_prefill, cu_q_lens, block_tables_prefill,
+                                     context_lens_prefill, B_prefill, total_q, max_q_len, pplan,
+                                     prefill_workspace, out_decode, q_decode,
+                                     block_tables_decode, context_lens_decode, B_decode, dplan,
+                                     decode_workspace, k_cache, v_cache, Hq, Hkv, num_blocks,
+                                     max_blocks_per_seq, scale, s),
+          "pkv_attn_prefill_decode");
+  }
+  // one half only, or a shape the one-grid launch does not take: the two
+  // launches one after the other
+  if (!pdone) {
+    rc = launch_status(pkv::launch_prefill(out_prefill, q_prefill, cu_q_lens, k_cache, v_cache,
+                                           nullptr, nullptr, block_tables_prefill,
+                                           context_lens_prefill, B_prefill, total_q, max_q_len,
+                                           Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0,
+                                           pplan, prefill_workspace, s),
+                       "pkv_attn_prefill_decode");
+    if (rc) return rc;
+  }
+  if (!ddone)
+    return launch_status(pkv::launch_decode(out_decode, q_decode, k_cache, v_cache,
+                                            block_tables_decode, context_lens_decode, B_decode,
+                                            Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0,
+                                            dplan, decode_workspace, s),
+                         "pkv_attn_prefill_decode");
+  return PKV_OK;
 }
 
 }  // extern "C"

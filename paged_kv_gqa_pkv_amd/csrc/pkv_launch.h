@@ -99,6 +99,7 @@ struct PrefillPlan {
   int tiles_per_split;
   size_t ws_acc_bytes;      // float [groups][S][D][128]
   size_t ws_ml_bytes;       // float [groups][S][128][2]
+  size_t ws_counter_bytes;  // int [groups], split arrivals (zero between calls)
   size_t ws_bytes;          // total, 0 without splits
 };
 
@@ -112,5 +113,19 @@ hipError_t launch_prefill(void* out, const void* q, const int32_t* cu_q, const v
                           const int32_t* ctx_lens, int B, int total_q, int max_q_len, int Hq,
                           int Hkv, int num_blocks, int max_blocks, float scale, int window,
                           const PrefillPlan& plan, void* workspace, hipStream_t stream);
+
+// Mixed step (bf16 pages): the chunk of launch_prefill and the decode of
+// launch_decode in one grid, each with its own plan and workspace.  Needs a
+// decode plan of 4 page-part waves and a group size G = Hq / Hkv of at most
+// 4 (mixed_plan_fits).
+bool mixed_plan_fits(const DecodePlan& dplan, int G);
+hipError_t launch_prefill_decode(void* out_p, const void* q_p, const int32_t* cu_q,
+                                 const int32_t* bt_p, const int32_t* ctx_p, int B_p, int total_q,
+                                 int max_q_len, const PrefillPlan& pplan, void* ws_p,
+                                 void* out_d, const void* q_d, const int32_t* bt_d,
+                                 const int32_t* ctx_d, int B_d, const DecodePlan& dplan,
+                                 void* ws_d, const void* k_cache, const void* v_cache, int Hq,
+                                 int Hkv, int num_blocks, int max_blocks, float scale,
+                                 hipStream_t stream);
 
 }  // namespace pkv

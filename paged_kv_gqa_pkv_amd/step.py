@@ -11,7 +11,9 @@ context, which gives the same numbers as the page's read-then-write order
 since the append is a bit copy.  A step with no prefill chunk (every
 sequence appends its one decode token) runs each layer as one fused call,
 pkv_attn_decode_append, which takes the step's own K/V from the new rows and
-writes them into their slots, as the page's forward does.
+writes them into their slots, as the page's forward does.  A step with both
+runs each layer as the append and one pkv_attn_prefill_decode call, whose
+single launch holds the chunk's and the decode's workgroups.
 
 Host code only marshals arguments: every operation is a library kernel.
 """
@@ -49,6 +51,7 @@ class StepPlan:
     prefill_workspace: Optional[torch.Tensor]
     scale: float
     fused: bool = False            # decode-only step: one fused append + decode call per layer
+    mixed: bool = False            # chunk and decode: one pkv_attn_prefill_decode call per layer
 
     @property
     def bt_prefill(self):
@@ -68,10 +71,12 @@ class StepPlan:
 
 
 def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = None,
-              fused: bool = True) -> StepPlan:
+              fused: bool = True, mixed: bool = True) -> StepPlan:
     """Index data and workspaces of a step.  fused: run a decode-only step as
     one pkv_attn_decode_append call per layer (else pkv_append, then
-    pkv_attn_decode)."""
+    pkv_attn_decode).  mixed: run the attention of a step with both chunks
+    and decode tokens as one pkv_attn_prefill_decode call per layer (else
+    pkv_attn_prefill_chunk, then pkv_attn_decode)."""
     pre, dec = w.prefill_seqs, w.decode_seqs
     if pre != list(range(len(pre))):
         raise ValueError("prefill sequences must come first")
@@ -105,7 +110,7 @@ def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = No
         max_q_len=max_q, max_ctx_prefill=max_ctx_pre,
         max_ctx_decode=max_ctx_dec, workspace=ws, prefill_workspace=pws,
         scale=scale if scale is not None else w.D ** -0.5,
-        fused=bool(fused and dec and not pre))
+        fused=bool(fused and dec and not pre), mixed=bool(mixed and dec and pre))
 
 
 def slot_mapping(plan: StepPlan, stream=None) -> None:
@@ -120,10 +125,11 @@ def layer(plan: StepPlan, k_cache, v_cache, k_new, v_new, q_decode=None, out_dec
           q_prefill=None, out_prefill=None, stream=None, decode_stream=None) -> None:
     """Append the layer's new K/V, then run the chunk and decode attention.
 
-    With ``decode_stream`` (a stream of default priority), a step that has
-    both runs its decode launch there, concurrently with the chunk: both only
-    read the pools once the append is done, so the decode stream waits for
-    the append and ``stream`` waits for the decode before anything after.
+    A plan made with mixed=False and a ``decode_stream`` (a stream of default
+    priority) runs a step that has both with its decode launch there,
+    concurrently with the chunk: both only read the pools once the append is
+    done, so the decode stream waits for the append and ``stream`` waits for
+    the decode before anything after.
     """
     s = stream if stream is not None else torch.cuda.current_stream()
     if plan.fused:
@@ -132,6 +138,14 @@ def layer(plan: StepPlan, k_cache, v_cache, k_new, v_new, q_decode=None, out_dec
                                   plan.scale, workspace=plan.workspace, stream=s)
         return
     bd.pkv_append(k_new, v_new, plan.slot_mapping, k_cache, v_cache, stream=s)
+    if plan.mixed:
+        bd.pkv_attn_prefill_decode(out_prefill, q_prefill, plan.cu_q, plan.bt_prefill,
+                                   plan.ctx_prefill, plan.max_q_len, plan.max_ctx_prefill,
+                                   out_decode, q_decode, plan.bt_decode, plan.ctx_decode,
+                                   plan.max_ctx_decode, k_cache, v_cache, plan.scale,
+                                   prefill_workspace=plan.prefill_workspace,
+                                   decode_workspace=plan.workspace, stream=s)
+        return
     both = bool(plan.n_prefill and plan.n_decode and decode_stream is not None)
     if both:
         appended = torch.cuda.Event()

@@ -216,3 +216,33 @@ def test_fused_decode_append_rejects_bad_arguments(lib):
     assert call(mcl=65) == bd.PKV_EINVAL                            # beyond the table
     assert call(out=7, q=7) == bd.PKV_EINVAL
     assert call(B=0, out=NULL, kn=NULL) == bd.PKV_OK
+
+
+def _mixed(lib, out_p=1, out_d=2, Bp=1, T=64, mql=64, mclp=64, Bd=2, mcld=64, Hq=16, Hkv=8,
+           D=128, mb=4, pws=NULL, pwb=0, dws=NULL, dwb=0):
+    return lib.pkv_attn_prefill_decode(out_p, 3, 4, 5, 6, Bp, T, mql, mclp,
+                                       out_d, 7, 8, 9, Bd, mcld, 10, 11, Hq, Hkv, D, 16, 32, mb,
+                                       0.088, pws, pwb, dws, dwb, NULL)
+
+
+def test_prefill_decode_rejects_bad_arguments(lib):
+    assert _mixed(lib, Hq=12) == bd.PKV_EUNSUPPORTED                # Hq % Hkv
+    assert _mixed(lib, D=64) == bd.PKV_EUNSUPPORTED
+    assert _mixed(lib, out_p=NULL) == bd.PKV_EINVAL                 # a half's null pointer
+    assert _mixed(lib, out_d=NULL) == bd.PKV_EINVAL
+    assert _mixed(lib, out_d=1) == bd.PKV_EINVAL                    # one output for both halves
+    assert b"outputs" in lib.pkv_last_error()
+    assert _mixed(lib, mql=65) == bd.PKV_EINVAL                     # max_q_len > total_q
+    # a decode half that needs split buffers, given none
+    need = bd.pkv_decode_workspace_bytes(2, 16, 8, 128, 64 * 16)
+    assert need > 0
+    assert _mixed(lib, mb=64, mcld=64 * 16) == bd.PKV_EWORKSPACE
+    # the same buffer as both workspaces
+    pneed = bd.pkv_prefill_workspace_bytes(1, 64, 16, 8, 128, 64 * 16)
+    assert pneed > 0
+    size = max(need, pneed)
+    assert _mixed(lib, mb=64, mcld=64 * 16, mclp=64 * 16, pws=99, pwb=size, dws=99,
+                  dwb=size) == bd.PKV_EINVAL
+    assert b"workspaces" in lib.pkv_last_error()
+    # nothing to do in either half
+    assert _mixed(lib, Bp=0, T=0, mql=0, Bd=0) == bd.PKV_OK

@@ -430,7 +430,7 @@ def test_concurrent_decode_stream_matches_and_replays():
                           base_seed=98)
     t = S.make_tables(w)
     d = S.make_layer(w, t, 0, device="cuda")
-    plan = ST.plan_step(w, t)
+    plan = ST.plan_step(w, t, mixed=False)      # the two-launch path
     k0, v0 = d.k_cache.clone(), d.v_cache.clone()
     out_d, out_p = torch.empty_like(d.q_decode), torch.empty_like(d.q_prefill)
 

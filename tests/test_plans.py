@@ -52,17 +52,19 @@ def test_prefill_workspace_covers_the_partials(lib):
         assert ws >= 0
         if ws:
             # at least two splits of every (128-row tile, KV head) group: partial
-            # outputs [D][128] and (m, l) [128][2] in fp32
+            # outputs [D][128] and (m, l) [128][2] in fp32, and a counter each
             groups = B * -(-T * (Hq // Hkv) // 128) * Hkv
-            assert ws >= groups * 2 * 128 * (D + 2) * 4, (B, T, Hq, Hkv, ctx, ws)
+            assert ws >= groups * (2 * 128 * (D + 2) * 4 + 4), (B, T, Hq, Hkv, ctx, ws)
 
 
 def test_prefill_plans_quoted_in_the_measurements(lib):
     # short contexts (at most 4 key tiles) run without splits
     assert bd.pkv_prefill_workspace_bytes(2, 106, 16, 8, D, 256) == 0
     # a c5 chunk (Qwen3-0.6B heads, 512 queries, up to 3000 keys): 8 row tiles
-    # x 8 KV heads x 4 key splits of partials [D][128] and (m, l) [128][2]
-    assert bd.pkv_prefill_workspace_bytes(1, 512, 16, 8, D, 3000) == 64 * 4 * 128 * (D + 2) * 4
+    # x 8 KV heads x 4 key splits of partials [D][128] and (m, l) [128][2],
+    # then one arrival counter per (row tile, KV head), padded to 256 bytes
+    assert bd.pkv_prefill_workspace_bytes(1, 512, 16, 8, D, 3000) == \
+        64 * 4 * 128 * (D + 2) * 4 + 256
     # the longest supported context, and one key more (unsupported: 0)
     assert bd.pkv_prefill_workspace_bytes(1, 64, 32, 8, D, 131072) > 0
     assert bd.pkv_prefill_workspace_bytes(1, 64, 32, 8, D, 131073) == 0
