@@ -6,10 +6,11 @@
 // for every sequence b and query head h the softmax-weighted sum of the V
 // rows of KV head h / G over positions 0 .. context_lens[b]-1.
 //
-// Decomposition.  One workgroup owns one (sequence b, KV head g, context
-// split) and serves all G = Hq/Hkv query heads of the group from the same
-// loaded K/V rows, so every K/V byte is read from HBM once per step.  The
-// workgroup's 4 waves take disjoint page ranges of the split.  Pages are
+// Decomposition.  One workgroup owns one (sequence b, context split, group
+// of heads_per_wg KV heads) and serves all G = Hq/Hkv query heads of each
+// KV head from the same loaded K/V rows, so every K/V byte is read from HBM
+// once per step.  Each KV head has `parts` waves, which take disjoint page
+// ranges of the split.  Pages are
 // stored token-major as in the Module 12 page's paged.py ([page][16 slots][KV
 // head][D]), so a 16-token page of one head is 16 rows of 256 B, Hkv*256 B
 // apart: lane l holds rows (l>>3) and (l>>3)+8 and the 16-byte chunks (l&7)
@@ -25,8 +26,8 @@
 //
 // Long contexts with few (sequence, head) pairs are cut into splits of
 // pages_per_split pages (flash-decoding); each split writes its unnormalised
-// (m, l, acc) to the workspace, and the last split of a (sequence, KV head)
-// to finish merges them all in split order, so results are run-to-run
+// (m, l, acc) to the workspace, and the last split of a (sequence, head
+// group) to finish merges them all in split order, so results are run-to-run
 // bit-identical and the whole call is one kernel.
 //
 // This header holds the device code (and the host-side argument packing)
