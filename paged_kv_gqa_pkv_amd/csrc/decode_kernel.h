@@ -156,6 +156,36 @@ __device__ __forceinline__ float softmax_ref(const float (&s)[U][2], float& m, f
   return (m == kNegInf) ? 0.f : m;
 }
 
+// One reduce-scatter step of the lane states: exchange with lane ^ (8 << K)
+// (row bit K of the lane), keep the upper half of `in` if that bit is set,
+// else the lower half, merged with the partner's copy of the same half.
+template <int K>
+__device__ __forceinline__ float xchg(float x) {
+  if constexpr (K == 0)
+    return xor8(x);
+  else
+    return shfl_xor(x, 8 << K);
+}
+template <int K, int N>
+__device__ __forceinline__ void rs_step(float& m, float& l, const float (&in)[N],
+                                        float (&out)[N / 2], int r0) {
+  const bool hi = (r0 >> K) & 1;
+  float send[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    send[i] = hi ? in[i] : in[N / 2 + i];
+    out[i] = hi ? in[N / 2 + i] : in[i];
+  }
+  const float mo = xchg<K>(m), lo = xchg<K>(l);
+  const float M = fmaxf(m, mo);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  const float wa = fast_exp2(m - Mu), wb = fast_exp2(mo - Mu);
+  l = l * wa + lo * wb;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) out[i] = out[i] * wa + xchg<K>(send[i]) * wb;
+  m = M;
+}
+
 // bf16 pages.  A 16-token page of one head is 16 rows of 256 B, one per slot
 // (Hkv rows apart): lane l holds rows r0 = l>>3 and r0+8, and the 16-byte
 // chunks c = l&7 and c+8 of each, i.e. head dims 8c..8c+7 and 64+8c..64+8c+7
@@ -168,13 +198,40 @@ struct Bf16Page {
   static __device__ __forceinline__ int dim(int c, int d) {
     return d < 8 ? 8 * c + d : 64 + 8 * c + (d - 8);
   }
-  static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
-    const u32x4 lo = qp[c], hi = qp[c + 8];
+  // q of the G heads: the lane's two 16-byte chunks of each.
+  template <int G>
+  struct Q {
+    uint32_t w[G][8];
+  };
+  // Per-lane online-softmax state of each head over the lane's rows.
+  template <int G>
+  struct State {
+    float m[G], l[G], acc[G][16];
+  };
+  template <int G>
+  static __device__ __forceinline__ void init(State<G>& st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { qw[i] = lo[i]; qw[4 + i] = hi[i]; }
+    for (int j = 0; j < G; ++j) {
+      st.m[j] = kNegInf;
+      st.l[j] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) st.acc[j][d] = 0.f;
+    }
+  }
+  // qp: the group's first head (16 chunks per head).
+  template <int G>
+  static __device__ __forceinline__ void load_q(Q<G>& q, const u32x4* qp, int lane) {
+    const int c = lane & 7;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const u32x4 lo = qp[16 * j + c], hi = qp[16 * j + c + 8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { q.w[j][i] = lo[i]; q.w[j][4 + i] = hi[i]; }
+    }
   }
   static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
-                                              int r0, int c) {
+                                              int lane) {
+    const int r0 = lane >> 3, c = lane & 7;
     const int64_t base = ((blk * kPage + r0) * a.Hkv + g) * 16 + c;   // 16 chunks per row
     const int64_t r8 = (int64_t)8 * a.Hkv * 16;                       // row r0 + 8
     const u32x4* kp = a.k_cache + base;
@@ -191,10 +248,14 @@ struct Bf16Page {
   // valid_rows are excluded (score -inf, V forced to 0 so canary data cannot
   // leak).
   template <int G, int U, bool kMask>
-  static __device__ __forceinline__ void process(const Regs (&buf)[U], const uint32_t (&qw)[G][8],
-                                                 float (&m)[G], float (&l)[G],
-                                                 float (&acc)[G][16], float scale_log2, int r0,
+  static __device__ __forceinline__ void process(const Regs (&buf)[U], const Q<G>& q,
+                                                 State<G>& st, float scale_log2, int lane,
                                                  int valid_rows) {
+    const int r0 = lane >> 3;
+    const uint32_t (&qw)[G][8] = q.w;
+    float (&m)[G] = st.m;
+    float (&l)[G] = st.l;
+    float (&acc)[G][16] = st.acc;
     float s[G][U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -244,6 +305,28 @@ struct Bf16Page {
         }
     }
   }
+  // The wave's merged state of each head, two dims per lane: a
+  // reduce-scatter over the 8 row groups (lane bits r0 = 0..2).  At step k
+  // each lane merges half of its accumulators with those of lane ^ (8 << k)
+  // and keeps that half, so after three steps lane (r0, c) holds head dims
+  // d0 and d0 + 1 of its 16 (dim(c, .)), d0 = 8 (r0 & 1) + 4 ((r0 >> 1) & 1)
+  // + 2 (r0 >> 2).  Returns the first of the two dims; m and l come out the
+  // same in every lane.
+  template <int G>
+  static __device__ __forceinline__ int finish(State<G>& st, float (&m)[G], float (&l)[G],
+                                               float (&v2)[G][2], int lane) {
+    const int r0 = lane >> 3, c = lane & 7;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float v8[8], v4[4];
+      rs_step<0, 16>(st.m[j], st.l[j], st.acc[j], v8, r0);
+      rs_step<1, 8>(st.m[j], st.l[j], v8, v4, r0);
+      rs_step<2, 4>(st.m[j], st.l[j], v4, v2[j], r0);
+      m[j] = st.m[j];
+      l[j] = st.l[j];
+    }
+    return dim(c, 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2));
+  }
 };
 
 // int8 pages (codes with one float32 scale per (slot, head), read as
@@ -265,13 +348,29 @@ struct Int8Page {
     float s;         // lane c & 3 of the quad: K(r0), K(r0+8), V(r0), V(r0+8)
   };
   static __device__ __forceinline__ int dim(int c, int d) { return 16 * c + d; }
-  static __device__ __forceinline__ void load_q(uint32_t (&qw)[8], const u32x4* qp, int c) {
-    const u32x4 lo = qp[2 * c], hi = qp[2 * c + 1];
+  template <int G>
+  struct Q {
+    uint32_t w[G][8];     // q of dims 16c .. 16c+15 of each head
+  };
+  template <int G>
+  using State = Bf16Page::State<G>;
+  template <int G>
+  static __device__ __forceinline__ void init(State<G>& st) {
+    Bf16Page::init<G>(st);
+  }
+  template <int G>
+  static __device__ __forceinline__ void load_q(Q<G>& q, const u32x4* qp, int lane) {
+    const int c = lane & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { qw[i] = lo[i]; qw[4 + i] = hi[i]; }
+    for (int j = 0; j < G; ++j) {
+      const u32x4 lo = qp[16 * j + 2 * c], hi = qp[16 * j + 2 * c + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { q.w[j][i] = lo[i]; q.w[j][4 + i] = hi[i]; }
+    }
   }
   static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
-                                              int r0, int c) {
+                                              int lane) {
+    const int r0 = lane >> 3, c = lane & 7;
     const int64_t row = (blk * kPage + r0) * a.Hkv + g;        // 8 chunks per row
     const int64_t r8 = (int64_t)8 * a.Hkv;                      // row r0 + 8
     r.k[0] = load_kv(a.k_cache + row * 8 + c);
@@ -285,10 +384,14 @@ struct Int8Page {
     return bf16x2{(__bf16)sbyte(w, lo), (__bf16)sbyte(w, lo + 1)};
   }
   template <int G, int U, bool kMask>
-  static __device__ __forceinline__ void process(const Regs (&buf)[U], const uint32_t (&qw)[G][8],
-                                                 float (&m)[G], float (&l)[G],
-                                                 float (&acc)[G][16], float scale_log2, int r0,
+  static __device__ __forceinline__ void process(const Regs (&buf)[U], const Q<G>& q,
+                                                 State<G>& st, float scale_log2, int lane,
                                                  int valid_rows) {
+    const int r0 = lane >> 3;
+    const uint32_t (&qw)[G][8] = q.w;
+    float (&m)[G] = st.m;
+    float (&l)[G] = st.l;
+    float (&acc)[G][16] = st.acc;
     // the quad's four scales in every lane: K(r0), K(r0+8), V(r0), V(r0+8)
     float ks[U][2], vs[U][2];
 #pragma unroll
@@ -354,37 +457,23 @@ struct Int8Page {
       }
     }
   }
-};
-
-// One reduce-scatter step of the lane states: exchange with lane ^ (8 << K)
-// (row bit K of the lane), keep the upper half of `in` if that bit is set,
-// else the lower half, merged with the partner's copy of the same half.
-template <int K>
-__device__ __forceinline__ float xchg(float x) {
-  if constexpr (K == 0)
-    return xor8(x);
-  else
-    return shfl_xor(x, 8 << K);
-}
-template <int K, int N>
-__device__ __forceinline__ void rs_step(float& m, float& l, const float (&in)[N],
-                                        float (&out)[N / 2], int r0) {
-  const bool hi = (r0 >> K) & 1;
-  float send[N / 2];
+  // As Bf16Page::finish; the lane's 16 dims are 16c .. 16c+15.
+  template <int G>
+  static __device__ __forceinline__ int finish(State<G>& st, float (&m)[G], float (&l)[G],
+                                               float (&v2)[G][2], int lane) {
+    const int r0 = lane >> 3, c = lane & 7;
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    send[i] = hi ? in[i] : in[N / 2 + i];
-    out[i] = hi ? in[N / 2 + i] : in[i];
+    for (int j = 0; j < G; ++j) {
+      float v8[8], v4[4];
+      rs_step<0, 16>(st.m[j], st.l[j], st.acc[j], v8, r0);
+      rs_step<1, 8>(st.m[j], st.l[j], v8, v4, r0);
+      rs_step<2, 4>(st.m[j], st.l[j], v4, v2[j], r0);
+      m[j] = st.m[j];
+      l[j] = st.l[j];
+    }
+    return dim(c, 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2));
   }
-  const float mo = xchg<K>(m), lo = xchg<K>(l);
-  const float M = fmaxf(m, mo);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  const float wa = fast_exp2(m - Mu), wb = fast_exp2(mo - Mu);
-  l = l * wa + lo * wb;
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) out[i] = out[i] * wa + xchg<K>(send[i]) * wb;
-  m = M;
-}
+};
 
 // Workgroup = one (sequence b, context split, group of heads_per_wg KV
 // heads); its heads_per_wg * parts waves are (head hw, page part pw), wave
@@ -428,9 +517,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs a, const int bid) {
   const int wp0 = p0 + pw * ppw;
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
   const int my_id = (lane < ppw && wp0 + lane < a.max_blocks) ? bt[wp0 + lane] : 0;
-  uint32_t qw[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j) P::load_q(qw[j], a.q + ((int64_t)b * a.Hq + g * G + j) * 16, c);
+  typename P::template Q<G> qv;
+  P::template load_q<G>(qv, a.q + ((int64_t)b * a.Hq + g * G) * 16, lane);
 
   // A length outside [0, planned maximum] poisons the outputs of the sequence
   // (the plan covers splits * pages_per_split pages; no read goes past it).
@@ -502,13 +590,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs a, const int bid) {
   const int nfull = max(0, min(w1, n_full) - w0);
   const bool has_tail = (n_cache % kPage) != 0 && n_full >= w0 && n_full < w1;
 
-  float m[G], l[G], acc[G][16];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = kNegInf; l[j] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) acc[j][d] = 0.f;
-  }
+  typename P::template State<G> st;
+  P::template init<G>(st);
 
   const int id_base = w0 - wp0;               // lane of my_id holding page w0
   int bad = (bad_len || (has_new && new_bad)) ? 1 : 0;
@@ -532,7 +615,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs a, const int bid) {
   __builtin_amdgcn_s_waitcnt(0);
   if (ngroups > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id(u), g, r0, c);
+    for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id(u), g, lane);
     const int steady = (ngroups - 1) / 2;
     // The scheduling barriers keep each prefetch between the two reductions:
     // issued before the group it overlaps is reduced, and after the group
@@ -541,56 +624,45 @@ __device__ __forceinline__ void decode_body(const DecodeArgs a, const int bid) {
     for (int pi = 0; pi < steady; ++pi) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) P::load(bufB[u], a, page_id((2 * pi + 1) * U + u), g, r0, c);
+      for (int u = 0; u < U; ++u) P::load(bufB[u], a, page_id((2 * pi + 1) * U + u), g, lane);
       __builtin_amdgcn_sched_barrier(0);
-      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
+      P::template process<G, U, false>(bufA, qv, st, a.scale_log2, lane, kPage);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id((2 * pi + 2) * U + u), g, r0, c);
+      for (int u = 0; u < U; ++u) P::load(bufA[u], a, page_id((2 * pi + 2) * U + u), g, lane);
       __builtin_amdgcn_sched_barrier(0);
-      P::template process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
+      P::template process<G, U, false>(bufB, qv, st, a.scale_log2, lane, kPage);
     }
     if (ngroups - 2 * steady == 2) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        P::load(bufB[u], a, page_id((2 * steady + 1) * U + u), g, r0, c);
-      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
-      P::template process<G, U, false>(bufB, qw, m, l, acc, a.scale_log2, r0, kPage);
+        P::load(bufB[u], a, page_id((2 * steady + 1) * U + u), g, lane);
+      P::template process<G, U, false>(bufA, qv, st, a.scale_log2, lane, kPage);
+      P::template process<G, U, false>(bufB, qv, st, a.scale_log2, lane, kPage);
     } else {
-      P::template process<G, U, false>(bufA, qw, m, l, acc, a.scale_log2, r0, kPage);
+      P::template process<G, U, false>(bufA, qv, st, a.scale_log2, lane, kPage);
     }
   }
   // Leftover full pages (fewer than U), one at a time.
   for (int j = ngroups * U; j < nfull; ++j) {
     typename P::Regs one[1];
-    P::load(one[0], a, page_id(j), g, r0, c);
-    P::template process<G, 1, false>(one, qw, m, l, acc, a.scale_log2, r0, kPage);
+    P::load(one[0], a, page_id(j), g, lane);
+    P::template process<G, 1, false>(one, qv, st, a.scale_log2, lane, kPage);
   }
   if (has_tail) {
     typename P::Regs one[1];
-    P::load(one[0], a, page_id(n_full - w0), g, r0, c);
-    P::template process<G, 1, true>(one, qw, m, l, acc, a.scale_log2, r0, n_cache % kPage);
+    P::load(one[0], a, page_id(n_full - w0), g, lane);
+    P::template process<G, 1, true>(one, qv, st, a.scale_log2, lane, n_cache % kPage);
   }
   if constexpr (kAppend) {
     // the new position as a page whose only valid row is row 0 (lanes 0..7)
-    if (has_new) P::template process<G, 1, true>(nrow, qw, m, l, acc, a.scale_log2, r0, 1);
+    if (has_new) P::template process<G, 1, true>(nrow, qv, st, a.scale_log2, lane, 1);
   }
 
-  // Reduce-scatter over the wave's 8 row groups (lane bits r0 = 0..2): at
-  // step k each lane merges half of its accumulators with those of lane
-  // ^ (8 << k) and keeps that half, so after three steps lane (r0, c) holds
-  // the wave's merged state for two head dims, d0 and d0 + 1 of its 16
-  // (P::dim(c, .)), with d0 = 8 (r0 & 1) + 4 ((r0 >> 1) & 1) + 2 (r0 >> 2).
-  float v2[G][2];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float v8[8], v4[4];
-    rs_step<0, 16>(m[j], l[j], acc[j], v8, r0);
-    rs_step<1, 8>(m[j], l[j], v8, v4, r0);
-    rs_step<2, 4>(m[j], l[j], v4, v2[j], r0);
-  }
-  const int d0 = 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2);
-  const int dd = P::dim(c, d0);               // head dims dd, dd + 1
+  // The wave's merged state of each head, two head dims per lane (dd and
+  // dd + 1), the same (m, l) in every lane.
+  float m[G], l[G], v2[G][2];
+  const int dd = P::template finish<G>(st, m, l, v2, lane);
 
   // Merge the page parts of each head through LDS into its part-0 wave.
   if (PW > 1) {
