@@ -332,144 +332,224 @@ struct Bf16Page {
 // int8 pages (codes with one float32 scale per (slot, head), read as
 // code * scale; Module 04 page, kv_cache.py listing, section 5).  A page of
 // one head is 16 rows of 128 codes (Hkv*128 B apart) plus 16 K and 16 V
-// scales: lane l holds rows r0 = l>>3 and r0+8 and the 16-byte chunk c = l&7
-// of each (head dims 16c..16c+15).  The four scales of those two rows are
-// loaded once per 4-lane quad, lane c & 3 of it taking K(r0), K(r0+8), V(r0)
-// or V(r0+8), and handed to the whole quad by DPP broadcasts (a page is 5
-// loads per lane).  Codes are integers in [-127, 127], exact in bf16, so
-// q . codes runs on v_dot2_f32_bf16 and the row's K scale multiplies the
-// score; the row's V scale is folded into its probability before the PV
-// product.
-constexpr int kQuadBcast0 = 0x00, kQuadBcast1 = 0x55, kQuadBcast2 = 0xAA, kQuadBcast3 = 0xFF;
+// scales.  Codes are integers in [-127, 127], exact in bf16.
+//
+// The scores run on the matrix cores: S[key][head] = codes[key] . q[head]
+// for the page's 16 keys is four v_mfma_f32_16x16x32_bf16 (16 keys x 16
+// head columns, G of them used, 32 dims each).  The K rows arrive as in the
+// bf16 policy (lane (r0, c) = (l>>3, l&7): 16-byte chunk c of rows r0 and
+// r0+8, so every load instruction moves eight whole 128-byte lines) and go
+// through a wave-private LDS buffer, whose rows keep their chunks swizzled
+// by row, to the MFMA operand layout: lane (g4, t) = (l>>4, l&15) takes key
+// row t, dims 32 g4 .. 32 g4 + 31 (and q of head t, the same dims, as the
+// other operand; zero for t >= G), and gets back S of keys 4 g4 .. 4 g4 + 3
+// for head t.  (Loading the operand layout straight from memory splits
+// each row over four lanes: half-used lines per instruction, which the
+// counters showed saturating the L1's tag lookups.)  Lane (g4, t < G) keeps
+// head t's online-softmax reference and row sum over the keys 4 g4 .. +3 of
+// every page; the keys' K scales turn S into scores, the V scales scale the
+// probabilities, and DPP row broadcasts hand those weights to the 16 lanes
+// of row g4.  There the PV product runs on v_dot2_f32_bf16: lane (g4, t)
+// holds chunk t & 7 (16 dims) of keys 4 g4 + (t >> 3) and 4 g4 + 2 + (t >> 3)
+// (again whole lines per load instruction), paired with those two keys'
+// weights.  Every lane of a row uses that row's references, so a rescale of
+// head j's accumulators takes lane (g4, j)'s factor.
+template <int n>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp_f<0x150 + n>(x);     // row_newbcast: lane n of each row of 16
+}
+template <int n>
+__device__ __forceinline__ uint32_t row_bcast_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + n, 0xf, 0xf, false);
+}
+// Lane n's value of each row of 16, n = 0 .. G-1, for a compile-time G.
+template <int G>
+__device__ __forceinline__ void row_bcast_all(float x, float (&out)[G]) {
+  if constexpr (G > 0) out[0] = row_bcast<0>(x);
+  if constexpr (G > 1) out[1] = row_bcast<1>(x);
+  if constexpr (G > 2) { out[2] = row_bcast<2>(x); out[3] = row_bcast<3>(x); }
+  if constexpr (G > 4) {
+    out[4] = row_bcast<4>(x); out[5] = row_bcast<5>(x);
+    out[6] = row_bcast<6>(x); out[7] = row_bcast<7>(x);
+  }
+}
+template <int G>
+__device__ __forceinline__ void row_bcast_all_u(uint32_t x, uint32_t (&out)[G]) {
+  if constexpr (G > 0) out[0] = row_bcast_u<0>(x);
+  if constexpr (G > 1) out[1] = row_bcast_u<1>(x);
+  if constexpr (G > 2) { out[2] = row_bcast_u<2>(x); out[3] = row_bcast_u<3>(x); }
+  if constexpr (G > 4) {
+    out[4] = row_bcast_u<4>(x); out[5] = row_bcast_u<5>(x);
+    out[6] = row_bcast_u<6>(x); out[7] = row_bcast_u<7>(x);
+  }
+}
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int kI8LdsWaves = 8;    // waves of a workgroup (at most)
+constexpr int kI8LdsPages = 2;    // pages per process call (at most)
+// The K transpose buffers, 2 KB per (wave, page): one array per kernel
+// (declared in a function that is not a template, so the instantiations of
+// the page loop share it).
+__device__ __forceinline__ u32x4 (*i8_k_lds())[kI8LdsPages][kPage * 8] {
+  __shared__ u32x4 s_k[kI8LdsWaves][kI8LdsPages][kPage * 8];
+  return s_k;
+}
+
 struct Int8Page {
   struct Regs {
-    u32x4 k[2];      // [row r0 / r0+8], 16 codes each
-    u32x4 v[2];
-    float s;         // lane c & 3 of the quad: K(r0), K(r0+8), V(r0), V(r0+8)
+    u32x4 k[2];      // rows r0 and r0 + 8: chunk c
+    u32x4 v[2];      // keys 4 g4 + (t >> 3) and that + 2: chunk t & 7
+    float s;         // t < 4: K scale of key 4 g4 + t; t = 4..7: V scale of key 4 g4 + t - 4
   };
   static __device__ __forceinline__ int dim(int c, int d) { return 16 * c + d; }
   template <int G>
   struct Q {
-    uint32_t w[G][8];     // q of dims 16c .. 16c+15 of each head
+    bf16x8 b[4];     // head t's q, dims 32 g4 + 8 kk .. +8, per MFMA kk
   };
   template <int G>
-  using State = Bf16Page::State<G>;
+  struct State {
+    float m, l;          // lane (g4, t < G): head t over keys 4 g4 .. +3 of each page
+    float acc[G][16];    // dims 16 (t & 7) .. +16 of each head; row g4's references
+  };
   template <int G>
   static __device__ __forceinline__ void init(State<G>& st) {
-    Bf16Page::init<G>(st);
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int d = 0; d < 16; ++d) st.acc[j][d] = 0.f;
   }
   template <int G>
   static __device__ __forceinline__ void load_q(Q<G>& q, const u32x4* qp, int lane) {
-    const int c = lane & 7;
+    const int t = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const u32x4 lo = qp[16 * j + 2 * c], hi = qp[16 * j + 2 * c + 1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { q.w[j][i] = lo[i]; q.w[j][4 + i] = hi[i]; }
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t < G) v = qp[16 * t + 4 * g4 + kk];
+      q.b[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
   static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
                                               int lane) {
-    const int r0 = lane >> 3, c = lane & 7;
-    const int64_t row = (blk * kPage + r0) * a.Hkv + g;        // 8 chunks per row
-    const int64_t r8 = (int64_t)8 * a.Hkv;                      // row r0 + 8
-    r.k[0] = load_kv(a.k_cache + row * 8 + c);
-    r.k[1] = load_kv(a.k_cache + (row + r8) * 8 + c);
-    r.v[0] = load_kv(a.v_cache + row * 8 + c);
-    r.v[1] = load_kv(a.v_cache + (row + r8) * 8 + c);
-    r.s = ((c & 2) ? a.v_scales : a.k_scales)[row + ((c & 1) ? r8 : 0)];
-  }
-  // Codes of one 4-code word as two bf16 pairs (exact).
-  static __device__ __forceinline__ bf16x2 pair(uint32_t w, int lo) {
-    return bf16x2{(__bf16)sbyte(w, lo), (__bf16)sbyte(w, lo + 1)};
+    const int r0 = lane >> 3, c = lane & 7, t = lane & 15, g4 = lane >> 4;
+    const int64_t krow = (blk * kPage + r0) * a.Hkv + g;            // 8 chunks per row
+    const int64_t r8 = (int64_t)8 * a.Hkv;                           // row r0 + 8
+    r.k[0] = load_kv(a.k_cache + krow * 8 + c);
+    r.k[1] = load_kv(a.k_cache + (krow + r8) * 8 + c);
+    const int64_t vrow = (blk * kPage + 4 * g4 + (t >> 3)) * a.Hkv + g;
+    const int64_t r2 = (int64_t)2 * a.Hkv;                           // key + 2
+    r.v[0] = load_kv(a.v_cache + vrow * 8 + (t & 7));
+    r.v[1] = load_kv(a.v_cache + (vrow + r2) * 8 + (t & 7));
+    const int64_t srow = (blk * kPage + 4 * g4 + (t & 3)) * a.Hkv + g;
+    r.s = ((t & 4) ? a.v_scales : a.k_scales)[srow];
   }
   template <int G, int U, bool kMask>
   static __device__ __forceinline__ void process(const Regs (&buf)[U], const Q<G>& q,
                                                  State<G>& st, float scale_log2, int lane,
                                                  int valid_rows) {
-    const int r0 = lane >> 3;
-    const uint32_t (&qw)[G][8] = q.w;
-    float (&m)[G] = st.m;
-    float (&l)[G] = st.l;
-    float (&acc)[G][16] = st.acc;
-    // the quad's four scales in every lane: K(r0), K(r0+8), V(r0), V(r0+8)
-    float ks[U][2], vs[U][2];
+    static_assert(U <= kI8LdsPages, "LDS pages per wave");
+    u32x4 (*s_k)[kI8LdsPages][kPage * 8] = i8_k_lds();
+    const int wv = uniform(threadIdx.x >> 6);
+    const int r0 = lane >> 3, c = lane & 7, t = lane & 15, g4 = lane >> 4;
+    // the K rows of this call's pages into the wave's buffer (chunk cc of
+    // row r at position cc ^ (r & 7))
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      ks[u][0] = dpp_f<kQuadBcast0>(buf[u].s);
-      ks[u][1] = dpp_f<kQuadBcast1>(buf[u].s);
-      vs[u][0] = dpp_f<kQuadBcast2>(buf[u].s);
-      vs[u][1] = dpp_f<kQuadBcast3>(buf[u].s);
+      s_k[wv][u][r0 * 8 + (c ^ (r0 & 7))] = buf[u].k[0];
+      s_k[wv][u][(r0 + 8) * 8 + (c ^ (r0 & 7))] = buf[u].k[1];
     }
-    float s[G][U][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        bf16x2 kp[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kp[2 * i] = pair(buf[u].k[rr][i], 0);
-          kp[2 * i + 1] = pair(buf[u].k[rr][i], 2);
-        }
-        const float rs = ks[u][rr] * scale_log2;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          float d = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            d = __builtin_amdgcn_fdot2_f32_bf16(kp[i], as_bf16x2(qw[j][i]), d, false);
-          d = sum8(d) * rs;
-          if (kMask) d = (r0 + 8 * rr < valid_rows) ? d : kNegInf;
-          s[j][u][rr] = d;
-        }
-      }
-    bf16x2 pp[U][G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mu = softmax_ref<U>(s[j], m[j], l[j], acc[j]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p0 = fast_exp2(s[j][u][0] - mu), p1 = fast_exp2(s[j][u][1] - mu);
-        l[j] += p0 + p1;
-        // masked rows: weight exactly 0 (their scale may be a NaN canary)
-        const float w0 = (!kMask || r0 < valid_rows) ? p0 * vs[u][0] : 0.f;
-        const float w1 = (!kMask || r0 + 8 < valid_rows) ? p1 * vs[u][1] : 0.f;
-        pp[u][j] = bf16x2{(__bf16)w0, (__bf16)w1};
-      }
-    }
+    // the wave's LDS accesses run in order; keep the compiler from moving
+    // the reads above the writes of other lanes
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool keep0 = !kMask || (r0 < valid_rows);
-      const bool keep1 = !kMask || (r0 + 8 < valid_rows);
+      const u32x4 ka = s_k[wv][u][t * 8 + ((2 * g4) ^ (t & 7))];
+      const u32x4 kb = s_k[wv][u][t * 8 + ((2 * g4 + 1) ^ (t & 7))];
+      f32x4v s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = keep0 ? buf[u].v[0][i] : 0u;   // row r0, dims 4i .. 4i+3
-        const uint32_t w1 = keep1 ? buf[u].v[1][i] : 0u;   // row r0 + 8
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4& kw = (kk < 2) ? ka : kb;
+        const uint32_t w0 = kw[2 * (kk & 1)], w1 = kw[2 * (kk & 1) + 1];
+        const bf16x8 a8 = {(__bf16)sbyte0(w0), (__bf16)sbyte1(w0), (__bf16)sbyte2(w0),
+                           (__bf16)sbyte3(w0), (__bf16)sbyte0(w1), (__bf16)sbyte1(w1),
+                           (__bf16)sbyte2(w1), (__bf16)sbyte3(w1)};
+        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, q.b[kk], s4, 0, 0, 0);
+      }
+      const float ks[4] = {row_bcast<0>(buf[u].s), row_bcast<1>(buf[u].s),
+                           row_bcast<2>(buf[u].s), row_bcast<3>(buf[u].s)};
+      const float vs[4] = {row_bcast<4>(buf[u].s), row_bcast<5>(buf[u].s),
+                           row_bcast<6>(buf[u].s), row_bcast<7>(buf[u].s)};
+      float sc[4];
+      bool keep[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        keep[rr] = !kMask || 4 * g4 + rr < valid_rows;
+        sc[rr] = keep[rr] ? s4[rr] * (ks[rr] * scale_log2) : kNegInf;
+      }
+      // this lane's reference, raised (wave-uniformly skipped) only when a
+      // score exceeds it by more than the slack
+      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const bool up = t < G && mx > st.m + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+        const float alpha = up ? fast_exp2(st.m - mx) : 1.f;   // m = -inf gives 0
+        st.m = up ? mx : st.m;
+        st.l *= alpha;
+        float aj[G];
+        row_bcast_all<G>(alpha, aj);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int d = 0; d < 16; ++d) st.acc[j][d] *= aj[j];
+      }
+      const float mu = (st.m == kNegInf) ? 0.f : st.m;
+      float p[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(sc[rr] - mu);
+      st.l += (p[0] + p[1]) + (p[2] + p[3]);
+      // PV weights p * V scale as bf16 pairs of keys (0, 2) and (1, 3) of
+      // the row's four; masked keys weigh exactly 0 (their scale may be a
+      // NaN canary)
+      float wv4[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) wv4[rr] = keep[rr] ? p[rr] * vs[rr] : 0.f;
+      uint32_t w02[G], w13[G];
+      row_bcast_all_u<G>(pack_bf16x2(wv4[0], wv4[2]), w02);
+      row_bcast_all_u<G>(pack_bf16x2(wv4[1], wv4[3]), w13);
+      const bool odd = (t & 8) != 0;           // keys 4 g4 + 1 and + 3
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bf16x2 vv = bf16x2{(__bf16)sbyte(w0, e), (__bf16)sbyte(w1, e)};
+          const bf16x2 vv = {(__bf16)sbyte(buf[u].v[0][i], e), (__bf16)sbyte(buf[u].v[1][i], e)};
           const int d = 4 * i + e;
 #pragma unroll
           for (int j = 0; j < G; ++j)
-            acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(vv, pp[u][j], acc[j][d], false);
+            st.acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(
+                vv, as_bf16x2(odd ? w13[j] : w02[j]), st.acc[j][d], false);
         }
-      }
     }
   }
-  // As Bf16Page::finish; the lane's 16 dims are 16c .. 16c+15.
+  // Every lane of row g4 takes that row's (m, l) of head j from lane
+  // (g4, j), l counted once for the two lanes t and t ^ 8 that hold the same
+  // dims of different keys; then the reduce-scatter of the bf16 policy over
+  // lane ^ 8, ^ 16 and ^ 32 (the same bits as its rows r0) leaves lane l
+  // with dims dim(l & 7, d0) and the next, and the same (m, l) in every lane.
   template <int G>
   static __device__ __forceinline__ int finish(State<G>& st, float (&m)[G], float (&l)[G],
                                                float (&v2)[G][2], int lane) {
     const int r0 = lane >> 3, c = lane & 7;
+    float mj[G], lj[G];
+    row_bcast_all<G>(st.m, mj);
+    row_bcast_all<G>(st.l, lj);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
+      if (lane & 8) lj[j] = 0.f;
       float v8[8], v4[4];
-      rs_step<0, 16>(st.m[j], st.l[j], st.acc[j], v8, r0);
-      rs_step<1, 8>(st.m[j], st.l[j], v8, v4, r0);
-      rs_step<2, 4>(st.m[j], st.l[j], v4, v2[j], r0);
-      m[j] = st.m[j];
-      l[j] = st.l[j];
+      rs_step<0, 16>(mj[j], lj[j], st.acc[j], v8, r0);
+      rs_step<1, 8>(mj[j], lj[j], v8, v4, r0);
+      rs_step<2, 4>(mj[j], lj[j], v4, v2[j], r0);
+      m[j] = mj[j];
+      l[j] = lj[j];
     }
     return dim(c, 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2));
   }
