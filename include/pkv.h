@@ -346,8 +346,10 @@ int pkv_qk_norm_rope_append(void* q_out, const void* q_in, const void* k_in, con
  * ks, vs [L, cap, H_kv] with cap cut into pages of 16 slots:
  *   k_codes, v_codes    int8 [num_blocks][16][Hkv][D], the order of the bf16
  *                       pools; a row of codes reads back as code * scale.
- *   k_scales, v_scales  float32 [num_blocks][16][Hkv]: the scale of the row
- *                       of (page b, slot s, KV head g) at [b][s][g].
+ *   k_scales, v_scales  float32 [num_blocks][Hkv][16]: the scale of the row
+ *                       of (page b, slot s, KV head g) at [b][g][s].  Inside
+ *                       a page the scales are head-major, so the 16 scales
+ *                       one KV head reads from a page are one 64-byte run.
  * Unwritten slots may hold anything; a NaN scale there is never read.
  */
 
@@ -371,7 +373,8 @@ int pkv_append_int8(const void* k_new, const void* v_new, const int32_t* slot_ma
  * outputs, error behaviour, split plan and workspace as pkv_attn_decode
  * (pkv_decode_workspace_bytes / pkv_decode_num_splits apply unchanged).
  * Scores use q . codes times the row's K scale; the row's V scale multiplies
- * its probability, which is rounded to bf16 for the PV product.
+ * its probability, which is rounded to bf16 for the PV product (bf16 weights
+ * times codes, accumulated in float32).
  */
 int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
                          const float* k_scales, const float* v_scales,

@@ -17,11 +17,13 @@ The quantiser is the page's, step by step and in the page's precision
   * reading returns code_i * scale (float32).
 Here x is the bf16 K or V row widened exactly to float32.
 
-Pages hold codes and scales in the pages' token-major order: codes
-int8 [num_blocks][16][Hkv][D], scales float32 [num_blocks][16][Hkv] (the
-per-layer slice of KV8Cache's k [L, cap, H_kv, D] and ks [L, cap, H_kv],
-with cap cut into 16-slot pages as [P1] paged.py does).  Attention on the
-dequantised rows is the pinned float64 definition of pkv_oracle.
+Pages hold codes in the pages' token-major order, int8
+[num_blocks][16][Hkv][D] (the per-layer slice of KV8Cache's k [L, cap,
+H_kv, D], with cap cut into 16-slot pages as [P1] paged.py does), and the
+per-layer slice of ks [L, cap, H_kv] cut the same way with each page's
+block stored head-major: float32 [num_blocks][Hkv][16], the scale of (page
+b, slot s, KV head g) at [b][g][s].  Attention on the dequantised rows is
+the pinned float64 definition of pkv_oracle.
 """
 from __future__ import annotations
 
@@ -62,7 +64,7 @@ def append_int8_ref(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarr
     its slot ([P2] KV8Cache.write; slots as [P1] PagedKVCache.write).
 
     k_new/v_new: uint16 bf16 [T][Hkv][D]; codes int8 [num_blocks][bs][Hkv][D];
-    scales float32 [num_blocks][bs][Hkv].  Negative slots are skipped; a
+    scales float32 [num_blocks][Hkv][bs].  Negative slots are skipped; a
     repeated slot keeps the last write.  Returns updated copies.
     """
     kc, vc = np.array(k_codes, np.int8, copy=True), np.array(v_codes, np.int8, copy=True)
@@ -75,16 +77,17 @@ def append_int8_ref(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarr
         blk, off = divmod(s, block_size)
         if not 0 <= blk < num_blocks:
             raise IndexError(f"slot {s} outside a pool of {num_blocks} pages")
-        kc[blk, off], ks[blk, off] = quantize_ref(bf16_to_f32(k_new[t]))
-        vc[blk, off], vs[blk, off] = quantize_ref(bf16_to_f32(v_new[t]))
+        kc[blk, off], ks[blk, :, off] = quantize_ref(bf16_to_f32(k_new[t]))
+        vc[blk, off], vs[blk, :, off] = quantize_ref(bf16_to_f32(v_new[t]))
     return kc, vc, ks, vs
 
 
 def gather_int8_ref(codes: np.ndarray, scales: np.ndarray, table_row: Sequence[int], n: int,
                     block_size: int = BLOCK_SIZE) -> np.ndarray:
-    """Logical positions 0..n-1 -> dequantised float32 [n][Hkv][D]."""
+    """Logical positions 0..n-1 -> dequantised float32 [n][Hkv][D] (scales
+    [num_blocks][Hkv][bs], read slot-major here)."""
     c = gather_ref(codes, table_row, n, block_size)
-    s = gather_ref(scales, table_row, n, block_size)
+    s = gather_ref(np.swapaxes(np.asarray(scales), 1, 2), table_row, n, block_size)
     return dequantize_ref(c, s)
 
 

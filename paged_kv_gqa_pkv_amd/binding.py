@@ -311,15 +311,16 @@ def pkv_attn_prefill_decode(out_prefill: torch.Tensor, q_prefill: torch.Tensor,
 def _need_scales(k_scales: torch.Tensor, v_scales: torch.Tensor, codes: torch.Tensor) -> None:
     for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
         _need(t, torch.float32, n, 3)
-    if k_scales.shape != codes.shape[:3] or v_scales.shape != codes.shape[:3]:
-        raise ValueError("scales must be [num_blocks, 16, Hkv] like the codes' first dims")
+    want = (codes.shape[0], codes.shape[2], codes.shape[1])
+    if tuple(k_scales.shape) != want or tuple(v_scales.shape) != want:
+        raise ValueError("scales must be [num_blocks, Hkv, 16] (a page's scales head-major)")
 
 
 def pkv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
                     k_codes: torch.Tensor, v_codes: torch.Tensor, k_scales: torch.Tensor,
                     v_scales: torch.Tensor, stream=None) -> None:
     """Quantise k_new/v_new [T, Hkv, D] into int8 pools: codes [num_blocks, 16, Hkv, D],
-    scales [num_blocks, 16, Hkv] for K and for V."""
+    scales [num_blocks, Hkv, 16] for K and for V."""
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t, torch.bfloat16, n, 3)
     for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):

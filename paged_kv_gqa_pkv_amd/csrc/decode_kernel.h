@@ -102,7 +102,7 @@ struct DecodeArgs {
   const u32x4* q;                // bf16 [B][Hq][D] as 16-byte chunks
   const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D], or int8 codes (same order)
   const u32x4* v_cache;
-  const float* k_scales;         // int8 pages: float32 [num_blocks][16][Hkv]
+  const float* k_scales;         // int8 pages: float32 [num_blocks][Hkv][16]
   const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
@@ -334,33 +334,36 @@ struct Bf16Page {
 // one head is 16 rows of 128 codes (Hkv*128 B apart) plus 16 K and 16 V
 // scales.  Codes are integers in [-127, 127], exact in bf16.
 //
-// The scores run on the matrix cores: S[key][head] = codes[key] . q[head]
-// for the page's 16 keys is four v_mfma_f32_16x16x32_bf16 (16 keys x 16
-// head columns, G of them used, 32 dims each).  The K rows arrive as in the
+// Both products run on the matrix cores.  The K and V rows arrive as in the
 // bf16 policy (lane (r0, c) = (l>>3, l&7): 16-byte chunk c of rows r0 and
-// r0+8, so every load instruction moves eight whole 128-byte lines) and go
-// through a wave-private LDS buffer, whose rows keep their chunks swizzled
-// by row, to the MFMA operand layout: lane (g4, t) = (l>>4, l&15) takes key
-// row t, dims 32 g4 .. 32 g4 + 31 (and q of head t, the same dims, as the
-// other operand; zero for t >= G), and gets back S of keys 4 g4 .. 4 g4 + 3
-// for head t.  (Loading the operand layout straight from memory splits
-// each row over four lanes: half-used lines per instruction, which the
-// counters showed saturating the L1's tag lookups.)  Lane (g4, t < G) keeps
-// head t's online-softmax reference and row sum over the keys 4 g4 .. +3 of
-// every page; the keys' K scales turn S into scores, the V scales scale the
-// probabilities, and DPP row broadcasts hand those weights to the 16 lanes
-// of row g4.  There the PV product runs on v_dot2_f32_bf16: lane (g4, t)
-// holds chunk t & 7 (16 dims) of keys 4 g4 + (t >> 3) and 4 g4 + 2 + (t >> 3)
-// (again whole lines per load instruction), paired with those two keys'
-// weights.  Every lane of a row uses that row's references, so a rescale of
-// head j's accumulators takes lane (g4, j)'s factor.
+// r0 + 8, so every load instruction moves eight whole 128-byte lines) and
+// pass, one after the other, through a wave-private 2 KB LDS buffer per page.
+//  - Scores: S[key][head] = codes[key] . q[head] for the page's 16 keys is
+//    four v_mfma_f32_16x16x32_bf16 (16 keys x 16 head columns, G of them
+//    used, 32 dims each).  Lane (g4, t) = (l>>4, l&15) reads key row t, dims
+//    32 g4 .. +31, from the buffer and gets back S of keys 4 g4 .. 4 g4 + 3
+//    for head t.  (Loading that layout straight from memory splits each row
+//    over four lanes: half-used lines per instruction, which the counters
+//    showed saturating the L1's tag lookups.)
+//  - Softmax: the keys' K scales (DPP row broadcasts) turn S into scores.
+//    Each head has one reference, kept alike in the four lanes (g4, t) that
+//    hold its scores; lane (g4, t) sums head t's probabilities of keys
+//    4 g4 .. +3 of every page.
+//  - PV: the probabilities times the keys' V scales, rounded to bf16, are
+//    already the A operand of v_mfma_f32_16x16x16_bf16 (lane (g4, t): row
+//    head t, k = keys 4 g4 .. +3).  One ds_read_b64_tr_b8 gathers the B
+//    operands of two 16-dim blocks: in each group of 16 lanes, lane i
+//    receives byte i of eight 16-byte rows, row r being the 8-byte pieces
+//    that lanes 2r and 2r + 1 address (checked with probe kernels on the
+//    part, as were the MFMA layouts and row_newbcast).  Lane (g4, t)
+//    addresses keys 4 g4 .. +3 at dims 32 j .. 32 j + 31 and receives the
+//    codes (key 4 g4 + e, dim 32 j + t) and (key 4 g4 + e, dim 32 j + 16 + t),
+//    e = 0 .. 3.  Eight MFMAs per page accumulate O[head][dim]: lane (g4, t)
+//    holds heads 4 g4 .. 4 g4 + 3, one per accumulator register, at dims
+//    16 blk + t (blk = 0 .. 7).
 template <int n>
 __device__ __forceinline__ float row_bcast(float x) {
   return dpp_f<0x150 + n>(x);     // row_newbcast: lane n of each row of 16
-}
-template <int n>
-__device__ __forceinline__ uint32_t row_bcast_u(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + n, 0xf, 0xf, false);
 }
 // Lane n's value of each row of 16, n = 0 .. G-1, for a compile-time G.
 template <int G>
@@ -373,51 +376,65 @@ __device__ __forceinline__ void row_bcast_all(float x, float (&out)[G]) {
     out[6] = row_bcast<6>(x); out[7] = row_bcast<7>(x);
   }
 }
-template <int G>
-__device__ __forceinline__ void row_bcast_all_u(uint32_t x, uint32_t (&out)[G]) {
-  if constexpr (G > 0) out[0] = row_bcast_u<0>(x);
-  if constexpr (G > 1) out[1] = row_bcast_u<1>(x);
-  if constexpr (G > 2) { out[2] = row_bcast_u<2>(x); out[3] = row_bcast_u<3>(x); }
-  if constexpr (G > 4) {
-    out[4] = row_bcast_u<4>(x); out[5] = row_bcast_u<5>(x);
-    out[6] = row_bcast_u<6>(x); out[7] = row_bcast_u<7>(x);
-  }
-}
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 constexpr int kI8LdsWaves = 8;    // waves of a workgroup (at most)
 constexpr int kI8LdsPages = 2;    // pages per process call (at most)
-// The K transpose buffers, 2 KB per (wave, page): one array per kernel
+// The K/V staging buffers, 2 KB per (wave, page): one array per kernel
 // (declared in a function that is not a template, so the instantiations of
 // the page loop share it).
-__device__ __forceinline__ u32x4 (*i8_k_lds())[kI8LdsPages][kPage * 8] {
-  __shared__ u32x4 s_k[kI8LdsWaves][kI8LdsPages][kPage * 8];
-  return s_k;
+__device__ __forceinline__ u32x4 (*i8_lds())[kI8LdsPages][kPage * 8] {
+  __shared__ u32x4 s_kv[kI8LdsWaves][kI8LdsPages][kPage * 8];
+  return s_kv;
+}
+// Accumulator register i of row g4 belongs to head 4 g4 + i; its rescale
+// factor sits in lane 4 g4 + i of the same row (every row holds every
+// head's factor).  Rows past the last head hold nothing of use.
+template <int G>
+__device__ __forceinline__ void head_factors(float a, float (&ai)[4], int lane) {
+  static_assert(G <= 8, "two rows of heads at most");
+  if constexpr (G <= 4) {
+    ai[0] = row_bcast<0>(a); ai[1] = row_bcast<1>(a);
+    ai[2] = row_bcast<2>(a); ai[3] = row_bcast<3>(a);
+  } else {
+    const bool r1 = (lane & 16) != 0;
+    ai[0] = r1 ? row_bcast<4>(a) : row_bcast<0>(a);
+    ai[1] = r1 ? row_bcast<5>(a) : row_bcast<1>(a);
+    ai[2] = r1 ? row_bcast<6>(a) : row_bcast<2>(a);
+    ai[3] = r1 ? row_bcast<7>(a) : row_bcast<3>(a);
+  }
+}
+__device__ __forceinline__ s16x4 codes_bf16x4(uint32_t w) {
+  const bf16x2 lo = {(__bf16)sbyte0(w), (__bf16)sbyte1(w)};
+  const bf16x2 hi = {(__bf16)sbyte2(w), (__bf16)sbyte3(w)};
+  const uint32_t u[2] = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  return __builtin_bit_cast(s16x4, u);
 }
 
 struct Int8Page {
   struct Regs {
     u32x4 k[2];      // rows r0 and r0 + 8: chunk c
-    u32x4 v[2];      // keys 4 g4 + (t >> 3) and that + 2: chunk t & 7
+    u32x4 v[2];
     float s;         // t < 4: K scale of key 4 g4 + t; t = 4..7: V scale of key 4 g4 + t - 4
   };
-  static __device__ __forceinline__ int dim(int c, int d) { return 16 * c + d; }
   template <int G>
   struct Q {
     bf16x8 b[4];     // head t's q, dims 32 g4 + 8 kk .. +8, per MFMA kk
   };
   template <int G>
   struct State {
-    float m, l;          // lane (g4, t < G): head t over keys 4 g4 .. +3 of each page
-    float acc[G][16];    // dims 16 (t & 7) .. +16 of each head; row g4's references
+    float m, l;      // lane (g4, t): head t's reference; its sum over keys 4 g4 .. +3 of each page
+    f32x4v o[8];     // O[head 4 g4 + i][dim 16 blk + t] in o[blk][i]
   };
   template <int G>
   static __device__ __forceinline__ void init(State<G>& st) {
     st.m = kNegInf;
     st.l = 0.f;
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int d = 0; d < 16; ++d) st.acc[j][d] = 0.f;
+    for (int b = 0; b < 8; ++b) st.o[b] = f32x4v{0.f, 0.f, 0.f, 0.f};
   }
   template <int G>
   static __device__ __forceinline__ void load_q(Q<G>& q, const u32x4* qp, int lane) {
@@ -429,46 +446,66 @@ struct Int8Page {
       q.b[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // The page's base is uniform; each lane adds a small 32-bit byte offset.
+  // A page's scales are head-major ([page][KV head][slot]): head g's 16 K
+  // scales are one 64-byte run, as are its 16 V scales.
   static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
                                               int lane) {
     const int r0 = lane >> 3, c = lane & 7, t = lane & 15, g4 = lane >> 4;
-    const int64_t krow = (blk * kPage + r0) * a.Hkv + g;            // 8 chunks per row
-    const int64_t r8 = (int64_t)8 * a.Hkv;                           // row r0 + 8
-    r.k[0] = load_kv(a.k_cache + krow * 8 + c);
-    r.k[1] = load_kv(a.k_cache + (krow + r8) * 8 + c);
-    const int64_t vrow = (blk * kPage + 4 * g4 + (t >> 3)) * a.Hkv + g;
-    const int64_t r2 = (int64_t)2 * a.Hkv;                           // key + 2
-    r.v[0] = load_kv(a.v_cache + vrow * 8 + (t & 7));
-    r.v[1] = load_kv(a.v_cache + (vrow + r2) * 8 + (t & 7));
-    const int64_t srow = (blk * kPage + 4 * g4 + (t & 3)) * a.Hkv + g;
-    r.s = ((t & 4) ? a.v_scales : a.k_scales)[srow];
+    const int64_t row0 = blk * (int64_t)(kPage * a.Hkv);      // the page's first (slot, head) row
+    const char* kp = reinterpret_cast<const char*>(a.k_cache) + row0 * kD;
+    const char* vp = reinterpret_cast<const char*>(a.v_cache) + row0 * kD;
+    const uint32_t o0 = (uint32_t)((r0 * a.Hkv + g) * kD + 16 * c);
+    const uint32_t o8 = o0 + (uint32_t)(8 * a.Hkv * kD);     // row r0 + 8
+    const uint32_t os = (uint32_t)(4 * (g * kPage + 4 * g4 + (t & 3)));
+    r.k[0] = load_kv(reinterpret_cast<const u32x4*>(kp + o0));
+    r.k[1] = load_kv(reinterpret_cast<const u32x4*>(kp + o8));
+    r.v[0] = load_kv(reinterpret_cast<const u32x4*>(vp + o0));
+    r.v[1] = load_kv(reinterpret_cast<const u32x4*>(vp + o8));
+    const char* sp = reinterpret_cast<const char*>((t & 4) ? a.v_scales : a.k_scales) + row0 * 4;
+    r.s = *reinterpret_cast<const float*>(sp + os);
   }
   template <int G, int U, bool kMask>
   static __device__ __forceinline__ void process(const Regs (&buf)[U], const Q<G>& q,
                                                  State<G>& st, float scale_log2, int lane,
                                                  int valid_rows) {
     static_assert(U <= kI8LdsPages, "LDS pages per wave");
-    u32x4 (*s_k)[kI8LdsPages][kPage * 8] = i8_k_lds();
+    u32x4 (*s)[kI8LdsPages][kPage * 8] = i8_lds();
     const int wv = uniform(threadIdx.x >> 6);
     const int r0 = lane >> 3, c = lane & 7, t = lane & 15, g4 = lane >> 4;
-    // the K rows of this call's pages into the wave's buffer (chunk cc of
-    // row r at position cc ^ (r & 7))
+    // K rows into the buffer, chunk cc of row r at position cc ^ (r & 7)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      s_k[wv][u][r0 * 8 + (c ^ (r0 & 7))] = buf[u].k[0];
-      s_k[wv][u][(r0 + 8) * 8 + (c ^ (r0 & 7))] = buf[u].k[1];
+      s[wv][u][r0 * 8 + (c ^ r0)] = buf[u].k[0];
+      s[wv][u][(r0 + 8) * 8 + (c ^ r0)] = buf[u].k[1];
     }
-    // the wave's LDS accesses run in order; keep the compiler from moving
-    // the reads above the writes of other lanes
+    // a wave's LDS accesses run in order; keep the compiler from moving
+    // the reads above the writes of other lanes (and the V writes above
+    // the K reads)
     asm volatile("" ::: "memory");
+    u32x4 ka[U], kb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const u32x4 ka = s_k[wv][u][t * 8 + ((2 * g4) ^ (t & 7))];
-      const u32x4 kb = s_k[wv][u][t * 8 + ((2 * g4 + 1) ^ (t & 7))];
+      ka[u] = s[wv][u][t * 8 + ((2 * g4) ^ (t & 7))];
+      kb[u] = s[wv][u][t * 8 + ((2 * g4 + 1) ^ (t & 7))];
+    }
+    asm volatile("" ::: "memory");
+    // V rows into the same buffer, chunk cc of row r at position
+    // cc ^ ((r >> 1) & 7): the transposed reads below (16 rows, 32 B each)
+    // then fall on every bank twice
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[wv][u][r0 * 8 + (c ^ (r0 >> 1))] = buf[u].v[0];
+      s[wv][u][(r0 + 8) * 8 + (c ^ (4 + (r0 >> 1)))] = buf[u].v[1];
+    }
+    asm volatile("" ::: "memory");
+    const int vkey = 4 * g4 + ((t >> 1) & 3);     // the row this lane addresses
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       f32x4v s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const u32x4& kw = (kk < 2) ? ka : kb;
+        const u32x4& kw = (kk < 2) ? ka[u] : kb[u];
         const uint32_t w0 = kw[2 * (kk & 1)], w1 = kw[2 * (kk & 1) + 1];
         const bf16x8 a8 = {(__bf16)sbyte0(w0), (__bf16)sbyte1(w0), (__bf16)sbyte2(w0),
                            (__bf16)sbyte3(w0), (__bf16)sbyte0(w1), (__bf16)sbyte1(w1),
@@ -486,72 +523,79 @@ struct Int8Page {
         keep[rr] = !kMask || 4 * g4 + rr < valid_rows;
         sc[rr] = keep[rr] ? s4[rr] * (ks[rr] * scale_log2) : kNegInf;
       }
-      // this lane's reference, raised (wave-uniformly skipped) only when a
-      // score exceeds it by more than the slack
+      // the head's reference, raised (wave-uniformly skipped) only when a
+      // score in one of its four lanes exceeds it by more than the slack;
+      // the new reference is the largest of the four, so it stays alike
       const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      const bool up = t < G && mx > st.m + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(up) != 0) {
-        const float alpha = up ? fast_exp2(st.m - mx) : 1.f;   // m = -inf gives 0
-        st.m = up ? mx : st.m;
+      if (__builtin_amdgcn_ballot_w64(t < G && mx > st.m + kRescaleSlack) != 0) {
+        float mh = fmaxf(mx, shfl_xor(mx, 16));
+        mh = fmaxf(mh, shfl_xor(mh, 32));
+        const bool up = mh > st.m + kRescaleSlack;
+        const float alpha = up ? fast_exp2(st.m - mh) : 1.f;   // m = -inf gives 0
+        st.m = up ? mh : st.m;
         st.l *= alpha;
-        float aj[G];
-        row_bcast_all<G>(alpha, aj);
+        float ai[4];
+        head_factors<G>(alpha, ai, lane);
 #pragma unroll
-        for (int j = 0; j < G; ++j)
+        for (int b = 0; b < 8; ++b)
 #pragma unroll
-          for (int d = 0; d < 16; ++d) st.acc[j][d] *= aj[j];
+          for (int i = 0; i < 4; ++i) st.o[b][i] *= ai[i];
       }
       const float mu = (st.m == kNegInf) ? 0.f : st.m;
       float p[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(sc[rr] - mu);
       st.l += (p[0] + p[1]) + (p[2] + p[3]);
-      // PV weights p * V scale as bf16 pairs of keys (0, 2) and (1, 3) of
-      // the row's four; masked keys weigh exactly 0 (their scale may be a
-      // NaN canary)
+      // PV weights p * V scale; masked keys weigh exactly 0 (their scale
+      // may be a NaN canary)
       float wv4[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) wv4[rr] = keep[rr] ? p[rr] * vs[rr] : 0.f;
-      uint32_t w02[G], w13[G];
-      row_bcast_all_u<G>(pack_bf16x2(wv4[0], wv4[2]), w02);
-      row_bcast_all_u<G>(pack_bf16x2(wv4[1], wv4[3]), w13);
-      const bool odd = (t & 8) != 0;           // keys 4 g4 + 1 and + 3
+      const uint32_t wp[2] = {pack_bf16x2(wv4[0], wv4[1]), pack_bf16x2(wv4[2], wv4[3])};
+      const s16x4 wa = __builtin_bit_cast(s16x4, wp);
+      const char* vb = reinterpret_cast<const char*>(&s[wv][u][0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 vv = {(__bf16)sbyte(buf[u].v[0][i], e), (__bf16)sbyte(buf[u].v[1][i], e)};
-          const int d = 4 * i + e;
-#pragma unroll
-          for (int j = 0; j < G; ++j)
-            st.acc[j][d] = __builtin_amdgcn_fdot2_f32_bf16(
-                vv, as_bf16x2(odd ? w13[j] : w02[j]), st.acc[j][d], false);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int blk = 2 * j + (t >> 3);
+        const int off = vkey * 128 + 16 * (blk ^ ((vkey >> 1) & 7)) + 8 * (t & 1);
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + off));
+        st.o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            wa, codes_bf16x4((uint32_t)x[0]), st.o[2 * j], 0, 0, 0);
+        st.o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            wa, codes_bf16x4((uint32_t)x[1]), st.o[2 * j + 1], 0, 0, 0);
+      }
     }
   }
-  // Every lane of row g4 takes that row's (m, l) of head j from lane
-  // (g4, j), l counted once for the two lanes t and t ^ 8 that hold the same
-  // dims of different keys; then the reduce-scatter of the bf16 policy over
-  // lane ^ 8, ^ 16 and ^ 32 (the same bits as its rows r0) leaves lane l
-  // with dims dim(l & 7, d0) and the next, and the same (m, l) in every lane.
+  // Every lane takes head j's reference from lane j of its row and the sum
+  // of its four rows' sums; O goes through the wave's buffer (whose last
+  // reads have been served) to two dims per lane: dims 2 lane, 2 lane + 1.
   template <int G>
   static __device__ __forceinline__ int finish(State<G>& st, float (&m)[G], float (&l)[G],
                                                float (&v2)[G][2], int lane) {
-    const int r0 = lane >> 3, c = lane & 7;
-    float mj[G], lj[G];
-    row_bcast_all<G>(st.m, mj);
-    row_bcast_all<G>(st.l, lj);
+    static_assert(G * kD * 4 <= kI8LdsPages * kPage * 8 * 16, "O fits the wave's buffer");
+    const int t = lane & 15, g4 = lane >> 4;
+    float ls = st.l + shfl_xor(st.l, 16);
+    ls += shfl_xor(ls, 32);
+    row_bcast_all<G>(st.m, m);
+    row_bcast_all<G>(ls, l);
+    float* so = reinterpret_cast<float*>(&i8_lds()[uniform(threadIdx.x >> 6)][0][0]);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * g4 + i < G) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) so[(4 * g4 + i) * kD + 16 * b + t] = st.o[b][i];
+      }
+    }
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      if (lane & 8) lj[j] = 0.f;
-      float v8[8], v4[4];
-      rs_step<0, 16>(mj[j], lj[j], st.acc[j], v8, r0);
-      rs_step<1, 8>(mj[j], lj[j], v8, v4, r0);
-      rs_step<2, 4>(mj[j], lj[j], v4, v2[j], r0);
-      m[j] = mj[j];
-      l[j] = lj[j];
+      const f32x2 v = *reinterpret_cast<const f32x2*>(so + j * kD + 2 * lane);
+      v2[j][0] = v[0];
+      v2[j][1] = v[1];
     }
-    return dim(c, 8 * (r0 & 1) + 4 * ((r0 >> 1) & 1) + 2 * (r0 >> 2));
+    asm volatile("" ::: "memory");
+    return 2 * lane;
   }
 };
 

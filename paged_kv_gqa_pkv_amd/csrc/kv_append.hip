@@ -73,9 +73,10 @@ append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
 // float32 arithmetic bit for bit.  16 lanes own one row of 128 values (8 per
 // lane): the row max is a DPP reduction inside the 16-lane row, each lane
 // writes its 8 codes (8 bytes), and the first lane writes the scale.  Codes
-// are token-major like the bf16 pools ([page][16 slots][KV head][D]) and the
-// scales sit at [page][slot][KV head] of k_scales or v_scales (the listing's
-// ks and vs [L, cap, H_kv], one layer, cap cut into pages).
+// are token-major like the bf16 pools ([page][16 slots][KV head][D]); the
+// scales (the listing's ks and vs [L, cap, H_kv], one layer, cap cut into
+// pages) sit at [page][KV head][slot] of k_scales or v_scales, so the 16
+// scales a KV head needs from a page are one 64-byte run.
 //
 // The quotients x_d / scale are the correctly rounded ones without a full
 // division each: with y = 1 / scale correctly rounded (one IEEE division per
@@ -127,7 +128,8 @@ append_int8_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_
   if (slot < 0 || slot >= num_slots) return;
   const int64_t row = slot * Hkv + h;                             // codes row (128 B)
   (which ? v_codes : k_codes)[row * 16 + sub] = make_uint2(pk[0], pk[1]);
-  if (sub == 0) (which ? v_scales : k_scales)[row] = scale;
+  const int64_t srow = ((slot / kPage) * Hkv + h) * kPage + slot % kPage;
+  if (sub == 0) (which ? v_scales : k_scales)[srow] = scale;
 }
 
 hipError_t launch_append_int8(const void* k_new, const void* v_new, const int32_t* slots,

@@ -77,7 +77,7 @@ hipError_t launch_decode_noalloc(void* out, const void* q, const void* k_cache,
                                  hipStream_t stream);
 
 // Decode over int8 pages (codes in the bf16 page order; float32 scales
-// [num_blocks][16][Hkv] for K and for V); same plan and workspace as
+// [num_blocks][Hkv][16] for K and for V); same plan and workspace as
 // launch_decode.
 hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
                               const float* k_scales, const float* v_scales,

@@ -121,7 +121,7 @@ struct PrefillArgs {
   const int32_t* cu_q;           // [B+1]
   const u32x4* k_cache;          // bf16 [num_blocks][16][Hkv][D], or int8 codes
   const u32x4* v_cache;
-  const float* k_scales;         // int8 pages: float [num_blocks][16][Hkv]
+  const float* k_scales;         // int8 pages: float [num_blocks][Hkv][16]
   const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
@@ -371,7 +371,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
         dma16(a.v_cache + row * 8 + (lane & 7), cs + kCodeTileBytes + off);
       }
       const int si = lane & 31;
-      dma4(((si & 16) ? a.v_scales : a.k_scales) + (blk * kPage + (si & 15)) * a.Hkv + g,
+      dma4(((si & 16) ? a.v_scales : a.k_scales) + (blk * a.Hkv + g) * kPage + (si & 15),
            cs + 2 * kCodeTileBytes + w * kScaleSlotBytes);
     } else {
 #pragma unroll

@@ -301,7 +301,7 @@ class LayerDataInt8:
     """One layer's tensors for a step over int8 pages (all on ``device``)."""
     k_codes: torch.Tensor        # int8 [num_blocks, 16, Hkv, D], pre-append
     v_codes: torch.Tensor
-    k_scales: torch.Tensor       # float32 [num_blocks, 16, Hkv]
+    k_scales: torch.Tensor       # float32 [num_blocks, Hkv, 16] (head-major pages)
     v_scales: torch.Tensor
     k_new: torch.Tensor          # bf16 [T_total, Hkv, D]
     v_new: torch.Tensor
@@ -316,13 +316,15 @@ def _codes(shape, seed, device) -> torch.Tensor:
 
 
 def _kv_scales(w: Workload, fill: torch.Tensor, seed: int, device):
-    """(k_scales, v_scales), float32 [num_blocks, 16, Hkv] each, drawn as one
-    [2, num_blocks, 16, Hkv] array."""
+    """(k_scales, v_scales), float32 [num_blocks, Hkv, 16] each (a page's
+    scales head-major), drawn as one [2, num_blocks, 16, Hkv] array (slot-major,
+    so a (page, slot, head) gets the same value in either layout)."""
     g = _gen(seed, device)
     sc = torch.empty((2, w.num_blocks, PAGE, w.Hkv), device=device, dtype=torch.float32)
     sc.uniform_(SCALE_LO, SCALE_HI, generator=g)
     dead = _dead_slots(w, fill, device).view(1, w.num_blocks, PAGE, 1)
     sc.view(torch.int32).masked_fill_(dead, F32_CANARY_BITS)
+    sc = sc.transpose(2, 3)
     return sc[0].contiguous(), sc[1].contiguous()
 
 
@@ -393,6 +395,6 @@ def large_chunk_inputs(device="cpu", T: int = 2048, offset: int = 6144, Hq: int 
         "v_cache": randn_bf16((nbp, PAGE, Hkv, D), seed + 2, device),
         "k_codes": _codes((nbp, PAGE, Hkv, D), seed + 3, "cpu").to(device),
         "v_codes": _codes((nbp, PAGE, Hkv, D), seed + 4, "cpu").to(device),
-        "k_scales": scales[0].contiguous().to(device),
-        "v_scales": scales[1].contiguous().to(device),
+        "k_scales": scales[0].transpose(1, 2).contiguous().to(device),   # [nb, Hkv, 16]
+        "v_scales": scales[1].transpose(1, 2).contiguous().to(device),
     }

@@ -109,8 +109,8 @@ def check_append_semantics():
     nb, Hkv, D = 3, 2, 8
     kc = rng.integers(-127, 128, (nb, BS, Hkv, D)).astype(np.int8)
     vc = rng.integers(-127, 128, (nb, BS, Hkv, D)).astype(np.int8)
-    ks = rng.uniform(0.1, 1, (nb, BS, Hkv)).astype(np.float32)
-    vs = rng.uniform(0.1, 1, (nb, BS, Hkv)).astype(np.float32)
+    ks = rng.uniform(0.1, 1, (nb, Hkv, BS)).astype(np.float32)    # head-major pages
+    vs = rng.uniform(0.1, 1, (nb, Hkv, BS)).astype(np.float32)
     vals = (rng.integers(-64, 64, (4, Hkv, D)) / 8.0).astype(np.float32)   # exact in bf16
     k_new = f32_bits_to_bf16(vals)
     v_new = f32_bits_to_bf16(-vals)
@@ -122,13 +122,14 @@ def check_append_semantics():
         for g in range(Hkv):
             m = np.abs(vals[t, g]).max()
             sc = np.float32(np.float32(m) / np.float32(127)) + np.float32(1e-8)
-            want_ks[s // BS, s % BS, g] = sc
+            want_ks[s // BS, g, s % BS] = sc
             want_k[s // BS, s % BS, g] = np.clip(np.rint(vals[t, g] / sc), -127, 127)
     assert np.array_equal(okc, want_k) and np.array_equal(oks, want_ks)
-    assert np.array_equal(ovc[0, 5], -okc[0, 5]) and np.array_equal(ovs[0, 5], oks[0, 5])
-    assert np.array_equal(ovs[2, 8], oks[2, 8])
+    assert np.array_equal(ovc[0, 5], -okc[0, 5]) and np.array_equal(ovs[0, :, 5], oks[0, :, 5])
+    assert np.array_equal(ovs[2, :, 8], oks[2, :, 8])
     untouched = np.ones((nb, BS), bool); untouched[0, 5] = untouched[2, 8] = False
     assert np.array_equal(okc[untouched], kc[untouched])
+    assert np.array_equal(oks.transpose(0, 2, 1)[untouched], ks.transpose(0, 2, 1)[untouched])
     with pytest.raises(IndexError):
         Q.append_int8_ref(kc, vc, ks, vs, k_new[:1], v_new[:1], [nb * BS])
 
@@ -139,13 +140,13 @@ def check_gather_brute_force():
     rng = np.random.default_rng(5)
     nb, Hkv, D = 6, 2, 4
     codes = rng.integers(-127, 128, (nb, BS, Hkv, D)).astype(np.int8)
-    scales = rng.uniform(0.01, 0.05, (nb, BS, Hkv)).astype(np.float32)
+    scales = rng.uniform(0.01, 0.05, (nb, Hkv, BS)).astype(np.float32)   # head-major pages
     row, n = [4, 0, 3], 37
     got = Q.gather_int8_ref(codes, scales, row, n)
     for p in range(n):
         for g in range(Hkv):
             for d in range(D):
-                want = np.float32(codes[row[p // 16], p % 16, g, d]) * scales[row[p // 16], p % 16, g]
+                want = np.float32(codes[row[p // 16], p % 16, g, d]) * scales[row[p // 16], g, p % 16]
                 assert got[p, g, d] == want
 
 
@@ -155,7 +156,7 @@ def _integer_pools(rng, nb, Hkv, D):
     vals = rng.integers(-127, 128, (nb, BS, Hkv, D)).astype(np.float32)
     vals[..., 0] = 127.0
     codes = vals.astype(np.int8)
-    scales = np.ones((nb, BS, Hkv), np.float32)
+    scales = np.ones((nb, Hkv, BS), np.float32)
     return vals, codes, scales
 
 

@@ -146,11 +146,11 @@ def test_int8_append_bulk_bit_exact_with_edge_rows():
     k_new = k.to(torch.bfloat16)
     kc = torch.zeros((nb, 16, Hkv, D), dtype=torch.int8, device="cuda")
     vc = torch.zeros_like(kc)
-    ks = torch.ones((nb, 16, Hkv), dtype=torch.float32, device="cuda")
+    ks = torch.ones((nb, Hkv, 16), dtype=torch.float32, device="cuda")   # head-major pages
     vs = torch.ones_like(ks)
     bd.pkv_append_int8(k_new.cuda(), v_new.cuda(), slots.cuda(), kc, vc, ks, vs)
     torch.cuda.synchronize()
-    ks0 = np.ones((nb, 16, Hkv), np.float32)
+    ks0 = np.ones((nb, Hkv, 16), np.float32)
     z = np.zeros((nb, 16, Hkv, D), np.int8)
     okc, ovc, oks, ovs = Q.append_int8_ref(z, z, ks0, ks0, u16(k_new), u16(v_new),
                                            slots.numpy().tolist())
@@ -166,12 +166,12 @@ def test_int8_append_skips_negative_slots():
     v_new = S.randn_bf16((3, Hkv, D), 42).cuda()
     kc = torch.full((nb, 16, Hkv, D), 7, dtype=torch.int8, device="cuda")
     vc = kc.clone()
-    ks = torch.full((nb, 16, Hkv), 0.5, dtype=torch.float32, device="cuda")
+    ks = torch.full((nb, Hkv, 16), 0.5, dtype=torch.float32, device="cuda")
     vs = ks.clone()
     slots = torch.tensor([5, -1, 63], dtype=torch.int32, device="cuda")
     bd.pkv_append_int8(k_new, v_new, slots, kc, vc, ks, vs)
     torch.cuda.synchronize()
-    ks0 = np.full((nb, 16, Hkv), 0.5, np.float32)
+    ks0 = np.full((nb, Hkv, 16), 0.5, np.float32)
     c0 = np.full((nb, 16, Hkv, D), 7, np.int8)
     okc, ovc, oks, ovs = Q.append_int8_ref(c0, c0, ks0, ks0, u16(k_new), u16(v_new), [5, -1, 63])
     gks, gvs = host(ks), host(vs)

@@ -58,3 +58,33 @@ def test_canaries_mark_unwritten_slots_and_data_is_seeded():
     assert d1.q_decode.shape == (8, 16, 128) and d1.k_new.shape == (8, 8, 128)
     d3 = S.make_layer(w, t, 1)
     assert not torch.equal(d1.q_decode, d3.q_decode)
+
+
+def test_int8_pools_hold_head_major_scales_with_canaries():
+    """int8 pools: codes token-major, scales [num_blocks, Hkv, 16] (a page's
+    scales head-major) with the NaN canary on exactly the unwritten slots."""
+    w = S.workload("c2")
+    t = S.make_tables(w)
+    d = S.make_layer_int8(w, t, 0)
+    assert d.k_codes.shape == (w.num_blocks, S.PAGE, w.Hkv, w.D)
+    assert d.k_scales.shape == (w.num_blocks, w.Hkv, S.PAGE) == d.v_scales.shape
+    assert d.k_scales.is_contiguous() and d.v_scales.is_contiguous()
+    fill = S.page_fill_counts(w, t).numpy()
+    bits = d.k_scales.view(torch.int32).numpy()
+    for page in range(w.num_blocks):
+        dead = bits[page, :, fill[page]:]
+        assert np.all(dead == np.int32(S.F32_CANARY_BITS))
+        live = d.k_scales[page, :, :fill[page]].numpy()
+        assert np.all((live >= S.SCALE_LO) & (live <= S.SCALE_HI))
+
+
+def test_binding_rejects_slot_major_scales(monkeypatch):
+    import pytest
+    from paged_kv_gqa_pkv_amd import binding as bd
+    monkeypatch.setattr(bd, "_need", lambda *a, **k: None)     # host tensors here
+    codes = torch.zeros((4, S.PAGE, 2, 128), dtype=torch.int8)
+    good = torch.zeros((4, 2, S.PAGE), dtype=torch.float32)
+    bd._need_scales(good, good.clone(), codes)
+    bad = torch.zeros((4, S.PAGE, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="head-major"):
+        bd._need_scales(bad, bad.clone(), codes)
