@@ -59,8 +59,9 @@ def parse():
                         "on its own stream, and a mixed step's decode on a second stream, "
                         "concurrent with the chunk)")
     p.add_argument("--no-fuse", dest="fuse", action="store_false",
-                   help="run a decode-only step's layers as pkv_append + pkv_attn_decode "
-                        "(default: one pkv_attn_decode_append call per layer, bf16 pages)")
+                   help="run a decode-only step's layers as an append call + a decode call "
+                        "(default: one pkv_attn_decode_append call per layer, or "
+                        "pkv_attn_decode_append_int8 over int8 pages)")
     p.add_argument("--no-mixed", dest="mixed", action="store_false",
                    help="run a mixed step's attention as pkv_attn_prefill_chunk + "
                         "pkv_attn_decode (default: one pkv_attn_prefill_decode call per "
@@ -298,8 +299,10 @@ class Part:
         self.kv = kv
         nd = len(w.decode_seqs)
         self.dec_bytes = decode_bytes(w, t, w.decode_seqs, kv) if nd else 0
-        # the timed decode launch: a fused call also writes the step's K/V rows
-        # (read from the new rows in place of the pool: the same bytes)
+        # the timed decode launch: a fused call also reads the step's new bf16
+        # K/V rows in place of that position's pool rows, and writes those
+        # rows into the pool (int8 pages: their codes and scales), which adds
+        # the new rows' bf16 bytes in either format
         self.launch_bytes = self.dec_bytes + (nd * 2 * w.Hkv * w.D * 2 if plan.fused else 0)
         self.pre_bytes, self.pre_flops = prefill_work(w, t)
         self.step_bytes = slot_bytes(w, t) + w.n_layers * (append_bytes(w, t, kv) +
@@ -345,7 +348,7 @@ def build_parts(name, rotate_mib, device, kv="bf16", fuse=True, mixed=True):
             w = S.workload(sub)
             t = S.make_tables(w)
             layers, copies = _layers(w, t, rotate_mib, device, kv)
-            parts.append(Part(w, t, ST.plan_step(w, t, device=device, fused=fuse and kv == "bf16"),
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device, fused=fuse),
                               layers, _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [0, 1])
     if name == "c5":
@@ -367,7 +370,7 @@ def build_parts(name, rotate_mib, device, kv="bf16", fuse=True, mixed=True):
     w = S.workload(name)
     t = S.make_tables(w)
     layers, copies = _layers(w, t, rotate_mib, device, kv)
-    return [Part(w, t, ST.plan_step(w, t, device=device, fused=fuse and kv == "bf16"), layers,
+    return [Part(w, t, ST.plan_step(w, t, device=device, fused=fuse), layers,
                  _bufs(w, t, device), copies, kv)], (lambda i: [0])
 
 
@@ -417,10 +420,17 @@ def run(args):
                     if record == "gated":
                         torch.cuda._sleep(args.gate_cycles)
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
-                bd.pkv_attn_decode_append(qb["od"], qb["qd"], qb["kn"], qb["vn"], d.k_cache,
-                                          d.v_cache, plan.bt_decode, plan.ctx_decode,
-                                          plan.max_ctx_decode, plan.scale,
-                                          workspace=plan.workspace, stream=stream)
+                if pt.kv == "int8":
+                    bd.pkv_attn_decode_append_int8(qb["od"], qb["qd"], qb["kn"], qb["vn"],
+                                                   d.k_codes, d.v_codes, d.k_scales, d.v_scales,
+                                                   plan.bt_decode, plan.ctx_decode,
+                                                   plan.max_ctx_decode, plan.scale,
+                                                   workspace=plan.workspace, stream=stream)
+                else:
+                    bd.pkv_attn_decode_append(qb["od"], qb["qd"], qb["kn"], qb["vn"], d.k_cache,
+                                              d.v_cache, plan.bt_decode, plan.ctx_decode,
+                                              plan.max_ctx_decode, plan.scale,
+                                              workspace=plan.workspace, stream=stream)
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     dec_events.append((k, e0, e1, 1))
@@ -571,8 +581,11 @@ def run(args):
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(args.workload if args.kv == "bf16"
                                                 else f"{args.workload}-int8"),
-                    "kernel": ("decode_kernel<Int8Page> (pkv_attn_decode_int8)" if args.kv == "int8"
-                               else "decode_kernel<Bf16Page, append> (pkv_attn_decode_append)"
+                    "kernel": (("decode_kernel<Int8Page, append> (pkv_attn_decode_append_int8)"
+                                if parts[0].plan.fused else
+                                "decode_kernel<Int8Page> (pkv_attn_decode_int8)")
+                               if args.kv == "int8" else
+                               "decode_kernel<Bf16Page, append> (pkv_attn_decode_append)"
                                if parts[0].plan.fused else "decode_kernel (pkv_attn_decode)"),
                     "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                     "bytes_per_launch": int(sum(byts) / n_launch),

@@ -385,6 +385,30 @@ int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const vo
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode over int8 pages with the step's append fused in ([P1] model.py
+ * forward, as pkv_attn_decode_append; [P2] KV8Cache.write for the new rows):
+ * position p = context_lens[b] - 1 of every sequence b takes k_new[b] /
+ * v_new[b], quantised exactly as pkv_append_int8 quantises them (the same
+ * codes and scale bits), and the call writes those codes and scales into the
+ * slot of p (found from block_tables; nothing is written where there is
+ * none), then attends as pkv_attn_decode_int8 with position p's codes taken
+ * from registers.  The result equals pkv_append_int8 followed by
+ * pkv_attn_decode_int8 up to the order of float32 sums.  One launch; no slot
+ * mapping needed.  Same errors, split plan and workspace as
+ * pkv_attn_decode_int8.
+ *   k_new, v_new        bf16 [B][Hkv][D], the step's rows (finite)
+ *   k_codes, v_codes    the int8 pools, read and written
+ *   k_scales, v_scales  their scales, read and written
+ */
+int pkv_attn_decode_append_int8(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * Causal chunked prefill over int8 pages ([P2] KV8Cache.read: K and V read
  * back as code * scale; then the attention of pkv_attn_prefill_chunk).  Same
  * arguments, outputs, error behaviour, split plan and workspace as

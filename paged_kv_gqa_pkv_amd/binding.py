@@ -39,6 +39,7 @@ SIGNATURES = {
                                 [_f, _vp, _c_size, _vp, _c_size, _vp]),
     "pkv_append_int8": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_vp]),
     "pkv_attn_decode_int8": (_c_int, [_vp] * 8 + [_c_int] * 8 + [_f, _vp, _c_size, _vp]),
+    "pkv_attn_decode_append_int8": (_c_int, [_vp] * 10 + [_c_int] * 8 + [_f, _vp, _c_size, _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _c_int,
                                  ctypes.c_int64, _vp]),
     "pkv_slot_mapping_ring": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
@@ -335,6 +336,38 @@ def pkv_append_int8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torc
     _check(load().pkv_append_int8(_p(k_new), _p(v_new), _p(slot_mapping), _p(k_codes),
                                   _p(v_codes), _p(k_scales), _p(v_scales), T, nb, Hkv, D,
                                   k_codes.shape[1], _stream(stream)))
+
+
+def pkv_attn_decode_append_int8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                v_new: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                                k_scales: torch.Tensor, v_scales: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                max_context_len: int, scale: float,
+                                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Quantise and append k_new/v_new [B, Hkv, D] (one token per sequence, at
+    position context_lens[b] - 1) into int8 pools and run decode attention,
+    in one launch (same workspace as pkv_attn_decode)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need(t, torch.int8, n, 4)
+    _need_scales(k_scales, v_scales, k_codes)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_codes.shape
+    if out.shape != q.shape or D2 != D or v_codes.shape != k_codes.shape or \
+            k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape or \
+            block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent shapes")
+    ws_ptr, ws_bytes = _ws(workspace)
+    _check(load().pkv_attn_decode_append_int8(_p(out), _p(q), _p(k_new), _p(v_new), _p(k_codes),
+                                              _p(v_codes), _p(k_scales), _p(v_scales),
+                                              _p(block_tables), _p(context_lens), B, Hq, Hkv, D,
+                                              bs, nb, block_tables.shape[1], int(max_context_len),
+                                              float(scale), ws_ptr, ws_bytes, _stream(stream)))
 
 
 def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tensor,

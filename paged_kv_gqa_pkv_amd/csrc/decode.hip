@@ -216,6 +216,26 @@ hipError_t launch_decode_noalloc(void* out, const void* q, const void* k_cache,
   return launch_by_group<Bf16Page>(a, Hq / Hkv, stream);
 }
 
+hipError_t launch_decode_append_int8(void* out, const void* q, const void* k_new,
+                                     const void* v_new, void* k_codes, void* v_codes,
+                                     float* k_scales, float* v_scales,
+                                     const int32_t* block_tables, const int32_t* ctx_lens, int B,
+                                     int Hq, int Hkv, int num_blocks, int max_blocks, float scale,
+                                     const DecodePlan& plan, void* workspace,
+                                     hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  DecodeArgs a = make_args(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, ctx_lens,
+                           B, Hq, Hkv, num_blocks, max_blocks, scale, plan,
+                           workspace_buffers(plan, workspace), 0);
+  a.k_new = static_cast<const u32x4*>(k_new);
+  a.v_new = static_cast<const u32x4*>(v_new);
+  a.k_pool = static_cast<u32x4*>(k_codes);
+  a.v_pool = static_cast<u32x4*>(v_codes);
+  a.ks_pool = k_scales;
+  a.vs_pool = v_scales;
+  return launch_by_group<Int8Page, true>(a, Hq / Hkv, stream);
+}
+
 hipError_t launch_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
                               const float* k_scales, const float* v_scales,
                               const int32_t* block_tables, const int32_t* ctx_lens, int B, int Hq,

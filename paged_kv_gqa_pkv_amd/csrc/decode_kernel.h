@@ -106,14 +106,17 @@ struct DecodeArgs {
   const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
-  // Fused append (bf16 pages, no ring): each sequence's newest position,
-  // context_lens[b] - 1, takes its K/V rows from k_new/v_new [B][Hkv][D]
-  // instead of the pool, and the call writes those rows into that position's
-  // slot (k_pool/v_pool are the same pools as k_cache/v_cache).
+  // Fused append (no ring): each sequence's newest position, context_lens[b]
+  // - 1, takes its K/V rows from k_new/v_new (bf16 [B][Hkv][D]) instead of
+  // the pool, and the call writes those rows into that position's slot
+  // (k_pool/v_pool are the same pools as k_cache/v_cache; over int8 pages
+  // the rows are quantised, and ks_pool/vs_pool are k_scales/v_scales).
   const u32x4* k_new;
   const u32x4* v_new;
   u32x4* k_pool;
   u32x4* v_pool;
+  float* ks_pool;
+  float* vs_pool;
   float* ws_ml;                  // [B][Hq][S][2] (m, l), log2 domain
   float* ws_acc;                 // [B][Hq][S][D]
   int* counters;                 // [B][Hkv / heads_per_wg] arrivals per (sequence, head group)
@@ -197,6 +200,23 @@ struct Bf16Page {
   };
   static __device__ __forceinline__ int dim(int c, int d) {
     return d < 8 ? 8 * c + d : 64 + 8 * c + (d - 8);
+  }
+  // Fused append: sequence b's new K/V rows of head g as row 0 of a page
+  // (lanes 0..7 hold chunks c and c + 8; the other rows stay zero), written
+  // into `slot` when it is >= 0.
+  static __device__ __forceinline__ void new_row(Regs& r, const DecodeArgs& a, int b, int g,
+                                                 int lane, int64_t slot) {
+    const int r0 = lane >> 3, c = lane & 7;
+    const u32x4* kn = a.k_new + ((int64_t)b * a.Hkv + g) * 16;
+    const u32x4* vn = a.v_new + ((int64_t)b * a.Hkv + g) * 16;
+    r.k[0][0] = kn[c]; r.k[0][1] = kn[c + 8];
+    r.v[0][0] = vn[c]; r.v[0][1] = vn[c + 8];
+    if (slot >= 0 && r0 == 0) {
+      u32x4* kd = a.k_pool + (slot * a.Hkv + g) * 16;
+      u32x4* vd = a.v_pool + (slot * a.Hkv + g) * 16;
+      kd[c] = r.k[0][0]; kd[c + 8] = r.k[0][1];
+      vd[c] = r.v[0][0]; vd[c + 8] = r.v[0][1];
+    }
   }
   // q of the G heads: the lane's two 16-byte chunks of each.
   template <int G>
@@ -407,6 +427,33 @@ __device__ __forceinline__ void head_factors(float a, float (&ai)[4], int lane) 
     ai[3] = r1 ? row_bcast<7>(a) : row_bcast<3>(a);
   }
 }
+// Max over the 8 lanes of each aligned group of 8.
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadSwap2>(x));
+  return fmaxf(x, dpp_f<kDppHalfMirror>(x));
+}
+// Quantise a row of 128 bf16 values held 16 per lane by the 8 lanes of a
+// group (lo: values 0..7 of the lane's 16, hi: 8..15): the lane's 16 codes,
+// and the row's scale in every lane of the group.
+__device__ __forceinline__ u32x4 quantize_row16(const u32x4& lo, const u32x4& hi, float& scale) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16lo(lo[i]); x[2 * i + 1] = bf16hi(lo[i]);
+    x[8 + 2 * i] = bf16lo(hi[i]); x[9 + 2 * i] = bf16hi(hi[i]);
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(x[i]));
+  mx = max8(mx);
+  scale = int8_row_scale(mx);
+  const float y = 1.0f / scale;
+  u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) out[i >> 2] |= int8_code(x[i], scale, y) << (8 * (i & 3));
+  return out;
+}
 __device__ __forceinline__ s16x4 codes_bf16x4(uint32_t w) {
   const bf16x2 lo = {(__bf16)sbyte0(w), (__bf16)sbyte1(w)};
   const bf16x2 hi = {(__bf16)sbyte2(w), (__bf16)sbyte3(w)};
@@ -464,6 +511,37 @@ struct Int8Page {
     r.v[1] = load_kv(reinterpret_cast<const u32x4*>(vp + o8));
     const char* sp = reinterpret_cast<const char*>((t & 4) ? a.v_scales : a.k_scales) + row0 * 4;
     r.s = *reinterpret_cast<const float*>(sp + os);
+  }
+  // Fused append: sequence b's new K and V rows of head g, quantised as the
+  // append kernel quantises them (the same int8_row_scale / int8_code, so
+  // codes and scales agree bit for bit), as row 0 of a page: lane c of row
+  // group r0 takes dims 16c .. 16c + 15, lanes 0..7 keep the codes (the
+  // other rows stay zero), and lanes t = 0 and t = 4 hold the K and V scale
+  // where load() puts key 0's.  Written into `slot` when it is >= 0.
+  static __device__ __forceinline__ void new_row(Regs& r, const DecodeArgs& a, int b, int g,
+                                                 int lane, int64_t slot) {
+    const int r0 = lane >> 3, c = lane & 7, t = lane & 15;
+    const u32x4* kn = a.k_new + ((int64_t)b * a.Hkv + g) * 16 + 2 * c;
+    const u32x4* vn = a.v_new + ((int64_t)b * a.Hkv + g) * 16 + 2 * c;
+    float ks, vs;
+    const u32x4 kc = quantize_row16(kn[0], kn[1], ks);
+    const u32x4 vc = quantize_row16(vn[0], vn[1], vs);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    r.k[0] = r0 == 0 ? kc : zero;
+    r.k[1] = zero;
+    r.v[0] = r0 == 0 ? vc : zero;
+    r.v[1] = zero;
+    r.s = (t & 4) ? vs : ks;
+    if (slot >= 0 && r0 == 0) {
+      const int64_t row = (slot * a.Hkv + g) * kD;               // bytes
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.k_pool) + row + 16 * c) = kc;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.v_pool) + row + 16 * c) = vc;
+      if (c == 0) {
+        const int64_t si = ((slot / kPage) * a.Hkv + g) * kPage + slot % kPage;
+        a.ks_pool[si] = ks;
+        a.vs_pool[si] = vs;
+      }
+    }
   }
   template <int G, int U, bool kMask>
   static __device__ __forceinline__ void process(const Regs (&buf)[U], const Q<G>& q,
@@ -628,7 +706,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs a, const int bid) {
   const int w = uniform(threadIdx.x >> 6);
   const int hw = w % HG, pw = w / HG;
   const int g = grp * HG + hw;
-  const int r0 = lane >> 3, c = lane & 7;
   const int S = a.splits;
   const int pps = a.pages_per_split;
   const int ppw = pps / PW;                   // pages per wave (the plan keeps this exact)
@@ -677,21 +754,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs a, const int bid) {
   bool new_bad = false;
   if constexpr (kAppend) {
     if (split == app_split && pw == 0) {
-      const u32x4* kn = a.k_new + ((int64_t)b * a.Hkv + g) * 16;
-      const u32x4* vn = a.v_new + ((int64_t)b * a.Hkv + g) * 16;
-      nrow[0].k[0][0] = kn[c]; nrow[0].k[0][1] = kn[c + 8];
-      nrow[0].v[0][0] = vn[c]; nrow[0].v[0][1] = vn[c + 8];
       const int tp = (n_ctx - 1) / kPage;
       const int id = tp < a.max_blocks ? bt[tp] : -1;
       new_bad = !(id >= 0 && id < a.num_blocks);
-      // lanes 0..7 (r0 = 0) hold chunks c and c + 8 of the new rows
-      if (!new_bad && id < kMaxSlotBlocks && r0 == 0) {
-        const int64_t slot = (int64_t)id * kPage + (n_ctx - 1) % kPage;
-        u32x4* kd = a.k_pool + (slot * a.Hkv + g) * 16;
-        u32x4* vd = a.v_pool + (slot * a.Hkv + g) * 16;
-        kd[c] = nrow[0].k[0][0]; kd[c + 8] = nrow[0].k[0][1];
-        vd[c] = nrow[0].v[0][0]; vd[c + 8] = nrow[0].v[0][1];
-      }
+      const int64_t slot =
+          (!new_bad && id < kMaxSlotBlocks) ? (int64_t)id * kPage + (n_ctx - 1) % kPage : -1;
+      P::new_row(nrow[0], a, b, g, lane, slot);
     }
   }
   const int p1 = min(p0 + pps, n_pages);
@@ -980,6 +1048,7 @@ DecodeArgs make_args(void* out, const void* q, const void* k_cache, const void* 
   a.ctx_lens = ctx_lens;
   a.k_new = a.v_new = nullptr;
   a.k_pool = a.v_pool = nullptr;
+  a.ks_pool = a.vs_pool = nullptr;
   const bool split = plan.splits > 1;
   a.ws_ml = split ? wsb.ml : nullptr;
   a.ws_acc = split ? wsb.acc : nullptr;

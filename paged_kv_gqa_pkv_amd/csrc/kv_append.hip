@@ -76,15 +76,9 @@ append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
 // are token-major like the bf16 pools ([page][16 slots][KV head][D]); the
 // scales (the listing's ks and vs [L, cap, H_kv], one layer, cap cut into
 // pages) sit at [page][KV head][slot] of k_scales or v_scales, so the 16
-// scales a KV head needs from a page are one 64-byte run.
-//
-// The quotients x_d / scale are the correctly rounded ones without a full
-// division each: with y = 1 / scale correctly rounded (one IEEE division per
-// row) and q = x * y, the residual e = x - q * scale is exact in an fma and
-// q + e * y rounds to the correctly rounded quotient (Markstein's theorem for
-// round-to-nearest division; it needs no underflow in the residual, which
-// holds for every |x| >= scale / 2, the only quotients that can round to a
-// nonzero code; smaller ones give code 0 either way).
+// scales a KV head needs from a page are one 64-byte run.  The arithmetic
+// is int8_row_scale / int8_code (correctly rounded quotients without a
+// division per value).
 __device__ __forceinline__ float max16(float x) {
   x = fmaxf(x, dpp_f<kDppQuadSwap1>(x));
   x = fmaxf(x, dpp_f<kDppQuadSwap2>(x));
@@ -114,17 +108,11 @@ append_int8_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_
 #pragma unroll
   for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(x[i]));
   mx = max16(mx);
-  const float scale = mx / 127.0f + 1e-8f;
+  const float scale = int8_row_scale(mx);
   const float y = 1.0f / scale;
   uint32_t pk[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q0 = x[i] * y;
-    const float e = __builtin_fmaf(-q0, scale, x[i]);
-    const float q = __builtin_fmaf(e, y, q0);
-    const float c = fminf(fmaxf(__builtin_rintf(q), -127.f), 127.f);
-    pk[i >> 2] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (i & 3));
-  }
+  for (int i = 0; i < 8; ++i) pk[i >> 2] |= int8_code(x[i], scale, y) << (8 * (i & 3));
   if (slot < 0 || slot >= num_slots) return;
   const int64_t row = slot * Hkv + h;                             // codes row (128 B)
   (which ? v_codes : k_codes)[row * 16 + sub] = make_uint2(pk[0], pk[1]);

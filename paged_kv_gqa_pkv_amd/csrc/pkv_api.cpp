@@ -468,6 +468,31 @@ int pkv_attn_decode_ring(void* out, const void* q, const void* k_cache, const vo
                        "pkv_attn_decode_ring");
 }
 
+int pkv_attn_decode_append_int8(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  pkv::DecodePlan plan;
+  bool done = false;
+  if (B > 0 && (!k_scales || !v_scales)) return fail(PKV_EINVAL, "null pointer argument");
+  int rc = check_decode(out, q, k_codes, v_codes, block_tables, context_lens, B, Hq, Hkv, D,
+                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale,
+                        workspace, workspace_bytes, stream, plan, done);
+  if (rc || done) return rc;
+  if (!k_new || !v_new) return fail(PKV_EINVAL, "null pointer argument");
+  if (k_codes == v_codes) return fail(PKV_EINVAL, "k_codes and v_codes must differ");
+  if (k_scales == v_scales) return fail(PKV_EINVAL, "k_scales and v_scales must differ");
+  return launch_status(pkv::launch_decode_append_int8(out, q, k_new, v_new, k_codes, v_codes,
+                                                      k_scales, v_scales, block_tables,
+                                                      context_lens, B, Hq, Hkv, num_blocks,
+                                                      max_blocks_per_seq, scale, plan, workspace,
+                                                      static_cast<hipStream_t>(stream)),
+                       "pkv_attn_decode_append_int8");
+}
+
 int pkv_attn_decode_int8(void* out, const void* q, const void* k_codes, const void* v_codes,
                          const float* k_scales, const float* v_scales,
                          const int32_t* block_tables,

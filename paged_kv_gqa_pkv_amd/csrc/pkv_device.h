@@ -119,4 +119,25 @@ __device__ __forceinline__ float sbyte(uint32_t w, int i) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The int8 quantiser of one (token, KV head) row, in float32 as the Module
+// 04 page's KV8Cache.write does (kv_cache.py listing, section 5):
+//   scale = max_d |x_d| / 127 + 1e-8,   code_d = clip(rint(x_d / scale), -127, 127)
+// with round half to even.  The quotients x_d / scale are the correctly
+// rounded ones without a full division each: with y = 1 / scale correctly
+// rounded (one IEEE division per row) and q = x * y, the residual
+// e = x - q * scale is exact in an fma and q + e * y rounds to the correctly
+// rounded quotient (Markstein's theorem for round-to-nearest division; it
+// needs no underflow in the residual, which holds for every |x| >= scale / 2,
+// the only quotients that can round to a nonzero code; smaller ones give code
+// 0 either way).  Every kernel that quantises uses these two functions, so
+// their codes and scales agree bit for bit.
+__device__ __forceinline__ float int8_row_scale(float amax) { return amax / 127.0f + 1e-8f; }
+__device__ __forceinline__ uint32_t int8_code(float x, float scale, float y) {
+  const float q0 = x * y;
+  const float e = __builtin_fmaf(-q0, scale, x);
+  const float q = __builtin_fmaf(e, y, q0);
+  const float c = fminf(fmaxf(__builtin_rintf(q), -127.f), 127.f);
+  return (uint32_t)(int32_t)c & 0xffu;
+}
+
 }  // namespace pkv

@@ -67,6 +67,16 @@ hipError_t launch_decode_append(void* out, const void* q, const void* k_new, con
                                 int max_blocks, float scale, const DecodePlan& plan,
                                 void* workspace, hipStream_t stream);
 
+// The same over int8 pages: the new rows are quantised as launch_append_int8
+// quantises them and written with their scales.
+hipError_t launch_decode_append_int8(void* out, const void* q, const void* k_new,
+                                     const void* v_new, void* k_codes, void* v_codes,
+                                     float* k_scales, float* v_scales,
+                                     const int32_t* block_tables, const int32_t* ctx_lens, int B,
+                                     int Hq, int Hkv, int num_blocks, int max_blocks, float scale,
+                                     const DecodePlan& plan, void* workspace,
+                                     hipStream_t stream);
+
 // Decode with the split buffers in the library's own per-device array
 // (no caller workspace).  noalloc_fits tells whether a plan fits that array.
 bool noalloc_fits(const DecodePlan& plan, int B, int Hkv);

@@ -218,6 +218,26 @@ def test_fused_decode_append_rejects_bad_arguments(lib):
     assert call(B=0, out=NULL, kn=NULL) == bd.PKV_OK
 
 
+def test_fused_int8_decode_append_rejects_bad_arguments(lib):
+    """pkv_attn_decode_append_int8 checks what pkv_attn_decode_int8 checks,
+    plus its new rows, two distinct code pools and two distinct scale arrays."""
+    def call(out=1, q=2, kn=3, vn=4, kc=5, vc=6, ks=10, vs=11, B=2, Hq=16, Hkv=8, D=128, mb=4,
+             mcl=64):
+        return lib.pkv_attn_decode_append_int8(out, q, kn, vn, kc, vc, ks, vs, 7, 8, B, Hq, Hkv,
+                                               D, 16, 32, mb, mcl, 0.088, NULL, 0, NULL)
+    assert call(ks=NULL) == bd.PKV_EINVAL
+    assert call(vs=NULL) == bd.PKV_EINVAL
+    assert call(kn=NULL) == bd.PKV_EINVAL
+    assert call(vn=NULL) == bd.PKV_EINVAL
+    assert call(kc=9, vc=9) == bd.PKV_EINVAL                       # one code pool for K and V
+    assert call(ks=12, vs=12) == bd.PKV_EINVAL                     # one scale array for both
+    assert b"scales" in lib.pkv_last_error()
+    assert call(Hq=24) == bd.PKV_EUNSUPPORTED
+    assert call(D=64) == bd.PKV_EUNSUPPORTED
+    assert call(mcl=65) == bd.PKV_EINVAL                            # beyond the table
+    assert call(B=0, out=NULL, kn=NULL, ks=NULL) == bd.PKV_OK
+
+
 def _mixed(lib, out_p=1, out_d=2, Bp=1, T=64, mql=64, mclp=64, Bd=2, mcld=64, Hq=16, Hkv=8,
            D=128, mb=4, pws=NULL, pwb=0, dws=NULL, dwb=0):
     return lib.pkv_attn_prefill_decode(out_p, 3, 4, 5, 6, Bp, T, mql, mclp,
