@@ -25,16 +25,26 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 }
 
 
-// Instantiations by group size G = Hq / Hkv (pages per pipeline stage U by
-// the register budget of each).
+// One group size: bf16 pages from PKV_DECODE_MFMA_MIN_G on run the matrix-core
+// policy; the pages per pipeline stage U follow each policy's register budget.
+template <class P, int G, int U, int UI8, bool kAppend>
+hipError_t launch_policy(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (std::is_same<P, Int8Page>::value)
+    return launch_g<Int8Page, G, UI8, kAppend>(a, stream);
+  else if constexpr (G >= PKV_DECODE_MFMA_MIN_G)
+    return launch_g<Bf16MfmaPage, G, PKV_DECODE_B16M_U, kAppend>(a, stream);
+  else
+    return launch_g<P, G, U, kAppend>(a, stream);
+}
+
+// Instantiations by group size G = Hq / Hkv.
 template <class P, bool kAppend = false>
 hipError_t launch_by_group(const DecodeArgs& a, int G, hipStream_t stream) {
-  constexpr bool kI8 = std::is_same<P, Int8Page>::value;
   switch (G) {
-    case 1: return launch_g<P, 1, kI8 ? PKV_DECODE_I8_U_G1 : PKV_DECODE_U_G1, kAppend>(a, stream);
-    case 2: return launch_g<P, 2, kI8 ? PKV_DECODE_I8_U_G2 : PKV_DECODE_U_G2, kAppend>(a, stream);
-    case 4: return launch_g<P, 4, kI8 ? PKV_DECODE_I8_U_G4 : PKV_DECODE_U_G4, kAppend>(a, stream);
-    case 8: return launch_g<P, 8, kI8 ? PKV_DECODE_I8_U_G8 : PKV_DECODE_U_G8, kAppend>(a, stream);
+    case 1: return launch_policy<P, 1, PKV_DECODE_U_G1, PKV_DECODE_I8_U_G1, kAppend>(a, stream);
+    case 2: return launch_policy<P, 2, PKV_DECODE_U_G2, PKV_DECODE_I8_U_G2, kAppend>(a, stream);
+    case 4: return launch_policy<P, 4, PKV_DECODE_U_G4, PKV_DECODE_I8_U_G4, kAppend>(a, stream);
+    case 8: return launch_policy<P, 8, PKV_DECODE_U_G8, PKV_DECODE_I8_U_G8, kAppend>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -78,6 +78,14 @@ namespace {
 #endif
 
 constexpr int kMaxPagesPerWave = 64;         // one VGPR of page ids per wave
+// Waves a workgroup may hold: eight (two per SIMD, so at most 256 registers
+// per lane) for every group size.  At G = 8 that holds because both pages'
+// policies there keep O in MFMA tiles (about 190 VGPRs); the v_dot2 bf16
+// policy's 16 G accumulators per lane would not fit.
+constexpr int max_waves_for(int) { return 8; }
+#ifndef PKV_DECODE_MFMA_MIN_G
+#define PKV_DECODE_MFMA_MIN_G 8    // bf16 pages: group sizes from which decode runs on the matrix cores
+#endif
 
 __device__ __forceinline__ u32x4 load_kv(const u32x4* p) {
 #if PKV_DECODE_NT
@@ -677,6 +685,184 @@ struct Int8Page {
   }
 };
 
+// bf16 pages on the matrix cores, for large groups (the v_dot2 policy keeps
+// 16 G accumulators per lane, so at G = 8 its registers leave one wave per
+// SIMD).  The products and the softmax bookkeeping are those of Int8Page,
+// without codes or scales: per page and wave, four v_mfma_f32_16x16x32_bf16
+// give S[key][head] (A = K rows read from a wave-private LDS tile, lane
+// (g4, t): row t, dims 32 g4 + 8 kk .. +8 for MFMA kk; B = q of head t, the
+// same dims, zero for t >= G), and eight v_mfma_f32_16x16x16_bf16 add the
+// rounded probabilities times V into O[head][dim] (B operands from
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j + 4k addresses V[key
+// 4 g4 + k][16 blk + 4 j .. +4] and lane i receives V[keys 4 g4 .. +3][16 blk
+// + i], the layout the prefill kernel's V^T reads rely on).  The rows arrive
+// in the v_dot2 policy's registers (full 128-byte lines per load
+// instruction) and go through a 4 KB tile per page whose 16-byte chunks are
+// swizzled by row, chunk ^ ((r & 7) << 1 | r >> 3): the 16 rows one K read
+// instruction touches, and the 8 rows of each half-wave of a V^T read, fall
+// on distinct banks.  Rows of a partial page past its last token are zeroed
+// before they reach the tile (an unwritten slot may hold NaN, and a zero
+// weight times NaN is NaN).  The row sums add the bf16-rounded
+// probabilities, the values the PV product uses.
+#ifndef PKV_DECODE_B16M_U
+#define PKV_DECODE_B16M_U 1        // pages per pipeline stage of the MFMA bf16 policy
+#endif
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4v lds_i16x4v;
+// The tiles of one kernel: kPages pages of kWaves waves, 4 KB each (one
+// array per kernel: every process<> instantiation of it uses the same
+// template arguments).
+template <int kWaves, int kPages>
+__device__ __forceinline__ u32x4 (*b16_lds())[kPages][kPage * 16] {
+  __shared__ u32x4 s_kv[kWaves][kPages][kPage * 16];
+  return s_kv;
+}
+__device__ __forceinline__ int b16_swz(int r) { return ((r & 7) << 1) | (r >> 3); }
+
+struct Bf16MfmaPage {
+  using Regs = Bf16Page::Regs;
+  template <int G>
+  using Q = Int8Page::Q<G>;
+  template <int G>
+  using State = Int8Page::State<G>;
+  template <int G>
+  static __device__ __forceinline__ void init(State<G>& st) { Int8Page::init<G>(st); }
+  template <int G>
+  static __device__ __forceinline__ void load_q(Q<G>& q, const u32x4* qp, int lane) {
+    Int8Page::load_q<G>(q, qp, lane);
+  }
+  static __device__ __forceinline__ void load(Regs& r, const DecodeArgs& a, int64_t blk, int g,
+                                              int lane) {
+    Bf16Page::load(r, a, blk, g, lane);
+  }
+  static __device__ __forceinline__ void new_row(Regs& r, const DecodeArgs& a, int b, int g,
+                                                 int lane, int64_t slot) {
+    Bf16Page::new_row(r, a, b, g, lane, slot);
+  }
+  template <int G, int U, bool kMask>
+  static __device__ __forceinline__ void process(const Regs (&buf)[U], const Q<G>& q,
+                                                 State<G>& st, float scale_log2, int lane,
+                                                 int valid_rows) {
+    static_assert(U <= PKV_DECODE_B16M_U, "tile pages per wave");
+    u32x4 (*s)[PKV_DECODE_B16M_U][kPage * 16] = b16_lds<max_waves_for(G), PKV_DECODE_B16M_U>();
+    const int wv = uniform(threadIdx.x >> 6);
+    const int r0 = lane >> 3, c = lane & 7, t = lane & 15, g4 = lane >> 4;
+    const int sw0 = b16_swz(r0), sw8 = b16_swz(r0 + 8);
+    // K rows into the tiles (chunk cc of row r at position cc ^ swz(r))
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[wv][u][r0 * 16 + ((c + 8 * h) ^ sw0)] = buf[u].k[0][h];
+        s[wv][u][(r0 + 8) * 16 + ((c + 8 * h) ^ sw8)] = buf[u].k[1][h];
+      }
+    }
+    // a wave's LDS accesses run in order; keep the compiler from moving the
+    // reads above the writes of other lanes (and the V writes above the K
+    // reads)
+    asm volatile("" ::: "memory");
+    u32x4 kt[U][4];
+    const int swt = b16_swz(t);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kt[u][kk] = s[wv][u][t * 16 + ((4 * g4 + kk) ^ swt)];
+    asm volatile("" ::: "memory");
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool v0 = !kMask || r0 < valid_rows, v8 = !kMask || r0 + 8 < valid_rows;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[wv][u][r0 * 16 + ((c + 8 * h) ^ sw0)] = v0 ? buf[u].v[0][h] : zero;
+        s[wv][u][(r0 + 8) * 16 + ((c + 8 * h) ^ sw8)] = v8 ? buf[u].v[1][h] : zero;
+      }
+    }
+    asm volatile("" ::: "memory");
+    // the lane's V^T address: key 4 g4 + (t >> 2), dims 16 blk + 4 (t & 3)
+    const int vkey = 4 * g4 + (t >> 2);
+    const int vsw = b16_swz(vkey);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4v s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[u][kk]),
+                                                     q.b[kk], s4, 0, 0, 0);
+      float sc[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const bool keep = !kMask || 4 * g4 + rr < valid_rows;
+        sc[rr] = keep ? s4[rr] * scale_log2 : kNegInf;
+      }
+      const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (__builtin_amdgcn_ballot_w64(t < G && mx > st.m + kRescaleSlack) != 0) {
+        float mh = fmaxf(mx, shfl_xor(mx, 16));
+        mh = fmaxf(mh, shfl_xor(mh, 32));
+        const bool up = mh > st.m + kRescaleSlack;
+        const float alpha = up ? fast_exp2(st.m - mh) : 1.f;   // m = -inf gives 0
+        st.m = up ? mh : st.m;
+        st.l *= alpha;
+        float ai[4];
+        head_factors<G>(alpha, ai, lane);
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st.o[b][i] *= ai[i];
+      }
+      const float mu = (st.m == kNegInf) ? 0.f : st.m;
+      float p[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) p[rr] = fast_exp2(sc[rr] - mu);
+      const uint32_t wp[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wp[0]), as_bf16x2(kBf16PairOne), st.l,
+                                             false);
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wp[1]), as_bf16x2(kBf16PairOne), st.l,
+                                             false);
+      const s16x4 wa = __builtin_bit_cast(s16x4, wp);
+      const char* vb = reinterpret_cast<const char*>(&s[wv][u][0]) + vkey * 256 + 8 * (t & 1);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int chunk = 2 * blk + ((t & 3) >> 1);
+        const i16x4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4v*)(vb + 16 * (chunk ^ vsw)));
+        st.o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            wa, __builtin_bit_cast(s16x4, x), st.o[blk], 0, 0, 0);
+      }
+    }
+  }
+  // As Int8Page::finish, through this policy's tile.
+  template <int G>
+  static __device__ __forceinline__ int finish(State<G>& st, float (&m)[G], float (&l)[G],
+                                               float (&v2)[G][2], int lane) {
+    static_assert(G * kD * 4 <= kPage * 16 * 16, "O fits one tile");
+    const int t = lane & 15, g4 = lane >> 4;
+    float ls = st.l + shfl_xor(st.l, 16);
+    ls += shfl_xor(ls, 32);
+    row_bcast_all<G>(st.m, m);
+    row_bcast_all<G>(ls, l);
+    float* so = reinterpret_cast<float*>(
+        &b16_lds<max_waves_for(G), PKV_DECODE_B16M_U>()[uniform(threadIdx.x >> 6)][0][0]);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * g4 + i < G) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) so[(4 * g4 + i) * kD + 16 * b + t] = st.o[b][i];
+      }
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(so + j * kD + 2 * lane);
+      v2[j][0] = v[0];
+      v2[j][1] = v[1];
+    }
+    asm volatile("" ::: "memory");
+    return 2 * lane;
+  }
+};
+
 // Workgroup = one (sequence b, context split, group of heads_per_wg KV
 // heads); its heads_per_wg * parts waves are (head hw, page part pw), wave
 // w = pw * heads_per_wg + hw.  Wave (hw, pw) serves KV head g = group *
@@ -1012,10 +1198,6 @@ __global__ void __launch_bounds__(kMaxWaves * kWave) decode_kernel(const DecodeA
 #define PKV_DECODE_I8_U_G8 1
 #endif
 
-// Waves a workgroup may hold: two waves per SIMD (eight per CU) fit the
-// register budget of the G <= 4 kernels (at most 256 VGPRs), one per SIMD the
-// G = 8 kernels.
-constexpr int max_waves_for(int G) { return G >= 8 ? 4 : 8; }
 
 // Where the split path keeps its partials and arrival counters.
 struct SplitBuffers {

@@ -129,6 +129,18 @@ def test_decode_long_context_many_splits():
     check_workload(w)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_group_size_8_heads_of_a_large_model_with_splits(fused):
+    """G = 8 (64 query heads over 8 KV heads, the bf16 policy on the matrix
+    cores) with a context long enough for splits, a page boundary, a partial
+    page and a one-token context, every output row compared."""
+    ctxs = [4500, 2048, 1025, 17, 1]
+    w = S.custom_workload("g8_splits", _seqs_decode(ctxs), Hq=64, Hkv=8, D=128,
+                          num_blocks=520, base_seed=83)
+    assert bd.pkv_decode_num_splits(len(ctxs), 64, 8, 128, 4500) > 1
+    check_workload(w, fused=fused)
+
+
 def test_decode_single_pass_large_batch():
     ctxs = [int(x) for x in np.random.default_rng(81).integers(1, 90, size=160)]
     w = S.custom_workload("wide_batch", _seqs_decode(ctxs), Hq=16, Hkv=8, D=128,
