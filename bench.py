@@ -831,8 +831,8 @@ def kernel_bench():
          f"{n_tok} tokens: read K/V rows and slot, write K/V rows")
     i8 = [(torch.zeros((nb, 16, Hkv, D), dtype=torch.int8, device=dev),
            torch.zeros((nb, 16, Hkv, D), dtype=torch.int8, device=dev),
-           torch.zeros((nb, 16, Hkv), dtype=torch.float32, device=dev),
-           torch.zeros((nb, 16, Hkv), dtype=torch.float32, device=dev)) for _ in range(copies)]
+           torch.zeros((nb, Hkv, 16), dtype=torch.float32, device=dev),
+           torch.zeros((nb, Hkv, 16), dtype=torch.float32, device=dev)) for _ in range(copies)]
     sec = _graph_time(lambda i: bd.pkv_append_int8(sets[i % copies][1], sets[i % copies][2],
                                                     sets[i % copies][0], *i8[i % copies]), copies)
     line("append_int8", sec, n_tok * (2 * Hkv * D * 2 + 2 * Hkv * (D + 4) + 4),
@@ -951,6 +951,44 @@ def kernel_bench():
                                  "work": f"one {T}-query chunk at positions {n_r}..{n_p - 1} over a "
                                          f"ring of {W} tokens, Hq {Hq} Hkv {Hkv}, "
                                          f"{flops / 1e9:.1f} GFLOP"}
+    del pools
+    # decode at group sizes 2, 4 and 8 (Hkv 8, Hq 8 G; Qwen3-0.6B-, Qwen3-8B-
+    # and 70B-class head ratios): a batch of 64 at context 4096, pages placed
+    # at random, two pool copies alternated; bf16 pages run the v_dot2 policy
+    # below G = 8 and the matrix-core one at G = 8, int8 pages the
+    # matrix-core one throughout
+    Bg, ng = 64, 4096
+    gpages = ng // 16
+    npg = Bg * gpages + 16
+    btg = (torch.randperm(npg, generator=torch.Generator().manual_seed(19))[:Bg * gpages]
+           .view(Bg, gpages).to(torch.int32).to(dev))
+    ctxg = torch.full((Bg,), ng, dtype=torch.int32, device=dev)
+    for kv in ("bf16", "int8"):
+        if kv == "bf16":
+            gp = [(S.randn_bf16((npg, 16, Hkv, D), 480 + 2 * c, dev),
+                   S.randn_bf16((npg, 16, Hkv, D), 481 + 2 * c, dev)) for c in range(2)]
+            per_tok = 2 * Hkv * D * 2
+        else:
+            gp = [S.int8_pools(npg, Hkv, D, 484 + 3 * c, dev) for c in range(2)]
+            per_tok = 2 * Hkv * (D + 4)
+        for G in (2, 4, 8):
+            Hqg = Hkv * G
+            qg = S.randn_bf16((Bg, Hqg, D), 490 + G, dev)
+            og = torch.empty_like(qg)
+            nw = bd.pkv_decode_workspace_bytes(Bg, Hqg, Hkv, D, ng)
+            wsg = torch.zeros(max(nw, 1), dtype=torch.uint8, device=dev) if nw else None
+            if kv == "bf16":
+                fn = lambda i: bd.pkv_attn_decode(og, qg, gp[i % 2][0], gp[i % 2][1], btg, ctxg,
+                                                  ng, D ** -0.5, workspace=wsg)
+            else:
+                fn = lambda i: bd.pkv_attn_decode_int8(og, qg, *gp[i % 2], btg, ctxg, ng,
+                                                       D ** -0.5, workspace=wsg)
+            sec = _graph_time(fn, 2)
+            line(f"decode_{kv}_g{G}", sec,
+                 Bg * (ng * per_tok + 2 * Hqg * D * 2 + 4 * gpages + 4),
+                 f"batch {Bg} at context {ng}, Hq {Hqg} Hkv {Hkv}, {kv} pages: read the K/V "
+                 "once, q, the table and length, write out")
+        del gp
     return {"kernels": out, "note": "GPU time per call from HIP-graph replay of >= 8 calls"}
 
 

@@ -371,6 +371,17 @@ def bulk_append_inputs(n_tokens: int, num_blocks: int, Hkv: int, D: int, seed: i
     return slots, k_new, v_new, pool_k, pool_v
 
 
+def int8_pools(num_blocks: int, Hkv: int, D: int, seed: int, device="cpu"):
+    """(k_codes, v_codes, k_scales, v_scales) of a fully written int8 pool:
+    codes N(0, CODE_SD) rounded and clamped to +-127, [num_blocks, 16, Hkv, D];
+    scales U[SCALE_LO, SCALE_HI], [num_blocks, Hkv, 16] (head-major pages)."""
+    kc = _codes((num_blocks, PAGE, Hkv, D), seed, "cpu").to(device)
+    vc = _codes((num_blocks, PAGE, Hkv, D), seed + 1, "cpu").to(device)
+    sc = torch.empty((2, num_blocks, Hkv, PAGE), dtype=torch.float32)
+    sc.uniform_(SCALE_LO, SCALE_HI, generator=_gen(seed + 2, "cpu"))
+    return kc, vc, sc[0].contiguous().to(device), sc[1].contiguous().to(device)
+
+
 def large_chunk_inputs(device="cpu", T: int = 2048, offset: int = 6144, Hq: int = 32,
                        Hkv: int = 8, D: int = 128, seed: int = 430) -> dict:
     """One causal chunk of T queries at positions offset..offset+T-1 of a
