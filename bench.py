@@ -59,9 +59,10 @@ def parse():
                         "on its own stream, and a mixed step's decode on a second stream, "
                         "concurrent with the chunk)")
     p.add_argument("--no-fuse", dest="fuse", action="store_false",
-                   help="run a decode-only step's layers as an append call + a decode call "
-                        "(default: one pkv_attn_decode_append call per layer, or "
-                        "pkv_attn_decode_append_int8 over int8 pages)")
+                   help="run each layer's append as its own call before the attention "
+                        "(default: decode-only steps run pkv_attn_decode_append, or "
+                        "pkv_attn_decode_append_int8 over int8 pages, and mixed steps "
+                        "pkv_attn_prefill_decode_append, one call per layer)")
     p.add_argument("--no-mixed", dest="mixed", action="store_false",
                    help="run a mixed step's attention as pkv_attn_prefill_chunk + "
                         "pkv_attn_decode (default: one pkv_attn_prefill_decode call per "
@@ -305,6 +306,9 @@ class Part:
         # the new rows' bf16 bytes in either format
         self.launch_bytes = self.dec_bytes + (nd * 2 * w.Hkv * w.D * 2 if plan.fused else 0)
         self.pre_bytes, self.pre_flops = prefill_work(w, t)
+        # the step's new K/V rows, as one fused mixed call writes them
+        self.new_row_bytes = (int(t.cu_new[-1]) * 2 * w.Hkv * w.D * 2
+                              if plan.fused and plan.mixed else 0)
         self.step_bytes = slot_bytes(w, t) + w.n_layers * (append_bytes(w, t, kv) +
                                                            self.dec_bytes + self.pre_bytes)
 
@@ -363,7 +367,7 @@ def build_parts(name, rotate_mib, device, kv="bf16", fuse=True, mixed=True):
             new = torch.tensor([0, p.new_len] + [1] * len(w.decode_seqs), dtype=torch.int64)
             t = S.Tables(base_t.block_tables, ctx, torch.cumsum(new, 0).to(torch.int32),
                          torch.tensor([q.pre_len for q in w.seqs], dtype=torch.int32))
-            parts.append(Part(w, t, ST.plan_step(w, t, device=device,
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device, fused=fuse,
                                                  mixed=mixed and kv == "bf16"), layers,
                               _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [i % 6])
@@ -410,11 +414,11 @@ def run(args):
         plan, qb = pt.plan, pt.bufs
         c = i % pt.copies
         n_layers = pt.w.n_layers
-        if only is None and not plan.fused:
+        if only is None and plan.needs_slots:
             ST.slot_mapping(plan, stream=stream)
         for l in range(n_layers):
             d = pt.layers[c * n_layers + l]
-            if plan.fused:
+            if plan.fused and not plan.mixed:
                 # decode-only step: the layer's append and decode in one call
                 if record:
                     if record == "gated":
@@ -435,7 +439,9 @@ def run(args):
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     dec_events.append((k, e0, e1, 1))
                 continue
-            if only is None and pt.kv == "int8":
+            if only is None and plan.fused:
+                pass                  # the mixed call below appends the layer's rows itself
+            elif only is None and pt.kv == "int8":
                 bd.pkv_append_int8(qb["kn"], qb["vn"], plan.slot_mapping, d.k_codes, d.v_codes,
                                    d.k_scales, d.v_scales, stream=stream)
             elif only is None:
@@ -447,12 +453,23 @@ def run(args):
                     if record == "gated":
                         torch.cuda._sleep(args.gate_cycles)
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
-                bd.pkv_attn_prefill_decode(qb["op"], qb["qp"], plan.cu_q, plan.bt_prefill,
-                                           plan.ctx_prefill, plan.max_q_len, plan.max_ctx_prefill,
-                                           qb["od"], qb["qd"], plan.bt_decode, plan.ctx_decode,
-                                           plan.max_ctx_decode, d.k_cache, d.v_cache, plan.scale,
-                                           prefill_workspace=plan.prefill_workspace,
-                                           decode_workspace=plan.workspace, stream=stream)
+                if plan.fused:
+                    bd.pkv_attn_prefill_decode_append(
+                        qb["op"], qb["qp"], plan.cu_q, plan.bt_prefill, plan.ctx_prefill,
+                        plan.max_q_len, plan.max_ctx_prefill, qb["od"], qb["qd"],
+                        plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode, qb["kn"],
+                        qb["vn"], plan.slot_mapping, d.k_cache, d.v_cache, plan.scale,
+                        prefill_workspace=plan.prefill_workspace,
+                        decode_workspace=plan.workspace, stream=stream)
+                else:
+                    bd.pkv_attn_prefill_decode(qb["op"], qb["qp"], plan.cu_q, plan.bt_prefill,
+                                               plan.ctx_prefill, plan.max_q_len,
+                                               plan.max_ctx_prefill, qb["od"], qb["qd"],
+                                               plan.bt_decode, plan.ctx_decode,
+                                               plan.max_ctx_decode, d.k_cache, d.v_cache,
+                                               plan.scale,
+                                               prefill_workspace=plan.prefill_workspace,
+                                               decode_workspace=plan.workspace, stream=stream)
                 if record:
                     e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
                     mix_events.append((k, e0, e1, 1))
@@ -611,16 +628,22 @@ def run(args):
     if mix_events:
         durs = [a.elapsed_time(b) * 1e-3 for (_, a, b, _) in mix_events]
         n_launch = sum(n for (_, _, _, n) in mix_events)
-        byts = sum((parts[k].dec_bytes + parts[k].pre_bytes) * n for (k, _, _, n) in mix_events)
+        # a fused call also writes the step's new rows (read from k_new in place
+        # of the pool: the reads are counted above)
+        byts = sum((parts[k].dec_bytes + parts[k].pre_bytes + parts[k].new_row_bytes) * n
+                   for (k, _, _, n) in mix_events)
         fl = sum(parts[k].pre_flops * n for (k, _, _, n) in mix_events)
         achieved = byts / sum(durs) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "mixed_kernel (pkv_attn_prefill_decode)",
+                    "kernel": ("mixed_append_kernel (pkv_attn_prefill_decode_append)"
+                               if parts[0].plan.fused else "mixed_kernel (pkv_attn_prefill_decode)"),
                     "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                     "bytes_per_launch": int(byts / n_launch), "launches": n_launch,
                     "work": "the decode half's K/V, q/out and tables plus the chunk's keys "
-                            "0..o+T-1, q and out, once each",
+                            "0..o+T-1, q and out, once each" + (
+                                "; the step's new K/V rows written into their slots"
+                                if parts[0].plan.fused else ""),
                     "trace": None,
                     "timing": ("HIP events around each launch of an eager pass after the timed "
                                "graph replays, each launch queued behind a GPU sleep"
@@ -632,8 +655,11 @@ def run(args):
                                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                                  "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                                  "launches": n_launch,
-                                 "kernel": "mixed_kernel (pkv_attn_prefill_decode): the chunk's "
-                                           "causal FLOPs over the whole launch, decode included"}
+                                 "kernel": ("mixed_append_kernel (pkv_attn_prefill_decode_append)"
+                                            if parts[0].plan.fused else
+                                            "mixed_kernel (pkv_attn_prefill_decode)") +
+                                           ": the chunk's causal FLOPs over the whole launch, "
+                                           "decode included"}
     w0 = parts[0].w
     cfg = {"workload": WORKLOAD_TEXT.get(args.workload, f"{args.workload}: {w0.description}"),
            "parts": [{"name": p.w.name, "layers": p.w.n_layers, "Hq": p.w.Hq, "Hkv": p.w.Hkv,
@@ -655,7 +681,9 @@ def run(args):
                                               not p.plan.mixed for p in parts)
                else ", one stream") + (
                "; decode-only layers: one fused append + decode call"
-               if any(p.plan.fused for p in parts) else "") + (
+               if any(p.plan.fused and not p.plan.mixed for p in parts) else "") + (
+               "; mixed layers: one launch for the append, the chunk and the decode"
+               if any(p.plan.mixed and p.plan.fused for p in parts) else
                "; mixed layers: append, then one launch for the chunk and the decode"
                if any(p.plan.mixed for p in parts) else ""))}
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,

@@ -304,6 +304,42 @@ int pkv_attn_prefill_decode(void* out_prefill, const void* q_prefill, const int3
                             void* stream);
 
 /*
+ * A mixed step's append and attention in one call ([P1] model.py forward:
+ * each layer writes the step's K/V into the cache and attends over the
+ * cached prefix plus those rows): pkv_append of the step's rows followed by
+ * pkv_attn_prefill_decode, in one launch for group sizes 1, 2 and 4.  The
+ * chunk workgroups read their chunk's own rows from k_new / v_new instead of
+ * the pool (the same bits, so the prefill output is that of the two calls
+ * bit for bit); the decode workgroups take their sequence's new row from
+ * k_new / v_new and write it into its slot, found from the block table as
+ * pkv_attn_decode_append finds it (decode outputs equal those of the two
+ * calls up to the order of float32 sums); further workgroups in the same
+ * grid copy the chunk rows into their slots.  Nothing in the grid reads a
+ * slot the grid writes.  Group size 8, or one half empty, runs pkv_append,
+ * then the attention launches in order.
+ *   k_new, v_new   bf16 [total_q + B_decode][Hkv][D]: the chunk rows of the
+ *                  prefill sequences in cu_q_lens order, then one row per
+ *                  decode sequence
+ *   slot_mapping   int32 [total_q + B_decode], the slots of those rows as
+ *                  pkv_slot_mapping gives them for the step (chunk rows
+ *                  first); a negative slot writes nothing
+ *   k_cache, v_cache   the pools, read and written (distinct)
+ *   the other arguments as for pkv_attn_prefill_decode
+ * Errors: those of pkv_attn_prefill_decode, and PKV_EINVAL for a null
+ * k_new, v_new or slot_mapping or one pool for K and V.
+ */
+int pkv_attn_prefill_decode_append(
+    void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
+    const int32_t* block_tables_prefill, const int32_t* context_lens_prefill, int32_t B_prefill,
+    int32_t total_q, int32_t max_q_len, int32_t max_context_len_prefill, void* out_decode,
+    const void* q_decode, const int32_t* block_tables_decode, const int32_t* context_lens_decode,
+    int32_t B_decode, int32_t max_context_len_decode, const void* k_new, const void* v_new,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t Hq, int32_t Hkv, int32_t D,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+    void* prefill_workspace, size_t prefill_workspace_bytes, void* decode_workspace,
+    size_t decode_workspace_bytes, void* stream);
+
+/*
  * The step before attention, fused ([P1] model.py: rms_norm, _rope_tables,
  * apply_rope and forward, which normalises q and k per head, rotates both at
  * the token's absolute position and writes k and v into the cache; the

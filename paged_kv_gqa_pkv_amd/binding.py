@@ -37,6 +37,9 @@ SIGNATURES = {
     "pkv_attn_prefill_decode": (_c_int, [_vp] * 5 + [_c_int] * 4 + [_vp] * 4 + [_c_int] * 2 +
                                 [_vp] * 2 + [_c_int] * 6 +
                                 [_f, _vp, _c_size, _vp, _c_size, _vp]),
+    "pkv_attn_prefill_decode_append": (_c_int, [_vp] * 5 + [_c_int] * 4 + [_vp] * 4 +
+                                       [_c_int] * 2 + [_vp] * 5 + [_c_int] * 6 +
+                                       [_f, _vp, _c_size, _vp, _c_size, _vp]),
     "pkv_append_int8": (_c_int, [_vp] * 7 + [_c_int] * 5 + [_vp]),
     "pkv_attn_decode_int8": (_c_int, [_vp] * 8 + [_c_int] * 8 + [_f, _vp, _c_size, _vp]),
     "pkv_attn_decode_append_int8": (_c_int, [_vp] * 10 + [_c_int] * 8 + [_f, _vp, _c_size, _vp]),
@@ -307,6 +310,57 @@ def pkv_attn_prefill_decode(out_prefill: torch.Tensor, q_prefill: torch.Tensor,
         _p(out_decode), _p(q_decode), _p(block_tables_decode), _p(context_lens_decode), B_d,
         int(max_context_len_decode), _p(k_cache), _p(v_cache), Hq, Hkv, D, bs, nb, width,
         float(scale), pw, pwb, dw, dwb, _stream(stream)))
+
+
+def pkv_attn_prefill_decode_append(out_prefill: torch.Tensor, q_prefill: torch.Tensor,
+                                   cu_q_lens: torch.Tensor, block_tables_prefill: torch.Tensor,
+                                   context_lens_prefill: torch.Tensor, max_q_len: int,
+                                   max_context_len_prefill: int, out_decode: torch.Tensor,
+                                   q_decode: torch.Tensor, block_tables_decode: torch.Tensor,
+                                   context_lens_decode: torch.Tensor,
+                                   max_context_len_decode: int, k_new: torch.Tensor,
+                                   v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                                   k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float,
+                                   prefill_workspace: Optional[torch.Tensor] = None,
+                                   decode_workspace: Optional[torch.Tensor] = None,
+                                   stream=None) -> None:
+    """A mixed step's append and attention in one call: k_new/v_new
+    [total_q + B_decode, Hkv, D] (the chunk rows, then one row per decode
+    sequence) go into their slots (slot_mapping, the step's) and both halves'
+    attention runs as in pkv_attn_prefill_decode."""
+    for t, n in ((q_prefill, "q_prefill"), (out_prefill, "out_prefill"),
+                 (q_decode, "q_decode"), (out_decode, "out_decode"), (k_new, "k_new"),
+                 (v_new, "v_new")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n, 4)
+    for t, n in ((cu_q_lens, "cu_q_lens"), (context_lens_prefill, "context_lens_prefill"),
+                 (context_lens_decode, "context_lens_decode"), (slot_mapping, "slot_mapping")):
+        _need(t, torch.int32, n, 1)
+    for t, n in ((block_tables_prefill, "block_tables_prefill"),
+                 (block_tables_decode, "block_tables_decode")):
+        _need(t, torch.int32, n, 2)
+    total_q, Hq, D = q_prefill.shape
+    B_d = q_decode.shape[0]
+    nb, bs, Hkv, D2 = k_cache.shape            # [num_blocks, 16, Hkv, D] pages
+    B_p = context_lens_prefill.numel()
+    width = block_tables_prefill.shape[1]
+    if out_prefill.shape != q_prefill.shape or out_decode.shape != q_decode.shape or \
+            q_decode.shape[1:] != (Hq, D) or D2 != D or v_cache.shape != k_cache.shape or \
+            block_tables_prefill.shape[0] != B_p or cu_q_lens.numel() != B_p + 1 or \
+            block_tables_decode.shape != (B_d, width) or context_lens_decode.numel() != B_d or \
+            k_new.shape != (total_q + B_d, Hkv, D) or v_new.shape != k_new.shape or \
+            slot_mapping.numel() != total_q + B_d:
+        raise ValueError("inconsistent shapes")
+    pw, pwb = _ws(prefill_workspace)
+    dw, dwb = _ws(decode_workspace)
+    _check(load().pkv_attn_prefill_decode_append(
+        _p(out_prefill), _p(q_prefill), _p(cu_q_lens), _p(block_tables_prefill),
+        _p(context_lens_prefill), B_p, total_q, int(max_q_len), int(max_context_len_prefill),
+        _p(out_decode), _p(q_decode), _p(block_tables_decode), _p(context_lens_decode), B_d,
+        int(max_context_len_decode), _p(k_new), _p(v_new), _p(slot_mapping), _p(k_cache),
+        _p(v_cache), Hq, Hkv, D, bs, nb, width, float(scale), pw, pwb, dw, dwb,
+        _stream(stream)))
 
 
 def _need_scales(k_scales: torch.Tensor, v_scales: torch.Tensor, codes: torch.Tensor) -> None:

@@ -42,28 +42,15 @@ slot_mapping_kernel(int32_t* __restrict__ slots, const int32_t* __restrict__ blo
   slots[t] = slot;
 }
 
-// Work item = one 16-byte chunk of one token's K or V row ([Hkv][D]).
-// Consecutive threads take consecutive chunks of that row, so both the read
-// from k_new and the write into the token's slot are contiguous runs.
+// Grid-stride row copy (append_rows): consecutive threads take consecutive
+// 16-byte chunks of a token's K or V row.
 __global__ void __launch_bounds__(256)
 append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
               const int32_t* __restrict__ slots, u32x4* __restrict__ k_cache,
               u32x4* __restrict__ v_cache, int64_t n_items, int Hkv, int chunks_per_head,
               int64_t num_slots) {
-  // slot s of the pool starts at chunk s * chunks_per_row (pages of 16 slots)
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int chunks_per_row = Hkv * chunks_per_head;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_items; i += stride) {
-    const int64_t t = i / (2 * chunks_per_row);
-    const int row_item = (int)(i % (2 * chunks_per_row));
-    const int which = row_item / chunks_per_row;
-    const int r = row_item % chunks_per_row;     // chunk within the token's [Hkv][D] row
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const u32x4* src = which ? v_new : k_new;
-    u32x4* dst = which ? v_cache : k_cache;
-    dst[slot * chunks_per_row + r] = src[t * chunks_per_row + r];
-  }
+  append_rows(k_new, v_new, slots, k_cache, v_cache, n_items, Hkv, chunks_per_head, num_slots,
+              (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
 }
 
 // int8 append: quantise each new (token, KV head) row as the Module 04 page

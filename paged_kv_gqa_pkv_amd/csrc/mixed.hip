@@ -24,6 +24,7 @@
 // an XCD as in the separate launches.
 #include "decode_kernel.h"
 #include "prefill_kernel.h"
+#include <algorithm>
 
 namespace pkv {
 
@@ -44,6 +45,50 @@ hipError_t launch_g(const pf::PrefillArgs& pa, const dec::DecodeArgs& da, int n_
                     hipStream_t stream) {
   hipLaunchKernelGGL((mixed_kernel<G, U>), dim3(n_pre + n_dec), dim3(pf::kWaves * kWave), 0,
                      stream, pa, da, n_pre);
+  return hipGetLastError();
+}
+
+// The same step with its append in the grid too (Module 12 page, model.py
+// forward: each layer writes the step's K/V into the cache and attends over
+// the cached prefix plus those rows).  Nothing in the grid reads a slot that
+// the grid writes: the chunk workgroups read their chunk's own rows from
+// k_new (pa.k_new), the decode workgroups take their sequence's new row from
+// k_new and write it into its slot (the fused decode-append body), and the
+// last n_app workgroups copy the chunk rows into their slots.
+struct AppendArgs {
+  const u32x4* k_new;
+  const u32x4* v_new;
+  const int32_t* slots;          // the chunk rows' slots (first total_q entries of the step's)
+  u32x4* k_cache;
+  u32x4* v_cache;
+  int64_t n_items;               // total_q * 2 * Hkv * chunks_per_head
+  int Hkv, chunks_per_head;
+  int64_t num_slots;
+};
+
+template <int G, int U>
+__global__ void __launch_bounds__(pf::kWaves * kWave, 2)
+mixed_append_kernel(const pf::PrefillArgs pa, const dec::DecodeArgs da, const AppendArgs ap,
+                    const int n_prefill_wgs, const int n_decode_wgs) {
+  const int bid = blockIdx.x;
+  if (bid < n_prefill_wgs) {
+    pf::prefill_body<false, true>(pa, bid);
+  } else if (bid < n_prefill_wgs + n_decode_wgs) {
+    dec::decode_body<dec::Bf16Page, G, U, pf::kWaves, true>(da, bid - n_prefill_wgs);
+  } else {
+    const int64_t nt = (int64_t)(gridDim.x - n_prefill_wgs - n_decode_wgs) * blockDim.x;
+    append_rows(ap.k_new, ap.v_new, ap.slots, ap.k_cache, ap.v_cache, ap.n_items, ap.Hkv,
+                ap.chunks_per_head, ap.num_slots,
+                (int64_t)(bid - n_prefill_wgs - n_decode_wgs) * blockDim.x + threadIdx.x, nt);
+  }
+}
+
+template <int G, int U>
+hipError_t launch_append_g(const pf::PrefillArgs& pa, const dec::DecodeArgs& da,
+                           const AppendArgs& ap, int n_pre, int n_dec, int n_app,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL((mixed_append_kernel<G, U>), dim3(n_pre + n_dec + n_app),
+                     dim3(pf::kWaves * kWave), 0, stream, pa, da, ap, n_pre, n_dec);
   return hipGetLastError();
 }
 
@@ -83,6 +128,54 @@ hipError_t launch_prefill_decode(void* out_p, const void* q_p, const int32_t* cu
     case 1: return launch_g<1, PKV_DECODE_U_G1>(pa, da, (int)n_pre, (int)n_dec, stream);
     case 2: return launch_g<2, PKV_DECODE_U_G2>(pa, da, (int)n_pre, (int)n_dec, stream);
     case 4: return launch_g<4, PKV_DECODE_U_G4>(pa, da, (int)n_pre, (int)n_dec, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_decode_append(
+    void* out_p, const void* q_p, const int32_t* cu_q, const int32_t* bt_p, const int32_t* ctx_p,
+    int B_p, int total_q, int max_q_len, const PrefillPlan& pplan, void* ws_p, void* out_d,
+    const void* q_d, const int32_t* bt_d, const int32_t* ctx_d, int B_d, const DecodePlan& dplan,
+    void* ws_d, const void* k_new, const void* v_new, const int32_t* slot_mapping,
+    void* k_cache, void* v_cache, int Hq, int Hkv, int num_blocks, int max_blocks, float scale,
+    hipStream_t stream) {
+  if (!mixed_plan_fits(dplan, Hq / Hkv)) return hipErrorInvalidValue;
+  pf::PrefillArgs pa =
+      pf::make_prefill_args(out_p, q_p, cu_q, k_cache, v_cache, nullptr, nullptr, bt_p, ctx_p,
+                            B_p, total_q, max_q_len, Hq, Hkv, num_blocks, max_blocks, scale, 0,
+                            pplan, ws_p);
+  pa.k_new = static_cast<const u32x4*>(k_new);
+  pa.v_new = static_cast<const u32x4*>(v_new);
+  DecodePlan dp = dplan;
+  dp.heads_per_wg = 1;
+  dec::DecodeArgs da =
+      dec::make_args(out_d, q_d, k_cache, v_cache, nullptr, nullptr, bt_d, ctx_d, B_d, Hq, Hkv,
+                     num_blocks, max_blocks, scale, dp, dec::workspace_buffers(dp, ws_d), 0);
+  // decode sequence b's new row is row total_q + b of k_new / v_new
+  const int64_t row_chunks = (int64_t)Hkv * (kD * 2 / 16);
+  da.k_new = static_cast<const u32x4*>(k_new) + total_q * row_chunks;
+  da.v_new = static_cast<const u32x4*>(v_new) + total_q * row_chunks;
+  da.k_pool = static_cast<u32x4*>(k_cache);
+  da.v_pool = static_cast<u32x4*>(v_cache);
+  AppendArgs ap;
+  ap.k_new = static_cast<const u32x4*>(k_new);
+  ap.v_new = static_cast<const u32x4*>(v_new);
+  ap.slots = slot_mapping;
+  ap.k_cache = static_cast<u32x4*>(k_cache);
+  ap.v_cache = static_cast<u32x4*>(v_cache);
+  ap.chunks_per_head = kD * 2 / 16;
+  ap.Hkv = Hkv;
+  ap.n_items = (int64_t)total_q * 2 * row_chunks;
+  ap.num_slots = (int64_t)num_blocks * kPage;
+  const int64_t n_pre = (int64_t)B_p * pa.qtiles * pa.splits * Hkv;
+  const int64_t n_dec = (int64_t)B_d * dp.splits * Hkv;
+  // one 16-byte item per thread and round; at most 64 workgroups
+  const int64_t n_app = std::min<int64_t>(64, (ap.n_items + 255) / 256);
+  if (n_pre + n_dec + n_app > 0x7fffffff) return hipErrorInvalidValue;
+  switch (Hq / Hkv) {
+    case 1: return launch_append_g<1, PKV_DECODE_U_G1>(pa, da, ap, (int)n_pre, (int)n_dec, (int)n_app, stream);
+    case 2: return launch_append_g<2, PKV_DECODE_U_G2>(pa, da, ap, (int)n_pre, (int)n_dec, (int)n_app, stream);
+    case 4: return launch_append_g<4, PKV_DECODE_U_G4>(pa, da, ap, (int)n_pre, (int)n_dec, (int)n_app, stream);
     default: return hipErrorInvalidValue;
   }
 }

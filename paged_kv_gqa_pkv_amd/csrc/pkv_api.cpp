@@ -720,4 +720,77 @@ int pkv_attn_prefill_decode(void* out_prefill, const void* q_prefill, const int3
   return PKV_OK;
 }
 
+int pkv_attn_prefill_decode_append(
+    void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
+    const int32_t* block_tables_prefill, const int32_t* context_lens_prefill, int32_t B_prefill,
+    int32_t total_q, int32_t max_q_len, int32_t max_context_len_prefill, void* out_decode,
+    const void* q_decode, const int32_t* block_tables_decode, const int32_t* context_lens_decode,
+    int32_t B_decode, int32_t max_context_len_decode, const void* k_new, const void* v_new,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t Hq, int32_t Hkv, int32_t D,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+    void* prefill_workspace, size_t prefill_workspace_bytes, void* decode_workspace,
+    size_t decode_workspace_bytes, void* stream) {
+  pkv::PrefillPlan pplan;
+  bool pdone = true;
+  int rc = check_prefill(out_prefill, q_prefill, cu_q_lens, k_cache, v_cache,
+                         block_tables_prefill, context_lens_prefill, B_prefill, total_q,
+                         max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                         max_context_len_prefill, 0, scale, prefill_workspace,
+                         prefill_workspace_bytes, stream, pplan, pdone);
+  if (rc) return rc;
+  pkv::DecodePlan dplan;
+  bool ddone = false;
+  rc = check_decode(out_decode, q_decode, k_cache, v_cache, block_tables_decode,
+                    context_lens_decode, B_decode, Hq, Hkv, D, block_size, num_blocks,
+                    max_blocks_per_seq, max_context_len_decode, scale, decode_workspace,
+                    decode_workspace_bytes, stream, dplan, ddone);
+  if (rc) return rc;
+  if (pdone && ddone) return PKV_OK;
+  const int32_t n_chunk = pdone ? 0 : total_q;            // chunk rows, then decode rows
+  const int32_t n_rows = n_chunk + (ddone ? 0 : B_decode);
+  if (!k_new || !v_new || !slot_mapping) return fail(PKV_EINVAL, "null pointer argument");
+  if (k_cache == v_cache) return fail(PKV_EINVAL, "k_cache and v_cache must differ");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    rc = validate_slots(slot_mapping, n_rows, num_blocks, s);
+    if (rc) return rc;
+  }
+  if (!pdone && !ddone) {
+    if (out_prefill == out_decode) return fail(PKV_EINVAL, "the two outputs must differ");
+    if (pplan.ws_bytes && dplan.ws_bytes && prefill_workspace == decode_workspace)
+      return fail(PKV_EINVAL, "the two workspaces must differ");
+    if (pkv::mixed_plan_fits(dplan, Hq / Hkv))
+      return launch_status(
+          pkv::launch_prefill_decode_append(
+              out_prefill, q_prefill, cu_q_lens, block_tables_prefill, context_lens_prefill,
+              B_prefill, total_q, max_q_len, pplan, prefill_workspace, out_decode, q_decode,
+              block_tables_decode, context_lens_decode, B_decode, dplan, decode_workspace, k_new,
+              v_new, slot_mapping, k_cache, v_cache, Hq, Hkv, num_blocks, max_blocks_per_seq,
+              scale, s),
+          "pkv_attn_prefill_decode_append");
+  }
+  // one half only, or a shape the one-grid launch does not take: the append,
+  // then the attention launches one after the other
+  rc = launch_status(pkv::launch_append(k_new, v_new, slot_mapping, k_cache, v_cache, n_rows,
+                                        num_blocks, Hkv, D, s),
+                     "pkv_attn_prefill_decode_append");
+  if (rc) return rc;
+  if (!pdone) {
+    rc = launch_status(pkv::launch_prefill(out_prefill, q_prefill, cu_q_lens, k_cache, v_cache,
+                                           nullptr, nullptr, block_tables_prefill,
+                                           context_lens_prefill, B_prefill, total_q, max_q_len,
+                                           Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0,
+                                           pplan, prefill_workspace, s),
+                       "pkv_attn_prefill_decode_append");
+    if (rc) return rc;
+  }
+  if (!ddone)
+    return launch_status(pkv::launch_decode(out_decode, q_decode, k_cache, v_cache,
+                                            block_tables_decode, context_lens_decode, B_decode,
+                                            Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0,
+                                            dplan, decode_workspace, s),
+                         "pkv_attn_prefill_decode_append");
+  return PKV_OK;
+}
+
 }  // extern "C"

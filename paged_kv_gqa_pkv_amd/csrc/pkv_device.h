@@ -119,6 +119,34 @@ __device__ __forceinline__ float sbyte(uint32_t w, int i) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Append as a row copy (Module 12 page, paged.py PagedKVCache.write: the
+// token's K and V rows into its slot; pages token-major, so one token's rows
+// for all KV heads are one contiguous run of Hkv*D*2 bytes).  Work item = one
+// 16-byte chunk of one token's K or V row; items first, first + stride, ...
+// of the n_items = T * 2 * Hkv * chunks_per_head; consecutive items are
+// consecutive chunks of a row, so reads and writes are contiguous runs.
+// Tokens whose slot is outside [0, num_slots) are skipped.
+__device__ __forceinline__ void append_rows(const u32x4* __restrict__ k_new,
+                                            const u32x4* __restrict__ v_new,
+                                            const int32_t* __restrict__ slots,
+                                            u32x4* __restrict__ k_cache,
+                                            u32x4* __restrict__ v_cache, int64_t n_items, int Hkv,
+                                            int chunks_per_head, int64_t num_slots,
+                                            int64_t first, int64_t stride) {
+  const int chunks_per_row = Hkv * chunks_per_head;
+  for (int64_t i = first; i < n_items; i += stride) {
+    const int64_t t = i / (2 * chunks_per_row);
+    const int row_item = (int)(i % (2 * chunks_per_row));
+    const int which = row_item / chunks_per_row;
+    const int r = row_item % chunks_per_row;     // chunk within the token's [Hkv][D] row
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const u32x4* src = which ? v_new : k_new;
+    u32x4* dst = which ? v_cache : k_cache;
+    dst[slot * chunks_per_row + r] = src[t * chunks_per_row + r];
+  }
+}
+
 // The int8 quantiser of one (token, KV head) row, in float32 as the Module
 // 04 page's KV8Cache.write does (kv_cache.py listing, section 5):
 //   scale = max_d |x_d| / 127 + 1e-8,   code_d = clip(rint(x_d / scale), -127, 127)

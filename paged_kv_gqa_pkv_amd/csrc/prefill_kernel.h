@@ -125,6 +125,13 @@ struct PrefillArgs {
   const float* v_scales;
   const int32_t* block_tables;   // [B][max_blocks]
   const int32_t* ctx_lens;       // [B]
+  // Chunk rows taken from the step's new rows (bf16 pages, no ring; the
+  // prefill body's kFresh instance): positions n - T .. n - 1 of sequence b (its chunk) are read
+  // from rows cu_q[b] .. cu_q[b] + T - 1 of k_new / v_new ([total_q][Hkv][D],
+  // the same row stride as a page) instead of the pool, whose slots for them
+  // are written by others during the same launch.
+  const u32x4* k_new;
+  const u32x4* v_new;
   float* ws_acc;                 // [groups][splits][D][128 rows]
   float* ws_ml;                  // [groups][splits][128 rows][2]
   int* counters;                 // [groups] arrivals of the group's splits
@@ -255,7 +262,7 @@ __device__ __forceinline__ TileKeys tile_keys(const PrefillArgs& a, int b, int x
 }
 
 // The workgroup of block bid (see the grid order below).
-template <bool kI8>
+template <bool kI8, bool kFresh = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid) {
   using Lds = PrefillLds<kI8>;
   __shared__ __attribute__((aligned(1024))) char smem[Lds::kBytes];
@@ -374,16 +381,26 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
       dma4(((si & 16) ? a.v_scales : a.k_scales) + (blk * a.Hkv + g) * kPage + (si & 15),
            cs + 2 * kCodeTileBytes + w * kScaleSlotBytes);
     } else {
+      // kFresh (chunk rows from k_new): rows at positions n - T .. n - 1 come
+      // from there (per lane: a page may straddle the chunk's start)
+      const int pos0 = ((tile0 + i) * 4 + w) * kPage;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const int r16 = 4 * qd + dma_r16;
         const int c = (lane & 15) ^ (is_v ? swzv(r16) : swz(r16));
-        const int64_t idx = ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
         const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
-        if (is_v)
-          dma16(a.v_cache + idx, v_lds + off);
-        else
-          dma16(a.k_cache + idx, k_lds + off);
+        const u32x4* src;
+        if constexpr (kFresh) {
+          const int pos = pos0 + r16;
+          const bool fresh = pos >= n - T && pos < n;
+          const int64_t idx = fresh ? ((int64_t)(q_lo + pos - (n - T)) * a.Hkv + g) * 16 + c
+                                    : ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
+          src = (is_v ? (fresh ? a.v_new : a.v_cache) : (fresh ? a.k_new : a.k_cache)) + idx;
+        } else {
+          (void)pos0;
+          src = (is_v ? a.v_cache : a.k_cache) + ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
+        }
+        dma16(src, is_v ? v_lds + off : k_lds + off);
       }
     }
   };
@@ -830,6 +847,7 @@ inline PrefillArgs make_prefill_args(void* out, const void* q, const int32_t* cu
   a.v_scales = v_scales;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
+  a.k_new = a.v_new = nullptr;
   char* ws = static_cast<char*>(workspace);
   const bool split = plan.splits > 1;
   a.ws_acc = split ? reinterpret_cast<float*>(ws) : nullptr;

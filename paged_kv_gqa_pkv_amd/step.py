@@ -12,8 +12,11 @@ since the append is a bit copy.  A step with no prefill chunk (every
 sequence appends its one decode token) runs each layer as one fused call,
 pkv_attn_decode_append, which takes the step's own K/V from the new rows and
 writes them into their slots, as the page's forward does.  A step with both
-runs each layer as the append and one pkv_attn_prefill_decode call, whose
-single launch holds the chunk's and the decode's workgroups.
+runs each layer as one pkv_attn_prefill_decode_append call, whose single
+launch holds the chunk's and the decode's workgroups and the copy of the
+chunk rows into their slots (the chunk reads its own rows from the new rows,
+so nothing in the launch reads a slot it writes); unfused, the append and
+one pkv_attn_prefill_decode call.
 
 Host code only marshals arguments: every operation is a library kernel.
 """
@@ -50,8 +53,14 @@ class StepPlan:
     workspace: Optional[torch.Tensor]
     prefill_workspace: Optional[torch.Tensor]
     scale: float
-    fused: bool = False            # decode-only step: one fused append + decode call per layer
-    mixed: bool = False            # chunk and decode: one pkv_attn_prefill_decode call per layer
+    fused: bool = False            # the layer's append runs inside its attention call
+    mixed: bool = False            # chunk and decode: one call for both halves' attention
+
+    @property
+    def needs_slots(self) -> bool:
+        """Whether the step's slot mapping is used (a fused decode-only step
+        finds its slots inside the decode calls)."""
+        return not self.fused or self.mixed
 
     @property
     def bt_prefill(self):
@@ -72,11 +81,11 @@ class StepPlan:
 
 def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = None,
               fused: bool = True, mixed: bool = True) -> StepPlan:
-    """Index data and workspaces of a step.  fused: run a decode-only step as
-    one pkv_attn_decode_append call per layer (else pkv_append, then
-    pkv_attn_decode).  mixed: run the attention of a step with both chunks
-    and decode tokens as one pkv_attn_prefill_decode call per layer (else
-    pkv_attn_prefill_chunk, then pkv_attn_decode)."""
+    """Index data and workspaces of a step.  mixed: run the attention of a
+    step with both chunks and decode tokens as one call for both halves (else
+    pkv_attn_prefill_chunk, then pkv_attn_decode).  fused: fold the layer's
+    append into that call: pkv_attn_decode_append for a decode-only step,
+    pkv_attn_prefill_decode_append for a mixed one (else pkv_append first)."""
     pre, dec = w.prefill_seqs, w.decode_seqs
     if pre != list(range(len(pre))):
         raise ValueError("prefill sequences must come first")
@@ -110,13 +119,13 @@ def plan_step(w: Workload, t: Tables, device="cuda", scale: Optional[float] = No
         max_q_len=max_q, max_ctx_prefill=max_ctx_pre,
         max_ctx_decode=max_ctx_dec, workspace=ws, prefill_workspace=pws,
         scale=scale if scale is not None else w.D ** -0.5,
-        fused=bool(fused and dec and not pre), mixed=bool(mixed and dec and pre))
+        fused=bool(fused and dec and (not pre or mixed)), mixed=bool(mixed and dec and pre))
 
 
 def slot_mapping(plan: StepPlan, stream=None) -> None:
     """Slots of the step's new tokens; shared by every layer's append (a
     fused decode-only step finds them inside its decode calls and needs
-    none)."""
+    none: plan.needs_slots)."""
     bd.pkv_slot_mapping(plan.slot_mapping, plan.block_tables, plan.cu_new, plan.context_lens,
                         stream=stream)
 
@@ -132,6 +141,15 @@ def layer(plan: StepPlan, k_cache, v_cache, k_new, v_new, q_decode=None, out_dec
     the decode before anything after.
     """
     s = stream if stream is not None else torch.cuda.current_stream()
+    if plan.fused and plan.mixed:
+        bd.pkv_attn_prefill_decode_append(out_prefill, q_prefill, plan.cu_q, plan.bt_prefill,
+                                          plan.ctx_prefill, plan.max_q_len, plan.max_ctx_prefill,
+                                          out_decode, q_decode, plan.bt_decode, plan.ctx_decode,
+                                          plan.max_ctx_decode, k_new, v_new, plan.slot_mapping,
+                                          k_cache, v_cache, plan.scale,
+                                          prefill_workspace=plan.prefill_workspace,
+                                          decode_workspace=plan.workspace, stream=s)
+        return
     if plan.fused:
         bd.pkv_attn_decode_append(out_decode, q_decode, k_new, v_new, k_cache, v_cache,
                                   plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode,

@@ -5,7 +5,11 @@ followed by pkv_attn_decode on the same inputs (the one-grid launch runs the
 same per-workgroup arithmetic), and within the usual tolerance of the
 oracle: for the six c5 steps, group sizes 1, 2, 4 (one launch) and 8 (two
 launches), key splits on both sides, and a HIP graph replayed several
-times."""
+times.  pkv_attn_prefill_decode_append, the same with the layer's append in
+the launch: the pools afterwards bit-identical to the append's, the prefill
+half bit-identical to append + pkv_attn_prefill_chunk, the decode half within
+1e-2 of append + pkv_attn_decode (its new rows are reduced from registers)
+and within the oracle's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -32,7 +36,7 @@ def setup(w):
     t = S.make_tables(w)
     d = S.make_layer(w, t, 0, device="cuda")
     k0, v0 = u16(d.k_cache), u16(d.v_cache)
-    plan = ST.plan_step(w, t)
+    plan = ST.plan_step(w, t, fused=False)
     assert plan.mixed and not plan.fused
     ST.slot_mapping(plan)
     bd.pkv_append(d.k_new, d.v_new, plan.slot_mapping, d.k_cache, d.v_cache)
@@ -136,3 +140,102 @@ def test_graph_replays_are_bit_identical():
         e_p, e_d = mixed_call(d, plan)                # eager work between replays
         torch.cuda.synchronize()
         assert bits_equal(e_p, want_p) and bits_equal(e_d, want_d), rep
+
+
+# --------------------------------------------------------------------------
+# pkv_attn_prefill_decode_append: the layer's append in the same launch
+# --------------------------------------------------------------------------
+
+def fused_setup(w):
+    """Pools before the append (the fused call writes the step's rows)."""
+    t = S.make_tables(w)
+    d = S.make_layer(w, t, 0, device="cuda")
+    k0, v0 = u16(d.k_cache), u16(d.v_cache)
+    plan = ST.plan_step(w, t)
+    assert plan.mixed and plan.fused and plan.needs_slots
+    ST.slot_mapping(plan)
+    return t, d, plan, k0, v0
+
+
+def fused_call(d, plan, kc, vc, stream=None):
+    op = torch.full_like(d.q_prefill, float("nan"))
+    od = torch.full_like(d.q_decode, float("nan"))
+    bd.pkv_attn_prefill_decode_append(op, d.q_prefill, plan.cu_q, plan.bt_prefill,
+                                      plan.ctx_prefill, plan.max_q_len, plan.max_ctx_prefill, od,
+                                      d.q_decode, plan.bt_decode, plan.ctx_decode,
+                                      plan.max_ctx_decode, d.k_new, d.v_new, plan.slot_mapping,
+                                      kc, vc, plan.scale,
+                                      prefill_workspace=plan.prefill_workspace,
+                                      decode_workspace=plan.workspace, stream=stream)
+    return op, od
+
+
+def run_fused(w):
+    print(f"[mixed fused] {w.name}: {w.description}", flush=True)
+    t, d, plan, k0, v0 = fused_setup(w)
+    kc, vc = d.k_cache.clone(), d.v_cache.clone()
+    op, od = fused_call(d, plan, kc, vc)
+    # the same step as separate calls: append, then the chunk and the decode
+    bd.pkv_append(d.k_new, d.v_new, plan.slot_mapping, d.k_cache, d.v_cache)
+    sp, sd = separate_calls(d, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(torch.int16), d.k_cache.view(torch.int16)), "K pool"
+    assert torch.equal(vc.view(torch.int16), d.v_cache.view(torch.int16)), "V pool"
+    assert bits_equal(op, sp), "prefill half differs from append + pkv_attn_prefill_chunk"
+    diff = (od.float() - sd.float()).abs().max().item()
+    print(f"{w.name}: decode half vs append + pkv_attn_decode: max abs {diff:.3e}", flush=True)
+    assert torch.isfinite(od.float()).all() and diff <= 1e-2
+    check_oracle(w, t, d, k0, v0, op, od, w.name + " fused")
+    return t, d, plan, kc, vc, op, od
+
+
+@pytest.mark.parametrize("chunk_step", range(6))
+def test_fused_c5_steps(chunk_step):
+    run_fused(S.workload("c5", chunk_step))
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_fused_group_sizes_chunks_starting_mid_page(G):
+    """Chunks that start inside a page (positions 3000 and 40: the page holds
+    cached rows before the chunk's first and fresh ones from it on), key
+    splits, decode sequences of ragged lengths; G = 8 takes the separate
+    launches."""
+    Hkv = 2
+    seqs = [S.SeqSpec(3000, 200, True), S.SeqSpec(40, 33, True),
+            S.SeqSpec(0, 1, False), S.SeqSpec(16, 1, False), S.SeqSpec(300, 1, False),
+            S.SeqSpec(5000, 1, False)]
+    w = S.custom_workload(f"mixed_fused_G{G}", seqs, Hq=Hkv * G, Hkv=Hkv, D=128,
+                          num_blocks=640, base_seed=720 + G)
+    run_fused(w)
+
+
+def test_fused_graph_replays_are_bit_identical():
+    """The fused call writes the same rows into the same slots on every call,
+    so replays and eager calls in between give the same outputs and pools."""
+    w = S.workload("c5", 3)
+    t, d, plan, k0, v0 = fused_setup(w)
+    want_p, want_d = fused_call(d, plan, d.k_cache, d.v_cache)
+    torch.cuda.synchronize()
+    kc_want = d.k_cache.clone()
+    op = torch.empty_like(want_p)
+    od = torch.empty_like(want_d)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            p_, d_ = fused_call(d, plan, d.k_cache, d.v_cache, stream=cap)
+            op.copy_(p_)
+            od.copy_(d_)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        op.fill_(0)
+        od.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bits_equal(op, want_p) and bits_equal(od, want_d), rep
+        e_p, e_d = fused_call(d, plan, d.k_cache, d.v_cache)        # eager work between replays
+        torch.cuda.synchronize()
+        assert bits_equal(e_p, want_p) and bits_equal(e_d, want_d), rep
+    assert torch.equal(d.k_cache.view(torch.int16), kc_want.view(torch.int16))

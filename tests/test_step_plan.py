@@ -30,6 +30,7 @@ def test_c5_steps_plan_the_chunk_and_the_decode_batch(lib):
         o, T = 512 * s, min(512, 3000 - 512 * s)
         assert (p.n_prefill, p.n_decode, p.max_q_len, p.max_ctx_prefill) == (1, 7, T, o + T)
         assert p.cu_q.tolist() == [0, T]
+        assert p.mixed and p.fused and p.needs_slots   # one append + attention call per layer
         assert p.slot_mapping.numel() == T + 7
         assert p.ctx_prefill.tolist() == [o + T]
         assert p.bt_prefill.shape[0] == 1 and p.bt_decode.shape[0] == 7
@@ -53,7 +54,19 @@ def test_decode_only_steps(lib):
     assert p.workspace.numel() == bd.pkv_decode_workspace_bytes(13, 32, 8, 128, 32768)
     p = ST.plan_step(S.workload("c3"), S.make_tables(S.workload("c3")), device="cpu",
                      fused=False)
-    assert not p.fused
+    assert not p.fused and p.needs_slots
+
+
+def test_fused_and_mixed_flags(lib):
+    w = S.workload("c5", 2)
+    t = S.make_tables(w)
+    p = ST.plan_step(w, t, device="cpu", fused=False)
+    assert p.mixed and not p.fused and p.needs_slots       # append, then one attention call
+    p = ST.plan_step(w, t, device="cpu", mixed=False)
+    assert not p.mixed and not p.fused and p.needs_slots   # append, chunk call, decode call
+    w = S.workload("c4a")
+    p = ST.plan_step(w, S.make_tables(w), device="cpu")
+    assert p.fused and not p.mixed and not p.needs_slots
 
 
 def test_step_at_the_budget_is_accepted(lib):
