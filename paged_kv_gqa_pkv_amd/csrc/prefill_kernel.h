@@ -167,6 +167,13 @@ __device__ __forceinline__ void dma16(const u32x4* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(lds) : "memory");
 }
+// The same from a uniform base (SGPRs) plus a 32-bit per-lane byte offset:
+// the address costs no vector instructions when only the base changes from
+// one page to the next.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory");
+}
 // The same with 4 bytes per lane: lane i writes LDS bytes [lds + 4 i, lds + 4 i + 4).
 __device__ __forceinline__ void dma4(const float* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
@@ -351,6 +358,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
   // loading during the table reads) keeps those waits out of the loop.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
+  // Lane t of this wave holds the id of the wave's page of tile t (nt <= 64),
+  // so that a step takes its page ids with readlane instead of LDS reads.
+  const int wave_ids = lane < nt ? s_ids[4 * lane + w] : 0;
 
   // DMA of tile i (relative): wave w copies page w of the tile, the 16 rows
   // of KV head g (token-major pages: Hkv rows apart).  bf16: the K or the V
@@ -364,44 +374,75 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
   const uint32_t k_lds = lds_offset(smem);
   const uint32_t v_lds = k_lds + Lds::kVOff;
   const int dma_r16 = lane >> 4;              // + 4q: row within the page
+  // Byte offsets of this lane's 16-byte piece within a page (bf16: row
+  // r16 = 4q + lane/16 of head g, chunk (lane%16) ^ swizzle, per DMA
+  // instruction q and K or V; int8: row 8q + lane/8, chunk lane%8), and the
+  // bytes of one page of the pool.
+  uint32_t koff[kI8 ? 2 : 4], voff[kI8 ? 1 : 4];
+  if constexpr (kI8) {
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd)
+      koff[qd] = (uint32_t)((((8 * qd + (lane >> 3)) * a.Hkv + g) * 8 + (lane & 7)) * 16);
+    voff[0] = 0;
+  } else {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int r16 = 4 * qd + dma_r16;
+      koff[qd] = (uint32_t)(((r16 * a.Hkv + g) * 16 + ((lane & 15) ^ swz(r16))) * 16);
+      voff[qd] = (uint32_t)(((r16 * a.Hkv + g) * 16 + ((lane & 15) ^ swzv(r16))) * 16);
+    }
+  }
+  const int64_t page_bytes = (int64_t)kPage * a.Hkv * kD * (kI8 ? 1 : 2);
   auto issue = [&](int i, bool is_v = false) {
     const int stage = kI8 ? i % kStages : (i & 1);
-    const int64_t blk = __builtin_amdgcn_readfirstlane(s_ids[4 * i + w]);
+    const int64_t blk = __builtin_amdgcn_readlane(wave_ids, i);
     if constexpr (kI8) {
       (void)is_v;
       const uint32_t cs = k_lds + Lds::kCodeOff + stage * kCodeStageBytes;
+      const char* kb = reinterpret_cast<const char*>(a.k_cache) + blk * page_bytes;
+      const char* vb = reinterpret_cast<const char*>(a.v_cache) + blk * page_bytes;
 #pragma unroll
       for (int qd = 0; qd < 2; ++qd) {
         const uint32_t off = (uint32_t)(w * kPage * kD + qd * 1024);
-        const int64_t row = (blk * kPage + 8 * qd + (lane >> 3)) * a.Hkv + g;   // 8 chunks per row
-        dma16(a.k_cache + row * 8 + (lane & 7), cs + off);
-        dma16(a.v_cache + row * 8 + (lane & 7), cs + kCodeTileBytes + off);
+        dma16s(kb, koff[qd], cs + off);
+        dma16s(vb, koff[qd], cs + kCodeTileBytes + off);
       }
       const int si = lane & 31;
       dma4(((si & 16) ? a.v_scales : a.k_scales) + (blk * a.Hkv + g) * kPage + (si & 15),
            cs + 2 * kCodeTileBytes + w * kScaleSlotBytes);
     } else {
-      // kFresh (chunk rows from k_new): rows at positions n - T .. n - 1 come
-      // from there (per lane: a page may straddle the chunk's start)
-      const int pos0 = ((tile0 + i) * 4 + w) * kPage;
+      const uint32_t lds0 = (is_v ? v_lds : k_lds) + stage * kTileBytes + 16 * w * kRowBytes;
+      const char* base = reinterpret_cast<const char*>(is_v ? a.v_cache : a.k_cache) +
+                         blk * page_bytes;
+      if constexpr (kFresh) {
+        // Chunk rows from k_new / v_new: positions n - T .. n - 1 come from
+        // there.  A page wholly inside them is one base (the new rows have a
+        // page's row stride); a page that straddles either end of them
+        // picks its source per lane.
+        const int pos0 = ((tile0 + i) * 4 + w) * kPage;
+        const int f0 = n - T;
+        if (pos0 >= f0 && pos0 + kPage <= n) {
+          base = reinterpret_cast<const char*>(is_v ? a.v_new : a.k_new) +
+                 (int64_t)(q_lo + pos0 - f0) * a.Hkv * kRowBytes;
+        } else if (pos0 + kPage > f0 && pos0 < n) {
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int r16 = 4 * qd + dma_r16;
-        const int c = (lane & 15) ^ (is_v ? swzv(r16) : swz(r16));
-        const uint32_t off = (uint32_t)(stage * kTileBytes + (16 * w + 4 * qd) * kRowBytes);
-        const u32x4* src;
-        if constexpr (kFresh) {
-          const int pos = pos0 + r16;
-          const bool fresh = pos >= n - T && pos < n;
-          const int64_t idx = fresh ? ((int64_t)(q_lo + pos - (n - T)) * a.Hkv + g) * 16 + c
-                                    : ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
-          src = (is_v ? (fresh ? a.v_new : a.v_cache) : (fresh ? a.k_new : a.k_cache)) + idx;
-        } else {
-          (void)pos0;
-          src = (is_v ? a.v_cache : a.k_cache) + ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
+          for (int qd = 0; qd < 4; ++qd) {
+            const int r16 = 4 * qd + dma_r16;
+            const int c = (lane & 15) ^ (is_v ? swzv(r16) : swz(r16));
+            const int pos = pos0 + r16;
+            const bool fresh = pos >= f0 && pos < n;
+            const int64_t idx = fresh ? ((int64_t)(q_lo + pos - f0) * a.Hkv + g) * 16 + c
+                                      : ((blk * kPage + r16) * a.Hkv + g) * 16 + c;
+            const u32x4* src =
+                (is_v ? (fresh ? a.v_new : a.v_cache) : (fresh ? a.k_new : a.k_cache)) + idx;
+            dma16(src, lds0 + 4 * qd * kRowBytes);
+          }
+          return;
         }
-        dma16(src, is_v ? v_lds + off : k_lds + off);
       }
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        dma16s(base, is_v ? voff[qd] : koff[qd], lds0 + 4 * qd * kRowBytes);
     }
   };
 
