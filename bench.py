@@ -914,6 +914,28 @@ def kernel_bench():
     sec = _graph_time(lambda i: dst.copy_(src), 1)
     line("device_copy", sec, 2 << 29, "torch copy of 512 MiB: read and write each byte once")
     del src, dst
+    # what a tuned library GEMM reaches on this part in bf16 (hipBLASLt
+    # through torch.mm, timed eagerly with events): the box's practical
+    # matrix-core ceiling, beside the 2.5 PFLOP/s figure
+    ga = S.randn_bf16((8192, 8192), 11, dev)
+    gb = S.randn_bf16((8192, 8192), 12, dev)
+    gc = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.mm(ga, gb, out=gc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        torch.mm(ga, gb, out=gc)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / 20
+    gemm_tflops = 2 * 8192 ** 3 / sec / 1e12
+    out["bf16_gemm_8192"] = {"us": round(sec * 1e6, 2), "TFLOPs": round(gemm_tflops, 1),
+                             "frac_of_bf16_peak": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+                             "work": "torch.mm of two 8192 x 8192 bf16 matrices, "
+                                     "1099.5 GFLOP: the box's library GEMM ceiling"}
+    del ga, gb, gc
     # chunked prefill on a large chunk: 2048 queries at positions 6144..8191
     # (Qwen3-8B heads: 64 row tiles of 128 rows per KV head, 512 in all, which
     # the planner cuts into 2 key splits), bf16 and int8 pages; reported
@@ -930,6 +952,7 @@ def kernel_bench():
                                                           workspace=ws), 1)
     out["prefill_2048x8192"] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 1),
                                 "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                "frac_of_gemm": round(flops / sec / 1e12 / gemm_tflops, 4),
                                 "work": f"one {T}-query causal chunk at positions {o}..{n - 1}, "
                                         f"Hq {Hq} Hkv {Hkv}, {flops / 1e9:.1f} GFLOP"}
     sec = _graph_time(lambda i: bd.pkv_attn_prefill_chunk_int8(
@@ -938,6 +961,7 @@ def kernel_bench():
     out["prefill_int8_2048x8192"] = {"us": round(sec * 1e6, 2),
                                      "TFLOPs": round(flops / sec / 1e12, 1),
                                      "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                     "frac_of_gemm": round(flops / sec / 1e12 / gemm_tflops, 4),
                                      "work": "the same chunk over int8 pages"}
     del c
     # sliding-window ring paging, a window of 4096 tokens (Module 04 page,
@@ -976,6 +1000,7 @@ def kernel_bench():
         workspace=wsp), 2)
     out["prefill_ring_w4096"] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 1),
                                  "frac_of_bf16_peak": round(flops / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                 "frac_of_gemm": round(flops / sec / 1e12 / gemm_tflops, 4),
                                  "work": f"one {T}-query chunk at positions {n_r}..{n_p - 1} over a "
                                          f"ring of {W} tokens, Hq {Hq} Hkv {Hkv}, "
                                          f"{flops / 1e9:.1f} GFLOP"}
@@ -1017,7 +1042,8 @@ def kernel_bench():
                  f"batch {Bg} at context {ng}, Hq {Hqg} Hkv {Hkv}, {kv} pages: read the K/V "
                  "once, q, the table and length, write out")
         del gp
-    return {"kernels": out, "note": "GPU time per call from HIP-graph replay of >= 8 calls"}
+    return {"kernels": out, "note": "GPU time per call from HIP-graph replay of >= 8 calls "
+                                   "(the library GEMM: 20 eager calls between HIP events)"}
 
 
 def main():
