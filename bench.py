@@ -66,7 +66,7 @@ def parse():
     p.add_argument("--no-mixed", dest="mixed", action="store_false",
                    help="run a mixed step's attention as pkv_attn_prefill_chunk + "
                         "pkv_attn_decode (default: one pkv_attn_prefill_decode call per "
-                        "layer, bf16 pages)")
+                        "layer; int8 pages: pkv_attn_prefill_decode_int8)")
     p.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                    help="page format: bf16, or int8 codes with per-(slot, head) scales")
     p.add_argument("--kernels", action="store_true",
@@ -278,14 +278,16 @@ def slot_bytes(w, t):
     return T * 12 + 4 * (len(w.seqs) * 2 + 1)
 
 
-def prefill_work(w, t):
-    """(bytes, causal FLOPs) of the prefill chunks: K/V of keys 0..o+T-1 once,
-    q and out; FLOPs over visible (query, key) pairs only."""
+def prefill_work(w, t, kv="bf16"):
+    """(bytes, causal FLOPs) of the prefill chunks: K/V of keys 0..o+T-1 once
+    (int8 pages: codes and a float32 scale per key and KV head), q and out;
+    FLOPs over visible (query, key) pairs only."""
     by, fl = 0, 0
+    per_key = 2 * w.Hkv * (w.D * 2 if kv == "bf16" else w.D + 4)
     for i in w.prefill_seqs:
         s = w.seqs[i]
         o, T, n = s.pre_len, s.new_len, s.ctx
-        by += n * 2 * w.Hkv * w.D * 2 + 2 * T * w.Hq * w.D * 2 + 4 * ((n + 15) // 16)
+        by += n * per_key + 2 * T * w.Hq * w.D * 2 + 4 * ((n + 15) // 16)
         fl += 4 * w.D * w.Hq * (T * o + T * (T + 1) // 2)
     return by, fl
 
@@ -305,7 +307,7 @@ class Part:
         # rows into the pool (int8 pages: their codes and scales), which adds
         # the new rows' bf16 bytes in either format
         self.launch_bytes = self.dec_bytes + (nd * 2 * w.Hkv * w.D * 2 if plan.fused else 0)
-        self.pre_bytes, self.pre_flops = prefill_work(w, t)
+        self.pre_bytes, self.pre_flops = prefill_work(w, t, kv)
         # the step's new K/V rows, as one fused mixed call writes them
         self.new_row_bytes = (int(t.cu_new[-1]) * 2 * w.Hkv * w.D * 2
                               if plan.fused and plan.mixed else 0)
@@ -367,9 +369,11 @@ def build_parts(name, rotate_mib, device, kv="bf16", fuse=True, mixed=True):
             new = torch.tensor([0, p.new_len] + [1] * len(w.decode_seqs), dtype=torch.int64)
             t = S.Tables(base_t.block_tables, ctx, torch.cumsum(new, 0).to(torch.int32),
                          torch.tensor([q.pre_len for q in w.seqs], dtype=torch.int32))
-            parts.append(Part(w, t, ST.plan_step(w, t, device=device, fused=fuse,
-                                                 mixed=mixed and kv == "bf16"), layers,
-                              _bufs(w, t, device), copies, kv))
+            # int8 pages: the append stays a launch of its own (no int8 form
+            # of the one-launch append + attention)
+            parts.append(Part(w, t, ST.plan_step(w, t, device=device,
+                                                 fused=fuse and kv == "bf16", mixed=mixed),
+                              layers, _bufs(w, t, device), copies, kv))
         return parts, (lambda i: [i % 6])
     w = S.workload(name)
     t = S.make_tables(w)
@@ -453,7 +457,15 @@ def run(args):
                     if record == "gated":
                         torch.cuda._sleep(args.gate_cycles)
                     e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
-                if plan.fused:
+                if pt.kv == "int8":
+                    bd.pkv_attn_prefill_decode_int8(
+                        qb["op"], qb["qp"], plan.cu_q, plan.bt_prefill, plan.ctx_prefill,
+                        plan.max_q_len, plan.max_ctx_prefill, qb["od"], qb["qd"],
+                        plan.bt_decode, plan.ctx_decode, plan.max_ctx_decode, d.k_codes,
+                        d.v_codes, d.k_scales, d.v_scales, plan.scale,
+                        prefill_workspace=plan.prefill_workspace,
+                        decode_workspace=plan.workspace, stream=stream)
+                elif plan.fused:
                     bd.pkv_attn_prefill_decode_append(
                         qb["op"], qb["qp"], plan.cu_q, plan.bt_prefill, plan.ctx_prefill,
                         plan.max_q_len, plan.max_ctx_prefill, qb["od"], qb["qd"],
@@ -634,10 +646,12 @@ def run(args):
                    for (k, _, _, n) in mix_events)
         fl = sum(parts[k].pre_flops * n for (k, _, _, n) in mix_events)
         achieved = byts / sum(durs) / 1e9
+        mix_kernel = ("mixed_int8_kernel (pkv_attn_prefill_decode_int8)" if args.kv == "int8"
+                      else "mixed_append_kernel (pkv_attn_prefill_decode_append)"
+                      if parts[0].plan.fused else "mixed_kernel (pkv_attn_prefill_decode)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": ("mixed_append_kernel (pkv_attn_prefill_decode_append)"
-                               if parts[0].plan.fused else "mixed_kernel (pkv_attn_prefill_decode)"),
+                    "kernel": mix_kernel,
                     "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                     "bytes_per_launch": int(byts / n_launch), "launches": n_launch,
                     "work": "the decode half's K/V, q/out and tables plus the chunk's keys "
@@ -655,9 +669,7 @@ def run(args):
                                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                                  "avg_launch_us": round(sum(durs) / n_launch * 1e6, 2),
                                  "launches": n_launch,
-                                 "kernel": ("mixed_append_kernel (pkv_attn_prefill_decode_append)"
-                                            if parts[0].plan.fused else
-                                            "mixed_kernel (pkv_attn_prefill_decode)") +
+                                 "kernel": mix_kernel +
                                            ": the chunk's causal FLOPs over the whole launch, "
                                            "decode included"}
     w0 = parts[0].w

@@ -463,6 +463,30 @@ int pkv_attn_prefill_chunk_int8(void* out, const void* q, const int32_t* cu_q_le
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The attention of a mixed step over int8 pages ([P1] "Why chunked prefill";
+ * [P2] KV8Cache.read): pkv_attn_prefill_chunk_int8 over the prefill
+ * sequences and pkv_attn_decode_int8 over the decode sequences, with the same
+ * outputs bit for bit, as pkv_attn_prefill_decode does for bf16 pages.
+ * Group sizes 1, 2 and 4 run as one launch holding both kinds of workgroup
+ * (one per compute unit: the chunk's code ring takes most of the LDS); group
+ * size 8, or one half empty, runs the two launches in order.  Arguments as
+ * for pkv_attn_prefill_decode, with the pools replaced by k_codes, v_codes,
+ * k_scales and v_scales in the layout above.  Errors: those of
+ * pkv_attn_prefill_decode, and PKV_EINVAL for null scales.  The step's rows
+ * must be appended (pkv_append_int8) before the call.
+ */
+int pkv_attn_prefill_decode_int8(
+    void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
+    const int32_t* block_tables_prefill, const int32_t* context_lens_prefill, int32_t B_prefill,
+    int32_t total_q, int32_t max_q_len, int32_t max_context_len_prefill, void* out_decode,
+    const void* q_decode, const int32_t* block_tables_decode, const int32_t* context_lens_decode,
+    int32_t B_decode, int32_t max_context_len_decode, const void* k_codes, const void* v_codes,
+    const float* k_scales, const float* v_scales, int32_t Hq, int32_t Hkv, int32_t D,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+    void* prefill_workspace, size_t prefill_workspace_bytes, void* decode_workspace,
+    size_t decode_workspace_bytes, void* stream);
+
+/*
  * Ring (sliding-window) paging ([P2] section 4, "Capacity-cache": beyond the
  * capacity the cache becomes a ring, position p is written at index
  * p % capacity over the oldest token, a read returns the last

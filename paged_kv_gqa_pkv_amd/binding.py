@@ -37,6 +37,9 @@ SIGNATURES = {
     "pkv_attn_prefill_decode": (_c_int, [_vp] * 5 + [_c_int] * 4 + [_vp] * 4 + [_c_int] * 2 +
                                 [_vp] * 2 + [_c_int] * 6 +
                                 [_f, _vp, _c_size, _vp, _c_size, _vp]),
+    "pkv_attn_prefill_decode_int8": (_c_int, [_vp] * 5 + [_c_int] * 4 + [_vp] * 4 + [_c_int] * 2 +
+                                     [_vp] * 4 + [_c_int] * 6 +
+                                     [_f, _vp, _c_size, _vp, _c_size, _vp]),
     "pkv_attn_prefill_decode_append": (_c_int, [_vp] * 5 + [_c_int] * 4 + [_vp] * 4 +
                                        [_c_int] * 2 + [_vp] * 5 + [_c_int] * 6 +
                                        [_f, _vp, _c_size, _vp, _c_size, _vp]),
@@ -449,6 +452,52 @@ def pkv_attn_decode_int8(out: torch.Tensor, q: torch.Tensor, k_codes: torch.Tens
                                        Hkv, D, bs, nb, block_tables.shape[1],
                                        int(max_context_len), float(scale), ws_ptr, ws_bytes,
                                        _stream(stream)))
+
+
+def pkv_attn_prefill_decode_int8(out_prefill: torch.Tensor, q_prefill: torch.Tensor,
+                                 cu_q_lens: torch.Tensor, block_tables_prefill: torch.Tensor,
+                                 context_lens_prefill: torch.Tensor, max_q_len: int,
+                                 max_context_len_prefill: int, out_decode: torch.Tensor,
+                                 q_decode: torch.Tensor, block_tables_decode: torch.Tensor,
+                                 context_lens_decode: torch.Tensor, max_context_len_decode: int,
+                                 k_codes: torch.Tensor, v_codes: torch.Tensor,
+                                 k_scales: torch.Tensor, v_scales: torch.Tensor, scale: float,
+                                 prefill_workspace: Optional[torch.Tensor] = None,
+                                 decode_workspace: Optional[torch.Tensor] = None,
+                                 stream=None) -> None:
+    """pkv_attn_prefill_decode over int8 pools (codes [num_blocks, 16, Hkv, D],
+    scales [num_blocks, Hkv, 16]): the outputs of pkv_attn_prefill_chunk_int8
+    and pkv_attn_decode_int8 from one call."""
+    for t, n in ((q_prefill, "q_prefill"), (out_prefill, "out_prefill"),
+                 (q_decode, "q_decode"), (out_decode, "out_decode")):
+        _need(t, torch.bfloat16, n, 3)
+    for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _need(t, torch.int8, n, 4)
+    _need_scales(k_scales, v_scales, k_codes)
+    for t, n in ((cu_q_lens, "cu_q_lens"), (context_lens_prefill, "context_lens_prefill"),
+                 (context_lens_decode, "context_lens_decode")):
+        _need(t, torch.int32, n, 1)
+    for t, n in ((block_tables_prefill, "block_tables_prefill"),
+                 (block_tables_decode, "block_tables_decode")):
+        _need(t, torch.int32, n, 2)
+    total_q, Hq, D = q_prefill.shape
+    B_d = q_decode.shape[0]
+    nb, bs, Hkv, D2 = k_codes.shape
+    B_p = context_lens_prefill.numel()
+    width = block_tables_prefill.shape[1]
+    if out_prefill.shape != q_prefill.shape or out_decode.shape != q_decode.shape or \
+            q_decode.shape[1:] != (Hq, D) or D2 != D or v_codes.shape != k_codes.shape or \
+            block_tables_prefill.shape[0] != B_p or cu_q_lens.numel() != B_p + 1 or \
+            block_tables_decode.shape != (B_d, width) or context_lens_decode.numel() != B_d:
+        raise ValueError("inconsistent shapes")
+    pw, pwb = _ws(prefill_workspace)
+    dw, dwb = _ws(decode_workspace)
+    _check(load().pkv_attn_prefill_decode_int8(
+        _p(out_prefill), _p(q_prefill), _p(cu_q_lens), _p(block_tables_prefill),
+        _p(context_lens_prefill), B_p, total_q, int(max_q_len), int(max_context_len_prefill),
+        _p(out_decode), _p(q_decode), _p(block_tables_decode), _p(context_lens_decode), B_d,
+        int(max_context_len_decode), _p(k_codes), _p(v_codes), _p(k_scales), _p(v_scales), Hq,
+        Hkv, D, bs, nb, width, float(scale), pw, pwb, dw, dwb, _stream(stream)))
 
 
 def pkv_attn_prefill_chunk_int8(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,

@@ -409,7 +409,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-constexpr int kI8LdsWaves = 8;    // waves of a workgroup (at most)
+#ifndef PKV_I8_LDS_WAVES
+#define PKV_I8_LDS_WAVES 8          // waves of an int8 decode workgroup (at most)
+#endif
+constexpr int kI8LdsWaves = PKV_I8_LDS_WAVES;
 constexpr int kI8LdsPages = 2;    // pages per process call (at most)
 // The K/V staging buffers, 2 KB per (wave, page): one array per kernel
 // (declared in a function that is not a template, so the instantiations of

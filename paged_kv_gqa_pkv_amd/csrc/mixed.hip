@@ -22,6 +22,9 @@
 // workgroups come first in the grid (they are the longer ones); both halves
 // keep their own KV-head-fastest order, so each KV head's workgroups share
 // an XCD as in the separate launches.
+// Every decode workgroup here has four waves: the int8 page staging buffers
+// are sized for that, which leaves room in the LDS for the int8 chunk body.
+#define PKV_I8_LDS_WAVES 4
 #include "decode_kernel.h"
 #include "prefill_kernel.h"
 #include <algorithm>
@@ -44,6 +47,28 @@ template <int G, int U>
 hipError_t launch_g(const pf::PrefillArgs& pa, const dec::DecodeArgs& da, int n_pre, int n_dec,
                     hipStream_t stream) {
   hipLaunchKernelGGL((mixed_kernel<G, U>), dim3(n_pre + n_dec), dim3(pf::kWaves * kWave), 0,
+                     stream, pa, da, n_pre);
+  return hipGetLastError();
+}
+
+// The same over int8 pages: the int8 chunk body (its code ring fills most of
+// the LDS, one workgroup per CU) beside the int8 decode body with one KV
+// head and four page-part waves per workgroup.
+template <int G, int U>
+__global__ void __launch_bounds__(pf::kWaves * kWave, 1)
+mixed_int8_kernel(const pf::PrefillArgs pa, const dec::DecodeArgs da, const int n_prefill_wgs) {
+  static_assert(pf::kWaves <= dec::kI8LdsWaves, "int8 staging buffers for every wave");
+  const int bid = blockIdx.x;
+  if (bid < n_prefill_wgs)
+    pf::prefill_body<true>(pa, bid);
+  else
+    dec::decode_body<dec::Int8Page, G, U, pf::kWaves, false>(da, bid - n_prefill_wgs);
+}
+
+template <int G, int U>
+hipError_t launch_int8_g(const pf::PrefillArgs& pa, const dec::DecodeArgs& da, int n_pre,
+                         int n_dec, hipStream_t stream) {
+  hipLaunchKernelGGL((mixed_int8_kernel<G, U>), dim3(n_pre + n_dec), dim3(pf::kWaves * kWave), 0,
                      stream, pa, da, n_pre);
   return hipGetLastError();
 }
@@ -128,6 +153,36 @@ hipError_t launch_prefill_decode(void* out_p, const void* q_p, const int32_t* cu
     case 1: return launch_g<1, PKV_DECODE_U_G1>(pa, da, (int)n_pre, (int)n_dec, stream);
     case 2: return launch_g<2, PKV_DECODE_U_G2>(pa, da, (int)n_pre, (int)n_dec, stream);
     case 4: return launch_g<4, PKV_DECODE_U_G4>(pa, da, (int)n_pre, (int)n_dec, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_decode_int8(void* out_p, const void* q_p, const int32_t* cu_q,
+                                      const int32_t* bt_p, const int32_t* ctx_p, int B_p,
+                                      int total_q, int max_q_len, const PrefillPlan& pplan,
+                                      void* ws_p, void* out_d, const void* q_d,
+                                      const int32_t* bt_d, const int32_t* ctx_d, int B_d,
+                                      const DecodePlan& dplan, void* ws_d, const void* k_codes,
+                                      const void* v_codes, const float* k_scales,
+                                      const float* v_scales, int Hq, int Hkv, int num_blocks,
+                                      int max_blocks, float scale, hipStream_t stream) {
+  if (!mixed_plan_fits(dplan, Hq / Hkv)) return hipErrorInvalidValue;
+  const pf::PrefillArgs pa =
+      pf::make_prefill_args(out_p, q_p, cu_q, k_codes, v_codes, k_scales, v_scales, bt_p, ctx_p,
+                            B_p, total_q, max_q_len, Hq, Hkv, num_blocks, max_blocks, scale, 0,
+                            pplan, ws_p);
+  DecodePlan dp = dplan;
+  dp.heads_per_wg = 1;
+  const dec::DecodeArgs da =
+      dec::make_args(out_d, q_d, k_codes, v_codes, k_scales, v_scales, bt_d, ctx_d, B_d, Hq, Hkv,
+                     num_blocks, max_blocks, scale, dp, dec::workspace_buffers(dp, ws_d), 0);
+  const int64_t n_pre = (int64_t)B_p * pa.qtiles * pa.splits * Hkv;
+  const int64_t n_dec = (int64_t)B_d * dp.splits * Hkv;
+  if (n_pre + n_dec > 0x7fffffff) return hipErrorInvalidValue;
+  switch (Hq / Hkv) {
+    case 1: return launch_int8_g<1, PKV_DECODE_I8_U_G1>(pa, da, (int)n_pre, (int)n_dec, stream);
+    case 2: return launch_int8_g<2, PKV_DECODE_I8_U_G2>(pa, da, (int)n_pre, (int)n_dec, stream);
+    case 4: return launch_int8_g<4, PKV_DECODE_I8_U_G4>(pa, da, (int)n_pre, (int)n_dec, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -720,6 +720,69 @@ int pkv_attn_prefill_decode(void* out_prefill, const void* q_prefill, const int3
   return PKV_OK;
 }
 
+int pkv_attn_prefill_decode_int8(
+    void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
+    const int32_t* block_tables_prefill, const int32_t* context_lens_prefill, int32_t B_prefill,
+    int32_t total_q, int32_t max_q_len, int32_t max_context_len_prefill, void* out_decode,
+    const void* q_decode, const int32_t* block_tables_decode, const int32_t* context_lens_decode,
+    int32_t B_decode, int32_t max_context_len_decode, const void* k_codes, const void* v_codes,
+    const float* k_scales, const float* v_scales, int32_t Hq, int32_t Hkv, int32_t D,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+    void* prefill_workspace, size_t prefill_workspace_bytes, void* decode_workspace,
+    size_t decode_workspace_bytes, void* stream) {
+  if (((B_prefill > 0 && total_q > 0) || B_decode > 0) && (!k_scales || !v_scales))
+    return fail(PKV_EINVAL, "null pointer argument");
+  pkv::PrefillPlan pplan;
+  bool pdone = true;
+  int rc = check_prefill(out_prefill, q_prefill, cu_q_lens, k_codes, v_codes,
+                         block_tables_prefill, context_lens_prefill, B_prefill, total_q,
+                         max_q_len, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                         max_context_len_prefill, 0, scale, prefill_workspace,
+                         prefill_workspace_bytes, stream, pplan, pdone);
+  if (rc) return rc;
+  pkv::DecodePlan dplan;
+  bool ddone = false;
+  rc = check_decode(out_decode, q_decode, k_codes, v_codes, block_tables_decode,
+                    context_lens_decode, B_decode, Hq, Hkv, D, block_size, num_blocks,
+                    max_blocks_per_seq, max_context_len_decode, scale, decode_workspace,
+                    decode_workspace_bytes, stream, dplan, ddone);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!pdone && !ddone) {
+    if (out_prefill == out_decode) return fail(PKV_EINVAL, "the two outputs must differ");
+    if (pplan.ws_bytes && dplan.ws_bytes && prefill_workspace == decode_workspace)
+      return fail(PKV_EINVAL, "the two workspaces must differ");
+    if (pkv::mixed_plan_fits(dplan, Hq / Hkv))
+      return launch_status(
+          pkv::launch_prefill_decode_int8(
+              out_prefill, q_prefill, cu_q_lens, block_tables_prefill, context_lens_prefill,
+              B_prefill, total_q, max_q_len, pplan, prefill_workspace, out_decode, q_decode,
+              block_tables_decode, context_lens_decode, B_decode, dplan, decode_workspace,
+              k_codes, v_codes, k_scales, v_scales, Hq, Hkv, num_blocks, max_blocks_per_seq,
+              scale, s),
+          "pkv_attn_prefill_decode_int8");
+  }
+  // one half only, or a shape the one-grid launch does not take: the two
+  // launches one after the other
+  if (!pdone) {
+    rc = launch_status(pkv::launch_prefill(out_prefill, q_prefill, cu_q_lens, k_codes, v_codes,
+                                           k_scales, v_scales, block_tables_prefill,
+                                           context_lens_prefill, B_prefill, total_q, max_q_len,
+                                           Hq, Hkv, num_blocks, max_blocks_per_seq, scale, 0,
+                                           pplan, prefill_workspace, s),
+                       "pkv_attn_prefill_decode_int8");
+    if (rc) return rc;
+  }
+  if (!ddone)
+    return launch_status(pkv::launch_decode_int8(out_decode, q_decode, k_codes, v_codes,
+                                                 k_scales, v_scales, block_tables_decode,
+                                                 context_lens_decode, B_decode, Hq, Hkv,
+                                                 num_blocks, max_blocks_per_seq, scale, dplan,
+                                                 decode_workspace, s),
+                         "pkv_attn_prefill_decode_int8");
+  return PKV_OK;
+}
+
 int pkv_attn_prefill_decode_append(
     void* out_prefill, const void* q_prefill, const int32_t* cu_q_lens,
     const int32_t* block_tables_prefill, const int32_t* context_lens_prefill, int32_t B_prefill,

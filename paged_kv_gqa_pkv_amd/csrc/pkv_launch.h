@@ -137,6 +137,17 @@ hipError_t launch_prefill_decode(void* out_p, const void* q_p, const int32_t* cu
                                  void* ws_d, const void* k_cache, const void* v_cache, int Hq,
                                  int Hkv, int num_blocks, int max_blocks, float scale,
                                  hipStream_t stream);
+// The same over int8 pages (codes and head-major scales as for
+// launch_prefill / launch_decode_int8), one workgroup per CU.
+hipError_t launch_prefill_decode_int8(void* out_p, const void* q_p, const int32_t* cu_q,
+                                      const int32_t* bt_p, const int32_t* ctx_p, int B_p,
+                                      int total_q, int max_q_len, const PrefillPlan& pplan,
+                                      void* ws_p, void* out_d, const void* q_d,
+                                      const int32_t* bt_d, const int32_t* ctx_d, int B_d,
+                                      const DecodePlan& dplan, void* ws_d, const void* k_codes,
+                                      const void* v_codes, const float* k_scales,
+                                      const float* v_scales, int Hq, int Hkv, int num_blocks,
+                                      int max_blocks, float scale, hipStream_t stream);
 // The same with the step's append in the grid: the chunk reads its own rows
 // from k_new ([total_q + B_d][Hkv][D]: the chunk rows in cu_q order, then one
 // row per decode sequence), the decode half takes its rows from there and

@@ -245,6 +245,24 @@ def _mixed(lib, out_p=1, out_d=2, Bp=1, T=64, mql=64, mclp=64, Bd=2, mcld=64, Hq
                                        0.088, pws, pwb, dws, dwb, NULL)
 
 
+def _mixed_int8(lib, out_p=1, out_d=2, Bp=1, T=64, mql=64, mclp=64, Bd=2, mcld=64, Hq=16,
+                Hkv=8, D=128, mb=4, ks=12, vs=13):
+    return lib.pkv_attn_prefill_decode_int8(out_p, 3, 4, 5, 6, Bp, T, mql, mclp,
+                                            out_d, 7, 8, 9, Bd, mcld, 10, 11, ks, vs, Hq, Hkv, D,
+                                            16, 32, mb, 0.088, NULL, 0, NULL, 0, NULL)
+
+
+def test_prefill_decode_int8_rejects_bad_arguments(lib):
+    assert _mixed_int8(lib, ks=NULL) == bd.PKV_EINVAL               # scales required
+    assert _mixed_int8(lib, vs=NULL) == bd.PKV_EINVAL
+    assert _mixed_int8(lib, Hq=12) == bd.PKV_EUNSUPPORTED           # Hq % Hkv
+    assert _mixed_int8(lib, out_p=NULL) == bd.PKV_EINVAL
+    assert _mixed_int8(lib, out_d=1) == bd.PKV_EINVAL               # one output for both halves
+    assert b"outputs" in lib.pkv_last_error()
+    assert _mixed_int8(lib, mql=65) == bd.PKV_EINVAL                # max_q_len > total_q
+    assert _mixed_int8(lib, Bp=0, T=0, mql=0, Bd=0, ks=NULL, vs=NULL) == bd.PKV_OK
+
+
 def test_prefill_decode_rejects_bad_arguments(lib):
     assert _mixed(lib, Hq=12) == bd.PKV_EUNSUPPORTED                # Hq % Hkv
     assert _mixed(lib, D=64) == bd.PKV_EUNSUPPORTED
