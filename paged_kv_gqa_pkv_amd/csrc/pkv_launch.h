@@ -107,7 +107,7 @@ struct PrefillPlan {
   int qtiles;
   int splits;
   int tiles_per_split;
-  size_t ws_acc_bytes;      // float [groups][S][D][128]
+  size_t ws_acc_bytes;      // float [groups][S][D/4][128][4]
   size_t ws_ml_bytes;       // float [groups][S][128][2]
   size_t ws_counter_bytes;  // int [groups], split arrivals (zero between calls)
   size_t ws_bytes;          // total, 0 without splits

@@ -132,7 +132,7 @@ struct PrefillArgs {
   // are written by others during the same launch.
   const u32x4* k_new;
   const u32x4* v_new;
-  float* ws_acc;                 // [groups][splits][D][128 rows]
+  float* ws_acc;                 // [groups][splits][D/4][128 rows][4]
   float* ws_ml;                  // [groups][splits][128 rows][2]
   int* counters;                 // [groups] arrivals of the group's splits
   int B, total_q, max_q_len, Hq, Hkv, G, num_blocks, max_blocks, qtiles, splits,
@@ -186,6 +186,33 @@ __device__ __forceinline__ void ws_store(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes per lane with the same coherence (the store instruction the
+// agent-scope atomic store above compiles to, for four floats).  The s_nop
+// is the wait state a store of more than 8 bytes needs before its data
+// registers may be overwritten, which the compiler does not insert after
+// inline asm.
+__device__ __forceinline__ void ws_store4(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 0" :: "v"(p), "v"(v) : "memory");
+}
+// Agent-coherent loads of the partials (the instruction a relaxed
+// agent-scope atomic load compiles to), issued with no wait of their own: the
+// caller waits once for a batch (ws_wait) and then passes each result through
+// ws_ready, which orders its uses after that wait.  Coherent loads need no
+// acquire fence, whose cache invalidation would also drop the K/V lines that
+// other workgroups on the same XCD are reading.
+__device__ __forceinline__ f32x4 ws_load4(const float* p) {
+  f32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ f32x2 ws_load2(const float* p) {
+  f32x2 r;
+  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ void ws_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <class T>
+__device__ __forceinline__ void ws_ready(T& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void ws_store2(float* p, float lo, float hi) {
   const uint64_t bits = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
@@ -781,20 +808,28 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
   }
 
   // Split path: write this split's unnormalised state for the workgroup's
-  // rows (dim-major, so a store instruction covers 32 consecutive rows) with
-  // agent-coherent stores, wait for them, and count the arrival.  The last of
-  // the group's ns splits to arrive merges all of them, in split order (the
-  // same arithmetic whichever split arrives last), and writes the rows.
+  // rows with agent-coherent stores, wait for them, and count the arrival.
+  // The last of the group's ns splits to arrive merges all of them, in split
+  // order (the same arithmetic whichever split arrives last), and writes the
+  // rows.  A partial is laid out [D/4][128 rows][4]: the four consecutive
+  // dims a lane holds in each accumulator quad are 16 contiguous bytes, and
+  // the 32 rows of a half-wave 512 contiguous bytes, so each lane writes and
+  // reads its 64 values in 16 four-float accesses that coalesce.
   const int lrow = w * kRowsPerWave + (lane & 31);          // row within the tile
   const int64_t g0 = (int64_t)group * a.splits;              // the group's first split
-  float* pacc = a.ws_acc + (g0 + ks) * kD * kRowsPerWG + lrow;
+  // dims 32 db + 8 k + 4 half + (0..3) of row lrow: quad 8 db + 2 k + half
+  const uint32_t lane_quad = (uint32_t)((half * kRowsPerWG + lrow) * 4);   // floats
+  {
+    float* pacc = a.ws_acc + (g0 + ks) * kD * kRowsPerWG + lane_quad;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 32 * db + 8 * (i >> 2) + 4 * half + (i & 3);
-      ws_store(pacc + d * kRowsPerWG, poisoned ? nan : o[db][i]);
-    }
+      for (int k = 0; k < 4; ++k) {
+        f32x4 v = {o[db][4 * k], o[db][4 * k + 1], o[db][4 * k + 2], o[db][4 * k + 3]};
+        if (poisoned) v = f32x4{nan, nan, nan, nan};
+        ws_store4(pacc + (8 * db + 2 * k) * kRowsPerWG * 4, v);
+      }
+  }
   if (half == 0) ws_store2(a.ws_ml + 2 * ((g0 + ks) * kRowsPerWG + lrow), m, poisoned ? nan : l);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -804,34 +839,40 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
              tk.ns - 1;
   __syncthreads();
   if (!s_last) return;                        // uniform: not the last split
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // Leave the counter at zero for the next call on this workspace.
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!row_ok) return;
-  // Online merge of the ns splits in split order, kMB splits' loads (their
-  // (m, l) and the lane's 64 dims of each partial) in flight at a time: one
-  // for bf16 pages (two workgroups per CU leave 256 registers), two for
-  // int8.  The order is fixed, so the result does not depend on which split
-  // came last.
-  constexpr int kMB = kI8 ? 2 : 1;
+  // Online merge of the ns splits in split order, one split's loads (its
+  // (m, l) and the lane's 64 dims of its partial, coherent loads waited for
+  // together) at a time: two at a time measured no faster, and slower over
+  // int8 pages.  The order is fixed, so the result does not depend on which
+  // split came last.
+  constexpr int kMB = 1;
   const int ns = tk.ns;
   const float* mlr = a.ws_ml + 2 * (g0 * kRowsPerWG + lrow);
-  const float* paccs = a.ws_acc + g0 * kD * kRowsPerWG + lrow;
   float acc[4][16] = {};
   float Mr = kNegInf, Lr = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kMB) {
     f32x2 mlv[kMB];
-    float v[kMB][4][16];
+    f32x4 c[kMB][4][4];
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
       const int sj = min(s0 + j, ns - 1);     // past the last split: loaded, not used
-      mlv[j] = *reinterpret_cast<const f32x2*>(mlr + 2 * sj * kRowsPerWG);
-      const float* ps = paccs + (int64_t)sj * kD * kRowsPerWG;
+      mlv[j] = ws_load2(mlr + 2 * sj * kRowsPerWG);
+      const float* ps = a.ws_acc + (g0 + sj) * kD * kRowsPerWG + lane_quad;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          v[j][db][i] = ps[(32 * db + 8 * (i >> 2) + 4 * half + (i & 3)) * kRowsPerWG];
+        for (int k = 0; k < 4; ++k) c[j][db][k] = ws_load4(ps + (8 * db + 2 * k) * kRowsPerWG * 4);
+    }
+    ws_wait();
+#pragma unroll
+    for (int j = 0; j < kMB; ++j) {
+      ws_ready(mlv[j]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ws_ready(c[j][db][k]);
     }
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
@@ -843,7 +884,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] = __builtin_fmaf(v[j][db][i], ws, acc[db][i] * r);
+        for (int i = 0; i < 16; ++i)
+          acc[db][i] = __builtin_fmaf(c[j][db][i >> 2][i & 3], ws, acc[db][i] * r);
       Mr = Mn;
     }
   }
