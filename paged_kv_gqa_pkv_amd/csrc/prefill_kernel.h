@@ -194,25 +194,6 @@ __device__ __forceinline__ void ws_store(float* p, float v) {
 __device__ __forceinline__ void ws_store4(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 0" :: "v"(p), "v"(v) : "memory");
 }
-// Agent-coherent loads of the partials (the instruction a relaxed
-// agent-scope atomic load compiles to), issued with no wait of their own: the
-// caller waits once for a batch (ws_wait) and then passes each result through
-// ws_ready, which orders its uses after that wait.  Coherent loads need no
-// acquire fence, whose cache invalidation would also drop the K/V lines that
-// other workgroups on the same XCD are reading.
-__device__ __forceinline__ f32x4 ws_load4(const float* p) {
-  f32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-__device__ __forceinline__ f32x2 ws_load2(const float* p) {
-  f32x2 r;
-  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-__device__ __forceinline__ void ws_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-template <class T>
-__device__ __forceinline__ void ws_ready(T& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void ws_store2(float* p, float lo, float hi) {
   const uint64_t bits = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
@@ -858,21 +839,22 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
       const int sj = min(s0 + j, ns - 1);     // past the last split: loaded, not used
-      mlv[j] = ws_load2(mlr + 2 * sj * kRowsPerWG);
+      mlv[j] = coherent_load2(mlr + 2 * sj * kRowsPerWG);
       const float* ps = a.ws_acc + (g0 + sj) * kD * kRowsPerWG + lane_quad;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) c[j][db][k] = ws_load4(ps + (8 * db + 2 * k) * kRowsPerWG * 4);
+        for (int k = 0; k < 4; ++k)
+          c[j][db][k] = coherent_load4(ps + (8 * db + 2 * k) * kRowsPerWG * 4);
     }
-    ws_wait();
+    coherent_wait();
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
-      ws_ready(mlv[j]);
+      coherent_ready(mlv[j]);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) ws_ready(c[j][db][k]);
+        for (int k = 0; k < 4; ++k) coherent_ready(c[j][db][k]);
     }
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
