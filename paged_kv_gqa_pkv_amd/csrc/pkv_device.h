@@ -81,27 +81,6 @@ __device__ __forceinline__ Halves halves32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Agent-coherent loads of split partials (the instruction a relaxed
-// agent-scope atomic load compiles to: it reads past the non-coherent
-// caches), issued with no wait of their own.  The caller waits once for a
-// batch (coherent_wait) and then passes each result through coherent_ready,
-// which orders its uses after that wait.  Reading partials this way needs no
-// acquire fence, whose cache invalidation would also drop the lines that the
-// XCD's other workgroups are reading.
-__device__ __forceinline__ f32x4 coherent_load4(const float* p) {
-  f32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-__device__ __forceinline__ f32x2 coherent_load2(const float* p) {
-  f32x2 r;
-  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-__device__ __forceinline__ void coherent_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-template <class T>
-__device__ __forceinline__ void coherent_ready(T& v) { asm volatile("" : "+v"(v)); }
-
 // Sum and max over the 64 lanes of a wave; every lane gets the result.
 __device__ __forceinline__ float wave_sum(float x) {
   x = sum8(x);

@@ -186,6 +186,13 @@ __device__ __forceinline__ void ws_store(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
+// Buffer loads of the split partials: the descriptor's last word for
+// untyped 32-bit data on this architecture family, and the cache-policy
+// operand of an agent-coherent access (sc1: read past the non-coherent
+// caches, as the agent-scope stores wrote past them).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCoherent = 16;
+
 // 16 bytes per lane with the same coherence (the store instruction the
 // agent-scope atomic store above compiles to, for four floats).  The s_nop
 // is the wait state a store of more than 8 bytes needs before its data
@@ -830,31 +837,32 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
   // split came last.
   constexpr int kMB = 1;
   const int ns = tk.ns;
-  const float* mlr = a.ws_ml + 2 * (g0 * kRowsPerWG + lrow);
   float acc[4][16] = {};
   float Mr = kNegInf, Lr = 0.f;
+  // The group's partials and (m, l) pairs as two buffer resources (the
+  // buffer form takes the coherence bit as an operand the compiler tracks).
+  const __amdgpu_buffer_rsrc_t acc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.ws_acc + g0 * kD * kRowsPerWG), (short)0,
+      ns * kD * kRowsPerWG * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.ws_ml + 2 * g0 * kRowsPerWG), (short)0, ns * kRowsPerWG * 8,
+      kBufferWord3);
   for (int s0 = 0; s0 < ns; s0 += kMB) {
     f32x2 mlv[kMB];
     f32x4 c[kMB][4][4];
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
       const int sj = min(s0 + j, ns - 1);     // past the last split: loaded, not used
-      mlv[j] = coherent_load2(mlr + 2 * sj * kRowsPerWG);
-      const float* ps = a.ws_acc + (g0 + sj) * kD * kRowsPerWG + lane_quad;
+      mlv[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             ml_rsrc, (sj * kRowsPerWG + lrow) * 8, 0, kCoherent));
+      const int split_off = (sj * kD * kRowsPerWG + (int)lane_quad) * 4;   // bytes
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          c[j][db][k] = coherent_load4(ps + (8 * db + 2 * k) * kRowsPerWG * 4);
-    }
-    coherent_wait();
-#pragma unroll
-    for (int j = 0; j < kMB; ++j) {
-      coherent_ready(mlv[j]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) coherent_ready(c[j][db][k]);
+          c[j][db][k] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         acc_rsrc, split_off + (8 * db + 2 * k) * kRowsPerWG * 16, 0, kCoherent));
     }
 #pragma unroll
     for (int j = 0; j < kMB; ++j) {
