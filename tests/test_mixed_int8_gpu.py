@@ -156,3 +156,23 @@ def test_graph_replays_are_bit_identical():
         e_p, e_d = mixed_call(dev, plan)              # eager work between replays
         torch.cuda.synchronize()
         assert bits_equal(e_p, want_p) and bits_equal(e_d, want_d), rep
+
+
+def test_invalid_pages_poison_their_sequences_in_both_forms():
+    """A prefill sequence whose table holds an invalid page id and a decode
+    sequence whose table holds one: their outputs are NaN, the others'
+    finite, and the one-launch form gives the two calls' outputs bit for
+    bit (the poisoned rows included)."""
+    w = S.workload("c5", 2)
+    t, d, dev, plan, host_pools = setup(w)
+    npre = len(w.prefill_seqs)
+    plan.block_tables[0, 3] = -1                      # a page of the chunk's prefix
+    plan.block_tables[npre + 1, 0] = 1 << 30          # past the pool
+    op, od = mixed_call(dev, plan)
+    sp, sd = separate_calls(dev, plan)
+    torch.cuda.synchronize()
+    assert bits_equal(op, sp) and bits_equal(od, sd)
+    assert torch.isnan(op.float()).all(), "the chunk's rows are poisoned"
+    assert torch.isnan(od[1].float()).all()
+    keep = [i for i in range(od.shape[0]) if i != 1]
+    assert torch.isfinite(od[keep].float()).all()
