@@ -842,11 +842,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs a, const int bid)
   // The group's partials and (m, l) pairs as two buffer resources (the
   // buffer form takes the coherence bit as an operand the compiler tracks).
   const __amdgpu_buffer_rsrc_t acc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.ws_acc + g0 * kD * kRowsPerWG), (short)0,
-      ns * kD * kRowsPerWG * 4, kBufferWord3);
+      a.ws_acc + g0 * kD * kRowsPerWG, (short)0, ns * kD * kRowsPerWG * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.ws_ml + 2 * g0 * kRowsPerWG), (short)0, ns * kRowsPerWG * 8,
-      kBufferWord3);
+      a.ws_ml + 2 * g0 * kRowsPerWG, (short)0, ns * kRowsPerWG * 8, kBufferWord3);
   for (int s0 = 0; s0 < ns; s0 += kMB) {
     f32x2 mlv[kMB];
     f32x4 c[kMB][4][4];
