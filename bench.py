@@ -672,6 +672,21 @@ def run(args):
                                  "kernel": mix_kernel +
                                            ": the chunk's causal FLOPs over the whole launch, "
                                            "decode included"}
+    def pcts(events):
+        # p10 / median / p90 of the timed launches, in us, per part of the step
+        by = {}
+        for (k, a, b, _) in events:
+            by.setdefault(parts[k].w.name, []).append(a.elapsed_time(b) * 1e3)
+        out = {}
+        for name, d in by.items():
+            d.sort()
+            out[name] = [round(d[min(len(d) - 1, int(q * len(d)))], 2) for q in (0.1, 0.5, 0.9)]
+        return out
+
+    if roofline is not None and (dec_events or mix_events):
+        roofline["launch_us_p10_p50_p90"] = pcts(dec_events or mix_events)
+    if "prefill_mfma" in extra and (pre_events or mix_events):
+        extra["prefill_mfma"]["launch_us_p10_p50_p90"] = pcts(pre_events or mix_events)
     w0 = parts[0].w
     cfg = {"workload": WORKLOAD_TEXT.get(args.workload, f"{args.workload}: {w0.description}"),
            "parts": [{"name": p.w.name, "layers": p.w.n_layers, "Hq": p.w.Hq, "Hkv": p.w.Hkv,
